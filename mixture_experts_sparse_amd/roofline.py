@@ -1,0 +1,91 @@
+"""Algorithmic work counts and roofline arithmetic for the MoE layer forward.
+
+These are the figures the benchmark divides by measured time. They count
+what the method must do, not what an implementation adds:
+
+* FLOPs = 2*T*d*E (router) + 2*P*3*d*h (routed SwiGLU experts, P = T*k)
+          + 2*T*3*d*hs + 2*T*d (shared expert and its sigmoid gate).
+  Softmax, top-k, dispatch and combine are not counted (well under 0.1%).
+* bytes = U*3*d*h*b (the weights of the U experts that received at least one
+          token) + E*d*b (router) + T*d*b (x) + T*d*b (out)
+          + 3*d*hs*b + d*b (shared expert) + 4*E (fp32 router bias),
+  with b the bytes per activation/weight element. Intermediates (act, y,
+  dispatch tables) are implementation traffic and are not counted.
+
+Two formulas from the pages pin this module's arithmetic:
+* the gathered-weight tensor a naive dispatch builds, T*h*d*bytes
+  ("Small models, sparse experts", section "Dispatch decides everything":
+  one projection, one layer, 2,048 tokens, [2048, 512, 640] fp32 = 2.68 GB);
+* the batch-1 decode ceiling, bandwidth / bytes of active weights
+  ("Small MoE Architecture, in depth", section "Worked example: the batch-1
+  budget on a device").
+"""
+
+from __future__ import annotations
+
+# MI355X published peaks.
+PEAK_BF16_MFMA_FLOPS = 2.5e15       # dense bf16 MFMA
+PEAK_FP32_VALU_FLOPS = 157.3e12     # fp32 vector
+PEAK_HBM_BYTES = 8.0e12             # HBM3E
+
+
+def layer_flops(T, d, E, h, k, hs=0, shared_gate=False):
+    f = 2.0 * T * d * E + 2.0 * T * k * 3 * d * h
+    if hs:
+        f += 2.0 * T * 3 * d * hs
+        if shared_gate:
+            f += 2.0 * T * d
+    return f
+
+
+def layer_bytes(T, d, E, h, U, elem_bytes, hs=0, shared_gate=False, has_bias=False):
+    b = elem_bytes
+    n = U * 3.0 * d * h * b + E * d * b + 2.0 * T * d * b
+    if hs:
+        n += 3.0 * d * hs * b
+        if shared_gate:
+            n += d * b
+    if has_bias:
+        n += 4.0 * E
+    return n
+
+
+def gate_up_flops(P, d, h, T=0, hs=0):
+    """Gate and up projections of the routed rows (+ the shared expert's)."""
+    return 2.0 * P * 2 * d * h + 2.0 * T * 2 * d * hs
+
+
+def gate_up_bytes(T, d, h, U, elem_bytes, hs=0):
+    """Gate and up weights of the touched experts (+ shared) and x, once."""
+    return (U * 2.0 * d * h + 2.0 * d * hs + T * d) * elem_bytes
+
+
+def down_flops(P, d, h, T=0, hs=0):
+    return 2.0 * P * d * h + 2.0 * T * d * hs
+
+
+def down_bytes(d, h, U, elem_bytes, hs=0):
+    return (U * d * h + d * hs) * elem_bytes
+
+
+def gathered_weight_bytes(T, h, d, elem_bytes):
+    """Bytes of one projection's per-token gathered weights [T, h, d]."""
+    return T * h * d * elem_bytes
+
+
+def dense_to_sparse_flop_ratio(E, k):
+    """Running all E experts instead of the k selected multiplies expert
+    arithmetic by E/k."""
+    return E / k
+
+
+def batch1_decode_ceiling(total_params, active_params, bytes_per_param, mem_gb_s):
+    """(footprint GB, upper bound tokens/s) when every active weight is
+    streamed once per token."""
+    footprint_gb = total_params * bytes_per_param / 1e9
+    per_token_gb = active_params * bytes_per_param / 1e9
+    return footprint_gb, mem_gb_s / per_token_gb
+
+
+def ridge_flop_per_byte(peak_flops=PEAK_BF16_MFMA_FLOPS, peak_bytes=PEAK_HBM_BYTES):
+    return peak_flops / peak_bytes

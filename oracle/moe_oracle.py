@@ -1,0 +1,318 @@
+"""CPU oracle for the sparse mixture-of-experts FFN layer forward.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or
+execute this module; only the tests, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg use it. It shares no code with the HIP path:
+it receives the generated input arrays (bf16 bit patterns or float32) and
+converts them exactly to float64; every step below runs in float64 with no
+intermediate rounding.
+
+Steps, in the order the pages give them:
+
+1. router logits  L = x W_r^T (+ b)
+   ("Tutorial 11: Mixture of Experts (MoE)", section 2 "The Router": a plain
+   linear map from hidden states to one score per expert; the router of
+   "Mixture-of-Experts -- more capacity per byte of weight", section "What's
+   wired today", is bias-free. The bias is an extra input of the skewed
+   workload only.)
+2. top-k selection on L, ties to the lower expert index, slots in descending
+   logit order (Tutorial 11, section 2, step 3 picks the k largest; "Small MoE
+   Architecture, in depth", section "A small MoE layer in PyTorch", uses topk).
+3. gates: softmax over all experts, gathered at the selection and optionally
+   renormalised to sum 1 (Tutorial 11, section 2, steps 2, 4 and 5), or a
+   softmax over the k selected logits ("Small models, sparse experts",
+   section "How it works", step 3).
+4. dispatch: counts per expert, exclusive offsets and a stable sort of the
+   flattened (token, slot) pairs by expert (Tutorial 11, section 3, step 1;
+   the per-expert load is the bincount of "Small MoE Architecture, in depth",
+   section "A small MoE layer in PyTorch").
+5. expert FFN, looping over experts and running each expert's SwiGLU
+   W_d (silu(W_g x) * (W_u x)) on its own rows only (Tutorial 11, section 3,
+   step 2; "Small MoE Architecture, in depth", class Expert and the
+   loop-over-experts of SmallMoE.forward).
+6. combine: out[t] = sum_j g[t, j] y[t, j], an additive weighted sum in slot
+   order (Tutorial 11, section 3, step 3 and section 4, step 5).
+7. shared expert: an always-on SwiGLU added to the routed output ("Small MoE
+   Architecture, in depth", section "A small MoE layer in PyTorch"); the
+   sigmoid(w_s . x) scale on it is an input option of the shared-plus-routed
+   workload, not a formula on the pages.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+SOFTMAX_ALL = 0
+SOFTMAX_SELECTED = 1
+
+NEAR_TIE_EPS = 1e-5
+
+
+# ----------------------------------------------------------------------------
+# exact input conversion
+# ----------------------------------------------------------------------------
+
+def to_f64(a):
+    """bf16 bit patterns (uint16) or float32 -> float64, exactly."""
+    if a is None:
+        return None
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if a.dtype in (np.float32, np.float64):
+        return a.astype(np.float64)
+    raise TypeError(f"unsupported input dtype {a.dtype}")
+
+
+# ----------------------------------------------------------------------------
+# textbook building blocks
+# ----------------------------------------------------------------------------
+
+def silu(z):
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    return z / (1.0 + np.exp(-z))
+
+
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def softmax(z, axis=-1):
+    """Max-subtracted softmax (the numerically careful form)."""
+    m = np.max(z, axis=axis, keepdims=True)
+    e = np.exp(z - m)
+    return e / np.sum(e, axis=axis, keepdims=True)
+
+
+def swiglu(X, Wg, Wu, Wd):
+    """The SwiGLU FFN W_d (silu(W_g x) * (W_u x)) on the rows of X.
+
+    "Small MoE Architecture, in depth", section "A small MoE layer in
+    PyTorch", class Expert; Tutorial 11, section 4, step 4.
+    """
+    return (silu(X @ Wg.T) * (X @ Wu.T)) @ Wd.T
+
+
+# ----------------------------------------------------------------------------
+# step 1-3: route
+# ----------------------------------------------------------------------------
+
+def router_logits(x, w_router, b_router=None):
+    """L[t, e] = sum_i x[t, i] W_r[e, i] (+ b[e])."""
+    L = to_f64(x) @ to_f64(w_router).T
+    if b_router is not None:
+        L = L + to_f64(b_router)[None, :]
+    return L
+
+
+def topk_select(L, k):
+    """The k largest logits per row: ties go to the lower expert index, and
+    slots are ordered by descending logit (lower index first among equals).
+
+    A stable ascending sort of -L keeps equal keys in index order, which is
+    exactly that order.
+    """
+    E = L.shape[1]
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    return np.argsort(-L, axis=1, kind="stable")[:, :k].astype(np.int64)
+
+
+def gate_weights(L, ids, mode, renormalize):
+    """Gate weights for the selected experts.
+
+    SOFTMAX_ALL: p = softmax(L) over all E experts; g[t, j] = p[t, ids[t, j]];
+    optionally g /= sum_j g (Tutorial 11, section 2, steps 2, 4, 5).
+    SOFTMAX_SELECTED: g = softmax over the k selected logits ("Small models,
+    sparse experts", section "How it works", step 3).
+    Returns (g, p) where p is the full softmax (None for SOFTMAX_SELECTED).
+    """
+    if mode == SOFTMAX_ALL:
+        p = softmax(L, axis=1)
+        g = np.take_along_axis(p, ids, axis=1)
+        if renormalize:
+            g = g / np.sum(g, axis=1, keepdims=True)
+        return g, p
+    if mode == SOFTMAX_SELECTED:
+        g = softmax(np.take_along_axis(L, ids, axis=1), axis=1)
+        if renormalize:
+            g = g / np.sum(g, axis=1, keepdims=True)
+        return g, None
+    raise ValueError(f"unknown gate mode {mode}")
+
+
+def near_ties(L, k, eps=NEAR_TIE_EPS):
+    """Tokens whose routing is decided by a logit gap below ``eps``.
+
+    Returns (select, order): ``select`` marks tokens where the k-th and
+    (k+1)-th largest logits differ by less than eps (the selected *set* is
+    then ambiguous at fp32 precision); ``order`` marks tokens where two
+    adjacent selected logits differ by less than eps (the slot *order* is then
+    ambiguous). Both are empty when k == E for ``select``.
+    """
+    s = -np.sort(-L, axis=1)
+    T, E = L.shape
+    if k < E:
+        select = (s[:, k - 1] - s[:, k]) < eps
+    else:
+        select = np.zeros(T, dtype=bool)
+    if k > 1:
+        order = np.any((s[:, : k - 1] - s[:, 1:k]) < eps, axis=1)
+    else:
+        order = np.zeros(T, dtype=bool)
+    return select, order
+
+
+# ----------------------------------------------------------------------------
+# step 4: dispatch
+# ----------------------------------------------------------------------------
+
+def dispatch(ids, E):
+    """Counting sort of the T*k (token, slot) pairs by expert.
+
+    Pair p = t*k + j has expert ids[t, j]. Returns counts[E], offsets[E+1]
+    (exclusive prefix sum, offsets[E] = T*k), perm[P] (sorted row -> pair,
+    stable: rows of one expert keep ascending p) and inv[P] = perm^-1.
+    """
+    flat = np.asarray(ids).reshape(-1).astype(np.int64)
+    counts = np.bincount(flat, minlength=E).astype(np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    perm = np.argsort(flat, kind="stable").astype(np.int64)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.size, dtype=np.int64)
+    return counts, offsets, perm, inv
+
+
+# ----------------------------------------------------------------------------
+# step 5: grouped expert FFN
+# ----------------------------------------------------------------------------
+
+def gate_up(x, perm, offsets, k, w_gate, w_up):
+    """act[r] = silu(W_g[e] x_t) * (W_u[e] x_t) for sorted row r of expert e,
+    t = perm[r] // k. Loops over experts, not tokens."""
+    X = to_f64(x)
+    E, h, _ = w_gate.shape
+    P = perm.size
+    act = np.zeros((P, h))
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r0 == r1:
+            continue
+        Xe = X[perm[r0:r1] // k]
+        act[r0:r1] = silu(Xe @ to_f64(w_gate[e]).T) * (Xe @ to_f64(w_up[e]).T)
+    return act
+
+
+def down(act, offsets, w_down):
+    """y[r] = W_d[e] act[r] for sorted row r of expert e."""
+    E, d, _ = w_down.shape
+    y = np.zeros((act.shape[0], d))
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r0 == r1:
+            continue
+        y[r0:r1] = act[r0:r1] @ to_f64(w_down[e]).T
+    return y
+
+
+def expert_ffn(x, perm, offsets, k, w_gate, w_up, w_down):
+    """y[P, d] in sorted order, un-gated: each expert's SwiGLU on its rows."""
+    return down(gate_up(x, perm, offsets, k, w_gate, w_up), offsets, w_down)
+
+
+# ----------------------------------------------------------------------------
+# step 6-7: combine and shared expert
+# ----------------------------------------------------------------------------
+
+def combine(y_sorted, inv, gates, shared=None):
+    """out[t] = sum_{j<k} g[t, j] y[inv[t*k + j]] (+ shared[t]), summed in
+    slot order j = 0..k-1."""
+    T, k = gates.shape
+    d = y_sorted.shape[1]
+    Y = y_sorted[np.asarray(inv).reshape(T, k)]  # [T, k, d]
+    out = np.zeros((T, d))
+    for j in range(k):
+        out += gates[:, j, None] * Y[:, j, :]
+    if shared is not None:
+        out += shared
+    return out
+
+
+def shared_expert(x, ws_gate, ws_up, ws_down, w_shared_gate=None):
+    """s[t] = (sigmoid(w_s . x_t) if gated else 1) * SwiGLU_shared(x_t)."""
+    X = to_f64(x)
+    s = swiglu(X, to_f64(ws_gate), to_f64(ws_up), to_f64(ws_down))
+    if w_shared_gate is not None:
+        s = s * sigmoid(X @ to_f64(w_shared_gate))[:, None]
+    return s
+
+
+# ----------------------------------------------------------------------------
+# the whole layer
+# ----------------------------------------------------------------------------
+
+def _spec_fields(spec):
+    return spec.E, spec.k, spec.mode, bool(spec.renormalize)
+
+
+def route(inp, ids_override=None):
+    """Steps 1-3. ``ids_override`` (dict token -> k expert ids) replaces the
+    selection of those tokens; their gates are still computed by step 3 from
+    the float64 logits (used for tokens whose selection is a near tie)."""
+    spec = inp["spec"]
+    E, k, mode, renorm = _spec_fields(spec)
+    L = router_logits(inp["x"], inp["w_router"], inp.get("b_router"))
+    ids = topk_select(L, k)
+    if ids_override:
+        for t, sel in ids_override.items():
+            ids[t] = np.asarray(sel, dtype=np.int64)
+    g, p = gate_weights(L, ids, mode, renorm)
+    return L, ids, g, p
+
+
+def layer_forward(inp, ids_override=None):
+    """Steps 1-7 on the whole batch. Returns a dict with out [T, d] (float64),
+    logits, ids, gates, counts, offsets, perm, inv, y (sorted, un-gated),
+    shared (or None) and the near-tie masks."""
+    spec = inp["spec"]
+    E, k = spec.E, spec.k
+    L, ids, g, p = route(inp, ids_override)
+    counts, offsets, perm, inv = dispatch(ids, E)
+    y = expert_ffn(inp["x"], perm, offsets, k, inp["w_gate"], inp["w_up"], inp["w_down"])
+    shared = None
+    if inp.get("ws_gate") is not None:
+        shared = shared_expert(inp["x"], inp["ws_gate"], inp["ws_up"], inp["ws_down"],
+                               inp.get("w_shared_gate"))
+    out = combine(y, inv, g, shared)
+    sel_tie, ord_tie = near_ties(L, k)
+    return {"out": out, "logits": L, "probs": p, "ids": ids, "gates": g,
+            "counts": counts, "offsets": offsets, "perm": perm, "inv": inv,
+            "y": y, "shared": shared, "near_tie_select": sel_tie,
+            "near_tie_order": ord_tie}
+
+
+def token_forward(inp, tokens, ids, gates):
+    """Output rows for a few tokens, one token at a time, from a given
+    selection and gates: out[t] = sum_j g[t, j] SwiGLU_{ids[t, j]}(x_t)
+    (+ shared). This is the per-token statement of the same layer, used to
+    check sampled rows of full-size runs."""
+    X = to_f64(inp["x"])
+    has_shared = inp.get("ws_gate") is not None
+    if has_shared:
+        Sg, Su, Sd = (to_f64(inp[n]) for n in ("ws_gate", "ws_up", "ws_down"))
+        wsg = to_f64(inp.get("w_shared_gate")) if inp.get("w_shared_gate") is not None else None
+    rows = []
+    for t, sel, g in zip(tokens, ids, gates):
+        xt = X[t:t + 1]
+        o = np.zeros(X.shape[1])
+        for e, ge in zip(sel, g):
+            o += ge * swiglu(xt, to_f64(inp["w_gate"][e]), to_f64(inp["w_up"][e]),
+                             to_f64(inp["w_down"][e]))[0]
+        if has_shared:
+            s = swiglu(xt, Sg, Su, Sd)[0]
+            if wsg is not None:
+                s = s * sigmoid(float(xt[0] @ wsg))
+            o += s
+        rows.append(o)
+    return np.stack(rows) if rows else np.zeros((0, X.shape[1]))

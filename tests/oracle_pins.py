@@ -1,0 +1,398 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each ``check_*`` function raises AssertionError when the oracle disagrees
+with what the pages or the mathematics fix. ``test_oracle_pins.py`` runs
+them as they are; ``test_oracle_mutations.py`` plants plausible mistakes in
+the oracle and confirms that at least one of them fails.
+
+The pins:
+  worked example  - the renormalisation example of "Tutorial 11: Mixture of
+                    Experts (MoE)", section 2 (tests/golden)
+  brute force     - top-k by a rank-count definition and by maximising the
+                    sum of selected logits over all subsets (tiny E)
+  dense mask      - running every expert on every token and masking with the
+                    gate scattered to [T, E] ("Small models, sparse experts",
+                    section "Dispatch decides everything"; "Mixture-of-Experts
+                    -- more capacity per byte of weight", section "What's NOT
+                    shipped yet") gives the same output as sparse dispatch
+  invariants      - conservation of pairs, permutation, monotone offsets,
+                    stable groups, gate sums
+  special cases   - k=1 with renorm is the argmax expert; k=E is the full
+                    softmax mixture; identical experts give the plain FFN;
+                    x = 0 gives 0; hidden-slice concatenation
+  textbook        - silu / sigmoid / softmax values and scipy
+"""
+
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle.moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _inputs(T, d, E, h, k, mode, renorm, seed=0, shared_h=0, gated=False, bias=False,
+            scale=1.0):
+    """A small float32 input dict in the generator's layout (drawn here so the
+    pins do not depend on the generator)."""
+    from moe_inputs.spec import MoESpec, F32
+    r = _rng(seed)
+    spec = MoESpec(name="pin", T=T, d=d, E=E, h=h, k=k, dtype=F32, mode=mode,
+                   renormalize=renorm, shared_h=shared_h, shared_gate=gated,
+                   router_bias="zipf" if bias else None)
+    inp = {
+        "spec": spec,
+        "x": r.standard_normal((T, d)).astype(np.float32),
+        "w_router": (r.standard_normal((E, d)) * 0.3 * scale).astype(np.float32),
+        "b_router": (r.standard_normal(E) * 0.5).astype(np.float32) if bias else None,
+        "w_gate": (r.standard_normal((E, h, d)) * 0.2).astype(np.float32),
+        "w_up": (r.standard_normal((E, h, d)) * 0.2).astype(np.float32),
+        "w_down": (r.standard_normal((E, d, h)) * 0.2).astype(np.float32),
+    }
+    if shared_h:
+        inp["ws_gate"] = (r.standard_normal((shared_h, d)) * 0.2).astype(np.float32)
+        inp["ws_up"] = (r.standard_normal((shared_h, d)) * 0.2).astype(np.float32)
+        inp["ws_down"] = (r.standard_normal((d, shared_h)) * 0.2).astype(np.float32)
+        inp["w_shared_gate"] = (r.standard_normal(d) * 0.3).astype(np.float32) if gated else None
+    else:
+        inp["ws_gate"] = inp["ws_up"] = inp["ws_down"] = inp["w_shared_gate"] = None
+    return inp
+
+
+# ---------------------------------------------------------------------------
+# worked example
+# ---------------------------------------------------------------------------
+
+def check_worked_example():
+    with open(os.path.join(GOLDEN, "renorm_worked_example.json")) as f:
+        g = json.load(f)
+    probs = np.array(g["probs"], dtype=np.float64)
+    L = np.log(probs)[None, :]
+    k = g["top_k"]
+    ids = O.topk_select(L, k)
+    assert ids[0].tolist() == g["expected_ids"], ids
+    raw, p = O.gate_weights(L, ids, O.SOFTMAX_ALL, False)
+    np.testing.assert_allclose(p[0], probs, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(raw[0], g["expected_scores_raw"], rtol=1e-12, atol=0)
+    assert abs(raw[0].sum() - g["expected_raw_sum"]) < 1e-12
+    half = 0.5 * 10.0 ** (-g["printed_decimals"])
+    for mode in (O.SOFTMAX_ALL, O.SOFTMAX_SELECTED):
+        ren, _ = O.gate_weights(L, ids, mode, mode == O.SOFTMAX_ALL)
+        got = ren[0]
+        assert np.all(np.abs(got - np.array(g["expected_scores_renorm_printed"])) <= half), got
+        # exact values behind the printed ones: 0.3/0.55 = 6/11, 0.25/0.55 = 5/11
+        np.testing.assert_allclose(got, [6 / 11, 5 / 11], rtol=1e-12, atol=0)
+        assert abs(got.sum() - g["expected_renorm_sum"]) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# brute-force top-k
+# ---------------------------------------------------------------------------
+
+def _rank_count_topk(Lrow, k):
+    """e is selected iff fewer than k experts beat it, where e' beats e if its
+    logit is larger, or equal with a lower index. Slot = that count."""
+    E = Lrow.size
+    out = [None] * k
+    for e in range(E):
+        beats = sum(1 for f in range(E)
+                    if Lrow[f] > Lrow[e] or (Lrow[f] == Lrow[e] and f < e))
+        if beats < k:
+            out[beats] = e
+    return out
+
+
+def _subset_max(Lrow, k):
+    best = None
+    for sub in itertools.combinations(range(Lrow.size), k):
+        s = sum(Lrow[i] for i in sub)
+        if best is None or s > best[0]:
+            best = (s, sub)
+    return best
+
+
+def check_brute_force_topk():
+    r = _rng(1)
+    for trial in range(300):
+        E = int(r.integers(1, 9))
+        k = int(r.integers(1, E + 1))
+        if trial % 3 == 0:
+            Lrow = r.integers(-2, 3, size=E).astype(np.float64)  # many exact ties
+        else:
+            Lrow = r.standard_normal(E)
+        ids = O.topk_select(Lrow[None, :], k)[0].tolist()
+        assert ids == _rank_count_topk(Lrow, k), (Lrow, k, ids)
+        assert len(set(ids)) == k
+        s, _ = _subset_max(Lrow, k)
+        assert abs(sum(Lrow[i] for i in ids) - s) <= 1e-12 * max(1.0, abs(s))
+    # all-equal logits: ids are the first k experts in index order
+    for E in (1, 5, 8):
+        for k in range(1, E + 1):
+            ids = O.topk_select(np.zeros((3, E)), k)
+            assert (ids == np.arange(k)[None, :]).all()
+
+
+# ---------------------------------------------------------------------------
+# sparse dispatch == dense all-experts-then-mask
+# ---------------------------------------------------------------------------
+
+def dense_mask_forward(inp):
+    """Every expert on every token, weighted by a gate that is zero outside
+    the top-k. Computed without the oracle's dispatch, combine or top-k."""
+    spec = inp["spec"]
+    X = inp["x"].astype(np.float64)
+    Wr = inp["w_router"].astype(np.float64)
+    L = X @ Wr.T
+    if inp.get("b_router") is not None:
+        L = L + inp["b_router"].astype(np.float64)[None, :]
+    T, E = L.shape
+    k = spec.k
+    mask = np.zeros((T, E))
+    for t in range(T):
+        for e in _rank_count_topk(L[t], k):
+            mask[t, e] = 1.0
+    if spec.mode == O.SOFTMAX_ALL:
+        z = np.exp(L - L.max(axis=1, keepdims=True))
+        G = z / z.sum(axis=1, keepdims=True) * mask
+        if spec.renormalize:
+            G = G / G.sum(axis=1, keepdims=True)
+    else:
+        z = np.exp(L - L.max(axis=1, keepdims=True)) * mask
+        G = z / z.sum(axis=1, keepdims=True)
+    out = np.zeros((T, X.shape[1]))
+    for e in range(E):
+        Wg = inp["w_gate"][e].astype(np.float64)
+        Wu = inp["w_up"][e].astype(np.float64)
+        Wd = inp["w_down"][e].astype(np.float64)
+        a = X @ Wg.T
+        ye = ((a / (1.0 + np.exp(-a))) * (X @ Wu.T)) @ Wd.T
+        out += G[:, e:e + 1] * ye
+    if inp.get("ws_gate") is not None:
+        a = X @ inp["ws_gate"].astype(np.float64).T
+        s = ((a / (1.0 + np.exp(-a))) * (X @ inp["ws_up"].astype(np.float64).T)) \
+            @ inp["ws_down"].astype(np.float64).T
+        if inp.get("w_shared_gate") is not None:
+            s = s / (1.0 + np.exp(-(X @ inp["w_shared_gate"].astype(np.float64))))[:, None]
+        out += s
+    return out
+
+
+def check_dense_mask_equivalence():
+    cases = [
+        dict(T=37, d=24, E=8, h=16, k=2, mode=O.SOFTMAX_ALL, renorm=True),
+        dict(T=29, d=16, E=6, h=12, k=3, mode=O.SOFTMAX_ALL, renorm=False),
+        dict(T=31, d=16, E=7, h=8, k=4, mode=O.SOFTMAX_SELECTED, renorm=False),
+        dict(T=23, d=16, E=5, h=8, k=2, mode=O.SOFTMAX_ALL, renorm=True, bias=True),
+        dict(T=19, d=16, E=6, h=8, k=2, mode=O.SOFTMAX_ALL, renorm=False,
+             shared_h=20, gated=True),
+        dict(T=17, d=16, E=4, h=8, k=4, mode=O.SOFTMAX_ALL, renorm=False),
+    ]
+    for i, c in enumerate(cases):
+        inp = _inputs(seed=10 + i, **c)
+        got = O.layer_forward(inp)["out"]
+        ref = dense_mask_forward(inp)
+        err = np.max(np.abs(got - ref))
+        assert err <= 1e-12 * max(1.0, np.max(np.abs(ref))), (c, err)
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+
+def check_dispatch_invariants():
+    r = _rng(2)
+    for trial in range(50):
+        E = int(r.integers(1, 40))
+        k = int(r.integers(1, min(E, 8) + 1))
+        T = int(r.integers(0, 60))
+        ids = np.stack([r.permutation(E)[:k] for _ in range(T)]) if T else np.zeros((0, k), int)
+        counts, offsets, perm, inv = O.dispatch(ids, E)
+        P = T * k
+        assert counts.sum() == P
+        assert offsets[0] == 0 and offsets[-1] == P
+        assert np.all(np.diff(offsets) == counts)
+        assert sorted(perm.tolist()) == list(range(P))
+        assert np.all(inv[perm] == np.arange(P))
+        flat = ids.reshape(-1)
+        for e in range(E):
+            grp = perm[offsets[e]:offsets[e + 1]]
+            assert np.all(flat[grp] == e)
+            assert np.all(np.diff(grp) > 0)  # stable: ascending pair index
+            assert counts[e] == int(np.sum(flat == e))
+
+
+def check_gate_sums():
+    r = _rng(3)
+    for trial in range(40):
+        E = int(r.integers(2, 20))
+        k = int(r.integers(1, E + 1))
+        L = r.standard_normal((11, E)) * 3
+        ids = O.topk_select(L, k)
+        g, p = O.gate_weights(L, ids, O.SOFTMAX_ALL, True)
+        assert np.allclose(g.sum(1), 1.0, rtol=0, atol=1e-12)
+        g, p = O.gate_weights(L, ids, O.SOFTMAX_SELECTED, False)
+        assert np.allclose(g.sum(1), 1.0, rtol=0, atol=1e-12)
+        g2, _ = O.gate_weights(L, ids, O.SOFTMAX_ALL, True)
+        assert np.allclose(g, g2, rtol=0, atol=1e-12)  # the two modes agree
+        g, p = O.gate_weights(L, ids, O.SOFTMAX_ALL, False)
+        assert np.all(g.sum(1) <= 1.0 + 1e-12)
+        assert np.all(np.diff(g, axis=1) <= 1e-15)  # slot order = descending score
+        # full softmax is scipy's
+        from scipy.special import softmax as sp_softmax
+        np.testing.assert_allclose(p, sp_softmax(L, axis=1), rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# special cases and closed forms
+# ---------------------------------------------------------------------------
+
+def _ffn(x, Wg, Wu, Wd):
+    a = x @ Wg.T
+    return ((a / (1.0 + np.exp(-a))) * (x @ Wu.T)) @ Wd.T
+
+
+def check_k1_is_argmax_expert():
+    inp = _inputs(T=25, d=16, E=6, h=10, k=1, mode=O.SOFTMAX_ALL, renorm=True, seed=4)
+    res = O.layer_forward(inp)
+    assert np.all(res["gates"] == 1.0)
+    X = inp["x"].astype(np.float64)
+    L = X @ inp["w_router"].astype(np.float64).T
+    for t in range(25):
+        e = int(np.argmax(L[t]))
+        ref = _ffn(X[t:t + 1], inp["w_gate"][e].astype(np.float64),
+                   inp["w_up"][e].astype(np.float64), inp["w_down"][e].astype(np.float64))[0]
+        np.testing.assert_allclose(res["out"][t], ref, rtol=1e-12, atol=1e-12)
+
+
+def check_k_equals_E_is_soft_mixture():
+    for renorm in (False, True):
+        inp = _inputs(T=13, d=12, E=5, h=6, k=5, mode=O.SOFTMAX_ALL, renorm=renorm, seed=5)
+        res = O.layer_forward(inp)
+        X = inp["x"].astype(np.float64)
+        L = X @ inp["w_router"].astype(np.float64).T
+        from scipy.special import softmax as sp_softmax
+        p = sp_softmax(L, axis=1)
+        ref = np.zeros_like(res["out"])
+        for e in range(5):
+            ref += p[:, e:e + 1] * _ffn(X, inp["w_gate"][e].astype(np.float64),
+                                        inp["w_up"][e].astype(np.float64),
+                                        inp["w_down"][e].astype(np.float64))
+        np.testing.assert_allclose(res["out"], ref, rtol=1e-11, atol=1e-12)
+        assert not res["near_tie_select"].any()
+
+
+def check_identical_experts():
+    for mode, renorm in ((O.SOFTMAX_ALL, True), (O.SOFTMAX_SELECTED, False)):
+        inp = _inputs(T=21, d=16, E=6, h=10, k=3, mode=mode, renorm=renorm, seed=6)
+        for n in ("w_gate", "w_up", "w_down"):
+            inp[n] = np.repeat(inp[n][:1], 6, axis=0)
+        res = O.layer_forward(inp)
+        X = inp["x"].astype(np.float64)
+        ref = _ffn(X, inp["w_gate"][0].astype(np.float64), inp["w_up"][0].astype(np.float64),
+                   inp["w_down"][0].astype(np.float64))
+        np.testing.assert_allclose(res["out"], ref, rtol=1e-11, atol=1e-12)
+
+
+def check_zero_input():
+    inp = _inputs(T=9, d=16, E=5, h=8, k=2, mode=O.SOFTMAX_ALL, renorm=False, seed=7,
+                  bias=True, shared_h=8, gated=True)
+    inp["x"] = np.zeros_like(inp["x"])
+    res = O.layer_forward(inp)
+    assert np.all(res["out"] == 0.0)
+    # all logits equal the bias: selection follows the bias order
+    order = np.argsort(-inp["b_router"].astype(np.float64), kind="stable")[:2]
+    assert np.all(res["ids"] == order[None, :])
+
+
+def check_hidden_slice_concatenation():
+    """A SwiGLU of hidden H is the sum of the SwiGLUs on a partition of its
+    hidden units: four slices of a dense FFN routed with a zero router (all
+    logits tie, so ids = 0..3 and softmax-all gates are 1/4) give FFN/4; the
+    shared expert of hidden 4*h equals the sum of four hidden-h pieces."""
+    r = _rng(8)
+    T, d, h = 15, 16, 6
+    G = r.standard_normal((4 * h, d)) * 0.3
+    U = r.standard_normal((4 * h, d)) * 0.3
+    D = r.standard_normal((d, 4 * h)) * 0.3
+    X = r.standard_normal((T, d))
+    from moe_inputs.spec import MoESpec, F32
+    spec = MoESpec(name="slices", T=T, d=d, E=4, h=h, k=4, dtype=F32,
+                   mode=O.SOFTMAX_ALL, renormalize=False)
+    inp = {"spec": spec, "x": X, "w_router": np.zeros((4, d)), "b_router": None,
+           "w_gate": np.stack([G[s * h:(s + 1) * h] for s in range(4)]),
+           "w_up": np.stack([U[s * h:(s + 1) * h] for s in range(4)]),
+           "w_down": np.stack([D[:, s * h:(s + 1) * h] for s in range(4)]),
+           "ws_gate": None, "ws_up": None, "ws_down": None, "w_shared_gate": None}
+    res = O.layer_forward(inp)
+    assert np.all(res["ids"] == np.arange(4)[None, :])
+    np.testing.assert_allclose(res["gates"], 0.25, rtol=0, atol=1e-15)
+    dense = _ffn(X, G, U, D)
+    np.testing.assert_allclose(res["out"], dense / 4, rtol=1e-11, atol=1e-12)
+    s = O.shared_expert(X, G, U, D)
+    parts = sum(_ffn(X, G[i * h:(i + 1) * h], U[i * h:(i + 1) * h], D[:, i * h:(i + 1) * h])
+                for i in range(4))
+    np.testing.assert_allclose(s, parts, rtol=1e-11, atol=1e-12)
+
+
+def check_textbook_functions():
+    from scipy.special import expit
+    z = np.linspace(-30, 30, 121)
+    np.testing.assert_allclose(O.sigmoid(z), expit(z), rtol=1e-14, atol=0)
+    np.testing.assert_allclose(O.silu(z), z * expit(z), rtol=1e-13, atol=1e-300)
+    assert O.silu(np.array(0.0)) == 0.0
+    assert O.sigmoid(np.array(0.0)) == 0.5
+    assert abs(float(O.silu(np.array(1.0))) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+    # softmax of logs of a distribution returns it
+    q = np.array([[1.0, 2.0, 3.0, 4.0]]) / 10.0
+    np.testing.assert_allclose(O.softmax(np.log(q)), q, rtol=1e-14)
+    # shift invariance (the max subtraction must not change values)
+    a = np.array([[1000.0, 1001.0, 999.0]])
+    np.testing.assert_allclose(O.softmax(a), O.softmax(a - 1000.0), rtol=1e-14)
+
+
+def check_combine_gather_vs_loop():
+    """The combine against the per-token statement of the layer: for each
+    token, the weighted sum of its selected experts' SwiGLU outputs."""
+    inp = _inputs(T=14, d=12, E=5, h=7, k=3, mode=O.SOFTMAX_ALL, renorm=False, seed=9,
+                  shared_h=9, gated=True)
+    res = O.layer_forward(inp)
+    rows = O.token_forward(inp, list(range(14)), res["ids"], res["gates"])
+    np.testing.assert_allclose(res["out"], rows, rtol=1e-12, atol=1e-13)
+
+
+def check_near_tie_detection():
+    L = np.array([[1.0, 0.5, 0.5 - 5e-6, -1.0],    # k=2: 2nd vs 3rd within eps
+                  [2.0, 2.0 - 3e-6, 0.0, -1.0],     # order tie among selected
+                  [3.0, 2.0, 1.0, 0.0]])            # clean
+    sel, order = O.near_ties(L, 2)
+    assert sel.tolist() == [True, False, False]
+    assert order.tolist() == [False, True, False]
+    sel, order = O.near_ties(L, 4)
+    assert not sel.any()
+
+
+ALL_CHECKS = [
+    check_worked_example,
+    check_brute_force_topk,
+    check_dense_mask_equivalence,
+    check_dispatch_invariants,
+    check_gate_sums,
+    check_k1_is_argmax_expert,
+    check_k_equals_E_is_soft_mixture,
+    check_identical_experts,
+    check_zero_input,
+    check_hidden_slice_concatenation,
+    check_textbook_functions,
+    check_combine_gather_vs_loop,
+    check_near_tie_detection,
+]

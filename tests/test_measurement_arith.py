@@ -1,0 +1,56 @@
+"""The roofline arithmetic against the figures the pages print."""
+
+import json
+import os
+
+from mixture_experts_sparse_amd import roofline as R
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _fig():
+    with open(os.path.join(GOLDEN, "measurement_figures.json")) as f:
+        return json.load(f)
+
+
+def test_gathered_weight_bytes_matches_printed():
+    g = _fig()["gathered_weights"]
+    b = R.gathered_weight_bytes(g["T"], g["h"], g["d"], g["elem_bytes"])
+    assert b == 2_684_354_560
+    assert round(b / 1e9, g["printed_decimals"]) == g["printed_gb"]
+
+
+def test_dense_waste_ratio_matches_printed():
+    g = _fig()["dense_expert_waste"]
+    assert R.dense_to_sparse_flop_ratio(g["E"], g["k"]) == g["printed_ratio"]
+    # the same ratio falls out of the FLOP counter: all-E experts vs top-k
+    T, d, h = 100, 640, 512
+    routed = R.layer_flops(T, d, g["E"], h, g["k"]) - 2.0 * T * d * g["E"]
+    dense = R.layer_flops(T, d, g["E"], h, g["E"]) - 2.0 * T * d * g["E"]
+    assert dense / routed == g["printed_ratio"]
+
+
+def test_decode_ceilings_match_printed():
+    g = _fig()["decode_ceilings"]
+    for row in g["rows"]:
+        fp, tps = R.batch1_decode_ceiling(row["total"], row["active"], g["bytes_per_param"],
+                                          g["mem_gb_s"])
+        assert round(fp, 2) == row["footprint_gb"], row
+        assert round(tps) == row["ceiling_tok_s"], row
+
+
+def test_workload_counts():
+    # gemma_upcycled: T=8192, d=640, E=256, h=512, k=4, all experts touched
+    f = R.layer_flops(8192, 640, 256, 512, 4)
+    assert abs(f - 6.711e10) / 6.711e10 < 1e-3
+    b = R.layer_bytes(8192, 640, 256, 512, 256, 2)
+    assert abs(b - 5.246e8) / 5.246e8 < 1e-3
+    # shared_routed: half routed, half shared
+    f5 = R.layer_flops(8192, 2048, 60, 1408, 4, hs=5632, shared_gate=True)
+    assert abs(f5 - 1.13592e12) / 1.13592e12 < 1e-3
+    # skewed_prefill
+    f4 = R.layer_flops(16384, 2048, 128, 768, 8)
+    assert abs(f4 - 1.2455e12) / 1.2455e12 < 1e-3
+    # decode: 12,582,912 bytes per expert
+    assert 3 * 2048 * 1024 * 2 == 12_582_912
+    assert abs(R.ridge_flop_per_byte() - 312.5) < 1e-9

@@ -1,0 +1,118 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that at
+least one pin fails for each. This shows the pins constrain every step:
+selection, gating, dispatch, expert FFN, combine, shared expert, bias."""
+
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as O
+import oracle_pins as pins
+
+
+def _topk_ties_high(L, k):
+    E = L.shape[1]
+    rev = np.argsort(-L[:, ::-1], axis=1, kind="stable")[:, :k]
+    return (E - 1 - rev).astype(np.int64)
+
+
+def _gates_no_renorm(L, ids, mode, renormalize):
+    return _ORIG["gate_weights"](L, ids, mode, False)
+
+
+def _gates_selected_as_all(L, ids, mode, renormalize):
+    if mode == O.SOFTMAX_SELECTED:
+        mode = O.SOFTMAX_ALL
+    return _ORIG["gate_weights"](L, ids, mode, renormalize)
+
+
+def _dispatch_unstable(ids, E):
+    counts, offsets, perm, inv = _ORIG["dispatch"](ids, E)
+    perm = perm.copy()
+    for e in range(E):
+        perm[offsets[e]:offsets[e + 1]] = perm[offsets[e]:offsets[e + 1]][::-1]
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.size)
+    return counts, offsets, perm, inv
+
+
+def _combine_wrong_index(y_sorted, inv, gates, shared=None):
+    T, k = gates.shape
+    perm = np.empty_like(inv)
+    perm[inv] = np.arange(inv.size)
+    return _ORIG["combine"](y_sorted, perm, gates, shared)
+
+
+def _silu_dropped_z(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def _gate_up_swapped(x, perm, offsets, k, w_gate, w_up):
+    return _ORIG["gate_up"](x, perm, offsets, k, w_up, w_gate)
+
+
+def _gate_up_token_mod(x, perm, offsets, k, w_gate, w_up):
+    # wrong token index: pair % k instead of pair // k
+    X = O.to_f64(x)
+    E, h, _ = w_gate.shape
+    act = np.zeros((perm.size, h))
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r0 == r1:
+            continue
+        Xe = X[perm[r0:r1] % k]
+        act[r0:r1] = O.silu(Xe @ O.to_f64(w_gate[e]).T) * (Xe @ O.to_f64(w_up[e]).T)
+    return act
+
+
+def _down_transposed(act, offsets, w_down):
+    return _ORIG["down"](act, offsets, np.swapaxes(w_down, 1, 2))
+
+
+def _shared_ungated(x, ws_gate, ws_up, ws_down, w_shared_gate=None):
+    return _ORIG["shared_expert"](x, ws_gate, ws_up, ws_down, None)
+
+
+def _logits_no_bias(x, w_router, b_router=None):
+    return _ORIG["router_logits"](x, w_router, None)
+
+
+def _combine_drop_last_slot(y_sorted, inv, gates, shared=None):
+    g = gates.copy()
+    g[:, -1] = 0.0
+    return _ORIG["combine"](y_sorted, inv, g, shared)
+
+
+_ORIG = {n: getattr(O, n) for n in ("gate_weights", "dispatch", "combine", "gate_up",
+                                    "down", "shared_expert", "router_logits", "topk_select",
+                                    "silu")}
+
+MUTATIONS = [
+    ("topk_select", _topk_ties_high),
+    ("gate_weights", _gates_no_renorm),
+    ("gate_weights", _gates_selected_as_all),
+    ("dispatch", _dispatch_unstable),
+    ("combine", _combine_wrong_index),
+    ("combine", _combine_drop_last_slot),
+    ("silu", _silu_dropped_z),
+    ("gate_up", _gate_up_swapped),
+    ("gate_up", _gate_up_token_mod),
+    ("down", _down_transposed),
+    ("shared_expert", _shared_ungated),
+    ("router_logits", _logits_no_bias),
+]
+
+
+def _any_pin_fails():
+    for check in pins.ALL_CHECKS:
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError):
+            return check.__name__
+    return None
+
+
+@pytest.mark.parametrize("name,fn", MUTATIONS, ids=[m[1].__name__ for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(O, name, fn)
+    failed = _any_pin_fails()
+    assert failed is not None, f"no pin caught the planted mistake {fn.__name__}"
