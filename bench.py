@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Sparse MoE FFN layer forward on one MI355X: tokens/s and roofline fractions.
+
+A step is one moe_layer_forward call (route, dispatch, gate/up, down,
+combine, and the shared expert where the workload has one) over one batch of
+seeded synthetic tokens, with the inputs already resident in HBM. Steps
+rotate over R distinct copies of the layer's weights (like a stack of
+layers), R chosen so that the copies span at least 2 GiB: the 256 MB
+Infinity Cache cannot serve repeats, so every step streams its weights from
+HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+Prints one JSON line. Stage durations come from HIP events the library
+records on its own stream inside the timed loop; ``roofline`` is the
+dominant stage's algorithmic bytes (HBM-bound workloads) or FLOPs
+(MFMA-bound workloads) per launch divided by its measured duration.
+"""
+
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd tokens/s on 1 GPU; % bf16 MFMA peak (prefill) / % HBM BW (decode)"
+
+# Binding roofline of each workload (algorithmic intensity vs the 312.5
+# FLOP/B ridge of 2.5 PFLOP/s bf16 over 8 TB/s).
+BOUND = {"tiny_fp32": "alu", "gemma_upcycled": "hbm", "decode": "hbm",
+         "skewed_prefill": "mfma", "shared_routed": "mfma"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def stage_work(spec, U, T):
+    """Algorithmic (bytes, flops) of each stage of one layer call."""
+    from mixture_experts_sparse_amd import roofline as R
+    b = spec.act_bytes
+    d, h, E, k, hs = spec.d, spec.h, spec.E, spec.k, spec.shared_h
+    P = T * k
+    route_b = (E * d + T * d) * b + (4 * E if spec.router_bias else 0) + (d * b if spec.shared_gate else 0)
+    route_f = 2.0 * T * d * E + (2.0 * T * d if spec.shared_gate else 0)
+    return {
+        "route": (route_b, route_f),
+        "dispatch": (0.0, 0.0),
+        "gate_up": (R.gate_up_bytes(T, d, h, U, b, hs), R.gate_up_flops(P, d, h, T, hs)),
+        "down": (R.down_bytes(d, h, U, b, hs), R.down_flops(P, d, h, T, hs)),
+        "combine": (T * d * b, 0.0),
+    }
+
+
+def cpu_baseline(inp, budget_s=20.0):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle.moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = os.cpu_count() or 1
+    spec = inp["spec"]
+
+    def run(Ts):
+        sub = dict(inp)
+        sub["x"] = inp["x"][:Ts]
+        sub["spec"] = dataclasses.replace(spec, T=Ts)
+        t0 = time.perf_counter()
+        O.layer_forward(sub)
+        return time.perf_counter() - t0
+
+    Ts = min(spec.T, 512)
+    t = run(Ts)
+    # grow the sample towards ~1/3 of the budget per run, capped at the batch
+    while Ts < spec.T and t < budget_s / 6:
+        Ts = min(spec.T, Ts * 2)
+        t = run(Ts)
+    times = [t]
+    while len(times) < 3 and sum(times) + t < budget_s:
+        times.append(run(Ts))
+    med = statistics.median(times)
+    return {"value": Ts / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {Ts} of {spec.T} tokens of the same inputs, float64 NumPy oracle, "
+                      f"median of {len(times)} run(s) of {med:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="gemma_upcycled",
+                    help="workload name (gemma_upcycled, skewed_prefill, shared_routed, "
+                         "decode@T1/4/16/64, tiny_fp32)")
+    ap.add_argument("--rotate-gib", type=float, default=2.0,
+                    help="minimum bytes of distinct weight copies cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the layer forward here runs on a single MI355X "
+              "and has no multi-GPU path (--gpus must be 1).", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_sparse_amd.binding as B
+    from mixture_experts_sparse_amd import roofline as R
+    from mixture_experts_sparse_amd.hip_timing import StageEvents
+    from moe_inputs import generate, spec_by_name
+
+    spec = spec_by_name(args.config)
+    base = args.config.split("@")[0]
+    t0 = time.perf_counter()
+    inp = generate(spec)
+    log(f"[bench] generated {args.config} in {time.perf_counter() - t0:.1f} s")
+    torch.cuda.set_device(0)
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    wnames = ("w_router", "b_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down",
+              "w_shared_gate")
+    w0 = {n: dev(inp.get(n)) for n in wnames}
+    set_bytes = sum(t.numel() * t.element_size() for t in w0.values() if t is not None)
+    nsets = max(1, math.ceil(args.rotate_gib * 2**30 / set_bytes))
+    wsets = [w0] + [{n: (t.clone() if t is not None else None) for n, t in w0.items()}
+                    for _ in range(nsets - 1)]
+    wstructs = [B.weights_struct(w) for w in wsets]
+    x = dev(inp["x"])
+    cfg = B.config_from_spec(spec)
+    T = spec.T
+    out = torch.empty((T, spec.d), dtype=x.dtype, device="cuda")
+    ids = torch.empty((T, spec.k), dtype=torch.int32, device="cuda")
+    counts = torch.empty(spec.E, dtype=torch.int32, device="cuda")
+    ws = B.alloc_workspace(cfg)
+    log(f"[bench] {nsets} weight copies of {set_bytes / 2**20:.1f} MiB, workspace "
+        f"{ws.numel() / 2**20:.1f} MiB")
+
+    for i in range(args.warmup):
+        B.layer_forward(cfg, wstructs[i % nsets], x, out=out, ids=ids, counts=counts, ws=ws)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    ev = StageEvents(args.steps)
+    torch.cuda.synchronize()
+    w_start = time.perf_counter()
+    for i in range(args.steps):
+        B.layer_forward(cfg, wstructs[i % nsets], x, out=out, ids=ids, counts=counts, ws=ws,
+                        stage_events=ev.row(i))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w_start
+    span_ms = ev.span_ms()
+    stage = np.array(ev.stage_ms())  # [steps, stages]
+    ev.destroy()
+    ms_per_step = span_ms / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (events), "
+        f"{wall / args.steps * 1e6:.1f} us/step (wall)")
+
+    cnt = counts.cpu().numpy()
+    U = int((cnt > 0).sum())
+    mean_stage_us = {n: float(stage[:, i].mean() * 1e3) for i, n in enumerate(B.STAGE_NAMES)}
+    work = stage_work(spec, U, T)
+    bound = BOUND[base]
+    dom = max(mean_stage_us, key=mean_stage_us.get)
+    dbytes, dflops = work[dom]
+    dsec = mean_stage_us[dom] * 1e-6
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": dflops / dsec / 1e12,
+                "peak": R.PEAK_BF16_MFMA_FLOPS / 1e12, "unit": "TFLOP/s"}
+    elif bound == "alu":
+        roof = {"bound": "alu", "achieved": dflops / dsec / 1e12,
+                "peak": R.PEAK_FP32_VALU_FLOPS / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": dbytes / dsec / 1e9,
+                "peak": R.PEAK_HBM_BYTES / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+
+    sec = ms_per_step * 1e-3
+    lflops = R.layer_flops(T, spec.d, spec.E, spec.h, spec.k, spec.shared_h, spec.shared_gate)
+    lbytes = R.layer_bytes(T, spec.d, spec.E, spec.h, U, spec.act_bytes, spec.shared_h,
+                           spec.shared_gate, spec.router_bias is not None)
+    result = {
+        "metric": METRIC,
+        "value": T / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.dtype == 1 else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.config, "T": T, "d": spec.d, "E": spec.E, "h": spec.h,
+                   "top_k": spec.k, "shared_h": spec.shared_h,
+                   "gates": ["softmax over all", "softmax over the selected"][spec.mode]
+                   + (" + renormalised" if spec.renormalize else ""),
+                   "weight_copies": nsets, "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": {"mfma_frac": lflops / sec / R.PEAK_BF16_MFMA_FLOPS,
+                  "hbm_frac": lbytes / sec / R.PEAK_HBM_BYTES,
+                  "alg_flops": lflops, "alg_bytes": lbytes, "touched_experts": U,
+                  "max_over_mean_load": float(cnt.max() / max(cnt.mean(), 1e-9))},
+        "stages_us": mean_stage_us,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

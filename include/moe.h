@@ -1,0 +1,206 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the sparse mixture-of-experts FFN layer
+ * forward on AMD MI355X (gfx950).
+ *
+ * The layer (the method of "Tutorial 11: Mixture of Experts (MoE)",
+ * sections 2-4, and of "Small MoE Architecture, in depth", section "A small
+ * MoE layer in PyTorch"):
+ *
+ *   logits  L = x W_r^T (+ b)                                     [T, E]
+ *   ids     the top_k experts per token, ties to the lower index,
+ *           slots in descending logit order                        [T, k]
+ *   gates   MOE_SOFTMAX_ALL:      softmax over all E, gathered at ids,
+ *                                 optionally renormalised to sum 1
+ *           MOE_SOFTMAX_SELECTED: softmax over the k selected logits
+ *   dispatch  stable counting sort of the P = T*k pairs p = t*k + j by
+ *             expert ids[t, j]: counts[E], offsets[E+1], perm[P] (sorted
+ *             row -> pair), inv[P] (pair -> sorted row)
+ *   expert  y[r] = W_d[e] (silu(W_g[e] x_t) * (W_u[e] x_t)) for sorted row r
+ *           of expert e, t = perm[r] / k                           [P, d]
+ *   combine out[t] = sum_{j<k} gates[t, j] y[inv[t*k + j]] (+ shared[t])
+ *   shared  shared[t] = (sigmoid(w_s . x_t) if gated) *
+ *                       Ws_d (silu(Ws_g x_t) * (Ws_u x_t))
+ *
+ * Conventions for every entry point:
+ *  - Tensors are dense row-major device pointers (HBM), 16-byte aligned.
+ *    Activation/weight tensors use cfg->dtype (MOE_F32: float, MOE_BF16:
+ *    bfloat16 bit patterns); gates, logits and the router bias are float32;
+ *    indices and counts are int32.
+ *  - The caller owns every buffer; the library allocates nothing and keeps
+ *    no state between calls. Inputs are read-only; outputs must not alias
+ *    inputs. Scratch memory is the caller's workspace `ws` of at least
+ *    moe_workspace_size_entry(cfg, entry) bytes (256-byte aligned).
+ *  - `stream` is a hipStream_t (NULL = the default stream). Kernels are
+ *    enqueued on it and the library never synchronises; asynchronous faults
+ *    surface at the caller's next synchronisation.
+ *  - All argument validation happens on the host before any HIP call, so an
+ *    error status means nothing was enqueued. T = 0 returns MOE_OK and
+ *    enqueues nothing.
+ *  - Errors: MOE_ERR_INVALID_ARG (NULL required pointer; T < 0; d, h or
+ *    E <= 0; top_k < 1 or top_k > E; bad enum), MOE_ERR_UNSUPPORTED (d, h or
+ *    shared_h not a multiple of 8; E > MOE_MAX_EXPERTS; a pointer not 16-byte
+ *    aligned), MOE_ERR_WORKSPACE (ws too small or not 256-byte aligned),
+ *    MOE_ERR_HIP (a launch failed).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_EXPERTS 256
+#define MOE_NUM_STAGES 5 /* route, dispatch, gate_up, down, combine */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum { MOE_SOFTMAX_ALL = 0, MOE_SOFTMAX_SELECTED = 1 } moe_score_mode;
+
+/* Which entry point a workspace is sized for (moe_workspace_size_entry). */
+typedef enum {
+  MOE_ENTRY_LAYER_FORWARD = 0,
+  MOE_ENTRY_DISPATCH = 1,
+  MOE_ENTRY_GATE_UP = 2,
+  MOE_ENTRY_DOWN = 3,
+  MOE_ENTRY_EXPERT_FFN = 4,
+  MOE_ENTRY_SHARED_EXPERT = 5
+} moe_entry;
+
+/* Shapes and options of one layer call. One (E, h) per call: every routed
+ * expert has the same hidden width ("Mixture-of-Experts -- more capacity per
+ * byte of weight", section "What's wired today": the same N in every block). */
+typedef struct {
+  int32_t T;               /* tokens (rows of x) */
+  int32_t d;               /* model width */
+  int32_t E;               /* routed experts, 1..MOE_MAX_EXPERTS */
+  int32_t h;               /* hidden width of each routed expert */
+  int32_t top_k;           /* experts per token, 1..E */
+  int32_t dtype;           /* moe_dtype of x, weights, act, y, out */
+  int32_t mode;            /* moe_score_mode */
+  int32_t renormalize;     /* 1: divide the k gates by their sum */
+  int32_t has_router_bias; /* 1: b_router [E] float32 is added to the logits */
+  int32_t shared_h;        /* hidden width of the shared expert, 0 = none */
+  int32_t shared_gate;     /* 1: the shared expert is scaled by sigmoid(w_s . x) */
+} moe_config;
+
+/* Weights of one layer, in cfg->dtype unless stated otherwise. */
+typedef struct {
+  const void* w_router;      /* [E, d] */
+  const float* b_router;     /* [E] float32, or NULL when !has_router_bias */
+  const void* w_gate;        /* [E, h, d] */
+  const void* w_up;          /* [E, h, d] */
+  const void* w_down;        /* [E, d, h] */
+  const void* ws_gate;       /* [shared_h, d]  (shared_h > 0) */
+  const void* ws_up;         /* [shared_h, d]  (shared_h > 0) */
+  const void* ws_down;       /* [d, shared_h]  (shared_h > 0) */
+  const void* w_shared_gate; /* [d]            (shared_gate) */
+} moe_weights;
+
+/* Library ABI version (MOE_ABI_VERSION). */
+int32_t moe_abi_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_string(moe_status s);
+
+/* Host-only check of a configuration (no HIP call). */
+moe_status moe_validate_config(const moe_config* cfg);
+
+/* Workspace bytes the given entry point needs for cfg (0 on a bad cfg).
+ * It is O(T*k*(d+h) + T*(d+shared_h) + E*T/64), never O(T*h*d): per-token
+ * gathered weights are never materialised ("Small models, sparse experts",
+ * section "Dispatch decides everything"). */
+size_t moe_workspace_size_entry(const moe_config* cfg, int32_t entry);
+
+/* Workspace bytes for moe_layer_forward (the largest of all entries). */
+size_t moe_workspace_size(const moe_config* cfg);
+
+/* Router: logits, top-k selection and gates ("Tutorial 11: Mixture of
+ * Experts (MoE)", section 2 "The Router"; "Small models, sparse experts",
+ * section "How it works", step 3 for MOE_SOFTMAX_SELECTED).
+ *   x [T, d], w_router [E, d], b_router [E] f32 (iff has_router_bias)
+ *   -> ids [T, k] int32, gates [T, k] f32, logits [T, E] f32 (optional, NULL
+ *   to skip). Logits are accumulated in float32; the top-k compares float32
+ *   logits, ties to the lower expert index. */
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* b_router, int32_t* ids, float* gates, float* logits,
+                     void* stream);
+
+/* Dispatch: stable counting sort of the T*k (token, slot) pairs by expert
+ * ("Tutorial 11: Mixture of Experts (MoE)", section 3, step 1).
+ *   ids [T, k] int32 (each in [0, E)) -> counts [E], offsets [E+1], perm [P],
+ *   inv [P] (all int32). Rows of one expert keep ascending pair order. */
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* ids, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Grouped gate/up projection with the SiLU-gated product
+ * ("Tutorial 11: Mixture of Experts (MoE)", section 3, step 2):
+ *   act[r] = silu(W_g[e] x_t) * (W_u[e] x_t), t = perm[r] / k, for every
+ *   sorted row r of expert e (offsets[e] <= r < offsets[e+1]).
+ *   x [T, d], perm [P], offsets [E+1], w_gate/w_up [E, h, d] -> act [P, h]. */
+moe_status moe_gate_up(const moe_config* cfg, const void* x, const int32_t* perm,
+                       const int32_t* offsets, const void* w_gate, const void* w_up,
+                       void* act, void* ws, size_t ws_bytes, void* stream);
+
+/* Grouped down projection: y[r] = W_d[e] act[r] for sorted row r of expert e.
+ *   act [P, h], offsets [E+1], w_down [E, d, h] -> y [P, d] (sorted order). */
+moe_status moe_down(const moe_config* cfg, const void* act, const int32_t* offsets,
+                    const void* w_down, void* y, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_gate_up then moe_down, with act kept in the workspace:
+ *   -> y [P, d] in sorted order, not yet scaled by the gates. */
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* perm,
+                          const int32_t* offsets, const void* w_gate, const void* w_up,
+                          const void* w_down, void* y, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Always-on shared expert ("Small MoE Architecture, in depth", section "A
+ * small MoE layer in PyTorch"), optionally scaled by sigmoid(w_s . x_t):
+ *   x [T, d], ws_gate/ws_up [shared_h, d], ws_down [d, shared_h],
+ *   w_shared_gate [d] (NULL: ungated) -> s_out [T, d]. Needs shared_h > 0. */
+moe_status moe_shared_expert(const moe_config* cfg, const void* x, const void* ws_gate,
+                             const void* ws_up, const void* ws_down,
+                             const void* w_shared_gate, void* s_out, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* Gate-weighted combine back to token order ("Tutorial 11: Mixture of
+ * Experts (MoE)", section 3, step 3): an additive sum in slot order with
+ * float32 accumulation, rounded once to cfg->dtype.
+ *   y [P, d] (sorted), inv [P], gates [T, k] f32, shared [T, d] or NULL
+ *   -> out [T, d]. */
+moe_status moe_combine(const moe_config* cfg, const void* y, const int32_t* inv,
+                       const float* gates, const void* shared, void* out, void* stream);
+
+/* The whole layer: route, dispatch, gate/up, down, combine (+ shared).
+ *   x [T, d] -> out [T, d]. ids [T, k], gates [T, k] and counts [E] are
+ *   optional copies of the routing (NULL to skip). */
+moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x,
+                             void* out, int32_t* ids, float* gates, int32_t* counts,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* moe_layer_forward that also records stage_events[0] before the first
+ * launch and stage_events[i + 1] after stage i (MOE_NUM_STAGES stages:
+ * route, dispatch, gate_up, down, combine). stage_events holds
+ * MOE_NUM_STAGES + 1 hipEvent_t created by the caller; NULL = untraced. */
+moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
+                                    const void* x, void* out, int32_t* ids, float* gates,
+                                    int32_t* counts, void* ws, size_t ws_bytes,
+                                    void* const* stage_events, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

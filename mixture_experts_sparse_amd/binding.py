@@ -1,0 +1,290 @@
+"""ctypes binding of libmoe.so (include/moe.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the layer runs in the library's kernels.
+There is no fallback: if libmoe.so is missing or a call fails, this module
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_HIP = 4
+
+MOE_F32 = 0
+MOE_BF16 = 1
+MOE_SOFTMAX_ALL = 0
+MOE_SOFTMAX_SELECTED = 1
+
+MOE_ENTRY_LAYER_FORWARD = 0
+MOE_ENTRY_DISPATCH = 1
+MOE_ENTRY_GATE_UP = 2
+MOE_ENTRY_DOWN = 3
+MOE_ENTRY_EXPERT_FFN = 4
+MOE_ENTRY_SHARED_EXPERT = 5
+
+MOE_NUM_STAGES = 5
+STAGE_NAMES = ("route", "dispatch", "gate_up", "down", "combine")
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "T", "d", "E", "h", "top_k", "dtype", "mode", "renormalize", "has_router_bias",
+        "shared_h", "shared_gate")]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [
+        ("w_router", ctypes.c_void_p), ("b_router", ctypes.c_void_p),
+        ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+        ("ws_gate", ctypes.c_void_p), ("ws_up", ctypes.c_void_p), ("ws_down", ctypes.c_void_p),
+        ("w_shared_gate", ctypes.c_void_p),
+    ]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_SIG = {
+    "moe_abi_version": ([], ctypes.c_int32),
+    "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "moe_validate_config": ([_P], ctypes.c_int),
+    "moe_workspace_size_entry": ([_P, ctypes.c_int32], ctypes.c_size_t),
+    "moe_workspace_size": ([_P], ctypes.c_size_t),
+    "moe_route": ([_P] * 8, ctypes.c_int),
+    "moe_dispatch": ([_P] * 7 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_gate_up": ([_P] * 8 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_down": ([_P] * 6 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_expert_ffn": ([_P] * 9 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_shared_expert": ([_P] * 8 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_combine": ([_P] * 7, ctypes.c_int),
+    "moe_layer_forward": ([_P] * 8 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_layer_forward_traced": ([_P] * 8 + [ctypes.c_size_t, _P, _P], ctypes.c_int),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m mixture_experts_sparse_amd.build` (there is no fallback path)")
+        # torch first: its bundled HIP runtime carries the same SONAME
+        # (libamdhip64.so.7), so libmoe binds to the runtime torch's streams
+        # and allocations belong to instead of loading a second copy.
+        import torch  # noqa: F401
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIG.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/moe.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != MOE_OK:
+        raise MoeError(status, what)
+
+
+# ----------------------------------------------------------------------------
+# config helpers
+# ----------------------------------------------------------------------------
+
+def make_config(T, d, E, h, top_k, dtype=MOE_BF16, mode=MOE_SOFTMAX_ALL, renormalize=False,
+                has_router_bias=False, shared_h=0, shared_gate=False) -> MoeConfig:
+    return MoeConfig(int(T), int(d), int(E), int(h), int(top_k), int(dtype), int(mode),
+                     int(bool(renormalize)), int(bool(has_router_bias)), int(shared_h),
+                     int(bool(shared_gate)))
+
+
+def config_from_spec(spec, T: Optional[int] = None) -> MoeConfig:
+    """Config from a moe_inputs.MoESpec-like object (duck-typed)."""
+    return make_config(spec.T if T is None else T, spec.d, spec.E, spec.h, spec.k,
+                       dtype=spec.dtype, mode=spec.mode, renormalize=spec.renormalize,
+                       has_router_bias=spec.router_bias is not None, shared_h=spec.shared_h,
+                       shared_gate=spec.shared_gate and spec.shared_h > 0)
+
+
+def validate_config(cfg: MoeConfig) -> int:
+    return lib().moe_validate_config(ctypes.byref(cfg))
+
+
+def workspace_size(cfg: MoeConfig, entry: int = MOE_ENTRY_LAYER_FORWARD) -> int:
+    return int(lib().moe_workspace_size_entry(ctypes.byref(cfg), int(entry)))
+
+
+# ----------------------------------------------------------------------------
+# tensor marshalling
+# ----------------------------------------------------------------------------
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _torch_dtype(cfg: MoeConfig):
+    import torch
+    return torch.bfloat16 if cfg.dtype == MOE_BF16 else torch.float32
+
+
+def alloc_workspace(cfg: MoeConfig, entry: int = MOE_ENTRY_LAYER_FORWARD, device="cuda"):
+    import torch
+    n = workspace_size(cfg, entry)
+    if n == 0 and validate_config(cfg) != MOE_OK:
+        _check(validate_config(cfg), "workspace_size")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def route(cfg, x, w_router, b_router=None, ids=None, gates=None, logits=None, stream=None):
+    import torch
+    dev = x.device
+    if ids is None:
+        ids = torch.empty((cfg.T, cfg.top_k), dtype=torch.int32, device=dev)
+    if gates is None:
+        gates = torch.empty((cfg.T, cfg.top_k), dtype=torch.float32, device=dev)
+    _check(lib().moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(b_router),
+                           _ptr(ids), _ptr(gates), _ptr(logits), _stream(stream)), "moe_route")
+    return ids, gates
+
+
+def dispatch(cfg, ids, ws=None, stream=None):
+    import torch
+    dev = ids.device
+    P = cfg.T * cfg.top_k
+    counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(cfg.E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(P, 1), dtype=torch.int32, device=dev)
+    inv = torch.empty(max(P, 1), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = alloc_workspace(cfg, MOE_ENTRY_DISPATCH, dev)
+    _check(lib().moe_dispatch(ctypes.byref(cfg), _ptr(ids), _ptr(counts), _ptr(offsets),
+                              _ptr(perm), _ptr(inv), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_dispatch")
+    return counts, offsets, perm[:P], inv[:P]
+
+
+def gate_up(cfg, x, perm, offsets, w_gate, w_up, act=None, ws=None, stream=None):
+    import torch
+    if act is None:
+        act = torch.empty((cfg.T * cfg.top_k, cfg.h), dtype=_torch_dtype(cfg), device=x.device)
+    if ws is None:
+        ws = alloc_workspace(cfg, MOE_ENTRY_GATE_UP, x.device)
+    _check(lib().moe_gate_up(ctypes.byref(cfg), _ptr(x), _ptr(perm), _ptr(offsets),
+                             _ptr(w_gate), _ptr(w_up), _ptr(act), _ptr(ws), ws.numel(),
+                             _stream(stream)), "moe_gate_up")
+    return act
+
+
+def down(cfg, act, offsets, w_down, y=None, ws=None, stream=None):
+    import torch
+    if y is None:
+        y = torch.empty((cfg.T * cfg.top_k, cfg.d), dtype=_torch_dtype(cfg), device=act.device)
+    if ws is None:
+        ws = alloc_workspace(cfg, MOE_ENTRY_DOWN, act.device)
+    _check(lib().moe_down(ctypes.byref(cfg), _ptr(act), _ptr(offsets), _ptr(w_down), _ptr(y),
+                          _ptr(ws), ws.numel(), _stream(stream)), "moe_down")
+    return y
+
+
+def expert_ffn(cfg, x, perm, offsets, w_gate, w_up, w_down, y=None, ws=None, stream=None):
+    import torch
+    if y is None:
+        y = torch.empty((cfg.T * cfg.top_k, cfg.d), dtype=_torch_dtype(cfg), device=x.device)
+    if ws is None:
+        ws = alloc_workspace(cfg, MOE_ENTRY_EXPERT_FFN, x.device)
+    _check(lib().moe_expert_ffn(ctypes.byref(cfg), _ptr(x), _ptr(perm), _ptr(offsets),
+                                _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y), _ptr(ws),
+                                ws.numel(), _stream(stream)), "moe_expert_ffn")
+    return y
+
+
+def shared_expert(cfg, x, ws_gate, ws_up, ws_down, w_shared_gate=None, out=None, ws=None,
+                  stream=None):
+    import torch
+    if out is None:
+        out = torch.empty((cfg.T, cfg.d), dtype=_torch_dtype(cfg), device=x.device)
+    if ws is None:
+        ws = alloc_workspace(cfg, MOE_ENTRY_SHARED_EXPERT, x.device)
+    _check(lib().moe_shared_expert(ctypes.byref(cfg), _ptr(x), _ptr(ws_gate), _ptr(ws_up),
+                                   _ptr(ws_down), _ptr(w_shared_gate), _ptr(out), _ptr(ws),
+                                   ws.numel(), _stream(stream)), "moe_shared_expert")
+    return out
+
+
+def combine(cfg, y, inv, gates, shared=None, out=None, stream=None):
+    import torch
+    if out is None:
+        out = torch.empty((cfg.T, cfg.d), dtype=_torch_dtype(cfg), device=y.device)
+    _check(lib().moe_combine(ctypes.byref(cfg), _ptr(y), _ptr(inv), _ptr(gates), _ptr(shared),
+                             _ptr(out), _stream(stream)), "moe_combine")
+    return out
+
+
+def weights_struct(w: dict) -> MoeWeights:
+    """w: dict of device tensors keyed like moe_weights' fields."""
+    return MoeWeights(*[_ptr(w.get(n)) for n, _ in MoeWeights._fields_])
+
+
+def layer_forward(cfg, weights, x, out=None, ids=None, gates=None, counts=None, ws=None,
+                  stage_events=None, stream=None):
+    """The whole layer. ``weights`` is a MoeWeights or a dict of tensors.
+    ``stage_events``: a ctypes array of MOE_NUM_STAGES + 1 hipEvent_t, or None."""
+    import torch
+    if out is None:
+        out = torch.empty((cfg.T, cfg.d), dtype=_torch_dtype(cfg), device=x.device)
+    if ws is None:
+        ws = alloc_workspace(cfg, MOE_ENTRY_LAYER_FORWARD, x.device)
+    wst = weights if isinstance(weights, MoeWeights) else weights_struct(weights)
+    args = (ctypes.byref(cfg), ctypes.byref(wst), _ptr(x), _ptr(out), _ptr(ids), _ptr(gates),
+            _ptr(counts), _ptr(ws), ws.numel())
+    if stage_events is None:
+        st = lib().moe_layer_forward(*args, _stream(stream))
+    else:
+        st = lib().moe_layer_forward_traced(*args, ctypes.cast(stage_events, ctypes.c_void_p),
+                                            _stream(stream))
+    _check(st, "moe_layer_forward")
+    return out

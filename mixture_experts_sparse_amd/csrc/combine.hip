@@ -1,0 +1,90 @@
+// Gate-weighted combine back to token order (gfx950):
+//   out[t] = sum_{j<k} gates[t, j] * y[inv[t*k + j]] (+ shared[t])
+// ("Tutorial 11: Mixture of Experts (MoE)", section 3, step 3, and section 4,
+// step 5). An additive gather in fixed slot order with fp32 accumulation,
+// rounded once to the activation dtype; each thread owns 16 contiguous bytes
+// of one output row, so every y row read is a coalesced 16-byte-per-lane
+// stream.
+
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void combine_bf16_kernel(CombineParams p) {
+  const int cpr = p.d >> 3;  // 8-element chunks per row
+  const long long item = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (item >= static_cast<long long>(p.T) * cpr) return;
+  const int t = static_cast<int>(item / cpr);
+  const int c = static_cast<int>(item - static_cast<long long>(t) * cpr) * 8;
+  const uint16_t* y = static_cast<const uint16_t*>(p.y);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int j = 0; j < p.k; ++j) {
+    const size_t q = static_cast<size_t>(t) * p.k + j;
+    const int r = min(max(p.inv[q], 0), p.y_rows - 1);
+    const float g = p.gates[q];
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(y + static_cast<size_t>(r) * p.d + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(g, __uint_as_float(v[i] << 16), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(g, __uint_as_float(v[i] & 0xFFFF0000u), acc[2 * i + 1]);
+    }
+  }
+  if (p.shared != nullptr) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.shared) +
+                                                         static_cast<size_t>(t) * p.d + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += __uint_as_float(v[i] << 16);
+      acc[2 * i + 1] += __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+  }
+  u32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i])) |
+           (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
+  }
+  *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.out) + static_cast<size_t>(t) * p.d + c) = o;
+}
+
+__global__ __launch_bounds__(256) void combine_f32_kernel(CombineParams p) {
+  const int cpr = p.d >> 2;  // 4-element chunks per row
+  const long long item = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (item >= static_cast<long long>(p.T) * cpr) return;
+  const int t = static_cast<int>(item / cpr);
+  const int c = static_cast<int>(item - static_cast<long long>(t) * cpr) * 4;
+  const float* y = static_cast<const float*>(p.y);
+  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < p.k; ++j) {
+    const size_t q = static_cast<size_t>(t) * p.k + j;
+    const int r = min(max(p.inv[q], 0), p.y_rows - 1);
+    const float g = p.gates[q];
+    const floatx4_t v = *reinterpret_cast<const floatx4_t*>(y + static_cast<size_t>(r) * p.d + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+  }
+  if (p.shared != nullptr) {
+    const floatx4_t v = *reinterpret_cast<const floatx4_t*>(static_cast<const float*>(p.shared) +
+                                                            static_cast<size_t>(t) * p.d + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += v[i];
+  }
+  *reinterpret_cast<floatx4_t*>(static_cast<float*>(p.out) + static_cast<size_t>(t) * p.d + c) = acc;
+}
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
+  const int per = p.dtype == MOE_BF16 ? 8 : 4;
+  const long long items = static_cast<long long>(p.T) * (p.d / per);
+  const long long nblk = (items + 255) / 256;
+  if (nblk <= 0) return hipSuccess;
+  if (p.dtype == MOE_BF16) combine_bf16_kernel<<<static_cast<unsigned>(nblk), 256, 0, s>>>(p);
+  else combine_f32_kernel<<<static_cast<unsigned>(nblk), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

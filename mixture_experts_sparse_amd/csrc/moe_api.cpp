@@ -1,0 +1,449 @@
+// Host side of libmoe.so: argument validation, workspace planning and the
+// launch sequence of every entry point declared in include/moe.h.
+//
+// Every check below is plain host arithmetic that runs before the first HIP
+// call, so a rejected call enqueues nothing and the checks run on machines
+// without a GPU.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+size_t elem_bytes(const moe_config& c) { return c.dtype == MOE_BF16 ? 2 : 4; }
+
+moe_status check_cfg(const moe_config* c) {
+  if (c == nullptr) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->d <= 0 || c->E <= 0 || c->h <= 0) return MOE_ERR_INVALID_ARG;
+  if (c->top_k < 1 || c->top_k > c->E) return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->mode != MOE_SOFTMAX_ALL && c->mode != MOE_SOFTMAX_SELECTED) return MOE_ERR_INVALID_ARG;
+  if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (c->has_router_bias != 0 && c->has_router_bias != 1) return MOE_ERR_INVALID_ARG;
+  if (c->shared_gate != 0 && c->shared_gate != 1) return MOE_ERR_INVALID_ARG;
+  if (c->shared_h < 0) return MOE_ERR_INVALID_ARG;
+  if (c->shared_gate && c->shared_h == 0) return MOE_ERR_INVALID_ARG;
+  if (c->E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  if (c->d % 8 != 0 || c->h % 8 != 0 || c->shared_h % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  // int32 row/element indices inside the kernels
+  const long long P = static_cast<long long>(c->T) * c->top_k;
+  const long long big = 1LL << 31;
+  if (P * c->d >= big || P * c->h >= big || static_cast<long long>(c->T) * c->d >= big ||
+      static_cast<long long>(c->T) * (c->shared_h > 0 ? c->shared_h : 1) >= big)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Required tensor pointer: non-null and 16-byte aligned.
+moe_status need(const void* p) {
+  if (p == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Optional tensor pointer: null, or 16-byte aligned.
+moe_status maybe(const void* p) {
+  if (p != nullptr && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)                   \
+  do {                                  \
+    const moe_status st_ = (expr);      \
+    if (st_ != MOE_OK) return st_;      \
+  } while (0)
+
+#define MOE_HIP(expr)                         \
+  do {                                        \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+moe_status check_ws(const moe_config& c, int entry, const void* ws, size_t ws_bytes) {
+  const size_t need_bytes = moe_workspace_size_entry(&c, entry);
+  if (ws_bytes < need_bytes) return MOE_ERR_WORKSPACE;
+  if (need_bytes > 0 && (ws == nullptr || !aligned256(ws))) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<unsigned char*>(ws) + off);
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+WsLayout ws_layout(const moe_config& c) {
+  const size_t T = static_cast<size_t>(c.T), E = static_cast<size_t>(c.E);
+  const size_t P = T * static_cast<size_t>(c.top_k);
+  const size_t NB = static_cast<size_t>(ceil_div(c.T, kRouteTokens));
+  const size_t MT = static_cast<size_t>(max_m_tiles(static_cast<int>(P), c.E));
+  const size_t eb = elem_bytes(c);
+  const size_t hs = static_cast<size_t>(c.shared_h);
+  WsLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at_ = o;
+    o += align256(bytes);
+    return at_;
+  };
+  L.blk_hist = take(NB * E * 4);
+  L.lrank = take(P * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.perm = take(P * 4);
+  L.inv = take(P * 4);
+  L.tile_e = take(MT * 4);
+  L.exp_tile0 = take((E + 1) * 4);
+  L.meta = take(16);
+  L.ids = take(P * 4);
+  L.gates = take(P * 4);
+  L.sgate = take(T * 4);
+  L.end_tables = o;
+  L.act = take(P * static_cast<size_t>(c.h) * eb);
+  L.act_s = take(T * hs * eb);
+  L.end_act = o;
+  L.y = take(P * static_cast<size_t>(c.d) * eb);
+  L.ys = take(hs > 0 ? T * static_cast<size_t>(c.d) * eb : 0);
+  L.end = o;
+  return L;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: a required pointer is NULL or a size/option is out of range";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape, alignment or expert count outside what the kernels support";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, too small or not 256-byte aligned";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+moe_status moe_validate_config(const moe_config* cfg) { return check_cfg(cfg); }
+
+size_t moe_workspace_size_entry(const moe_config* cfg, int32_t entry) {
+  if (check_cfg(cfg) != MOE_OK) return 0;
+  const WsLayout L = ws_layout(*cfg);
+  switch (entry) {
+    case MOE_ENTRY_LAYER_FORWARD: return L.end;
+    case MOE_ENTRY_DISPATCH:
+    case MOE_ENTRY_GATE_UP:
+    case MOE_ENTRY_DOWN: return L.end_tables;
+    case MOE_ENTRY_EXPERT_FFN: return L.act_s;
+    case MOE_ENTRY_SHARED_EXPERT: return L.end_act;
+    default: return 0;
+  }
+}
+
+size_t moe_workspace_size(const moe_config* cfg) {
+  return moe_workspace_size_entry(cfg, MOE_ENTRY_LAYER_FORWARD);
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
+                     const float* b_router, int32_t* ids, float* gates, float* logits,
+                     void* stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  MOE_TRY(need(x));
+  MOE_TRY(need(w_router));
+  MOE_TRY(need(ids));
+  MOE_TRY(need(gates));
+  MOE_TRY(maybe(logits));
+  if (c.has_router_bias) MOE_TRY(need(b_router));
+  RouteParams p{};
+  p.x = x;
+  p.w_router = w_router;
+  p.bias = c.has_router_bias ? b_router : nullptr;
+  p.T = c.T; p.d = c.d; p.E = c.E; p.k = c.top_k; p.mode = c.mode; p.renorm = c.renormalize;
+  p.ids = ids;
+  p.gates = gates;
+  p.logits = logits;
+  MOE_HIP(launch_route(p, c.dtype, as_stream(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* ids, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
+                        size_t ws_bytes, void* stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  MOE_TRY(need(ids));
+  MOE_TRY(need(counts));
+  MOE_TRY(need(offsets));
+  MOE_TRY(need(perm));
+  MOE_TRY(need(inv));
+  MOE_TRY(check_ws(c, MOE_ENTRY_DISPATCH, ws, ws_bytes));
+  const WsLayout L = ws_layout(c);
+  hipStream_t s = as_stream(stream);
+  RankParams rp{ids, c.T, c.E, c.top_k, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank)};
+  MOE_HIP(launch_rank(rp, s));
+  ScanParams sp{at<int32_t>(ws, L.blk_hist), ceil_div(c.T, kRouteTokens), c.E, c.T * c.top_k,
+                max_m_tiles(c.T * c.top_k, c.E), counts, offsets, at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0),
+                at<int32_t>(ws, L.meta)};
+  MOE_HIP(launch_scan(sp, s));
+  ScatterParams xp{ids, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank), c.T, c.E,
+                   c.top_k, perm, inv};
+  MOE_HIP(launch_scatter(xp, s));
+  return MOE_OK;
+}
+
+namespace {
+
+GemmParams gemm_base(const moe_config& c, void* ws, const int32_t* offsets, int kind) {
+  const WsLayout L = ws_layout(c);
+  GemmParams g{};
+  g.kind = kind;
+  g.dtype = c.dtype;
+  g.k = c.top_k;
+  g.offsets = offsets;
+  g.tile_e = at<int32_t>(ws, L.tile_e);
+  g.exp_tile0 = at<int32_t>(ws, L.exp_tile0);
+  g.meta = at<int32_t>(ws, L.meta);
+  g.E = c.E;
+  g.P = c.T * c.top_k;
+  g.max_mtiles = max_m_tiles(g.P, c.E);
+  g.a_rows = c.T;
+  return g;
+}
+
+moe_status run_tiles(const moe_config& c, void* ws, const int32_t* offsets, hipStream_t s) {
+  const WsLayout L = ws_layout(c);
+  TilesParams tp{offsets, c.E, c.T * c.top_k, max_m_tiles(c.T * c.top_k, c.E), at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0),
+                 at<int32_t>(ws, L.meta)};
+  MOE_HIP(launch_tiles(tp, s));
+  return MOE_OK;
+}
+
+moe_status run_gate_up(const moe_config& c, void* ws, const void* x, const int32_t* perm,
+                       const int32_t* offsets, const void* wg, const void* wu, void* act,
+                       hipStream_t s) {
+  GemmParams g = gemm_base(c, ws, offsets, 0);
+  g.a = x; g.perm = perm; g.K = c.d;
+  g.b0 = wg; g.b1 = wu; g.N = c.h; g.out = act;
+  MOE_HIP(launch_gemm(g, s));
+  return MOE_OK;
+}
+
+moe_status run_down(const moe_config& c, void* ws, const void* act, const int32_t* offsets,
+                    const void* wd, void* y, hipStream_t s) {
+  GemmParams g = gemm_base(c, ws, offsets, 1);
+  g.a = act; g.K = c.h;
+  g.b0 = wd; g.N = c.d; g.out = y;
+  MOE_HIP(launch_gemm(g, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status moe_gate_up(const moe_config* cfg, const void* x, const int32_t* perm,
+                       const int32_t* offsets, const void* w_gate, const void* w_up,
+                       void* act, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  MOE_TRY(need(x)); MOE_TRY(need(perm)); MOE_TRY(need(offsets));
+  MOE_TRY(need(w_gate)); MOE_TRY(need(w_up)); MOE_TRY(need(act));
+  MOE_TRY(check_ws(c, MOE_ENTRY_GATE_UP, ws, ws_bytes));
+  hipStream_t s = as_stream(stream);
+  MOE_TRY(run_tiles(c, ws, offsets, s));
+  return run_gate_up(c, ws, x, perm, offsets, w_gate, w_up, act, s);
+}
+
+moe_status moe_down(const moe_config* cfg, const void* act, const int32_t* offsets,
+                    const void* w_down, void* y, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  MOE_TRY(need(act)); MOE_TRY(need(offsets)); MOE_TRY(need(w_down)); MOE_TRY(need(y));
+  MOE_TRY(check_ws(c, MOE_ENTRY_DOWN, ws, ws_bytes));
+  hipStream_t s = as_stream(stream);
+  MOE_TRY(run_tiles(c, ws, offsets, s));
+  return run_down(c, ws, act, offsets, w_down, y, s);
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* perm,
+                          const int32_t* offsets, const void* w_gate, const void* w_up,
+                          const void* w_down, void* y, void* ws, size_t ws_bytes,
+                          void* stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  MOE_TRY(need(x)); MOE_TRY(need(perm)); MOE_TRY(need(offsets));
+  MOE_TRY(need(w_gate)); MOE_TRY(need(w_up)); MOE_TRY(need(w_down)); MOE_TRY(need(y));
+  MOE_TRY(check_ws(c, MOE_ENTRY_EXPERT_FFN, ws, ws_bytes));
+  const WsLayout L = ws_layout(c);
+  hipStream_t s = as_stream(stream);
+  MOE_TRY(run_tiles(c, ws, offsets, s));
+  void* act = at<void>(ws, L.act);
+  MOE_TRY(run_gate_up(c, ws, x, perm, offsets, w_gate, w_up, act, s));
+  return run_down(c, ws, act, offsets, w_down, y, s);
+}
+
+moe_status moe_shared_expert(const moe_config* cfg, const void* x, const void* ws_gate,
+                             const void* ws_up, const void* ws_down,
+                             const void* w_shared_gate, void* s_out, void* ws,
+                             size_t ws_bytes, void* stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (c.shared_h <= 0) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(need(x)); MOE_TRY(need(ws_gate)); MOE_TRY(need(ws_up)); MOE_TRY(need(ws_down));
+  MOE_TRY(maybe(w_shared_gate)); MOE_TRY(need(s_out));
+  MOE_TRY(check_ws(c, MOE_ENTRY_SHARED_EXPERT, ws, ws_bytes));
+  const WsLayout L = ws_layout(c);
+  hipStream_t s = as_stream(stream);
+  float* sg = nullptr;
+  if (w_shared_gate != nullptr) {
+    sg = at<float>(ws, L.sgate);
+    RowDotSigmoidParams rp{x, w_shared_gate, c.T, c.d, c.dtype, sg};
+    MOE_HIP(launch_rowdot_sigmoid(rp, s));
+  }
+  void* act_s = at<void>(ws, L.act_s);
+  GemmParams g{};
+  g.kind = 0; g.dtype = c.dtype; g.k = c.top_k; g.E = c.E;
+  g.P = 0; g.max_mtiles = 0; g.a_rows = c.T;  // no routed rows: the launch is the shared group only
+  g.shared_T = c.T; g.sa = x; g.sK = c.d; g.sb0 = ws_gate; g.sb1 = ws_up; g.sN = c.shared_h;
+  g.sout = act_s;
+  MOE_HIP(launch_gemm(g, s));
+  GemmParams g2 = g;
+  g2.kind = 1; g2.sa = act_s; g2.sK = c.shared_h; g2.sb0 = ws_down; g2.sb1 = nullptr;
+  g2.sN = c.d; g2.sout = s_out; g2.srow_scale = sg;
+  MOE_HIP(launch_gemm(g2, s));
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* y, const int32_t* inv,
+                       const float* gates, const void* shared, void* out, void* stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  MOE_TRY(need(y)); MOE_TRY(need(inv)); MOE_TRY(need(gates)); MOE_TRY(maybe(shared));
+  MOE_TRY(need(out));
+  CombineParams p{y, inv, gates, shared, out, c.T, c.d, c.top_k, c.dtype, c.T * c.top_k};
+  MOE_HIP(launch_combine(p, as_stream(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
+                                    const void* x, void* out, int32_t* ids, float* gates,
+                                    int32_t* counts, void* ws, size_t ws_bytes,
+                                    void* const* stage_events, void* stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  if (w == nullptr) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(need(x)); MOE_TRY(need(out));
+  MOE_TRY(need(w->w_router)); MOE_TRY(need(w->w_gate)); MOE_TRY(need(w->w_up));
+  MOE_TRY(need(w->w_down));
+  if (c.has_router_bias) MOE_TRY(need(w->b_router));
+  if (c.shared_h > 0) {
+    MOE_TRY(need(w->ws_gate)); MOE_TRY(need(w->ws_up)); MOE_TRY(need(w->ws_down));
+    if (c.shared_gate) MOE_TRY(need(w->w_shared_gate));
+  }
+  MOE_TRY(maybe(ids)); MOE_TRY(maybe(gates)); MOE_TRY(maybe(counts));
+  MOE_TRY(check_ws(c, MOE_ENTRY_LAYER_FORWARD, ws, ws_bytes));
+  if (c.T == 0) return MOE_OK;
+
+  const WsLayout L = ws_layout(c);
+  hipStream_t s = as_stream(stream);
+  auto mark = [&](int i) -> hipError_t {
+    if (stage_events == nullptr) return hipSuccess;
+    return hipEventRecord(reinterpret_cast<hipEvent_t>(stage_events[i]), s);
+  };
+  const int NB = ceil_div(c.T, kRouteTokens);
+  int32_t* ids_p = ids != nullptr ? ids : at<int32_t>(ws, L.ids);
+  float* gates_p = gates != nullptr ? gates : at<float>(ws, L.gates);
+  int32_t* counts_p = counts != nullptr ? counts : at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm = at<int32_t>(ws, L.perm);
+  int32_t* inv = at<int32_t>(ws, L.inv);
+  const bool gated = c.shared_h > 0 && c.shared_gate;
+  float* sg = gated ? at<float>(ws, L.sgate) : nullptr;
+
+  MOE_HIP(mark(0));
+  RouteParams rp{};
+  rp.x = x;
+  rp.w_router = w->w_router;
+  rp.bias = c.has_router_bias ? w->b_router : nullptr;
+  rp.w_sgate = gated ? w->w_shared_gate : nullptr;
+  rp.T = c.T; rp.d = c.d; rp.E = c.E; rp.k = c.top_k; rp.mode = c.mode; rp.renorm = c.renormalize;
+  rp.ids = ids_p;
+  rp.gates = gates_p;
+  rp.logits = nullptr;
+  rp.sgate = sg;
+  rp.blk_hist = at<int32_t>(ws, L.blk_hist);
+  rp.lrank = at<int32_t>(ws, L.lrank);
+  if (NB == 1) {
+    rp.counts = counts_p; rp.offsets = offsets; rp.perm = perm; rp.inv = inv;
+    rp.tile_e = at<int32_t>(ws, L.tile_e); rp.exp_tile0 = at<int32_t>(ws, L.exp_tile0);
+    rp.meta = at<int32_t>(ws, L.meta);
+    rp.max_tiles = max_m_tiles(c.T * c.top_k, c.E);
+  }
+  MOE_HIP(launch_route(rp, c.dtype, s));
+  MOE_HIP(mark(1));
+  if (NB > 1) {
+    ScanParams sp{at<int32_t>(ws, L.blk_hist), NB, c.E, c.T * c.top_k,
+                  max_m_tiles(c.T * c.top_k, c.E), counts_p, offsets,
+                  at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0), at<int32_t>(ws, L.meta)};
+    MOE_HIP(launch_scan(sp, s));
+    ScatterParams xp{ids_p, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank), c.T, c.E,
+                     c.top_k, perm, inv};
+    MOE_HIP(launch_scatter(xp, s));
+  }
+  MOE_HIP(mark(2));
+
+  void* act = at<void>(ws, L.act);
+  void* act_s = at<void>(ws, L.act_s);
+  void* y = at<void>(ws, L.y);
+  void* ys = at<void>(ws, L.ys);
+  GemmParams g = gemm_base(c, ws, offsets, 0);
+  g.a = x; g.perm = perm; g.K = c.d; g.b0 = w->w_gate; g.b1 = w->w_up; g.N = c.h; g.out = act;
+  if (c.shared_h > 0) {
+    g.shared_T = c.T; g.sa = x; g.sK = c.d; g.sb0 = w->ws_gate; g.sb1 = w->ws_up;
+    g.sN = c.shared_h; g.sout = act_s;
+  }
+  MOE_HIP(launch_gemm(g, s));
+  MOE_HIP(mark(3));
+  GemmParams g2 = gemm_base(c, ws, offsets, 1);
+  g2.a = act; g2.K = c.h; g2.b0 = w->w_down; g2.N = c.d; g2.out = y;
+  if (c.shared_h > 0) {
+    g2.shared_T = c.T; g2.sa = act_s; g2.sK = c.shared_h; g2.sb0 = w->ws_down;
+    g2.sN = c.d; g2.sout = ys; g2.srow_scale = sg;
+  }
+  MOE_HIP(launch_gemm(g2, s));
+  MOE_HIP(mark(4));
+  CombineParams cp{y, inv, gates_p, c.shared_h > 0 ? ys : nullptr, out, c.T, c.d, c.top_k,
+                    c.dtype, c.T * c.top_k};
+  MOE_HIP(launch_combine(cp, s));
+  MOE_HIP(mark(5));
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x,
+                             void* out, int32_t* ids, float* gates, int32_t* counts, void* ws,
+                             size_t ws_bytes, void* stream) {
+  return moe_layer_forward_traced(cfg, w, x, out, ids, gates, counts, ws, ws_bytes, nullptr,
+                                  stream);
+}
+
+}  // extern "C"

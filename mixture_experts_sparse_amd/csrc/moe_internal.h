@@ -1,0 +1,163 @@
+// Internal interfaces between the host API (moe_api.cpp) and the HIP kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// Route block: tokens per workgroup of the router / top-k kernel. The
+// dispatch histogram is kept per route block.
+constexpr int kRouteTokens = 64;
+// Grouped-GEMM M tile (rows of one expert per workgroup).
+constexpr int kTileM = 128;
+// Gate/up N tile (hidden units per workgroup; gate and up both) and down N
+// tile (model-width columns per workgroup).
+constexpr int kTileNGateUp = 64;
+constexpr int kTileNDown = 128;
+
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Upper bound on the number of M tiles over all experts:
+// sum_e ceil(c_e / BM) <= floor(P / BM) + min(E, P).
+inline int max_m_tiles(int P, int E) { return P / kTileM + (E < P ? E : P) + 1; }
+
+// Workspace carve-up. Offsets are in bytes from the start of ws.
+struct WsLayout {
+  size_t blk_hist, lrank, counts, offsets, perm, inv, tile_e, exp_tile0, meta;
+  size_t ids, gates, sgate;
+  size_t end_tables;
+  size_t act, act_s, end_act;
+  size_t y, ys, end;
+};
+WsLayout ws_layout(const moe_config& c);
+
+// ---------------------------------------------------------------- kernels --
+
+struct RouteParams {
+  const void* x;          // [T, d]
+  const void* w_router;   // [E, d]
+  const float* bias;      // [E] or null
+  const void* w_sgate;    // [d] or null: sigmoid(w_s . x) -> sgate
+  int T, d, E, k, mode, renorm;
+  int32_t* ids;           // [T, k]
+  float* gates;           // [T, k]
+  float* logits;          // [T, E] or null
+  float* sgate;           // [T] or null
+  // dispatch partials (null: route only)
+  int32_t* blk_hist;      // [NB, E]
+  int32_t* lrank;         // [P]
+  // single-block finish (NB == 1): full dispatch inline
+  int32_t* counts;        // [E]
+  int32_t* offsets;       // [E+1]
+  int32_t* perm;          // [P]
+  int32_t* inv;           // [P]
+  int32_t* tile_e;        // [max tiles]
+  int32_t* exp_tile0;     // [E+1]
+  int32_t* meta;          // [4]
+  int max_tiles;
+};
+
+// Dispatch from given ids (moe_dispatch): histogram + local ranks.
+struct RankParams {
+  const int32_t* ids;
+  int T, E, k;
+  int32_t* blk_hist;
+  int32_t* lrank;
+};
+
+struct ScanParams {
+  int32_t* blk_hist;  // in: per-block counts; out: per-block base rows
+  int NB, E, P, max_tiles;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* tile_e;
+  int32_t* exp_tile0;
+  int32_t* meta;
+};
+
+struct ScatterParams {
+  const int32_t* ids;
+  const int32_t* blk_base;
+  const int32_t* lrank;
+  int T, E, k;
+  int32_t* perm;
+  int32_t* inv;
+};
+
+// Tile table from offsets alone (standalone gate_up / down / expert_ffn).
+struct TilesParams {
+  const int32_t* offsets;
+  int E, P, max_tiles;
+  int32_t* tile_e;
+  int32_t* exp_tile0;
+  int32_t* meta;
+};
+
+// One grouped GEMM launch. Kind 0: gate/up (+ SiLU product) -> act.
+// Kind 1: down -> y. Routed rows come from the tile table; an optional
+// dense "shared" group (identity rows 0..shared_T-1) rides in the same launch.
+struct GemmParams {
+  int kind;
+  int dtype;
+  // A operand
+  const void* a;          // gate/up: x [T, d]; down: act [P, h]
+  const int32_t* perm;    // gate/up routed rows: sorted row -> pair (token = pair / k)
+  int k;
+  int K;                  // reduction length (d for gate/up, h for down)
+  // B operand, routed experts
+  const void* b0;         // gate/up: w_gate [E, h, d]; down: w_down [E, d, h]
+  const void* b1;         // gate/up: w_up   [E, h, d]; down: unused
+  int N;                  // output columns: h (gate/up) or d (down)
+  void* out;              // act [P, h] or y [P, d]
+  // tile table
+  const int32_t* offsets;
+  const int32_t* tile_e;
+  const int32_t* exp_tile0;
+  const int32_t* meta;
+  int E, P;
+  int max_mtiles;
+  int a_rows;             // rows of the gathered A operand (T): token indices are clamped to it
+  // shared group
+  int shared_T;           // 0: none
+  const void* sa;         // gate/up: x; down: act_s [T, hs]
+  int sK;                 // d or hs
+  const void* sb0;        // ws_gate [hs, d] or ws_down [d, hs]
+  const void* sb1;        // ws_up or unused
+  int sN;                 // hs or d
+  void* sout;             // act_s [T, hs] or ys [T, d]
+  const float* srow_scale;  // down only: per-row scale of the shared output (sgate) or null
+};
+
+struct CombineParams {
+  const void* y;        // [P, d]
+  const int32_t* inv;   // [P]
+  const float* gates;   // [T, k]
+  const void* shared;   // [T, d] or null
+  void* out;            // [T, d]
+  int T, d, k, dtype;
+  int y_rows;           // rows of y (P): row indices are clamped to it
+};
+
+struct RowDotSigmoidParams {
+  const void* x;  // [T, d]
+  const void* w;  // [d]
+  int T, d, dtype;
+  float* out;     // [T]
+};
+
+hipError_t launch_route(const RouteParams& p, int dtype, hipStream_t s);
+hipError_t launch_rank(const RankParams& p, hipStream_t s);
+hipError_t launch_scan(const ScanParams& p, hipStream_t s);
+hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
+hipError_t launch_tiles(const TilesParams& p, hipStream_t s);
+hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+hipError_t launch_rowdot_sigmoid(const RowDotSigmoidParams& p, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,124 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+function include/moe.h declares, and rejects bad arguments on the host before
+any HIP call (only null or fake pointers are passed here, and every call is
+one that must fail validation, so nothing reaches the device)."""
+
+import ctypes
+
+import pytest
+
+import mixture_experts_sparse_amd.binding as B
+from mixture_experts_sparse_amd import build as build_mod
+
+
+def test_library_exports_every_header_function():
+    L = B.lib()
+    names = B.header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.moe_abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(5):
+        assert B.status_string(s).startswith("MOE_")
+    assert "UNKNOWN" in B.status_string(99)
+
+
+def _cfg(**kw):
+    base = dict(T=100, d=64, E=8, h=32, top_k=2)
+    base.update(kw)
+    return B.make_config(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), B.MOE_OK),
+    (dict(T=0), B.MOE_OK),
+    (dict(T=-1), B.MOE_ERR_INVALID_ARG),
+    (dict(d=0), B.MOE_ERR_INVALID_ARG),
+    (dict(E=0), B.MOE_ERR_INVALID_ARG),
+    (dict(h=-8), B.MOE_ERR_INVALID_ARG),
+    (dict(top_k=0), B.MOE_ERR_INVALID_ARG),
+    (dict(top_k=9), B.MOE_ERR_INVALID_ARG),     # k > E is rejected, not capped
+    (dict(top_k=8), B.MOE_OK),                  # k = E is legal
+    (dict(dtype=7), B.MOE_ERR_INVALID_ARG),
+    (dict(mode=3), B.MOE_ERR_INVALID_ARG),
+    (dict(shared_gate=True), B.MOE_ERR_INVALID_ARG),  # gate without a shared expert
+    (dict(d=60), B.MOE_ERR_UNSUPPORTED),
+    (dict(h=36), B.MOE_ERR_UNSUPPORTED),
+    (dict(shared_h=12), B.MOE_ERR_UNSUPPORTED),
+    (dict(E=257, top_k=2), B.MOE_ERR_UNSUPPORTED),
+    (dict(E=256, top_k=256), B.MOE_OK),
+])
+def test_config_validation(kw, status):
+    assert B.validate_config(_cfg(**kw)) == status
+
+
+def test_workspace_sizes_are_bounded():
+    # the skewed prefill shape: workspace is O(P*(d+h)), never O(T*h*d)
+    c = B.make_config(16384, 2048, 128, 768, 8)
+    ws = B.workspace_size(c)
+    P = 16384 * 8
+    assert ws >= P * (2048 + 768) * 2
+    assert ws < 1.1 * P * (2048 + 768) * 2 + 16 * 2**20
+    gathered = 16384 * 768 * 2048 * 2
+    assert ws < gathered / 10
+    for e in range(6):
+        assert B.workspace_size(c, e) <= ws
+    assert B.workspace_size(c, B.MOE_ENTRY_DISPATCH) < 8 * 2**20
+    assert B.workspace_size(B.make_config(1, 64, 8, 32, 9)) == 0  # invalid cfg
+
+
+FAKE = 0x1000  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def test_entry_points_reject_bad_args_without_gpu():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("fake-pointer validation checks run only where no GPU is present")
+    L = B.lib()
+    c = _cfg()
+    bad = _cfg(top_k=0)
+    cp, bp = ctypes.byref(c), ctypes.byref(bad)
+    # null required pointers
+    assert L.moe_route(cp, None, FAKE, None, FAKE, FAKE, None, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_route(cp, FAKE, FAKE, None, None, FAKE, None, None) == B.MOE_ERR_INVALID_ARG
+    # misaligned pointer
+    assert L.moe_route(cp, FAKE + 2, FAKE, None, FAKE, FAKE, None, None) == B.MOE_ERR_UNSUPPORTED
+    # bias required when has_router_bias
+    cb = _cfg(has_router_bias=True)
+    assert L.moe_route(ctypes.byref(cb), FAKE, FAKE, None, FAKE, FAKE, None, None) == B.MOE_ERR_INVALID_ARG
+    # bad config
+    assert L.moe_route(bp, FAKE, FAKE, None, FAKE, FAKE, None, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_route(None, FAKE, FAKE, None, FAKE, FAKE, None, None) == B.MOE_ERR_INVALID_ARG
+    # workspace too small / misaligned
+    need = B.workspace_size(c, B.MOE_ENTRY_DISPATCH)
+    assert L.moe_dispatch(cp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_dispatch(cp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, need, None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_dispatch(cp, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_gate_up(cp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_down(cp, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn(cp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, None) == B.MOE_ERR_WORKSPACE
+    # shared expert without shared_h
+    assert L.moe_shared_expert(cp, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(cp, FAKE, FAKE, None, None, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    # layer forward: null weights struct, missing shared weights, tiny workspace
+    assert L.moe_layer_forward(cp, None, FAKE, FAKE, None, None, None, FAKE, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    w = B.MoeWeights(FAKE, None, FAKE, FAKE, FAKE, None, None, None, None)
+    assert L.moe_layer_forward(cp, ctypes.byref(w), FAKE, FAKE, None, None, None, FAKE, 16, None) == B.MOE_ERR_WORKSPACE
+    cs = _cfg(shared_h=16, shared_gate=True)
+    assert L.moe_layer_forward(ctypes.byref(cs), ctypes.byref(w), FAKE, FAKE, None, None, None, FAKE,
+                               1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    w2 = B.MoeWeights(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert L.moe_layer_forward(ctypes.byref(cs), ctypes.byref(w2), FAKE, FAKE, None, None, None, FAKE,
+                               1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    # misaligned optional output
+    assert L.moe_layer_forward(cp, ctypes.byref(w), FAKE, FAKE, FAKE + 4, None, None, FAKE,
+                               1 << 40, None) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_build_script_lists_existing_sources():
+    import os
+    for s in build_mod.SOURCES:
+        assert os.path.exists(os.path.join(build_mod.CSRC, s)), s

@@ -1,0 +1,260 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small shapes run the whole-batch oracle and span several tiles with ragged
+tails (T not a multiple of the 64-token route block or the 128-row M tile,
+d not a multiple of the 64-deep K chunk, h not a multiple of the N tile).
+Full-size workloads check routing and counts for every token and outputs for
+a sample of rows. Every comparison follows the protocol in gpu_helpers.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_sparse_amd.binding as B
+import oracle.moe_oracle as O
+from gpu_helpers import (check_gates, check_out, check_routing, dev, device_inputs, full_parity,
+                         host, run_layer, sampled_parity, say)
+from moe_inputs import generate, small_spec, spec_by_name
+from moe_inputs.spec import BF16, F32, SOFTMAX_ALL, SOFTMAX_SELECTED, SPECS, MoESpec
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    B.lib()
+
+
+SMALL = {
+    "tiny_fp32": SPECS["tiny_fp32"],
+    "tiny_fp32_ragged": small_spec("tiny_fp32", T=203, d=72, E=8, h=40, k=2),
+    "gemma_small": small_spec("gemma_upcycled", T=300, d=200, E=16, h=136, k=4),
+    "decode_small": small_spec("decode", T=37, d=264, E=64, h=96, k=8),
+    "skewed_small": small_spec("skewed_prefill", T=700, d=256, E=32, h=200, k=8),
+    "shared_small": small_spec("shared_routed", T=520, d=264, E=12, h=96, k=4, shared_h=376),
+    "shared_fp32_small": small_spec("shared_routed", T=130, d=48, E=6, h=24, k=2, shared_h=40,
+                                    dtype=F32),
+    "e256_small": MoESpec(name="e256", T=150, d=64, E=256, h=32, k=6, mode=SOFTMAX_SELECTED),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_small(name):
+    spec = SMALL[name]
+    say(f"[gpu] layer_forward {name}: T={spec.T} d={spec.d} E={spec.E} h={spec.h} k={spec.k}")
+    inp = generate(spec)
+    full_parity(inp)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_entry_points_small(name):
+    """route -> dispatch -> gate_up -> down -> (shared) -> combine, each entry
+    point checked against the matching oracle step, then the chain against the
+    fused call (bitwise: same kernels, same order)."""
+    spec = SMALL[name]
+    say(f"[gpu] entry points {name}")
+    inp = generate(spec)
+    d = device_inputs(inp)
+    cfg = B.config_from_spec(spec)
+    T, k, E = spec.T, spec.k, spec.E
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ids, gates = B.route(cfg, d["x"], d["w_router"], d["b_router"], logits=logits)
+    torch.cuda.synchronize()
+    L = O.router_logits(inp["x"], inp["w_router"], inp.get("b_router"))
+    lerr = float(np.max(np.abs(host(logits) - L)))
+    say(f"    logits max err {lerr:.2e}")
+    assert lerr <= (1e-5 if spec.dtype == F32 else 1e-4) * max(1.0, float(np.max(np.abs(L))))
+    gids = ids.cpu().numpy().astype(np.int64)
+    near, mism = check_routing(L, gids, k)
+    ref_ids = O.topk_select(L, k)
+    ref_ids[mism] = gids[mism]
+    ref_g, _ = O.gate_weights(L, ref_ids, spec.mode, spec.renormalize)
+    check_gates(gates.cpu().numpy().astype(np.float64), ref_g)
+
+    counts, offsets, perm, inv = B.dispatch(cfg, ids)
+    torch.cuda.synchronize()
+    rc, ro, rp, ri = O.dispatch(gids, E)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(perm.cpu().numpy(), rp)
+    assert np.array_equal(inv.cpu().numpy(), ri)
+
+    act = B.gate_up(cfg, d["x"], perm, offsets, d["w_gate"], d["w_up"])
+    y = B.down(cfg, act, offsets, d["w_down"])
+    y2 = B.expert_ffn(cfg, d["x"], perm, offsets, d["w_gate"], d["w_up"], d["w_down"])
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    ref_act = O.gate_up(inp["x"], rp, ro, k, inp["w_gate"], inp["w_up"])
+    check_out(host(act), ref_act, spec.dtype, "act")
+    ref_y = O.down(ref_act, ro, inp["w_down"])
+    check_out(host(y), ref_y, spec.dtype, "y")
+
+    shared = None
+    ref_s = None
+    if spec.shared_h:
+        shared = B.shared_expert(cfg, d["x"], d["ws_gate"], d["ws_up"], d["ws_down"],
+                                 d["w_shared_gate"])
+        torch.cuda.synchronize()
+        ref_s = O.shared_expert(inp["x"], inp["ws_gate"], inp["ws_up"], inp["ws_down"],
+                                inp.get("w_shared_gate"))
+        check_out(host(shared), ref_s, spec.dtype, "shared")
+    out = B.combine(cfg, y, inv, gates, shared)
+    torch.cuda.synchronize()
+    ref_out = O.combine(ref_y, ri, ref_g, ref_s)
+    check_out(host(out), ref_out, spec.dtype, "combine")
+
+    fused = run_layer(inp, d)
+    assert np.array_equal(fused["ids"], gids)
+    if spec.shared_h == 0:
+        # same kernels in the same order: bitwise equal
+        assert torch.equal(fused["out_t"], out)
+
+
+FULL = ["tiny_fp32", "gemma_upcycled", "skewed_prefill", "shared_routed",
+        "decode@T1", "decode@T4", "decode@T16", "decode@T64"]
+
+_cache = {}
+
+
+def _full_inputs(name):
+    """Full-size inputs; the decode batch sizes share one draw (x rows are a
+    prefix of the same 64 drawn tokens)."""
+    base = name.split("@")[0]
+    key = "decode@T64" if base == "decode" else name
+    if key not in _cache:
+        _cache.clear()
+        _cache[key] = generate(spec_by_name(key))
+    inp = _cache[key]
+    if key != name:
+        spec = spec_by_name(name)
+        inp = dict(inp, spec=spec, x=inp["x"][:spec.T])
+    return inp
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_layer_full_size(name):
+    spec = spec_by_name(name)
+    say(f"[gpu] full-size {name}: T={spec.T} d={spec.d} E={spec.E} h={spec.h} k={spec.k}")
+    inp = _full_inputs(name)
+    if spec.T <= 64:
+        full_parity(inp)
+        return
+    rng = np.random.default_rng(1234)
+    sample = list(rng.choice(spec.T, size=48, replace=False)) + [0, spec.T - 1, spec.T // 2]
+    g, _ = sampled_parity(inp, sample)
+    # the hottest expert's rows: sample tokens routed to it
+    hot = int(np.argmax(g["counts"]))
+    rows = np.nonzero(np.any(g["ids"] == hot, axis=1))[0]
+    if rows.size:
+        pick = rows[np.linspace(0, rows.size - 1, 8).astype(int)]
+        sampled_parity(inp, pick)
+
+
+def test_determinism():
+    spec = small_spec("skewed_prefill", T=333, d=128, E=32, h=64, k=8)
+    say("[gpu] determinism")
+    inp = generate(spec)
+    d = device_inputs(inp)
+    a = run_layer(inp, d)
+    b = run_layer(inp, d)
+    assert np.array_equal(a["ids"], b["ids"])
+    assert np.array_equal(a["counts"], b["counts"])
+    assert torch.equal(a["out_t"], b["out_t"])
+
+
+EDGE = {
+    "T1_bf16": small_spec("decode", T=1, d=128, E=16, h=64, k=4),
+    "T1_fp32": small_spec("tiny_fp32", T=1),
+    "T65": small_spec("skewed_prefill", T=65, d=128, E=16, h=64, k=3),
+    "T129": small_spec("gemma_upcycled", T=129, d=64, E=8, h=64, k=2),
+    "k1": small_spec("skewed_prefill", T=200, d=128, E=16, h=64, k=1),
+    "k_eq_E": small_spec("decode", T=90, d=64, E=8, h=32, k=8),
+    "k_eq_E_renorm": small_spec("skewed_prefill", T=70, d=64, E=6, h=32, k=6),
+    "E1": small_spec("decode", T=50, d=64, E=1, h=32, k=1),
+    "d8": small_spec("decode", T=70, d=8, E=4, h=8, k=2),
+    "big_k": MoESpec(name="big_k", T=40, d=64, E=200, h=16, k=130),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_cases(name):
+    spec = EDGE[name]
+    say(f"[gpu] edge {name}: T={spec.T} d={spec.d} E={spec.E} h={spec.h} k={spec.k}")
+    full_parity(generate(spec))
+
+
+def test_all_tokens_one_expert_and_empty_experts():
+    """Router weights zero plus a bias that favours expert 5: every token
+    picks 5 first (then the next-largest biases), most experts stay empty,
+    and one expert's group spans many M tiles."""
+    spec = small_spec("skewed_prefill", T=600, d=128, E=16, h=64, k=2)
+    inp = generate(spec)
+    inp["w_router"] = np.zeros_like(inp["w_router"])
+    b = np.full(spec.E, -5.0, dtype=np.float32)
+    b[5], b[9] = 3.0, 2.0
+    inp["b_router"] = b
+    say("[gpu] all tokens on experts 5 and 9")
+    g, ref, _ = full_parity(inp)
+    assert g["counts"][5] == 600 and g["counts"][9] == 600 and g["counts"].sum() == 1200
+
+
+def test_tie_break_lower_index():
+    """All-zero router: every logit ties, so the ids are 0..k-1 in order and
+    softmax-all gates are 1/E (a pin of the selection rule, with exact ties)."""
+    spec = small_spec("decode", T=77, d=64, E=12, h=32, k=3)
+    inp = generate(spec)
+    inp["w_router"] = np.zeros_like(inp["w_router"])
+    g = run_layer(inp)
+    assert np.all(g["ids"] == np.arange(3)[None, :])
+    assert np.allclose(g["gates"], 1.0 / 12, rtol=0, atol=1e-7)
+
+
+def test_hidden_slice_identity():
+    """Four experts holding the four hidden slices of one dense SwiGLU, zero
+    router, k=4, softmax-all: out = FFN_dense(x) / 4."""
+    T, d, h = 150, 128, 64
+    rng = np.random.default_rng(5)
+    from moe_inputs import bf16_bits_from_f32
+    G = bf16_bits_from_f32(rng.standard_normal((4 * h, d)).astype(np.float32) * 0.05)
+    U = bf16_bits_from_f32(rng.standard_normal((4 * h, d)).astype(np.float32) * 0.05)
+    D = bf16_bits_from_f32(rng.standard_normal((d, 4 * h)).astype(np.float32) * 0.05)
+    X = bf16_bits_from_f32(rng.standard_normal((T, d)).astype(np.float32))
+    spec = MoESpec(name="slices", T=T, d=d, E=4, h=h, k=4, dtype=BF16, mode=SOFTMAX_ALL)
+    inp = {"spec": spec, "x": X, "w_router": np.zeros((4, d), np.uint16), "b_router": None,
+           "w_gate": np.ascontiguousarray(np.stack([G[s * h:(s + 1) * h] for s in range(4)])),
+           "w_up": np.ascontiguousarray(np.stack([U[s * h:(s + 1) * h] for s in range(4)])),
+           "w_down": np.ascontiguousarray(np.stack([D[:, s * h:(s + 1) * h] for s in range(4)])),
+           "ws_gate": None, "ws_up": None, "ws_down": None, "w_shared_gate": None}
+    g = run_layer(inp)
+    dense = O.swiglu(O.to_f64(X), O.to_f64(G), O.to_f64(U), O.to_f64(D)) / 4
+    check_out(g["out"], dense, BF16, "slices vs dense/4")
+
+
+def test_zero_tokens_is_noop():
+    spec = small_spec("decode", T=0, d=64, E=8, h=32, k=2)
+    cfg = B.config_from_spec(spec)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    wg = torch.zeros((8, 32, 64), dtype=torch.bfloat16, device="cuda")
+    wd = torch.zeros((8, 64, 32), dtype=torch.bfloat16, device="cuda")
+    B.layer_forward(cfg, {"w_router": w, "w_gate": wg, "w_up": wg, "w_down": wd}, x, out=out,
+                    ws=ws)
+    torch.cuda.synchronize()
+
+
+def test_workspace_too_small_is_rejected_on_gpu():
+    spec = small_spec("decode", T=10, d=64, E=8, h=32, k=2)
+    inp = generate(spec)
+    d = device_inputs(inp)
+    cfg = B.config_from_spec(spec)
+    ws = torch.empty(B.workspace_size(cfg) - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.MoeError) as ei:
+        B.layer_forward(cfg, {n: d[n] for n in ("w_router", "w_gate", "w_up", "w_down")},
+                        d["x"], ws=ws)
+    assert ei.value.status == B.MOE_ERR_WORKSPACE
