@@ -26,10 +26,8 @@ namespace moe {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int GBM = kTileM;     // 128
-constexpr int GBK = 64;
-constexpr int GLD = GBK + 8;    // padded LDS row, bf16 elements
-constexpr int GBR = 128;        // B rows staged per K chunk
+constexpr int GBK = 32;        // K per pipeline stage
+constexpr int GBR = 128;       // B rows per tile (gate 64 + up 64, or down 128)
 
 struct TileInfo {
   int e;          // expert, or -1 for the shared group
@@ -37,15 +35,37 @@ struct TileInfo {
   int n0;
 };
 
+// Local tile index -> (n, m) for a group of mt M tiles x NT N tiles, in
+// blocks of up to 4 M tiles: within a block N runs slowest and M fastest, so
+// ~32 consecutive tiles (the ones an XCD runs at the same time) touch at most
+// 4 distinct A slabs and 8 distinct B slabs.
+__device__ __forceinline__ void grouped_nm(int l, int mt, int NT, int& n, int& m) {
+  constexpr int G = 4;
+  const int full = mt / G;
+  const int in_full = full * G * NT;
+  if (l < in_full) {
+    const int g = l / (G * NT);
+    const int r = l - g * G * NT;
+    n = r / G;
+    m = g * G + (r - n * G);
+  } else {
+    const int r = l - in_full;
+    const int g2 = mt - full * G;
+    n = r / g2;
+    m = full * G + (r - n * g2);
+  }
+}
+
 // Decodes the logical tile of this workgroup; returns false for surplus blocks.
 template <int BN>
 __device__ __forceinline__ bool decode_tile(const GemmParams& p, TileInfo& ti) {
+  const int BM = p.tile_m;
   const int ntiles = p.meta != nullptr ? p.meta[0] : 0;  // null: shared group only
   const int NT = (p.N + BN - 1) / BN;
   const int routed = NT * ntiles;
   int MTs = 0, NTs = 0;
   if (p.shared_T > 0) {
-    MTs = (p.shared_T + GBM - 1) / GBM;
+    MTs = (p.shared_T + BM - 1) / BM;
     NTs = (p.sN + BN - 1) / BN;
   }
   const int total = routed + MTs * NTs;
@@ -53,41 +73,91 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, TileInfo& ti) {
   const int per = (total + 7) >> 3;
   const int j = b >> 3;
   if (j >= per) return false;
-  const int L = (b & 7) * per + j;
+  int L = (b & 7) * per + j;
   if (L >= total) return false;
-  if (L < routed) {
-    const int q = L / NT;
-    const int e = p.tile_e[q];
-    const int tp0 = p.exp_tile0[e];
-    const int mt = p.exp_tile0[e + 1] - tp0;
-    const int local = L - NT * tp0;
-    const int n = local / mt;
-    const int m = local - n * mt;
-    // offsets clamped to [0, P]: caller-provided tables cannot push rows out of bounds
-    const int o0 = min(max(p.offsets[e], 0), p.P), o1 = min(max(p.offsets[e + 1], 0), p.P);
-    ti.e = e;
-    ti.row0 = o0 + m * GBM;
-    ti.nrows = min(GBM, o1 - ti.row0);
-    ti.n0 = n * BN;
-  } else {
-    const int Ls = L - routed;
-    const int n = Ls / MTs;
-    const int m = Ls - n * MTs;
+  int n, m;
+  // The shared group (long K for its down projection) is scheduled first.
+  if (L < MTs * NTs) {
+    grouped_nm(L, MTs, NTs, n, m);
     ti.e = -1;
-    ti.row0 = m * GBM;
-    ti.nrows = min(GBM, p.shared_T - ti.row0);
+    ti.row0 = m * BM;
+    ti.nrows = min(BM, p.shared_T - ti.row0);
     ti.n0 = n * BN;
+    return ti.nrows > 0;
   }
+  L -= MTs * NTs;
+  const int q = L / NT;
+  const int e = p.tile_e[q];
+  const int tp0 = p.exp_tile0[e];
+  const int mt = p.exp_tile0[e + 1] - tp0;
+  grouped_nm(L - NT * tp0, mt, NT, n, m);
+  // offsets clamped to [0, P]: caller-provided tables cannot push rows out of bounds
+  const int o0 = min(max(p.offsets[e], 0), p.P), o1 = min(max(p.offsets[e + 1], 0), p.P);
+  ti.e = e;
+  ti.row0 = o0 + m * BM;
+  ti.nrows = min(BM, o1 - ti.row0);
+  ti.n0 = n * BN;
   return ti.nrows > 0;
 }
 
-// KIND 0: gate/up (B rows 0..63 gate, 64..127 up; N tile 64).
-// KIND 1: down (B rows 0..127; N tile 128).
-template <int KIND>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmParams p) {
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] in bits 3:0,
+// vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8): at most N vector
+// loads (the newer stages' DMA) still in flight, and every LDS access of this
+// wave complete, so that after the barrier no wave still reads a buffer the
+// next DMA overwrites.
+template <int N>
+__device__ __forceinline__ void wait_stage() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier for the stage pipeline. __builtin_amdgcn_s_barrier has
+// no memory semantics for the compiler, which may then hoist the next
+// stage's LDS fragment reads (or the next DMA issue) above it; the empty asm
+// statements with a memory clobber pin every memory access to its side of
+// the barrier without emitting the wait-for-all-loads that __syncthreads'
+// fences would add.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS stage layout: rows of GBK = 32 bf16 (64 bytes = 4 chunks of 16 bytes),
+// no padding; logical chunk c of row r lives at physical chunk
+// c ^ ((r >> 1) & 3), so the 8 lanes that LDS serves per cycle (rows r..r+7
+// of one MFMA fragment, same chunk) hit 8 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * GBK + ((chunk ^ ((row >> 1) & 3)) << 3);
+}
+
+// KIND 0: gate/up (B rows 0..63 gate, 64..127 up; N tile 64 hidden units).
+// KIND 1: down (B rows 0..127; N tile 128 model columns).
+// BM rows per tile with BM / 64 x 2 waves of 64 x 64; S-stage pipeline of
+// direct global->LDS loads (global_load_lds_dwordx4), one stage per LDS
+// array so the compiler tracks each stage's loads separately. Every lane
+// issues every load (addresses clamped into the operand) so the wave's
+// outstanding-load count is the same on every path, and a stage is known to
+// have landed once at most (S - 2) stages' loads are outstanding.
+template <int KIND, int BM, int S>
+__global__ __launch_bounds__(BM * 2) void gemm_bf16_kernel(GemmParams p) {
+  constexpr int NTHR = BM * 2;
   constexpr int BN = KIND == 0 ? kTileNGateUp : kTileNDown;
-  __shared__ __align__(16) uint16_t As[2][GBM * GLD];
-  __shared__ __align__(16) uint16_t Bs[2][GBR * GLD];
+  constexpr int SA = BM * GBK;              // A elements per stage
+  constexpr int SEL = SA + GBR * GBK;       // elements per stage
+  constexpr int CPR = GBK / 8;              // 16-byte chunks per LDS row (4)
+  constexpr int LA = SA / 8 / NTHR;         // 16-byte A loads per thread per stage (2)
+  constexpr int LB = GBR * GBK / 8 / NTHR;  // B loads per thread per stage (2 or 1)
+  constexpr int LPS = LA + LB;
+  static_assert(S >= 2 && S <= 4, "stages");
+  __shared__ __align__(16) uint16_t L0[SEL];
+  __shared__ __align__(16) uint16_t L1[SEL];
+  __shared__ __align__(16) uint16_t L2[S >= 3 ? SEL : 8];
+  __shared__ __align__(16) uint16_t L3[S >= 4 ? SEL : 8];
 
   TileInfo ti;
   if (!decode_tile<BN>(p, ti)) return;
@@ -105,125 +175,170 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmParams p) {
   }
 
   const int tid = threadIdx.x;
-  const int lr = tid >> 3;         // staging row (plus 32 * i)
-  const int lc = (tid & 7) * 8;    // staging column (bf16 elements)
-
-  const uint16_t* arow[4];
-  const uint16_t* brow[4];
-  bool aok[4], bok[4];
+  const int wbase = tid & ~63;  // first thread of this wave
+  // Load i of this thread fills LDS slot q = i * NTHR + tid: row q / CPR,
+  // physical chunk tid % CPR, holding logical chunk (tid % CPR) ^ ((row >> 1) % CPR).
+  const uint16_t* asrc[LA];
+  int achunk[LA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = lr + 32 * i;
-    aok[i] = r < ti.nrows;
-    arow[i] = A;
-    if (aok[i]) {
-      const int srow = ti.row0 + r;
-      int src = srow;
-      if (KIND == 0 && !shared) src = min(max(p.perm[srow] / p.k, 0), p.a_rows - 1);
-      arow[i] = A + static_cast<size_t>(src) * K;
-    }
+  for (int i = 0; i < LA; ++i) {
+    const int r = (i * NTHR + tid) / CPR;
+    achunk[i] = ((tid % CPR) ^ ((r >> 1) % CPR)) * 8;
+    const int rr = r < ti.nrows ? r : 0;  // rows past the group reload row 0 (never stored)
+    const int srow = ti.row0 + rr;
+    int src = srow;
+    if (KIND == 0 && !shared) src = min(max(p.perm[srow] / p.k, 0), p.a_rows - 1);
+    asrc[i] = A + static_cast<size_t>(src) * K;
+  }
+  const uint16_t* bsrc[LB];
+  int bchunk[LB];
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int r = (i * NTHR + tid) / CPR;
+    bchunk[i] = ((tid % CPR) ^ ((r >> 1) % CPR)) * 8;
     int n;
     const uint16_t* base;
-    if (KIND == 0) {
-      n = ti.n0 + (r & 63);
-      base = r < 64 ? B0 : B1;
-    } else {
-      n = ti.n0 + r;
-      base = B0;
-    }
-    bok[i] = n < N;
-    brow[i] = base + static_cast<size_t>(bok[i] ? n : 0) * K;
+    if (KIND == 0) { n = ti.n0 + (r & 63); base = r < 64 ? B0 : B1; }
+    else { n = ti.n0 + r; base = B0; }
+    n = n < N ? n : N - 1;  // columns past N reload a valid row (never stored)
+    bsrc[i] = base + static_cast<size_t>(n) * K;
   }
 
-  u32x4_t ra[4], rb[4];
-  auto gload = [&](int k0) {
-    const int kk = k0 + lc;
-    const bool kok = kk < K;
+  const int nk = (K + GBK - 1) / GBK;
+  const bool ktail = (K % GBK) != 0;
+  auto issue = [&](uint16_t* st, int kc) {
+    const int k0 = min(kc, nk - 1) * GBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = (aok[i] && kok) ? *reinterpret_cast<const u32x4_t*>(arow[i] + kk) : u32x4_t{0u, 0u, 0u, 0u};
-      rb[i] = (bok[i] && kok) ? *reinterpret_cast<const u32x4_t*>(brow[i] + kk) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < LA; ++i) {
+      const int kk = min(k0 + achunk[i], K - 8);
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(asrc[i] + kk),
+                                       (lds_void_t*)(st + (i * NTHR + wbase) * 8), 16, 0, 0);
     }
-  };
-  auto sstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4_t*>(&As[buf][(lr + 32 * i) * GLD + lc]) = ra[i];
-      *reinterpret_cast<u32x4_t*>(&Bs[buf][(lr + 32 * i) * GLD + lc]) = rb[i];
+    for (int i = 0; i < LB; ++i) {
+      const int kk = min(k0 + bchunk[i], K - 8);
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(bsrc[i] + kk),
+                                       (lds_void_t*)(st + SA + (i * NTHR + wbase) * 8), 16, 0, 0);
     }
   };
 
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-
-  constexpr int NF = KIND == 0 ? 4 : 4;  // B fragments per wave (gate 2 + up 2, or 4)
+  const int wm = wave % (BM / 64), wn = wave / (BM / 64);
+  const int fr = lane & 15, fq = lane >> 4;
+  constexpr int NF = 4;
   floatx4_t acc[4][NF];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < NF; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (K + GBK - 1) / GBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kc = 0; kc < nk; ++kc) {
-    const int buf = kc & 1;
-    if (kc + 1 < nk) gload((kc + 1) * GBK);
+  // fragment offsets within a stage (the same for every stage)
+  int aoff[4], boff[NF];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8_t af[4], bf[NF];
+  for (int mf = 0; mf < 4; ++mf) aoff[mf] = swz(wm * 64 + mf * 16 + fr, fq);
 #pragma unroll
-      for (int mf = 0; mf < 4; ++mf) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&As[buf][(wm * 64 + mf * 16 + fr) * GLD + s * 32 + fk]);
-        af[mf] = __builtin_bit_cast(bf16x8_t, v);
-      }
-#pragma unroll
-      for (int nf = 0; nf < NF; ++nf) {
-        int brw;
-        if (KIND == 0) brw = (nf < 2 ? 0 : 64) + wn * 32 + (nf & 1) * 16 + fr;
-        else brw = wn * 64 + nf * 16 + fr;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&Bs[buf][brw * GLD + s * 32 + fk]);
-        bf[nf] = __builtin_bit_cast(bf16x8_t, v);
-      }
-#pragma unroll
-      for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-        for (int nf = 0; nf < NF; ++nf)
-          acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mf], bf[nf], acc[mf][nf], 0, 0, 0);
-    }
-    if (kc + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
+  for (int nf = 0; nf < NF; ++nf) {
+    int r;
+    if (KIND == 0) r = (nf < 2 ? 0 : 64) + wn * 32 + (nf & 1) * 16 + fr;
+    else r = wn * 64 + nf * 16 + fr;
+    boff[nf] = SA + swz(r, fq);
   }
 
-  // epilogue
+  auto compute = [&](const uint16_t* st) {
+    bf16x8_t af[4], bf[NF];
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+      af[mf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + aoff[mf]));
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf)
+      bf[nf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + boff[nf]));
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf)
+        acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mf], bf[nf], acc[mf][nf], 0, 0, 0);
+  };
+
+  // One pipeline step: stage kc lives in `cur`; `nxt` receives stage kc + S - 1.
+  auto step = [&](int kc, uint16_t* cur, uint16_t* nxt) {
+    wait_stage<(S - 2) * LPS>();
+    stage_barrier();
+    issue(nxt, kc + S - 1);
+    if (kc < nk) {
+      if (ktail && kc == nk - 1) {
+        // last, partial K chunk: zero A's columns past K (B's clamped
+        // duplicates then multiply zeros)
+        const int k0 = kc * GBK;
+#pragma unroll
+        for (int i = 0; i < LA; ++i) {
+          if (k0 + achunk[i] >= K)
+            *reinterpret_cast<u32x4_t*>(cur + (i * NTHR + tid) * 8) = u32x4_t{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
+      }
+      compute(cur);
+    }
+  };
+
+  issue(L0, 0);
+  if (S >= 3) issue(L1, 1);
+  if (S >= 4) issue(L2, 2);
+  for (int kb = 0; kb < nk; kb += S) {
+    if constexpr (S == 2) {
+      step(kb + 0, L0, L1);
+      step(kb + 1, L1, L0);
+    } else if constexpr (S == 3) {
+      step(kb + 0, L0, L2);
+      step(kb + 1, L1, L0);
+      step(kb + 2, L2, L1);
+    } else {
+      step(kb + 0, L0, L3);
+      step(kb + 1, L1, L0);
+      step(kb + 2, L2, L1);
+      step(kb + 3, L3, L2);
+    }
+  }
+  // drain the clamped loads past the last stage before L0 is reused
+  __syncthreads();
+
+  // epilogue: each wave stages its own sub-tile through a private slice of
+  // L0, 16 rows at a time, so every lane stores 16 contiguous bytes of an
+  // output row; no block barrier is needed (a wave reads only what it wrote).
+  constexpr int WC = KIND == 0 ? 32 : 64;  // output columns per wave
+  constexpr int WLD = WC + 8;
+  static_assert((NTHR / 64) * 16 * WLD <= SEL, "epilogue slices must fit in one stage buffer");
+  uint16_t* Cw = L0 + wave * 16 * WLD;
+  const int c0 = ti.n0 + wn * WC;  // first output column of this wave
+  constexpr int LPR = WC / 8;      // lanes per output row (4 or 8)
 #pragma unroll
   for (int mf = 0; mf < 4; ++mf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = wm * 64 + mf * 16 + (lane >> 4) * 4 + i;
-      if (r >= ti.nrows) continue;
-      const size_t orow = static_cast<size_t>(ti.row0 + r) * N;
+      const int rc = fq * 4 + i;
       if (KIND == 0) {
 #pragma unroll
-        for (int nf = 0; nf < 2; ++nf) {
-          const int c = ti.n0 + wn * 32 + nf * 16 + fr;
-          if (c < N) {
-            const float g = acc[mf][nf][i];
-            const float u = acc[mf][nf + 2][i];
-            OUT[orow + c] = f32_to_bf16(silu_f32(g) * u);
-          }
-        }
+        for (int nf = 0; nf < 2; ++nf)
+          Cw[rc * WLD + nf * 16 + fr] = f32_to_bf16(silu_f32(acc[mf][nf][i]) * acc[mf][nf + 2][i]);
       } else {
-        const float sc = (shared && p.srow_scale != nullptr) ? p.srow_scale[ti.row0 + r] : 1.0f;
+        const int rt = wm * 64 + mf * 16 + rc;
+        const float sc = (shared && p.srow_scale != nullptr && rt < ti.nrows)
+                             ? p.srow_scale[ti.row0 + rt] : 1.0f;
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf) {
-          const int c = ti.n0 + wn * 64 + nf * 16 + fr;
-          if (c < N) OUT[orow + c] = f32_to_bf16(acc[mf][nf][i] * sc);
-        }
+        for (int nf = 0; nf < NF; ++nf) Cw[rc * WLD + nf * 16 + fr] = f32_to_bf16(acc[mf][nf][i] * sc);
       }
     }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+#pragma unroll
+    for (int pass = 0; pass < (16 * LPR) / 64; ++pass) {
+      const int idx = pass * 64 + lane;
+      const int rc = idx / LPR, ch = (idx % LPR) * 8;
+      const int rt = wm * 64 + mf * 16 + rc;
+      if (rt < ti.nrows && c0 + ch < N) {
+        *reinterpret_cast<u32x4_t*>(OUT + static_cast<size_t>(ti.row0 + rt) * N + c0 + ch) =
+            *reinterpret_cast<const u32x4_t*>(Cw + rc * WLD + ch);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the slice is rewritten
   }
 }
 
@@ -277,16 +392,25 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
   }
 }
 
+template <int KIND, int BM>
+static void launch_bf16(const GemmParams& p, unsigned nblk, hipStream_t s) {
+  constexpr int S = 4;
+  gemm_bf16_kernel<KIND, BM, S><<<nblk, BM * 2, 0, s>>>(p);
+}
+
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (p.dtype == MOE_BF16) {
     const int BN = p.kind == 0 ? kTileNGateUp : kTileNDown;
+    const int BM = p.tile_m;
+    if (BM != 128 && BM != 256) return hipErrorInvalidValue;
     long long nblk = static_cast<long long>(ceil_div(p.N, BN)) * p.max_mtiles;
-    if (p.shared_T > 0) nblk += static_cast<long long>(ceil_div(p.shared_T, GBM)) * ceil_div(p.sN, BN);
+    if (p.shared_T > 0) nblk += static_cast<long long>(ceil_div(p.shared_T, BM)) * ceil_div(p.sN, BN);
     nblk = (nblk + 7) / 8 * 8;
     if (nblk <= 0) return hipSuccess;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (p.kind == 0) gemm_bf16_kernel<0><<<static_cast<unsigned>(nblk), 256, 0, s>>>(p);
-    else gemm_bf16_kernel<1><<<static_cast<unsigned>(nblk), 256, 0, s>>>(p);
+    const unsigned nb = static_cast<unsigned>(nblk);
+    if (p.kind == 0) { if (BM == 128) launch_bf16<0, 128>(p, nb, s); else launch_bf16<0, 256>(p, nb, s); }
+    else { if (BM == 128) launch_bf16<1, 128>(p, nb, s); else launch_bf16<1, 256>(p, nb, s); }
   } else {
     const long long n = static_cast<long long>(p.P) * p.N + static_cast<long long>(p.shared_T) * p.sN;
     const long long nblk = (n + 255) / 256;

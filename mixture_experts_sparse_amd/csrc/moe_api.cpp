@@ -197,8 +197,9 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* ids, int32_t* coun
   hipStream_t s = as_stream(stream);
   RankParams rp{ids, c.T, c.E, c.top_k, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank)};
   MOE_HIP(launch_rank(rp, s));
+  const int tm = choose_tile_m(c.T * c.top_k, c.E);
   ScanParams sp{at<int32_t>(ws, L.blk_hist), ceil_div(c.T, kRouteTokens), c.E, c.T * c.top_k,
-                max_m_tiles(c.T * c.top_k, c.E), counts, offsets, at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0),
+                max_m_tiles(c.T * c.top_k, c.E, tm), tm, counts, offsets, at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0),
                 at<int32_t>(ws, L.meta)};
   MOE_HIP(launch_scan(sp, s));
   ScatterParams xp{ids, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank), c.T, c.E,
@@ -221,14 +222,17 @@ GemmParams gemm_base(const moe_config& c, void* ws, const int32_t* offsets, int 
   g.meta = at<int32_t>(ws, L.meta);
   g.E = c.E;
   g.P = c.T * c.top_k;
-  g.max_mtiles = max_m_tiles(g.P, c.E);
+  g.tile_m = choose_tile_m(g.P, c.E);
+  g.max_mtiles = max_m_tiles(g.P, c.E, g.tile_m);
   g.a_rows = c.T;
   return g;
 }
 
 moe_status run_tiles(const moe_config& c, void* ws, const int32_t* offsets, hipStream_t s) {
   const WsLayout L = ws_layout(c);
-  TilesParams tp{offsets, c.E, c.T * c.top_k, max_m_tiles(c.T * c.top_k, c.E), at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0),
+  const int tm = choose_tile_m(c.T * c.top_k, c.E);
+  TilesParams tp{offsets, c.E, c.T * c.top_k, max_m_tiles(c.T * c.top_k, c.E, tm), tm,
+                 at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0),
                  at<int32_t>(ws, L.meta)};
   MOE_HIP(launch_tiles(tp, s));
   return MOE_OK;
@@ -321,7 +325,8 @@ moe_status moe_shared_expert(const moe_config* cfg, const void* x, const void* w
   void* act_s = at<void>(ws, L.act_s);
   GemmParams g{};
   g.kind = 0; g.dtype = c.dtype; g.k = c.top_k; g.E = c.E;
-  g.P = 0; g.max_mtiles = 0; g.a_rows = c.T;  // no routed rows: the launch is the shared group only
+  g.P = 0; g.max_mtiles = 0; g.a_rows = c.T;  // no routed rows: the shared group only
+  g.tile_m = choose_tile_m(c.T, 1);
   g.shared_T = c.T; g.sa = x; g.sK = c.d; g.sb0 = ws_gate; g.sb1 = ws_up; g.sN = c.shared_h;
   g.sout = act_s;
   MOE_HIP(launch_gemm(g, s));
@@ -371,6 +376,7 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
     return hipEventRecord(reinterpret_cast<hipEvent_t>(stage_events[i]), s);
   };
   const int NB = ceil_div(c.T, kRouteTokens);
+  const int tm = choose_tile_m(c.T * c.top_k, c.E);
   int32_t* ids_p = ids != nullptr ? ids : at<int32_t>(ws, L.ids);
   float* gates_p = gates != nullptr ? gates : at<float>(ws, L.gates);
   int32_t* counts_p = counts != nullptr ? counts : at<int32_t>(ws, L.counts);
@@ -397,13 +403,14 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
     rp.counts = counts_p; rp.offsets = offsets; rp.perm = perm; rp.inv = inv;
     rp.tile_e = at<int32_t>(ws, L.tile_e); rp.exp_tile0 = at<int32_t>(ws, L.exp_tile0);
     rp.meta = at<int32_t>(ws, L.meta);
-    rp.max_tiles = max_m_tiles(c.T * c.top_k, c.E);
+    rp.tile_m = tm;
+    rp.max_tiles = max_m_tiles(c.T * c.top_k, c.E, tm);
   }
   MOE_HIP(launch_route(rp, c.dtype, s));
   MOE_HIP(mark(1));
   if (NB > 1) {
     ScanParams sp{at<int32_t>(ws, L.blk_hist), NB, c.E, c.T * c.top_k,
-                  max_m_tiles(c.T * c.top_k, c.E), counts_p, offsets,
+                  max_m_tiles(c.T * c.top_k, c.E, tm), tm, counts_p, offsets,
                   at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0), at<int32_t>(ws, L.meta)};
     MOE_HIP(launch_scan(sp, s));
     ScatterParams xp{ids_p, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank), c.T, c.E,

@@ -13,8 +13,10 @@ namespace moe {
 // Route block: tokens per workgroup of the router / top-k kernel. The
 // dispatch histogram is kept per route block.
 constexpr int kRouteTokens = 64;
-// Grouped-GEMM M tile (rows of one expert per workgroup).
+// Grouped-GEMM M tile (rows of one expert per workgroup): 128, or 256 when
+// experts average at least 256 rows (tile_m in the parameter blocks).
 constexpr int kTileM = 128;
+constexpr int kTileMLarge = 256;
 // Gate/up N tile (hidden units per workgroup; gate and up both) and down N
 // tile (model-width columns per workgroup).
 constexpr int kTileNGateUp = 64;
@@ -25,7 +27,11 @@ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Upper bound on the number of M tiles over all experts:
 // sum_e ceil(c_e / BM) <= floor(P / BM) + min(E, P).
-inline int max_m_tiles(int P, int E) { return P / kTileM + (E < P ? E : P) + 1; }
+inline int max_m_tiles(int P, int E, int bm = kTileM) { return P / bm + (E < P ? E : P) + 1; }
+
+// M tile for a call: 256 rows when the routed rows per expert average at
+// least 256 (prefill-shaped batches), else 128.
+inline int choose_tile_m(int P, int E) { return P >= kTileMLarge * E ? kTileMLarge : kTileM; }
 
 // Workspace carve-up. Offsets are in bytes from the start of ws.
 struct WsLayout {
@@ -61,6 +67,7 @@ struct RouteParams {
   int32_t* exp_tile0;     // [E+1]
   int32_t* meta;          // [4]
   int max_tiles;
+  int tile_m;
 };
 
 // Dispatch from given ids (moe_dispatch): histogram + local ranks.
@@ -73,7 +80,7 @@ struct RankParams {
 
 struct ScanParams {
   int32_t* blk_hist;  // in: per-block counts; out: per-block base rows
-  int NB, E, P, max_tiles;
+  int NB, E, P, max_tiles, tile_m;
   int32_t* counts;
   int32_t* offsets;
   int32_t* tile_e;
@@ -93,7 +100,7 @@ struct ScatterParams {
 // Tile table from offsets alone (standalone gate_up / down / expert_ffn).
 struct TilesParams {
   const int32_t* offsets;
-  int E, P, max_tiles;
+  int E, P, max_tiles, tile_m;
   int32_t* tile_e;
   int32_t* exp_tile0;
   int32_t* meta;
@@ -122,6 +129,7 @@ struct GemmParams {
   const int32_t* meta;
   int E, P;
   int max_mtiles;
+  int tile_m;             // M tile of the table (128 or 256)
   int a_rows;             // rows of the gathered A operand (T): token indices are clamped to it
   // shared group
   int shared_T;           // 0: none

@@ -52,17 +52,20 @@ __device__ __forceinline__ int bits_for(int E) { return E > 1 ? 32 - __clz(E - 1
 
 // ---------------------------------------------------------------------------
 // Stable ranks of the block's pairs (pair order), block histogram in run[].
-// sel[q] = expert of local pair q, q < npairs. Must be called by all threads.
+// sel[q] = expert of local pair q, q < npairs. Must be called by all NTHR
+// threads; wh has one row per wave.
 // ---------------------------------------------------------------------------
+template <int NTHR>
 __device__ void block_rank(const uint8_t* sel, int npairs, int E, int32_t* lrank_out,
                            int (*wh)[kMaxE], int* run) {
+  constexpr int NW = NTHR / kWave;
   const int tid = threadIdx.x, wave = tid >> 6;
   const int nbits = bits_for(E);
-  if (tid < E) run[tid] = 0;
-  for (int base = 0; base < npairs; base += 256) {
-    if (tid < E) {
+  for (int e = tid; e < E; e += NTHR) run[e] = 0;
+  for (int base = 0; base < npairs; base += NTHR) {
+    for (int e = tid; e < E; e += NTHR) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) wh[w][tid] = 0;
+      for (int w = 0; w < NW; ++w) wh[w][e] = 0;
     }
     __syncthreads();
     const int q = base + tid;
@@ -77,15 +80,15 @@ __device__ void block_rank(const uint8_t* sel, int npairs, int E, int32_t* lrank
     const int rank = __popcll(peers & lanemask_lt());
     if (valid && rank == 0) wh[wave][e] = __popcll(peers);
     __syncthreads();
-    if (tid < E) {
-      int r = run[tid];
+    for (int x = tid; x < E; x += NTHR) {
+      int r = run[x];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int c = wh[w][tid];
-        wh[w][tid] = r;
+      for (int w = 0; w < NW; ++w) {
+        const int c = wh[w][x];
+        wh[w][x] = r;
         r += c;
       }
-      run[tid] = r;
+      run[x] = r;
     }
     __syncthreads();
     if (valid) lrank_out[q] = wh[wave][e] + rank;
@@ -112,66 +115,105 @@ __device__ void write_tile_table(const int* tp, int E, int max_tiles, int32_t* t
 }
 
 // ---------------------------------------------------------------------------
-// route kernel
+// route kernel: 512 threads, 64 tokens. Logits: 8 waves as 4 token groups of
+// 16 x 2 column halves; router rows staged through LDS in 64-deep K chunks,
+// double-buffered with the next chunk's loads issued before the MFMAs.
 // ---------------------------------------------------------------------------
+constexpr int RTHR = 512;
+constexpr int RNW = RTHR / kWave;
+
 template <int NCH>
 struct RouteSmem {
   static constexpr int NC = NCH * 64;  // padded logit columns (E experts + optional shared gate)
   static constexpr int LDL = NC + 1;   // fp32 logit row stride
-  static constexpr int kStageBytes = NC * RLD * 2;
+  static constexpr int kStageBytes = 2 * NC * RLD * 2;  // two K-chunk buffers
   static constexpr int kLogitBytes = RT * LDL * 4;
   static constexpr int kRawBytes = kStageBytes > kLogitBytes ? kStageBytes : kLogitBytes;
+  static constexpr int kLoads = NC * 8 / RTHR;  // 16-byte staging loads per thread per chunk
 };
 
 template <int NCH>
 __device__ void route_logits_bf16(const RouteParams& p, int t0, unsigned char* raw) {
   using S = RouteSmem<NCH>;
+  constexpr int NF = NCH * 2;  // 16-column fragments per wave (half of NC)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 3, wn = wave >> 2;
   const uint16_t* X = static_cast<const uint16_t*>(p.x);
   const uint16_t* W = static_cast<const uint16_t*>(p.w_router);
   const uint16_t* WS = static_cast<const uint16_t*>(p.w_sgate);
   uint16_t* stage = reinterpret_cast<uint16_t*>(raw);
-  floatx4_t acc[NCH * 4];
+  floatx4_t acc[NF];
 #pragma unroll
-  for (int f = 0; f < NCH * 4; ++f) acc[f] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  const int arow = t0 + wave * 16 + (lane & 15);
+  for (int f = 0; f < NF; ++f) acc[f] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  const int arow = t0 + wm * 16 + (lane & 15);
   const bool arow_ok = arow < p.T;
   const int kq = (lane >> 4) * 8;
-  for (int k0 = 0; k0 < p.d; k0 += RK) {
-    for (int c = tid; c < S::NC * 8; c += 256) {
-      const int r = c >> 3, ch = c & 7, kk = k0 + ch * 8;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (kk < p.d) {
-        if (r < p.E) v = *reinterpret_cast<const u32x4_t*>(W + static_cast<size_t>(r) * p.d + kk);
-        else if (r == p.E && WS != nullptr) v = *reinterpret_cast<const u32x4_t*>(WS + kk);
-      }
-      *reinterpret_cast<u32x4_t*>(stage + r * RLD + ch * 8) = v;
+
+  // staging rows handled by this thread: c = tid + i * RTHR -> row c / 8, chunk c % 8
+  const uint16_t* srow[S::kLoads];
+#pragma unroll
+  for (int i = 0; i < S::kLoads; ++i) {
+    const int r = (tid + i * RTHR) >> 3;
+    srow[i] = r < p.E ? W + static_cast<size_t>(r) * p.d : (r == p.E ? WS : nullptr);
+  }
+  const int sch = (tid & 7) * 8;
+  u32x4_t pre[S::kLoads];
+  u32x4_t apre[2];
+  auto gload = [&](int k0) {
+    const int kk = k0 + sch;
+#pragma unroll
+    for (int i = 0; i < S::kLoads; ++i) {
+      pre[i] = (srow[i] != nullptr && kk < p.d)
+                   ? *reinterpret_cast<const u32x4_t*>(srow[i] + kk) : u32x4_t{0u, 0u, 0u, 0u};
     }
-    bf16x8_t a[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int kk = k0 + s * 32 + kq;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (arow_ok && kk < p.d) v = *reinterpret_cast<const u32x4_t*>(X + static_cast<size_t>(arow) * p.d + kk);
-      a[s] = __builtin_bit_cast(bf16x8_t, v);
+      const int ka = k0 + s * 32 + kq;
+      apre[s] = (arow_ok && ka < p.d)
+                    ? *reinterpret_cast<const u32x4_t*>(X + static_cast<size_t>(arow) * p.d + ka)
+                    : u32x4_t{0u, 0u, 0u, 0u};
     }
-    __syncthreads();
+  };
+  auto sstore = [&](int buf) {
+    uint16_t* st = stage + buf * S::NC * RLD;
+#pragma unroll
+    for (int i = 0; i < S::kLoads; ++i) {
+      const int r = (tid + i * RTHR) >> 3;
+      *reinterpret_cast<u32x4_t*>(st + r * RLD + sch) = pre[i];
+    }
+  };
+  const int nk = (p.d + RK - 1) / RK;
+  gload(0);
+  sstore(0);
+  u32x4_t acur[2] = {apre[0], apre[1]};
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const int buf = kc & 1;
+    if (kc + 1 < nk) gload((kc + 1) * RK);
+    const uint16_t* st = stage + buf * S::NC * RLD;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, acur[s]);
 #pragma unroll
-      for (int f = 0; f < NCH * 4; ++f) {
-        const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(stage + (f * 16 + (lane & 15)) * RLD + s * 32 + kq);
-        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], __builtin_bit_cast(bf16x8_t, bv), acc[f], 0, 0, 0);
+      for (int f = 0; f < NF; ++f) {
+        const int col = wn * (S::NC / 2) + f * 16 + (lane & 15);
+        const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(st + col * RLD + s * 32 + kq);
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bv), acc[f], 0, 0, 0);
       }
+    }
+    if (kc + 1 < nk) {
+      sstore(buf ^ 1);
+      acur[0] = apre[0];
+      acur[1] = apre[1];
     }
     __syncthreads();
   }
   float* lg = reinterpret_cast<float*>(raw);
 #pragma unroll
-  for (int f = 0; f < NCH * 4; ++f) {
+  for (int f = 0; f < NF; ++f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      lg[(wave * 16 + (lane >> 4) * 4 + i) * S::LDL + f * 16 + (lane & 15)] = acc[f][i];
+      lg[(wm * 16 + (lane >> 4) * 4 + i) * S::LDL + wn * (S::NC / 2) + f * 16 + (lane & 15)] = acc[f][i];
     }
   }
   __syncthreads();
@@ -185,7 +227,7 @@ __device__ void route_logits_f32(const RouteParams& p, int t0, unsigned char* ra
   const float* W = static_cast<const float*>(p.w_router);
   const float* WS = static_cast<const float*>(p.w_sgate);
   float* lg = reinterpret_cast<float*>(raw);
-  for (int idx = tid; idx < RT * S::NC; idx += 256) {
+  for (int idx = tid; idx < RT * S::NC; idx += RTHR) {
     const int r = idx / S::NC, e = idx - r * S::NC, t = t0 + r;
     float s = 0.f;
     const float* wr = e < p.E ? W + static_cast<size_t>(e) * p.d : (e == p.E ? WS : nullptr);
@@ -198,15 +240,17 @@ __device__ void route_logits_f32(const RouteParams& p, int t0, unsigned char* ra
   __syncthreads();
 }
 
-// Top-k, gates, logits and shared-gate outputs for the block's tokens; the
-// local selection goes to sel[] for the rank pass.
+// Top-k, gates, logits and shared-gate outputs for the block's tokens (one
+// wave per token, 8 tokens per wave); the selection also goes to sel[] for
+// the rank pass.
 template <int NCH>
 __device__ void route_select(const RouteParams& p, int t0, const float* lg, uint8_t* sel) {
   using S = RouteSmem<NCH>;
+  constexpr int TPW = RT / RNW;  // tokens per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = p.E, k = p.k;
-  for (int rr = 0; rr < 16; ++rr) {
-    const int r = wave * 16 + rr, t = t0 + r;
+  for (int rr = 0; rr < TPW; ++rr) {
+    const int r = wave * TPW + rr, t = t0 + r;
     if (t >= p.T) break;
     float v[NCH], ov[NCH];
 #pragma unroll
@@ -275,11 +319,11 @@ __device__ void route_select(const RouteParams& p, int t0, const float* lg, uint
 }
 
 template <int NCH, bool BF16>
-__global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
+__global__ __launch_bounds__(RTHR) void route_kernel(RouteParams p) {
   using S = RouteSmem<NCH>;
   __shared__ __align__(16) unsigned char raw[S::kRawBytes];
   __shared__ uint8_t sel[RT * kMaxE];
-  __shared__ int wh[4][kMaxE];
+  __shared__ int wh[RNW][kMaxE];
   __shared__ int run[kMaxE + 1];
   __shared__ int scan_a[kMaxE + 1];
   __shared__ int scan_b[kMaxE + 1];
@@ -292,23 +336,23 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
   const int nt = min(RT, p.T - t0);
   const int npairs = nt * p.k;
   int32_t* lrank = p.lrank + static_cast<size_t>(t0) * p.k;
-  block_rank(sel, npairs, p.E, lrank, wh, run);
+  block_rank<RTHR>(sel, npairs, p.E, lrank, wh, run);
   const int tid = threadIdx.x;
   if (p.counts == nullptr) {
-    if (tid < p.E) p.blk_hist[blockIdx.x * p.E + tid] = run[tid];
+    for (int e = tid; e < p.E; e += RTHR) p.blk_hist[blockIdx.x * p.E + e] = run[e];
     return;
   }
   // One route block covers every token: finish the dispatch here.
   __syncthreads();
   if (tid < kWave) wave_exclusive_scan256(run, scan_a, p.E);  // offsets
-  if (tid < p.E) scan_b[tid] = (run[tid] + kTileM - 1) / kTileM;
+  for (int e = tid; e < p.E; e += RTHR) scan_b[e] = (run[e] + p.tile_m - 1) / p.tile_m;
   __syncthreads();
   if (tid < kWave) wave_exclusive_scan256(scan_b, scan_b, p.E);  // tile prefix (in place per lane)
   __syncthreads();
-  if (tid < p.E) { p.counts[tid] = run[tid]; p.offsets[tid] = scan_a[tid]; }
+  for (int e = tid; e < p.E; e += RTHR) { p.counts[e] = run[e]; p.offsets[e] = scan_a[e]; }
   if (tid == 0) p.offsets[p.E] = scan_a[p.E];
   write_tile_table(scan_b, p.E, p.max_tiles, p.tile_e, p.exp_tile0, p.meta);
-  for (int q = tid; q < npairs; q += 256) {
+  for (int q = tid; q < npairs; q += RTHR) {
     const int pos = scan_a[sel[q]] + lrank[q];
     p.perm[pos] = q;
     p.inv[q] = pos;
@@ -331,19 +375,44 @@ __global__ __launch_bounds__(256) void rank_kernel(RankParams p) {
   for (int q = threadIdx.x; q < npairs; q += 256)
     sel[q] = static_cast<uint8_t>(min(max(ids[q], 0), p.E - 1));
   __syncthreads();
-  block_rank(sel, npairs, p.E, p.lrank + static_cast<size_t>(t0) * p.k, wh, run);
+  block_rank<256>(sel, npairs, p.E, p.lrank + static_cast<size_t>(t0) * p.k, wh, run);
   if (static_cast<int>(threadIdx.x) < p.E) p.blk_hist[blockIdx.x * p.E + threadIdx.x] = run[threadIdx.x];
 }
 
 // ---------------------------------------------------------------------------
-// scan kernel (one workgroup of 1024 threads)
+// scan kernel (one workgroup of 1024 threads). The per-block histogram is
+// pulled into LDS with batched loads when it fits (NB * E <= kScanLdsInts),
+// so the column scans run at LDS latency instead of one HBM round trip per
+// block.
 // ---------------------------------------------------------------------------
+constexpr int kScanLdsInts = 32768;  // 128 KiB
+
 __global__ __launch_bounds__(1024) void scan_kernel(ScanParams p) {
+  extern __shared__ int hl[];  // [NB * E] when it fits
   __shared__ int part[1024];
   __shared__ int cnt[kMaxE + 1];
   __shared__ int off[kMaxE + 1];
   __shared__ int tp[kMaxE + 1];
   const int tid = threadIdx.x, E = p.E, NB = p.NB;
+  const int n = NB * E;
+  const bool in_lds = n <= kScanLdsInts;
+  int* h = in_lds ? hl : p.blk_hist;
+  if (in_lds) {
+    for (int base = tid; base < n; base += 8 * 1024) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * 1024;
+        v[u] = i < n ? p.blk_hist[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * 1024;
+        if (i < n) hl[i] = v[u];
+      }
+    }
+    __syncthreads();
+  }
   int G = 1024 / E;
   if (G > NB) G = NB;
   const int g = tid / E, e = tid - g * E;
@@ -352,7 +421,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(ScanParams p) {
   const int b0 = g * chunk, b1 = min(NB, b0 + chunk);
   if (active) {
     int s = 0;
-    for (int b = b0; b < b1; ++b) s += p.blk_hist[b * E + e];
+    for (int b = b0; b < b1; ++b) s += h[b * E + e];
     part[g * E + e] = s;
   }
   __syncthreads();
@@ -367,14 +436,14 @@ __global__ __launch_bounds__(1024) void scan_kernel(ScanParams p) {
   }
   __syncthreads();
   if (tid < kWave) wave_exclusive_scan256(cnt, off, E);
-  if (tid < E) tp[tid] = (cnt[tid] + kTileM - 1) / kTileM;
+  if (tid < E) tp[tid] = (cnt[tid] + p.tile_m - 1) / p.tile_m;
   __syncthreads();
   if (tid < kWave) wave_exclusive_scan256(tp, tp, E);
   __syncthreads();
   if (active) {
     int base = off[e] + part[g * E + e];
     for (int b = b0; b < b1; ++b) {
-      const int c = p.blk_hist[b * E + e];
+      const int c = h[b * E + e];
       p.blk_hist[b * E + e] = base;
       base += c;
     }
@@ -408,7 +477,7 @@ __global__ __launch_bounds__(256) void tiles_kernel(TilesParams p) {
   if (tid < p.E) {
     // caller-provided offsets: counts clamped to [0, P] so the table stays in bounds
     const int c = min(max(p.offsets[tid + 1] - p.offsets[tid], 0), p.P);
-    tp[tid] = (c + kTileM - 1) / kTileM;
+    tp[tid] = (c + p.tile_m - 1) / p.tile_m;
   }
   __syncthreads();
   if (tid < kWave) wave_exclusive_scan256(tp, tp, p.E);
@@ -442,8 +511,8 @@ __global__ __launch_bounds__(256) void rowdot_sigmoid_kernel(RowDotSigmoidParams
 // ---------------------------------------------------------------------------
 template <int NCH>
 static void launch_route_nch(const RouteParams& p, int dtype, int nb, hipStream_t s) {
-  if (dtype == MOE_BF16) route_kernel<NCH, true><<<nb, 256, 0, s>>>(p);
-  else route_kernel<NCH, false><<<nb, 256, 0, s>>>(p);
+  if (dtype == MOE_BF16) route_kernel<NCH, true><<<nb, RTHR, 0, s>>>(p);
+  else route_kernel<NCH, false><<<nb, RTHR, 0, s>>>(p);
 }
 
 hipError_t launch_route(const RouteParams& p, int dtype, hipStream_t s) {
@@ -467,7 +536,9 @@ hipError_t launch_rank(const RankParams& p, hipStream_t s) {
 }
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t s) {
-  scan_kernel<<<1, 1024, 0, s>>>(p);
+  const int n = p.NB * p.E;
+  const size_t lds = n <= kScanLdsInts ? static_cast<size_t>(n) * 4 : 0;
+  scan_kernel<<<1, 1024, lds, s>>>(p);
   return hipGetLastError();
 }
 
