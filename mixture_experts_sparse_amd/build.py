@@ -27,7 +27,7 @@ SOURCES = ["moe_api.cpp", "route_dispatch.hip", "expert_gemm.hip", "combine.hip"
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-Wall",
     "-Wno-unused-function",
@@ -44,9 +44,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmoe.so)")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, defines=(), tag: str = "") -> str:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + tag + ".o")
+    cmd = [hipcc(), *COMMON_FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
@@ -62,20 +63,22 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every source and links libmoe.so; returns its path."""
+def build(verbose: bool = False, defines=(), lib_path: str = LIB_PATH) -> str:
+    """Compiles every source and links libmoe.so (or ``lib_path``); returns its
+    path. ``defines`` are extra -D flags (tuning variants)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        tag = "" if not defines else "_" + "_".join(d.replace("=", "") for d in defines)
+        objs = list(ex.map(lambda s: _compile(s, verbose, defines, tag), SOURCES))
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

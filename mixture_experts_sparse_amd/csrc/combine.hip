@@ -11,8 +11,6 @@
 
 namespace moe {
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
 __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineParams p) {
   const int cpr = p.d >> 3;  // 8-element chunks per row
   const long long item = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;

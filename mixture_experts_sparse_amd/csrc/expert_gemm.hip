@@ -19,14 +19,13 @@
 // logical tile (b mod 8) * ceil(n/8) + b / 8: consecutive logical tiles (the
 // M tiles that share one weight slab) land on the same XCD and its L2.
 
+#include <utility>
+
 #include "device_common.h"
 #include "moe_internal.h"
 
 namespace moe {
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int GBK = 32;        // K per pipeline stage
 constexpr int GBR = 128;       // B rows per tile (gate 64 + up 64, or down 128)
 
 struct TileInfo {
@@ -100,41 +99,6 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, TileInfo& ti) {
   return ti.nrows > 0;
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void gbl_void_t;
-
-// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] in bits 3:0,
-// vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8): at most N vector
-// loads (the newer stages' DMA) still in flight, and every LDS access of this
-// wave complete, so that after the barrier no wave still reads a buffer the
-// next DMA overwrites.
-template <int N>
-__device__ __forceinline__ void wait_stage() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-}
-
-// Workgroup barrier for the stage pipeline. __builtin_amdgcn_s_barrier has
-// no memory semantics for the compiler, which may then hoist the next
-// stage's LDS fragment reads (or the next DMA issue) above it; the empty asm
-// statements with a memory clobber pin every memory access to its side of
-// the barrier without emitting the wait-for-all-loads that __syncthreads'
-// fences would add.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// LDS stage layout: rows of GBK = 32 bf16 (64 bytes = 4 chunks of 16 bytes),
-// no padding; logical chunk c of row r lives at physical chunk
-// c ^ ((r >> 1) & 3), so the 8 lanes that LDS serves per cycle (rows r..r+7
-// of one MFMA fragment, same chunk) hit 8 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * GBK + ((chunk ^ ((row >> 1) & 3)) << 3);
-}
-
 // KIND 0: gate/up (B rows 0..63 gate, 64..127 up; N tile 64 hidden units).
 // KIND 1: down (B rows 0..127; N tile 128 model columns).
 // BM rows per tile with BM / 64 x 2 waves of 64 x 64; S-stage pipeline of
@@ -143,21 +107,39 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 // issues every load (addresses clamped into the operand) so the wave's
 // outstanding-load count is the same on every path, and a stage is known to
 // have landed once at most (S - 2) stages' loads are outstanding.
-template <int KIND, int BM, int S>
+template <int KIND, int BM, int S, int BK>
 __global__ __launch_bounds__(BM * 2) void gemm_bf16_kernel(GemmParams p) {
+  constexpr int GBK = BK;
   constexpr int NTHR = BM * 2;
   constexpr int BN = KIND == 0 ? kTileNGateUp : kTileNDown;
   constexpr int SA = BM * GBK;              // A elements per stage
   constexpr int SEL = SA + GBR * GBK;       // elements per stage
-  constexpr int CPR = GBK / 8;              // 16-byte chunks per LDS row (4)
-  constexpr int LA = SA / 8 / NTHR;         // 16-byte A loads per thread per stage (2)
-  constexpr int LB = GBR * GBK / 8 / NTHR;  // B loads per thread per stage (2 or 1)
+  constexpr int CPR = GBK / 8;              // 16-byte chunks per LDS row (4 or 8)
+  constexpr int KS = GBK / 32;              // MFMA K steps per stage
+  constexpr int LA = SA / 8 / NTHR;         // 16-byte A loads per thread per stage
+  constexpr int LB = GBR * GBK / 8 / NTHR;  // B loads per thread per stage
   constexpr int LPS = LA + LB;
-  static_assert(S >= 2 && S <= 4, "stages");
+  static_assert(S >= 2 && S <= 8, "stages");
   __shared__ __align__(16) uint16_t L0[SEL];
   __shared__ __align__(16) uint16_t L1[SEL];
-  __shared__ __align__(16) uint16_t L2[S >= 3 ? SEL : 8];
-  __shared__ __align__(16) uint16_t L3[S >= 4 ? SEL : 8];
+  __shared__ __align__(16) uint16_t L2[S > 2 ? SEL : 8];
+  __shared__ __align__(16) uint16_t L3[S > 3 ? SEL : 8];
+  __shared__ __align__(16) uint16_t L4[S > 4 ? SEL : 8];
+  __shared__ __align__(16) uint16_t L5[S > 5 ? SEL : 8];
+  __shared__ __align__(16) uint16_t L6[S > 6 ? SEL : 8];
+  __shared__ __align__(16) uint16_t L7[S > 7 ? SEL : 8];
+  // stage i lives in its own LDS array (static index after unrolling), so the
+  // compiler can tell one stage's DMA from another stage's fragment reads
+  auto buf = [&]<int I>() -> uint16_t* {
+    if constexpr (I == 0) return L0;
+    else if constexpr (I == 1) return L1;
+    else if constexpr (I == 2) return L2;
+    else if constexpr (I == 3) return L3;
+    else if constexpr (I == 4) return L4;
+    else if constexpr (I == 5) return L5;
+    else if constexpr (I == 6) return L6;
+    else return L7;
+  };
 
   TileInfo ti;
   if (!decode_tile<BN>(p, ti)) return;
@@ -177,13 +159,13 @@ __global__ __launch_bounds__(BM * 2) void gemm_bf16_kernel(GemmParams p) {
   const int tid = threadIdx.x;
   const int wbase = tid & ~63;  // first thread of this wave
   // Load i of this thread fills LDS slot q = i * NTHR + tid: row q / CPR,
-  // physical chunk tid % CPR, holding logical chunk (tid % CPR) ^ ((row >> 1) % CPR).
+  // physical chunk tid % CPR (the swizzle decides which logical chunk).
   const uint16_t* asrc[LA];
   int achunk[LA];
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
     const int r = (i * NTHR + tid) / CPR;
-    achunk[i] = ((tid % CPR) ^ ((r >> 1) % CPR)) * 8;
+    achunk[i] = swz_phys_to_logical<BK>(r, tid % CPR) * 8;
     const int rr = r < ti.nrows ? r : 0;  // rows past the group reload row 0 (never stored)
     const int srow = ti.row0 + rr;
     int src = srow;
@@ -195,7 +177,7 @@ __global__ __launch_bounds__(BM * 2) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
     const int r = (i * NTHR + tid) / CPR;
-    bchunk[i] = ((tid % CPR) ^ ((r >> 1) % CPR)) * 8;
+    bchunk[i] = swz_phys_to_logical<BK>(r, tid % CPR) * 8;
     int n;
     const uint16_t* base;
     if (KIND == 0) { n = ti.n0 + (r & 63); base = r < 64 ? B0 : B1; }
@@ -233,30 +215,36 @@ __global__ __launch_bounds__(BM * 2) void gemm_bf16_kernel(GemmParams p) {
     for (int b = 0; b < NF; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   // fragment offsets within a stage (the same for every stage)
-  int aoff[4], boff[NF];
+  int aoff[KS][4], boff[KS][NF];
 #pragma unroll
-  for (int mf = 0; mf < 4; ++mf) aoff[mf] = swz(wm * 64 + mf * 16 + fr, fq);
+  for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-  for (int nf = 0; nf < NF; ++nf) {
-    int r;
-    if (KIND == 0) r = (nf < 2 ? 0 : 64) + wn * 32 + (nf & 1) * 16 + fr;
-    else r = wn * 64 + nf * 16 + fr;
-    boff[nf] = SA + swz(r, fq);
+    for (int mf = 0; mf < 4; ++mf) aoff[ks][mf] = swz<BK>(wm * 64 + mf * 16 + fr, ks * 4 + fq);
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf) {
+      int r;
+      if (KIND == 0) r = (nf < 2 ? 0 : 64) + wn * 32 + (nf & 1) * 16 + fr;
+      else r = wn * 64 + nf * 16 + fr;
+      boff[ks][nf] = SA + swz<BK>(r, ks * 4 + fq);
+    }
   }
 
   auto compute = [&](const uint16_t* st) {
-    bf16x8_t af[4], bf[NF];
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
-      af[mf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + aoff[mf]));
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8_t af[4], bf[NF];
 #pragma unroll
-    for (int nf = 0; nf < NF; ++nf)
-      bf[nf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + boff[nf]));
-#pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
+      for (int mf = 0; mf < 4; ++mf)
+        af[mf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + aoff[ks][mf]));
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf)
-        acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mf], bf[nf], acc[mf][nf], 0, 0, 0);
+        bf[nf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + boff[ks][nf]));
+#pragma unroll
+      for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+          acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mf], bf[nf], acc[mf][nf], 0, 0, 0);
+    }
   };
 
   // One pipeline step: stage kc lives in `cur`; `nxt` receives stage kc + S - 1.
@@ -280,24 +268,13 @@ __global__ __launch_bounds__(BM * 2) void gemm_bf16_kernel(GemmParams p) {
     }
   };
 
-  issue(L0, 0);
-  if (S >= 3) issue(L1, 1);
-  if (S >= 4) issue(L2, 2);
-  for (int kb = 0; kb < nk; kb += S) {
-    if constexpr (S == 2) {
-      step(kb + 0, L0, L1);
-      step(kb + 1, L1, L0);
-    } else if constexpr (S == 3) {
-      step(kb + 0, L0, L2);
-      step(kb + 1, L1, L0);
-      step(kb + 2, L2, L1);
-    } else {
-      step(kb + 0, L0, L3);
-      step(kb + 1, L1, L0);
-      step(kb + 2, L2, L1);
-      step(kb + 3, L3, L2);
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    // prologue: stages 0 .. S-2
+    ((I < S - 1 ? issue(buf.template operator()<I>(), I) : void()), ...);
+    for (int kb = 0; kb < nk; kb += S) {
+      (step(kb + I, buf.template operator()<I>(), buf.template operator()<(I + S - 1) % S>()), ...);
     }
-  }
+  }(std::make_integer_sequence<int, S>{});
   // drain the clamped loads past the last stage before L0 is reused
   __syncthreads();
 
@@ -392,10 +369,24 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
   }
 }
 
+#ifndef MOE_STAGES_BM128
+#define MOE_STAGES_BM128 4
+#endif
+#ifndef MOE_STAGES_BM256
+#define MOE_STAGES_BM256 4
+#endif
+#ifndef MOE_BK_BM128
+#define MOE_BK_BM128 32
+#endif
+#ifndef MOE_BK_BM256
+#define MOE_BK_BM256 32
+#endif
+
 template <int KIND, int BM>
 static void launch_bf16(const GemmParams& p, unsigned nblk, hipStream_t s) {
-  constexpr int S = 4;
-  gemm_bf16_kernel<KIND, BM, S><<<nblk, BM * 2, 0, s>>>(p);
+  constexpr int S = BM == 128 ? MOE_STAGES_BM128 : MOE_STAGES_BM256;
+  constexpr int BK = BM == 128 ? MOE_BK_BM128 : MOE_BK_BM256;
+  gemm_bf16_kernel<KIND, BM, S, BK><<<nblk, BM * 2, 0, s>>>(p);
 }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {

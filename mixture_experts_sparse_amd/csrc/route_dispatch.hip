@@ -11,12 +11,12 @@
 // scatter: perm[base + rank] = pair, inv[pair] = row.
 // A launch of one route block (T <= 64) finishes the whole dispatch inline.
 
+#include <utility>
+
 #include "device_common.h"
 #include "moe_internal.h"
 
 namespace moe {
-
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int RT = kRouteTokens;  // tokens per route block
 constexpr int RK = 64;            // K chunk of the router GEMM
@@ -115,204 +115,233 @@ __device__ void write_tile_table(const int* tp, int E, int max_tiles, int32_t* t
 }
 
 // ---------------------------------------------------------------------------
-// route kernel: 512 threads, 64 tokens. Logits: 8 waves as 4 token groups of
-// 16 x 2 column halves; router rows staged through LDS in 64-deep K chunks,
-// double-buffered with the next chunk's loads issued before the MFMAs.
+// route kernel: 256 threads (4 waves), 64 tokens per workgroup.
+//
+// Logits: wave w computes its 16 tokens x all NC columns (E experts, the
+// optional shared-gate row, padding) on bf16 MFMA, keeping them in the MFMA
+// accumulators. x rows and router rows stream through an S-stage pipeline
+// of 32-deep K slices loaded straight into LDS (every thread issues one x
+// load and NCH router loads per stage, clamped in bounds).
+//
+// Select: lane l holds column f * 16 + (l & 15) of token rows (l >> 4) * 4 + i
+// of its wave; each 16-lane group therefore owns one token per round i and
+// runs the top-k with xor-shuffles inside the group.
 // ---------------------------------------------------------------------------
-constexpr int RTHR = 512;
+constexpr int RTHR = 256;
 constexpr int RNW = RTHR / kWave;
+constexpr int RBK = 32;
 
 template <int NCH>
-struct RouteSmem {
-  static constexpr int NC = NCH * 64;  // padded logit columns (E experts + optional shared gate)
-  static constexpr int LDL = NC + 1;   // fp32 logit row stride
-  static constexpr int kStageBytes = 2 * NC * RLD * 2;  // two K-chunk buffers
-  static constexpr int kLogitBytes = RT * LDL * 4;
-  static constexpr int kRawBytes = kStageBytes > kLogitBytes ? kStageBytes : kLogitBytes;
-  static constexpr int kLoads = NC * 8 / RTHR;  // 16-byte staging loads per thread per chunk
+struct RouteCfg {
+  static constexpr int NC = NCH * 64;            // padded logit columns
+  static constexpr int NF = NC / 16;             // 16-column MFMA fragments
+  static constexpr int S = NCH <= 2 ? 8 : 4;     // pipeline stages
+  static constexpr int SX = RT * RBK;            // x elements per stage
+  static constexpr int SEL = SX + NC * RBK;      // elements per stage
+  static constexpr int LPS = 1 + NCH;            // 16-byte loads per thread per stage
 };
 
+// Router logits on bf16 MFMA into acc[f] (fp32), rows/cols as above.
 template <int NCH>
-__device__ void route_logits_bf16(const RouteParams& p, int t0, unsigned char* raw) {
-  using S = RouteSmem<NCH>;
-  constexpr int NF = NCH * 2;  // 16-column fragments per wave (half of NC)
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 3, wn = wave >> 2;
+__device__ void route_logits_bf16(const RouteParams& p, int t0, floatx4_t* acc) {
+  using C = RouteCfg<NCH>;
+  constexpr int S = C::S, SEL = C::SEL, LPS = C::LPS, NF = C::NF;
+  __shared__ __align__(16) uint16_t L0[SEL];
+  __shared__ __align__(16) uint16_t L1[SEL];
+  __shared__ __align__(16) uint16_t L2[SEL];
+  __shared__ __align__(16) uint16_t L3[SEL];
+  __shared__ __align__(16) uint16_t L4[S > 4 ? SEL : 8];
+  __shared__ __align__(16) uint16_t L5[S > 5 ? SEL : 8];
+  __shared__ __align__(16) uint16_t L6[S > 6 ? SEL : 8];
+  __shared__ __align__(16) uint16_t L7[S > 7 ? SEL : 8];
+  auto buf = [&]<int I>() -> uint16_t* {
+    if constexpr (I == 0) return L0;
+    else if constexpr (I == 1) return L1;
+    else if constexpr (I == 2) return L2;
+    else if constexpr (I == 3) return L3;
+    else if constexpr (I == 4) return L4;
+    else if constexpr (I == 5) return L5;
+    else if constexpr (I == 6) return L6;
+    else return L7;
+  };
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wbase = tid & ~63;
   const uint16_t* X = static_cast<const uint16_t*>(p.x);
   const uint16_t* W = static_cast<const uint16_t*>(p.w_router);
   const uint16_t* WS = static_cast<const uint16_t*>(p.w_sgate);
-  uint16_t* stage = reinterpret_cast<uint16_t*>(raw);
-  floatx4_t acc[NF];
+  const int d = p.d;
+  // x slot: row tid / 4 of the block, physical chunk tid % 4
+  const int xr = tid >> 2;
+  const int xchunk = swz_phys_to_logical<RBK>(xr, tid & 3) * 8;
+  const uint16_t* xsrc = X + static_cast<size_t>(t0 + xr < p.T ? t0 + xr : t0) * d;
+  // router slots: rows i * 64 + tid / 4
+  const uint16_t* wsrc[NCH];
+  int wchunk[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int r = i * 64 + xr;
+    wchunk[i] = swz_phys_to_logical<RBK>(r, tid & 3) * 8;
+    const uint16_t* row = W;  // padding columns reload row 0 (never read back)
+    if (r < p.E) row = W + static_cast<size_t>(r) * d;
+    else if (r == p.E && WS != nullptr) row = WS;
+    wsrc[i] = row;
+  }
+  const int nk = (d + RBK - 1) / RBK;
+  const bool ktail = (d % RBK) != 0;
+  auto issue = [&](uint16_t* st, int kc) {
+    const int k0 = min(kc, nk - 1) * RBK;
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(xsrc + min(k0 + xchunk, d - 8)),
+                                     (lds_void_t*)(st + wbase * 8), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(wsrc[i] + min(k0 + wchunk[i], d - 8)),
+                                       (lds_void_t*)(st + C::SX + (i * RTHR + wbase) * 8), 16, 0, 0);
+    }
+  };
+  const int fr = lane & 15, fq = lane >> 4;
+  const int aoff = swz<RBK>(wave * 16 + fr, fq);
+  const int boff = C::SX + swz<RBK>(fr, fq);  // + f * 16 rows
 #pragma unroll
   for (int f = 0; f < NF; ++f) acc[f] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  const int arow = t0 + wm * 16 + (lane & 15);
-  const bool arow_ok = arow < p.T;
-  const int kq = (lane >> 4) * 8;
-
-  // staging rows handled by this thread: c = tid + i * RTHR -> row c / 8, chunk c % 8
-  const uint16_t* srow[S::kLoads];
-#pragma unroll
-  for (int i = 0; i < S::kLoads; ++i) {
-    const int r = (tid + i * RTHR) >> 3;
-    srow[i] = r < p.E ? W + static_cast<size_t>(r) * p.d : (r == p.E ? WS : nullptr);
-  }
-  const int sch = (tid & 7) * 8;
-  u32x4_t pre[S::kLoads];
-  u32x4_t apre[2];
-  auto gload = [&](int k0) {
-    const int kk = k0 + sch;
-#pragma unroll
-    for (int i = 0; i < S::kLoads; ++i) {
-      pre[i] = (srow[i] != nullptr && kk < p.d)
-                   ? *reinterpret_cast<const u32x4_t*>(srow[i] + kk) : u32x4_t{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int ka = k0 + s * 32 + kq;
-      apre[s] = (arow_ok && ka < p.d)
-                    ? *reinterpret_cast<const u32x4_t*>(X + static_cast<size_t>(arow) * p.d + ka)
-                    : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
-  auto sstore = [&](int buf) {
-    uint16_t* st = stage + buf * S::NC * RLD;
-#pragma unroll
-    for (int i = 0; i < S::kLoads; ++i) {
-      const int r = (tid + i * RTHR) >> 3;
-      *reinterpret_cast<u32x4_t*>(st + r * RLD + sch) = pre[i];
-    }
-  };
-  const int nk = (p.d + RK - 1) / RK;
-  gload(0);
-  sstore(0);
-  u32x4_t acur[2] = {apre[0], apre[1]};
-  __syncthreads();
-  for (int kc = 0; kc < nk; ++kc) {
-    const int buf = kc & 1;
-    if (kc + 1 < nk) gload((kc + 1) * RK);
-    const uint16_t* st = stage + buf * S::NC * RLD;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, acur[s]);
+  auto step = [&](int kc, uint16_t* cur, uint16_t* nxt) {
+    wait_stage<(S - 2) * LPS>();
+    stage_barrier();
+    issue(nxt, kc + S - 1);
+    if (kc < nk) {
+      if (ktail && kc == nk - 1) {
+        // zero x's columns past d (the router's clamped duplicates then multiply zeros)
+        if (kc * RBK + xchunk >= d)
+          *reinterpret_cast<u32x4_t*>(cur + tid * 8) = u32x4_t{0u, 0u, 0u, 0u};
+        __syncthreads();
+      }
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(cur + aoff));
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const int col = wn * (S::NC / 2) + f * 16 + (lane & 15);
-        const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(st + col * RLD + s * 32 + kq);
-        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bv), acc[f], 0, 0, 0);
+        const bf16x8_t b = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(cur + boff + f * 16 * RBK));
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[f], 0, 0, 0);
       }
     }
-    if (kc + 1 < nk) {
-      sstore(buf ^ 1);
-      acur[0] = apre[0];
-      acur[1] = apre[1];
+  };
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    ((I < S - 1 ? issue(buf.template operator()<I>(), I) : void()), ...);
+    for (int kb = 0; kb < nk; kb += S) {
+      (step(kb + I, buf.template operator()<I>(), buf.template operator()<(I + S - 1) % S>()), ...);
     }
-    __syncthreads();
-  }
-  float* lg = reinterpret_cast<float*>(raw);
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lg[(wm * 16 + (lane >> 4) * 4 + i) * S::LDL + wn * (S::NC / 2) + f * 16 + (lane & 15)] = acc[f][i];
-    }
-  }
-  __syncthreads();
+  }(std::make_integer_sequence<int, S>{});
+  __syncthreads();  // drain the clamped loads past the last stage
 }
 
+// fp32 router logits by VALU into the same register layout (small layers);
+// the K loop is outermost so every accumulator index is static.
 template <int NCH>
-__device__ void route_logits_f32(const RouteParams& p, int t0, unsigned char* raw) {
-  using S = RouteSmem<NCH>;
-  const int tid = threadIdx.x;
+__device__ void route_logits_f32(const RouteParams& p, int t0, floatx4_t* acc) {
+  constexpr int NF = RouteCfg<NCH>::NF;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* X = static_cast<const float*>(p.x);
   const float* W = static_cast<const float*>(p.w_router);
   const float* WS = static_cast<const float*>(p.w_sgate);
-  float* lg = reinterpret_cast<float*>(raw);
-  for (int idx = tid; idx < RT * S::NC; idx += RTHR) {
-    const int r = idx / S::NC, e = idx - r * S::NC, t = t0 + r;
-    float s = 0.f;
-    const float* wr = e < p.E ? W + static_cast<size_t>(e) * p.d : (e == p.E ? WS : nullptr);
-    if (t < p.T && wr != nullptr) {
-      const float* xr = X + static_cast<size_t>(t) * p.d;
-      for (int i = 0; i < p.d; ++i) s = fmaf(xr[i], wr[i], s);
-    }
-    lg[r * S::LDL + e] = s;
+  const float* wr[NF];
+  const float* xr[4];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int e = f * 16 + (lane & 15);
+    // columns without a router row read row 0 (their logits are never used)
+    wr[f] = e < p.E ? W + static_cast<size_t>(e) * p.d : (e == p.E && WS != nullptr ? WS : W);
+    acc[f] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + wave * 16 + (lane >> 4) * 4 + i;
+    xr[i] = X + static_cast<size_t>(t < p.T ? t : t0) * p.d;
+  }
+  for (int c = 0; c < p.d; ++c) {
+    float xv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[i] = xr[i][c];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const float w = wr[f][c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[f][i] = fmaf(xv[i], w, acc[f][i]);
+    }
+  }
 }
 
-// Top-k, gates, logits and shared-gate outputs for the block's tokens (one
-// wave per token, 8 tokens per wave); the selection also goes to sel[] for
-// the rank pass.
+// Top-k, gates, logits and shared-gate outputs from the accumulator layout;
+// the selection also goes to sel[] for the rank pass. Within a 16-lane
+// group, lane c holds columns f * 16 + c (ascending with f), so a strict >
+// over f keeps the lower index among equal values.
 template <int NCH>
-__device__ void route_select(const RouteParams& p, int t0, const float* lg, uint8_t* sel) {
-  using S = RouteSmem<NCH>;
-  constexpr int TPW = RT / RNW;  // tokens per wave
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ void route_select(const RouteParams& p, int t0, const floatx4_t* acc, uint8_t* sel) {
+  constexpr int NF = RouteCfg<NCH>::NF;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15;
   const int E = p.E, k = p.k;
-  for (int rr = 0; rr < TPW; ++rr) {
-    const int r = wave * TPW + rr, t = t0 + r;
-    if (t >= p.T) break;
-    float v[NCH], ov[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int e = c * 64 + lane;
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave * 16 + (lane >> 4) * 4 + i;  // token row in the block
+    const int t = t0 + r;
+    const bool live = t < p.T;                       // uniform across the 16-lane group
+    float v[NF], ov[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int e = f * 16 + c;
       float val = -INFINITY;
       if (e < E) {
-        val = lg[r * S::LDL + e];
+        val = acc[f][i];
         if (p.bias != nullptr) val += p.bias[e];
-        if (p.logits != nullptr) p.logits[static_cast<size_t>(t) * E + e] = val;
+        if (live && p.logits != nullptr) p.logits[static_cast<size_t>(t) * E + e] = val;
       }
-      v[c] = val;
-      ov[c] = val;
+      v[f] = val;
+      ov[f] = val;
     }
-    if (p.sgate != nullptr && lane == 0) p.sgate[t] = sigmoid_f32(lg[r * S::LDL + E]);
-    float sv[4] = {0.f, 0.f, 0.f, 0.f};
-    int si[4] = {0, 0, 0, 0};
+    if (live && p.sgate != nullptr && c == (E & 15)) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        if (f == (E >> 4)) p.sgate[t] = sigmoid_f32(acc[f][i]);
+    }
+    float m = 0.f, ssel = 0.f;
     for (int j = 0; j < k; ++j) {
       float bv = v[0];
-      int bi = lane;
+      int bi = c;
 #pragma unroll
-      for (int c = 1; c < NCH; ++c) {
-        if (v[c] > bv) { bv = v[c]; bi = c * 64 + lane; }
+      for (int f = 1; f < NF; ++f) {
+        if (v[f] > bv) { bv = v[f]; bi = f * 16 + c; }
       }
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
+      for (int off = 8; off > 0; off >>= 1) {
         const float ovv = __shfl_xor(bv, off, kWave);
         const int oi = __shfl_xor(bi, off, kWave);
         if (ovv > bv || (ovv == bv && oi < bi)) { bv = ovv; bi = oi; }
       }
-      if ((bi & 63) == lane) {
+      if ((bi & 15) == c) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) if (c == (bi >> 6)) v[c] = -INFINITY;
+        for (int f = 0; f < NF; ++f) if (f == (bi >> 4)) v[f] = -INFINITY;
       }
-      if ((j & 63) == lane) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) if (q == (j >> 6)) { sv[q] = bv; si[q] = bi; }
+      if (j == 0) m = bv;  // the largest logit
+      const float ej = expf(bv - m);
+      ssel += ej;
+      if (live && (j & 15) == c) {
+        // un-normalised gate; divided by the denominator below
+        p.ids[static_cast<size_t>(t) * k + j] = bi;
+        p.gates[static_cast<size_t>(t) * k + j] = ej;
+        sel[r * k + j] = static_cast<uint8_t>(bi);
       }
     }
-    const float m = __shfl(sv[0], 0, kWave);  // slot 0 holds the largest logit
-    float es[4];
-    float ssel = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      es[q] = 0.f;
-      if (q * 64 + lane < k) { es[q] = expf(sv[q] - m); ssel += es[q]; }
-    }
-    ssel = wave_sum(ssel);
     float denom = ssel;
     if (p.mode == MOE_SOFTMAX_ALL && !p.renorm) {
       float sall = 0.f;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) if (c * 64 + lane < E) sall += expf(ov[c] - m);
-      denom = wave_sum(sall);
-    }
+      for (int f = 0; f < NF; ++f) if (f * 16 + c < E) sall += expf(ov[f] - m);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int j = q * 64 + lane;
-      if (j < k) {
-        p.ids[static_cast<size_t>(t) * k + j] = si[q];
-        p.gates[static_cast<size_t>(t) * k + j] = es[q] / denom;
-        sel[r * k + j] = static_cast<uint8_t>(si[q]);
+      for (int off = 8; off > 0; off >>= 1) sall += __shfl_xor(sall, off, kWave);
+      denom = sall;
+    }
+    const float inv = 1.0f / denom;
+    if (live) {
+      for (int j = c; j < k; j += 16) {
+        float* g = p.gates + static_cast<size_t>(t) * k + j;
+        *g = *g * inv;
       }
     }
   }
@@ -320,17 +349,16 @@ __device__ void route_select(const RouteParams& p, int t0, const float* lg, uint
 
 template <int NCH, bool BF16>
 __global__ __launch_bounds__(RTHR) void route_kernel(RouteParams p) {
-  using S = RouteSmem<NCH>;
-  __shared__ __align__(16) unsigned char raw[S::kRawBytes];
   __shared__ uint8_t sel[RT * kMaxE];
   __shared__ int wh[RNW][kMaxE];
   __shared__ int run[kMaxE + 1];
   __shared__ int scan_a[kMaxE + 1];
   __shared__ int scan_b[kMaxE + 1];
   const int t0 = blockIdx.x * RT;
-  if constexpr (BF16) route_logits_bf16<NCH>(p, t0, raw);
-  else route_logits_f32<NCH>(p, t0, raw);
-  route_select<NCH>(p, t0, reinterpret_cast<const float*>(raw), sel);
+  floatx4_t acc[RouteCfg<NCH>::NF];
+  if constexpr (BF16) route_logits_bf16<NCH>(p, t0, acc);
+  else route_logits_f32<NCH>(p, t0, acc);
+  route_select<NCH>(p, t0, acc, sel);
   if (p.blk_hist == nullptr && p.counts == nullptr) return;
   __syncthreads();
   const int nt = min(RT, p.T - t0);
@@ -388,7 +416,7 @@ __global__ __launch_bounds__(256) void rank_kernel(RankParams p) {
 constexpr int kScanLdsInts = 32768;  // 128 KiB
 
 __global__ __launch_bounds__(1024) void scan_kernel(ScanParams p) {
-  extern __shared__ int hl[];  // [NB * E] when it fits
+  extern __shared__ __align__(16) int hl[];  // [NB * E] when it fits
   __shared__ int part[1024];
   __shared__ int cnt[kMaxE + 1];
   __shared__ int off[kMaxE + 1];
@@ -398,19 +426,24 @@ __global__ __launch_bounds__(1024) void scan_kernel(ScanParams p) {
   const bool in_lds = n <= kScanLdsInts;
   int* h = in_lds ? hl : p.blk_hist;
   if (in_lds) {
-    for (int base = tid; base < n; base += 8 * 1024) {
-      int v[8];
+    // 16-byte loads, all issued before any is used (one round trip when
+    // n <= 4 * 8 * 1024), then the scalar tail
+    const int n4 = n >> 2;
+    const int4* src4 = reinterpret_cast<const int4*>(p.blk_hist);
+    for (int base = tid; base < n4; base += 8 * 1024) {
+      int4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int i = base + u * 1024;
-        v[u] = i < n ? p.blk_hist[i] : 0;
+        v[u] = i < n4 ? src4[i] : int4{0, 0, 0, 0};
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int i = base + u * 1024;
-        if (i < n) hl[i] = v[u];
+        if (i < n4) reinterpret_cast<int4*>(hl)[i] = v[u];
       }
     }
+    for (int i = (n4 << 2) + tid; i < n; i += 1024) hl[i] = p.blk_hist[i];
     __syncthreads();
   }
   int G = 1024 / E;
