@@ -39,7 +39,7 @@
  *  - Errors: MOE_ERR_INVALID_ARG (NULL required pointer; T < 0; d, h or
  *    E <= 0; top_k < 1 or top_k > E; bad enum), MOE_ERR_UNSUPPORTED (d, h or
  *    shared_h not a multiple of 8; E > MOE_MAX_EXPERTS; a pointer not 16-byte
- *    aligned), MOE_ERR_WORKSPACE (ws too small or not 256-byte aligned),
+ *    aligned; T*k*d, T*k*h, T*d or T*shared_h at least 2^30 elements), MOE_ERR_WORKSPACE (ws too small or not 256-byte aligned),
  *    MOE_ERR_HIP (a launch failed).
  */
 #ifndef MOE_H

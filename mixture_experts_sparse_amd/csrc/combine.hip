@@ -1,5 +1,6 @@
 // Gate-weighted combine back to token order (gfx950):
-//   out[t] = sum_{j<k} gates[t, j] * y[inv[t*k + j]] (+ shared[t])
+//   out[t] = sum_{j<k} gates[t, j] * y[inv[t*k + j]] (+ s_t * shared[t])
+// where s_t is the shared expert's sigmoid gate (1 when ungated)
 // ("Tutorial 11: Mixture of Experts (MoE)", section 3, step 3, and section 4,
 // step 5). An additive gather in fixed slot order with fp32 accumulation,
 // rounded once to the activation dtype; each thread owns 16 contiguous bytes
@@ -33,12 +34,13 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineParams p) {
     }
   }
   if (p.shared != nullptr) {
+    const float sc = p.shared_scale != nullptr ? p.shared_scale[t] : 1.0f;
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.shared) +
                                                          static_cast<size_t>(t) * p.d + c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += __uint_as_float(v[i] << 16);
-      acc[2 * i + 1] += __uint_as_float(v[i] & 0xFFFF0000u);
+      acc[2 * i] = fmaf(sc, __uint_as_float(v[i] << 16), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(sc, __uint_as_float(v[i] & 0xFFFF0000u), acc[2 * i + 1]);
     }
   }
   u32x4_t o;
@@ -67,12 +69,46 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(CombineParams p) {
     for (int i = 0; i < 4; ++i) acc[i] = fmaf(g, v[i], acc[i]);
   }
   if (p.shared != nullptr) {
+    const float sc = p.shared_scale != nullptr ? p.shared_scale[t] : 1.0f;
     const floatx4_t v = *reinterpret_cast<const floatx4_t*>(static_cast<const float*>(p.shared) +
                                                             static_cast<size_t>(t) * p.d + c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += v[i];
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, v[i], acc[i]);
   }
   *reinterpret_cast<floatx4_t*>(static_cast<float*>(p.out) + static_cast<size_t>(t) * p.d + c) = acc;
+}
+
+// rows[t, :] *= scale[t]: one thread per 16 bytes, product rounded once.
+__global__ __launch_bounds__(256) void scale_rows_kernel(ScaleRowsParams p) {
+  const int per = p.dtype == MOE_BF16 ? 8 : 4;
+  const int cpr = p.d / per;
+  const long long item = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (item >= static_cast<long long>(p.T) * cpr) return;
+  const int t = static_cast<int>(item / cpr);
+  const float sc = p.scale[t];
+  u32x4_t* q = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.rows) + item * 16);
+  u32x4_t v = *q;
+  if (p.dtype == MOE_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = sc * __uint_as_float(v[i] << 16);
+      const float hi = sc * __uint_as_float(v[i] & 0xFFFF0000u);
+      v[i] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(sc * __uint_as_float(v[i]));
+  }
+  *q = v;
+}
+
+hipError_t launch_scale_rows(const ScaleRowsParams& p, hipStream_t s) {
+  const int per = p.dtype == MOE_BF16 ? 8 : 4;
+  const long long items = static_cast<long long>(p.T) * (p.d / per);
+  const long long nblk = (items + 255) / 256;
+  if (nblk <= 0) return hipSuccess;
+  scale_rows_kernel<<<static_cast<unsigned>(nblk), 256, 0, s>>>(p);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {

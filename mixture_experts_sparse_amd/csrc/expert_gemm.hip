@@ -297,11 +297,8 @@ __global__ __launch_bounds__(BM * 2) void gemm_bf16_kernel(GemmParams p) {
         for (int nf = 0; nf < 2; ++nf)
           Cw[rc * WLD + nf * 16 + fr] = f32_to_bf16(silu_f32(acc[mf][nf][i]) * acc[mf][nf + 2][i]);
       } else {
-        const int rt = wm * 64 + mf * 16 + rc;
-        const float sc = (shared && p.srow_scale != nullptr && rt < ti.nrows)
-                             ? p.srow_scale[ti.row0 + rt] : 1.0f;
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf) Cw[rc * WLD + nf * 16 + fr] = f32_to_bf16(acc[mf][nf][i] * sc);
+        for (int nf = 0; nf < NF; ++nf) Cw[rc * WLD + nf * 16 + fr] = f32_to_bf16(acc[mf][nf][i]);
       }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
@@ -364,7 +361,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     const float* wd = B0 + static_cast<size_t>(c) * K;
     float s = 0.f;
     for (int i = 0; i < K; ++i) s = fmaf(a[i], wd[i], s);
-    if (shared && p.srow_scale != nullptr) s *= p.srow_scale[r];
     OUT[static_cast<size_t>(r) * N + c] = s;
   }
 }

@@ -33,9 +33,10 @@ moe_status check_cfg(const moe_config* c) {
   if (c->shared_gate && c->shared_h == 0) return MOE_ERR_INVALID_ARG;
   if (c->E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
   if (c->d % 8 != 0 || c->h % 8 != 0 || c->shared_h % 8 != 0) return MOE_ERR_UNSUPPORTED;
-  // int32 row/element indices inside the kernels
+  // int32 row/element indices inside the kernels, and byte offsets of the
+  // bf16 outputs below 2^31 (buffer stores mask lanes with offset 2^31)
   const long long P = static_cast<long long>(c->T) * c->top_k;
-  const long long big = 1LL << 31;
+  const long long big = 1LL << 30;
   if (P * c->d >= big || P * c->h >= big || static_cast<long long>(c->T) * c->d >= big ||
       static_cast<long long>(c->T) * (c->shared_h > 0 ? c->shared_h : 1) >= big)
     return MOE_ERR_UNSUPPORTED;
@@ -198,12 +199,11 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* ids, int32_t* coun
   RankParams rp{ids, c.T, c.E, c.top_k, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank)};
   MOE_HIP(launch_rank(rp, s));
   const int tm = choose_tile_m(c.T * c.top_k, c.E);
-  ScanParams sp{at<int32_t>(ws, L.blk_hist), ceil_div(c.T, kRouteTokens), c.E, c.T * c.top_k,
-                max_m_tiles(c.T * c.top_k, c.E, tm), tm, counts, offsets, at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0),
-                at<int32_t>(ws, L.meta)};
+  ScanParams sp{at<int32_t>(ws, L.blk_hist), ceil_div(c.T, kRouteTokens), c.E, counts};
   MOE_HIP(launch_scan(sp, s));
   ScatterParams xp{ids, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank), c.T, c.E,
-                   c.top_k, perm, inv};
+                   c.top_k, perm, inv, counts, offsets, max_m_tiles(c.T * c.top_k, c.E, tm), tm,
+                   at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0), at<int32_t>(ws, L.meta)};
   MOE_HIP(launch_scatter(xp, s));
   return MOE_OK;
 }
@@ -332,8 +332,12 @@ moe_status moe_shared_expert(const moe_config* cfg, const void* x, const void* w
   MOE_HIP(launch_gemm(g, s));
   GemmParams g2 = g;
   g2.kind = 1; g2.sa = act_s; g2.sK = c.shared_h; g2.sb0 = ws_down; g2.sb1 = nullptr;
-  g2.sN = c.d; g2.sout = s_out; g2.srow_scale = sg;
+  g2.sN = c.d; g2.sout = s_out;
   MOE_HIP(launch_gemm(g2, s));
+  if (sg != nullptr) {
+    ScaleRowsParams sp{s_out, sg, c.T, c.d, c.dtype};
+    MOE_HIP(launch_scale_rows(sp, s));
+  }
   return MOE_OK;
 }
 
@@ -344,7 +348,7 @@ moe_status moe_combine(const moe_config* cfg, const void* y, const int32_t* inv,
   if (c.T == 0) return MOE_OK;
   MOE_TRY(need(y)); MOE_TRY(need(inv)); MOE_TRY(need(gates)); MOE_TRY(maybe(shared));
   MOE_TRY(need(out));
-  CombineParams p{y, inv, gates, shared, out, c.T, c.d, c.top_k, c.dtype, c.T * c.top_k};
+  CombineParams p{y, inv, gates, shared, nullptr, out, c.T, c.d, c.top_k, c.dtype, c.T * c.top_k};
   MOE_HIP(launch_combine(p, as_stream(stream)));
   return MOE_OK;
 }
@@ -409,12 +413,11 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
   MOE_HIP(launch_route(rp, c.dtype, s));
   MOE_HIP(mark(1));
   if (NB > 1) {
-    ScanParams sp{at<int32_t>(ws, L.blk_hist), NB, c.E, c.T * c.top_k,
-                  max_m_tiles(c.T * c.top_k, c.E, tm), tm, counts_p, offsets,
-                  at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0), at<int32_t>(ws, L.meta)};
+    ScanParams sp{at<int32_t>(ws, L.blk_hist), NB, c.E, counts_p};
     MOE_HIP(launch_scan(sp, s));
     ScatterParams xp{ids_p, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank), c.T, c.E,
-                     c.top_k, perm, inv};
+                     c.top_k, perm, inv, counts_p, offsets, max_m_tiles(c.T * c.top_k, c.E, tm), tm,
+                     at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0), at<int32_t>(ws, L.meta)};
     MOE_HIP(launch_scatter(xp, s));
   }
   MOE_HIP(mark(2));
@@ -435,11 +438,11 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
   g2.a = act; g2.K = c.h; g2.b0 = w->w_down; g2.N = c.d; g2.out = y;
   if (c.shared_h > 0) {
     g2.shared_T = c.T; g2.sa = act_s; g2.sK = c.shared_h; g2.sb0 = w->ws_down;
-    g2.sN = c.d; g2.sout = ys; g2.srow_scale = sg;
+    g2.sN = c.d; g2.sout = ys;
   }
   MOE_HIP(launch_gemm(g2, s));
   MOE_HIP(mark(4));
-  CombineParams cp{y, inv, gates_p, c.shared_h > 0 ? ys : nullptr, out, c.T, c.d, c.top_k,
+  CombineParams cp{y, inv, gates_p, c.shared_h > 0 ? ys : nullptr, sg, out, c.T, c.d, c.top_k,
                     c.dtype, c.T * c.top_k};
   MOE_HIP(launch_combine(cp, s));
   MOE_HIP(mark(5));

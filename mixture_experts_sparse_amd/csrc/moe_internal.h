@@ -78,16 +78,15 @@ struct RankParams {
   int32_t* lrank;
 };
 
+// Per-expert exclusive scan over route blocks (in place) and expert counts.
 struct ScanParams {
-  int32_t* blk_hist;  // in: per-block counts; out: per-block base rows
-  int NB, E, P, max_tiles, tile_m;
-  int32_t* counts;
-  int32_t* offsets;
-  int32_t* tile_e;
-  int32_t* exp_tile0;
-  int32_t* meta;
+  int32_t* blk_hist;  // in: per-block counts; out: per-block base row within the expert
+  int NB, E;
+  int32_t* counts;    // [E]
 };
 
+// perm / inv from the per-block bases; every workgroup rebuilds the expert
+// offsets from counts, workgroup 0 also writes offsets and the tile table.
 struct ScatterParams {
   const int32_t* ids;
   const int32_t* blk_base;
@@ -95,6 +94,12 @@ struct ScatterParams {
   int T, E, k;
   int32_t* perm;
   int32_t* inv;
+  const int32_t* counts;
+  int32_t* offsets;
+  int max_tiles, tile_m;
+  int32_t* tile_e;
+  int32_t* exp_tile0;
+  int32_t* meta;
 };
 
 // Tile table from offsets alone (standalone gate_up / down / expert_ffn).
@@ -139,7 +144,6 @@ struct GemmParams {
   const void* sb1;        // ws_up or unused
   int sN;                 // hs or d
   void* sout;             // act_s [T, hs] or ys [T, d]
-  const float* srow_scale;  // down only: per-row scale of the shared output (sgate) or null
 };
 
 struct CombineParams {
@@ -147,9 +151,17 @@ struct CombineParams {
   const int32_t* inv;   // [P]
   const float* gates;   // [T, k]
   const void* shared;   // [T, d] or null
+  const float* shared_scale;  // [T] per-token scale of shared (sigmoid gate) or null
   void* out;            // [T, d]
   int T, d, k, dtype;
   int y_rows;           // rows of y (P): row indices are clamped to it
+};
+
+// In-place row scaling: rows[t, :] *= scale[t] (rounded once to dtype).
+struct ScaleRowsParams {
+  void* rows;           // [T, d]
+  const float* scale;   // [T]
+  int T, d, dtype;
 };
 
 struct RowDotSigmoidParams {
@@ -166,6 +178,7 @@ hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
 hipError_t launch_tiles(const TilesParams& p, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+hipError_t launch_scale_rows(const ScaleRowsParams& p, hipStream_t s);
 hipError_t launch_rowdot_sigmoid(const RowDotSigmoidParams& p, hipStream_t s);
 
 }  // namespace moe

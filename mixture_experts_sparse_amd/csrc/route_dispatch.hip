@@ -6,9 +6,10 @@
 //   (MoE)", section 2 "The Router"; "Small models, sparse experts", section
 //   "How it works", step 3), and the first half of the counting sort:
 //   per-route-block expert histograms and stable in-block ranks.
-// scan: per-expert exclusive scan over route blocks -> counts, offsets,
-//   per-block base rows and the grouped-GEMM tile table.
-// scatter: perm[base + rank] = pair, inv[pair] = row.
+// scan: per-expert exclusive scan over route blocks -> counts and each
+//   block's first row inside its expert's group.
+// scatter: offsets (exclusive scan of counts), the grouped-GEMM tile table,
+//   perm[offset + block base + rank] = pair, inv[pair] = row.
 // A launch of one route block (T <= 64) finishes the whole dispatch inline.
 
 #include <utility>
@@ -115,143 +116,175 @@ __device__ void write_tile_table(const int* tp, int E, int max_tiles, int32_t* t
 }
 
 // ---------------------------------------------------------------------------
-// route kernel: 256 threads (4 waves), 64 tokens per workgroup.
+// route kernel: 512 threads (8 waves), 64 tokens per workgroup.
 //
-// Logits: wave w computes its 16 tokens x all NC columns (E experts, the
-// optional shared-gate row, padding) on bf16 MFMA, keeping them in the MFMA
-// accumulators. x rows and router rows stream through an S-stage pipeline
-// of 32-deep K slices loaded straight into LDS (every thread issues one x
-// load and NCH router loads per stage, clamped in bounds).
+// Logits: wave w computes token rows 16 * (w % 4) .. + 15 against one half of
+// the NC columns (E experts, the optional shared-gate row, padding), half
+// w / 4, on bf16 MFMA. K is streamed in 32-deep slices by direct
+// global->LDS loads through two rings: waves 0-3 stream the block's x rows
+// (read once, from HBM) RX - 1 slices ahead, waves 4-7 stream the router
+// rows (shared by every workgroup, so mostly L2 hits) RR - 1 slices ahead.
+// A wave's outstanding-load counter retires in issue order, so giving each
+// stream its own waves lets the HBM stream run far ahead of the L2 one.
 //
-// Select: lane l holds column f * 16 + (l & 15) of token rows (l >> 4) * 4 + i
-// of its wave; each 16-lane group therefore owns one token per round i and
-// runs the top-k with xor-shuffles inside the group.
+// The logits then go through LDS (one padded fp32 row per token) and the
+// selection runs on 16-lane groups, one token per group and round: lane c
+// holds columns f * 16 + c.
 // ---------------------------------------------------------------------------
-constexpr int RTHR = 256;
+constexpr int RTHR = 512;
 constexpr int RNW = RTHR / kWave;
 constexpr int RBK = 32;
 
 template <int NCH>
 struct RouteCfg {
   static constexpr int NC = NCH * 64;            // padded logit columns
-  static constexpr int NF = NC / 16;             // 16-column MFMA fragments
-  static constexpr int S = NCH <= 2 ? 8 : 4;     // pipeline stages
-  static constexpr int SX = RT * RBK;            // x elements per stage
-  static constexpr int SEL = SX + NC * RBK;      // elements per stage
-  static constexpr int LPS = 1 + NCH;            // 16-byte loads per thread per stage
+  static constexpr int NF = NC / 16;             // 16-column fragments of a row
+  static constexpr int NH = NC / 2;              // columns per half
+  static constexpr int NF2 = NH / 16;            // fragments per wave
+  static constexpr int SX = RT * RBK;            // x elements per slice
+  static constexpr int SW = NC * RBK;            // router elements per slice
+  static constexpr int RR = NCH <= 4 ? 4 : 3;    // router ring slots
+  static constexpr int RX = 16;                  // x ring slots
+  static constexpr int LX = SX / 8 / 256;        // 16-byte x loads per x-wave thread per slice
+  static constexpr int LW = SW / 8 / 256;        // router loads per router-wave thread per slice
+  static constexpr int LGLD = NC + 4;            // logit row stride in LDS (floats)
+  // LDS after the logits: selections, per-wave histograms, running counts
+  static constexpr int CARVE = RT * kMaxE + RNW * kMaxE * 4 + 3 * (kMaxE + 1) * 4;
+  static constexpr int XBYTES = RX * SX * 2 > CARVE ? RX * SX * 2 : CARVE;
+  static constexpr int LGBYTES = RT * LGLD * 4;
+  static constexpr int WBYTES = RR * SW * 2 > LGBYTES ? RR * SW * 2 : LGBYTES;
 };
 
-// Router logits on bf16 MFMA into acc[f] (fp32), rows/cols as above.
+// LDS destination of a direct global->LDS load, hidden from the compiler's
+// load-counter tracking: every wait on these loads is explicit and followed
+// by a workgroup barrier before any wave reads the data.
+__device__ __forceinline__ lds_void_t* lds_untracked(uint16_t* q) {
+  lds_void_t* r = (lds_void_t*)q;
+  asm volatile("" : "+s"(r));
+  return r;
+}
+
+// Router logits on bf16 MFMA: acc[f][i] = logit of token row
+// 16 * (w % 4) + 4 * (lane / 16) + i, column NH * (w / 4) + 16 * f + lane % 16.
 template <int NCH>
-__device__ void route_logits_bf16(const RouteParams& p, int t0, floatx4_t* acc) {
+__device__ void route_logits_bf16(const RouteParams& p, int t0, floatx4_t* acc, uint16_t* Xr,
+                                  uint16_t* Wr) {
   using C = RouteCfg<NCH>;
-  constexpr int S = C::S, SEL = C::SEL, LPS = C::LPS, NF = C::NF;
-  __shared__ __align__(16) uint16_t L0[SEL];
-  __shared__ __align__(16) uint16_t L1[SEL];
-  __shared__ __align__(16) uint16_t L2[SEL];
-  __shared__ __align__(16) uint16_t L3[SEL];
-  __shared__ __align__(16) uint16_t L4[S > 4 ? SEL : 8];
-  __shared__ __align__(16) uint16_t L5[S > 5 ? SEL : 8];
-  __shared__ __align__(16) uint16_t L6[S > 6 ? SEL : 8];
-  __shared__ __align__(16) uint16_t L7[S > 7 ? SEL : 8];
-  auto buf = [&]<int I>() -> uint16_t* {
-    if constexpr (I == 0) return L0;
-    else if constexpr (I == 1) return L1;
-    else if constexpr (I == 2) return L2;
-    else if constexpr (I == 3) return L3;
-    else if constexpr (I == 4) return L4;
-    else if constexpr (I == 5) return L5;
-    else if constexpr (I == 6) return L6;
-    else return L7;
-  };
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wbase = tid & ~63;
+  constexpr int RX = C::RX, RR = C::RR, LX = C::LX, LW = C::LW, NF2 = C::NF2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool xw = wave < 4;                  // x-stream waves
+  const int lt = tid & 255;                  // thread index within the stream
+  const int lwb = (wave & 3) * 64;
   const uint16_t* X = static_cast<const uint16_t*>(p.x);
   const uint16_t* W = static_cast<const uint16_t*>(p.w_router);
   const uint16_t* WS = static_cast<const uint16_t*>(p.w_sgate);
   const int d = p.d;
-  // x slot: row tid / 4 of the block, physical chunk tid % 4
-  const int xr = tid >> 2;
-  const int xchunk = swz_phys_to_logical<RBK>(xr, tid & 3) * 8;
-  const uint16_t* xsrc = X + static_cast<size_t>(t0 + xr < p.T ? t0 + xr : t0) * d;
-  // router slots: rows i * 64 + tid / 4
-  const uint16_t* wsrc[NCH];
-  int wchunk[NCH];
+  constexpr int LM = LX > LW ? LX : LW;
+  // load i of a stream thread fills slot chunk q = i * 256 + lt: row q / 4,
+  // physical chunk q % 4 (the swizzle picks the logical K chunk)
+  const uint16_t* src[LM];
+  int chunk[LM];
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int r = i * 64 + xr;
-    wchunk[i] = swz_phys_to_logical<RBK>(r, tid & 3) * 8;
-    const uint16_t* row = W;  // padding columns reload row 0 (never read back)
-    if (r < p.E) row = W + static_cast<size_t>(r) * d;
-    else if (r == p.E && WS != nullptr) row = WS;
-    wsrc[i] = row;
+  for (int i = 0; i < LM; ++i) {
+    const int q = i * 256 + lt;
+    const int r = q >> 2;
+    chunk[i] = swz_phys_to_logical<RBK>(r, q & 3) * 8;
+    if (xw) {
+      src[i] = X + static_cast<size_t>(t0 + r < p.T ? t0 + r : t0) * d;
+    } else {
+      const uint16_t* row = W;  // padding columns reload row 0 (never read back)
+      if (r < p.E) row = W + static_cast<size_t>(r) * d;
+      else if (r == p.E && WS != nullptr) row = WS;
+      src[i] = row;
+    }
   }
   const int nk = (d + RBK - 1) / RBK;
   const bool ktail = (d % RBK) != 0;
-  auto issue = [&](uint16_t* st, int kc) {
+  // every lane issues every load (clamped in bounds), so each wave's count
+  // of outstanding loads is the same on every path
+  auto issue = [&]<int L>(uint16_t* slot, int kc) {
     const int k0 = min(kc, nk - 1) * RBK;
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(xsrc + min(k0 + xchunk, d - 8)),
-                                     (lds_void_t*)(st + wbase * 8), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(wsrc[i] + min(k0 + wchunk[i], d - 8)),
-                                       (lds_void_t*)(st + C::SX + (i * RTHR + wbase) * 8), 16, 0, 0);
-    }
+    for (int i = 0; i < L; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(src[i] + min(k0 + chunk[i], d - 8)),
+                                       lds_untracked(slot + (i * 256 + lwb) * 8), 16, 0, 0);
   };
   const int fr = lane & 15, fq = lane >> 4;
-  const int aoff = swz<RBK>(wave * 16 + fr, fq);
-  const int boff = C::SX + swz<RBK>(fr, fq);  // + f * 16 rows
+  const int aoff = swz<RBK>((wave & 3) * 16 + fr, fq);
+  const int boff = swz<RBK>((wave >> 2) * C::NH + fr, fq);  // + f * 16 rows
 #pragma unroll
-  for (int f = 0; f < NF; ++f) acc[f] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  auto step = [&](int kc, uint16_t* cur, uint16_t* nxt) {
-    wait_stage<(S - 2) * LPS>();
+  for (int f = 0; f < NF2; ++f) acc[f] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  if (xw) {
+#pragma unroll
+    for (int st = 0; st < RX - 1; ++st) issue.template operator()<LX>(Xr + st * C::SX, st);
+  } else {
+#pragma unroll
+    for (int st = 0; st < RR - 1; ++st) issue.template operator()<LW>(Wr + st * C::SW, st);
+  }
+  int cx = 0, cw = 0, ix = RX - 1, iw = RR - 1;
+  for (int kc = 0; kc < nk; ++kc) {
+    // slice kc is in x slot cx / router slot cw once this wave's own loads
+    // of it are done (all but the newer slices') and every wave has passed
+    // the barrier
+    if (xw) wait_stage<(RX - 2) * LX>();
+    else wait_stage<(RR - 2) * LW>();
     stage_barrier();
-    issue(nxt, kc + S - 1);
-    if (kc < nk) {
-      if (ktail && kc == nk - 1) {
-        // zero x's columns past d (the router's clamped duplicates then multiply zeros)
-        if (kc * RBK + xchunk >= d)
-          *reinterpret_cast<u32x4_t*>(cur + tid * 8) = u32x4_t{0u, 0u, 0u, 0u};
-        __syncthreads();
-      }
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(cur + aoff));
+    if (xw) issue.template operator()<LX>(Xr + ix * C::SX, kc + RX - 1);
+    else issue.template operator()<LW>(Wr + iw * C::SW, kc + RR - 1);
+    ix = ix + 1 == RX ? 0 : ix + 1;
+    iw = iw + 1 == RR ? 0 : iw + 1;
+    uint16_t* xs = Xr + cx * C::SX;
+    const uint16_t* ws = Wr + cw * C::SW;
+    if (ktail && kc == nk - 1) {
+      // zero x's columns past d (the router's clamped duplicates then multiply zeros)
+      if (xw) {
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const bf16x8_t b = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const u32x4_t*>(cur + boff + f * 16 * RBK));
-        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[f], 0, 0, 0);
+        for (int i = 0; i < LX; ++i)
+          if (kc * RBK + chunk[i] >= d)
+            *reinterpret_cast<u32x4_t*>(xs + (i * 256 + lt) * 8) = u32x4_t{0u, 0u, 0u, 0u};
       }
+      wait_stage<63>();
+      stage_barrier();
     }
-  };
-  [&]<int... I>(std::integer_sequence<int, I...>) {
-    ((I < S - 1 ? issue(buf.template operator()<I>(), I) : void()), ...);
-    for (int kb = 0; kb < nk; kb += S) {
-      (step(kb + I, buf.template operator()<I>(), buf.template operator()<(I + S - 1) % S>()), ...);
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + aoff));
+#pragma unroll
+    for (int f = 0; f < NF2; ++f) {
+      const bf16x8_t b = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const u32x4_t*>(ws + boff + f * 16 * RBK));
+      acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[f], 0, 0, 0);
     }
-  }(std::make_integer_sequence<int, S>{});
-  __syncthreads();  // drain the clamped loads past the last stage
+    cx = cx + 1 == RX ? 0 : cx + 1;
+    cw = cw + 1 == RR ? 0 : cw + 1;
+  }
+  // the clamped loads past the last slice are drained before the rings'
+  // LDS is reused
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
 // fp32 router logits by VALU into the same register layout (small layers);
 // the K loop is outermost so every accumulator index is static.
 template <int NCH>
 __device__ void route_logits_f32(const RouteParams& p, int t0, floatx4_t* acc) {
-  constexpr int NF = RouteCfg<NCH>::NF;
+  using C = RouteCfg<NCH>;
+  constexpr int NF2 = C::NF2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* X = static_cast<const float*>(p.x);
   const float* W = static_cast<const float*>(p.w_router);
   const float* WS = static_cast<const float*>(p.w_sgate);
-  const float* wr[NF];
+  const float* wr[NF2];
   const float* xr[4];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int e = f * 16 + (lane & 15);
+  for (int f = 0; f < NF2; ++f) {
+    const int e = (wave >> 2) * C::NH + f * 16 + (lane & 15);
     // columns without a router row read row 0 (their logits are never used)
     wr[f] = e < p.E ? W + static_cast<size_t>(e) * p.d : (e == p.E && WS != nullptr ? WS : W);
     acc[f] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int t = t0 + wave * 16 + (lane >> 4) * 4 + i;
+    const int t = t0 + (wave & 3) * 16 + (lane >> 4) * 4 + i;
     xr[i] = X + static_cast<size_t>(t < p.T ? t : t0) * p.d;
   }
   for (int c = 0; c < p.d; ++c) {
@@ -259,7 +292,7 @@ __device__ void route_logits_f32(const RouteParams& p, int t0, floatx4_t* acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) xv[i] = xr[i][c];
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
+    for (int f = 0; f < NF2; ++f) {
       const float w = wr[f][c];
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[f][i] = fmaf(xv[i], w, acc[f][i]);
@@ -267,81 +300,145 @@ __device__ void route_logits_f32(const RouteParams& p, int t0, floatx4_t* acc) {
   }
 }
 
-// Top-k, gates, logits and shared-gate outputs from the accumulator layout;
-// the selection also goes to sel[] for the rank pass. Within a 16-lane
-// group, lane c holds columns f * 16 + c (ascending with f), so a strict >
-// over f keeps the lower index among equal values.
+// Accumulators -> one padded fp32 row of logits per token in LDS.
 template <int NCH>
-__device__ void route_select(const RouteParams& p, int t0, const floatx4_t* acc, uint8_t* sel) {
+__device__ __forceinline__ void store_logits(const floatx4_t* acc, float* Lg) {
+  using C = RouteCfg<NCH>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int f = 0; f < C::NF2; ++f)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (wave & 3) * 16 + (lane >> 4) * 4 + i;
+      Lg[r * C::LGLD + (wave >> 2) * C::NH + f * 16 + (lane & 15)] = acc[f][i];
+    }
+}
+
+// Selection keys: the float's bits mapped to an unsigned integer of the same
+// order in the high word, the bitwise complement of the expert index in the
+// low word, so the largest key is the largest logit and, among equal
+// logits, the lower expert index. 0 (below every key) marks no candidate.
+__device__ __forceinline__ uint64_t sel_key(float v, int e) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(o) << 32) | static_cast<uint32_t>(~e);
+}
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t o = static_cast<uint32_t>(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ int key_index(uint64_t key) {
+  return static_cast<int>(~static_cast<uint32_t>(key));
+}
+// max of a 64-bit key with its DPP partner inside each row of 16 lanes
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max(uint64_t a) {
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(a)), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(a >> 32)), CTRL, 0xF, 0xF, false);
+  const uint64_t b = (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+  return b > a ? b : a;
+}
+// Maximum over the 16 lanes of each row: swap neighbours, swap pairs
+// (quad permutations), then mirror within 8 lanes and within 16 lanes;
+// every lane ends with the row's maximum.
+__device__ __forceinline__ uint64_t row16_max(uint64_t a) {
+  a = dpp_max<0xB1>(a);   // quad_perm [1,0,3,2]
+  a = dpp_max<0x4E>(a);   // quad_perm [2,3,0,1]
+  a = dpp_max<0x141>(a);  // row_half_mirror
+  a = dpp_max<0x140>(a);  // row_mirror
+  return a;
+}
+
+// Router bias of this lane's columns (f * 16 + lane % 16), loaded before
+// the logits so that no load is outstanding in the selection.
+template <int NCH>
+__device__ __forceinline__ void load_bias(const RouteParams& p, float* bias) {
   constexpr int NF = RouteCfg<NCH>::NF;
+  const int c = threadIdx.x & 15;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) bias[f] = 0.f;
+  if (p.bias != nullptr) {
+#pragma unroll
+    // columns past E read bias[E - 1]; their logits are never used
+    for (int f = 0; f < NF; ++f) bias[f] = p.bias[min(f * 16 + c, p.E - 1)];
+  }
+}
+
+// Top-k, gates, logits and shared-gate outputs from the logit rows in LDS;
+// the selection also goes to sel[] for the rank pass. 16-lane group g of the
+// workgroup owns token rows g and g + 32.
+template <int NCH>
+__device__ void route_select(const RouteParams& p, int t0, const float* Lg, const float* bias,
+                             uint8_t* sel) {
+  using C = RouteCfg<NCH>;
+  constexpr int NF = C::NF;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15;
   const int E = p.E, k = p.k;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wave * 16 + (lane >> 4) * 4 + i;  // token row in the block
+  for (int rnd = 0; rnd < 2; ++rnd) {
+    const int r = rnd * 32 + wave * 4 + (lane >> 4);  // token row in the block
     const int t = t0 + r;
-    const bool live = t < p.T;                       // uniform across the 16-lane group
-    float v[NF], ov[NF];
+    const bool live = t < p.T;                          // uniform across the 16-lane group
+    const float* row = Lg + r * C::LGLD;
+    float v[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int e = f * 16 + c;
       float val = -INFINITY;
       if (e < E) {
-        val = acc[f][i];
-        if (p.bias != nullptr) val += p.bias[e];
+        val = row[e] + bias[f];
         if (live && p.logits != nullptr) p.logits[static_cast<size_t>(t) * E + e] = val;
       }
-      v[f] = val;
-      ov[f] = val;
+      v[f] = val + 0.0f;  // -0 -> +0: equal logits must get equal keys
     }
-    if (live && p.sgate != nullptr && c == (E & 15)) {
+    if (live && p.sgate != nullptr && c == 0) p.sgate[t] = sigmoid_f32(row[E]);
+    uint64_t key[NF];
 #pragma unroll
-      for (int f = 0; f < NF; ++f)
-        if (f == (E >> 4)) p.sgate[t] = sigmoid_f32(acc[f][i]);
-    }
+    for (int f = 0; f < NF; ++f) key[f] = f * 16 + c < E ? sel_key(v[f], f * 16 + c) : 0ull;
     float m = 0.f, ssel = 0.f;
+    float mine = 0.f;  // lane c: un-normalised gate of slot c (k <= 16)
     for (int j = 0; j < k; ++j) {
-      float bv = v[0];
-      int bi = c;
+      uint64_t b = key[0];
 #pragma unroll
-      for (int f = 1; f < NF; ++f) {
-        if (v[f] > bv) { bv = v[f]; bi = f * 16 + c; }
-      }
+      for (int f = 1; f < NF; ++f) b = key[f] > b ? key[f] : b;
+      b = row16_max(b);
+      const float bv = key_value(b);
+      const int bi = key_index(b);
+      // keys are unique (they carry the index): the winner's entry drops out
 #pragma unroll
-      for (int off = 8; off > 0; off >>= 1) {
-        const float ovv = __shfl_xor(bv, off, kWave);
-        const int oi = __shfl_xor(bi, off, kWave);
-        if (ovv > bv || (ovv == bv && oi < bi)) { bv = ovv; bi = oi; }
-      }
-      if ((bi & 15) == c) {
-#pragma unroll
-        for (int f = 0; f < NF; ++f) if (f == (bi >> 4)) v[f] = -INFINITY;
-      }
+      for (int f = 0; f < NF; ++f) key[f] = key[f] == b ? 0ull : key[f];
       if (j == 0) m = bv;  // the largest logit
       const float ej = expf(bv - m);
       ssel += ej;
-      if (live && (j & 15) == c) {
-        // un-normalised gate; divided by the denominator below
-        p.ids[static_cast<size_t>(t) * k + j] = bi;
-        p.gates[static_cast<size_t>(t) * k + j] = ej;
+      if ((j & 15) == c) {
+        if (live) {
+          p.ids[static_cast<size_t>(t) * k + j] = bi;
+          // k > 16: un-normalised gate, divided in place below
+          if (k > 16) p.gates[static_cast<size_t>(t) * k + j] = ej;
+        }
         sel[r * k + j] = static_cast<uint8_t>(bi);
+        mine = ej;
       }
     }
     float denom = ssel;
     if (p.mode == MOE_SOFTMAX_ALL && !p.renorm) {
       float sall = 0.f;
 #pragma unroll
-      for (int f = 0; f < NF; ++f) if (f * 16 + c < E) sall += expf(ov[f] - m);
+      for (int f = 0; f < NF; ++f) if (f * 16 + c < E) sall += expf(v[f] - m);
 #pragma unroll
       for (int off = 8; off > 0; off >>= 1) sall += __shfl_xor(sall, off, kWave);
       denom = sall;
     }
     const float inv = 1.0f / denom;
     if (live) {
-      for (int j = c; j < k; j += 16) {
-        float* g = p.gates + static_cast<size_t>(t) * k + j;
-        *g = *g * inv;
+      if (k <= 16) {
+        if (c < k) p.gates[static_cast<size_t>(t) * k + c] = mine * inv;
+      } else {
+        for (int j = c; j < k; j += 16) {
+          float* g = p.gates + static_cast<size_t>(t) * k + j;
+          *g = *g * inv;
+        }
       }
     }
   }
@@ -349,16 +446,28 @@ __device__ void route_select(const RouteParams& p, int t0, const floatx4_t* acc,
 
 template <int NCH, bool BF16>
 __global__ __launch_bounds__(RTHR) void route_kernel(RouteParams p) {
-  __shared__ uint8_t sel[RT * kMaxE];
-  __shared__ int wh[RNW][kMaxE];
-  __shared__ int run[kMaxE + 1];
-  __shared__ int scan_a[kMaxE + 1];
-  __shared__ int scan_b[kMaxE + 1];
+  using C = RouteCfg<NCH>;
+  // x ring during the logits, then the selections and histograms; router
+  // ring during the logits, then the logit rows
+  __shared__ __align__(16) uint16_t Xr[(BF16 ? C::XBYTES : C::CARVE) / 2];
+  __shared__ __align__(16) uint16_t Wr[(BF16 ? C::WBYTES : C::LGBYTES) / 2];
+  uint8_t* sel = reinterpret_cast<uint8_t*>(Xr);                          // [RT * kMaxE]
+  int (*wh)[kMaxE] = reinterpret_cast<int (*)[kMaxE]>(sel + RT * kMaxE);  // [RNW][kMaxE]
+  int* run = reinterpret_cast<int*>(wh + RNW);                             // [kMaxE + 1]
+  int* scan_a = run + (kMaxE + 1);
+  int* scan_b = scan_a + (kMaxE + 1);
+  float* Lg = reinterpret_cast<float*>(Wr);                                // [RT][LGLD]
   const int t0 = blockIdx.x * RT;
-  floatx4_t acc[RouteCfg<NCH>::NF];
-  if constexpr (BF16) route_logits_bf16<NCH>(p, t0, acc);
-  else route_logits_f32<NCH>(p, t0, acc);
-  route_select<NCH>(p, t0, acc, sel);
+  float bias[C::NF];
+  load_bias<NCH>(p, bias);
+  {
+    floatx4_t acc[C::NF2];
+    if constexpr (BF16) route_logits_bf16<NCH>(p, t0, acc, Xr, Wr);
+    else route_logits_f32<NCH>(p, t0, acc);
+    store_logits<NCH>(acc, Lg);
+  }
+  __syncthreads();
+  route_select<NCH>(p, t0, Lg, bias, sel);
   if (p.blk_hist == nullptr && p.counts == nullptr) return;
   __syncthreads();
   const int nt = min(RT, p.T - t0);
@@ -408,95 +517,79 @@ __global__ __launch_bounds__(256) void rank_kernel(RankParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// scan kernel (one workgroup of 1024 threads). The per-block histogram is
-// pulled into LDS with batched loads when it fits (NB * E <= kScanLdsInts),
-// so the column scans run at LDS latency instead of one HBM round trip per
-// block.
+// scan kernel: 16 experts per workgroup of 256 threads. Thread (c, j) owns
+// expert 16 * blockIdx.x + j over the c-th sixteenth of the route blocks:
+// it sums its blocks, the 16 chunk sums of each expert are scanned in LDS,
+// and the blocks are rewritten in place with their exclusive prefix (the
+// first row of the block's pairs inside the expert's group).
 // ---------------------------------------------------------------------------
-constexpr int kScanLdsInts = 32768;  // 128 KiB
-
-__global__ __launch_bounds__(1024) void scan_kernel(ScanParams p) {
-  extern __shared__ __align__(16) int hl[];  // [NB * E] when it fits
-  __shared__ int part[1024];
-  __shared__ int cnt[kMaxE + 1];
-  __shared__ int off[kMaxE + 1];
-  __shared__ int tp[kMaxE + 1];
-  const int tid = threadIdx.x, E = p.E, NB = p.NB;
-  const int n = NB * E;
-  const bool in_lds = n <= kScanLdsInts;
-  int* h = in_lds ? hl : p.blk_hist;
-  if (in_lds) {
-    // 16-byte loads, all issued before any is used (one round trip when
-    // n <= 4 * 8 * 1024), then the scalar tail
-    const int n4 = n >> 2;
-    const int4* src4 = reinterpret_cast<const int4*>(p.blk_hist);
-    for (int base = tid; base < n4; base += 8 * 1024) {
-      int4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * 1024;
-        v[u] = i < n4 ? src4[i] : int4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * 1024;
-        if (i < n4) reinterpret_cast<int4*>(hl)[i] = v[u];
-      }
-    }
-    for (int i = (n4 << 2) + tid; i < n; i += 1024) hl[i] = p.blk_hist[i];
-    __syncthreads();
+__global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
+  __shared__ int part[16][17];
+  const int tid = threadIdx.x, j = tid & 15, c = tid >> 4;
+  const int e = blockIdx.x * 16 + j;
+  const int NB = p.NB, E = p.E;
+  const int per = (NB + 15) / 16;
+  const int b0 = min(c * per, NB), b1 = min(b0 + per, NB);
+  int s = 0;
+  if (e < E) {
+#pragma unroll 8
+    for (int b = b0; b < b1; ++b) s += p.blk_hist[static_cast<size_t>(b) * E + e];
   }
-  int G = 1024 / E;
-  if (G > NB) G = NB;
-  const int g = tid / E, e = tid - g * E;
-  const bool active = g < G;
-  const int chunk = (NB + G - 1) / G;
-  const int b0 = g * chunk, b1 = min(NB, b0 + chunk);
-  if (active) {
-    int s = 0;
-    for (int b = b0; b < b1; ++b) s += h[b * E + e];
-    part[g * E + e] = s;
-  }
+  part[c][j] = s;
   __syncthreads();
-  if (tid < E) {
+  if (tid < 16) {
     int r = 0;
-    for (int gg = 0; gg < G; ++gg) {
-      const int c = part[gg * E + tid];
-      part[gg * E + tid] = r;
-      r += c;
+    for (int cc = 0; cc < 16; ++cc) {
+      const int v = part[cc][tid];
+      part[cc][tid] = r;
+      r += v;
     }
-    cnt[tid] = r;
+    if (e < E) p.counts[e] = r;
   }
   __syncthreads();
-  if (tid < kWave) wave_exclusive_scan256(cnt, off, E);
-  if (tid < E) tp[tid] = (cnt[tid] + p.tile_m - 1) / p.tile_m;
-  __syncthreads();
-  if (tid < kWave) wave_exclusive_scan256(tp, tp, E);
-  __syncthreads();
-  if (active) {
-    int base = off[e] + part[g * E + e];
-    for (int b = b0; b < b1; ++b) {
-      const int c = h[b * E + e];
-      p.blk_hist[b * E + e] = base;
-      base += c;
+  if (e < E) {
+    int base = part[c][j];
+    for (int b = b0; b < b1; b += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = b + u < b1 ? p.blk_hist[static_cast<size_t>(b + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (b + u < b1) {
+          p.blk_hist[static_cast<size_t>(b + u) * E + e] = base;
+          base += v[u];
+        }
+      }
     }
   }
-  if (tid < E) { p.counts[tid] = cnt[tid]; p.offsets[tid] = off[tid]; }
-  if (tid == 0) p.offsets[E] = off[E];
-  write_tile_table(tp, E, p.max_tiles, p.tile_e, p.exp_tile0, p.meta);
 }
 
 // ---------------------------------------------------------------------------
-// scatter kernel
+// scatter kernel: perm[offsets[e] + block base + local rank] = pair, inv[pair]
+// = that row. Each workgroup scans the E counts itself; workgroup 0 also
+// writes offsets and the grouped-GEMM tile table.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void scatter_kernel(ScatterParams p) {
+  __shared__ int offs[kMaxE + 1];
+  __shared__ int tp[kMaxE + 1];
+  const int tid = threadIdx.x, E = p.E;
+  if (tid < kWave) wave_exclusive_scan256(p.counts, offs, E);
+  if (blockIdx.x == 0) {
+    for (int e = tid; e < E; e += 256) tp[e] = (p.counts[e] + p.tile_m - 1) / p.tile_m;
+    __syncthreads();
+    if (tid < kWave) wave_exclusive_scan256(tp, tp, E);
+    __syncthreads();
+    for (int e = tid; e <= E; e += 256) p.offsets[e] = offs[e];
+    write_tile_table(tp, E, p.max_tiles, p.tile_e, p.exp_tile0, p.meta);
+  }
+  __syncthreads();
   const int P = p.T * p.k;
-  const int q = blockIdx.x * 256 + threadIdx.x;
+  const int q = blockIdx.x * 256 + tid;
   if (q >= P) return;
   const int t = q / p.k;
   const int b = t / RT;
-  const int e = min(max(p.ids[q], 0), p.E - 1);
-  const int pos = p.blk_base[b * p.E + e] + p.lrank[q];
+  const int e = min(max(p.ids[q], 0), E - 1);
+  const int pos = offs[e] + p.blk_base[static_cast<size_t>(b) * E + e] + p.lrank[q];
   p.perm[pos] = q;
   p.inv[q] = pos;
 }
@@ -569,9 +662,7 @@ hipError_t launch_rank(const RankParams& p, hipStream_t s) {
 }
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t s) {
-  const int n = p.NB * p.E;
-  const size_t lds = n <= kScanLdsInts ? static_cast<size_t>(n) * 4 : 0;
-  scan_kernel<<<1, 1024, lds, s>>>(p);
+  scan_kernel<<<ceil_div(p.E, 16), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
