@@ -86,15 +86,17 @@ def lib() -> ctypes.CDLL:
     """The loaded libmoe.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
+        # MOE_LIBRARY: an alternative build of the same library (tuning builds)
+        path = os.environ.get("MOE_LIBRARY") or LIB_PATH
+        if not os.path.exists(path):
             raise RuntimeError(
-                f"{LIB_PATH} is missing: build it with "
+                f"{path} is missing: build it with "
                 "`python -m mixture_experts_sparse_amd.build` (there is no fallback path)")
         # torch first: its bundled HIP runtime carries the same SONAME
         # (libamdhip64.so.7), so libmoe binds to the runtime torch's streams
         # and allocations belong to instead of loading a second copy.
         import torch  # noqa: F401
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         for name, (args, res) in _SIG.items():
             fn = getattr(L, name)
             fn.argtypes = args

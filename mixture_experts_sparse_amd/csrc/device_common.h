@@ -24,6 +24,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z / (1 + e^-z) from the hardware base-2 exponential and
+// reciprocal (v_exp_f32, v_rcp_f32; about 1 ulp each): for activations that
+// are rounded to bf16 right after, well below the output's rounding.
+// e^-z overflows to +inf for very negative z, and the reciprocal gives 0.
+__device__ __forceinline__ float silu_fast(float z) {
+  const float e = __builtin_amdgcn_exp2f(z * -1.4426950408889634f);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
 __device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

@@ -26,8 +26,6 @@
 
 namespace moe {
 
-constexpr int GBR = 128;       // B rows per tile (gate 64 + up 64, or down 128)
-
 struct TileInfo {
   int e;          // expert, or -1 for the shared group
   int row0, nrows;
@@ -99,27 +97,42 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, TileInfo& ti) {
   return ti.nrows > 0;
 }
 
-// KIND 0: gate/up (B rows 0..63 gate, 64..127 up; N tile 64 hidden units).
-// KIND 1: down (B rows 0..127; N tile 128 model columns).
-// BM rows per tile with BM / 64 x 2 waves of 64 x 64; S-stage pipeline of
+// KIND 0: gate/up: B rows [0, GBR / 2) are gate rows n0.., [GBR / 2, GBR)
+//   the up rows of the same hidden units; N tile GBR / 2 hidden units.
+// KIND 1: down: B rows [0, GBR) are output columns n0..; N tile GBR.
+// NWM x NWN waves of 64 rows x 16 * NFW B rows each (BM = 64 * NWM,
+// GBR = 16 * NFW * NWN); S-stage pipeline of 32-deep K slices loaded by
 // direct global->LDS loads (global_load_lds_dwordx4), one stage per LDS
 // array so the compiler tracks each stage's loads separately. Every lane
 // issues every load (addresses clamped into the operand) so the wave's
 // outstanding-load count is the same on every path, and a stage is known to
 // have landed once at most (S - 2) stages' loads are outstanding.
-template <int KIND, int BM, int S, int BK>
-__global__ __launch_bounds__(BM * 2) void gemm_bf16_kernel(GemmParams p) {
-  constexpr int GBK = BK;
-  constexpr int NTHR = BM * 2;
-  constexpr int BN = KIND == 0 ? kTileNGateUp : kTileNDown;
-  constexpr int SA = BM * GBK;              // A elements per stage
-  constexpr int SEL = SA + GBR * GBK;       // elements per stage
-  constexpr int CPR = GBK / 8;              // 16-byte chunks per LDS row (4 or 8)
-  constexpr int KS = GBK / 32;              // MFMA K steps per stage
-  constexpr int LA = SA / 8 / NTHR;         // 16-byte A loads per thread per stage
-  constexpr int LB = GBR * GBK / 8 / NTHR;  // B loads per thread per stage
+// LDS destination of a direct global->LDS load of 4-byte words, hidden from
+// the compiler's load-counter tracking: the one wave that issues these loads
+// reads them back after an explicit wait.
+__device__ __forceinline__ lds_void_t* lds_untracked_i32(int32_t* q) {
+  lds_void_t* r = (lds_void_t*)q;
+  asm volatile("" : "+s"(r));
+  return r;
+}
+
+template <int KIND, int NWM, int NWN, int NFW, int S>
+__global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p) {
+  constexpr int BK = 32, CPR = 4;
+  constexpr int NTHR = NWM * NWN * 64;
+  constexpr int BM = NWM * 64;
+  constexpr int GBR = NWN * NFW * 16;           // B rows per tile
+  constexpr int HB = GBR / 2;                   // gate/up: hidden units per tile
+  constexpr int BN = KIND == 0 ? HB : GBR;      // output columns per tile
+  constexpr int SA = BM * BK;                   // A elements per stage
+  constexpr int SEL = SA + GBR * BK;            // elements per stage
+  constexpr int LA = SA / 8 / NTHR;             // 16-byte A loads per thread per stage
+  constexpr int LB = GBR * BK / 8 / NTHR;       // B loads per thread per stage
   constexpr int LPS = LA + LB;
+  static_assert(LA * NTHR * 8 == SA && LB * NTHR * 8 == GBR * BK, "whole loads per thread");
+  static_assert(KIND == 1 || NFW % 2 == 0, "gate/up pairs gate and up fragments");
   static_assert(S >= 2 && S <= 8, "stages");
+  static_assert((S - 2) * LPS < 64, "vmcnt range");
   __shared__ __align__(16) uint16_t L0[SEL];
   __shared__ __align__(16) uint16_t L1[SEL];
   __shared__ __align__(16) uint16_t L2[S > 2 ? SEL : 8];
@@ -128,6 +141,7 @@ __global__ __launch_bounds__(BM * 2) void gemm_bf16_kernel(GemmParams p) {
   __shared__ __align__(16) uint16_t L5[S > 5 ? SEL : 8];
   __shared__ __align__(16) uint16_t L6[S > 6 ? SEL : 8];
   __shared__ __align__(16) uint16_t L7[S > 7 ? SEL : 8];
+  __shared__ __align__(16) int32_t Pg[NTHR / 64 * LA * 64];  // perm words of each wave's A rows
   // stage i lives in its own LDS array (static index after unrolling), so the
   // compiler can tell one stage's DMA from another stage's fragment reads
   auto buf = [&]<int I>() -> uint16_t* {
@@ -160,18 +174,39 @@ __global__ __launch_bounds__(BM * 2) void gemm_bf16_kernel(GemmParams p) {
   const int wbase = tid & ~63;  // first thread of this wave
   // Load i of this thread fills LDS slot q = i * NTHR + tid: row q / CPR,
   // physical chunk tid % CPR (the swizzle decides which logical chunk).
+  // A source rows: gate/up gathers x rows through perm. The perm entries go
+  // out first (direct-to-LDS, one 4-byte word per lane into this wave's
+  // block of Pg), the weight slices of the prologue are issued while they
+  // are in flight, and only then are the A addresses formed.
   const uint16_t* asrc[LA];
-  int achunk[LA];
+  int achunk[LA], asrow[LA];
+  const bool gather = KIND == 0 && !shared;
+  const int uwave = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
     const int r = (i * NTHR + tid) / CPR;
     achunk[i] = swz_phys_to_logical<BK>(r, tid % CPR) * 8;
     const int rr = r < ti.nrows ? r : 0;  // rows past the group reload row 0 (never stored)
-    const int srow = ti.row0 + rr;
-    int src = srow;
-    if (KIND == 0 && !shared) src = min(max(p.perm[srow] / p.k, 0), p.a_rows - 1);
-    asrc[i] = A + static_cast<size_t>(src) * K;
+    asrow[i] = ti.row0 + rr;
+    if (gather) {
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(p.perm + asrow[i]),
+                                       lds_untracked_i32(&Pg[(uwave * LA + i) * 64]), 4, 0, 0);
+    }
   }
+  auto form_a = [&]() {
+    if (gather) {
+      // this wave's perm words are in: all its loads but the prologue's
+      // weight halves are done
+      wait_stage<(S - 1) * LB>();
+#pragma unroll
+      for (int i = 0; i < LA; ++i) asrow[i] = Pg[(uwave * LA + i) * 64 + (tid & 63)];
+    }
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int src = gather ? min(max(asrow[i] / p.k, 0), p.a_rows - 1) : asrow[i];
+      asrc[i] = A + static_cast<size_t>(src) * K;
+    }
+  };
   const uint16_t* bsrc[LB];
   int bchunk[LB];
 #pragma unroll
@@ -180,22 +215,25 @@ __global__ __launch_bounds__(BM * 2) void gemm_bf16_kernel(GemmParams p) {
     bchunk[i] = swz_phys_to_logical<BK>(r, tid % CPR) * 8;
     int n;
     const uint16_t* base;
-    if (KIND == 0) { n = ti.n0 + (r & 63); base = r < 64 ? B0 : B1; }
+    if (KIND == 0) { n = ti.n0 + (r < HB ? r : r - HB); base = r < HB ? B0 : B1; }
     else { n = ti.n0 + r; base = B0; }
     n = n < N ? n : N - 1;  // columns past N reload a valid row (never stored)
     bsrc[i] = base + static_cast<size_t>(n) * K;
   }
 
-  const int nk = (K + GBK - 1) / GBK;
-  const bool ktail = (K % GBK) != 0;
-  auto issue = [&](uint16_t* st, int kc) {
-    const int k0 = min(kc, nk - 1) * GBK;
+  const int nk = (K + BK - 1) / BK;
+  const bool ktail = (K % BK) != 0;
+  auto issue_a = [&](uint16_t* st, int kc) {
+    const int k0 = min(kc, nk - 1) * BK;
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       const int kk = min(k0 + achunk[i], K - 8);
       __builtin_amdgcn_global_load_lds((gbl_void_t*)(asrc[i] + kk),
                                        (lds_void_t*)(st + (i * NTHR + wbase) * 8), 16, 0, 0);
     }
+  };
+  auto issue_b = [&](uint16_t* st, int kc) {
+    const int k0 = min(kc, nk - 1) * BK;
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
       const int kk = min(k0 + bchunk[i], K - 8);
@@ -203,60 +241,74 @@ __global__ __launch_bounds__(BM * 2) void gemm_bf16_kernel(GemmParams p) {
                                        (lds_void_t*)(st + SA + (i * NTHR + wbase) * 8), 16, 0, 0);
     }
   };
+  auto issue = [&](uint16_t* st, int kc) {
+    issue_a(st, kc);
+    issue_b(st, kc);
+  };
 
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % (BM / 64), wn = wave / (BM / 64);
+  const int wm = wave % NWM, wn = wave / NWM;
   const int fr = lane & 15, fq = lane >> 4;
-  constexpr int NF = 4;
-  floatx4_t acc[4][NF];
+  floatx4_t acc[4][NFW];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < NF; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NFW; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   // fragment offsets within a stage (the same for every stage)
-  int aoff[KS][4], boff[KS][NF];
+  int aoff[4], boff[NFW];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
+  for (int mf = 0; mf < 4; ++mf) aoff[mf] = swz<BK>(wm * 64 + mf * 16 + fr, fq);
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf) aoff[ks][mf] = swz<BK>(wm * 64 + mf * 16 + fr, ks * 4 + fq);
-#pragma unroll
-    for (int nf = 0; nf < NF; ++nf) {
-      int r;
-      if (KIND == 0) r = (nf < 2 ? 0 : 64) + wn * 32 + (nf & 1) * 16 + fr;
-      else r = wn * 64 + nf * 16 + fr;
-      boff[ks][nf] = SA + swz<BK>(r, ks * 4 + fq);
+  for (int nf = 0; nf < NFW; ++nf) {
+    int r;
+    if (KIND == 0) {
+      constexpr int H = NFW / 2;  // gate fragments per wave (the up ones follow)
+      r = (nf < H ? 0 : HB) + wn * H * 16 + (nf % H) * 16 + fr;
+    } else {
+      r = wn * NFW * 16 + nf * 16 + fr;
     }
+    boff[nf] = SA + swz<BK>(r, fq);
   }
 
   auto compute = [&](const uint16_t* st) {
+    bf16x8_t af[4], bf[NFW];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8_t af[4], bf[NF];
+    for (int mf = 0; mf < 4; ++mf)
+      af[mf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + aoff[mf]));
 #pragma unroll
-      for (int mf = 0; mf < 4; ++mf)
-        af[mf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + aoff[ks][mf]));
+    for (int nf = 0; nf < NFW; ++nf)
+      bf[nf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + boff[nf]));
 #pragma unroll
-      for (int nf = 0; nf < NF; ++nf)
-        bf[nf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + boff[ks][nf]));
+    for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
-      for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-        for (int nf = 0; nf < NF; ++nf)
-          acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mf], bf[nf], acc[mf][nf], 0, 0, 0);
-    }
+      for (int nf = 0; nf < NFW; ++nf)
+        acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mf], bf[nf], acc[mf][nf], 0, 0, 0);
   };
 
+  // Wait for this wave's loads of stage kc. The prologue issues the weight
+  // halves of stages 0..S-2 first and their A halves after, so before step
+  // S - 2 the loads newer than A(kc) are A(kc+1..S-2) and the kc earlier
+  // steps' stages; from step S - 2 on, S - 2 whole stages.
+  auto wait_for = [&](int kc) {
+    if (kc >= S - 2) {
+      wait_stage<(S - 2) * LPS>();
+      return;
+    }
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+      ((kc == J ? wait_stage<(S - 2 - J) * LA + J * LPS>() : void()), ...);
+    }(std::make_integer_sequence<int, S - 2>{});
+  };
   // One pipeline step: stage kc lives in `cur`; `nxt` receives stage kc + S - 1.
   auto step = [&](int kc, uint16_t* cur, uint16_t* nxt) {
-    wait_stage<(S - 2) * LPS>();
+    wait_for(kc);
     stage_barrier();
     issue(nxt, kc + S - 1);
     if (kc < nk) {
       if (ktail && kc == nk - 1) {
         // last, partial K chunk: zero A's columns past K (B's clamped
         // duplicates then multiply zeros)
-        const int k0 = kc * GBK;
+        const int k0 = kc * BK;
 #pragma unroll
         for (int i = 0; i < LA; ++i) {
           if (k0 + achunk[i] >= K)
@@ -269,8 +321,10 @@ __global__ __launch_bounds__(BM * 2) void gemm_bf16_kernel(GemmParams p) {
   };
 
   [&]<int... I>(std::integer_sequence<int, I...>) {
-    // prologue: stages 0 .. S-2
-    ((I < S - 1 ? issue(buf.template operator()<I>(), I) : void()), ...);
+    // prologue: weight halves of stages 0 .. S-2, then (perm in hand) their A halves
+    ((I < S - 1 ? issue_b(buf.template operator()<I>(), I) : void()), ...);
+    form_a();
+    ((I < S - 1 ? issue_a(buf.template operator()<I>(), I) : void()), ...);
     for (int kb = 0; kb < nk; kb += S) {
       (step(kb + I, buf.template operator()<I>(), buf.template operator()<(I + S - 1) % S>()), ...);
     }
@@ -281,12 +335,13 @@ __global__ __launch_bounds__(BM * 2) void gemm_bf16_kernel(GemmParams p) {
   // epilogue: each wave stages its own sub-tile through a private slice of
   // L0, 16 rows at a time, so every lane stores 16 contiguous bytes of an
   // output row; no block barrier is needed (a wave reads only what it wrote).
-  constexpr int WC = KIND == 0 ? 32 : 64;  // output columns per wave
+  constexpr int WC = KIND == 0 ? NFW * 8 : NFW * 16;  // output columns per wave
   constexpr int WLD = WC + 8;
-  static_assert((NTHR / 64) * 16 * WLD <= SEL, "epilogue slices must fit in one stage buffer");
+  constexpr int LPR = WC / 8;      // lanes per output row
+  constexpr int NPASS = (16 * LPR + 63) / 64;
+  static_assert(NWM * NWN * 16 * WLD <= SEL, "epilogue slices must fit in one stage buffer");
   uint16_t* Cw = L0 + wave * 16 * WLD;
   const int c0 = ti.n0 + wn * WC;  // first output column of this wave
-  constexpr int LPR = WC / 8;      // lanes per output row (4 or 8)
 #pragma unroll
   for (int mf = 0; mf < 4; ++mf) {
 #pragma unroll
@@ -294,20 +349,20 @@ __global__ __launch_bounds__(BM * 2) void gemm_bf16_kernel(GemmParams p) {
       const int rc = fq * 4 + i;
       if (KIND == 0) {
 #pragma unroll
-        for (int nf = 0; nf < 2; ++nf)
-          Cw[rc * WLD + nf * 16 + fr] = f32_to_bf16(silu_f32(acc[mf][nf][i]) * acc[mf][nf + 2][i]);
+        for (int nf = 0; nf < NFW / 2; ++nf)
+          Cw[rc * WLD + nf * 16 + fr] = f32_to_bf16(silu_fast(acc[mf][nf][i]) * acc[mf][nf + NFW / 2][i]);
       } else {
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf) Cw[rc * WLD + nf * 16 + fr] = f32_to_bf16(acc[mf][nf][i]);
+        for (int nf = 0; nf < NFW; ++nf) Cw[rc * WLD + nf * 16 + fr] = f32_to_bf16(acc[mf][nf][i]);
       }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
 #pragma unroll
-    for (int pass = 0; pass < (16 * LPR) / 64; ++pass) {
+    for (int pass = 0; pass < NPASS; ++pass) {
       const int idx = pass * 64 + lane;
       const int rc = idx / LPR, ch = (idx % LPR) * 8;
       const int rt = wm * 64 + mf * 16 + rc;
-      if (rt < ti.nrows && c0 + ch < N) {
+      if (idx < 16 * LPR && rt < ti.nrows && c0 + ch < N) {
         *reinterpret_cast<u32x4_t*>(OUT + static_cast<size_t>(ti.row0 + rt) * N + c0 + ch) =
             *reinterpret_cast<const u32x4_t*>(Cw + rc * WLD + ch);
       }
@@ -365,46 +420,60 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
   }
 }
 
-#ifndef MOE_STAGES_BM128
-#define MOE_STAGES_BM128 4
+// Tile shapes (waves along M, waves along N, B fragments per wave, stages).
+template <int KIND, int NWM, int NWN, int NFW, int S>
+struct GemmShape {
+  static constexpr int BM = NWM * 64;
+  static constexpr int BN = KIND == 0 ? NWN * NFW * 8 : NWN * NFW * 16;
+  static void launch(const GemmParams& p, unsigned nblk, hipStream_t s) {
+    gemm_bf16_kernel<KIND, NWM, NWN, NFW, S><<<nblk, NWM * NWN * 64, 0, s>>>(p);
+  }
+};
+
+#ifndef MOE_GU_SHAPE
+#define MOE_GU_SHAPE 0
 #endif
-#ifndef MOE_STAGES_BM256
-#define MOE_STAGES_BM256 4
-#endif
-#ifndef MOE_BK_BM128
-#define MOE_BK_BM128 32
-#endif
-#ifndef MOE_BK_BM256
-#define MOE_BK_BM256 32
+#ifndef MOE_DN_SHAPE
+#define MOE_DN_SHAPE 0
 #endif
 
-template <int KIND, int BM>
-static void launch_bf16(const GemmParams& p, unsigned nblk, hipStream_t s) {
-  constexpr int S = BM == 128 ? MOE_STAGES_BM128 : MOE_STAGES_BM256;
-  constexpr int BK = BM == 128 ? MOE_BK_BM128 : MOE_BK_BM256;
-  gemm_bf16_kernel<KIND, BM, S, BK><<<nblk, BM * 2, 0, s>>>(p);
+template <class Sh>
+static hipError_t launch_shape(const GemmParams& p, hipStream_t s) {
+  if (p.tile_m != Sh::BM) return hipErrorInvalidValue;
+  long long nblk = static_cast<long long>(ceil_div(p.N, Sh::BN)) * p.max_mtiles;
+  if (p.shared_T > 0) nblk += static_cast<long long>(ceil_div(p.shared_T, Sh::BM)) * ceil_div(p.sN, Sh::BN);
+  nblk = (nblk + 7) / 8 * 8;
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+  Sh::launch(p, static_cast<unsigned>(nblk), s);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (p.dtype == MOE_BF16) {
-    const int BN = p.kind == 0 ? kTileNGateUp : kTileNDown;
-    const int BM = p.tile_m;
-    if (BM != 128 && BM != 256) return hipErrorInvalidValue;
-    long long nblk = static_cast<long long>(ceil_div(p.N, BN)) * p.max_mtiles;
-    if (p.shared_T > 0) nblk += static_cast<long long>(ceil_div(p.shared_T, BM)) * ceil_div(p.sN, BN);
-    nblk = (nblk + 7) / 8 * 8;
-    if (nblk <= 0) return hipSuccess;
-    if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-    const unsigned nb = static_cast<unsigned>(nblk);
-    if (p.kind == 0) { if (BM == 128) launch_bf16<0, 128>(p, nb, s); else launch_bf16<0, 256>(p, nb, s); }
-    else { if (BM == 128) launch_bf16<1, 128>(p, nb, s); else launch_bf16<1, 256>(p, nb, s); }
-  } else {
-    const long long n = static_cast<long long>(p.P) * p.N + static_cast<long long>(p.shared_T) * p.sN;
-    const long long nblk = (n + 255) / 256;
-    if (nblk <= 0) return hipSuccess;
-    if (p.kind == 0) gemm_f32_kernel<0><<<static_cast<unsigned>(nblk), 256, 0, s>>>(p);
-    else gemm_f32_kernel<1><<<static_cast<unsigned>(nblk), 256, 0, s>>>(p);
+    if (p.tile_m == 256) {
+      if (p.kind == 0) return launch_shape<GemmShape<0, 4, 2, 4, 4>>(p, s);
+      return launch_shape<GemmShape<1, 4, 2, 4, 4>>(p, s);
+    }
+    if (p.tile_m != 128) return hipErrorInvalidValue;
+    if (p.kind == 0) {
+      switch (MOE_GU_SHAPE) {
+        case 1: return launch_shape<GemmShape<0, 2, 4, 4, 4>>(p, s);
+        case 2: return launch_shape<GemmShape<0, 2, 4, 8, 3>>(p, s);
+        default: return launch_shape<GemmShape<0, 2, 2, 4, 4>>(p, s);
+      }
+    }
+    switch (MOE_DN_SHAPE) {
+      case 1: return launch_shape<GemmShape<1, 2, 4, 4, 4>>(p, s);
+      case 2: return launch_shape<GemmShape<1, 2, 4, 10, 3>>(p, s);
+      default: return launch_shape<GemmShape<1, 2, 2, 4, 4>>(p, s);
+    }
   }
+  const long long n = static_cast<long long>(p.P) * p.N + static_cast<long long>(p.shared_T) * p.sN;
+  const long long nblk = (n + 255) / 256;
+  if (nblk <= 0) return hipSuccess;
+  if (p.kind == 0) gemm_f32_kernel<0><<<static_cast<unsigned>(nblk), 256, 0, s>>>(p);
+  else gemm_f32_kernel<1><<<static_cast<unsigned>(nblk), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
