@@ -8,16 +8,23 @@
 // of x are read in place through the sorted dispatch table (t_r = perm[r] / k),
 // so no per-token copy of x or of the weights is ever built.
 //
-// bf16 path: v_mfma_f32_16x16x32_bf16 with fp32 accumulation, 256 threads as
-// 2x2 waves, 128-row M tiles, 64-deep K chunks double-buffered in LDS (rows
-// padded by 16 bytes so the MFMA fragment reads are bank-conflict free).
+// bf16 path: v_mfma_f32_16x16x32_bf16 with fp32 accumulation; each wave owns
+// a 64-row x 16*NFW-column block of a workgroup tile of NWM x NWN waves. K is
+// streamed through an S-stage LDS pipeline of direct global->LDS loads, each
+// stage a 32- or 64-deep K slice of the tile's A rows and weight rows (LDS
+// rows XOR-swizzled so the fragment reads are bank-conflict free). 64-deep
+// slices read 128 contiguous bytes of every row per stage, which the L2
+// delivers at about 1.6x the rate of 64-byte segments; they pay when a
+// workgroup has 8 waves to cover the larger stages. The gate/up epilogue
+// applies the SiLU product before the single rounding to bf16.
 // fp32 path: one thread per output element (small fp32 layers only).
 //
 // The launch grid is sized from an upper bound on the tile count; the true
 // count is read on the device, so no host synchronisation is needed. Tiles
-// are numbered expert-major, then N tile, then M tile, and block b runs
-// logical tile (b mod 8) * ceil(n/8) + b / 8: consecutive logical tiles (the
-// M tiles that share one weight slab) land on the same XCD and its L2.
+// are numbered shared group first, then expert-major, in blocks of 4 M tiles
+// x all N tiles, and block b runs logical tile (b mod 8) * ceil(n/8) + b / 8:
+// consecutive logical tiles (the M tiles that share one weight slab) land on
+// the same XCD and its L2.
 
 #include <utility>
 
@@ -116,9 +123,11 @@ __device__ __forceinline__ lds_void_t* lds_untracked_i32(int32_t* q) {
   return r;
 }
 
-template <int KIND, int NWM, int NWN, int NFW, int S>
+template <int KIND, int NWM, int NWN, int NFW, int S, int BK>
 __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p) {
-  constexpr int BK = 32, CPR = 4;
+  static_assert(BK == 32 || BK == 64, "K slice of 32 or 64 (64- or 128-byte row segments)");
+  constexpr int CPR = BK / 8;                   // 16-byte chunks per LDS row
+  constexpr int KS = BK / 32;                   // MFMA K steps per stage
   constexpr int NTHR = NWM * NWN * 64;
   constexpr int BM = NWM * 64;
   constexpr int GBR = NWN * NFW * 16;           // B rows per tile
@@ -255,35 +264,41 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
 #pragma unroll
     for (int b = 0; b < NFW; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  // fragment offsets within a stage (the same for every stage)
-  int aoff[4], boff[NFW];
+  // fragment offsets within a stage (the same for every stage), per MFMA K step
+  int aoff[KS][4], boff[KS][NFW];
 #pragma unroll
-  for (int mf = 0; mf < 4; ++mf) aoff[mf] = swz<BK>(wm * 64 + mf * 16 + fr, fq);
+  for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-  for (int nf = 0; nf < NFW; ++nf) {
-    int r;
-    if (KIND == 0) {
-      constexpr int H = NFW / 2;  // gate fragments per wave (the up ones follow)
-      r = (nf < H ? 0 : HB) + wn * H * 16 + (nf % H) * 16 + fr;
-    } else {
-      r = wn * NFW * 16 + nf * 16 + fr;
+    for (int mf = 0; mf < 4; ++mf) aoff[ks][mf] = swz<BK>(wm * 64 + mf * 16 + fr, ks * 4 + fq);
+#pragma unroll
+    for (int nf = 0; nf < NFW; ++nf) {
+      int r;
+      if (KIND == 0) {
+        constexpr int H = NFW / 2;  // gate fragments per wave (the up ones follow)
+        r = (nf < H ? 0 : HB) + wn * H * 16 + (nf % H) * 16 + fr;
+      } else {
+        r = wn * NFW * 16 + nf * 16 + fr;
+      }
+      boff[ks][nf] = SA + swz<BK>(r, ks * 4 + fq);
     }
-    boff[nf] = SA + swz<BK>(r, fq);
   }
 
   auto compute = [&](const uint16_t* st) {
-    bf16x8_t af[4], bf[NFW];
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
-      af[mf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + aoff[mf]));
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8_t af[4], bf[NFW];
 #pragma unroll
-    for (int nf = 0; nf < NFW; ++nf)
-      bf[nf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + boff[nf]));
-#pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
+      for (int mf = 0; mf < 4; ++mf)
+        af[mf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + aoff[ks][mf]));
 #pragma unroll
       for (int nf = 0; nf < NFW; ++nf)
-        acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mf], bf[nf], acc[mf][nf], 0, 0, 0);
+        bf[nf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + boff[ks][nf]));
+#pragma unroll
+      for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < NFW; ++nf)
+          acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mf], bf[nf], acc[mf][nf], 0, 0, 0);
+    }
   };
 
   // Wait for this wave's loads of stage kc. The prologue issues the weight
@@ -421,21 +436,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 }
 
 // Tile shapes (waves along M, waves along N, B fragments per wave, stages).
-template <int KIND, int NWM, int NWN, int NFW, int S>
+template <int KIND, int NWM, int NWN, int NFW, int S, int BK>
 struct GemmShape {
   static constexpr int BM = NWM * 64;
   static constexpr int BN = KIND == 0 ? NWN * NFW * 8 : NWN * NFW * 16;
   static void launch(const GemmParams& p, unsigned nblk, hipStream_t s) {
-    gemm_bf16_kernel<KIND, NWM, NWN, NFW, S><<<nblk, NWM * NWN * 64, 0, s>>>(p);
+    gemm_bf16_kernel<KIND, NWM, NWN, NFW, S, BK><<<nblk, NWM * NWN * 64, 0, s>>>(p);
   }
 };
-
-#ifndef MOE_GU_SHAPE
-#define MOE_GU_SHAPE 0
-#endif
-#ifndef MOE_DN_SHAPE
-#define MOE_DN_SHAPE 0
-#endif
 
 template <class Sh>
 static hipError_t launch_shape(const GemmParams& p, hipStream_t s) {
@@ -451,23 +459,22 @@ static hipError_t launch_shape(const GemmParams& p, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (p.dtype == MOE_BF16) {
+    // 256-row tiles (prefill-sized experts): 4 x 2 waves, 64-deep K slices
+    // (128-byte row segments: twice the L2->LDS rate of 64-byte ones).
     if (p.tile_m == 256) {
-      if (p.kind == 0) return launch_shape<GemmShape<0, 4, 2, 4, 4>>(p, s);
-      return launch_shape<GemmShape<1, 4, 2, 4, 4>>(p, s);
+      if (p.kind == 0) return launch_shape<GemmShape<0, 4, 2, 4, 3, 64>>(p, s);
+      return launch_shape<GemmShape<1, 4, 2, 4, 3, 64>>(p, s);
     }
     if (p.tile_m != 128) return hipErrorInvalidValue;
+    // gate/up with at least 32 rows per expert on average: 2 x 4 waves over
+    // 128 hidden units, 64-deep K slices; otherwise (decode-sized experts,
+    // and the down projection) 2 x 2 waves with 32-deep slices, two
+    // workgroups per CU.
     if (p.kind == 0) {
-      switch (MOE_GU_SHAPE) {
-        case 1: return launch_shape<GemmShape<0, 2, 4, 4, 4>>(p, s);
-        case 2: return launch_shape<GemmShape<0, 2, 4, 8, 3>>(p, s);
-        default: return launch_shape<GemmShape<0, 2, 2, 4, 4>>(p, s);
-      }
+      if (p.P >= 32 * p.E) return launch_shape<GemmShape<0, 2, 4, 4, 3, 64>>(p, s);
+      return launch_shape<GemmShape<0, 2, 2, 4, 4, 32>>(p, s);
     }
-    switch (MOE_DN_SHAPE) {
-      case 1: return launch_shape<GemmShape<1, 2, 4, 4, 4>>(p, s);
-      case 2: return launch_shape<GemmShape<1, 2, 4, 10, 3>>(p, s);
-      default: return launch_shape<GemmShape<1, 2, 2, 4, 4>>(p, s);
-    }
+    return launch_shape<GemmShape<1, 2, 2, 4, 4, 32>>(p, s);
   }
   const long long n = static_cast<long long>(p.P) * p.N + static_cast<long long>(p.shared_T) * p.sN;
   const long long nblk = (n + 255) / 256;

@@ -36,6 +36,9 @@ SMALL = {
     "decode_small": small_spec("decode", T=37, d=264, E=64, h=96, k=8),
     "skewed_small": small_spec("skewed_prefill", T=700, d=256, E=32, h=200, k=8),
     "shared_small": small_spec("shared_routed", T=520, d=264, E=12, h=96, k=4, shared_h=376),
+    # at least 256 rows per expert: the 256-row tiles; d and h leave K and N tails
+    "big_tile_small": small_spec("skewed_prefill", T=600, d=200, E=4, h=136, k=2),
+    "big_tile_shared_small": small_spec("shared_routed", T=700, d=264, E=3, h=96, k=2, shared_h=200),
     "shared_fp32_small": small_spec("shared_routed", T=130, d=48, E=6, h=24, k=2, shared_h=40,
                                     dtype=F32),
     "e256_small": MoESpec(name="e256", T=150, d=64, E=256, h=32, k=6, mode=SOFTMAX_SELECTED),
