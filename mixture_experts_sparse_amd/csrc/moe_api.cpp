@@ -86,7 +86,7 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 WsLayout ws_layout(const moe_config& c) {
   const size_t T = static_cast<size_t>(c.T), E = static_cast<size_t>(c.E);
   const size_t P = T * static_cast<size_t>(c.top_k);
-  const size_t NB = static_cast<size_t>(ceil_div(c.T, kRouteTokens));
+  const size_t NB = static_cast<size_t>(ceil_div(c.T, route_tokens(c.T)));
   const size_t MT = static_cast<size_t>(max_m_tiles(static_cast<int>(P), c.E));
   const size_t eb = elem_bytes(c);
   const size_t hs = static_cast<size_t>(c.shared_h);
@@ -175,6 +175,7 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
   p.w_router = w_router;
   p.bias = c.has_router_bias ? b_router : nullptr;
   p.T = c.T; p.d = c.d; p.E = c.E; p.k = c.top_k; p.mode = c.mode; p.renorm = c.renormalize;
+  p.rt = route_tokens(c.T);
   p.ids = ids;
   p.gates = gates;
   p.logits = logits;
@@ -196,13 +197,14 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* ids, int32_t* coun
   MOE_TRY(check_ws(c, MOE_ENTRY_DISPATCH, ws, ws_bytes));
   const WsLayout L = ws_layout(c);
   hipStream_t s = as_stream(stream);
-  RankParams rp{ids, c.T, c.E, c.top_k, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank)};
+  const int rt = route_tokens(c.T);
+  RankParams rp{ids, c.T, c.E, c.top_k, rt, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank)};
   MOE_HIP(launch_rank(rp, s));
   const int tm = choose_tile_m(c.T * c.top_k, c.E);
-  ScanParams sp{at<int32_t>(ws, L.blk_hist), ceil_div(c.T, kRouteTokens), c.E, counts};
+  ScanParams sp{at<int32_t>(ws, L.blk_hist), ceil_div(c.T, rt), c.E, counts};
   MOE_HIP(launch_scan(sp, s));
   ScatterParams xp{ids, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank), c.T, c.E,
-                   c.top_k, perm, inv, counts, offsets, max_m_tiles(c.T * c.top_k, c.E, tm), tm,
+                   c.top_k, rt, perm, inv, counts, offsets, max_m_tiles(c.T * c.top_k, c.E, tm), tm,
                    at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0), at<int32_t>(ws, L.meta)};
   MOE_HIP(launch_scatter(xp, s));
   return MOE_OK;
@@ -379,7 +381,8 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
     if (stage_events == nullptr) return hipSuccess;
     return hipEventRecord(reinterpret_cast<hipEvent_t>(stage_events[i]), s);
   };
-  const int NB = ceil_div(c.T, kRouteTokens);
+  const int rt = route_tokens(c.T);
+  const int NB = ceil_div(c.T, rt);
   const int tm = choose_tile_m(c.T * c.top_k, c.E);
   int32_t* ids_p = ids != nullptr ? ids : at<int32_t>(ws, L.ids);
   float* gates_p = gates != nullptr ? gates : at<float>(ws, L.gates);
@@ -397,6 +400,7 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
   rp.bias = c.has_router_bias ? w->b_router : nullptr;
   rp.w_sgate = gated ? w->w_shared_gate : nullptr;
   rp.T = c.T; rp.d = c.d; rp.E = c.E; rp.k = c.top_k; rp.mode = c.mode; rp.renorm = c.renormalize;
+  rp.rt = rt;
   rp.ids = ids_p;
   rp.gates = gates_p;
   rp.logits = nullptr;
@@ -416,7 +420,7 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
     ScanParams sp{at<int32_t>(ws, L.blk_hist), NB, c.E, counts_p};
     MOE_HIP(launch_scan(sp, s));
     ScatterParams xp{ids_p, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank), c.T, c.E,
-                     c.top_k, perm, inv, counts_p, offsets, max_m_tiles(c.T * c.top_k, c.E, tm), tm,
+                     c.top_k, rt, perm, inv, counts_p, offsets, max_m_tiles(c.T * c.top_k, c.E, tm), tm,
                      at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0), at<int32_t>(ws, L.meta)};
     MOE_HIP(launch_scatter(xp, s));
   }

@@ -10,9 +10,16 @@
 
 namespace moe {
 
-// Route block: tokens per workgroup of the router / top-k kernel. The
-// dispatch histogram is kept per route block.
-constexpr int kRouteTokens = 64;
+// Route block: tokens per workgroup of the router / top-k kernel; the
+// dispatch histogram is kept per route block. 64 tokens when they all fit
+// one block (the dispatch then finishes inside it) or when 64-token blocks
+// already give every CU (256) a workgroup; otherwise 32, for twice the
+// workgroups (each re-reads the router rows, so not beyond that).
+constexpr int kRouteTokensMax = 64;
+constexpr int kRouteTokensMin = 32;
+inline int route_tokens(int T) {
+  return (T <= kRouteTokensMax || T >= 256 * kRouteTokensMax) ? kRouteTokensMax : kRouteTokensMin;
+}
 // Grouped-GEMM M tile (rows of one expert per workgroup): 128, or 256 when
 // experts average at least 256 rows (tile_m in the parameter blocks).
 constexpr int kTileM = 128;
@@ -51,6 +58,7 @@ struct RouteParams {
   const float* bias;      // [E] or null
   const void* w_sgate;    // [d] or null: sigmoid(w_s . x) -> sgate
   int T, d, E, k, mode, renorm;
+  int rt;                 // tokens per route block (route_tokens(T))
   int32_t* ids;           // [T, k]
   float* gates;           // [T, k]
   float* logits;          // [T, E] or null
@@ -73,7 +81,7 @@ struct RouteParams {
 // Dispatch from given ids (moe_dispatch): histogram + local ranks.
 struct RankParams {
   const int32_t* ids;
-  int T, E, k;
+  int T, E, k, rt;
   int32_t* blk_hist;
   int32_t* lrank;
 };
@@ -91,7 +99,7 @@ struct ScatterParams {
   const int32_t* ids;
   const int32_t* blk_base;
   const int32_t* lrank;
-  int T, E, k;
+  int T, E, k, rt;
   int32_t* perm;
   int32_t* inv;
   const int32_t* counts;

@@ -19,7 +19,7 @@
 
 namespace moe {
 
-constexpr int RT = kRouteTokens;  // tokens per route block
+constexpr int RTM = kRouteTokensMax;  // most tokens per route block
 constexpr int RK = 64;            // K chunk of the router GEMM
 constexpr int RLD = RK + 8;       // padded LDS row (bf16 elements)
 constexpr int kMaxE = MOE_MAX_EXPERTS;
@@ -135,17 +135,20 @@ constexpr int RTHR = 512;
 constexpr int RNW = RTHR / kWave;
 constexpr int RBK = 32;
 
-template <int NCH>
+template <int NCH, int RT>
 struct RouteCfg {
+  static_assert(RT == 32 || RT == 64, "route blocks of 32 or 64 tokens");
   static constexpr int NC = NCH * 64;            // padded logit columns
   static constexpr int NF = NC / 16;             // 16-column fragments of a row
-  static constexpr int NH = NC / 2;              // columns per half
+  static constexpr int NTG = RT / 16;            // token groups of 16 (waves along tokens)
+  static constexpr int NCG = RNW / NTG;          // column groups (waves along columns)
+  static constexpr int NH = NC / NCG;            // columns per wave
   static constexpr int NF2 = NH / 16;            // fragments per wave
   static constexpr int SX = RT * RBK;            // x elements per slice
   static constexpr int SW = NC * RBK;            // router elements per slice
   static constexpr int RR = NCH <= 4 ? 4 : 3;    // router ring slots
   static constexpr int RX = 16;                  // x ring slots
-  static constexpr int LX = SX / 8 / 256;        // 16-byte x loads per x-wave thread per slice
+  static constexpr int XW = SX / 8 / 64;         // x-stream waves (one 16-byte load per lane)
   static constexpr int LW = SW / 8 / 256;        // router loads per router-wave thread per slice
   static constexpr int LGLD = NC + 4;            // logit row stride in LDS (floats)
   // LDS after the logits: selections, per-wave histograms, running counts
@@ -165,15 +168,18 @@ __device__ __forceinline__ lds_void_t* lds_untracked(uint16_t* q) {
 }
 
 // Router logits on bf16 MFMA: acc[f][i] = logit of token row
-// 16 * (w % 4) + 4 * (lane / 16) + i, column NH * (w / 4) + 16 * f + lane % 16.
-template <int NCH>
+// 16 * (w % NTG) + 4 * (lane / 16) + i, column NH * (w / NTG) + 16 * f + lane % 16.
+// Waves 0 .. XW-1 stream x, waves 4-7 the router rows (waves XW..3 load nothing).
+template <int NCH, int RT>
 __device__ void route_logits_bf16(const RouteParams& p, int t0, floatx4_t* acc, uint16_t* Xr,
                                   uint16_t* Wr) {
-  using C = RouteCfg<NCH>;
-  constexpr int RX = C::RX, RR = C::RR, LX = C::LX, LW = C::LW, NF2 = C::NF2;
+  using C = RouteCfg<NCH, RT>;
+  constexpr int RX = C::RX, RR = C::RR, LW = C::LW, NF2 = C::NF2, NTG = C::NTG;
+  constexpr int LX = 1;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool xw = wave < 4;                  // x-stream waves
+  const bool xw = wave < C::XW;              // x-stream waves
+  const bool ww = wave >= 4;                 // router-stream waves
   const int lt = tid & 255;                  // thread index within the stream
   const int lwb = (wave & 3) * 64;
   const uint16_t* X = static_cast<const uint16_t*>(p.x);
@@ -182,7 +188,8 @@ __device__ void route_logits_bf16(const RouteParams& p, int t0, floatx4_t* acc, 
   const int d = p.d;
   constexpr int LM = LX > LW ? LX : LW;
   // load i of a stream thread fills slot chunk q = i * 256 + lt: row q / 4,
-  // physical chunk q % 4 (the swizzle picks the logical K chunk)
+  // physical chunk q % 4 (the swizzle picks the logical K chunk); waves that
+  // stream nothing keep a valid address they never use
   const uint16_t* src[LM];
   int chunk[LM];
 #pragma unroll
@@ -211,14 +218,14 @@ __device__ void route_logits_bf16(const RouteParams& p, int t0, floatx4_t* acc, 
                                        lds_untracked(slot + (i * 256 + lwb) * 8), 16, 0, 0);
   };
   const int fr = lane & 15, fq = lane >> 4;
-  const int aoff = swz<RBK>((wave & 3) * 16 + fr, fq);
-  const int boff = swz<RBK>((wave >> 2) * C::NH + fr, fq);  // + f * 16 rows
+  const int aoff = swz<RBK>((wave % NTG) * 16 + fr, fq);
+  const int boff = swz<RBK>((wave / NTG) * C::NH + fr, fq);  // + f * 16 rows
 #pragma unroll
   for (int f = 0; f < NF2; ++f) acc[f] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   if (xw) {
 #pragma unroll
     for (int st = 0; st < RX - 1; ++st) issue.template operator()<LX>(Xr + st * C::SX, st);
-  } else {
+  } else if (ww) {
 #pragma unroll
     for (int st = 0; st < RR - 1; ++st) issue.template operator()<LW>(Wr + st * C::SW, st);
   }
@@ -228,10 +235,11 @@ __device__ void route_logits_bf16(const RouteParams& p, int t0, floatx4_t* acc, 
     // of it are done (all but the newer slices') and every wave has passed
     // the barrier
     if (xw) wait_stage<(RX - 2) * LX>();
-    else wait_stage<(RR - 2) * LW>();
+    else if (ww) wait_stage<(RR - 2) * LW>();
+    else wait_stage<0>();
     stage_barrier();
     if (xw) issue.template operator()<LX>(Xr + ix * C::SX, kc + RX - 1);
-    else issue.template operator()<LW>(Wr + iw * C::SW, kc + RR - 1);
+    else if (ww) issue.template operator()<LW>(Wr + iw * C::SW, kc + RR - 1);
     ix = ix + 1 == RX ? 0 : ix + 1;
     iw = iw + 1 == RR ? 0 : iw + 1;
     uint16_t* xs = Xr + cx * C::SX;
@@ -265,10 +273,10 @@ __device__ void route_logits_bf16(const RouteParams& p, int t0, floatx4_t* acc, 
 
 // fp32 router logits by VALU into the same register layout (small layers);
 // the K loop is outermost so every accumulator index is static.
-template <int NCH>
+template <int NCH, int RT>
 __device__ void route_logits_f32(const RouteParams& p, int t0, floatx4_t* acc) {
-  using C = RouteCfg<NCH>;
-  constexpr int NF2 = C::NF2;
+  using C = RouteCfg<NCH, RT>;
+  constexpr int NF2 = C::NF2, NTG = C::NTG;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* X = static_cast<const float*>(p.x);
   const float* W = static_cast<const float*>(p.w_router);
@@ -277,14 +285,14 @@ __device__ void route_logits_f32(const RouteParams& p, int t0, floatx4_t* acc) {
   const float* xr[4];
 #pragma unroll
   for (int f = 0; f < NF2; ++f) {
-    const int e = (wave >> 2) * C::NH + f * 16 + (lane & 15);
+    const int e = (wave / NTG) * C::NH + f * 16 + (lane & 15);
     // columns without a router row read row 0 (their logits are never used)
     wr[f] = e < p.E ? W + static_cast<size_t>(e) * p.d : (e == p.E && WS != nullptr ? WS : W);
     acc[f] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int t = t0 + (wave & 3) * 16 + (lane >> 4) * 4 + i;
+    const int t = t0 + (wave % NTG) * 16 + (lane >> 4) * 4 + i;
     xr[i] = X + static_cast<size_t>(t < p.T ? t : t0) * p.d;
   }
   for (int c = 0; c < p.d; ++c) {
@@ -301,16 +309,16 @@ __device__ void route_logits_f32(const RouteParams& p, int t0, floatx4_t* acc) {
 }
 
 // Accumulators -> one padded fp32 row of logits per token in LDS.
-template <int NCH>
+template <int NCH, int RT>
 __device__ __forceinline__ void store_logits(const floatx4_t* acc, float* Lg) {
-  using C = RouteCfg<NCH>;
+  using C = RouteCfg<NCH, RT>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int f = 0; f < C::NF2; ++f)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = (wave & 3) * 16 + (lane >> 4) * 4 + i;
-      Lg[r * C::LGLD + (wave >> 2) * C::NH + f * 16 + (lane & 15)] = acc[f][i];
+      const int r = (wave % C::NTG) * 16 + (lane >> 4) * 4 + i;
+      Lg[r * C::LGLD + (wave / C::NTG) * C::NH + f * 16 + (lane & 15)] = acc[f][i];
     }
 }
 
@@ -353,7 +361,7 @@ __device__ __forceinline__ uint64_t row16_max(uint64_t a) {
 // the logits so that no load is outstanding in the selection.
 template <int NCH>
 __device__ __forceinline__ void load_bias(const RouteParams& p, float* bias) {
-  constexpr int NF = RouteCfg<NCH>::NF;
+  constexpr int NF = NCH * 4;
   const int c = threadIdx.x & 15;
 #pragma unroll
   for (int f = 0; f < NF; ++f) bias[f] = 0.f;
@@ -366,17 +374,17 @@ __device__ __forceinline__ void load_bias(const RouteParams& p, float* bias) {
 
 // Top-k, gates, logits and shared-gate outputs from the logit rows in LDS;
 // the selection also goes to sel[] for the rank pass. 16-lane group g of the
-// workgroup owns token rows g and g + 32.
-template <int NCH>
+// workgroup owns token rows g, g + 32, ...
+template <int NCH, int RT>
 __device__ void route_select(const RouteParams& p, int t0, const float* Lg, const float* bias,
                              uint8_t* sel) {
-  using C = RouteCfg<NCH>;
+  using C = RouteCfg<NCH, RT>;
   constexpr int NF = C::NF;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15;
   const int E = p.E, k = p.k;
 #pragma unroll
-  for (int rnd = 0; rnd < 2; ++rnd) {
+  for (int rnd = 0; rnd < RT / 32; ++rnd) {
     const int r = rnd * 32 + wave * 4 + (lane >> 4);  // token row in the block
     const int t = t0 + r;
     const bool live = t < p.T;                          // uniform across the 16-lane group
@@ -444,9 +452,9 @@ __device__ void route_select(const RouteParams& p, int t0, const float* Lg, cons
   }
 }
 
-template <int NCH, bool BF16>
+template <int NCH, bool BF16, int RT>
 __global__ __launch_bounds__(RTHR) void route_kernel(RouteParams p) {
-  using C = RouteCfg<NCH>;
+  using C = RouteCfg<NCH, RT>;
   // x ring during the logits, then the selections and histograms; router
   // ring during the logits, then the logit rows
   __shared__ __align__(16) uint16_t Xr[(BF16 ? C::XBYTES : C::CARVE) / 2];
@@ -462,12 +470,12 @@ __global__ __launch_bounds__(RTHR) void route_kernel(RouteParams p) {
   load_bias<NCH>(p, bias);
   {
     floatx4_t acc[C::NF2];
-    if constexpr (BF16) route_logits_bf16<NCH>(p, t0, acc, Xr, Wr);
-    else route_logits_f32<NCH>(p, t0, acc);
-    store_logits<NCH>(acc, Lg);
+    if constexpr (BF16) route_logits_bf16<NCH, RT>(p, t0, acc, Xr, Wr);
+    else route_logits_f32<NCH, RT>(p, t0, acc);
+    store_logits<NCH, RT>(acc, Lg);
   }
   __syncthreads();
-  route_select<NCH>(p, t0, Lg, bias, sel);
+  route_select<NCH, RT>(p, t0, Lg, bias, sel);
   if (p.blk_hist == nullptr && p.counts == nullptr) return;
   __syncthreads();
   const int nt = min(RT, p.T - t0);
@@ -500,11 +508,11 @@ __global__ __launch_bounds__(RTHR) void route_kernel(RouteParams p) {
 // rank kernel: the histogram / rank half of dispatch from given ids
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void rank_kernel(RankParams p) {
-  __shared__ uint8_t sel[RT * kMaxE];
+  __shared__ uint8_t sel[RTM * kMaxE];
   __shared__ int wh[4][kMaxE];
   __shared__ int run[kMaxE + 1];
-  const int t0 = blockIdx.x * RT;
-  const int nt = min(RT, p.T - t0);
+  const int t0 = blockIdx.x * p.rt;
+  const int nt = min(p.rt, p.T - t0);
   const int npairs = nt * p.k;
   const int32_t* ids = p.ids + static_cast<size_t>(t0) * p.k;
   // caller-provided ids are clamped into [0, E) (the scatter clamps the same
@@ -587,7 +595,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterParams p) {
   const int q = blockIdx.x * 256 + tid;
   if (q >= P) return;
   const int t = q / p.k;
-  const int b = t / RT;
+  const int b = t / p.rt;
   const int e = min(max(p.ids[q], 0), E - 1);
   const int pos = offs[e] + p.blk_base[static_cast<size_t>(b) * E + e] + p.lrank[q];
   p.perm[pos] = q;
@@ -637,12 +645,18 @@ __global__ __launch_bounds__(256) void rowdot_sigmoid_kernel(RowDotSigmoidParams
 // ---------------------------------------------------------------------------
 template <int NCH>
 static void launch_route_nch(const RouteParams& p, int dtype, int nb, hipStream_t s) {
-  if (dtype == MOE_BF16) route_kernel<NCH, true><<<nb, RTHR, 0, s>>>(p);
-  else route_kernel<NCH, false><<<nb, RTHR, 0, s>>>(p);
+  if (p.rt == kRouteTokensMax) {
+    if (dtype == MOE_BF16) route_kernel<NCH, true, kRouteTokensMax><<<nb, RTHR, 0, s>>>(p);
+    else route_kernel<NCH, false, kRouteTokensMax><<<nb, RTHR, 0, s>>>(p);
+  } else {
+    if (dtype == MOE_BF16) route_kernel<NCH, true, kRouteTokensMin><<<nb, RTHR, 0, s>>>(p);
+    else route_kernel<NCH, false, kRouteTokensMin><<<nb, RTHR, 0, s>>>(p);
+  }
 }
 
 hipError_t launch_route(const RouteParams& p, int dtype, hipStream_t s) {
-  const int nb = ceil_div(p.T, RT);
+  if (p.rt != kRouteTokensMax && p.rt != kRouteTokensMin) return hipErrorInvalidValue;
+  const int nb = ceil_div(p.T, p.rt);
   const int cols = p.E + (p.w_sgate != nullptr ? 1 : 0);
   const int nch = ceil_div(cols, 64);
   switch (nch) {
@@ -657,7 +671,8 @@ hipError_t launch_route(const RouteParams& p, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_rank(const RankParams& p, hipStream_t s) {
-  rank_kernel<<<ceil_div(p.T, RT), 256, 0, s>>>(p);
+  if (p.rt < 1 || p.rt > RTM) return hipErrorInvalidValue;
+  rank_kernel<<<ceil_div(p.T, p.rt), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
