@@ -387,6 +387,352 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
 }
 
 // ---------------------------------------------------------------------------
+// Persistent variant for 128-row tiles (short K per tile). The grid holds as
+// many workgroups as are resident at once (XCD x = id mod 8 owns the x-th
+// eighth of the tile order and its workgroups stride through it), and the
+// stage ring runs across tile boundaries: while the last slices of one tile
+// are multiplied the loads already stream the next tile, whose tile-table
+// lookups happen on the scalar unit and whose perm words were fetched into
+// LDS one tile ahead. The epilogue stages through its own LDS slice and uses
+// buffer stores (every lane issues every store; the buffer range check drops
+// the ones past the output), so each wave knows exactly how many stores sit
+// in its load counter behind the slices it waits for.
+// ---------------------------------------------------------------------------
+
+// Uniform loads of the tile tables through the constant address space, so
+// they are scalar loads and never enter the vector-memory counter.
+template <class T>
+__device__ __forceinline__ T ldc(const T* q, int i) {
+  return ((const __attribute__((address_space(4))) T*)q)[i];
+}
+
+struct Sched {
+  int x, j, W;      // XCD, slot on the XCD, workgroups per XCD
+  int per, total;   // tiles per XCD, tiles in all
+  int NT;           // routed N tiles per M tile
+  int nsh, NTs;     // shared-group tiles, shared N tiles per M tile
+};
+
+template <int BN>
+__device__ __forceinline__ Sched make_sched(const GemmParams& p) {
+  Sched s;
+  const int BM = p.tile_m;
+  int ntiles = p.meta != nullptr ? ldc(p.meta, 0) : 0;  // null: shared group only
+  ntiles = min(max(ntiles, 0), p.max_mtiles);
+  s.NT = (p.N + BN - 1) / BN;
+  s.nsh = 0;
+  s.NTs = 1;
+  if (p.shared_T > 0) {
+    s.NTs = (p.sN + BN - 1) / BN;
+    s.nsh = ((p.shared_T + BM - 1) / BM) * s.NTs;
+  }
+  s.total = s.NT * ntiles + s.nsh;
+  s.per = (s.total + 7) >> 3;
+  s.x = blockIdx.x & 7;
+  s.j = blockIdx.x >> 3;
+  s.W = gridDim.x >> 3;
+  return s;
+}
+
+// The i-th tile of this workgroup; false past its last one. (nrows <= 0 only
+// with inconsistent caller tables: such a tile is computed and not stored.)
+template <int BN>
+__device__ __forceinline__ bool tile_at(const GemmParams& p, const Sched& s, int i, TileInfo& ti) {
+  const int jj = s.j + i * s.W;
+  if (jj >= s.per) return false;
+  int L = s.x * s.per + jj;
+  if (L >= s.total) return false;
+  const int BM = p.tile_m;
+  int n, m;
+  if (L < s.nsh) {
+    grouped_nm(L, s.nsh / s.NTs, s.NTs, n, m);
+    ti.e = -1;
+    ti.row0 = m * BM;
+    ti.nrows = min(BM, p.shared_T - ti.row0);
+    ti.n0 = n * BN;
+    return true;
+  }
+  L -= s.nsh;
+  const int q = L / s.NT;
+  const int e = min(max(ldc(p.tile_e, q), 0), p.E - 1);
+  const int tp0 = ldc(p.exp_tile0, e);
+  grouped_nm(L - s.NT * tp0, ldc(p.exp_tile0, e + 1) - tp0, s.NT, n, m);
+  const int o0 = min(max(ldc(p.offsets, e), 0), p.P);
+  const int o1 = min(max(ldc(p.offsets, e + 1), 0), p.P);
+  ti.e = e;
+  ti.row0 = o0 + m * BM;
+  ti.nrows = min(BM, o1 - ti.row0);
+  ti.n0 = n * BN;
+  return true;
+}
+
+// LDS destination of a stage load, hidden from the compiler's load-counter
+// tracking (all waits on the ring are explicit and followed by a barrier).
+__device__ __forceinline__ lds_void_t* lds_untracked(uint16_t* q) {
+  lds_void_t* r = (lds_void_t*)q;
+  asm volatile("" : "+s"(r));
+  return r;
+}
+
+template <int N, int X>
+__device__ __forceinline__ void wait_relaxed(bool relax) {
+  if (relax) wait_stage<N + X>();
+  else wait_stage<N>();
+}
+
+template <int KIND, int NWM, int NWN, int NFW, int S, int BK>
+__global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_pers(GemmParams p) {
+  static_assert(BK == 32 || BK == 64, "K slice of 32 or 64");
+  constexpr int CPR = BK / 8, KS = BK / 32;
+  constexpr int NTHR = NWM * NWN * 64, NW = NWM * NWN;
+  constexpr int BM = NWM * 64;
+  constexpr int GBR = NWN * NFW * 16, HB = GBR / 2;
+  constexpr int BN = KIND == 0 ? HB : GBR;
+  constexpr int SA = BM * BK, SEL = SA + GBR * BK;
+  constexpr int LA = SA / 8 / NTHR, LB = GBR * BK / 8 / NTHR, LPS = LA + LB;
+  constexpr int WC = KIND == 0 ? NFW * 8 : NFW * 16;  // output columns per wave
+  constexpr int WLD = WC + 8, LPR = WC / 8;
+  constexpr int NPASS = (16 * LPR + 63) / 64;
+  constexpr int ES = 4 * NPASS;                       // stores per wave per epilogue
+  static_assert(LA * NTHR * 8 == SA && LB * NTHR * 8 == GBR * BK, "whole loads per thread");
+  static_assert(KIND == 1 || NFW % 2 == 0, "gate/up pairs gate and up fragments");
+  static_assert(S >= 3 && (S - 2) * LPS + ES < 64, "vmcnt range");
+  __shared__ __align__(16) uint16_t Ring[S * SEL];
+  __shared__ __align__(16) uint16_t Cs[NW * 16 * WLD];
+  // perm words of the next routed tile's A rows (one 64-word block per wave
+  // and load): written by DMA one tile ahead, read back by the same wave at
+  // that tile's setup, which completes before the next prefetch is issued
+  __shared__ __align__(16) int32_t Pg[NW * LA * 64];
+
+  const Sched sc = make_sched<BN>(p);
+  TileInfo ct;  // tile being multiplied
+  if (!tile_at<BN>(p, sc, 0, ct)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wbase = wave * 64;
+  int achunk[LA], bchunk[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i)
+    achunk[i] = swz_phys_to_logical<BK>((i * NTHR + tid) / CPR, tid % CPR) * 8;
+#pragma unroll
+  for (int i = 0; i < LB; ++i)
+    bchunk[i] = swz_phys_to_logical<BK>((i * NTHR + tid) / CPR, tid % CPR) * 8;
+
+  // ---- load cursor ----
+  const uint16_t* asrc[LA];
+  const uint16_t* bsrc[LB];
+  int lK = BK, lnk = 1, lk = 0, li = 0;
+  bool lpending = false;  // the next issue starts tile lnext
+  TileInfo lnext;
+  int gstep = 0, pf_step = -2;  // loop step; step of the last perm prefetch
+  // gate/up, routed tile: the perm words of this thread's A rows into Pg
+  auto pf_issue = [&](const TileInfo& t) {
+    if (KIND == 0 && t.e >= 0) {
+#pragma unroll
+      for (int i = 0; i < LA; ++i) {
+        const int r = (i * NTHR + tid) / CPR;
+        const int srow = min(max(t.row0 + (r < t.nrows ? r : 0), 0), p.P - 1);
+        lds_void_t* d = (lds_void_t*)(Pg + (wave * LA + i) * 64);
+        asm volatile("" : "+s"(d));
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(p.perm + srow), d, 4, 0, 0);
+      }
+      pf_step = gstep;
+    }
+  };
+  auto setup = [&](const TileInfo& t) {
+    const bool sh = t.e < 0;
+    lK = sh ? p.sK : p.K;
+    lnk = (lK + BK - 1) / BK;
+    const int N = sh ? p.sN : p.N;
+    const uint16_t* A = static_cast<const uint16_t*>(sh ? p.sa : p.a);
+    const uint16_t* B0 = static_cast<const uint16_t*>(sh ? p.sb0 : p.b0);
+    const uint16_t* B1 = static_cast<const uint16_t*>(sh ? p.sb1 : p.b1);
+    if (!sh) {
+      const size_t wstride = static_cast<size_t>(N) * lK;
+      B0 += static_cast<size_t>(t.e) * wstride;
+      if (KIND == 0) B1 += static_cast<size_t>(t.e) * wstride;
+    }
+    const int rows = sh ? p.shared_T : (KIND == 0 ? p.a_rows : p.P);
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int r = (i * NTHR + tid) / CPR;
+      int src = t.row0 + (r < t.nrows ? r : 0);  // rows past the tile reload its first row
+      if (KIND == 0 && !sh) src = Pg[(wave * LA + i) * 64 + lane] / p.k;
+      src = min(max(src, 0), rows - 1);
+      asrc[i] = A + static_cast<size_t>(src) * lK;
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int r = (i * NTHR + tid) / CPR;
+      int n;
+      const uint16_t* base;
+      if (KIND == 0) { n = t.n0 + (r < HB ? r : r - HB); base = r < HB ? B0 : B1; }
+      else { n = t.n0 + r; base = B0; }
+      n = min(n, N - 1);  // columns past N reload a valid row (never stored)
+      bsrc[i] = base + static_cast<size_t>(n) * lK;
+    }
+  };
+  // Issues the cursor's next K slice into stage st and advances the cursor;
+  // every lane issues every load (clamped in bounds).
+  auto issue = [&](uint16_t* st) {
+    if (lpending) {
+      lpending = false;
+      // this tile's perm words went out one step ago (previous tile of a
+      // single slice): not yet covered by the per-step waits
+      if (pf_step >= gstep - 1) wait_stage<0>();
+      setup(lnext);
+      TileInfo t2;
+      if (tile_at<BN>(p, sc, li + 1, t2)) pf_issue(t2);
+    }
+    const int k0 = min(lk, lnk - 1) * BK;
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(asrc[i] + min(k0 + achunk[i], lK - 8)),
+                                       lds_untracked(st + (i * NTHR + wbase) * 8), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < LB; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(bsrc[i] + min(k0 + bchunk[i], lK - 8)),
+                                       lds_untracked(st + SA + (i * NTHR + wbase) * 8), 16, 0, 0);
+    if (lk < lnk && ++lk == lnk) {
+      if (tile_at<BN>(p, sc, li + 1, lnext)) {
+        ++li;
+        lk = 0;
+        lpending = true;
+      }  // else: exhausted; the last slice is re-issued (never multiplied)
+    }
+  };
+
+  // ---- prologue ----
+  pf_issue(ct);
+  wait_stage<0>();
+  setup(ct);
+  {
+    TileInfo t1;
+    if (tile_at<BN>(p, sc, 1, t1)) pf_issue(t1);
+  }
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) issue(Ring + st * SEL);
+
+  // ---- compute ----
+  const int wm = wave % NWM, wn = wave / NWM;
+  const int fr = lane & 15, fq = lane >> 4;
+  floatx4_t acc[4][NFW];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < NFW; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  int aoff[KS][4], boff[KS][NFW];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf) aoff[ks][mf] = swz<BK>(wm * 64 + mf * 16 + fr, ks * 4 + fq);
+#pragma unroll
+    for (int nf = 0; nf < NFW; ++nf) {
+      int r;
+      if (KIND == 0) {
+        constexpr int H = NFW / 2;
+        r = (nf < H ? 0 : HB) + wn * H * 16 + (nf % H) * 16 + fr;
+      } else {
+        r = wn * NFW * 16 + nf * 16 + fr;
+      }
+      boff[ks][nf] = SA + swz<BK>(r, ks * 4 + fq);
+    }
+  }
+  int cK = ct.e < 0 ? p.sK : p.K;
+  int cnk = (cK + BK - 1) / BK;
+  int ci = 0, ca = 0, ia = S - 1;
+  int win = 0;  // waits still covering the last epilogue's stores
+  const bool ktail_any = (p.K % BK) != 0 || (p.shared_T > 0 && (p.sK % BK) != 0);
+  uint16_t* Cw = Cs + wave * 16 * WLD;
+
+  for (;;) {
+    for (int ck = 0; ck < cnk; ++ck) {
+      // slice ck of tile ct is in stage ca once this wave's loads of it are
+      // done (all but the newer S - 2 slices' loads, plus the stores of an
+      // epilogue issued after it) and every wave has passed the barrier
+      const bool relax = win > 0;
+      win = win > 0 ? win - 1 : 0;
+      wait_relaxed<(S - 2) * LPS, ES>(relax);
+      stage_barrier();
+      issue(Ring + ia * SEL);
+      ia = ia + 1 == S ? 0 : ia + 1;
+      uint16_t* st = Ring + ca * SEL;
+      if (ktail_any && ck == cnk - 1 && (cK % BK) != 0) {
+        // last, partial K slice: zero A's columns past K (B's clamped
+        // duplicates then multiply zeros)
+#pragma unroll
+        for (int i = 0; i < LA; ++i)
+          if (ck * BK + achunk[i] >= cK)
+            *reinterpret_cast<u32x4_t*>(st + (i * NTHR + tid) * 8) = u32x4_t{0u, 0u, 0u, 0u};
+        wait_stage<63>();
+        stage_barrier();
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8_t af[4], bf[NFW];
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf)
+          af[mf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + aoff[ks][mf]));
+#pragma unroll
+        for (int nf = 0; nf < NFW; ++nf)
+          bf[nf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + boff[ks][nf]));
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+          for (int nf = 0; nf < NFW; ++nf)
+            acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mf], bf[nf], acc[mf][nf], 0, 0, 0);
+      }
+      ca = ca + 1 == S ? 0 : ca + 1;
+      ++gstep;
+    }
+    // epilogue: this wave's sub-tile through its LDS slice, 16 rows at a time
+    {
+      const bool sh = ct.e < 0;
+      const int N = sh ? p.sN : p.N;
+      const int rows = sh ? p.shared_T : p.P;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          sh ? p.sout : p.out, 0, static_cast<int>(static_cast<unsigned>(rows) * N * 2u), 0x00020000);
+      const int c0 = ct.n0 + wn * WC;
+#pragma unroll
+      for (int mf = 0; mf < 4; ++mf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rc = fq * 4 + i;
+          if (KIND == 0) {
+#pragma unroll
+            for (int nf = 0; nf < NFW / 2; ++nf)
+              Cw[rc * WLD + nf * 16 + fr] = f32_to_bf16(silu_fast(acc[mf][nf][i]) * acc[mf][nf + NFW / 2][i]);
+          } else {
+#pragma unroll
+            for (int nf = 0; nf < NFW; ++nf) Cw[rc * WLD + nf * 16 + fr] = f32_to_bf16(acc[mf][nf][i]);
+          }
+        }
+#pragma unroll
+        for (int pass = 0; pass < NPASS; ++pass) {
+          const int idx = pass * 64 + lane;
+          const int rc = min(idx / LPR, 15), ch = (idx % LPR) * 8;
+          const int rt = wm * 64 + mf * 16 + rc;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(Cw + rc * WLD + ch);
+          const bool ok = idx < 16 * LPR && rt < ct.nrows && c0 + ch < N;
+          const unsigned off = ok ? (static_cast<unsigned>(ct.row0 + rt) * N + c0 + ch) * 2u : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b128(v, rs, static_cast<int>(off), 0, 0);
+        }
+      }
+    }
+    win = S - 1;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < NFW; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    if (!tile_at<BN>(p, sc, ++ci, ct)) break;
+    cK = ct.e < 0 ? p.sK : p.K;
+    cnk = (cK + BK - 1) / BK;
+  }
+  // no load may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path: one thread per output element.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int r) {
@@ -445,6 +791,43 @@ struct GemmShape {
   }
 };
 
+template <int KIND, int NWM, int NWN, int NFW, int S, int BK>
+struct PersShape {
+  static constexpr int BM = NWM * 64;
+  static constexpr int BN = KIND == 0 ? NWN * NFW * 8 : NWN * NFW * 16;
+  static constexpr int OCC = NWM * NWN == 4 ? 2 : 1;  // resident workgroups per CU
+  static void launch(const GemmParams& p, unsigned nblk, hipStream_t s) {
+    gemm_bf16_pers<KIND, NWM, NWN, NFW, S, BK><<<nblk, NWM * NWN * 64, 0, s>>>(p);
+  }
+};
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <class Sh>
+static hipError_t launch_pers(const GemmParams& p, hipStream_t s) {
+  if (p.tile_m != Sh::BM) return hipErrorInvalidValue;
+  long long ub = static_cast<long long>(ceil_div(p.N, Sh::BN)) * p.max_mtiles;
+  if (p.shared_T > 0) ub += static_cast<long long>(ceil_div(p.shared_T, Sh::BM)) * ceil_div(p.sN, Sh::BN);
+  if (ub <= 0) return hipSuccess;
+  const long long resident = static_cast<long long>(device_cus()) * Sh::OCC;
+  long long nblk = ub < resident ? ub : resident;
+  nblk = (nblk + 7) / 8 * 8;
+  Sh::launch(p, static_cast<unsigned>(nblk), s);
+  return hipGetLastError();
+}
+
 template <class Sh>
 static hipError_t launch_shape(const GemmParams& p, hipStream_t s) {
   if (p.tile_m != Sh::BM) return hipErrorInvalidValue;
@@ -467,11 +850,12 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     }
     if (p.tile_m != 128) return hipErrorInvalidValue;
     // gate/up with at least 32 rows per expert on average: 2 x 4 waves over
-    // 128 hidden units, 64-deep K slices; otherwise (decode-sized experts,
-    // and the down projection) 2 x 2 waves with 32-deep slices, two
-    // workgroups per CU.
+    // 128 hidden units, 64-deep K slices, persistent (one workgroup per CU,
+    // so tile changes are hidden by the pipeline running across them);
+    // otherwise (decode-sized experts, and the down projection) 2 x 2 waves
+    // with 32-deep slices and two workgroups per CU.
     if (p.kind == 0) {
-      if (p.P >= 32 * p.E) return launch_shape<GemmShape<0, 2, 4, 4, 3, 64>>(p, s);
+      if (p.P >= 32 * p.E) return launch_pers<PersShape<0, 2, 4, 4, 3, 64>>(p, s);
       return launch_shape<GemmShape<0, 2, 2, 4, 4, 32>>(p, s);
     }
     return launch_shape<GemmShape<1, 2, 2, 4, 4, 32>>(p, s);
