@@ -61,8 +61,10 @@ def stage_work(spec, U, T):
     }
 
 
-STAGE_KERNEL = {"route": "route_kernel", "dispatch": "scan_kernel", "gate_up": "gemm_bf16_kernel<0",
-                "down": "gemm_bf16_kernel<1", "combine": "combine_"}
+# kernel-name prefixes of each stage's (first) kernel in a rocprofv3 record
+STAGE_KERNEL = {"route": ("route_kernel",), "dispatch": ("scan_kernel",),
+                "gate_up": ("gemm_bf16_pers<0", "gemm_bf16_kernel<0"),
+                "down": ("gemm_bf16_pers<1", "gemm_bf16_kernel<1"), "combine": ("combine_",)}
 
 
 def kernel_sources_sha():
@@ -85,7 +87,7 @@ def recorded_traffic(workload, stage):
     if not rec or rec.get("kernels_sha256_16") != kernel_sources_sha():
         return None
     for name, t in rec["per_launch"].items():
-        if STAGE_KERNEL[stage] in name:
+        if any(k in name for k in STAGE_KERNEL[stage]):
             return t["fetch_bytes"] + t["write_bytes"]
     return None
 
