@@ -12,6 +12,11 @@
 
 namespace moe {
 
+// Slots are taken in batches of CKB: a batch's inv words and gates are
+// loaded together, then its y rows together, then added in slot order, so a
+// thread waits on two load latencies per batch rather than two per slot.
+constexpr int CKB = 8;
+
 __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineParams p) {
   const int cpr = p.d >> 3;  // 8-element chunks per row
   const long long item = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
@@ -22,25 +27,49 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineParams p) {
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int j = 0; j < p.k; ++j) {
-    const size_t q = static_cast<size_t>(t) * p.k + j;
-    const int r = min(max(p.inv[q], 0), p.y_rows - 1);
-    const float g = p.gates[q];
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(y + static_cast<size_t>(r) * p.d + c);
+  // the shared row does not depend on the tables: its load goes out first
+  u32x4_t sv = {0u, 0u, 0u, 0u};
+  float sc = 0.f;
+  if (p.shared != nullptr) {
+    sc = p.shared_scale != nullptr ? p.shared_scale[t] : 1.0f;
+    sv = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.shared) +
+                                           static_cast<size_t>(t) * p.d + c);
+  }
+  for (int j0 = 0; j0 < p.k; j0 += CKB) {
+    int r[CKB];
+    float g[CKB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(g, __uint_as_float(v[i] << 16), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(g, __uint_as_float(v[i] & 0xFFFF0000u), acc[2 * i + 1]);
+    for (int u = 0; u < CKB; ++u) {
+      const size_t q = static_cast<size_t>(t) * p.k + min(j0 + u, p.k - 1);
+      r[u] = p.inv[q];
+      g[u] = p.gates[q];
+    }
+#pragma unroll
+    for (int u = 0; u < CKB; ++u) { pin(r[u]); pin(g[u]); }
+    u32x4_t v[CKB];
+#pragma unroll
+    for (int u = 0; u < CKB; ++u) {
+      const int rr = min(max(r[u], 0), p.y_rows - 1);
+      v[u] = *reinterpret_cast<const u32x4_t*>(y + static_cast<size_t>(rr) * p.d + c);
+    }
+#pragma unroll
+    for (int u = 0; u < CKB; ++u) pin(v[u]);
+#pragma unroll
+    for (int u = 0; u < CKB; ++u) {
+      if (j0 + u < p.k) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(g[u], __uint_as_float(v[u][i] << 16), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(g[u], __uint_as_float(v[u][i] & 0xFFFF0000u), acc[2 * i + 1]);
+        }
+      }
     }
   }
   if (p.shared != nullptr) {
-    const float sc = p.shared_scale != nullptr ? p.shared_scale[t] : 1.0f;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.shared) +
-                                                         static_cast<size_t>(t) * p.d + c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(sc, __uint_as_float(v[i] << 16), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(sc, __uint_as_float(v[i] & 0xFFFF0000u), acc[2 * i + 1]);
+      acc[2 * i] = fmaf(sc, __uint_as_float(sv[i] << 16), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(sc, __uint_as_float(sv[i] & 0xFFFF0000u), acc[2 * i + 1]);
     }
   }
   u32x4_t o;
@@ -60,20 +89,42 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(CombineParams p) {
   const int c = static_cast<int>(item - static_cast<long long>(t) * cpr) * 4;
   const float* y = static_cast<const float*>(p.y);
   floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < p.k; ++j) {
-    const size_t q = static_cast<size_t>(t) * p.k + j;
-    const int r = min(max(p.inv[q], 0), p.y_rows - 1);
-    const float g = p.gates[q];
-    const floatx4_t v = *reinterpret_cast<const floatx4_t*>(y + static_cast<size_t>(r) * p.d + c);
+  floatx4_t sv = {0.f, 0.f, 0.f, 0.f};
+  float sc = 0.f;
+  if (p.shared != nullptr) {
+    sc = p.shared_scale != nullptr ? p.shared_scale[t] : 1.0f;
+    sv = *reinterpret_cast<const floatx4_t*>(static_cast<const float*>(p.shared) +
+                                             static_cast<size_t>(t) * p.d + c);
+  }
+  for (int j0 = 0; j0 < p.k; j0 += CKB) {
+    int r[CKB];
+    float g[CKB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+    for (int u = 0; u < CKB; ++u) {
+      const size_t q = static_cast<size_t>(t) * p.k + min(j0 + u, p.k - 1);
+      r[u] = p.inv[q];
+      g[u] = p.gates[q];
+    }
+#pragma unroll
+    for (int u = 0; u < CKB; ++u) { pin(r[u]); pin(g[u]); }
+    floatx4_t v[CKB];
+#pragma unroll
+    for (int u = 0; u < CKB; ++u) {
+      const int rr = min(max(r[u], 0), p.y_rows - 1);
+      v[u] = *reinterpret_cast<const floatx4_t*>(y + static_cast<size_t>(rr) * p.d + c);
+    }
+#pragma unroll
+    for (int u = 0; u < CKB; ++u) pin(v[u]);
+#pragma unroll
+    for (int u = 0; u < CKB; ++u)
+      if (j0 + u < p.k) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(g[u], v[u][i], acc[i]);
+      }
   }
   if (p.shared != nullptr) {
-    const float sc = p.shared_scale != nullptr ? p.shared_scale[t] : 1.0f;
-    const floatx4_t v = *reinterpret_cast<const floatx4_t*>(static_cast<const float*>(p.shared) +
-                                                            static_cast<size_t>(t) * p.d + c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, v[i], acc[i]);
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, sv[i], acc[i]);
   }
   *reinterpret_cast<floatx4_t*>(static_cast<float*>(p.out) + static_cast<size_t>(t) * p.d + c) = acc;
 }

@@ -9,6 +9,7 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -35,6 +36,22 @@ __device__ __forceinline__ float silu_fast(float z) {
 __device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Pins a loaded value where it stands: the compiler may otherwise sink a
+// load whose result is used under a condition into that branch and wait on
+// it there alone. Loads issued back to back and then pinned stay in flight
+// together (the waits come in issue order at the pins).
+template <typename V>
+__device__ __forceinline__ void pin(V& v) { asm volatile("" : "+v"(v)); }
+// The same for a wave-uniform value held in a scalar register.
+__device__ __forceinline__ void pin_s(int& v) { asm volatile("" : "+s"(v)); }
+
+// Uniform loads of tables through the constant address space, so they are
+// scalar loads and never enter the vector-memory counter.
+template <class T>
+__device__ __forceinline__ T ldc(const T* q, int i) {
+  return ((const __attribute__((address_space(4))) T*)q)[i];
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -399,12 +399,6 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
 // in its load counter behind the slices it waits for.
 // ---------------------------------------------------------------------------
 
-// Uniform loads of the tile tables through the constant address space, so
-// they are scalar loads and never enter the vector-memory counter.
-template <class T>
-__device__ __forceinline__ T ldc(const T* q, int i) {
-  return ((const __attribute__((address_space(4))) T*)q)[i];
-}
 
 struct Sched {
   int x, j, W;      // XCD, slot on the XCD, workgroups per XCD
@@ -802,7 +796,7 @@ struct PersShape {
 };
 
 // Compute units of the current device (cached per device).
-static int device_cus() {
+int device_cus() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

@@ -106,6 +106,11 @@ WsLayout ws_layout(const moe_config& c) {
   L.tile_e = take(MT * 4);
   L.exp_tile0 = take((E + 1) * 4);
   L.meta = take(16);
+  L.touched = take(E * 16);
+  // split-router logits (one route block)
+  const bool sg = c.shared_h > 0 && c.shared_gate;
+  const int ncp = route_part_cols(c.E, sg);
+  L.part = take(c.T <= kRouteTokensMax ? T * static_cast<size_t>(ncp) * 4 : 0);
   L.ids = take(P * 4);
   L.gates = take(P * 4);
   L.sgate = take(T * 4);
@@ -205,7 +210,8 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* ids, int32_t* coun
   MOE_HIP(launch_scan(sp, s));
   ScatterParams xp{ids, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank), c.T, c.E,
                    c.top_k, rt, perm, inv, counts, offsets, max_m_tiles(c.T * c.top_k, c.E, tm), tm,
-                   at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0), at<int32_t>(ws, L.meta)};
+                   at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0), at<int32_t>(ws, L.meta),
+                   at<int32_t>(ws, L.touched)};
   MOE_HIP(launch_scatter(xp, s));
   return MOE_OK;
 }
@@ -222,6 +228,7 @@ GemmParams gemm_base(const moe_config& c, void* ws, const int32_t* offsets, int 
   g.tile_e = at<int32_t>(ws, L.tile_e);
   g.exp_tile0 = at<int32_t>(ws, L.exp_tile0);
   g.meta = at<int32_t>(ws, L.meta);
+  g.touched = at<int32_t>(ws, L.touched);
   g.E = c.E;
   g.P = c.T * c.top_k;
   g.tile_m = choose_tile_m(g.P, c.E);
@@ -235,7 +242,7 @@ moe_status run_tiles(const moe_config& c, void* ws, const int32_t* offsets, hipS
   const int tm = choose_tile_m(c.T * c.top_k, c.E);
   TilesParams tp{offsets, c.E, c.T * c.top_k, max_m_tiles(c.T * c.top_k, c.E, tm), tm,
                  at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0),
-                 at<int32_t>(ws, L.meta)};
+                 at<int32_t>(ws, L.meta), at<int32_t>(ws, L.touched)};
   MOE_HIP(launch_tiles(tp, s));
   return MOE_OK;
 }
@@ -246,7 +253,7 @@ moe_status run_gate_up(const moe_config& c, void* ws, const void* x, const int32
   GemmParams g = gemm_base(c, ws, offsets, 0);
   g.a = x; g.perm = perm; g.K = c.d;
   g.b0 = wg; g.b1 = wu; g.N = c.h; g.out = act;
-  MOE_HIP(launch_gemm(g, s));
+  MOE_HIP(use_small_gemm(c) ? launch_gemm_small(g, s) : launch_gemm(g, s));
   return MOE_OK;
 }
 
@@ -255,7 +262,7 @@ moe_status run_down(const moe_config& c, void* ws, const void* act, const int32_
   GemmParams g = gemm_base(c, ws, offsets, 1);
   g.a = act; g.K = c.h;
   g.b0 = wd; g.N = c.d; g.out = y;
-  MOE_HIP(launch_gemm(g, s));
+  MOE_HIP(use_small_gemm(c) ? launch_gemm_small(g, s) : launch_gemm(g, s));
   return MOE_OK;
 }
 
@@ -411,17 +418,23 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
     rp.counts = counts_p; rp.offsets = offsets; rp.perm = perm; rp.inv = inv;
     rp.tile_e = at<int32_t>(ws, L.tile_e); rp.exp_tile0 = at<int32_t>(ws, L.exp_tile0);
     rp.meta = at<int32_t>(ws, L.meta);
+    rp.touched = at<int32_t>(ws, L.touched);
     rp.tile_m = tm;
     rp.max_tiles = max_m_tiles(c.T * c.top_k, c.E, tm);
+    rp.part = at<float>(ws, L.part);
+    rp.ncp = route_part_cols(c.E, gated);
+    MOE_HIP(launch_route_split(rp, c.dtype, s));
+  } else {
+    MOE_HIP(launch_route(rp, c.dtype, s));
   }
-  MOE_HIP(launch_route(rp, c.dtype, s));
   MOE_HIP(mark(1));
   if (NB > 1) {
     ScanParams sp{at<int32_t>(ws, L.blk_hist), NB, c.E, counts_p};
     MOE_HIP(launch_scan(sp, s));
     ScatterParams xp{ids_p, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank), c.T, c.E,
                      c.top_k, rt, perm, inv, counts_p, offsets, max_m_tiles(c.T * c.top_k, c.E, tm), tm,
-                     at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0), at<int32_t>(ws, L.meta)};
+                     at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0), at<int32_t>(ws, L.meta),
+                     at<int32_t>(ws, L.touched)};
     MOE_HIP(launch_scatter(xp, s));
   }
   MOE_HIP(mark(2));
@@ -430,13 +443,14 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
   void* act_s = at<void>(ws, L.act_s);
   void* y = at<void>(ws, L.y);
   void* ys = at<void>(ws, L.ys);
+  const bool small = use_small_gemm(c);
   GemmParams g = gemm_base(c, ws, offsets, 0);
   g.a = x; g.perm = perm; g.K = c.d; g.b0 = w->w_gate; g.b1 = w->w_up; g.N = c.h; g.out = act;
   if (c.shared_h > 0) {
     g.shared_T = c.T; g.sa = x; g.sK = c.d; g.sb0 = w->ws_gate; g.sb1 = w->ws_up;
     g.sN = c.shared_h; g.sout = act_s;
   }
-  MOE_HIP(launch_gemm(g, s));
+  MOE_HIP(small ? launch_gemm_small(g, s) : launch_gemm(g, s));
   MOE_HIP(mark(3));
   GemmParams g2 = gemm_base(c, ws, offsets, 1);
   g2.a = act; g2.K = c.h; g2.b0 = w->w_down; g2.N = c.d; g2.out = y;
@@ -444,7 +458,7 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
     g2.shared_T = c.T; g2.sa = act_s; g2.sK = c.shared_h; g2.sb0 = w->ws_down;
     g2.sN = c.d; g2.sout = ys;
   }
-  MOE_HIP(launch_gemm(g2, s));
+  MOE_HIP(small ? launch_gemm_small(g2, s) : launch_gemm(g2, s));
   MOE_HIP(mark(4));
   CombineParams cp{y, inv, gates_p, c.shared_h > 0 ? ys : nullptr, sg, out, c.T, c.d, c.top_k,
                     c.dtype, c.T * c.top_k};

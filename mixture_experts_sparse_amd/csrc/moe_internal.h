@@ -40,9 +40,38 @@ inline int max_m_tiles(int P, int E, int bm = kTileM) { return P / bm + (E < P ?
 // least 256 (prefill-shaped batches), else 128.
 inline int choose_tile_m(int P, int E) { return P >= kTileMLarge * E ? kTileMLarge : kTileM; }
 
+// Short batches (one route block, T <= 64): the router logits are computed
+// by a grid of workgroups (route_part_kernel, 16 columns x 16 tokens each)
+// into a [T, ncp] fp32 buffer, then one workgroup finishes the route and the
+// dispatch. ncp: logit columns (experts, optional shared-gate row) rounded
+// up to 16.
+inline int route_part_cols(int E, bool sgate) { return ceil_div(E + (sgate ? 1 : 0), 16) * 16; }
+
+// Grouped GEMMs for batches with few rows per expert (gemm_small_kernel):
+// a workgroup holds 16 * NT output columns of one expert's weights over the
+// whole reduction in registers, split across NW waves of KS 32-deep MFMA
+// steps each. A shape exists when K <= NW * KS * 32 for KS <= 16, NW <= 8.
+struct SmallShape {
+  int nw, ks;  // 0, 0: no shape fits
+};
+inline SmallShape small_shape(int K) {
+  if (K <= 4 * 4 * 32) return {4, 4};
+  if (K <= 4 * 8 * 32) return {4, 8};
+  if (K <= 4 * 16 * 32) return {4, 16};
+  if (K <= 8 * 16 * 32) return {8, 16};
+  return {0, 0};
+}
+// The small-batch GEMMs run when every expert averages at most 16 rows, the
+// layer is bf16 with no shared expert, and both reductions fit a shape.
+inline bool use_small_gemm(const moe_config& c) {
+  return c.dtype == MOE_BF16 && c.shared_h == 0 &&
+         static_cast<long long>(c.T) * c.top_k <= 16LL * c.E &&
+         small_shape(c.d).nw > 0 && small_shape(c.h).nw > 0;
+}
+
 // Workspace carve-up. Offsets are in bytes from the start of ws.
 struct WsLayout {
-  size_t blk_hist, lrank, counts, offsets, perm, inv, tile_e, exp_tile0, meta;
+  size_t blk_hist, lrank, counts, offsets, perm, inv, tile_e, exp_tile0, meta, touched, part;
   size_t ids, gates, sgate;
   size_t end_tables;
   size_t act, act_s, end_act;
@@ -73,9 +102,13 @@ struct RouteParams {
   int32_t* inv;           // [P]
   int32_t* tile_e;        // [max tiles]
   int32_t* exp_tile0;     // [E+1]
-  int32_t* meta;          // [4]
+  int32_t* meta;          // [4]: tiles, touched experts
+  int32_t* touched;       // [E][4]: non-empty experts in ascending order: {e, first row, rows, 0}
   int max_tiles;
   int tile_m;
+  // split router (route_part_kernel / route_finish_kernel)
+  float* part;            // [T][ncp] fp32 logits
+  int ncp;
 };
 
 // Dispatch from given ids (moe_dispatch): histogram + local ranks.
@@ -108,6 +141,7 @@ struct ScatterParams {
   int32_t* tile_e;
   int32_t* exp_tile0;
   int32_t* meta;
+  int32_t* touched;
 };
 
 // Tile table from offsets alone (standalone gate_up / down / expert_ffn).
@@ -117,6 +151,7 @@ struct TilesParams {
   int32_t* tile_e;
   int32_t* exp_tile0;
   int32_t* meta;
+  int32_t* touched;
 };
 
 // One grouped GEMM launch. Kind 0: gate/up (+ SiLU product) -> act.
@@ -140,6 +175,8 @@ struct GemmParams {
   const int32_t* tile_e;
   const int32_t* exp_tile0;
   const int32_t* meta;
+  const int32_t* touched;  // [E][4] {e, first row, rows, 0} of the non-empty experts (count in
+                           // meta[1]): small-batch kernels
   int E, P;
   int max_mtiles;
   int tile_m;             // M tile of the table (128 or 256)
@@ -184,7 +221,12 @@ hipError_t launch_rank(const RankParams& p, hipStream_t s);
 hipError_t launch_scan(const ScanParams& p, hipStream_t s);
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
 hipError_t launch_tiles(const TilesParams& p, hipStream_t s);
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus();
+
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+hipError_t launch_gemm_small(const GemmParams& p, hipStream_t s);
+hipError_t launch_route_split(const RouteParams& p, int dtype, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 hipError_t launch_scale_rows(const ScaleRowsParams& p, hipStream_t s);
 hipError_t launch_rowdot_sigmoid(const RowDotSigmoidParams& p, hipStream_t s);

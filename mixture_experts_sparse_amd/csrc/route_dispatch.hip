@@ -115,6 +115,25 @@ __device__ void write_tile_table(const int* tp, int E, int max_tiles, int32_t* t
   if (tid == 0) meta[0] = total;
 }
 
+// Non-empty experts in ascending order -> touched[i] = {e, first row, rows,
+// 0} for i < n, and n -> meta[1] (the small-batch GEMMs launch one
+// workgroup row per touched expert and read its whole entry in one load).
+// cnt(e) / first(e) are expert e's row count and first sorted row; flag and
+// pos are LDS scratch of kMaxE + 1 ints. Called by every thread.
+template <typename F, typename G>
+__device__ void write_touched(F cnt, G first, int E, int* flag, int* pos, int32_t* touched,
+                              int32_t* meta) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  for (int e = tid; e < E; e += nthr) flag[e] = cnt(e) > 0 ? 1 : 0;
+  __syncthreads();
+  if (tid < kWave) wave_exclusive_scan256(flag, pos, E);
+  __syncthreads();
+  for (int e = tid; e < E; e += nthr)
+    if (flag[e])
+      *reinterpret_cast<int4*>(touched + 4 * pos[e]) = make_int4(e, first(e), cnt(e), 0);
+  if (tid == 0) meta[1] = pos[E];
+}
+
 // ---------------------------------------------------------------------------
 // route kernel: 512 threads (8 waves), 64 tokens per workgroup.
 //
@@ -152,7 +171,7 @@ struct RouteCfg {
   static constexpr int LW = SW / 8 / 256;        // router loads per router-wave thread per slice
   static constexpr int LGLD = NC + 4;            // logit row stride in LDS (floats)
   // LDS after the logits: selections, per-wave histograms, running counts
-  static constexpr int CARVE = RT * kMaxE + RNW * kMaxE * 4 + 3 * (kMaxE + 1) * 4;
+  static constexpr int CARVE = RT * kMaxE + RNW * kMaxE * 4 + 5 * (kMaxE + 1) * 4;
   static constexpr int XBYTES = RX * SX * 2 > CARVE ? RX * SX * 2 : CARVE;
   static constexpr int LGBYTES = RT * LGLD * 4;
   static constexpr int WBYTES = RR * SW * 2 > LGBYTES ? RR * SW * 2 : LGBYTES;
@@ -374,7 +393,15 @@ __device__ __forceinline__ void load_bias(const RouteParams& p, float* bias) {
 
 // Top-k, gates, logits and shared-gate outputs from the logit rows in LDS;
 // the selection also goes to sel[] for the rank pass. 16-lane group g of the
-// workgroup owns token rows g, g + 32, ...
+// workgroup owns token rows g, g + 32, ...; rounds of 32 rows past the last
+// token are skipped.
+//
+// Each of the k selection steps is a 16-lane maximum of 64-bit keys (one
+// candidate per lane, the lane's best remaining key) followed by removing
+// the winner: a chain of dependent instructions with no memory access and no
+// branch. For k <= 16, lane c keeps slot c's winner in registers and the
+// exponentials, sums and stores run once after the loop, in parallel over
+// the slots.
 template <int NCH, int RT>
 __device__ void route_select(const RouteParams& p, int t0, const float* Lg, const float* bias,
                              uint8_t* sel) {
@@ -385,6 +412,7 @@ __device__ void route_select(const RouteParams& p, int t0, const float* Lg, cons
   const int E = p.E, k = p.k;
 #pragma unroll
   for (int rnd = 0; rnd < RT / 32; ++rnd) {
+    if (t0 + rnd * 32 >= p.T) break;  // uniform: no live token in this or later rounds
     const int r = rnd * 32 + wave * 4 + (lane >> 4);  // token row in the block
     const int t = t0 + r;
     const bool live = t < p.T;                          // uniform across the 16-lane group
@@ -404,45 +432,75 @@ __device__ void route_select(const RouteParams& p, int t0, const float* Lg, cons
     uint64_t key[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) key[f] = f * 16 + c < E ? sel_key(v[f], f * 16 + c) : 0ull;
-    float m = 0.f, ssel = 0.f;
-    float mine = 0.f;  // lane c: un-normalised gate of slot c (k <= 16)
-    for (int j = 0; j < k; ++j) {
-      uint64_t b = key[0];
+    // softmax-all without renormalisation divides by the sum over every expert
+    const bool all = p.mode == MOE_SOFTMAX_ALL && !p.renorm;
+    if (k <= 16) {
+      uint64_t mine = 0ull;  // lane c: slot c's key
+      for (int j = 0; j < k; ++j) {
+        uint64_t b = key[0];
 #pragma unroll
-      for (int f = 1; f < NF; ++f) b = key[f] > b ? key[f] : b;
-      b = row16_max(b);
-      const float bv = key_value(b);
-      const int bi = key_index(b);
-      // keys are unique (they carry the index): the winner's entry drops out
+        for (int f = 1; f < NF; ++f) b = key[f] > b ? key[f] : b;
+        b = row16_max(b);
+        // keys are unique (they carry the index): the winner's entry drops out
 #pragma unroll
-      for (int f = 0; f < NF; ++f) key[f] = key[f] == b ? 0ull : key[f];
-      if (j == 0) m = bv;  // the largest logit
-      const float ej = expf(bv - m);
-      ssel += ej;
-      if ((j & 15) == c) {
-        if (live) {
-          p.ids[static_cast<size_t>(t) * k + j] = bi;
-          // k > 16: un-normalised gate, divided in place below
-          if (k > 16) p.gates[static_cast<size_t>(t) * k + j] = ej;
-        }
-        sel[r * k + j] = static_cast<uint8_t>(bi);
-        mine = ej;
+        for (int f = 0; f < NF; ++f) key[f] = key[f] == b ? 0ull : key[f];
+        mine = j == c ? b : mine;
       }
-    }
-    float denom = ssel;
-    if (p.mode == MOE_SOFTMAX_ALL && !p.renorm) {
-      float sall = 0.f;
+      const float m = __shfl(key_value(mine), lane & 48, kWave);  // slot 0: the largest logit
+      const int mi = key_index(mine);
+      const float ej = c < k ? expf(key_value(mine) - m) : 0.f;
+      float denom = ej;
 #pragma unroll
-      for (int f = 0; f < NF; ++f) if (f * 16 + c < E) sall += expf(v[f] - m);
+      for (int off = 8; off > 0; off >>= 1) denom += __shfl_xor(denom, off, kWave);
+      if (all) {
+        float sall = 0.f;
 #pragma unroll
-      for (int off = 8; off > 0; off >>= 1) sall += __shfl_xor(sall, off, kWave);
-      denom = sall;
-    }
-    const float inv = 1.0f / denom;
-    if (live) {
-      if (k <= 16) {
-        if (c < k) p.gates[static_cast<size_t>(t) * k + c] = mine * inv;
-      } else {
+        for (int f = 0; f < NF; ++f) if (f * 16 + c < E) sall += expf(v[f] - m);
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) sall += __shfl_xor(sall, off, kWave);
+        denom = sall;
+      }
+      if (c < k) {
+        sel[r * k + c] = static_cast<uint8_t>(mi);
+        if (live) {
+          p.ids[static_cast<size_t>(t) * k + c] = mi;
+          p.gates[static_cast<size_t>(t) * k + c] = ej * (1.0f / denom);
+        }
+      }
+    } else {
+      // k > 16: each slot's id and un-normalised gate are stored as it is found
+      float m = 0.f, ssel = 0.f;
+      for (int j = 0; j < k; ++j) {
+        uint64_t b = key[0];
+#pragma unroll
+        for (int f = 1; f < NF; ++f) b = key[f] > b ? key[f] : b;
+        b = row16_max(b);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) key[f] = key[f] == b ? 0ull : key[f];
+        const float bv = key_value(b);
+        const int bi = key_index(b);
+        if (j == 0) m = bv;  // the largest logit
+        const float ej = expf(bv - m);
+        ssel += ej;
+        if ((j & 15) == c) {
+          if (live) {
+            p.ids[static_cast<size_t>(t) * k + j] = bi;
+            p.gates[static_cast<size_t>(t) * k + j] = ej;
+          }
+          sel[r * k + j] = static_cast<uint8_t>(bi);
+        }
+      }
+      float denom = ssel;
+      if (all) {
+        float sall = 0.f;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) if (f * 16 + c < E) sall += expf(v[f] - m);
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) sall += __shfl_xor(sall, off, kWave);
+        denom = sall;
+      }
+      const float inv = 1.0f / denom;
+      if (live) {
         for (int j = c; j < k; j += 16) {
           float* g = p.gates + static_cast<size_t>(t) * k + j;
           *g = *g * inv;
@@ -452,33 +510,114 @@ __device__ void route_select(const RouteParams& p, int t0, const float* Lg, cons
   }
 }
 
-template <int NCH, bool BF16, int RT>
-__global__ __launch_bounds__(RTHR) void route_kernel(RouteParams p) {
+// The same selection by rank counting, for blocks where T_block * E^2 is
+// small (few tokens): every (token, expert) item counts the experts whose
+// key beats its own -- a larger logit, or an equal logit at a lower index --
+// and an item of rank j < k is slot j. The items run in parallel over the
+// workgroup, so the cost is E compares per item instead of k dependent
+// 16-lane maximum steps. The logit rows in LDS are rewritten in place as
+// order-preserving 32-bit keys; gates then follow per token on 16-lane
+// groups (lane c: slots c, c + 16, ...). Called by every thread.
+__device__ __forceinline__ uint32_t order_key32(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_value32(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+template <int NCH, int RT>
+__device__ void route_select_rank(const RouteParams& p, int t0, float* Lg, const float* bias,
+                                  uint8_t* sel) {
   using C = RouteCfg<NCH, RT>;
-  // x ring during the logits, then the selections and histograms; router
-  // ring during the logits, then the logit rows
-  __shared__ __align__(16) uint16_t Xr[(BF16 ? C::XBYTES : C::CARVE) / 2];
-  __shared__ __align__(16) uint16_t Wr[(BF16 ? C::WBYTES : C::LGBYTES) / 2];
-  uint8_t* sel = reinterpret_cast<uint8_t*>(Xr);                          // [RT * kMaxE]
+  constexpr int NF = C::NF;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15;
+  const int E = p.E, k = p.k;
+  const int nt = min(RT, p.T - t0);
+  uint32_t* K32 = reinterpret_cast<uint32_t*>(Lg);
+  // keys (and the optional logits / shared-gate outputs)
+  for (int r0 = 0; r0 < nt; r0 += 32) {
+    const int r = r0 + wave * 4 + (lane >> 4);
+    if (r < nt) {
+      const int t = t0 + r;
+      float* row = Lg + r * C::LGLD;
+      if (p.sgate != nullptr && c == 0) p.sgate[t] = sigmoid_f32(row[E]);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int e = f * 16 + c;
+        if (e < E) {
+          const float val = row[e] + bias[f];
+          if (p.logits != nullptr) p.logits[static_cast<size_t>(t) * E + e] = val;
+          K32[r * C::LGLD + e] = order_key32(val + 0.0f);  // -0 -> +0
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nt * E; i += RTHR) {
+    const int r = i / E, e = i - r * E;
+    const uint32_t* row = K32 + r * C::LGLD;
+    const uint32_t o = row[e];
+    int rank = 0;
+#pragma unroll 8
+    for (int q = 0; q < E; ++q) {
+      const uint32_t oq = row[q];
+      rank += (oq > o || (oq == o && q < e)) ? 1 : 0;
+    }
+    if (rank < k) {
+      sel[r * k + rank] = static_cast<uint8_t>(e);
+      p.ids[static_cast<size_t>(t0 + r) * k + rank] = e;
+    }
+  }
+  __syncthreads();
+  const bool all = p.mode == MOE_SOFTMAX_ALL && !p.renorm;
+  for (int r0 = 0; r0 < nt; r0 += 32) {
+    const int r = r0 + wave * 4 + (lane >> 4);
+    if (r < nt) {  // uniform across the 16-lane group
+      const int t = t0 + r;
+      const uint32_t* row = K32 + r * C::LGLD;
+      const float m = order_value32(row[sel[r * k]]);  // slot 0: the largest logit
+      float sum = 0.f;
+      for (int j = c; j < k; j += 16) sum += expf(order_value32(row[sel[r * k + j]]) - m);
+      if (all) {
+        sum = 0.f;
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          if (f * 16 + c < E) sum += expf(order_value32(row[f * 16 + c]) - m);
+      }
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+      const float inv = 1.0f / sum;
+      for (int j = c; j < k; j += 16)
+        p.gates[static_cast<size_t>(t) * k + j] = expf(order_value32(row[sel[r * k + j]]) - m) * inv;
+    }
+  }
+}
+
+// Selection, then the block's histogram and ranks (several route blocks) or
+// the whole dispatch (one route block), from the logit rows in LDS. The
+// selections, histograms and scans live in the LDS at carve (CARVE bytes).
+template <int NCH, int RT>
+__device__ void route_tail(const RouteParams& p, int t0, float* Lg, const float* bias,
+                           void* carve) {
+  uint8_t* sel = static_cast<uint8_t*>(carve);                             // [RT * kMaxE]
   int (*wh)[kMaxE] = reinterpret_cast<int (*)[kMaxE]>(sel + RT * kMaxE);  // [RNW][kMaxE]
   int* run = reinterpret_cast<int*>(wh + RNW);                             // [kMaxE + 1]
   int* scan_a = run + (kMaxE + 1);
   int* scan_b = scan_a + (kMaxE + 1);
-  float* Lg = reinterpret_cast<float*>(Wr);                                // [RT][LGLD]
-  const int t0 = blockIdx.x * RT;
-  float bias[C::NF];
-  load_bias<NCH>(p, bias);
-  {
-    floatx4_t acc[C::NF2];
-    if constexpr (BF16) route_logits_bf16<NCH, RT>(p, t0, acc, Xr, Wr);
-    else route_logits_f32<NCH, RT>(p, t0, acc);
-    store_logits<NCH, RT>(acc, Lg);
-  }
-  __syncthreads();
-  route_select<NCH, RT>(p, t0, Lg, bias, sel);
+  int* flag = scan_b + (kMaxE + 1);
+  int* pos = flag + (kMaxE + 1);
+  const int nt = min(RT, p.T - t0);
+  // rank counting costs E compares per (token, expert) item, spread over the
+  // workgroup; the 16-lane maximum steps cost a fixed dependent chain per 32
+  // tokens: the first is cheaper while the block's T * E^2 stays small
+  if (static_cast<long long>(nt) * p.E * p.E <= (1LL << 17))
+    route_select_rank<NCH, RT>(p, t0, Lg, bias, sel);
+  else
+    route_select<NCH, RT>(p, t0, Lg, bias, sel);
   if (p.blk_hist == nullptr && p.counts == nullptr) return;
   __syncthreads();
-  const int nt = min(RT, p.T - t0);
   const int npairs = nt * p.k;
   int32_t* lrank = p.lrank + static_cast<size_t>(t0) * p.k;
   block_rank<RTHR>(sel, npairs, p.E, lrank, wh, run);
@@ -498,10 +637,157 @@ __global__ __launch_bounds__(RTHR) void route_kernel(RouteParams p) {
   if (tid == 0) p.offsets[p.E] = scan_a[p.E];
   write_tile_table(scan_b, p.E, p.max_tiles, p.tile_e, p.exp_tile0, p.meta);
   for (int q = tid; q < npairs; q += RTHR) {
-    const int pos = scan_a[sel[q]] + lrank[q];
-    p.perm[pos] = q;
-    p.inv[q] = pos;
+    const int pos_q = scan_a[sel[q]] + lrank[q];
+    p.perm[pos_q] = q;
+    p.inv[q] = pos_q;
   }
+  if (p.touched != nullptr)
+    write_touched([&](int e) { return run[e]; }, [&](int e) { return scan_a[e]; }, p.E, flag, pos,
+                  p.touched, p.meta);
+}
+
+template <int NCH, bool BF16, int RT>
+__global__ __launch_bounds__(RTHR) void route_kernel(RouteParams p) {
+  using C = RouteCfg<NCH, RT>;
+  // x ring during the logits, then the selections and histograms; router
+  // ring during the logits, then the logit rows
+  __shared__ __align__(16) uint16_t Xr[(BF16 ? C::XBYTES : C::CARVE) / 2];
+  __shared__ __align__(16) uint16_t Wr[(BF16 ? C::WBYTES : C::LGBYTES) / 2];
+  float* Lg = reinterpret_cast<float*>(Wr);  // [RT][LGLD]
+  const int t0 = blockIdx.x * RT;
+  float bias[C::NF];
+  load_bias<NCH>(p, bias);
+  {
+    floatx4_t acc[C::NF2];
+    if constexpr (BF16) route_logits_bf16<NCH, RT>(p, t0, acc, Xr, Wr);
+    else route_logits_f32<NCH, RT>(p, t0, acc);
+    store_logits<NCH, RT>(acc, Lg);
+  }
+  __syncthreads();
+  route_tail<NCH, RT>(p, t0, Lg, bias, Xr);
+}
+
+// ---------------------------------------------------------------------------
+// Split router for one route block (T <= 64). A single workgroup streaming
+// the whole router matrix is bound by its own load latency, so the logits
+// are spread over workgroups: workgroup (c, g) computes logit columns
+// 16 c .. 16 c + 15 (router rows, then the shared-gate row, then padding) for
+// tokens 16 g .. 16 g + 15 over the whole of K, its 8 waves each taking one
+// eighth of K with every load of its share issued at once; the eight partial
+// tiles are added in wave order through LDS and the logits go to a [T, ncp]
+// fp32 buffer. route_finish_kernel then runs the selection and the dispatch.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(RTHR) void route_part_kernel(RouteParams p) {
+  __shared__ float red[RNW][16][16];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = blockIdx.x * 16 + (lane & 15);
+  const int tok = min(static_cast<int>(blockIdx.y) * 16 + (lane & 15), p.T - 1);
+  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // K in batches of 8 steps: the batch's loads are all issued, then used
+  constexpr int KB = 8;
+  if constexpr (BF16) {
+    const int kw = (p.d + RNW * 32 - 1) / (RNW * 32) * 32;  // K per wave, whole 32-deep steps
+    const int k0 = wave * kw, k1 = min(p.d, k0 + kw);
+    const uint16_t* W = static_cast<const uint16_t*>(p.w_router);
+    const uint16_t* WS = static_cast<const uint16_t*>(p.w_sgate);
+    // padding columns reread router row 0; their sums are never used
+    const uint16_t* wrow = col < p.E ? W + static_cast<size_t>(col) * p.d
+                                     : (col == p.E && WS != nullptr ? WS : W);
+    const uint16_t* xrow = static_cast<const uint16_t*>(p.x) + static_cast<size_t>(tok) * p.d;
+    const int g = (lane >> 4) * 8;
+    for (int kk = k0; kk < k1; kk += 32 * KB) {
+      u32x4_t av[KB], bv[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int kq = min(kk + 32 * u + g, p.d - 8);
+        av[u] = *reinterpret_cast<const u32x4_t*>(xrow + kq);
+        bv[u] = *reinterpret_cast<const u32x4_t*>(wrow + kq);
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) { pin(av[u]); pin(bv[u]); }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        // d and k0 are multiples of 8: the 8 values are all in range or none is
+        const bool in = kk + 32 * u + g < k1;
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, in ? av[u] : z),
+                                                      __builtin_bit_cast(bf16x8_t, in ? bv[u] : z),
+                                                      acc, 0, 0, 0);
+      }
+    }
+  } else {
+    const int kw = (p.d + RNW * 16 - 1) / (RNW * 16) * 16;
+    const int k0 = wave * kw, k1 = min(p.d, k0 + kw);
+    const float* W = static_cast<const float*>(p.w_router);
+    const float* WS = static_cast<const float*>(p.w_sgate);
+    const float* wrow = col < p.E ? W + static_cast<size_t>(col) * p.d
+                                  : (col == p.E && WS != nullptr ? WS : W);
+    const float* xrow = static_cast<const float*>(p.x) + static_cast<size_t>(tok) * p.d;
+    const int g = (lane >> 4) * 4;
+    for (int kk = k0; kk < k1; kk += 16 * KB) {
+      floatx4_t av[KB], bv[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int kq = min(kk + 16 * u + g, p.d - 4);
+        av[u] = *reinterpret_cast<const floatx4_t*>(xrow + kq);
+        bv[u] = *reinterpret_cast<const floatx4_t*>(wrow + kq);
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) { pin(av[u]); pin(bv[u]); }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const bool in = kk + 16 * u + g < k1;
+        const floatx4_t z = {0.f, 0.f, 0.f, 0.f};
+        const floatx4_t a = in ? av[u] : z, b = in ? bv[u] : z;
+        // step i covers K indices kk + 16 u + 4 (lane / 16) + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+      }
+    }
+  }
+  // this lane: column lane % 16, token rows 4 (lane / 16) + i of the group
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][(lane >> 4) * 4 + i][lane & 15] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < RNW; ++w) v += red[w][r][c];
+    const int t = blockIdx.y * 16 + r;
+    if (t < p.T) p.part[static_cast<size_t>(t) * p.ncp + blockIdx.x * 16 + c] = v;
+  }
+}
+
+template <int NCH>
+__global__ __launch_bounds__(RTHR) void route_finish_kernel(RouteParams p) {
+  using C = RouteCfg<NCH, RTM>;
+  constexpr int IPT = RTM * C::NC / RTHR;  // logit slots per thread
+  __shared__ __align__(16) uint8_t carve[C::CARVE];
+  __shared__ __align__(16) float Lg[C::LGBYTES / 4];
+  float bias[C::NF];
+  load_bias<NCH>(p, bias);
+  const int tid = threadIdx.x;
+  // every load issued before the first use (clamped addresses, no branches)
+  float v[IPT];
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const int i = tid + j * RTHR;
+    const int r = i / C::NC, c = i - (i / C::NC) * C::NC;
+    v[j] = p.part[static_cast<size_t>(min(r, p.T - 1)) * p.ncp + min(c, p.ncp - 1)];
+  }
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) pin(v[j]);
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const int i = tid + j * RTHR;
+    const int r = i / C::NC, c = i - (i / C::NC) * C::NC;
+    Lg[r * C::LGLD + c] = (r < p.T && c < p.ncp) ? v[j] : 0.f;
+  }
+  __syncthreads();
+  route_tail<NCH, RTM>(p, 0, Lg, bias, carve);
 }
 
 // ---------------------------------------------------------------------------
@@ -580,6 +866,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanParams p) {
 __global__ __launch_bounds__(256) void scatter_kernel(ScatterParams p) {
   __shared__ int offs[kMaxE + 1];
   __shared__ int tp[kMaxE + 1];
+  __shared__ int flag[kMaxE + 1];
+  __shared__ int tpos[kMaxE + 1];
   const int tid = threadIdx.x, E = p.E;
   if (tid < kWave) wave_exclusive_scan256(p.counts, offs, E);
   if (blockIdx.x == 0) {
@@ -589,6 +877,9 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterParams p) {
     __syncthreads();
     for (int e = tid; e <= E; e += 256) p.offsets[e] = offs[e];
     write_tile_table(tp, E, p.max_tiles, p.tile_e, p.exp_tile0, p.meta);
+    if (p.touched != nullptr)
+      write_touched([&](int e) { return p.counts[e]; }, [&](int e) { return offs[e]; }, E, flag,
+                    tpos, p.touched, p.meta);
   }
   __syncthreads();
   const int P = p.T * p.k;
@@ -607,16 +898,27 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterParams p) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void tiles_kernel(TilesParams p) {
   __shared__ int tp[kMaxE + 1];
+  __shared__ int cnt[kMaxE + 1];
+  __shared__ int first[kMaxE + 1];
+  __shared__ int flag[kMaxE + 1];
+  __shared__ int pos[kMaxE + 1];
   const int tid = threadIdx.x;
   if (tid < p.E) {
-    // caller-provided offsets: counts clamped to [0, P] so the table stays in bounds
+    // caller-provided offsets: counts clamped to [0, P] so the table stays in
+    // bounds; the touched entries clamp rows the way the GEMMs do
     const int c = min(max(p.offsets[tid + 1] - p.offsets[tid], 0), p.P);
+    const int r0 = min(max(p.offsets[tid], 0), p.P);
+    first[tid] = r0;
+    cnt[tid] = min(max(p.offsets[tid + 1], r0), p.P) - r0;
     tp[tid] = (c + p.tile_m - 1) / p.tile_m;
   }
   __syncthreads();
   if (tid < kWave) wave_exclusive_scan256(tp, tp, p.E);
   __syncthreads();
   write_tile_table(tp, p.E, p.max_tiles, p.tile_e, p.exp_tile0, p.meta);
+  if (p.touched != nullptr)
+    write_touched([&](int e) { return cnt[e]; }, [&](int e) { return first[e]; }, p.E, flag, pos,
+                  p.touched, p.meta);
 }
 
 // ---------------------------------------------------------------------------
@@ -665,6 +967,29 @@ hipError_t launch_route(const RouteParams& p, int dtype, hipStream_t s) {
     case 3: launch_route_nch<3>(p, dtype, nb, s); break;
     case 4: launch_route_nch<4>(p, dtype, nb, s); break;
     case 5: launch_route_nch<5>(p, dtype, nb, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int NCH>
+static void launch_finish_nch(const RouteParams& p, hipStream_t s) {
+  route_finish_kernel<NCH><<<1, RTHR, 0, s>>>(p);
+}
+
+hipError_t launch_route_split(const RouteParams& p, int dtype, hipStream_t s) {
+  const int cols = p.E + (p.w_sgate != nullptr ? 1 : 0);
+  if (p.T < 1 || p.T > RTM || p.part == nullptr || p.ncp != ceil_div(cols, 16) * 16)
+    return hipErrorInvalidValue;
+  const dim3 grid(p.ncp / 16, ceil_div(p.T, 16));
+  if (dtype == MOE_BF16) route_part_kernel<true><<<grid, RTHR, 0, s>>>(p);
+  else route_part_kernel<false><<<grid, RTHR, 0, s>>>(p);
+  switch (ceil_div(cols, 64)) {
+    case 1: launch_finish_nch<1>(p, s); break;
+    case 2: launch_finish_nch<2>(p, s); break;
+    case 3: launch_finish_nch<3>(p, s); break;
+    case 4: launch_finish_nch<4>(p, s); break;
+    case 5: launch_finish_nch<5>(p, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
