@@ -421,6 +421,8 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
     rp.touched = at<int32_t>(ws, L.touched);
     rp.tile_m = tm;
     rp.max_tiles = max_m_tiles(c.T * c.top_k, c.E, tm);
+    // the small-batch GEMMs need no tile table
+    if (use_small_gemm(c)) rp.tile_e = nullptr;
     rp.part = at<float>(ws, L.part);
     rp.ncp = route_part_cols(c.E, gated);
     MOE_HIP(launch_route_split(rp, c.dtype, s));

@@ -99,11 +99,9 @@ __device__ void block_rank(const uint8_t* sel, int npairs, int E, int32_t* lrank
 
 // Tile table writes shared by the scan, tiles and single-block paths:
 // mt[e] = ceil(cnt[e] / kTileM) scanned into tp[]; tile_e[i] = owning expert.
-__device__ void write_tile_table(const int* tp, int E, int max_tiles, int32_t* tile_e,
-                                 int32_t* exp_tile0, int32_t* meta) {
+// tile_e[i] = the expert owning tile i < total (tp: tile prefix in LDS).
+__device__ void fill_tile_e(const int* tp, int E, int total, int32_t* tile_e) {
   const int tid = threadIdx.x, nthr = blockDim.x;
-  const int total = min(tp[E], max_tiles);
-  for (int e = tid; e <= E; e += nthr) exp_tile0[e] = tp[e];
   for (int i = tid; i < total; i += nthr) {
     int lo = 0, hi = E - 1;  // last e with tp[e] <= i
     while (lo < hi) {
@@ -112,6 +110,14 @@ __device__ void write_tile_table(const int* tp, int E, int max_tiles, int32_t* t
     }
     tile_e[i] = lo;
   }
+}
+
+__device__ void write_tile_table(const int* tp, int E, int max_tiles, int32_t* tile_e,
+                                 int32_t* exp_tile0, int32_t* meta) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int total = min(tp[E], max_tiles);
+  for (int e = tid; e <= E; e += nthr) exp_tile0[e] = tp[e];
+  fill_tile_e(tp, E, total, tile_e);
   if (tid == 0) meta[0] = total;
 }
 
@@ -171,7 +177,7 @@ struct RouteCfg {
   static constexpr int LW = SW / 8 / 256;        // router loads per router-wave thread per slice
   static constexpr int LGLD = NC + 4;            // logit row stride in LDS (floats)
   // LDS after the logits: selections, per-wave histograms, running counts
-  static constexpr int CARVE = RT * kMaxE + RNW * kMaxE * 4 + 5 * (kMaxE + 1) * 4;
+  static constexpr int CARVE = RT * kMaxE + RNW * kMaxE * 4 + 3 * (kMaxE + 1) * 4;
   static constexpr int XBYTES = RX * SX * 2 > CARVE ? RX * SX * 2 : CARVE;
   static constexpr int LGBYTES = RT * LGLD * 4;
   static constexpr int WBYTES = RR * SW * 2 > LGBYTES ? RR * SW * 2 : LGBYTES;
@@ -375,6 +381,21 @@ __device__ __forceinline__ uint64_t row16_max(uint64_t a) {
   a = dpp_max<0x140>(a);  // row_mirror
   return a;
 }
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float a) {
+  return a + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of each row, every lane ending with it: after the
+// two quad permutations each quad holds its sum in all four lanes, so each
+// mirror then adds a partner block of equal values. Same order on every
+// lane, so the result is identical across the row.
+__device__ __forceinline__ float row16_sum(float a) {
+  a = dpp_add<0xB1>(a);
+  a = dpp_add<0x4E>(a);
+  a = dpp_add<0x141>(a);
+  a = dpp_add<0x140>(a);
+  return a;
+}
 
 // Router bias of this lane's columns (f * 16 + lane % 16), loaded before
 // the logits so that no load is outstanding in the selection.
@@ -450,15 +471,12 @@ __device__ void route_select(const RouteParams& p, int t0, const float* Lg, cons
       const int mi = key_index(mine);
       const float ej = c < k ? expf(key_value(mine) - m) : 0.f;
       float denom = ej;
-#pragma unroll
-      for (int off = 8; off > 0; off >>= 1) denom += __shfl_xor(denom, off, kWave);
+      denom = row16_sum(denom);
       if (all) {
         float sall = 0.f;
 #pragma unroll
         for (int f = 0; f < NF; ++f) if (f * 16 + c < E) sall += expf(v[f] - m);
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) sall += __shfl_xor(sall, off, kWave);
-        denom = sall;
+        denom = row16_sum(sall);
       }
       if (c < k) {
         sel[r * k + c] = static_cast<uint8_t>(mi);
@@ -495,9 +513,7 @@ __device__ void route_select(const RouteParams& p, int t0, const float* Lg, cons
         float sall = 0.f;
 #pragma unroll
         for (int f = 0; f < NF; ++f) if (f * 16 + c < E) sall += expf(v[f] - m);
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) sall += __shfl_xor(sall, off, kWave);
-        denom = sall;
+        denom = row16_sum(sall);
       }
       const float inv = 1.0f / denom;
       if (live) {
@@ -557,14 +573,19 @@ __device__ void route_select_rank(const RouteParams& p, int t0, float* Lg, const
   __syncthreads();
   for (int i = tid; i < nt * E; i += RTHR) {
     const int r = i / E, e = i - r * E;
-    const uint32_t* row = K32 + r * C::LGLD;
+    const uint32_t* row = K32 + r * C::LGLD;  // 16-byte aligned rows
     const uint32_t o = row[e];
-    int rank = 0;
-#pragma unroll 8
-    for (int q = 0; q < E; ++q) {
-      const uint32_t oq = row[q];
-      rank += (oq > o || (oq == o && q < e)) ? 1 : 0;
+    // four keys per LDS read, four independent counts
+    int n4[4] = {0, 0, 0, 0};
+    int q = 0;
+#pragma unroll 4
+    for (; q + 4 <= E; q += 4) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + q);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) n4[u] += (v[u] > o || (v[u] == o && q + u < e)) ? 1 : 0;
     }
+    for (; q < E; ++q) n4[0] += (row[q] > o || (row[q] == o && q < e)) ? 1 : 0;
+    const int rank = (n4[0] + n4[1]) + (n4[2] + n4[3]);
     if (rank < k) {
       sel[r * k + rank] = static_cast<uint8_t>(e);
       p.ids[static_cast<size_t>(t0 + r) * k + rank] = e;
@@ -586,12 +607,55 @@ __device__ void route_select_rank(const RouteParams& p, int t0, float* Lg, const
         for (int f = 0; f < NF; ++f)
           if (f * 16 + c < E) sum += expf(order_value32(row[f * 16 + c]) - m);
       }
-#pragma unroll
-      for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+      sum = row16_sum(sum);
       const float inv = 1.0f / sum;
       for (int j = c; j < k; j += 16)
         p.gates[static_cast<size_t>(t) * k + j] = expf(order_value32(row[sel[r * k + j]]) - m) * inv;
     }
+  }
+}
+
+// One wave finishes the counting sort's tables for a single route block:
+// from the per-expert counts (run) it writes counts, offsets (also to
+// scan_a, total at E), the tile prefix (exp_tile0 and scan_b, total at E),
+// the tile count and the touched table; lane l owns experts 4l .. 4l + 3.
+// The three prefix sums share one pass of shuffles.
+__device__ void finish_scan(const RouteParams& p, const int* run, int* scan_a, int* scan_b) {
+  const int lane = lane_id();
+  const int E = p.E, b = lane * 4;
+  int v[4], tl[4], fl[4];
+  int sv = 0, st = 0, sf = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = b + i < E ? run[b + i] : 0;
+    tl[i] = (v[i] + p.tile_m - 1) / p.tile_m;
+    fl[i] = v[i] > 0 ? 1 : 0;
+    sv += v[i]; st += tl[i]; sf += fl[i];
+  }
+  int iv = sv, it = st, jf = sf;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int a = __shfl_up(iv, off, kWave), c = __shfl_up(it, off, kWave),
+              d = __shfl_up(jf, off, kWave);
+    if (lane >= off) { iv += a; it += c; jf += d; }
+  }
+  int ev = iv - sv, et = it - st, ef = jf - sf;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = b + i;
+    if (e < E) {
+      scan_a[e] = ev; scan_b[e] = et;
+      p.counts[e] = v[i]; p.offsets[e] = ev; p.exp_tile0[e] = et;
+      if (fl[i] && p.touched != nullptr)
+        *reinterpret_cast<int4*>(p.touched + 4 * ef) = make_int4(e, ev, v[i], 0);
+    }
+    ev += v[i]; et += tl[i]; ef += fl[i];
+  }
+  if (lane == kWave - 1) {
+    scan_a[E] = iv; scan_b[E] = it;
+    p.offsets[E] = iv; p.exp_tile0[E] = it;
+    p.meta[0] = min(it, p.max_tiles);
+    p.meta[1] = jf;
   }
 }
 
@@ -606,8 +670,6 @@ __device__ void route_tail(const RouteParams& p, int t0, float* Lg, const float*
   int* run = reinterpret_cast<int*>(wh + RNW);                             // [kMaxE + 1]
   int* scan_a = run + (kMaxE + 1);
   int* scan_b = scan_a + (kMaxE + 1);
-  int* flag = scan_b + (kMaxE + 1);
-  int* pos = flag + (kMaxE + 1);
   const int nt = min(RT, p.T - t0);
   // rank counting costs E compares per (token, expert) item, spread over the
   // workgroup; the 16-lane maximum steps cost a fixed dependent chain per 32
@@ -628,22 +690,15 @@ __device__ void route_tail(const RouteParams& p, int t0, float* Lg, const float*
   }
   // One route block covers every token: finish the dispatch here.
   __syncthreads();
-  if (tid < kWave) wave_exclusive_scan256(run, scan_a, p.E);  // offsets
-  for (int e = tid; e < p.E; e += RTHR) scan_b[e] = (run[e] + p.tile_m - 1) / p.tile_m;
+  if (tid < kWave) finish_scan(p, run, scan_a, scan_b);
   __syncthreads();
-  if (tid < kWave) wave_exclusive_scan256(scan_b, scan_b, p.E);  // tile prefix (in place per lane)
-  __syncthreads();
-  for (int e = tid; e < p.E; e += RTHR) { p.counts[e] = run[e]; p.offsets[e] = scan_a[e]; }
-  if (tid == 0) p.offsets[p.E] = scan_a[p.E];
-  write_tile_table(scan_b, p.E, p.max_tiles, p.tile_e, p.exp_tile0, p.meta);
+  // the grouped GEMMs' tile table (not needed by the small-batch GEMMs)
+  if (p.tile_e != nullptr) fill_tile_e(scan_b, p.E, min(scan_b[p.E], p.max_tiles), p.tile_e);
   for (int q = tid; q < npairs; q += RTHR) {
     const int pos_q = scan_a[sel[q]] + lrank[q];
     p.perm[pos_q] = q;
     p.inv[q] = pos_q;
   }
-  if (p.touched != nullptr)
-    write_touched([&](int e) { return run[e]; }, [&](int e) { return scan_a[e]; }, p.E, flag, pos,
-                  p.touched, p.meta);
 }
 
 template <int NCH, bool BF16, int RT>
