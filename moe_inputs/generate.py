@@ -62,6 +62,15 @@ def zipf_router_bias(E: int) -> np.ndarray:
     return (2.0 * np.log(1.0 / np.power(e + 1.0, 1.1))).astype(np.float32)
 
 
+def balance_router_bias(E: int, step: float = 1e-3) -> np.ndarray:
+    """A selection-only balance bias as the update rule of "Small MoE
+    Architecture, in depth" leaves it: whole multiples of the bias step
+    (default 1e-3), here b_e = step * (((7 e + 3) mod 41) - 20), at most 20
+    steps either way; deterministic (no draw), float32."""
+    e = np.arange(E, dtype=np.int64)
+    return (step * (((7 * e + 3) % 41) - 20)).astype(np.float32)
+
+
 def _upcycled_experts(spec: MoESpec, rng: np.random.Generator):
     S, C, h, d = spec.upcycle_slices, spec.upcycle_copies, spec.h, spec.d
     if S * C != spec.E:
@@ -101,6 +110,8 @@ def generate(spec: MoESpec) -> dict:
     out = {"spec": spec, "x": _cast(spec, x), "w_router": _cast(spec, w_router)}
     if spec.router_bias == "zipf":
         out["b_router"] = zipf_router_bias(spec.E)
+    elif spec.router_bias == "balance":
+        out["b_router"] = balance_router_bias(spec.E)
     elif spec.router_bias is not None:
         raise ValueError(f"unknown router bias {spec.router_bias!r}")
     else:

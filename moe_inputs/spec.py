@@ -21,6 +21,14 @@ distributions the generator draws from. The five named workloads are:
 * ``shared_routed``   T=8192, d=2048, E=60, h=1408, k=4, bf16, softmax over all
                       60 without renormalisation; plus one always-on shared
                       SwiGLU of hidden 5632 scaled by sigmoid(w_s . x).
+* ``small_moe_sigmoid`` the defaults of the SmallMoE module of "Small MoE
+                      Architecture, in depth" (d=1024, 64 experts, top-8,
+                      expert hidden 256, one ungated shared expert of hidden
+                      1024) on T=4096 tokens, bf16: sigmoid affinities, top-8
+                      on affinity + balance bias, gates = affinities of the
+                      chosen experts renormalised. The balance bias is a fixed
+                      pattern of multiples of the page's bias step 1e-3, at
+                      most 20 steps either way (``balance_router_bias``).
 
 Standard deviations are given as std (not variance). ``small_spec`` builds
 reduced shapes with the same structure for tests that the CPU oracle must
@@ -35,6 +43,7 @@ from typing import Optional
 # Gate modes. Values match the C ABI enum ``moe_score_mode``.
 SOFTMAX_ALL = 0
 SOFTMAX_SELECTED = 1
+SIGMOID = 2
 
 # Activation dtypes. Values match the C ABI enum ``moe_dtype``.
 F32 = 0
@@ -55,7 +64,8 @@ class MoESpec:
     x_std: float = 1.0
     router_std: float = 0.02
     expert_std: float = 0.02
-    # "zipf": b_e = 2*ln(1/(e+1)**1.1); None: no bias vector
+    # "zipf": b_e = 2*ln(1/(e+1)**1.1) added to the logits; "balance": a
+    # selection-only balance bias (SIGMOID mode); None: no bias vector
     router_bias: Optional[str] = None
     # 0: no shared expert
     shared_h: int = 0
@@ -111,6 +121,10 @@ SPECS = {
         name="shared_routed", T=8192, d=2048, E=60, h=1408, k=4, dtype=BF16,
         mode=SOFTMAX_ALL, renormalize=False, router_std=0.02, expert_std=0.02,
         shared_h=5632, shared_gate=True),
+    "small_moe_sigmoid": MoESpec(
+        name="small_moe_sigmoid", T=4096, d=1024, E=64, h=256, k=8, dtype=BF16,
+        mode=SIGMOID, renormalize=True, router_std=0.02, expert_std=0.02,
+        router_bias="balance", shared_h=1024, shared_gate=False),
 }
 
 DECODE_TOKENS = (1, 4, 16, 64)

@@ -36,6 +36,19 @@ Steps, in the order the pages give them:
    Architecture, in depth", section "A small MoE layer in PyTorch"); the
    sigmoid(w_s . x) scale on it is an input option of the shared-plus-routed
    workload, not a formula on the pages.
+
+Sigmoid scoring ("Small MoE Architecture, in depth", sections "A small MoE
+layer in PyTorch" and "Balancing without fighting the loss"): affinities
+s = sigmoid(L) of the bias-free logits; the top-k is taken on s + b, where b
+is a balance bias that only steers the choice; the gates are the raw s of
+the chosen experts divided by their sum. Steps 4-7 are unchanged.
+
+Routing statistics (``routing_stats``): the per-expert token share, the mean
+router probability per expert, the mean router entropy and the Switch
+load-balance term alpha * N * sum_e f_e P_e ("Mixture-of-Experts -- more
+capacity per byte of weight", section "What's wired today"; "Small MoE
+Architecture, in depth", section "Fine-tuning a small MoE", which asks for
+token share and router entropy to be logged).
 """
 
 from __future__ import annotations
@@ -44,6 +57,7 @@ import numpy as np
 
 SOFTMAX_ALL = 0
 SOFTMAX_SELECTED = 1
+SIGMOID = 2
 
 NEAR_TIE_EPS = 1e-5
 
@@ -118,6 +132,20 @@ def topk_select(L, k):
     return np.argsort(-L, axis=1, kind="stable")[:, :k].astype(np.int64)
 
 
+def selection_scores(L, mode, sel_bias=None):
+    """The scores the top-k is taken on. Softmax modes: the logits (any bias is
+    already inside L, it moves the softmax too). SIGMOID: sigmoid(L) + b, the
+    balance bias b steering the choice only ("Small MoE Architecture, in
+    depth", section "A small MoE layer in PyTorch": topk of scores plus the
+    balance bias)."""
+    if mode != SIGMOID:
+        return L
+    S = sigmoid(L)
+    if sel_bias is not None:
+        S = S + to_f64(sel_bias)[None, :]
+    return S
+
+
 def gate_weights(L, ids, mode, renormalize):
     """Gate weights for the selected experts.
 
@@ -138,11 +166,53 @@ def gate_weights(L, ids, mode, renormalize):
         if renormalize:
             g = g / np.sum(g, axis=1, keepdims=True)
         return g, None
+    if mode == SIGMOID:
+        # the raw affinities of the chosen experts weight the outputs; the
+        # balance bias is not part of them ("Small MoE Architecture, in
+        # depth", sections "A small MoE layer in PyTorch" and "Balancing
+        # without fighting the loss")
+        g = np.take_along_axis(sigmoid(L), ids, axis=1)
+        if renormalize:
+            g = g / np.sum(g, axis=1, keepdims=True)
+        return g, None
     raise ValueError(f"unknown gate mode {mode}")
 
 
+def router_probs(L, mode):
+    """The router's distribution over all E experts: softmax(L) in the softmax
+    modes; in the sigmoid mode the affinities normalised to sum 1 (a reading:
+    the pages log "router entropy" without defining the distribution for
+    sigmoid scores)."""
+    if mode == SIGMOID:
+        s = sigmoid(L)
+        return s / np.sum(s, axis=1, keepdims=True)
+    return softmax(L, axis=1)
+
+
+def routing_stats(L, counts, k, mode, alpha):
+    """Per-expert token share f_e = counts_e / (T k) (the fraction of the T k
+    token-to-expert assignments; a balanced 8-expert layer gives each 12.5%,
+    "Mini-MoE", section "Results"), mean router
+    probability P_e = mean_t p[t, e], mean router entropy
+    H = mean_t (-sum_e p[t, e] ln p[t, e]) in nats, and the Switch load-balance
+    term alpha * N * sum_e f_e P_e with N = E experts ("Mixture-of-Experts --
+    more capacity per byte of weight", section "What's wired today").
+    Returns (share [E], mean_prob [E], entropy, aux)."""
+    L = np.asarray(L, dtype=np.float64)
+    T, E = L.shape
+    counts = np.asarray(counts, dtype=np.float64)
+    share = counts / float(T * k) if T > 0 else np.zeros(E)
+    p = router_probs(L, mode) if T > 0 else np.zeros((0, E))
+    mean_prob = p.mean(axis=0) if T > 0 else np.zeros(E)
+    plogp = np.where(p > 0.0, p * np.log(np.where(p > 0.0, p, 1.0)), 0.0)
+    entropy = float(-plogp.sum(axis=1).mean()) if T > 0 else 0.0
+    aux = float(alpha * E * np.sum(share * mean_prob))
+    return share, mean_prob, entropy, aux
+
+
 def near_ties(L, k, eps=NEAR_TIE_EPS):
-    """Tokens whose routing is decided by a logit gap below ``eps``.
+    """Tokens whose routing is decided by a score gap below ``eps`` (L: the
+    selection scores, the logits in the softmax modes).
 
     Returns (select, order): ``select`` marks tokens where the k-th and
     (k+1)-th largest logits differ by less than eps (the selected *set* is
@@ -262,13 +332,28 @@ def route(inp, ids_override=None):
     the float64 logits (used for tokens whose selection is a near tie)."""
     spec = inp["spec"]
     E, k, mode, renorm = _spec_fields(spec)
-    L = router_logits(inp["x"], inp["w_router"], inp.get("b_router"))
-    ids = topk_select(L, k)
+    if mode == SIGMOID:
+        # bias-free logits; the bias only steers the selection
+        L = router_logits(inp["x"], inp["w_router"], None)
+        S = selection_scores(L, mode, inp.get("b_router"))
+    else:
+        L = router_logits(inp["x"], inp["w_router"], inp.get("b_router"))
+        S = L
+    ids = topk_select(S, k)
     if ids_override:
         for t, sel in ids_override.items():
             ids[t] = np.asarray(sel, dtype=np.int64)
     g, p = gate_weights(L, ids, mode, renorm)
     return L, ids, g, p
+
+
+def route_scores(inp):
+    """The selection scores of ``route`` (logits, or sigmoid + balance bias)."""
+    spec = inp["spec"]
+    if spec.mode == SIGMOID:
+        return selection_scores(router_logits(inp["x"], inp["w_router"], None), SIGMOID,
+                                inp.get("b_router"))
+    return router_logits(inp["x"], inp["w_router"], inp.get("b_router"))
 
 
 def layer_forward(inp, ids_override=None):
@@ -285,8 +370,9 @@ def layer_forward(inp, ids_override=None):
         shared = shared_expert(inp["x"], inp["ws_gate"], inp["ws_up"], inp["ws_down"],
                                inp.get("w_shared_gate"))
     out = combine(y, inv, g, shared)
-    sel_tie, ord_tie = near_ties(L, k)
-    return {"out": out, "logits": L, "probs": p, "ids": ids, "gates": g,
+    S = selection_scores(L, spec.mode, inp.get("b_router") if spec.mode == SIGMOID else None)
+    sel_tie, ord_tie = near_ties(S, k)
+    return {"out": out, "logits": L, "scores": S, "probs": p, "ids": ids, "gates": g,
             "counts": counts, "offsets": offsets, "perm": perm, "inv": inv,
             "y": y, "shared": shared, "near_tie_select": sel_tie,
             "near_tie_order": ord_tie}

@@ -21,6 +21,18 @@ The pins:
                     softmax mixture; identical experts give the plain FFN;
                     x = 0 gives 0; hidden-slice concatenation
   textbook        - silu / sigmoid / softmax values and scipy
+  sigmoid router  - selection on sigmoid(L) + balance bias, gates from the
+                    raw sigmoid ("Small MoE Architecture, in depth", sections
+                    "A small MoE layer in PyTorch" and "Balancing without
+                    fighting the loss"): zero bias reduces to the logit top-k,
+                    a large bias forces an expert in without entering its
+                    gate, rank-count brute force on the biased scores, and the
+                    dense-mask equivalence above
+  routing stats   - the 12.5% ideal share of a balanced 8-expert top-2 layer
+                    ("Mini-MoE", section "Results"; tests/golden), entropy ln E
+                    for a flat router and 0 in the one-hot limit, the Switch
+                    term equal to alpha at perfect balance, a two-expert closed
+                    form, Gibbs' bound
 """
 
 from __future__ import annotations
@@ -42,7 +54,7 @@ def _rng(seed):
 
 
 def _inputs(T, d, E, h, k, mode, renorm, seed=0, shared_h=0, gated=False, bias=False,
-            scale=1.0):
+            scale=1.0, bias_scale=0.5):
     """A small float32 input dict in the generator's layout (drawn here so the
     pins do not depend on the generator)."""
     from moe_inputs.spec import MoESpec, F32
@@ -54,7 +66,7 @@ def _inputs(T, d, E, h, k, mode, renorm, seed=0, shared_h=0, gated=False, bias=F
         "spec": spec,
         "x": r.standard_normal((T, d)).astype(np.float32),
         "w_router": (r.standard_normal((E, d)) * 0.3 * scale).astype(np.float32),
-        "b_router": (r.standard_normal(E) * 0.5).astype(np.float32) if bias else None,
+        "b_router": (r.standard_normal(E) * bias_scale).astype(np.float32) if bias else None,
         "w_gate": (r.standard_normal((E, h, d)) * 0.2).astype(np.float32),
         "w_up": (r.standard_normal((E, h, d)) * 0.2).astype(np.float32),
         "w_down": (r.standard_normal((E, d, h)) * 0.2).astype(np.float32),
@@ -158,10 +170,22 @@ def dense_mask_forward(inp):
     T, E = L.shape
     k = spec.k
     mask = np.zeros((T, E))
+    if spec.mode == O.SIGMOID:
+        # bias-free affinities; the bias only moves the choice
+        L = X @ Wr.T
+        aff = 1.0 / (1.0 + np.exp(-L))
+        sel = aff + (inp["b_router"].astype(np.float64)[None, :]
+                     if inp.get("b_router") is not None else 0.0)
+    else:
+        sel = L
     for t in range(T):
-        for e in _rank_count_topk(L[t], k):
+        for e in _rank_count_topk(sel[t], k):
             mask[t, e] = 1.0
-    if spec.mode == O.SOFTMAX_ALL:
+    if spec.mode == O.SIGMOID:
+        G = aff * mask
+        if spec.renormalize:
+            G = G / G.sum(axis=1, keepdims=True)
+    elif spec.mode == O.SOFTMAX_ALL:
         z = np.exp(L - L.max(axis=1, keepdims=True))
         G = z / z.sum(axis=1, keepdims=True) * mask
         if spec.renormalize:
@@ -196,6 +220,10 @@ def check_dense_mask_equivalence():
         dict(T=19, d=16, E=6, h=8, k=2, mode=O.SOFTMAX_ALL, renorm=False,
              shared_h=20, gated=True),
         dict(T=17, d=16, E=4, h=8, k=4, mode=O.SOFTMAX_ALL, renorm=False),
+        dict(T=27, d=16, E=9, h=8, k=3, mode=O.SIGMOID, renorm=True, bias=True,
+             bias_scale=0.05),
+        dict(T=21, d=16, E=6, h=8, k=2, mode=O.SIGMOID, renorm=False, bias=True,
+             bias_scale=0.05, shared_h=12),
     ]
     for i, c in enumerate(cases):
         inp = _inputs(seed=10 + i, **c)
@@ -381,6 +409,112 @@ def check_near_tie_detection():
     assert not sel.any()
 
 
+# ---------------------------------------------------------------------------
+# sigmoid scoring with a selection-only balance bias
+# ---------------------------------------------------------------------------
+
+def check_sigmoid_zero_bias_is_logit_topk():
+    """sigmoid is strictly increasing, so with no bias the choice is the
+    logit top-k; renormalised gates sum to 1 and follow the slot order."""
+    for seed, (E, k) in enumerate([(8, 2), (13, 5), (6, 6)]):
+        inp = _inputs(T=40, d=12, E=E, h=4, k=k, mode=O.SIGMOID, renorm=True, seed=30 + seed)
+        L, ids, g, _ = O.route(inp)
+        assert np.array_equal(ids, O.topk_select(L, k))
+        assert np.allclose(g.sum(1), 1.0, rtol=0, atol=1e-12)
+        assert np.all(np.diff(g, axis=1) <= 1e-15)
+        # unnormalised gates are affinities: strictly inside (0, 1)
+        inp2 = dict(inp, spec=inp["spec"].__class__(**{**inp["spec"].__dict__, "renormalize": False}))
+        _, _, g2, _ = O.route(inp2)
+        assert np.all((g2 > 0) & (g2 < 1))
+        # and renormalising them gives the renormalised gates
+        assert np.allclose(g2 / g2.sum(1, keepdims=True), g, rtol=0, atol=1e-12)
+
+
+def check_sigmoid_bias_steers_choice_not_gates():
+    """A bias far above any affinity gap forces its expert into slot 0 of every
+    token; the gates still come from the unbiased affinities, so a second bias
+    vector that leads to the same choice leaves the gates unchanged."""
+    inp = _inputs(T=50, d=12, E=10, h=4, k=3, mode=O.SIGMOID, renorm=True, seed=41)
+    b = np.zeros(10, np.float32)
+    b[7] = 3.0  # affinities lie in (0, 1): +3 always wins
+    L, ids, g, _ = O.route(dict(inp, b_router=b))
+    assert np.all(ids[:, 0] == 7)
+    aff = 1.0 / (1.0 + np.exp(-L))
+    np.testing.assert_allclose(g[:, 0], aff[:, 7] / np.take_along_axis(aff, ids, 1).sum(1),
+                               rtol=1e-12, atol=0)
+    b2 = b.copy()
+    b2[7] = 5.0  # same choice, larger bias
+    _, ids2, g2, _ = O.route(dict(inp, b_router=b2))
+    assert np.array_equal(ids, ids2) and np.array_equal(g, g2)
+
+
+def check_sigmoid_brute_force_topk():
+    """Small biases comparable to the affinity gaps: the oracle's choice is the
+    rank-count top-k of sigmoid(L) + b (computed here independently)."""
+    for seed in range(6):
+        inp = _inputs(T=60, d=10, E=7, h=4, k=3, mode=O.SIGMOID, renorm=True, seed=50 + seed,
+                      bias=True, bias_scale=0.05)
+        L, ids, _, _ = O.route(inp)
+        X = inp["x"].astype(np.float64)
+        aff = 1.0 / (1.0 + np.exp(-(X @ inp["w_router"].astype(np.float64).T)))
+        S = aff + inp["b_router"].astype(np.float64)[None, :]
+        for t in range(S.shape[0]):
+            assert list(ids[t]) == _rank_count_topk(S[t], 3), t
+
+
+# ---------------------------------------------------------------------------
+# routing statistics
+# ---------------------------------------------------------------------------
+
+def check_routing_stats_printed_share():
+    with open(os.path.join(GOLDEN, "mini_moe_share.json")) as f:
+        g = json.load(f)
+    E, k = g["experts"], g["top_k"]
+    T = 96
+    # perfectly balanced top-2 routing over 8 experts
+    ids = np.array([[(2 * t) % E, (2 * t + 1) % E] for t in range(T)])
+    counts, _, _, _ = O.dispatch(ids, E)
+    share, _, _, _ = O.routing_stats(np.zeros((T, E)), counts, k, O.SOFTMAX_ALL, 0.01)
+    assert np.allclose(share, g["ideal_share"], rtol=0, atol=1e-15)
+    lo, hi = g["observed_share_range"]
+    assert lo < g["ideal_share"] < hi
+
+
+def check_routing_stats_closed_forms():
+    alpha = 0.01
+    for E, k in [(8, 2), (5, 1), (16, 4)]:
+        T = 4 * E
+        ids = np.array([[(k * t + j) % E for j in range(k)] for t in range(T)])
+        counts, _, _, _ = O.dispatch(ids, E)
+        for mode in (O.SOFTMAX_ALL, O.SOFTMAX_SELECTED, O.SIGMOID):
+            # a flat router: p = 1/E everywhere, entropy ln E, and at perfect
+            # balance the Switch term is exactly alpha
+            share, P, H, aux = O.routing_stats(np.zeros((T, E)), counts, k, mode, alpha)
+            assert np.allclose(P, 1.0 / E, rtol=0, atol=1e-15)
+            assert abs(H - math.log(E)) < 1e-12
+            assert abs(aux - alpha) < 1e-15
+    # one-hot limit: entropy -> 0
+    L = np.zeros((3, 6))
+    L[:, 2] = 60.0
+    _, P, H, _ = O.routing_stats(L, np.array([3, 0, 0, 0, 0, 0]), 1, O.SOFTMAX_ALL, 0.01)
+    assert H < 1e-20 and abs(P[2] - 1.0) < 1e-20
+    # two experts, softmax: p = (1/(1+e^-a), 1/(1+e^a)) and
+    # H = ln(1 + e^a) - a e^a / (1 + e^a)
+    for a in (-3.0, -0.4, 0.0, 1.7, 5.0):
+        _, _, H, _ = O.routing_stats(np.array([[a, 0.0]]), np.array([1, 0]), 1, O.SOFTMAX_ALL, 0.0)
+        assert abs(H - (math.log1p(math.exp(a)) - a * math.exp(a) / (1.0 + math.exp(a)))) < 1e-13
+    # Gibbs: 0 <= H <= ln E; shares and mean probabilities sum to 1
+    r = _rng(9)
+    for mode in (O.SOFTMAX_ALL, O.SIGMOID):
+        L = r.standard_normal((30, 9)) * 2
+        ids = O.topk_select(L, 3)
+        counts, _, _, _ = O.dispatch(ids, 9)
+        share, P, H, aux = O.routing_stats(L, counts, 3, mode, 0.01)
+        assert 0.0 <= H <= math.log(9) + 1e-12
+        assert abs(share.sum() - 1.0) < 1e-12 and abs(P.sum() - 1.0) < 1e-12
+        assert aux >= 0.0
+
+
 ALL_CHECKS = [
     check_worked_example,
     check_brute_force_topk,
@@ -395,4 +529,9 @@ ALL_CHECKS = [
     check_textbook_functions,
     check_combine_gather_vs_loop,
     check_near_tie_detection,
+    check_sigmoid_zero_bias_is_logit_topk,
+    check_sigmoid_bias_steers_choice_not_gates,
+    check_sigmoid_brute_force_topk,
+    check_routing_stats_printed_share,
+    check_routing_stats_closed_forms,
 ]

@@ -86,3 +86,21 @@ def test_named_specs():
     assert SPECS["skewed_prefill"].dtype == BF16 and SPECS["tiny_fp32"].dtype == F32
     with pytest.raises(ValueError):
         spec_by_name("decode@T65")
+
+
+def test_balance_bias_is_whole_bias_steps():
+    from moe_inputs.generate import balance_router_bias
+    b = balance_router_bias(64)
+    steps = b.astype(np.float64) / 1e-3
+    assert np.allclose(steps, np.round(steps), atol=1e-4)
+    assert np.max(np.abs(steps)) <= 20 + 1e-6
+    assert len(set(np.round(steps).astype(int).tolist())) > 30  # a spread, not a constant
+    assert np.array_equal(b, balance_router_bias(64))
+
+
+def test_small_moe_sigmoid_spec_matches_page_defaults():
+    from moe_inputs.spec import SIGMOID
+    s = SPECS["small_moe_sigmoid"]
+    # SmallMoE(d=1024, n_experts=64, k=8, expert_hidden=256, shared_hidden=1024)
+    assert (s.d, s.E, s.k, s.h, s.shared_h) == (1024, 64, 8, 256, 1024)
+    assert s.mode == SIGMOID and s.renormalize and not s.shared_gate

@@ -82,9 +82,42 @@ def _combine_drop_last_slot(y_sorted, inv, gates, shared=None):
     return _ORIG["combine"](y_sorted, inv, g, shared)
 
 
+def _sigmoid_gates_biased(L, ids, mode, renormalize):
+    # the selection bias leaking into the gates: gate with a softmax of the
+    # selected logits instead of the raw affinities
+    if mode == O.SIGMOID:
+        mode = O.SOFTMAX_SELECTED
+    return _ORIG["gate_weights"](L, ids, mode, renormalize)
+
+
+def _selection_ignores_bias(L, mode, sel_bias=None):
+    return _ORIG["selection_scores"](L, mode, None)
+
+
+def _selection_bias_inside_sigmoid(L, mode, sel_bias=None):
+    if mode == O.SIGMOID and sel_bias is not None:
+        return O.sigmoid(L + O.to_f64(sel_bias)[None, :])
+    return _ORIG["selection_scores"](L, mode, sel_bias)
+
+
+def _stats_share_over_T(L, counts, k, mode, alpha):
+    share, P, H, aux = _ORIG["routing_stats"](L, counts, k, mode, alpha)
+    return share * k, P, H, aux
+
+
+def _stats_entropy_sign(L, counts, k, mode, alpha):
+    share, P, H, aux = _ORIG["routing_stats"](L, counts, k, mode, alpha)
+    return share, P, -H, aux
+
+
+def _stats_aux_without_N(L, counts, k, mode, alpha):
+    share, P, H, aux = _ORIG["routing_stats"](L, counts, k, mode, alpha)
+    return share, P, H, aux / L.shape[1]
+
+
 _ORIG = {n: getattr(O, n) for n in ("gate_weights", "dispatch", "combine", "gate_up",
                                     "down", "shared_expert", "router_logits", "topk_select",
-                                    "silu")}
+                                    "silu", "selection_scores", "routing_stats")}
 
 MUTATIONS = [
     ("topk_select", _topk_ties_high),
@@ -99,6 +132,12 @@ MUTATIONS = [
     ("down", _down_transposed),
     ("shared_expert", _shared_ungated),
     ("router_logits", _logits_no_bias),
+    ("gate_weights", _sigmoid_gates_biased),
+    ("selection_scores", _selection_ignores_bias),
+    ("selection_scores", _selection_bias_inside_sigmoid),
+    ("routing_stats", _stats_share_over_T),
+    ("routing_stats", _stats_entropy_sign),
+    ("routing_stats", _stats_aux_without_N),
 ]
 
 
