@@ -37,7 +37,7 @@ METRIC = "MoE layer fwd tokens/s on 1 GPU; % bf16 MFMA peak (prefill) / % HBM BW
 # Binding roofline of each workload (algorithmic intensity vs the 312.5
 # FLOP/B ridge of 2.5 PFLOP/s bf16 over 8 TB/s).
 BOUND = {"tiny_fp32": "alu", "gemma_upcycled": "hbm", "decode": "hbm",
-         "skewed_prefill": "mfma", "shared_routed": "mfma"}
+         "skewed_prefill": "mfma", "shared_routed": "mfma", "small_moe_sigmoid": "mfma"}
 
 
 def log(*a):
@@ -279,7 +279,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "T": T, "d": spec.d, "E": spec.E, "h": spec.h,
                    "top_k": spec.k, "shared_h": spec.shared_h,
-                   "gates": ["softmax over all", "softmax over the selected"][spec.mode]
+                   "gates": ["softmax over all", "softmax over the selected",
+                             "sigmoid affinities, selection-only balance bias"][spec.mode]
                    + (" + renormalised" if spec.renormalize else ""),
                    "weight_copies": nsets, "parallelism": "single GPU"},
         "roofline": roof,

@@ -12,6 +12,13 @@
  *   gates   MOE_SOFTMAX_ALL:      softmax over all E, gathered at ids,
  *                                 optionally renormalised to sum 1
  *           MOE_SOFTMAX_SELECTED: softmax over the k selected logits
+ *           MOE_SIGMOID:          affinities s = sigmoid(L) of the bias-free
+ *                                 logits; ids = the top_k of s + b (b: the
+ *                                 selection-only balance bias, when given);
+ *                                 gates = s at ids, optionally renormalised
+ *                                 ("Small MoE Architecture, in depth",
+ *                                 sections "A small MoE layer in PyTorch" and
+ *                                 "Balancing without fighting the loss")
  *   dispatch  stable counting sort of the P = T*k pairs p = t*k + j by
  *             expert ids[t, j]: counts[E], offsets[E+1], perm[P] (sorted
  *             row -> pair), inv[P] (pair -> sorted row)
@@ -66,7 +73,7 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
-typedef enum { MOE_SOFTMAX_ALL = 0, MOE_SOFTMAX_SELECTED = 1 } moe_score_mode;
+typedef enum { MOE_SOFTMAX_ALL = 0, MOE_SOFTMAX_SELECTED = 1, MOE_SIGMOID = 2 } moe_score_mode;
 
 /* Which entry point a workspace is sized for (moe_workspace_size_entry). */
 typedef enum {
@@ -75,7 +82,8 @@ typedef enum {
   MOE_ENTRY_GATE_UP = 2,
   MOE_ENTRY_DOWN = 3,
   MOE_ENTRY_EXPERT_FFN = 4,
-  MOE_ENTRY_SHARED_EXPERT = 5
+  MOE_ENTRY_SHARED_EXPERT = 5,
+  MOE_ENTRY_ROUTING_STATS = 6
 } moe_entry;
 
 /* Shapes and options of one layer call. One (E, h) per call: every routed
@@ -90,7 +98,9 @@ typedef struct {
   int32_t dtype;           /* moe_dtype of x, weights, act, y, out */
   int32_t mode;            /* moe_score_mode */
   int32_t renormalize;     /* 1: divide the k gates by their sum */
-  int32_t has_router_bias; /* 1: b_router [E] float32 is added to the logits */
+  int32_t has_router_bias; /* 1: b_router [E] float32 is added to the logits
+                              (softmax modes), or to the affinities for the
+                              choice only (MOE_SIGMOID) */
   int32_t shared_h;        /* hidden width of the shared expert, 0 = none */
   int32_t shared_gate;     /* 1: the shared expert is scaled by sigmoid(w_s . x) */
 } moe_config;
@@ -131,8 +141,10 @@ size_t moe_workspace_size(const moe_config* cfg);
  * section "How it works", step 3 for MOE_SOFTMAX_SELECTED).
  *   x [T, d], w_router [E, d], b_router [E] f32 (iff has_router_bias)
  *   -> ids [T, k] int32, gates [T, k] f32, logits [T, E] f32 (optional, NULL
- *   to skip). Logits are accumulated in float32; the top-k compares float32
- *   logits, ties to the lower expert index. */
+ *   to skip; they include b_router in the softmax modes and never in
+ *   MOE_SIGMOID). Logits are accumulated in float32; the top-k compares
+ *   float32 scores (the logits, or sigmoid(L) + b), ties to the lower expert
+ *   index. */
 moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
                      const float* b_router, int32_t* ids, float* gates, float* logits,
                      void* stream);
@@ -182,6 +194,24 @@ moe_status moe_shared_expert(const moe_config* cfg, const void* x, const void* w
  *   -> out [T, d]. */
 moe_status moe_combine(const moe_config* cfg, const void* y, const int32_t* inv,
                        const float* gates, const void* shared, void* out, void* stream);
+
+/* Routing statistics ("Mixture-of-Experts -- more capacity per byte of
+ * weight", section "What's wired today": the Switch load-balance term;
+ * "Small MoE Architecture, in depth", section "Fine-tuning a small MoE":
+ * per-expert token share and router entropy), from the router logits as
+ * moe_route returns them and the per-expert counts:
+ *   share[e]     = counts[e] / (T * top_k)
+ *   mean_prob[e] = mean over tokens of p[t, e]
+ *   scalars[0]   = mean over tokens of -sum_e p[t, e] ln p[t, e] (nats)
+ *   scalars[1]   = alpha * E * sum_e share[e] * mean_prob[e]
+ * p = softmax(logits) in the softmax modes, sigmoid(logits) normalised to
+ * sum 1 in MOE_SIGMOID. logits [T, E] f32, counts [E] int32 -> share [E],
+ * mean_prob [E], scalars [2] (all f32). alpha must be finite and >= 0
+ * (MOE_ERR_INVALID_ARG otherwise). Float32 arithmetic, summed in a fixed
+ * order (deterministic). Workspace: MOE_ENTRY_ROUTING_STATS. */
+moe_status moe_routing_stats(const moe_config* cfg, const float* logits, const int32_t* counts,
+                             float alpha, float* share, float* mean_prob, float* scalars,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* The whole layer: route, dispatch, gate/up, down, combine (+ shared).
  *   x [T, d] -> out [T, d]. ids [T, k], gates [T, k] and counts [E] are

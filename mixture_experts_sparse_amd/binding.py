@@ -28,6 +28,7 @@ MOE_F32 = 0
 MOE_BF16 = 1
 MOE_SOFTMAX_ALL = 0
 MOE_SOFTMAX_SELECTED = 1
+MOE_SIGMOID = 2
 
 MOE_ENTRY_LAYER_FORWARD = 0
 MOE_ENTRY_DISPATCH = 1
@@ -35,6 +36,7 @@ MOE_ENTRY_GATE_UP = 2
 MOE_ENTRY_DOWN = 3
 MOE_ENTRY_EXPERT_FFN = 4
 MOE_ENTRY_SHARED_EXPERT = 5
+MOE_ENTRY_ROUTING_STATS = 6
 
 MOE_NUM_STAGES = 5
 STAGE_NAMES = ("route", "dispatch", "gate_up", "down", "combine")
@@ -77,6 +79,8 @@ _SIG = {
     "moe_expert_ffn": ([_P] * 9 + [ctypes.c_size_t, _P], ctypes.c_int),
     "moe_shared_expert": ([_P] * 8 + [ctypes.c_size_t, _P], ctypes.c_int),
     "moe_combine": ([_P] * 7, ctypes.c_int),
+    "moe_routing_stats": ([_P] * 3 + [ctypes.c_float] + [_P] * 4 + [ctypes.c_size_t, _P],
+                          ctypes.c_int),
     "moe_layer_forward": ([_P] * 8 + [ctypes.c_size_t, _P], ctypes.c_int),
     "moe_layer_forward_traced": ([_P] * 8 + [ctypes.c_size_t, _P, _P], ctypes.c_int),
 }
@@ -264,6 +268,23 @@ def combine(cfg, y, inv, gates, shared=None, out=None, stream=None):
     _check(lib().moe_combine(ctypes.byref(cfg), _ptr(y), _ptr(inv), _ptr(gates), _ptr(shared),
                              _ptr(out), _stream(stream)), "moe_combine")
     return out
+
+
+def routing_stats(cfg, logits, counts, alpha=0.01, ws=None, stream=None):
+    """(share [E], mean_prob [E], scalars [2] = (entropy, aux)) as device
+    tensors, from router logits [T, E] f32 and counts [E] int32."""
+    import torch
+    dev = logits.device
+    share = torch.empty(cfg.E, dtype=torch.float32, device=dev)
+    mean_prob = torch.empty(cfg.E, dtype=torch.float32, device=dev)
+    scalars = torch.empty(4, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = alloc_workspace(cfg, MOE_ENTRY_ROUTING_STATS, dev)
+    _check(lib().moe_routing_stats(ctypes.byref(cfg), _ptr(logits), _ptr(counts),
+                                   ctypes.c_float(alpha), _ptr(share), _ptr(mean_prob),
+                                   _ptr(scalars), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_routing_stats")
+    return share, mean_prob, scalars[:2]
 
 
 def weights_struct(w: dict) -> MoeWeights:

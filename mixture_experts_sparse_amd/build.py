@@ -22,7 +22,8 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["moe_api.cpp", "route_dispatch.hip", "expert_gemm.hip", "expert_gemm_small.hip", "combine.hip"]
+SOURCES = ["moe_api.cpp", "route_dispatch.hip", "expert_gemm.hip", "expert_gemm_small.hip", "combine.hip",
+           "routing_stats.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

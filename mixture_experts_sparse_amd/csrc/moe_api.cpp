@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <cmath>
 #include <cstdint>
 
 #include "moe_internal.h"
@@ -25,7 +26,8 @@ moe_status check_cfg(const moe_config* c) {
   if (c->T < 0 || c->d <= 0 || c->E <= 0 || c->h <= 0) return MOE_ERR_INVALID_ARG;
   if (c->top_k < 1 || c->top_k > c->E) return MOE_ERR_INVALID_ARG;
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (c->mode != MOE_SOFTMAX_ALL && c->mode != MOE_SOFTMAX_SELECTED) return MOE_ERR_INVALID_ARG;
+  if (c->mode != MOE_SOFTMAX_ALL && c->mode != MOE_SOFTMAX_SELECTED && c->mode != MOE_SIGMOID)
+    return MOE_ERR_INVALID_ARG;
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
   if (c->has_router_bias != 0 && c->has_router_bias != 1) return MOE_ERR_INVALID_ARG;
   if (c->shared_gate != 0 && c->shared_gate != 1) return MOE_ERR_INVALID_ARG;
@@ -155,6 +157,8 @@ size_t moe_workspace_size_entry(const moe_config* cfg, int32_t entry) {
     case MOE_ENTRY_DOWN: return L.end_tables;
     case MOE_ENTRY_EXPERT_FFN: return L.act_s;
     case MOE_ENTRY_SHARED_EXPERT: return L.end_act;
+    case MOE_ENTRY_ROUTING_STATS:
+      return cfg->T > 0 ? align256(static_cast<size_t>(stats_blocks(cfg->T)) * (cfg->E + 1) * 4) : 0;
     default: return 0;
   }
 }
@@ -359,6 +363,22 @@ moe_status moe_combine(const moe_config* cfg, const void* y, const int32_t* inv,
   MOE_TRY(need(out));
   CombineParams p{y, inv, gates, shared, nullptr, out, c.T, c.d, c.top_k, c.dtype, c.T * c.top_k};
   MOE_HIP(launch_combine(p, as_stream(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_routing_stats(const moe_config* cfg, const float* logits, const int32_t* counts,
+                             float alpha, float* share, float* mean_prob, float* scalars,
+                             void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return MOE_OK;
+  MOE_TRY(need(logits)); MOE_TRY(need(counts)); MOE_TRY(need(share)); MOE_TRY(need(mean_prob));
+  MOE_TRY(need(scalars));
+  if (!(alpha >= 0.0f) || alpha == INFINITY) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_ws(c, MOE_ENTRY_ROUTING_STATS, ws, ws_bytes));
+  StatsParams p{logits, counts, c.T, c.E, c.top_k, c.mode, alpha, static_cast<float*>(ws),
+                stats_blocks(c.T), share, mean_prob, scalars};
+  MOE_HIP(launch_stats(p, as_stream(stream)));
   return MOE_OK;
 }
 

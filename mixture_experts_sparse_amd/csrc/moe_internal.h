@@ -216,6 +216,21 @@ struct RowDotSigmoidParams {
   float* out;     // [T]
 };
 
+// Routing statistics (routing_stats.hip).
+struct StatsParams {
+  const float* logits;    // [T, E]
+  const int32_t* counts;  // [E]
+  int T, E, k, mode;
+  float alpha;
+  float* part;            // [nb][E + 1] partial sums (workspace)
+  int nb;                 // stats_blocks(T)
+  float* share;           // [E]
+  float* mean_prob;       // [E]
+  float* scalars;         // [2]: entropy, aux
+};
+int stats_blocks(int T);
+hipError_t launch_stats(const StatsParams& p, hipStream_t s);
+
 hipError_t launch_route(const RouteParams& p, int dtype, hipStream_t s);
 hipError_t launch_rank(const RankParams& p, hipStream_t s);
 hipError_t launch_scan(const ScanParams& p, hipStream_t s);

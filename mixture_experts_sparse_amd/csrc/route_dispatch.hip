@@ -431,6 +431,7 @@ __device__ void route_select(const RouteParams& p, int t0, const float* Lg, cons
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15;
   const int E = p.E, k = p.k;
+  const bool sig = p.mode == MOE_SIGMOID;
 #pragma unroll
   for (int rnd = 0; rnd < RT / 32; ++rnd) {
     if (t0 + rnd * 32 >= p.T) break;  // uniform: no live token in this or later rounds
@@ -444,10 +445,17 @@ __device__ void route_select(const RouteParams& p, int t0, const float* Lg, cons
       const int e = f * 16 + c;
       float val = -INFINITY;
       if (e < E) {
-        val = row[e] + bias[f];
-        if (live && p.logits != nullptr) p.logits[static_cast<size_t>(t) * E + e] = val;
+        if (sig) {
+          // sigmoid scoring: the bias steers the choice only; the logits
+          // output stays bias-free
+          val = sigmoid_f32(row[e]) + bias[f];
+          if (live && p.logits != nullptr) p.logits[static_cast<size_t>(t) * E + e] = row[e];
+        } else {
+          val = row[e] + bias[f];
+          if (live && p.logits != nullptr) p.logits[static_cast<size_t>(t) * E + e] = val;
+        }
       }
-      v[f] = val + 0.0f;  // -0 -> +0: equal logits must get equal keys
+      v[f] = val + 0.0f;  // -0 -> +0: equal scores must get equal keys
     }
     if (live && p.sgate != nullptr && c == 0) p.sgate[t] = sigmoid_f32(row[E]);
     uint64_t key[NF];
@@ -468,10 +476,12 @@ __device__ void route_select(const RouteParams& p, int t0, const float* Lg, cons
         mine = j == c ? b : mine;
       }
       const float m = __shfl(key_value(mine), lane & 48, kWave);  // slot 0: the largest logit
-      const int mi = key_index(mine);
-      const float ej = c < k ? expf(key_value(mine) - m) : 0.f;
-      float denom = ej;
-      denom = row16_sum(denom);
+      const int mi = c < k ? key_index(mine) : 0;
+      // gate numerators: exp(L - max) in the softmax modes; in the sigmoid
+      // mode the raw affinity of the chosen expert (its bias left out)
+      const float ej = c < k ? (sig ? sigmoid_f32(row[mi]) : expf(key_value(mine) - m)) : 0.f;
+      float denom = row16_sum(ej);
+      if (sig && !p.renorm) denom = 1.0f;
       if (all) {
         float sall = 0.f;
 #pragma unroll
@@ -498,7 +508,7 @@ __device__ void route_select(const RouteParams& p, int t0, const float* Lg, cons
         const float bv = key_value(b);
         const int bi = key_index(b);
         if (j == 0) m = bv;  // the largest logit
-        const float ej = expf(bv - m);
+        const float ej = sig ? sigmoid_f32(row[bi]) : expf(bv - m);
         ssel += ej;
         if ((j & 15) == c) {
           if (live) {
@@ -509,6 +519,7 @@ __device__ void route_select(const RouteParams& p, int t0, const float* Lg, cons
         }
       }
       float denom = ssel;
+      if (sig && !p.renorm) denom = 1.0f;
       if (all) {
         float sall = 0.f;
 #pragma unroll
@@ -674,7 +685,8 @@ __device__ void route_tail(const RouteParams& p, int t0, float* Lg, const float*
   // rank counting costs E compares per (token, expert) item, spread over the
   // workgroup; the 16-lane maximum steps cost a fixed dependent chain per 32
   // tokens: the first is cheaper while the block's T * E^2 stays small
-  if (static_cast<long long>(nt) * p.E * p.E <= (1LL << 17))
+  // (the sigmoid mode keeps the raw logits for its gates: the second path)
+  if (p.mode != MOE_SIGMOID && static_cast<long long>(nt) * p.E * p.E <= (1LL << 17))
     route_select_rank<NCH, RT>(p, t0, Lg, bias, sel);
   else
     route_select<NCH, RT>(p, t0, Lg, bias, sel);

@@ -122,12 +122,23 @@ def check_out(gpu_out: np.ndarray, ref_out: np.ndarray, dtype: int, what: str = 
     return err / max(scale, 1e-300)
 
 
+def oracle_logits_scores(inp: dict):
+    """(L, S): the router logits as moe_route returns them (bias-free in the
+    sigmoid mode) and the scores the top-k is taken on."""
+    spec = inp["spec"]
+    if spec.mode == O.SIGMOID:
+        L = O.router_logits(inp["x"], inp["w_router"], None)
+        return L, O.selection_scores(L, O.SIGMOID, inp.get("b_router"))
+    L = O.router_logits(inp["x"], inp["w_router"], inp.get("b_router"))
+    return L, L
+
+
 def full_parity(inp: dict, d_inp: dict = None):
     """Fused layer on the GPU against the whole-batch oracle."""
     spec = inp["spec"]
     g = run_layer(inp, d_inp)
-    L = O.router_logits(inp["x"], inp["w_router"], inp.get("b_router"))
-    near, mism = check_routing(L, g["ids"], spec.k)
+    L, S = oracle_logits_scores(inp)
+    near, mism = check_routing(S, g["ids"], spec.k)
     override = {int(t): g["ids"][t] for t in mism}
     ref = O.layer_forward(inp, ids_override=override)
     assert np.array_equal(g["counts"], ref["counts"]), "counts differ"
@@ -142,9 +153,9 @@ def sampled_parity(inp: dict, tokens, d_inp: dict = None):
     for a sample of tokens computed one by one by the oracle."""
     spec = inp["spec"]
     g = run_layer(inp, d_inp)
-    L = O.router_logits(inp["x"], inp["w_router"], inp.get("b_router"))
-    near, mism = check_routing(L, g["ids"], spec.k)
-    ids = O.topk_select(L, spec.k)
+    L, S = oracle_logits_scores(inp)
+    near, mism = check_routing(S, g["ids"], spec.k)
+    ids = O.topk_select(S, spec.k)
     ids[mism] = g["ids"][mism]
     gates, _ = O.gate_weights(L, ids, spec.mode, spec.renormalize)
     counts, _, _, _ = O.dispatch(ids, spec.E)

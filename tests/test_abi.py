@@ -44,6 +44,7 @@ def _cfg(**kw):
     (dict(top_k=8), B.MOE_OK),                  # k = E is legal
     (dict(dtype=7), B.MOE_ERR_INVALID_ARG),
     (dict(mode=3), B.MOE_ERR_INVALID_ARG),
+    (dict(mode=B.MOE_SIGMOID, has_router_bias=True), B.MOE_OK),
     (dict(shared_gate=True), B.MOE_ERR_INVALID_ARG),  # gate without a shared expert
     (dict(d=60), B.MOE_ERR_UNSUPPORTED),
     (dict(h=36), B.MOE_ERR_UNSUPPORTED),
@@ -64,8 +65,10 @@ def test_workspace_sizes_are_bounded():
     assert ws < 1.1 * P * (2048 + 768) * 2 + 16 * 2**20
     gathered = 16384 * 768 * 2048 * 2
     assert ws < gathered / 10
-    for e in range(6):
+    for e in range(7):
         assert B.workspace_size(c, e) <= ws
+    # routing statistics: one row of E + 1 floats per 256 tokens
+    assert 0 < B.workspace_size(c, B.MOE_ENTRY_ROUTING_STATS) <= (16384 // 256) * 129 * 4 + 256
     assert B.workspace_size(c, B.MOE_ENTRY_DISPATCH) < 8 * 2**20
     assert B.workspace_size(B.make_config(1, 64, 8, 32, 9)) == 0  # invalid cfg
 
@@ -116,6 +119,20 @@ def test_entry_points_reject_bad_args_without_gpu():
     # misaligned optional output
     assert L.moe_layer_forward(cp, ctypes.byref(w), FAKE, FAKE, FAKE + 4, None, None, FAKE,
                                1 << 40, None) == B.MOE_ERR_UNSUPPORTED
+    # routing statistics: required pointers, alpha range, workspace
+    f32 = ctypes.c_float
+    assert L.moe_routing_stats(cp, None, FAKE, f32(0.01), FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                               None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_routing_stats(cp, FAKE, FAKE, f32(0.01), FAKE, None, FAKE, FAKE, 1 << 30,
+                               None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_routing_stats(cp, FAKE, FAKE, f32(-1.0), FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                               None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_routing_stats(cp, FAKE, FAKE, f32(float("nan")), FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                               None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_routing_stats(cp, FAKE, FAKE, f32(0.01), FAKE, FAKE, FAKE, FAKE, 8,
+                               None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_routing_stats(bp, FAKE, FAKE, f32(0.01), FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                               None) == B.MOE_ERR_INVALID_ARG
 
 
 def test_build_script_lists_existing_sources():

@@ -16,7 +16,8 @@ import torch
 import mixture_experts_sparse_amd.binding as B
 import oracle.moe_oracle as O
 from gpu_helpers import (EPS_TIE, check_gates, check_out, check_routing, dev, device_inputs,
-                         full_parity, host, run_layer, sampled_parity, say)
+                         full_parity, host, oracle_logits_scores, run_layer, sampled_parity,
+                         say)
 from moe_inputs import generate, small_spec, spec_by_name
 from moe_inputs.spec import BF16, F32, SOFTMAX_ALL, SOFTMAX_SELECTED, SPECS, MoESpec
 
@@ -59,6 +60,13 @@ SMALL = {
                                 mode=SOFTMAX_SELECTED),
     "split_route_e256_shared": small_spec("shared_routed", T=8, d=64, E=256, h=32, k=8,
                                           shared_h=64),
+    # sigmoid affinities, selection-only balance bias, renormalised raw gates:
+    # several route blocks with the shared expert; one route block with the
+    # small-batch GEMMs; more than 16 slots per token without renormalisation
+    "sigmoid_small": small_spec("small_moe_sigmoid", T=300, d=256, E=64, h=64, k=8, shared_h=128),
+    "sigmoid_one_block": small_spec("small_moe_sigmoid", T=16, d=256, E=64, h=64, k=8, shared_h=0),
+    "sigmoid_k20": small_spec("small_moe_sigmoid", T=90, d=128, E=64, h=32, k=20, shared_h=0,
+                              renormalize=False),
 }
 
 
@@ -84,13 +92,13 @@ def test_entry_points_small(name):
     logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
     ids, gates = B.route(cfg, d["x"], d["w_router"], d["b_router"], logits=logits)
     torch.cuda.synchronize()
-    L = O.router_logits(inp["x"], inp["w_router"], inp.get("b_router"))
+    L, S = oracle_logits_scores(inp)
     lerr = float(np.max(np.abs(host(logits) - L)))
     say(f"    logits max err {lerr:.2e}")
     assert lerr <= (1e-5 if spec.dtype == F32 else 1e-4) * max(1.0, float(np.max(np.abs(L))))
     gids = ids.cpu().numpy().astype(np.int64)
-    near, mism = check_routing(L, gids, k)
-    ref_ids = O.topk_select(L, k)
+    near, mism = check_routing(S, gids, k)
+    ref_ids = O.topk_select(S, k)
     ref_ids[mism] = gids[mism]
     ref_g, _ = O.gate_weights(L, ref_ids, spec.mode, spec.renormalize)
     check_gates(gates.cpu().numpy().astype(np.float64), ref_g)
@@ -137,13 +145,13 @@ def test_entry_points_small(name):
         # one route block: the fused layer splits the router GEMM over K
         # (another fp32 summation order than moe_route's single workgroup),
         # so ids agree outside near-ties and outputs to the bf16 tolerance
-        tie = np.logical_or(*O.near_ties(L, k, EPS_TIE))
+        tie = np.logical_or(*O.near_ties(S, k, EPS_TIE))
         assert np.array_equal(fused["ids"][~tie], gids[~tie])
         check_out(host(fused["out_t"]), host(out).astype(np.float64), spec.dtype, "fused vs chain")
 
 
 FULL = ["tiny_fp32", "gemma_upcycled", "skewed_prefill", "shared_routed",
-        "decode@T1", "decode@T4", "decode@T16", "decode@T64"]
+        "decode@T1", "decode@T4", "decode@T16", "decode@T64", "small_moe_sigmoid"]
 
 _cache = {}
 
@@ -286,3 +294,41 @@ def test_workspace_too_small_is_rejected_on_gpu():
         B.layer_forward(cfg, {n: d[n] for n in ("w_router", "w_gate", "w_up", "w_down")},
                         d["x"], ws=ws)
     assert ei.value.status == B.MOE_ERR_WORKSPACE
+
+
+STATS = {
+    "stats_softmax_all": small_spec("decode", T=300, d=128, E=64, h=32, k=8),
+    "stats_selected_e256": MoESpec(name="st_e256", T=1000, d=64, E=256, h=16, k=4,
+                                   mode=SOFTMAX_SELECTED),
+    "stats_biased": small_spec("skewed_prefill", T=700, d=128, E=32, h=32, k=8),
+    "stats_sigmoid": small_spec("small_moe_sigmoid", T=513, d=128, E=64, h=32, k=8, shared_h=0),
+    "stats_fp32_tiny": SPECS["tiny_fp32"],
+    "stats_T1": small_spec("decode", T=1, d=128, E=64, h=32, k=8),
+}
+
+
+@pytest.mark.parametrize("name", list(STATS))
+def test_routing_stats(name):
+    """moe_routing_stats on moe_route's logits and moe_dispatch's counts
+    against the oracle's statistics on its float64 logits and the same
+    counts."""
+    spec = STATS[name]
+    say(f"[gpu] routing stats {name}: T={spec.T} E={spec.E} k={spec.k} mode={spec.mode}")
+    inp = generate(spec)
+    d = device_inputs(inp)
+    cfg = B.config_from_spec(spec)
+    logits = torch.empty((spec.T, spec.E), dtype=torch.float32, device="cuda")
+    ids, _ = B.route(cfg, d["x"], d["w_router"], d["b_router"], logits=logits)
+    counts, _, _, _ = B.dispatch(cfg, ids)
+    share, mean_prob, scalars = B.routing_stats(cfg, logits, counts, alpha=0.01)
+    torch.cuda.synchronize()
+    L, _ = oracle_logits_scores(inp)
+    rs, rp, rh, ra = O.routing_stats(L, counts.cpu().numpy(), spec.k, spec.mode, 0.01)
+    gs, gp, (gh, ga) = share.cpu().numpy(), mean_prob.cpu().numpy(), scalars.cpu().numpy()
+    say(f"    share err {np.max(np.abs(gs - rs)):.2e}, mean prob err {np.max(np.abs(gp - rp)):.2e}, "
+        f"entropy {gh:.6f} vs {rh:.6f}, aux {ga:.6e} vs {ra:.6e}")
+    assert np.max(np.abs(gs - rs)) <= 1e-6
+    assert np.max(np.abs(gp - rp)) <= 1e-5 * max(1.0, float(np.max(rp)))
+    assert abs(gh - rh) <= 1e-5 * max(1.0, rh)
+    assert abs(ga - ra) <= 1e-5 * max(ra, 1e-3)
+    assert abs(float(gs.sum()) - 1.0) < 1e-5 and abs(float(gp.sum()) - 1.0) < 1e-4
