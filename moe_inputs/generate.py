@@ -62,6 +62,43 @@ def zipf_router_bias(E: int) -> np.ndarray:
     return (2.0 * np.log(1.0 / np.power(e + 1.0, 1.1))).astype(np.float32)
 
 
+def _bf16_round_toward(a: np.ndarray, up: bool) -> np.ndarray:
+    """float32 -> the nearest bf16 value at or above (up) / at or below a, as
+    float32 (finite inputs)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    t = (a.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)  # toward zero
+    step_away = ((t.view(np.uint32) + np.uint32(0x10000)).view(np.float32))  # next away from 0
+    need = (t < a) if up else (t > a)
+    return np.where(need, step_away, t).astype(np.float32)
+
+
+def quantize_q4_g64(w: np.ndarray):
+    """Input construction for the quantised-expert workloads: float32
+    weights [..., K] -> (packed [..., K/2] uint8, sb [..., K/64] uint32) in the
+    4-bit affine format the layer reads (groups of 64 along the last axis;
+    bf16 scale s in the low half of sb, bf16 bias b in the high half; code of
+    position 2i in the low nibble of byte i). b is the group minimum rounded
+    down to bf16 and s = (max - b) / 15 rounded up to bf16, so every weight
+    of the group lies in [b, b + 15 s] and q = round((w - b) / s) dequantises
+    within s / 2 of it."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    K = w.shape[-1]
+    if K % 64 != 0:
+        raise ValueError("K must be a multiple of 64")
+    g = w.reshape(w.shape[:-1] + (K // 64, 64))
+    lo = g.min(axis=-1)
+    hi = g.max(axis=-1)
+    b = _bf16_round_toward(lo, up=False)
+    s = _bf16_round_toward(np.maximum((hi.astype(np.float64) - b) / 15.0, 1e-30).astype(np.float32),
+                           up=True)
+    q = np.rint((g.astype(np.float64) - b[..., None]) / s[..., None])
+    q = np.clip(q, 0, 15).astype(np.uint8).reshape(w.shape)
+    packed = (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
+    sb = (bf16_bits_from_f32(s).astype(np.uint32) |
+          (bf16_bits_from_f32(b).astype(np.uint32) << np.uint32(16)))
+    return packed, sb
+
+
 def balance_router_bias(E: int, step: float = 1e-3) -> np.ndarray:
     """A selection-only balance bias as the update rule of "Small MoE
     Architecture, in depth" leaves it: whole multiples of the bias step
@@ -122,7 +159,16 @@ def generate(spec: MoESpec) -> dict:
         wg = _normal(rng, (spec.E, spec.h, spec.d), spec.expert_std)
         wu = _normal(rng, (spec.E, spec.h, spec.d), spec.expert_std)
         wd = _normal(rng, (spec.E, spec.d, spec.h), spec.expert_std)
-    out["w_gate"], out["w_up"], out["w_down"] = _cast(spec, wg), _cast(spec, wu), _cast(spec, wd)
+    if spec.expert_quant == "q4_g64":
+        # routed experts quantised from the same draws; the shared expert
+        # below stays in the activation dtype
+        for name, w in (("w_gate", wg), ("w_up", wu), ("w_down", wd)):
+            out[name], out[name + "_sb"] = quantize_q4_g64(w)
+    elif spec.expert_quant is not None:
+        raise ValueError(f"unknown expert quantisation {spec.expert_quant!r}")
+    else:
+        out["w_gate"], out["w_up"], out["w_down"] = _cast(spec, wg), _cast(spec, wu), _cast(spec, wd)
+        out["w_gate_sb"] = out["w_up_sb"] = out["w_down_sb"] = None
     del wg, wu, wd
     if spec.shared_h > 0:
         hs = spec.shared_h

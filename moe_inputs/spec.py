@@ -21,6 +21,9 @@ distributions the generator draws from. The five named workloads are:
 * ``shared_routed``   T=8192, d=2048, E=60, h=1408, k=4, bf16, softmax over all
                       60 without renormalisation; plus one always-on shared
                       SwiGLU of hidden 5632 scaled by sigmoid(w_s . x).
+* ``decode_q4``       the decode workload with its routed experts in 4-bit affine
+                      groups of 64 (``generate.quantize_q4_g64`` of the same
+                      draws); T in {1, 4, 16, 64}.
 * ``small_moe_sigmoid`` the defaults of the SmallMoE module of "Small MoE
                       Architecture, in depth" (d=1024, 64 experts, top-8,
                       expert hidden 256, one ungated shared expert of hidden
@@ -69,6 +72,9 @@ class MoESpec:
     router_bias: Optional[str] = None
     # 0: no shared expert
     shared_h: int = 0
+    # routed-expert weight format: None (activation dtype) or "q4_g64"
+    # (4-bit affine groups of 64 along the reduction axis, bf16 scale + bias)
+    expert_quant: Optional[str] = None
     # sigmoid(w_s . x) gate on the shared expert (only meaningful if shared_h > 0)
     shared_gate: bool = False
     # drop-upcycled expert construction (gemma_upcycled)
@@ -121,6 +127,10 @@ SPECS = {
         name="shared_routed", T=8192, d=2048, E=60, h=1408, k=4, dtype=BF16,
         mode=SOFTMAX_ALL, renormalize=False, router_std=0.02, expert_std=0.02,
         shared_h=5632, shared_gate=True),
+    "decode_q4": MoESpec(
+        name="decode_q4@T1", T=1, d=2048, E=64, h=1024, k=8, dtype=BF16,
+        mode=SOFTMAX_ALL, renormalize=False, router_std=0.02, expert_std=0.02,
+        x_rows=64, expert_quant="q4_g64"),
     "small_moe_sigmoid": MoESpec(
         name="small_moe_sigmoid", T=4096, d=1024, E=64, h=256, k=8, dtype=BF16,
         mode=SIGMOID, renormalize=True, router_std=0.02, expert_std=0.02,

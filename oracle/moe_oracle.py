@@ -43,6 +43,16 @@ s = sigmoid(L) of the bias-free logits; the top-k is taken on s + b, where b
 is a balance bias that only steers the choice; the gates are the raw s of
 the chosen experts divided by their sum. Steps 4-7 are unchanged.
 
+Quantised routed experts (``dequantize_q4``): the routed experts' weights
+may arrive as 4-bit affine groups, about half a byte per weight ("Small MoE
+Architecture, in depth", sections "Worked example: the batch-1 budget on a
+device" and "Quantisation fits MoE unusually well", where routed experts are
+quantised and the shared expert stays at higher precision). The format is a
+reading: groups of 64 consecutive weights along the reduction axis, each
+with a bf16 scale s and bias b, w = s * q + b for the 4-bit code q in
+[0, 15]; two codes per byte, the even position in the low nibble. The
+oracle dequantises exactly (float64) and runs the same layer.
+
 Routing statistics (``routing_stats``): the per-expert token share, the mean
 router probability per expert, the mean router entropy and the Switch
 load-balance term alpha * N * sum_e f_e P_e ("Mixture-of-Experts -- more
@@ -105,6 +115,41 @@ def swiglu(X, Wg, Wu, Wd):
     PyTorch", class Expert; Tutorial 11, section 4, step 4.
     """
     return (silu(X @ Wg.T) * (X @ Wu.T)) @ Wd.T
+
+
+# ----------------------------------------------------------------------------
+# quantised expert weights
+# ----------------------------------------------------------------------------
+
+Q4_GROUP = 64
+
+
+def dequantize_q4(packed, sb):
+    """packed [..., K/2] uint8 (code of position 2i in the low nibble of byte
+    i, 2i+1 in the high nibble), sb [..., K/64] uint32 (bf16 scale in the low
+    half, bf16 bias in the high half) -> float64 [..., K] with
+    w[..., k] = s[..., k // 64] * q[..., k] + b[..., k // 64]."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    sb = np.asarray(sb, dtype=np.uint32)
+    K = packed.shape[-1] * 2
+    q = np.empty(packed.shape[:-1] + (K,), dtype=np.float64)
+    q[..., 0::2] = packed & 0x0F
+    q[..., 1::2] = packed >> 4
+    scale = ((sb & 0xFFFF) << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    bias = ((sb >> 16) << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    if scale.shape[-1] * Q4_GROUP != K:
+        raise ValueError("scale groups do not cover K")
+    return q * np.repeat(scale, Q4_GROUP, axis=-1) + np.repeat(bias, Q4_GROUP, axis=-1)
+
+
+def expert_weights(inp):
+    """The routed experts' weights (gate, up, down) as float64, dequantised
+    when they arrive quantised."""
+    if inp.get("w_gate_sb") is not None:
+        return (dequantize_q4(inp["w_gate"], inp["w_gate_sb"]),
+                dequantize_q4(inp["w_up"], inp["w_up_sb"]),
+                dequantize_q4(inp["w_down"], inp["w_down_sb"]))
+    return to_f64(inp["w_gate"]), to_f64(inp["w_up"]), to_f64(inp["w_down"])
 
 
 # ----------------------------------------------------------------------------
@@ -364,7 +409,8 @@ def layer_forward(inp, ids_override=None):
     E, k = spec.E, spec.k
     L, ids, g, p = route(inp, ids_override)
     counts, offsets, perm, inv = dispatch(ids, E)
-    y = expert_ffn(inp["x"], perm, offsets, k, inp["w_gate"], inp["w_up"], inp["w_down"])
+    Wg, Wu, Wd = expert_weights(inp)
+    y = expert_ffn(inp["x"], perm, offsets, k, Wg, Wu, Wd)
     shared = None
     if inp.get("ws_gate") is not None:
         shared = shared_expert(inp["x"], inp["ws_gate"], inp["ws_up"], inp["ws_down"],
@@ -388,13 +434,13 @@ def token_forward(inp, tokens, ids, gates):
     if has_shared:
         Sg, Su, Sd = (to_f64(inp[n]) for n in ("ws_gate", "ws_up", "ws_down"))
         wsg = to_f64(inp.get("w_shared_gate")) if inp.get("w_shared_gate") is not None else None
+    Wg, Wu, Wd = expert_weights(inp)
     rows = []
     for t, sel, g in zip(tokens, ids, gates):
         xt = X[t:t + 1]
         o = np.zeros(X.shape[1])
         for e, ge in zip(sel, g):
-            o += ge * swiglu(xt, to_f64(inp["w_gate"][e]), to_f64(inp["w_up"][e]),
-                             to_f64(inp["w_down"][e]))[0]
+            o += ge * swiglu(xt, Wg[e], Wu[e], Wd[e])[0]
         if has_shared:
             s = swiglu(xt, Sg, Su, Sd)[0]
             if wsg is not None:

@@ -28,6 +28,13 @@ The pins:
                     a large bias forces an expert in without entering its
                     gate, rank-count brute force on the biased scores, and the
                     dense-mask equivalence above
+  4-bit experts   - the dequantisation against the error bound of an affine
+                    4-bit code (at most half a step), exact recovery of
+                    weights built from known codes (distinct per position, so
+                    a nibble-order or group-index slip shows), and the bytes
+                    per weight against the page's "about half a byte"
+                    ("Small MoE Architecture, in depth", section "Worked
+                    example: the batch-1 budget on a device")
   routing stats   - the 12.5% ideal share of a balanced 8-expert top-2 layer
                     ("Mini-MoE", section "Results"; tests/golden), entropy ln E
                     for a flat router and 0 in the one-hot limit, the Switch
@@ -515,6 +522,58 @@ def check_routing_stats_closed_forms():
         assert aux >= 0.0
 
 
+# ---------------------------------------------------------------------------
+# 4-bit routed-expert weights
+# ---------------------------------------------------------------------------
+
+def check_q4_roundtrip_error_bound():
+    from moe_inputs.generate import quantize_q4_g64
+    r = _rng(21)
+    w = (r.standard_normal((5, 7, 256)) * 0.05).astype(np.float32)
+    w[0, 0, :64] = 0.0  # a constant group
+    packed, sb = quantize_q4_g64(w)
+    dq = O.dequantize_q4(packed, sb)
+    scale = ((sb & 0xFFFF).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    step = np.repeat(scale, 64, axis=-1)
+    err = np.abs(dq - w.astype(np.float64))
+    assert np.all(err <= step / 2 * (1 + 1e-6)), float(np.max(err / step))
+    # the codes use the range: every non-constant group reaches 0 and 15
+    q = np.empty(w.shape, np.int64)
+    q[..., 0::2] = packed & 15
+    q[..., 1::2] = packed >> 4
+    g = q.reshape(5, 7, 4, 64)
+    live = np.ptp(w.reshape(5, 7, 4, 64), axis=-1) > 0
+    assert np.all(g.min(-1)[live] == 0) and np.all(g.max(-1)[live] >= 14)
+
+
+def check_q4_known_codes():
+    """Weights built exactly as s * q + b from known codes: quantising them
+    gives those codes back and dequantising gives the weights exactly."""
+    from moe_inputs.generate import quantize_q4_g64
+    K = 192
+    k = np.arange(K)
+    codes = (k * 7 + 3 + k // 64) % 16
+    for g0 in range(3):  # every group holds a 0 and a 15
+        codes[g0 * 64] = 0
+        codes[g0 * 64 + 1] = 15
+    s = np.array([2.0 ** -7, 2.0 ** -5, 2.0 ** -9])
+    b = np.array([-2.0 ** -4, 0.25, -1.0])
+    w = (s[k // 64] * codes + b[k // 64]).astype(np.float32)[None, :]
+    packed, sb = quantize_q4_g64(w)
+    assert np.array_equal(packed[0] & 15, codes[0::2]) and np.array_equal(packed[0] >> 4, codes[1::2])
+    np.testing.assert_array_equal(O.dequantize_q4(packed, sb), w.astype(np.float64))
+
+
+def check_q4_bytes_per_weight():
+    """Codes plus one bf16 scale and bias per 64 weights: 0.5625 bytes per
+    weight, the page's "about half a byte per parameter"."""
+    from moe_inputs.generate import quantize_q4_g64
+    w = np.zeros((3, 128), np.float32)
+    packed, sb = quantize_q4_g64(w)
+    per = (packed.nbytes + sb.nbytes) / w.size
+    assert per == 0.5625 and abs(per - 0.5) < 0.1
+
+
 ALL_CHECKS = [
     check_worked_example,
     check_brute_force_topk,
@@ -534,4 +593,7 @@ ALL_CHECKS = [
     check_sigmoid_brute_force_topk,
     check_routing_stats_printed_share,
     check_routing_stats_closed_forms,
+    check_q4_roundtrip_error_bound,
+    check_q4_known_codes,
+    check_q4_bytes_per_weight,
 ]

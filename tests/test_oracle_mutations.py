@@ -115,9 +115,27 @@ def _stats_aux_without_N(L, counts, k, mode, alpha):
     return share, P, H, aux / L.shape[1]
 
 
+def _q4_nibbles_swapped(packed, sb):
+    p = np.asarray(packed, dtype=np.uint8)
+    return _ORIG["dequantize_q4"](((p & 15) << 4) | (p >> 4), sb)
+
+
+def _q4_scale_bias_swapped(packed, sb):
+    sb = np.asarray(sb, dtype=np.uint32)
+    return _ORIG["dequantize_q4"](packed, (sb >> 16) | ((sb & 0xFFFF) << 16))
+
+
+def _q4_group_of_32(packed, sb):
+    # scales indexed per 32 positions instead of 64
+    sb = np.asarray(sb, dtype=np.uint32)
+    half = np.repeat(sb, 2, axis=-1)[..., : sb.shape[-1]]
+    return _ORIG["dequantize_q4"](packed, half)
+
+
 _ORIG = {n: getattr(O, n) for n in ("gate_weights", "dispatch", "combine", "gate_up",
                                     "down", "shared_expert", "router_logits", "topk_select",
-                                    "silu", "selection_scores", "routing_stats")}
+                                    "silu", "selection_scores", "routing_stats",
+                                    "dequantize_q4")}
 
 MUTATIONS = [
     ("topk_select", _topk_ties_high),
@@ -138,6 +156,9 @@ MUTATIONS = [
     ("routing_stats", _stats_share_over_T),
     ("routing_stats", _stats_entropy_sign),
     ("routing_stats", _stats_aux_without_N),
+    ("dequantize_q4", _q4_nibbles_swapped),
+    ("dequantize_q4", _q4_scale_bias_swapped),
+    ("dequantize_q4", _q4_group_of_32),
 ]
 
 
