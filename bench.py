@@ -37,7 +37,8 @@ METRIC = "MoE layer fwd tokens/s on 1 GPU; % bf16 MFMA peak (prefill) / % HBM BW
 # Binding roofline of each workload (algorithmic intensity vs the 312.5
 # FLOP/B ridge of 2.5 PFLOP/s bf16 over 8 TB/s).
 BOUND = {"tiny_fp32": "alu", "gemma_upcycled": "hbm", "decode": "hbm",
-         "skewed_prefill": "mfma", "shared_routed": "mfma", "small_moe_sigmoid": "mfma"}
+         "skewed_prefill": "mfma", "shared_routed": "mfma", "small_moe_sigmoid": "mfma",
+         "decode_q4": "hbm"}
 
 
 def log(*a):
@@ -50,21 +51,25 @@ def stage_work(spec, U, T):
     b = spec.act_bytes
     d, h, E, k, hs = spec.d, spec.h, spec.E, spec.k, spec.shared_h
     P = T * k
+    eb = R.Q4_BYTES_PER_WEIGHT if spec.expert_quant else None
     route_b = (E * d + T * d) * b + (4 * E if spec.router_bias else 0) + (d * b if spec.shared_gate else 0)
     route_f = 2.0 * T * d * E + (2.0 * T * d if spec.shared_gate else 0)
     return {
         "route": (route_b, route_f),
         "dispatch": (0.0, 0.0),
-        "gate_up": (R.gate_up_bytes(T, d, h, U, b, hs), R.gate_up_flops(P, d, h, T, hs)),
-        "down": (R.down_bytes(d, h, U, b, hs), R.down_flops(P, d, h, T, hs)),
+        "gate_up": (R.gate_up_bytes(T, d, h, U, b, hs, eb), R.gate_up_flops(P, d, h, T, hs)),
+        "down": (R.down_bytes(d, h, U, b, hs, eb), R.down_flops(P, d, h, T, hs)),
         "combine": (T * d * b, 0.0),
     }
 
 
 # kernel-name prefixes of each stage's (first) kernel in a rocprofv3 record
-STAGE_KERNEL = {"route": ("route_kernel",), "dispatch": ("scan_kernel",),
-                "gate_up": ("gemm_bf16_pers<0", "gemm_bf16_kernel<0"),
-                "down": ("gemm_bf16_pers<1", "gemm_bf16_kernel<1"), "combine": ("combine_",)}
+STAGE_KERNEL = {"route": ("route_kernel", "route_part_kernel"), "dispatch": ("scan_kernel",),
+                "gate_up": ("gemm_bf16_pers<0", "gemm_bf16_kernel<0", "gemm_small_kernel<0",
+                            "gemm_small_q4_kernel<0"),
+                "down": ("gemm_bf16_pers<1", "gemm_bf16_kernel<1", "gemm_small_kernel<1",
+                         "gemm_small_pers<1", "gemm_small_q4_kernel<1"),
+                "combine": ("combine_",)}
 
 
 def kernel_sources_sha():
@@ -170,10 +175,12 @@ def main():
             return None
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        if a.dtype == np.uint32:  # packed scale|bias words
+            return torch.from_numpy(a.view(np.int32)).cuda()
         return torch.from_numpy(a).cuda()
 
     wnames = ("w_router", "b_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down",
-              "w_shared_gate")
+              "w_shared_gate", "w_gate_sb", "w_up_sb", "w_down_sb")
     w0 = {n: dev(inp.get(n)) for n in wnames}
     set_bytes = sum(t.numel() * t.element_size() for t in w0.values() if t is not None)
     nsets = max(1, math.ceil(args.rotate_gib * 2**30 / set_bytes))
@@ -263,7 +270,8 @@ def main():
     sec = ms_per_step * 1e-3
     lflops = R.layer_flops(T, spec.d, spec.E, spec.h, spec.k, spec.shared_h, spec.shared_gate)
     lbytes = R.layer_bytes(T, spec.d, spec.E, spec.h, U, spec.act_bytes, spec.shared_h,
-                           spec.shared_gate, spec.router_bias is not None)
+                           spec.shared_gate, spec.router_bias is not None,
+                           R.Q4_BYTES_PER_WEIGHT if spec.expert_quant else None)
     result = {
         "metric": METRIC,
         "value": T / sec,
@@ -282,6 +290,7 @@ def main():
                    "gates": ["softmax over all", "softmax over the selected",
                              "sigmoid affinities, selection-only balance bias"][spec.mode]
                    + (" + renormalised" if spec.renormalize else ""),
+                   "routed_weights": spec.expert_quant or "activation dtype",
                    "weight_copies": nsets, "parallelism": "single GPU"},
         "roofline": roof,
         "layer": {"mfma_frac": lflops / sec / R.PEAK_BF16_MFMA_FLOPS,

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_EXPERTS 256
 #define MOE_NUM_STAGES 5 /* route, dispatch, gate_up, down, combine */
 
@@ -74,6 +74,17 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 typedef enum { MOE_SOFTMAX_ALL = 0, MOE_SOFTMAX_SELECTED = 1, MOE_SIGMOID = 2 } moe_score_mode;
+
+/* Storage of the routed experts' weights (the shared expert stays in
+ * cfg->dtype). MOE_QUANT_Q4_G64: 4-bit affine codes in groups of 64 along the
+ * reduction axis ("Small MoE Architecture, in depth", sections "Worked
+ * example: the batch-1 budget on a device" and "Quantisation fits MoE
+ * unusually well": routed experts at about half a byte per weight, the
+ * shared expert at higher precision). A weight matrix [.., N, K] becomes
+ * codes [.., N, K/2] bytes (position 2i in the low nibble of byte i) and
+ * sb [.., N, K/64] uint32 (bf16 scale s in the low half, bf16 bias b in the
+ * high half), w = s * q + b. */
+typedef enum { MOE_QUANT_NONE = 0, MOE_QUANT_Q4_G64 = 1 } moe_expert_quant;
 
 /* Which entry point a workspace is sized for (moe_workspace_size_entry). */
 typedef enum {
@@ -103,19 +114,23 @@ typedef struct {
                               choice only (MOE_SIGMOID) */
   int32_t shared_h;        /* hidden width of the shared expert, 0 = none */
   int32_t shared_gate;     /* 1: the shared expert is scaled by sigmoid(w_s . x) */
+  int32_t expert_quant;    /* moe_expert_quant of the routed experts */
 } moe_config;
 
 /* Weights of one layer, in cfg->dtype unless stated otherwise. */
 typedef struct {
   const void* w_router;      /* [E, d] */
   const float* b_router;     /* [E] float32, or NULL when !has_router_bias */
-  const void* w_gate;        /* [E, h, d] */
-  const void* w_up;          /* [E, h, d] */
-  const void* w_down;        /* [E, d, h] */
+  const void* w_gate;        /* [E, h, d]   (MOE_QUANT_Q4_G64: codes [E, h, d/2]) */
+  const void* w_up;          /* [E, h, d]   (MOE_QUANT_Q4_G64: codes [E, h, d/2]) */
+  const void* w_down;        /* [E, d, h]   (MOE_QUANT_Q4_G64: codes [E, d, h/2]) */
   const void* ws_gate;       /* [shared_h, d]  (shared_h > 0) */
   const void* ws_up;         /* [shared_h, d]  (shared_h > 0) */
   const void* ws_down;       /* [d, shared_h]  (shared_h > 0) */
   const void* w_shared_gate; /* [d]            (shared_gate) */
+  const uint32_t* w_gate_sb; /* [E, h, d/64] scale|bias (MOE_QUANT_Q4_G64, else unused) */
+  const uint32_t* w_up_sb;   /* [E, h, d/64] */
+  const uint32_t* w_down_sb; /* [E, d, h/64] */
 } moe_weights;
 
 /* Library ABI version (MOE_ABI_VERSION). */
@@ -161,7 +176,10 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* ids, int32_t* coun
  * ("Tutorial 11: Mixture of Experts (MoE)", section 3, step 2):
  *   act[r] = silu(W_g[e] x_t) * (W_u[e] x_t), t = perm[r] / k, for every
  *   sorted row r of expert e (offsets[e] <= r < offsets[e+1]).
- *   x [T, d], perm [P], offsets [E+1], w_gate/w_up [E, h, d] -> act [P, h]. */
+ *   x [T, d], perm [P], offsets [E+1], w_gate/w_up [E, h, d] -> act [P, h].
+ * moe_gate_up, moe_down and moe_expert_ffn take routed weights in
+ * cfg->dtype only: a configuration with expert_quant != MOE_QUANT_NONE
+ * returns MOE_ERR_UNSUPPORTED (use moe_layer_forward). */
 moe_status moe_gate_up(const moe_config* cfg, const void* x, const int32_t* perm,
                        const int32_t* offsets, const void* w_gate, const void* w_up,
                        void* act, void* ws, size_t ws_bytes, void* stream);
@@ -215,7 +233,14 @@ moe_status moe_routing_stats(const moe_config* cfg, const float* logits, const i
 
 /* The whole layer: route, dispatch, gate/up, down, combine (+ shared).
  *   x [T, d] -> out [T, d]. ids [T, k], gates [T, k] and counts [E] are
- *   optional copies of the routing (NULL to skip). */
+ *   optional copies of the routing (NULL to skip).
+ *   With cfg->expert_quant == MOE_QUANT_Q4_G64 the routed experts are read in
+ *   that format (w_gate_sb, w_up_sb, w_down_sb required) by the small-batch
+ *   expert kernels, which serve layers of at most 16 routed rows per expert
+ *   on average (T * top_k <= 16 * E) with d and h multiples of 64 and at most
+ *   4096, in bf16; other quantised shapes return MOE_ERR_UNSUPPORTED. The
+ *   dequantised weights are rounded to bf16 (to nearest, halves away from
+ *   zero) before the bf16 products. */
 moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x,
                              void* out, int32_t* ids, float* gates, int32_t* counts,
                              void* ws, size_t ws_bytes, void* stream);

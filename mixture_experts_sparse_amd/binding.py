@@ -29,6 +29,8 @@ MOE_BF16 = 1
 MOE_SOFTMAX_ALL = 0
 MOE_SOFTMAX_SELECTED = 1
 MOE_SIGMOID = 2
+MOE_QUANT_NONE = 0
+MOE_QUANT_Q4_G64 = 1
 
 MOE_ENTRY_LAYER_FORWARD = 0
 MOE_ENTRY_DISPATCH = 1
@@ -45,7 +47,7 @@ STAGE_NAMES = ("route", "dispatch", "gate_up", "down", "combine")
 class MoeConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "d", "E", "h", "top_k", "dtype", "mode", "renormalize", "has_router_bias",
-        "shared_h", "shared_gate")]
+        "shared_h", "shared_gate", "expert_quant")]
 
 
 class MoeWeights(ctypes.Structure):
@@ -54,6 +56,8 @@ class MoeWeights(ctypes.Structure):
         ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
         ("ws_gate", ctypes.c_void_p), ("ws_up", ctypes.c_void_p), ("ws_down", ctypes.c_void_p),
         ("w_shared_gate", ctypes.c_void_p),
+        ("w_gate_sb", ctypes.c_void_p), ("w_up_sb", ctypes.c_void_p),
+        ("w_down_sb", ctypes.c_void_p),
     ]
 
 
@@ -131,10 +135,11 @@ def _check(status: int, what: str):
 # ----------------------------------------------------------------------------
 
 def make_config(T, d, E, h, top_k, dtype=MOE_BF16, mode=MOE_SOFTMAX_ALL, renormalize=False,
-                has_router_bias=False, shared_h=0, shared_gate=False) -> MoeConfig:
+                has_router_bias=False, shared_h=0, shared_gate=False,
+                expert_quant=MOE_QUANT_NONE) -> MoeConfig:
     return MoeConfig(int(T), int(d), int(E), int(h), int(top_k), int(dtype), int(mode),
                      int(bool(renormalize)), int(bool(has_router_bias)), int(shared_h),
-                     int(bool(shared_gate)))
+                     int(bool(shared_gate)), int(expert_quant))
 
 
 def config_from_spec(spec, T: Optional[int] = None) -> MoeConfig:
@@ -142,7 +147,9 @@ def config_from_spec(spec, T: Optional[int] = None) -> MoeConfig:
     return make_config(spec.T if T is None else T, spec.d, spec.E, spec.h, spec.k,
                        dtype=spec.dtype, mode=spec.mode, renormalize=spec.renormalize,
                        has_router_bias=spec.router_bias is not None, shared_h=spec.shared_h,
-                       shared_gate=spec.shared_gate and spec.shared_h > 0)
+                       shared_gate=spec.shared_gate and spec.shared_h > 0,
+                       expert_quant=MOE_QUANT_Q4_G64 if getattr(spec, "expert_quant", None)
+                       else MOE_QUANT_NONE)
 
 
 def validate_config(cfg: MoeConfig) -> int:

@@ -39,6 +39,56 @@ __device__ __forceinline__ u32x4_t load_k8_w(const uint16_t* row, int kq, int K)
   return *reinterpret_cast<const u32x4_t*>(row + min(kq, K - 8));
 }
 
+// One 16-row block's epilogue: each wave's partial tiles (acc, MFMA C layout:
+// lane holds rows 4 (lane / 16) + i of column 16 t + lane % 16) go to LDS,
+// the NW partials are added in wave order, and the bf16 results (SiLU
+// product for gate/up) are stored for rows rb .. rb + 15 < cnt of the
+// expert's range starting at r0, columns n0 .. n0 + 16 NT - 1 < N.
+// Two workgroup barriers; called by every thread.
+template <int KIND, int NW, int NB, int NT>
+__device__ __forceinline__ void small_block_epilogue(const GemmParams& p,
+                                                     float (*red)[NB][16][16 * NT],
+                                                     const floatx4_t (&acc)[NB][NT], int r0,
+                                                     int rb, int cnt, int n0) {
+  constexpr int NCOL = 16 * NT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int N = p.N;
+#pragma unroll
+  for (int m = 0; m < NB; ++m)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][m][(lane >> 4) * 4 + i][t * 16 + (lane & 15)] = acc[m][t][i];
+  __syncthreads();
+  for (int it = threadIdx.x; it < 16 * NCOL / 2; it += NW * 64) {
+    const int row = it / (NCOL / 2);
+    const int c = (it - row * (NCOL / 2)) * 2;
+    const int n = n0 + c;
+    if (rb + row < cnt && n < N) {  // N is a multiple of 8: n + 1 < N too
+      float v[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float g = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) g += red[w][0][row][c + j];
+        if constexpr (KIND == 0) {
+          float u = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) u += red[w][NB - 1][row][c + j];
+          v[j] = silu_fast(g) * u;
+        } else {
+          v[j] = g;
+        }
+      }
+      const uint32_t o = static_cast<uint32_t>(f32_to_bf16(v[0])) |
+                         (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.out) +
+                                   static_cast<size_t>(r0 + rb + row) * N + n) = o;
+    }
+  }
+  __syncthreads();
+}
+
 template <int KIND, int NW, int KS, int NT>
 __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmParams p) {
   constexpr int NB = KIND == 0 ? 2 : 1;  // weight matrices: gate and up, or down
@@ -117,42 +167,124 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmParams p) {
           acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               a, __builtin_bit_cast(bf16x8_t, bq[m][t][s]), acc[m][t], 0, 0, 0);
     }
-    // lane holds rows 4 (lane / 16) + i of column 16 t + lane % 16
+    small_block_epilogue<KIND, NW, NB, NT>(p, red, acc, r0, rb, cnt, n0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4-bit routed weights (MOE_QUANT_Q4_G64): codes [E, N, K/2] (position 2i in
+// the low nibble of byte i) and scale|bias words [E, N, K/64], w = s q + b.
+// Every MFMA step must lie inside one 64-wide scale group, so the K layout
+// is: scale group G of a wave's range, half h in {0, 1}; lane group g holds
+// K values kb + 64 G + 16 g + 8 h .. + 7 (x and weights alike). A lane then
+// reads its 16 codes of a group as one 8-byte load and the group's scale and
+// bias as one 4-byte word; the codes stay packed in registers and are
+// dequantised to bf16 right before each MFMA (one FMA per weight, rounded
+// to nearest with halves away from zero).
+// ---------------------------------------------------------------------------
+
+// w_i = s * q_i + b for the 8 codes of D (code i in nibble i), as 8 bf16.
+__device__ __forceinline__ u32x4_t dequant8(uint32_t D, float s, float b) {
+  const uint32_t lo = D & 0x0F0F0F0Fu;          // codes 0, 2, 4, 6 (one per byte)
+  const uint32_t hi = (D >> 4) & 0x0F0F0F0Fu;   // codes 1, 3, 5, 7
+  u32x4_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float w0 = fmaf(s, static_cast<float>((lo >> (8 * j)) & 0xFFu), b);
+    const float w1 = fmaf(s, static_cast<float>((hi >> (8 * j)) & 0xFFu), b);
+    // high halves of the rounded words: w0 in the low bf16, w1 in the high
+    r[j] = __builtin_amdgcn_perm(__float_as_uint(w1) + 0x8000u, __float_as_uint(w0) + 0x8000u,
+                                 0x07060302u);
+  }
+  return r;
+}
+
+template <int KIND, int NW, int KS, int NT>
+__global__ __launch_bounds__(NW * 64) void gemm_small_q4_kernel(GemmParams p) {
+  constexpr int NB = KIND == 0 ? 2 : 1;
+  constexpr int NCOL = 16 * NT;
+  constexpr int KG = KS / 2;  // scale groups per wave
+  static_assert(KS % 2 == 0, "whole scale groups per wave");
+  __shared__ float red[NW][NB][16][NCOL];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int N = p.N, K = p.K;
+  const int ncs = (N + NCOL - 1) / NCOL;
+  const int slot = blockIdx.x / ncs;
+  const int n0 = (blockIdx.x - slot * ncs) * NCOL;
+  int ntouched = p.meta[1];
+  int4 ti = *reinterpret_cast<const int4*>(p.touched + 4 * slot);
+  pin_s(ntouched); pin_s(ti.x); pin_s(ti.y); pin_s(ti.z);
+  if (slot >= ntouched) return;
+  const int e = min(max(ti.x, 0), p.E - 1);
+  const int r0 = min(max(ti.y, 0), p.P);
+  const int cnt = min(max(ti.z, 0), p.P - r0);
+  const int kb = wave * KS * 32 + (lane >> 4) * 16;  // lane's first K index in group 0
+  const uint16_t* A = static_cast<const uint16_t*>(p.a);
+
+  int first_pair = 0;
+  if constexpr (KIND == 0) first_pair = p.perm[min(max(r0 + min(lane & 15, cnt - 1), 0), p.P - 1)];
+
+  uint2 qc[NB][NT][KG];
+  uint32_t sb[NB][NT][KG];
+#pragma unroll
+  for (int m = 0; m < NB; ++m) {
+    const uint8_t* Q = static_cast<const uint8_t*>(m == 0 ? p.b0 : p.b1) +
+                       static_cast<size_t>(e) * N * (K / 2);
+    const uint32_t* S = (m == 0 ? p.b0_sb : p.b1_sb) + static_cast<size_t>(e) * N * (K / 64);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      // columns past N reread column N - 1; their sums are never stored
+      const int n = min(n0 + t * 16 + (lane & 15), N - 1);
+#pragma unroll
+      for (int G = 0; G < KG; ++G) {
+        // groups past K reread the last one: the x operand is zero there
+        const int kq = min(kb + 64 * G, K - 16);
+        qc[m][t][G] = *reinterpret_cast<const uint2*>(Q + (static_cast<size_t>(n) * K + kq) / 2);
+        sb[m][t][G] = S[static_cast<size_t>(n) * (K / 64) + kq / 64];
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
+
+  for (int rb = 0; rb < cnt; rb += 16) {
+    const int rr = min(rb + (lane & 15), cnt - 1);
+    const uint16_t* arow;
+    if constexpr (KIND == 0) {
+      const int pair = rb == 0 ? first_pair : p.perm[r0 + rr];
+      const int tok = min(max(pair / p.k, 0), p.a_rows - 1);
+      arow = A + static_cast<size_t>(tok) * K;
+    } else {
+      arow = A + static_cast<size_t>(r0 + rr) * K;
+    }
+    u32x4_t aq[KS];
+#pragma unroll
+    for (int G = 0; G < KG; ++G)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) aq[2 * G + h] = load_k8(arow, kb + 64 * G + 8 * h, K);
+    floatx4_t acc[NB][NT];
 #pragma unroll
     for (int m = 0; m < NB; ++m)
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t) acc[m][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave][m][(lane >> 4) * 4 + i][t * 16 + (lane & 15)] = acc[m][t][i];
-    __syncthreads();
-    // epilogue: one thread per pair of adjacent columns of one row
-    for (int it = threadIdx.x; it < 16 * NCOL / 2; it += NW * 64) {
-      const int row = it / (NCOL / 2);
-      const int c = (it - row * (NCOL / 2)) * 2;
-      const int n = n0 + c;
-      if (rb + row < cnt && n < N) {  // N is a multiple of 8: n + 1 < N too
-        float v[2];
+    for (int G = 0; G < KG; ++G) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          float g = 0.f;
+      for (int m = 0; m < NB; ++m)
 #pragma unroll
-          for (int w = 0; w < NW; ++w) g += red[w][0][row][c + j];
-          if constexpr (KIND == 0) {
-            float u = 0.f;
+        for (int t = 0; t < NT; ++t) {
+          const float sc = bf16_to_f32(static_cast<uint16_t>(sb[m][t][G] & 0xFFFFu));
+          const float bi = bf16_to_f32(static_cast<uint16_t>(sb[m][t][G] >> 16));
 #pragma unroll
-            for (int w = 0; w < NW; ++w) u += red[w][NB - 1][row][c + j];
-            v[j] = silu_fast(g) * u;
-          } else {
-            v[j] = g;
+          for (int h = 0; h < 2; ++h) {
+            const u32x4_t w = dequant8(h == 0 ? qc[m][t][G].x : qc[m][t][G].y, sc, bi);
+            acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, aq[2 * G + h]), __builtin_bit_cast(bf16x8_t, w),
+                acc[m][t], 0, 0, 0);
           }
         }
-        const uint32_t o = static_cast<uint32_t>(f32_to_bf16(v[0])) |
-                           (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.out) +
-                                     static_cast<size_t>(r0 + rb + row) * N + n) = o;
-      }
     }
-    __syncthreads();
+    small_block_epilogue<KIND, NW, NB, NT>(p, red, acc, r0, rb, cnt, n0);
   }
 }
 
@@ -357,12 +489,32 @@ static hipError_t launch_small_kind(const GemmParams& p, int slots, hipStream_t 
   return hipGetLastError();
 }
 
+template <int KIND, int NT>
+static hipError_t launch_small_q4(const GemmParams& p, int slots, hipStream_t s) {
+  const SmallShape sh = small_shape(p.K);
+  const long long nblk = static_cast<long long>(slots) * ceil_div(p.N, 16 * NT);
+  if (nblk <= 0) return hipSuccess;
+  const unsigned g = static_cast<unsigned>(nblk);
+  if (sh.nw == 4 && sh.ks == 4) gemm_small_q4_kernel<KIND, 4, 4, NT><<<g, 256, 0, s>>>(p);
+  else if (sh.nw == 4 && sh.ks == 8) gemm_small_q4_kernel<KIND, 4, 8, NT><<<g, 256, 0, s>>>(p);
+  else if (sh.nw == 4 && sh.ks == 16) gemm_small_q4_kernel<KIND, 4, 16, NT><<<g, 256, 0, s>>>(p);
+  else if (sh.nw == 8 && sh.ks == 16) gemm_small_q4_kernel<KIND, 8, 16, NT><<<g, 512, 0, s>>>(p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_small(const GemmParams& p, hipStream_t s) {
   if (p.dtype != MOE_BF16 || p.touched == nullptr || p.shared_T != 0 || p.N % 8 != 0 ||
       p.K % 8 != 0 || small_shape(p.K).nw == 0)
     return hipErrorInvalidValue;
   // at most min(P, E) experts hold rows
   const int slots = p.P < p.E ? p.P : p.E;
+  if (p.quant == MOE_QUANT_Q4_G64) {
+    if (p.K % 64 != 0 || p.b0_sb == nullptr || (p.kind == 0 && p.b1_sb == nullptr))
+      return hipErrorInvalidValue;
+    if (p.kind == 0) return launch_small_q4<0, 1>(p, slots, s);
+    return launch_small_q4<1, 2>(p, slots, s);
+  }
   if (p.kind == 0) return launch_small_kind<0, 1>(p, slots, s);
   return launch_small_kind<1, 2>(p, slots, s);
 }

@@ -33,6 +33,8 @@ moe_status check_cfg(const moe_config* c) {
   if (c->shared_gate != 0 && c->shared_gate != 1) return MOE_ERR_INVALID_ARG;
   if (c->shared_h < 0) return MOE_ERR_INVALID_ARG;
   if (c->shared_gate && c->shared_h == 0) return MOE_ERR_INVALID_ARG;
+  if (c->expert_quant != MOE_QUANT_NONE && c->expert_quant != MOE_QUANT_Q4_G64)
+    return MOE_ERR_INVALID_ARG;
   if (c->E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
   if (c->d % 8 != 0 || c->h % 8 != 0 || c->shared_h % 8 != 0) return MOE_ERR_UNSUPPORTED;
   // int32 row/element indices inside the kernels, and byte offsets of the
@@ -277,6 +279,7 @@ moe_status moe_gate_up(const moe_config* cfg, const void* x, const int32_t* perm
                        void* act, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(check_cfg(cfg));
   const moe_config& c = *cfg;
+  if (c.expert_quant != MOE_QUANT_NONE) return MOE_ERR_UNSUPPORTED;
   if (c.T == 0) return MOE_OK;
   MOE_TRY(need(x)); MOE_TRY(need(perm)); MOE_TRY(need(offsets));
   MOE_TRY(need(w_gate)); MOE_TRY(need(w_up)); MOE_TRY(need(act));
@@ -290,6 +293,7 @@ moe_status moe_down(const moe_config* cfg, const void* act, const int32_t* offse
                     const void* w_down, void* y, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(check_cfg(cfg));
   const moe_config& c = *cfg;
+  if (c.expert_quant != MOE_QUANT_NONE) return MOE_ERR_UNSUPPORTED;
   if (c.T == 0) return MOE_OK;
   MOE_TRY(need(act)); MOE_TRY(need(offsets)); MOE_TRY(need(w_down)); MOE_TRY(need(y));
   MOE_TRY(check_ws(c, MOE_ENTRY_DOWN, ws, ws_bytes));
@@ -304,6 +308,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* p
                           void* stream) {
   MOE_TRY(check_cfg(cfg));
   const moe_config& c = *cfg;
+  if (c.expert_quant != MOE_QUANT_NONE) return MOE_ERR_UNSUPPORTED;
   if (c.T == 0) return MOE_OK;
   MOE_TRY(need(x)); MOE_TRY(need(perm)); MOE_TRY(need(offsets));
   MOE_TRY(need(w_gate)); MOE_TRY(need(w_up)); MOE_TRY(need(w_down)); MOE_TRY(need(y));
@@ -398,6 +403,11 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
     MOE_TRY(need(w->ws_gate)); MOE_TRY(need(w->ws_up)); MOE_TRY(need(w->ws_down));
     if (c.shared_gate) MOE_TRY(need(w->w_shared_gate));
   }
+  const bool q4 = c.expert_quant == MOE_QUANT_Q4_G64;
+  if (q4) {
+    if (!q4_supported(c)) return MOE_ERR_UNSUPPORTED;
+    MOE_TRY(need(w->w_gate_sb)); MOE_TRY(need(w->w_up_sb)); MOE_TRY(need(w->w_down_sb));
+  }
   MOE_TRY(maybe(ids)); MOE_TRY(maybe(gates)); MOE_TRY(maybe(counts));
   MOE_TRY(check_ws(c, MOE_ENTRY_LAYER_FORWARD, ws, ws_bytes));
   if (c.T == 0) return MOE_OK;
@@ -466,21 +476,48 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
   void* y = at<void>(ws, L.y);
   void* ys = at<void>(ws, L.ys);
   const bool small = use_small_gemm(c);
+  // the shared expert alone on the tiled kernel (the small-batch kernels run
+  // the routed experts only)
+  auto shared_only = [&](int kind) {
+    GemmParams g{};
+    g.kind = kind; g.dtype = c.dtype; g.k = c.top_k; g.E = c.E;
+    g.P = 0; g.max_mtiles = 0; g.a_rows = c.T;
+    g.tile_m = choose_tile_m(c.T, 1);
+    g.shared_T = c.T;
+    if (kind == 0) {
+      g.sa = x; g.sK = c.d; g.sb0 = w->ws_gate; g.sb1 = w->ws_up; g.sN = c.shared_h; g.sout = act_s;
+    } else {
+      g.sa = act_s; g.sK = c.shared_h; g.sb0 = w->ws_down; g.sN = c.d; g.sout = ys;
+    }
+    return g;
+  };
   GemmParams g = gemm_base(c, ws, offsets, 0);
   g.a = x; g.perm = perm; g.K = c.d; g.b0 = w->w_gate; g.b1 = w->w_up; g.N = c.h; g.out = act;
-  if (c.shared_h > 0) {
-    g.shared_T = c.T; g.sa = x; g.sK = c.d; g.sb0 = w->ws_gate; g.sb1 = w->ws_up;
-    g.sN = c.shared_h; g.sout = act_s;
+  if (q4) { g.quant = MOE_QUANT_Q4_G64; g.b0_sb = w->w_gate_sb; g.b1_sb = w->w_up_sb; }
+  if (small) {
+    MOE_HIP(launch_gemm_small(g, s));
+    if (c.shared_h > 0) MOE_HIP(launch_gemm(shared_only(0), s));
+  } else {
+    if (c.shared_h > 0) {
+      g.shared_T = c.T; g.sa = x; g.sK = c.d; g.sb0 = w->ws_gate; g.sb1 = w->ws_up;
+      g.sN = c.shared_h; g.sout = act_s;
+    }
+    MOE_HIP(launch_gemm(g, s));
   }
-  MOE_HIP(small ? launch_gemm_small(g, s) : launch_gemm(g, s));
   MOE_HIP(mark(3));
   GemmParams g2 = gemm_base(c, ws, offsets, 1);
   g2.a = act; g2.K = c.h; g2.b0 = w->w_down; g2.N = c.d; g2.out = y;
-  if (c.shared_h > 0) {
-    g2.shared_T = c.T; g2.sa = act_s; g2.sK = c.shared_h; g2.sb0 = w->ws_down;
-    g2.sN = c.d; g2.sout = ys;
+  if (q4) { g2.quant = MOE_QUANT_Q4_G64; g2.b0_sb = w->w_down_sb; }
+  if (small) {
+    MOE_HIP(launch_gemm_small(g2, s));
+    if (c.shared_h > 0) MOE_HIP(launch_gemm(shared_only(1), s));
+  } else {
+    if (c.shared_h > 0) {
+      g2.shared_T = c.T; g2.sa = act_s; g2.sK = c.shared_h; g2.sb0 = w->ws_down;
+      g2.sN = c.d; g2.sout = ys;
+    }
+    MOE_HIP(launch_gemm(g2, s));
   }
-  MOE_HIP(small ? launch_gemm_small(g2, s) : launch_gemm(g2, s));
   MOE_HIP(mark(4));
   CombineParams cp{y, inv, gates_p, c.shared_h > 0 ? ys : nullptr, sg, out, c.T, c.d, c.top_k,
                     c.dtype, c.T * c.top_k};

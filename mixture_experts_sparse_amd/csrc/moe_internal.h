@@ -61,12 +61,17 @@ inline SmallShape small_shape(int K) {
   if (K <= 8 * 16 * 32) return {8, 16};
   return {0, 0};
 }
-// The small-batch GEMMs run when every expert averages at most 16 rows, the
-// layer is bf16 with no shared expert, and both reductions fit a shape.
+// The small-batch GEMMs run the routed experts when every expert averages at
+// most 16 rows, the layer is bf16 and both reductions fit a shape (a shared
+// expert, if any, goes through the tiled kernel on its own).
 inline bool use_small_gemm(const moe_config& c) {
-  return c.dtype == MOE_BF16 && c.shared_h == 0 &&
-         static_cast<long long>(c.T) * c.top_k <= 16LL * c.E &&
+  return c.dtype == MOE_BF16 && static_cast<long long>(c.T) * c.top_k <= 16LL * c.E &&
          small_shape(c.d).nw > 0 && small_shape(c.h).nw > 0;
+}
+// 4-bit routed experts are read by the small-batch kernels only, with
+// reductions and widths in whole 64-wide scale groups.
+inline bool q4_supported(const moe_config& c) {
+  return use_small_gemm(c) && c.d % 64 == 0 && c.h % 64 == 0;
 }
 
 // Workspace carve-up. Offsets are in bytes from the start of ws.
@@ -168,6 +173,11 @@ struct GemmParams {
   // B operand, routed experts
   const void* b0;         // gate/up: w_gate [E, h, d]; down: w_down [E, d, h]
   const void* b1;         // gate/up: w_up   [E, h, d]; down: unused
+  // 4-bit routed weights (quant == MOE_QUANT_Q4_G64): b0/b1 hold codes
+  // [E, N, K/2] and these the per-64 scale|bias words [E, N, K/64]
+  const uint32_t* b0_sb;
+  const uint32_t* b1_sb;
+  int quant;
   int N;                  // output columns: h (gate/up) or d (down)
   void* out;              // act [P, h] or y [P, d]
   // tile table

@@ -9,8 +9,10 @@ what the method must do, not what an implementation adds:
 * bytes = U*3*d*h*b (the weights of the U experts that received at least one
           token) + E*d*b (router) + T*d*b (x) + T*d*b (out)
           + 3*d*hs*b + d*b (shared expert) + 4*E (fp32 router bias),
-  with b the bytes per activation/weight element. Intermediates (act, y,
-  dispatch tables) are implementation traffic and are not counted.
+  with b the bytes per activation/weight element; routed experts in the
+  4-bit format count Q4_BYTES_PER_WEIGHT (codes plus one bf16 scale and
+  bias per 64 weights) instead of b. Intermediates (act, y, dispatch
+  tables) are implementation traffic and are not counted.
 
 Two formulas from the pages pin this module's arithmetic:
 * the gathered-weight tensor a naive dispatch builds, T*h*d*bytes
@@ -28,6 +30,10 @@ PEAK_BF16_MFMA_FLOPS = 2.5e15       # dense bf16 MFMA
 PEAK_FP32_VALU_FLOPS = 157.3e12     # fp32 vector
 PEAK_HBM_BYTES = 8.0e12             # HBM3E
 
+# 4-bit routed-expert weights: half a byte per code plus 2 + 2 bytes of
+# scale and bias per group of 64 weights
+Q4_BYTES_PER_WEIGHT = 0.5 + 4.0 / 64
+
 
 def layer_flops(T, d, E, h, k, hs=0, shared_gate=False):
     f = 2.0 * T * d * E + 2.0 * T * k * 3 * d * h
@@ -38,9 +44,11 @@ def layer_flops(T, d, E, h, k, hs=0, shared_gate=False):
     return f
 
 
-def layer_bytes(T, d, E, h, U, elem_bytes, hs=0, shared_gate=False, has_bias=False):
+def layer_bytes(T, d, E, h, U, elem_bytes, hs=0, shared_gate=False, has_bias=False,
+                expert_bytes=None):
     b = elem_bytes
-    n = U * 3.0 * d * h * b + E * d * b + 2.0 * T * d * b
+    eb = b if expert_bytes is None else expert_bytes
+    n = U * 3.0 * d * h * eb + E * d * b + 2.0 * T * d * b
     if hs:
         n += 3.0 * d * hs * b
         if shared_gate:
@@ -55,17 +63,19 @@ def gate_up_flops(P, d, h, T=0, hs=0):
     return 2.0 * P * 2 * d * h + 2.0 * T * 2 * d * hs
 
 
-def gate_up_bytes(T, d, h, U, elem_bytes, hs=0):
+def gate_up_bytes(T, d, h, U, elem_bytes, hs=0, expert_bytes=None):
     """Gate and up weights of the touched experts (+ shared) and x, once."""
-    return (U * 2.0 * d * h + 2.0 * d * hs + T * d) * elem_bytes
+    eb = elem_bytes if expert_bytes is None else expert_bytes
+    return U * 2.0 * d * h * eb + (2.0 * d * hs + T * d) * elem_bytes
 
 
 def down_flops(P, d, h, T=0, hs=0):
     return 2.0 * P * d * h + 2.0 * T * d * hs
 
 
-def down_bytes(d, h, U, elem_bytes, hs=0):
-    return (U * d * h + d * hs) * elem_bytes
+def down_bytes(d, h, U, elem_bytes, hs=0, expert_bytes=None):
+    eb = elem_bytes if expert_bytes is None else expert_bytes
+    return U * d * h * eb + d * hs * elem_bytes
 
 
 def gathered_weight_bytes(T, h, d, elem_bytes):

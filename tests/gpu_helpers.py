@@ -45,6 +45,8 @@ def dev(a):
         return None
     if a.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    if a.dtype == np.uint32:  # packed words: only the bits matter
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).cuda()
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
@@ -56,7 +58,7 @@ def host(t) -> np.ndarray:
 
 def device_inputs(inp: dict) -> dict:
     names = ("x", "w_router", "b_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up",
-             "ws_down", "w_shared_gate")
+             "ws_down", "w_shared_gate", "w_gate_sb", "w_up_sb", "w_down_sb")
     return {n: dev(inp.get(n)) for n in names}
 
 
@@ -73,7 +75,8 @@ def run_layer(inp: dict, d_inp: dict = None, T: int = None):
     w = {"w_router": d_inp["w_router"], "b_router": d_inp["b_router"],
          "w_gate": d_inp["w_gate"], "w_up": d_inp["w_up"], "w_down": d_inp["w_down"],
          "ws_gate": d_inp["ws_gate"], "ws_up": d_inp["ws_up"], "ws_down": d_inp["ws_down"],
-         "w_shared_gate": d_inp["w_shared_gate"]}
+         "w_shared_gate": d_inp["w_shared_gate"], "w_gate_sb": d_inp.get("w_gate_sb"),
+         "w_up_sb": d_inp.get("w_up_sb"), "w_down_sb": d_inp.get("w_down_sb")}
     x = d_inp["x"][:Tn]
     out = B.layer_forward(cfg, w, x, ids=ids, gates=gates, counts=counts)
     torch.cuda.synchronize()

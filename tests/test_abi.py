@@ -17,7 +17,7 @@ def test_library_exports_every_header_function():
     assert len(names) >= 14
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 def test_status_strings():
@@ -45,6 +45,8 @@ def _cfg(**kw):
     (dict(dtype=7), B.MOE_ERR_INVALID_ARG),
     (dict(mode=3), B.MOE_ERR_INVALID_ARG),
     (dict(mode=B.MOE_SIGMOID, has_router_bias=True), B.MOE_OK),
+    (dict(expert_quant=B.MOE_QUANT_Q4_G64), B.MOE_OK),
+    (dict(expert_quant=2), B.MOE_ERR_INVALID_ARG),
     (dict(shared_gate=True), B.MOE_ERR_INVALID_ARG),  # gate without a shared expert
     (dict(d=60), B.MOE_ERR_UNSUPPORTED),
     (dict(h=36), B.MOE_ERR_UNSUPPORTED),
@@ -119,6 +121,21 @@ def test_entry_points_reject_bad_args_without_gpu():
     # misaligned optional output
     assert L.moe_layer_forward(cp, ctypes.byref(w), FAKE, FAKE, FAKE + 4, None, None, FAKE,
                                1 << 40, None) == B.MOE_ERR_UNSUPPORTED
+    # 4-bit routed experts: scale words required; only small-batch shapes;
+    # the standalone expert entry points take activation-dtype weights only
+    cq = _cfg(T=16, d=128, h=64, expert_quant=B.MOE_QUANT_Q4_G64)
+    wq = B.MoeWeights(FAKE, None, FAKE, FAKE, FAKE, None, None, None, None, FAKE, None, FAKE)
+    assert L.moe_layer_forward(ctypes.byref(cq), ctypes.byref(wq), FAKE, FAKE, None, None, None,
+                               FAKE, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    cq_big = _cfg(T=100, d=128, h=64, expert_quant=B.MOE_QUANT_Q4_G64)  # P = 200 > 16 * 8
+    wq2 = B.MoeWeights(FAKE, None, FAKE, FAKE, FAKE, None, None, None, None, FAKE, FAKE, FAKE)
+    assert L.moe_layer_forward(ctypes.byref(cq_big), ctypes.byref(wq2), FAKE, FAKE, None, None,
+                               None, FAKE, 1 << 40, None) == B.MOE_ERR_UNSUPPORTED
+    cq_odd = _cfg(T=16, d=96, h=64, expert_quant=B.MOE_QUANT_Q4_G64)  # d not whole groups
+    assert L.moe_layer_forward(ctypes.byref(cq_odd), ctypes.byref(wq2), FAKE, FAKE, None, None,
+                               None, FAKE, 1 << 40, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_gate_up(ctypes.byref(cq), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                         None) == B.MOE_ERR_UNSUPPORTED
     # routing statistics: required pointers, alpha range, workspace
     f32 = ctypes.c_float
     assert L.moe_routing_stats(cp, None, FAKE, f32(0.01), FAKE, FAKE, FAKE, FAKE, 1 << 30,

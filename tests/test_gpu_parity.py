@@ -150,8 +150,31 @@ def test_entry_points_small(name):
         check_out(host(fused["out_t"]), host(out).astype(np.float64), spec.dtype, "fused vs chain")
 
 
+# 4-bit routed experts (the fused layer only: the standalone expert entry
+# points take activation-dtype weights). Scale-group K tails, skewed routing
+# with several 16-row blocks per expert, a bf16 shared expert beside them,
+# and a reduction of 4096 (eight waves)
+SMALL_Q4 = {
+    "q4_small": small_spec("decode_q4", T=20, d=256, E=32, h=128, k=4),
+    "q4_group_tails": small_spec("decode_q4", T=37, d=192, E=16, h=320, k=3),
+    "q4_rowblocks": small_spec("decode_q4", T=64, d=128, E=8, h=64, k=1, router_bias="zipf",
+                               renormalize=True),
+    "q4_shared": small_spec("decode_q4", T=24, d=256, E=16, h=64, k=4, shared_h=128,
+                            shared_gate=True),
+    "q4_k4096": small_spec("decode_q4", T=8, d=4096, E=8, h=64, k=2),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_Q4))
+def test_layer_q4_small(name):
+    spec = SMALL_Q4[name]
+    say(f"[gpu] layer_forward q4 {name}: T={spec.T} d={spec.d} E={spec.E} h={spec.h} k={spec.k}")
+    full_parity(generate(spec))
+
+
 FULL = ["tiny_fp32", "gemma_upcycled", "skewed_prefill", "shared_routed",
-        "decode@T1", "decode@T4", "decode@T16", "decode@T64", "small_moe_sigmoid"]
+        "decode@T1", "decode@T4", "decode@T16", "decode@T64", "small_moe_sigmoid",
+        "decode_q4@T1", "decode_q4@T64"]
 
 _cache = {}
 
@@ -160,7 +183,7 @@ def _full_inputs(name):
     """Full-size inputs; the decode batch sizes share one draw (x rows are a
     prefix of the same 64 drawn tokens)."""
     base = name.split("@")[0]
-    key = "decode@T64" if base == "decode" else name
+    key = f"{base}@T64" if base in ("decode", "decode_q4") else name
     if key not in _cache:
         _cache.clear()
         _cache[key] = generate(spec_by_name(key))
