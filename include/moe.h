@@ -238,9 +238,9 @@ moe_status moe_routing_stats(const moe_config* cfg, const float* logits, const i
  *   that format (w_gate_sb, w_up_sb, w_down_sb required) by the small-batch
  *   expert kernels, which serve layers of at most 16 routed rows per expert
  *   on average (T * top_k <= 16 * E) with d and h multiples of 64 and at most
- *   4096, in bf16; other quantised shapes return MOE_ERR_UNSUPPORTED. The
- *   dequantised weights are rounded to bf16 (to nearest, halves away from
- *   zero) before the bf16 products. */
+ *   4096, in bf16; other quantised shapes return MOE_ERR_UNSUPPORTED. Per
+ *   scale group the kernels form s * sum x (128 + q) + (b - 128 s) * sum x
+ *   with bf16 products and float32 accumulation (128 + q is exact in bf16). */
 moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x,
                              void* out, int32_t* ids, float* gates, int32_t* counts,
                              void* ws, size_t ws_bytes, void* stream);

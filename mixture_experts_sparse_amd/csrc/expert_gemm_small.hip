@@ -178,24 +178,28 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmParams p) {
 // is: scale group G of a wave's range, half h in {0, 1}; lane group g holds
 // K values kb + 64 G + 16 g + 8 h .. + 7 (x and weights alike). A lane then
 // reads its 16 codes of a group as one 8-byte load and the group's scale and
-// bias as one 4-byte word; the codes stay packed in registers and are
-// dequantised to bf16 right before each MFMA (one FMA per weight, rounded
-// to nearest with halves away from zero).
+// bias as one 4-byte word.
+//
+// The weights are never dequantised one by one. Within a group,
+//   sum_k x_k (s q_k + b) = s sum_k x_k (128 + q_k) + (b - 128 s) sum_k x_k,
+// and 128 + q (q < 16) is an exact bf16 whose bit pattern is 0x4300 | q, so
+// the codes become MFMA operands with two integer operations per pair; each
+// group's two MFMA steps accumulate on their own, the x row sums of the group
+// come from two MFMAs against ones, and the scale and bias are applied to the
+// group's accumulator with two FMAs per output.
 // ---------------------------------------------------------------------------
 
-// w_i = s * q_i + b for the 8 codes of D (code i in nibble i), as 8 bf16.
-__device__ __forceinline__ u32x4_t dequant8(uint32_t D, float s, float b) {
+// bf16 pairs (128 + q_2j, 128 + q_2j+1), j = 0..3, of the 8 codes of D (code
+// i in nibble i), exact.
+__device__ __forceinline__ u32x4_t codes_bf16(uint32_t D) {
   const uint32_t lo = D & 0x0F0F0F0Fu;          // codes 0, 2, 4, 6 (one per byte)
   const uint32_t hi = (D >> 4) & 0x0F0F0F0Fu;   // codes 1, 3, 5, 7
   u32x4_t r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float w0 = fmaf(s, static_cast<float>((lo >> (8 * j)) & 0xFFu), b);
-    const float w1 = fmaf(s, static_cast<float>((hi >> (8 * j)) & 0xFFu), b);
-    // high halves of the rounded words: w0 in the low bf16, w1 in the high
-    r[j] = __builtin_amdgcn_perm(__float_as_uint(w1) + 0x8000u, __float_as_uint(w0) + 0x8000u,
-                                 0x07060302u);
-  }
+  // byte j of lo -> bits 0..7, byte j of hi -> bits 16..23 (selector 0x0C: zero)
+  r[0] = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u;
+  r[1] = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u;
+  r[2] = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x43004300u;
+  r[3] = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u;
   return r;
 }
 
@@ -267,22 +271,45 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_q4_kernel(GemmParams p) {
     for (int m = 0; m < NB; ++m)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[m][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+    const floatx4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int G = 0; G < KG; ++G) {
+      // one group at a time: its codes are taken (pinned) only after the
+      // previous group's accumulators are final, so the compiler forms each
+      // group's bf16 operands next to their MFMAs instead of all groups'
+      // at once (4x the registers of the packed codes, hoisted out of the
+      // row loop)
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) { pin(qc[m][t][G].x); pin(qc[m][t][G].y); }
+      const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, aq[2 * G]);
+      const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, aq[2 * G + 1]);
+      // x row sums over the group (every column of the tile holds its row's)
+      floatx4_t xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          a0, __builtin_bit_cast(bf16x8_t, ones), zero, 0, 0, 0);
+      xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8_t, ones), xs, 0,
+                                                   0, 0);
 #pragma unroll
       for (int m = 0; m < NB; ++m)
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
+          floatx4_t ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a0, __builtin_bit_cast(bf16x8_t, codes_bf16(qc[m][t][G].x)), zero, 0, 0, 0);
+          ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a1, __builtin_bit_cast(bf16x8_t, codes_bf16(qc[m][t][G].y)), ag, 0, 0, 0);
+          // this lane's column: its own scale word
           const float sc = bf16_to_f32(static_cast<uint16_t>(sb[m][t][G] & 0xFFFFu));
-          const float bi = bf16_to_f32(static_cast<uint16_t>(sb[m][t][G] >> 16));
+          const float b2 =
+              fmaf(-128.0f, sc, bf16_to_f32(static_cast<uint16_t>(sb[m][t][G] >> 16)));
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const u32x4_t w = dequant8(h == 0 ? qc[m][t][G].x : qc[m][t][G].y, sc, bi);
-            acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, aq[2 * G + h]), __builtin_bit_cast(bf16x8_t, w),
-                acc[m][t], 0, 0, 0);
-          }
+          for (int i = 0; i < 4; ++i) acc[m][t][i] = fmaf(sc, ag[i], fmaf(b2, xs[i], acc[m][t][i]));
         }
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) pin(acc[m][t]);
     }
     small_block_epilogue<KIND, NW, NB, NT>(p, red, acc, r0, rb, cnt, n0);
   }
