@@ -21,10 +21,12 @@
 //
 // The launch grid is sized from an upper bound on the tile count; the true
 // count is read on the device, so no host synchronisation is needed. Tiles
-// are numbered shared group first, then expert-major, in blocks of 4 M tiles
-// x all N tiles, and block b runs logical tile (b mod 8) * ceil(n/8) + b / 8:
+// are numbered expert-major, in blocks of 4 M tiles x all N tiles, and each
+// XCD (block b runs on XCD b mod 8) takes one contiguous eighth of them:
 // consecutive logical tiles (the M tiles that share one weight slab) land on
-// the same XCD and its L2.
+// the same XCD and its L2. The shared group, whose down-projection tiles
+// carry a longer reduction than the routed ones, is divided into eighths of
+// its own and scheduled first, so every XCD gets the same share of it.
 
 #include <utility>
 
@@ -61,6 +63,8 @@ __device__ __forceinline__ void grouped_nm(int l, int mt, int NT, int& n, int& m
 }
 
 // Decodes the logical tile of this workgroup; returns false for surplus blocks.
+// Blocks [0, 8 * ceil(nsh / 8)) run the nsh shared-group tiles, the rest the
+// routed ones; each region is split into per-XCD eighths.
 template <int BN>
 __device__ __forceinline__ bool decode_tile(const GemmParams& p, TileInfo& ti) {
   const int BM = p.tile_m;
@@ -72,16 +76,13 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, TileInfo& ti) {
     MTs = (p.shared_T + BM - 1) / BM;
     NTs = (p.sN + BN - 1) / BN;
   }
-  const int total = routed + MTs * NTs;
-  const int b = blockIdx.x;
-  const int per = (total + 7) >> 3;
-  const int j = b >> 3;
-  if (j >= per) return false;
-  int L = (b & 7) * per + j;
-  if (L >= total) return false;
+  const int nsh = MTs * NTs;
+  const int pers = (nsh + 7) >> 3;
+  int b = blockIdx.x;
   int n, m;
-  // The shared group (long K for its down projection) is scheduled first.
-  if (L < MTs * NTs) {
+  if (b < 8 * pers) {
+    const int L = (b & 7) * pers + (b >> 3);
+    if (L >= nsh) return false;
     grouped_nm(L, MTs, NTs, n, m);
     ti.e = -1;
     ti.row0 = m * BM;
@@ -89,7 +90,12 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, TileInfo& ti) {
     ti.n0 = n * BN;
     return ti.nrows > 0;
   }
-  L -= MTs * NTs;
+  b -= 8 * pers;
+  const int per = (routed + 7) >> 3;
+  const int j = b >> 3;
+  if (j >= per) return false;
+  const int L = (b & 7) * per + j;
+  if (L >= routed) return false;
   const int q = L / NT;
   const int e = p.tile_e[q];
   const int tp0 = p.exp_tile0[e];
@@ -402,7 +408,8 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
 
 struct Sched {
   int x, j, W;      // XCD, slot on the XCD, workgroups per XCD
-  int per, total;   // tiles per XCD, tiles in all
+  int per, routed;  // routed tiles per XCD, routed tiles in all
+  int sh0, nshx;    // this XCD's first shared tile and its count of them
   int NT;           // routed N tiles per M tile
   int nsh, NTs;     // shared-group tiles, shared N tiles per M tile
 };
@@ -420,11 +427,16 @@ __device__ __forceinline__ Sched make_sched(const GemmParams& p) {
     s.NTs = (p.sN + BN - 1) / BN;
     s.nsh = ((p.shared_T + BM - 1) / BM) * s.NTs;
   }
-  s.total = s.NT * ntiles + s.nsh;
-  s.per = (s.total + 7) >> 3;
+  s.routed = s.NT * ntiles;
+  s.per = (s.routed + 7) >> 3;
   s.x = blockIdx.x & 7;
   s.j = blockIdx.x >> 3;
   s.W = gridDim.x >> 3;
+  // XCD x walks its eighth of the shared group, then its eighth of the
+  // routed tiles
+  const int pers = (s.nsh + 7) >> 3;
+  s.sh0 = s.x * pers;
+  s.nshx = min(max(s.nsh - s.sh0, 0), pers);
   return s;
 }
 
@@ -433,20 +445,20 @@ __device__ __forceinline__ Sched make_sched(const GemmParams& p) {
 template <int BN>
 __device__ __forceinline__ bool tile_at(const GemmParams& p, const Sched& s, int i, TileInfo& ti) {
   const int jj = s.j + i * s.W;
-  if (jj >= s.per) return false;
-  int L = s.x * s.per + jj;
-  if (L >= s.total) return false;
   const int BM = p.tile_m;
   int n, m;
-  if (L < s.nsh) {
-    grouped_nm(L, s.nsh / s.NTs, s.NTs, n, m);
+  if (jj < s.nshx) {
+    grouped_nm(s.sh0 + jj, s.nsh / s.NTs, s.NTs, n, m);
     ti.e = -1;
     ti.row0 = m * BM;
     ti.nrows = min(BM, p.shared_T - ti.row0);
     ti.n0 = n * BN;
     return true;
   }
-  L -= s.nsh;
+  const int jr = jj - s.nshx;
+  if (jr >= s.per) return false;
+  const int L = s.x * s.per + jr;
+  if (L >= s.routed) return false;
   const int q = L / s.NT;
   const int e = min(max(ldc(p.tile_e, q), 0), p.E - 1);
   const int tp0 = ldc(p.exp_tile0, e);
@@ -825,9 +837,10 @@ static hipError_t launch_pers(const GemmParams& p, hipStream_t s) {
 template <class Sh>
 static hipError_t launch_shape(const GemmParams& p, hipStream_t s) {
   if (p.tile_m != Sh::BM) return hipErrorInvalidValue;
-  long long nblk = static_cast<long long>(ceil_div(p.N, Sh::BN)) * p.max_mtiles;
-  if (p.shared_T > 0) nblk += static_cast<long long>(ceil_div(p.shared_T, Sh::BM)) * ceil_div(p.sN, Sh::BN);
-  nblk = (nblk + 7) / 8 * 8;
+  // the shared and routed regions each take a multiple of 8 blocks
+  long long nblk = (static_cast<long long>(ceil_div(p.N, Sh::BN)) * p.max_mtiles + 7) / 8 * 8;
+  if (p.shared_T > 0)
+    nblk += (static_cast<long long>(ceil_div(p.shared_T, Sh::BM)) * ceil_div(p.sN, Sh::BN) + 7) / 8 * 8;
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
   Sh::launch(p, static_cast<unsigned>(nblk), s);
