@@ -12,11 +12,11 @@
 
 namespace moe {
 
-// Slots are taken in batches of CKB: a batch's inv words and gates are
-// loaded together, then its y rows together, then added in slot order, so a
-// thread waits on two load latencies per batch rather than two per slot.
-constexpr int CKB = 8;
-
+// Slots are taken in batches of CKB (4 for top_k <= 4, else 8): a batch's
+// inv words and gates are loaded together, then its y rows together, then
+// added in slot order, so a thread waits on two load latencies per batch
+// rather than two per slot.
+template <int CKB>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineParams p) {
   const int cpr = p.d >> 3;  // 8-element chunks per row
   const long long item = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
@@ -81,6 +81,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineParams p) {
   *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.out) + static_cast<size_t>(t) * p.d + c) = o;
 }
 
+template <int CKB>
 __global__ __launch_bounds__(256) void combine_f32_kernel(CombineParams p) {
   const int cpr = p.d >> 2;  // 4-element chunks per row
   const long long item = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
@@ -167,8 +168,14 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
   const long long items = static_cast<long long>(p.T) * (p.d / per);
   const long long nblk = (items + 255) / 256;
   if (nblk <= 0) return hipSuccess;
-  if (p.dtype == MOE_BF16) combine_bf16_kernel<<<static_cast<unsigned>(nblk), 256, 0, s>>>(p);
-  else combine_f32_kernel<<<static_cast<unsigned>(nblk), 256, 0, s>>>(p);
+  const unsigned g = static_cast<unsigned>(nblk);
+  if (p.dtype == MOE_BF16) {
+    if (p.k <= 4) combine_bf16_kernel<4><<<g, 256, 0, s>>>(p);
+    else combine_bf16_kernel<8><<<g, 256, 0, s>>>(p);
+  } else {
+    if (p.k <= 4) combine_f32_kernel<4><<<g, 256, 0, s>>>(p);
+    else combine_f32_kernel<8><<<g, 256, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 
