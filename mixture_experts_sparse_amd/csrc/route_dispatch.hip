@@ -158,7 +158,6 @@ __device__ void write_touched(F cnt, G first, int E, int* flag, int* pos, int32_
 // ---------------------------------------------------------------------------
 constexpr int RTHR = 512;
 constexpr int RNW = RTHR / kWave;
-constexpr int RBK = 32;
 
 template <int NCH, int RT>
 struct RouteCfg {
@@ -169,12 +168,21 @@ struct RouteCfg {
   static constexpr int NCG = RNW / NTG;          // column groups (waves along columns)
   static constexpr int NH = NC / NCG;            // columns per wave
   static constexpr int NF2 = NH / 16;            // fragments per wave
+  // K slice depth: 64 (128-byte row segments, which stream out of L2 at
+  // about 1.6x the rate of 64-byte ones) wherever the two rings fit in LDS
+  static constexpr int RBK = (NCH == 5 && RT == 64) ? 32 : 64;
+  static constexpr int CPR = RBK / 8;            // 16-byte chunks per LDS row
+  static constexpr int KS = RBK / 32;            // MFMA steps per slice
   static constexpr int SX = RT * RBK;            // x elements per slice
   static constexpr int SW = NC * RBK;            // router elements per slice
-  static constexpr int RR = NCH <= 4 ? 4 : 3;    // router ring slots
-  static constexpr int RX = 16;                  // x ring slots
-  static constexpr int XW = SX / 8 / 64;         // x-stream waves (one 16-byte load per lane)
-  static constexpr int LW = SW / 8 / 256;        // router loads per router-wave thread per slice
+  static constexpr int RR = RBK == 64 ? 3 : (NCH <= 4 ? 4 : 3);  // router ring slots
+  static constexpr int RX = RBK == 64 ? (RT == 64 ? 6 : 8) : 16;  // x ring slots
+  static constexpr int XCH = RT * CPR;           // x chunks per slice
+  static constexpr int LX = XCH <= 256 ? 1 : XCH / 256;  // x loads per x-wave lane per slice
+  static constexpr int XW = XCH <= 256 ? XCH / 64 : 4;    // x-stream waves
+  static constexpr int LW = NC * CPR / 256;      // router loads per router-wave thread per slice
+  static_assert(XW * 64 * LX == XCH && LW * 256 == NC * CPR, "whole loads per slice");
+  static_assert((RR - 2) * LW < 64 && (RX - 2) * LX < 64, "vmcnt range");
   static constexpr int LGLD = NC + 4;            // logit row stride in LDS (floats)
   // LDS after the logits: selections, per-wave histograms, running counts
   static constexpr int CARVE = RT * kMaxE + RNW * kMaxE * 4 + 3 * (kMaxE + 1) * 4;
@@ -200,7 +208,7 @@ __device__ void route_logits_bf16(const RouteParams& p, int t0, floatx4_t* acc, 
                                   uint16_t* Wr) {
   using C = RouteCfg<NCH, RT>;
   constexpr int RX = C::RX, RR = C::RR, LW = C::LW, NF2 = C::NF2, NTG = C::NTG;
-  constexpr int LX = 1;
+  constexpr int LX = C::LX, RBK = C::RBK, CPR = C::CPR, KS = C::KS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool xw = wave < C::XW;              // x-stream waves
@@ -212,16 +220,16 @@ __device__ void route_logits_bf16(const RouteParams& p, int t0, floatx4_t* acc, 
   const uint16_t* WS = static_cast<const uint16_t*>(p.w_sgate);
   const int d = p.d;
   constexpr int LM = LX > LW ? LX : LW;
-  // load i of a stream thread fills slot chunk q = i * 256 + lt: row q / 4,
-  // physical chunk q % 4 (the swizzle picks the logical K chunk); waves that
-  // stream nothing keep a valid address they never use
+  // load i of a stream thread fills slot chunk q = i * 256 + lt: row
+  // q / CPR, physical chunk q % CPR (the swizzle picks the logical K chunk);
+  // waves that stream nothing keep a valid address they never use
   const uint16_t* src[LM];
   int chunk[LM];
 #pragma unroll
   for (int i = 0; i < LM; ++i) {
     const int q = i * 256 + lt;
-    const int r = q >> 2;
-    chunk[i] = swz_phys_to_logical<RBK>(r, q & 3) * 8;
+    const int r = q / CPR;
+    chunk[i] = swz_phys_to_logical<RBK>(r, q % CPR) * 8;
     if (xw) {
       src[i] = X + static_cast<size_t>(t0 + r < p.T ? t0 + r : t0) * d;
     } else {
@@ -243,8 +251,12 @@ __device__ void route_logits_bf16(const RouteParams& p, int t0, floatx4_t* acc, 
                                        lds_untracked(slot + (i * 256 + lwb) * 8), 16, 0, 0);
   };
   const int fr = lane & 15, fq = lane >> 4;
-  const int aoff = swz<RBK>((wave % NTG) * 16 + fr, fq);
-  const int boff = swz<RBK>((wave / NTG) * C::NH + fr, fq);  // + f * 16 rows
+  int aoff[KS], boff[KS];  // MFMA step j reads logical chunk 4 j + fq
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    aoff[j] = swz<RBK>((wave % NTG) * 16 + fr, 4 * j + fq);
+    boff[j] = swz<RBK>((wave / NTG) * C::NH + fr, 4 * j + fq);  // + f * 16 rows
+  }
 #pragma unroll
   for (int f = 0; f < NF2; ++f) acc[f] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   if (xw) {
@@ -280,12 +292,16 @@ __device__ void route_logits_bf16(const RouteParams& p, int t0, floatx4_t* acc, 
       wait_stage<63>();
       stage_barrier();
     }
-    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + aoff));
 #pragma unroll
-    for (int f = 0; f < NF2; ++f) {
-      const bf16x8_t b = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const u32x4_t*>(ws + boff + f * 16 * RBK));
-      acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[f], 0, 0, 0);
+    for (int j = 0; j < KS; ++j) {
+      const bf16x8_t a =
+          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + aoff[j]));
+#pragma unroll
+      for (int f = 0; f < NF2; ++f) {
+        const bf16x8_t b = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(ws + boff[j] + f * 16 * RBK));
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[f], 0, 0, 0);
+      }
     }
     cx = cx + 1 == RX ? 0 : cx + 1;
     cw = cw + 1 == RR ? 0 : cw + 1;
@@ -381,6 +397,29 @@ __device__ __forceinline__ uint64_t row16_max(uint64_t a) {
   a = dpp_max<0x140>(a);  // row_mirror
   return a;
 }
+// Largest of a lane's NF keys by a pairwise tree (depth log2 NF instead of
+// a chain of NF - 1 dependent steps).
+template <int NF>
+__device__ __forceinline__ uint64_t max_keys(const uint64_t* key) {
+  uint64_t t[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) t[f] = key[f];
+#pragma unroll
+  for (int w = 1; w < NF; w *= 2)
+#pragma unroll
+    for (int f = 0; f + w < NF; f += 2 * w) t[f] = t[f + w] > t[f] ? t[f + w] : t[f];
+  return t[0];
+}
+// Drops the winner (expert idx) from further rounds: lane c holds expert
+// f * 16 + c in key[f]. Only the value word is cleared; a cleared key still
+// beats the all-zero keys of columns past E, but never a live key (whose
+// value word is at least 1), and at most k <= E keys are ever taken.
+template <int NF>
+__device__ __forceinline__ void drop_key(uint64_t* key, int idx, int c) {
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+    if (idx == f * 16 + c) key[f] &= 0xFFFFFFFFull;
+}
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float a) {
   return a + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), CTRL, 0xF, 0xF, false));
@@ -439,25 +478,25 @@ __device__ void route_select(const RouteParams& p, int t0, const float* Lg, cons
     const int t = t0 + r;
     const bool live = t < p.T;                          // uniform across the 16-lane group
     const float* row = Lg + r * C::LGLD;
+    // every column of the padded row is readable and finite: all reads go
+    // out together, columns past E are masked afterwards
     float v[NF];
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int e = f * 16 + c;
-      float val = -INFINITY;
-      if (e < E) {
-        if (sig) {
-          // sigmoid scoring: the bias steers the choice only; the logits
-          // output stays bias-free
-          val = sigmoid_f32(row[e]) + bias[f];
-          if (live && p.logits != nullptr) p.logits[static_cast<size_t>(t) * E + e] = row[e];
-        } else {
-          val = row[e] + bias[f];
-          if (live && p.logits != nullptr) p.logits[static_cast<size_t>(t) * E + e] = val;
-        }
-      }
-      v[f] = val + 0.0f;  // -0 -> +0: equal scores must get equal keys
+    for (int f = 0; f < NF; ++f) v[f] = row[f * 16 + c];
+    if (live && p.logits != nullptr) {
+      // sigmoid scoring keeps the logits output bias-free
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        if (f * 16 + c < E)
+          p.logits[static_cast<size_t>(t) * E + f * 16 + c] = sig ? v[f] : v[f] + bias[f];
     }
     if (live && p.sgate != nullptr && c == 0) p.sgate[t] = sigmoid_f32(row[E]);
+    // the score that selects: the bias steers the choice only
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const float val = (sig ? sigmoid_f32(v[f]) : v[f]) + bias[f];
+      v[f] = f * 16 + c < E ? val + 0.0f : -INFINITY;  // -0 -> +0: equal scores, equal keys
+    }
     uint64_t key[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) key[f] = f * 16 + c < E ? sel_key(v[f], f * 16 + c) : 0ull;
@@ -466,13 +505,8 @@ __device__ void route_select(const RouteParams& p, int t0, const float* Lg, cons
     if (k <= 16) {
       uint64_t mine = 0ull;  // lane c: slot c's key
       for (int j = 0; j < k; ++j) {
-        uint64_t b = key[0];
-#pragma unroll
-        for (int f = 1; f < NF; ++f) b = key[f] > b ? key[f] : b;
-        b = row16_max(b);
-        // keys are unique (they carry the index): the winner's entry drops out
-#pragma unroll
-        for (int f = 0; f < NF; ++f) key[f] = key[f] == b ? 0ull : key[f];
+        const uint64_t b = row16_max(max_keys<NF>(key));
+        drop_key<NF>(key, key_index(b), c);
         mine = j == c ? b : mine;
       }
       const float m = __shfl(key_value(mine), lane & 48, kWave);  // slot 0: the largest logit
@@ -499,12 +533,8 @@ __device__ void route_select(const RouteParams& p, int t0, const float* Lg, cons
       // k > 16: each slot's id and un-normalised gate are stored as it is found
       float m = 0.f, ssel = 0.f;
       for (int j = 0; j < k; ++j) {
-        uint64_t b = key[0];
-#pragma unroll
-        for (int f = 1; f < NF; ++f) b = key[f] > b ? key[f] : b;
-        b = row16_max(b);
-#pragma unroll
-        for (int f = 0; f < NF; ++f) key[f] = key[f] == b ? 0ull : key[f];
+        const uint64_t b = row16_max(max_keys<NF>(key));
+        drop_key<NF>(key, key_index(b), c);
         const float bv = key_value(b);
         const int bi = key_index(b);
         if (j == 0) m = bv;  // the largest logit
@@ -570,13 +600,15 @@ __device__ void route_select_rank(const RouteParams& p, int t0, float* Lg, const
       const int t = t0 + r;
       float* row = Lg + r * C::LGLD;
       if (p.sgate != nullptr && c == 0) p.sgate[t] = sigmoid_f32(row[E]);
+      float val[NF];  // the padded row is readable: all reads go out together
+#pragma unroll
+      for (int f = 0; f < NF; ++f) val[f] = row[f * 16 + c] + bias[f];
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const int e = f * 16 + c;
         if (e < E) {
-          const float val = row[e] + bias[f];
-          if (p.logits != nullptr) p.logits[static_cast<size_t>(t) * E + e] = val;
-          K32[r * C::LGLD + e] = order_key32(val + 0.0f);  // -0 -> +0
+          if (p.logits != nullptr) p.logits[static_cast<size_t>(t) * E + e] = val[f];
+          K32[r * C::LGLD + e] = order_key32(val[f] + 0.0f);  // -0 -> +0
         }
       }
     }
