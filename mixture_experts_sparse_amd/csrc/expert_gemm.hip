@@ -360,8 +360,11 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
   constexpr int WLD = WC + 8;
   constexpr int LPR = WC / 8;      // lanes per output row
   constexpr int NPASS = (16 * LPR + 63) / 64;
-  static_assert(NWM * NWN * 16 * WLD <= SEL, "epilogue slices must fit in one stage buffer");
-  uint16_t* Cw = L0 + wave * 16 * WLD;
+  // the waves' slices fill one stage buffer, or the first two
+  constexpr bool SPLIT = NWM * NWN * 16 * WLD > SEL;
+  constexpr int NWH = SPLIT ? NWM * NWN / 2 : NWM * NWN;
+  static_assert(NWH * 16 * WLD <= SEL, "epilogue slices must fit in two stage buffers");
+  uint16_t* Cw = (SPLIT && wave >= NWH ? L1 : L0) + (wave % NWH) * 16 * WLD;
   const int c0 = ti.n0 + wn * WC;  // first output column of this wave
 #pragma unroll
   for (int mf = 0; mf < 4; ++mf) {
@@ -852,8 +855,8 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     // 256-row tiles (prefill-sized experts): 4 x 2 waves, 64-deep K slices
     // (128-byte row segments: twice the L2->LDS rate of 64-byte ones).
     if (p.tile_m == 256) {
-      if (p.kind == 0) return launch_shape<GemmShape<0, 4, 2, 4, 3, 64>>(p, s);
-      return launch_shape<GemmShape<1, 4, 2, 4, 3, 64>>(p, s);
+      if (p.kind == 0) return launch_shape<GemmShape<0, 4, 2, 8, 2, 64>>(p, s);
+      return launch_shape<GemmShape<1, 4, 2, 8, 2, 64>>(p, s);
     }
     if (p.tile_m != 128) return hipErrorInvalidValue;
     // gate/up with at least 32 rows per expert on average: 2 x 4 waves over
