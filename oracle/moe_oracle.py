@@ -53,6 +53,18 @@ with a bf16 scale s and bias b, w = s * q + b for the 4-bit code q in
 [0, 15]; two codes per byte, the even position in the low nibble. The
 oracle dequantises exactly (float64) and runs the same layer.
 
+Backward (``layer_backward``): the gradients of the scalar sum(out * dO)
+for an upstream gradient dO, as a training step takes them ("Small models,
+sparse experts", section "Tuning the training loop": the whole step,
+forward, backward and optimiser, is compiled together, and activations are
+recomputed in the backward pass rather than stored). The pages print no
+backward formula; this is the derivative of steps 1-7 with the selection
+held fixed (top-k is piecewise constant in the logits): through the gates
+into the router logits and weights, through each expert's SwiGLU into its
+weights and the token rows, and through the shared expert and its gate. The
+router bias and the balance bias are constants (no gradient is returned for
+them).
+
 Routing statistics (``routing_stats``): the per-expert token share, the mean
 router probability per expert, the mean router entropy and the Switch
 load-balance term alpha * N * sum_e f_e P_e ("Mixture-of-Experts -- more
@@ -448,3 +460,120 @@ def token_forward(inp, tokens, ids, gates):
             o += s
         rows.append(o)
     return np.stack(rows) if rows else np.zeros((0, X.shape[1]))
+
+
+# ----------------------------------------------------------------------------
+# backward: the derivative of steps 1-7 with the selection held fixed
+# ----------------------------------------------------------------------------
+
+def silu_grad(z):
+    """d silu / dz = sigmoid(z) (1 + z (1 - sigmoid(z)))."""
+    s = sigmoid(z)
+    return s * (1.0 + z * (1.0 - s))
+
+
+def gate_logit_grad(L, ids, g, dG, mode, renormalize):
+    """dL [T, E] from the gate gradient dG [T, k] (step 3 differentiated).
+
+    SOFTMAX_ALL without renormalisation: g_j = p[ids_j] with p = softmax(L),
+    so dL_i = p_i (v_i - sum_j dG_j g_j) where v_i sums dG_j over the slots
+    that chose i. Renormalised, and SOFTMAX_SELECTED, the gates are the
+    softmax of the k selected logits: dL[ids_m] = g_m (dG_m - sum_j dG_j g_j),
+    zero elsewhere. SIGMOID: s = sigmoid(L); the gates are s[ids] (divided by
+    their sum when renormalised), and ds/dL = s (1 - s).
+    """
+    T, E = L.shape
+    k = ids.shape[1]
+    dL = np.zeros((T, E))
+    rows = np.arange(T)[:, None]
+    inner = np.sum(dG * g, axis=1, keepdims=True)       # sum_j dG_j g_j
+    if mode == SOFTMAX_ALL and not renormalize:
+        p = softmax(L, axis=1)
+        v = np.zeros((T, E))
+        np.add.at(v, (np.repeat(np.arange(T), k), ids.reshape(-1)), dG.reshape(-1))
+        return p * (v - inner)
+    if mode in (SOFTMAX_ALL, SOFTMAX_SELECTED):
+        np.add.at(dL, (np.broadcast_to(rows, ids.shape), ids), g * (dG - inner))
+        return dL
+    if mode == SIGMOID:
+        s = sigmoid(np.take_along_axis(L, ids, axis=1))
+        if renormalize:
+            ds = (dG - inner) / np.sum(s, axis=1, keepdims=True)
+        else:
+            ds = dG
+        np.add.at(dL, (np.broadcast_to(rows, ids.shape), ids), ds * s * (1.0 - s))
+        return dL
+    raise ValueError(f"unknown gate mode {mode}")
+
+
+def swiglu_backward(X, Wg, Wu, Wd, dY):
+    """Gradients of sum(SwiGLU(X) * dY) for one expert on its rows X:
+    returns (dX, dWg, dWu, dWd). z_g = X Wg^T, z_u = X Wu^T,
+    a = silu(z_g) z_u, Y = a Wd^T."""
+    zg = X @ Wg.T
+    zu = X @ Wu.T
+    a = silu(zg) * zu
+    dWd = dY.T @ a
+    da = dY @ Wd
+    dzg = da * zu * silu_grad(zg)
+    dzu = da * silu(zg)
+    return dzg @ Wg + dzu @ Wu, dzg.T @ X, dzu.T @ X, dWd
+
+
+def layer_backward(inp, dout, ids_override=None):
+    """Gradients of sum(out * dout) for the layer of ``layer_forward``.
+
+    Returns a dict of float64 arrays: dx [T, d], dw_router [E, d],
+    dw_gate / dw_up [E, h, d], dw_down [E, d, h] (zero for experts no token
+    chose), the gate and logit gradients dgates [T, k] and dlogits [T, E],
+    and, with a shared expert, dws_gate / dws_up [hs, d], dws_down [d, hs]
+    and dw_shared_gate [d] (None when ungated). Quantised experts are not
+    differentiated (their weights are not parameters here)."""
+    spec = inp["spec"]
+    if getattr(spec, "expert_quant", None):
+        raise ValueError("backward of quantised experts is not defined")
+    E, k, mode, renorm = _spec_fields(spec)
+    fwd = layer_forward(inp, ids_override)
+    X = to_f64(inp["x"])
+    dO = to_f64(dout)
+    T, d = X.shape
+    ids, g, perm, offsets = fwd["ids"], fwd["gates"], fwd["perm"], fwd["offsets"]
+    Wg, Wu, Wd = expert_weights(inp)
+    h = Wg.shape[1]
+    dX = np.zeros((T, d))
+    dWg = np.zeros((E, h, d))
+    dWu = np.zeros((E, h, d))
+    dWd = np.zeros((E, d, h))
+    dG = np.zeros((T, k))
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r0 == r1:
+            continue
+        pairs = perm[r0:r1]
+        toks, slots = pairs // k, pairs % k
+        Xe = X[toks]
+        ye = swiglu(Xe, Wg[e], Wu[e], Wd[e])                 # un-gated expert rows
+        dG[toks, slots] = np.sum(dO[toks] * ye, axis=1)
+        dXe, dWg[e], dWu[e], dWd[e] = swiglu_backward(Xe, Wg[e], Wu[e], Wd[e],
+                                                      g[toks, slots][:, None] * dO[toks])
+        np.add.at(dX, toks, dXe)
+    dL = gate_logit_grad(fwd["logits"], ids, g, dG, mode, renorm)
+    Wr = to_f64(inp["w_router"])
+    dX += dL @ Wr
+    res = {"dx": dX, "dw_router": dL.T @ X, "dw_gate": dWg, "dw_up": dWu, "dw_down": dWd,
+           "dgates": dG, "dlogits": dL, "ids": ids, "gates": g,
+           "dws_gate": None, "dws_up": None, "dws_down": None, "dw_shared_gate": None}
+    if inp.get("ws_gate") is not None:
+        Sg, Su, Sd = (to_f64(inp[n]) for n in ("ws_gate", "ws_up", "ws_down"))
+        dOs = dO
+        if inp.get("w_shared_gate") is not None:
+            ws = to_f64(inp["w_shared_gate"])
+            c = sigmoid(X @ ws)
+            f = swiglu(X, Sg, Su, Sd)
+            dpre = np.sum(dO * f, axis=1) * c * (1.0 - c)
+            res["dw_shared_gate"] = X.T @ dpre
+            dX += dpre[:, None] * ws[None, :]
+            dOs = c[:, None] * dO
+        dXs, res["dws_gate"], res["dws_up"], res["dws_down"] = swiglu_backward(X, Sg, Su, Sd, dOs)
+        dX += dXs
+    return res

@@ -574,6 +574,166 @@ def check_q4_bytes_per_weight():
     assert per == 0.5625 and abs(per - 0.5) < 0.1
 
 
+# ---------------------------------------------------------------------------
+# backward: pinned by automatic differentiation of the dense formulation and
+# by finite differences of the forward
+# ---------------------------------------------------------------------------
+
+def _dense_mask_torch(tensors, spec, mask, has_bias_in_logits, sel_bias):
+    """The dense all-experts forward of ``dense_mask_forward`` written in torch
+    (float64) so autograd can differentiate it; the 0/1 selection mask is an
+    input (top-k is piecewise constant)."""
+    import torch
+    X, Wr, Wg, Wu, Wd = (tensors[n] for n in ("x", "w_router", "w_gate", "w_up", "w_down"))
+    L = X @ Wr.T
+    if spec.mode == O.SIGMOID:
+        aff = torch.sigmoid(L)
+        G = aff * mask
+        if spec.renormalize:
+            G = G / G.sum(dim=1, keepdim=True)
+    else:
+        if has_bias_in_logits is not None:
+            L = L + has_bias_in_logits[None, :]
+        if spec.mode == O.SOFTMAX_ALL:
+            G = torch.softmax(L, dim=1) * mask
+            if spec.renormalize:
+                G = G / G.sum(dim=1, keepdim=True)
+        else:
+            z = torch.exp(L - L.max(dim=1, keepdim=True).values) * mask
+            G = z / z.sum(dim=1, keepdim=True)
+    out = torch.zeros_like(X)
+    for e in range(Wg.shape[0]):
+        a = X @ Wg[e].T
+        ye = (torch.nn.functional.silu(a) * (X @ Wu[e].T)) @ Wd[e].T
+        out = out + G[:, e:e + 1] * ye
+    if "ws_gate" in tensors:
+        a = X @ tensors["ws_gate"].T
+        sh = (torch.nn.functional.silu(a) * (X @ tensors["ws_up"].T)) @ tensors["ws_down"].T
+        if "w_shared_gate" in tensors:
+            sh = sh * torch.sigmoid(X @ tensors["w_shared_gate"])[:, None]
+        out = out + sh
+    return out
+
+
+def _autograd_grads(inp, dO):
+    import torch
+    spec = inp["spec"]
+    names = ["x", "w_router", "w_gate", "w_up", "w_down"]
+    if inp.get("ws_gate") is not None:
+        names += ["ws_gate", "ws_up", "ws_down"]
+        if inp.get("w_shared_gate") is not None:
+            names.append("w_shared_gate")
+    tensors = {n: torch.tensor(inp[n].astype(np.float64), requires_grad=True) for n in names}
+    # the selection, from this file's own rank-count top-k on float64 scores
+    X = inp["x"].astype(np.float64)
+    Lnp = X @ inp["w_router"].astype(np.float64).T
+    b = inp.get("b_router")
+    if spec.mode == O.SIGMOID:
+        sel = 1.0 / (1.0 + np.exp(-Lnp)) + (b.astype(np.float64)[None, :] if b is not None else 0.0)
+    else:
+        sel = Lnp + (b.astype(np.float64)[None, :] if b is not None else 0.0)
+    mask = np.zeros_like(Lnp)
+    for t in range(Lnp.shape[0]):
+        mask[t, _rank_count_topk(sel[t], spec.k)] = 1.0
+    bias_t = torch.tensor(b.astype(np.float64)) if (b is not None and spec.mode != O.SIGMOID) else None
+    out = _dense_mask_torch(tensors, spec, torch.tensor(mask), bias_t, None)
+    (out * torch.tensor(dO)).sum().backward()
+    return {n: tensors[n].grad.numpy() for n in names}
+
+
+_GRAD_KEYS = {"x": "dx", "w_router": "dw_router", "w_gate": "dw_gate", "w_up": "dw_up",
+              "w_down": "dw_down", "ws_gate": "dws_gate", "ws_up": "dws_up",
+              "ws_down": "dws_down", "w_shared_gate": "dw_shared_gate"}
+
+
+def check_backward_autograd_dense():
+    """The oracle's sparse backward equals torch autograd (float64) through
+    the dense run-every-expert-then-mask forward, in every gate mode, with a
+    logit bias, a balance bias and a gated or ungated shared expert."""
+    cases = [
+        dict(T=9, d=8, E=5, h=6, k=2, mode=O.SOFTMAX_ALL, renorm=False),
+        dict(T=9, d=8, E=5, h=6, k=2, mode=O.SOFTMAX_ALL, renorm=True, bias=True),
+        dict(T=9, d=8, E=5, h=6, k=3, mode=O.SOFTMAX_SELECTED, renorm=False),
+        dict(T=7, d=6, E=6, h=4, k=2, mode=O.SIGMOID, renorm=True, bias=True),
+        dict(T=7, d=6, E=6, h=4, k=2, mode=O.SIGMOID, renorm=False),
+        dict(T=8, d=8, E=4, h=5, k=2, mode=O.SOFTMAX_ALL, renorm=False, shared_h=7, gated=True),
+        dict(T=8, d=8, E=4, h=5, k=1, mode=O.SOFTMAX_SELECTED, renorm=False, shared_h=3),
+        dict(T=6, d=5, E=3, h=4, k=3, mode=O.SOFTMAX_ALL, renorm=False),  # k = E
+    ]
+    for i, c in enumerate(cases):
+        inp = _inputs(c["T"], c["d"], c["E"], c["h"], c["k"], c["mode"], c["renorm"], seed=40 + i,
+                      shared_h=c.get("shared_h", 0), gated=c.get("gated", False),
+                      bias=c.get("bias", False))
+        dO = _rng(90 + i).standard_normal((c["T"], c["d"]))
+        ref = _autograd_grads(inp, dO)
+        got = O.layer_backward(inp, dO)
+        for n, g in ref.items():
+            o = got[_GRAD_KEYS[n]]
+            assert o is not None and o.shape == g.shape, (i, n)
+            err = np.max(np.abs(o - g))
+            assert err <= 1e-10 * max(1.0, np.max(np.abs(g))), (i, n, err)
+
+
+def check_backward_finite_differences():
+    """Central differences of sum(out * dO) through the oracle's own forward
+    (float64 inputs) match the oracle's backward entry by entry."""
+    inp = _inputs(7, 6, 4, 5, 2, O.SOFTMAX_ALL, True, seed=61, shared_h=4, gated=True)
+    for n in ("x", "w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down",
+              "w_shared_gate"):
+        inp[n] = inp[n].astype(np.float64)
+    dO = _rng(62).standard_normal((7, 6))
+    got = O.layer_backward(inp, dO)
+    base_ids = got["ids"]
+    r = _rng(63)
+    step = 1e-6
+    for n in ("x", "w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down",
+              "w_shared_gate"):
+        a = inp[n]
+        for _ in range(4):
+            idx = tuple(int(r.integers(0, s)) for s in a.shape)
+            keep = a[idx]
+            vals = []
+            for sgn in (1.0, -1.0):
+                a[idx] = keep + sgn * step
+                f = O.layer_forward(inp)
+                assert np.array_equal(f["ids"], base_ids)  # the selection must not move
+                vals.append(np.sum(f["out"] * dO))
+            a[idx] = keep
+            fd = (vals[0] - vals[1]) / (2 * step)
+            an = got[_GRAD_KEYS[n]][idx]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (n, idx, fd, an)
+
+
+def check_backward_softmax_logit_grads_sum_to_zero():
+    """Adding one constant to all of a token's logits leaves softmax gates
+    unchanged, so each row of dL sums to zero in both softmax modes; in the
+    sigmoid mode without renormalisation dL vanishes outside the selection."""
+    for mode, renorm in ((O.SOFTMAX_ALL, False), (O.SOFTMAX_ALL, True), (O.SOFTMAX_SELECTED, False)):
+        inp = _inputs(10, 6, 5, 4, 2, mode, renorm, seed=71)
+        dO = _rng(72).standard_normal((10, 6))
+        dL = O.layer_backward(inp, dO)["dlogits"]
+        assert np.max(np.abs(dL.sum(axis=1))) <= 1e-12 * max(1.0, np.max(np.abs(dL)))
+        assert np.max(np.abs(dL)) > 1e-6
+    inp = _inputs(10, 6, 5, 4, 2, O.SIGMOID, False, seed=73)
+    res = O.layer_backward(inp, _rng(74).standard_normal((10, 6)))
+    off = np.ones_like(res["dlogits"], dtype=bool)
+    np.put_along_axis(off, res["ids"], False, axis=1)
+    assert np.all(res["dlogits"][off] == 0.0)
+
+
+def check_backward_untouched_experts_have_zero_grads():
+    """An expert no token chose gets exactly zero weight gradients."""
+    inp = _inputs(6, 6, 6, 4, 1, O.SOFTMAX_ALL, False, seed=81)
+    inp["b_router"] = np.array([0, 0, 0, -40, -40, -40], dtype=np.float32)
+    from moe_inputs.spec import MoESpec, F32
+    inp["spec"] = MoESpec(name="pin", T=6, d=6, E=6, h=4, k=1, dtype=F32, mode=O.SOFTMAX_ALL,
+                          renormalize=False, router_bias="zipf")
+    res = O.layer_backward(inp, _rng(82).standard_normal((6, 6)))
+    assert set(np.unique(res["ids"])) <= {0, 1, 2}
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        assert np.all(res[n][3:] == 0.0) and np.max(np.abs(res[n][:3])) > 0
+
+
 ALL_CHECKS = [
     check_worked_example,
     check_brute_force_topk,
@@ -596,4 +756,8 @@ ALL_CHECKS = [
     check_q4_roundtrip_error_bound,
     check_q4_known_codes,
     check_q4_bytes_per_weight,
+    check_backward_autograd_dense,
+    check_backward_finite_differences,
+    check_backward_softmax_logit_grads_sum_to_zero,
+    check_backward_untouched_experts_have_zero_grads,
 ]

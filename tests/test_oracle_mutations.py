@@ -1,6 +1,7 @@
 """Plant plausible mistakes in the oracle (on the CPU) and check that at
 least one pin fails for each. This shows the pins constrain every step:
-selection, gating, dispatch, expert FFN, combine, shared expert, bias."""
+selection, gating, dispatch, expert FFN, combine, shared expert, bias, and
+the backward (SwiGLU derivative, gate-to-logit derivative, weight grads)."""
 
 import numpy as np
 import pytest
@@ -132,10 +133,38 @@ def _q4_group_of_32(packed, sb):
     return _ORIG["dequantize_q4"](packed, half)
 
 
+def _silu_grad_no_curvature(z):
+    # d silu / dz taken as sigmoid(z) alone
+    return O.sigmoid(z)
+
+
+def _logit_grad_sign(L, ids, g, dG, mode, renormalize):
+    return -_ORIG["gate_logit_grad"](L, ids, g, dG, mode, renormalize)
+
+
+def _logit_grad_renorm_ignored(L, ids, g, dG, mode, renormalize):
+    return _ORIG["gate_logit_grad"](L, ids, g, dG, mode, False)
+
+
+def _swiglu_bwd_up_uses_z(X, Wg, Wu, Wd, dY):
+    # the up-projection gradient scaled by z_g instead of silu(z_g)
+    zg, zu = X @ Wg.T, X @ Wu.T
+    a = O.silu(zg) * zu
+    da = dY @ Wd
+    dzg = da * zu * O.silu_grad(zg)
+    dzu = da * zg
+    return dzg @ Wg + dzu @ Wu, dzg.T @ X, dzu.T @ X, dY.T @ a
+
+
+def _swiglu_bwd_down_from_preactivation(X, Wg, Wu, Wd, dY):
+    dX, dWg, dWu, _ = _ORIG["swiglu_backward"](X, Wg, Wu, Wd, dY)
+    return dX, dWg, dWu, dY.T @ (X @ Wu.T)
+
+
 _ORIG = {n: getattr(O, n) for n in ("gate_weights", "dispatch", "combine", "gate_up",
                                     "down", "shared_expert", "router_logits", "topk_select",
                                     "silu", "selection_scores", "routing_stats",
-                                    "dequantize_q4")}
+                                    "dequantize_q4", "gate_logit_grad", "swiglu_backward")}
 
 MUTATIONS = [
     ("topk_select", _topk_ties_high),
@@ -159,6 +188,11 @@ MUTATIONS = [
     ("dequantize_q4", _q4_nibbles_swapped),
     ("dequantize_q4", _q4_scale_bias_swapped),
     ("dequantize_q4", _q4_group_of_32),
+    ("silu_grad", _silu_grad_no_curvature),
+    ("gate_logit_grad", _logit_grad_sign),
+    ("gate_logit_grad", _logit_grad_renorm_ignored),
+    ("swiglu_backward", _swiglu_bwd_up_uses_z),
+    ("swiglu_backward", _swiglu_bwd_down_from_preactivation),
 ]
 
 
