@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 #define MOE_MAX_EXPERTS 256
 #define MOE_NUM_STAGES 5 /* route, dispatch, gate_up, down, combine */
 
@@ -94,7 +94,8 @@ typedef enum {
   MOE_ENTRY_DOWN = 3,
   MOE_ENTRY_EXPERT_FFN = 4,
   MOE_ENTRY_SHARED_EXPERT = 5,
-  MOE_ENTRY_ROUTING_STATS = 6
+  MOE_ENTRY_ROUTING_STATS = 6,
+  MOE_ENTRY_LAYER_BACKWARD = 7
 } moe_entry;
 
 /* Shapes and options of one layer call. One (E, h) per call: every routed
@@ -132,6 +133,28 @@ typedef struct {
   const uint32_t* w_up_sb;   /* [E, h, d/64] */
   const uint32_t* w_down_sb; /* [E, d, h/64] */
 } moe_weights;
+
+/* Gradients of one layer call (moe_layer_backward), all float32 and
+ * overwritten. Shapes follow the weights: dw_gate / dw_up [E, h, d],
+ * dw_down [E, d, h] (zero for experts no token chose), dw_router [E, d],
+ * dx [T, d]; the shared expert's dws_gate / dws_up [shared_h, d],
+ * dws_down [d, shared_h] and dw_shared_gate [d] are required when the layer
+ * has them and ignored otherwise. dgates [T, k] and dlogits [T, E] are
+ * optional copies of the intermediate gate and logit gradients (NULL to
+ * skip). */
+typedef struct {
+  float* dx;
+  float* dw_router;
+  float* dw_gate;
+  float* dw_up;
+  float* dw_down;
+  float* dws_gate;
+  float* dws_up;
+  float* dws_down;
+  float* dw_shared_gate;
+  float* dgates;
+  float* dlogits;
+} moe_grads;
 
 /* Library ABI version (MOE_ABI_VERSION). */
 int32_t moe_abi_version(void);
@@ -253,6 +276,28 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
                                     const void* x, void* out, int32_t* ids, float* gates,
                                     int32_t* counts, void* ws, size_t ws_bytes,
                                     void* const* stage_events, void* stream);
+
+/* Backward of moe_layer_forward: the gradients of sum(out * dout) with the
+ * selection held fixed (top-k is piecewise constant in the logits), for the
+ * training step of "Small models, sparse experts" (section "Tuning the
+ * training loop": forward, backward and optimiser compiled together, with
+ * activations recomputed in the backward pass instead of stored). x and
+ * dout are [T, d] in cfg->dtype, which must be MOE_BF16; quantised routed
+ * experts are MOE_ERR_UNSUPPORTED (they are not trained here). The call
+ * recomputes the route, the dispatch and each expert's gate and up
+ * pre-activations; it differentiates the gates in the configured mode
+ * (softmax over all experts with or without renormalisation, softmax over
+ * the selected, sigmoid affinities), the router weights, every expert's
+ * SwiGLU and the shared expert with its gate. The router bias and the
+ * balance bias are constants and get no gradient. Products run in bf16 on
+ * MFMA with float32 accumulation; the intermediate gradients that feed a
+ * product (the pre-activation gradients, the gated activations, dlogits)
+ * are rounded to bf16 there. Workspace: MOE_ENTRY_LAYER_BACKWARD. Every
+ * gradient is written by one workgroup in a fixed order (no atomics): the
+ * result is deterministic. */
+moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* w, const void* x,
+                              const void* dout, const moe_grads* grads, void* ws,
+                              size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -39,6 +39,7 @@ MOE_ENTRY_DOWN = 3
 MOE_ENTRY_EXPERT_FFN = 4
 MOE_ENTRY_SHARED_EXPERT = 5
 MOE_ENTRY_ROUTING_STATS = 6
+MOE_ENTRY_LAYER_BACKWARD = 7
 
 MOE_NUM_STAGES = 5
 STAGE_NAMES = ("route", "dispatch", "gate_up", "down", "combine")
@@ -59,6 +60,12 @@ class MoeWeights(ctypes.Structure):
         ("w_gate_sb", ctypes.c_void_p), ("w_up_sb", ctypes.c_void_p),
         ("w_down_sb", ctypes.c_void_p),
     ]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up", "dws_down",
+        "dw_shared_gate", "dgates", "dlogits")]
 
 
 class MoeError(RuntimeError):
@@ -87,6 +94,7 @@ _SIG = {
                           ctypes.c_int),
     "moe_layer_forward": ([_P] * 8 + [ctypes.c_size_t, _P], ctypes.c_int),
     "moe_layer_forward_traced": ([_P] * 8 + [ctypes.c_size_t, _P, _P], ctypes.c_int),
+    "moe_layer_backward": ([_P] * 6 + [ctypes.c_size_t, _P], ctypes.c_int),
 }
 
 
@@ -318,3 +326,36 @@ def layer_forward(cfg, weights, x, out=None, ids=None, gates=None, counts=None, 
                                             _stream(stream))
     _check(st, "moe_layer_forward")
     return out
+
+
+def layer_backward(cfg, weights, x, dout, grads=None, ws=None, want_intermediates=False,
+                   stream=None):
+    """Gradients of sum(out * dout) for the layer (moe_layer_backward). Returns
+    a dict of float32 device tensors keyed like moe_grads' fields (the shared
+    expert's only when the layer has one; dgates / dlogits only when
+    ``want_intermediates``). ``grads``: a dict of preallocated outputs."""
+    import torch
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(grads or {})
+    shapes = {"dx": (cfg.T, cfg.d), "dw_router": (cfg.E, cfg.d),
+              "dw_gate": (cfg.E, cfg.h, cfg.d), "dw_up": (cfg.E, cfg.h, cfg.d),
+              "dw_down": (cfg.E, cfg.d, cfg.h)}
+    if cfg.shared_h > 0:
+        shapes.update(dws_gate=(cfg.shared_h, cfg.d), dws_up=(cfg.shared_h, cfg.d),
+                      dws_down=(cfg.d, cfg.shared_h))
+        if cfg.shared_gate:
+            shapes["dw_shared_gate"] = (cfg.d,)
+    if want_intermediates:
+        shapes.update(dgates=(cfg.T, cfg.top_k), dlogits=(cfg.T, cfg.E))
+    for n, shp in shapes.items():
+        if n not in g:
+            g[n] = torch.empty(shp, **f32)
+    if ws is None:
+        ws = alloc_workspace(cfg, MOE_ENTRY_LAYER_BACKWARD, dev)
+    wst = weights if isinstance(weights, MoeWeights) else weights_struct(weights)
+    gs = MoeGrads(*[_ptr(g.get(n)) for n, _ in MoeGrads._fields_])
+    _check(lib().moe_layer_backward(ctypes.byref(cfg), ctypes.byref(wst), _ptr(x), _ptr(dout),
+                                    ctypes.byref(gs), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_layer_backward")
+    return g

@@ -128,6 +128,46 @@ WsLayout ws_layout(const moe_config& c) {
   return L;
 }
 
+// Backward workspace: the forward's routing tables (with 128-row tiles),
+// then the logits and the backward's own buffers.
+struct BwdLayout {
+  WsLayout tables;
+  size_t logits, z, gact, dz, part, dxr, z_s, gact_s, dz_s, part_s, dx_s, dlb, dpre, sg_part, end;
+};
+
+BwdLayout bwd_layout(const moe_config& c) {
+  BwdLayout B{};
+  B.tables = ws_layout(c);
+  size_t o = B.tables.end_tables;
+  auto take = [&](size_t bytes) {
+    const size_t at_ = o;
+    o += align256(bytes);
+    return at_;
+  };
+  const size_t T = static_cast<size_t>(c.T), P = T * static_cast<size_t>(c.top_k);
+  const size_t d = static_cast<size_t>(c.d), h = static_cast<size_t>(c.h);
+  const size_t hs = static_cast<size_t>(c.shared_h);
+  const size_t epad = static_cast<size_t>(ceil_div(c.E, 8) * 8);
+  const size_t np = 2 * static_cast<size_t>(ceil_div(c.h, 128));
+  const size_t nps = hs > 0 ? 2 * static_cast<size_t>(ceil_div(c.shared_h, 128)) : 0;
+  B.logits = take(T * static_cast<size_t>(c.E) * 4);
+  B.z = take(P * 2 * h * 4);
+  B.gact = take(P * h * 2);
+  B.dz = take(P * 2 * h * 2);
+  B.part = take(P * np * 4);
+  B.dxr = take(P * d * 4);
+  B.z_s = take(T * 2 * hs * 4);
+  B.gact_s = take(T * hs * 2);
+  B.dz_s = take(T * 2 * hs * 2);
+  B.part_s = take(T * nps * 4);
+  B.dx_s = take(hs > 0 ? T * d * 4 : 0);
+  B.dlb = take(T * epad * 2);
+  B.dpre = take(T * 4);
+  B.sg_part = take(static_cast<size_t>(ceil_div(c.T, 256)) * d * 4);
+  B.end = o;
+  return B;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -161,6 +201,7 @@ size_t moe_workspace_size_entry(const moe_config* cfg, int32_t entry) {
     case MOE_ENTRY_SHARED_EXPERT: return L.end_act;
     case MOE_ENTRY_ROUTING_STATS:
       return cfg->T > 0 ? align256(static_cast<size_t>(stats_blocks(cfg->T)) * (cfg->E + 1) * 4) : 0;
+    case MOE_ENTRY_LAYER_BACKWARD: return bwd_layout(*cfg).end;
     default: return 0;
   }
 }
@@ -531,6 +572,132 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const 
                              size_t ws_bytes, void* stream) {
   return moe_layer_forward_traced(cfg, w, x, out, ids, gates, counts, ws, ws_bytes, nullptr,
                                   stream);
+}
+
+moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* w, const void* x,
+                              const void* dout, const moe_grads* gr, void* ws, size_t ws_bytes,
+                              void* stream) {
+  MOE_TRY(check_cfg(cfg));
+  const moe_config& c = *cfg;
+  if (c.dtype != MOE_BF16 || c.expert_quant != MOE_QUANT_NONE) return MOE_ERR_UNSUPPORTED;
+  if (w == nullptr || gr == nullptr) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(need(w->w_router)); MOE_TRY(need(w->w_gate)); MOE_TRY(need(w->w_up));
+  MOE_TRY(need(w->w_down));
+  if (c.has_router_bias) MOE_TRY(need(w->b_router));
+  MOE_TRY(need(gr->dw_router)); MOE_TRY(need(gr->dw_gate)); MOE_TRY(need(gr->dw_up));
+  MOE_TRY(need(gr->dw_down));
+  const bool has_sh = c.shared_h > 0;
+  const bool gated = has_sh && c.shared_gate;
+  if (has_sh) {
+    MOE_TRY(need(w->ws_gate)); MOE_TRY(need(w->ws_up)); MOE_TRY(need(w->ws_down));
+    MOE_TRY(need(gr->dws_gate)); MOE_TRY(need(gr->dws_up)); MOE_TRY(need(gr->dws_down));
+    if (gated) { MOE_TRY(need(w->w_shared_gate)); MOE_TRY(need(gr->dw_shared_gate)); }
+  }
+  if (c.T > 0) { MOE_TRY(need(x)); MOE_TRY(need(dout)); MOE_TRY(need(gr->dx)); }
+  MOE_TRY(maybe(gr->dgates)); MOE_TRY(maybe(gr->dlogits));
+  MOE_TRY(check_ws(c, MOE_ENTRY_LAYER_BACKWARD, ws, ws_bytes));
+
+  hipStream_t s = as_stream(stream);
+  const BwdLayout B = bwd_layout(c);
+  const WsLayout& L = B.tables;
+  if (c.T == 0) {
+    // no token: every weight gradient is zero
+    const size_t E = static_cast<size_t>(c.E), d = static_cast<size_t>(c.d);
+    const size_t h = static_cast<size_t>(c.h), hs = static_cast<size_t>(c.shared_h);
+    MOE_HIP(launch_fill_zero(gr->dw_router, E * d, s));
+    MOE_HIP(launch_fill_zero(gr->dw_gate, E * h * d, s));
+    MOE_HIP(launch_fill_zero(gr->dw_up, E * h * d, s));
+    MOE_HIP(launch_fill_zero(gr->dw_down, E * d * h, s));
+    if (has_sh) {
+      MOE_HIP(launch_fill_zero(gr->dws_gate, hs * d, s));
+      MOE_HIP(launch_fill_zero(gr->dws_up, hs * d, s));
+      MOE_HIP(launch_fill_zero(gr->dws_down, d * hs, s));
+      if (gated) MOE_HIP(launch_fill_zero(gr->dw_shared_gate, d, s));
+    }
+    return MOE_OK;
+  }
+  const int rt = route_tokens(c.T);
+  const int NB = ceil_div(c.T, rt);
+  const int tm = kTileM;
+  const int P = c.T * c.top_k;
+  int32_t* ids = at<int32_t>(ws, L.ids);
+  float* gates = at<float>(ws, L.gates);
+  int32_t* counts = at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm = at<int32_t>(ws, L.perm);
+  int32_t* inv = at<int32_t>(ws, L.inv);
+  float* sg = gated ? at<float>(ws, L.sgate) : nullptr;
+  float* logits = at<float>(ws, B.logits);
+
+  RouteParams rp{};
+  rp.x = x;
+  rp.w_router = w->w_router;
+  rp.bias = c.has_router_bias ? w->b_router : nullptr;
+  rp.w_sgate = gated ? w->w_shared_gate : nullptr;
+  rp.T = c.T; rp.d = c.d; rp.E = c.E; rp.k = c.top_k; rp.mode = c.mode; rp.renorm = c.renormalize;
+  rp.rt = rt;
+  rp.ids = ids;
+  rp.gates = gates;
+  rp.logits = logits;
+  rp.sgate = sg;
+  rp.blk_hist = at<int32_t>(ws, L.blk_hist);
+  rp.lrank = at<int32_t>(ws, L.lrank);
+  if (NB == 1) {
+    rp.counts = counts; rp.offsets = offsets; rp.perm = perm; rp.inv = inv;
+    rp.tile_e = at<int32_t>(ws, L.tile_e); rp.exp_tile0 = at<int32_t>(ws, L.exp_tile0);
+    rp.meta = at<int32_t>(ws, L.meta);
+    rp.touched = at<int32_t>(ws, L.touched);
+    rp.tile_m = tm;
+    rp.max_tiles = max_m_tiles(P, c.E, tm);
+    rp.part = at<float>(ws, L.part);
+    rp.ncp = route_part_cols(c.E, gated);
+    MOE_HIP(launch_route_split(rp, c.dtype, s));
+  } else {
+    MOE_HIP(launch_route(rp, c.dtype, s));
+    ScanParams sp{at<int32_t>(ws, L.blk_hist), NB, c.E, counts};
+    MOE_HIP(launch_scan(sp, s));
+    ScatterParams xp{ids, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank), c.T, c.E,
+                     c.top_k, rt, perm, inv, counts, offsets, max_m_tiles(P, c.E, tm), tm,
+                     at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0), at<int32_t>(ws, L.meta),
+                     at<int32_t>(ws, L.touched)};
+    MOE_HIP(launch_scatter(xp, s));
+  }
+
+  BwdParams bp{};
+  bp.T = c.T; bp.d = c.d; bp.E = c.E; bp.Epad = ceil_div(c.E, 8) * 8; bp.h = c.h;
+  bp.hs = c.shared_h; bp.k = c.top_k; bp.mode = c.mode; bp.renorm = c.renormalize;
+  bp.max_mtiles = max_m_tiles(P, c.E, tm);
+  bp.meta = at<int32_t>(ws, L.meta); bp.tile_e = at<int32_t>(ws, L.tile_e);
+  bp.exp_tile0 = at<int32_t>(ws, L.exp_tile0); bp.offsets = offsets; bp.perm = perm;
+  bp.inv = inv; bp.ids = ids; bp.gates = gates; bp.logits = logits; bp.sgate = sg;
+  bp.x = static_cast<const uint16_t*>(x);
+  bp.dout = static_cast<const uint16_t*>(dout);
+  bp.w_router = static_cast<const uint16_t*>(w->w_router);
+  bp.w_gate = static_cast<const uint16_t*>(w->w_gate);
+  bp.w_up = static_cast<const uint16_t*>(w->w_up);
+  bp.w_down = static_cast<const uint16_t*>(w->w_down);
+  if (has_sh) {
+    bp.ws_gate = static_cast<const uint16_t*>(w->ws_gate);
+    bp.ws_up = static_cast<const uint16_t*>(w->ws_up);
+    bp.ws_down = static_cast<const uint16_t*>(w->ws_down);
+    bp.z_s = at<float>(ws, B.z_s); bp.gact_s = at<uint16_t>(ws, B.gact_s);
+    bp.dz_s = at<uint16_t>(ws, B.dz_s); bp.part_s = at<float>(ws, B.part_s);
+    bp.dx_s = at<float>(ws, B.dx_s);
+    bp.dws_gate = gr->dws_gate; bp.dws_up = gr->dws_up; bp.dws_down = gr->dws_down;
+    if (gated) {
+      bp.w_shared_gate = static_cast<const uint16_t*>(w->w_shared_gate);
+      bp.dpre = at<float>(ws, B.dpre);
+      bp.sg_part = at<float>(ws, B.sg_part);
+      bp.dw_shared_gate = gr->dw_shared_gate;
+    }
+  }
+  bp.z = at<float>(ws, B.z); bp.gact = at<uint16_t>(ws, B.gact); bp.dz = at<uint16_t>(ws, B.dz);
+  bp.part = at<float>(ws, B.part); bp.dxr = at<float>(ws, B.dxr);
+  bp.dlb = at<uint16_t>(ws, B.dlb);
+  bp.dx = gr->dx; bp.dw_router = gr->dw_router; bp.dw_gate = gr->dw_gate; bp.dw_up = gr->dw_up;
+  bp.dw_down = gr->dw_down; bp.dgates = gr->dgates; bp.dlogits = gr->dlogits;
+  MOE_HIP(launch_backward(bp, s));
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -256,4 +256,31 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 hipError_t launch_scale_rows(const ScaleRowsParams& p, hipStream_t s);
 hipError_t launch_rowdot_sigmoid(const RowDotSigmoidParams& p, hipStream_t s);
 
+// Backward of the layer (backward.hip). Routing tables come from the route
+// and dispatch kernels run with 128-row tiles; buffers are workspace.
+struct BwdParams {
+  int shared;                 // set by launch_backward for the shared expert's products
+  int T, d, E, Epad, h, hs, k, mode, renorm, max_mtiles;
+  const int32_t *meta, *tile_e, *exp_tile0, *offsets, *perm, *inv, *ids;
+  const float* gates;         // [T, k]
+  const float* logits;        // [T, E] (biased in the softmax modes, raw in MOE_SIGMOID)
+  const float* sgate;         // [T] sigmoid(w_s . x), or null
+  const uint16_t *x, *dout, *w_router, *w_gate, *w_up, *w_down;
+  const uint16_t *ws_gate, *ws_up, *ws_down, *w_shared_gate;
+  float *z, *z_s;             // [P, 2h], [T, 2hs] gate | up pre-activations
+  uint16_t *gact, *gact_s;    // [P, h], [T, hs] gate * silu(z_g) * z_u, bf16
+  uint16_t *dz, *dz_s;        // [P, 2h], [T, 2hs] pre-activation gradients, bf16
+  float *part, *part_s;       // [P, 2 ceil(h/128)], [T, 2 ceil(hs/128)] dG partial sums
+  float *dxr, *dx_s;          // [P, d] routed dx rows (sorted), [T, d] shared dx, or null
+  uint16_t* dlb;              // [T, Epad] dlogits, bf16, zero-padded
+  float* dpre;                // [T] shared gate pre-activation gradient, or null
+  float* sg_part;             // [ceil(T/256), d] partial sums of dw_shared_gate
+  float *dx, *dw_router, *dw_gate, *dw_up, *dw_down;
+  float *dws_gate, *dws_up, *dws_down, *dw_shared_gate;
+  float *dgates, *dlogits;    // optional copies
+};
+hipError_t launch_backward(const BwdParams& p, hipStream_t s);
+// n float zeros at p (a fill kernel, not a memset: safe under graph capture).
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
+
 }  // namespace moe

@@ -17,7 +17,7 @@ def test_library_exports_every_header_function():
     assert len(names) >= 14
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 def test_status_strings():
@@ -156,3 +156,43 @@ def test_build_script_lists_existing_sources():
     import os
     for s in build_mod.SOURCES:
         assert os.path.exists(os.path.join(build_mod.CSRC, s)), s
+
+
+def _fake(n=1):
+    # 16-byte aligned addresses that are never dereferenced (every call below
+    # fails host validation first)
+    return [ctypes.c_void_p(0x10000 + 256 * i) for i in range(n)]
+
+
+def _backward(cfg, grads_fields=None, ws_bytes=0, weights_null=False):
+    w = B.MoeWeights(*[None] * len(B.MoeWeights._fields_)) if weights_null else \
+        B.MoeWeights(*_fake(len(B.MoeWeights._fields_)))
+    gf = grads_fields if grads_fields is not None else _fake(len(B.MoeGrads._fields_))
+    g = B.MoeGrads(*gf)
+    x, dout, ws = _fake(3)
+    return B.lib().moe_layer_backward(ctypes.byref(cfg), ctypes.byref(w), x, dout,
+                                      ctypes.byref(g), ws, ws_bytes, None)
+
+
+def test_backward_workspace_size():
+    c = _cfg()
+    n = B.workspace_size(c, B.MOE_ENTRY_LAYER_BACKWARD)
+    P = 100 * 2
+    # at least the float32 pre-activations and the float32 dx rows
+    assert n >= P * 2 * 32 * 4 + P * 64 * 4
+    assert n % 256 == 0
+    assert B.workspace_size(_cfg(d=60), B.MOE_ENTRY_LAYER_BACKWARD) == 0
+
+
+def test_backward_host_validation():
+    c = _cfg()
+    assert _backward(_cfg(dtype=B.MOE_F32)) == B.MOE_ERR_UNSUPPORTED
+    assert _backward(_cfg(expert_quant=B.MOE_QUANT_Q4_G64)) == B.MOE_ERR_UNSUPPORTED
+    assert _backward(c, weights_null=True) == B.MOE_ERR_INVALID_ARG
+    assert _backward(c, grads_fields=[None] * len(B.MoeGrads._fields_)) == B.MOE_ERR_INVALID_ARG
+    assert _backward(c, ws_bytes=0) == B.MOE_ERR_WORKSPACE
+    assert _backward(_cfg(T=-1)) == B.MOE_ERR_INVALID_ARG
+    # a shared expert needs its gradient buffers
+    gf = _fake(len(B.MoeGrads._fields_))
+    gf[B.MoeGrads._fields_.index(("dws_gate", ctypes.c_void_p))] = None
+    assert _backward(_cfg(shared_h=64), grads_fields=gf) == B.MOE_ERR_INVALID_ARG
