@@ -144,6 +144,9 @@ def main():
                     help="minimum bytes of distinct weight copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
+                    help="forward (the headline) or the layer backward (gradients of "
+                         "sum(out * dout), recomputing route and pre-activations)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB "
                          "(a reference kernel for scaling profiler byte counters)")
@@ -190,6 +193,9 @@ def main():
     x = dev(inp["x"])
     cfg = B.config_from_spec(spec)
     T = spec.T
+    if args.which == "backward":
+        run_backward(args, spec, inp, cfg, x, wstructs, nsets, B, R, StageEvents)
+        return
     out = torch.empty((T, spec.d), dtype=x.dtype, device="cuda")
     ids = torch.empty((T, spec.k), dtype=torch.int32, device="cuda")
     counts = torch.empty(spec.E, dtype=torch.int32, device="cuda")
@@ -304,6 +310,111 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_backward(inp, dout, budget_s=20.0):
+    """The oracle's backward, as it stands, on a bounded sample of tokens."""
+    import oracle.moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    spec = inp["spec"]
+
+    def run(Ts):
+        sub = dict(inp)
+        sub["x"] = inp["x"][:Ts]
+        sub["spec"] = dataclasses.replace(spec, T=Ts)
+        t0 = time.perf_counter()
+        O.layer_backward(sub, dout[:Ts])
+        return time.perf_counter() - t0
+
+    Ts = min(spec.T, 256)
+    t = run(Ts)
+    while Ts < spec.T and t < budget_s / 6:
+        Ts = min(spec.T, Ts * 2)
+        t = run(Ts)
+    times = [t]
+    while len(times) < 3 and sum(times) + t < budget_s:
+        times.append(run(Ts))
+    med = statistics.median(times)
+    return {"value": Ts / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {Ts} of {spec.T} tokens of the same inputs, float64 NumPy oracle "
+                      f"backward, median of {len(times)} run(s) of {med:.2f} s"}
+
+
+def run_backward(args, spec, inp, cfg, x, wstructs, nsets, B, R, StageEvents):
+    """The layer backward: K timed moe_layer_backward calls (rotating weight
+    copies), then K traced calls for the stage durations."""
+    import numpy as np
+    import torch
+    from moe_inputs.generate import bf16_bits_from_f32
+    if spec.dtype != 1:
+        print("the layer backward runs on bf16 layers only", file=sys.stderr, flush=True)
+        sys.exit(2)
+    T = spec.T
+    rng = np.random.default_rng(1234)
+    dout_bits = bf16_bits_from_f32(rng.standard_normal((T, spec.d)).astype(np.float32))
+    dout = torch.from_numpy(dout_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    ws = B.alloc_workspace(cfg, B.MOE_ENTRY_LAYER_BACKWARD)
+    grads = B.layer_backward(cfg, wstructs[0], x, dout, ws=ws)
+    log(f"[bench] backward workspace {ws.numel() / 2**20:.1f} MiB")
+    for i in range(args.warmup):
+        B.layer_backward(cfg, wstructs[i % nsets], x, dout, grads=grads, ws=ws)
+    torch.cuda.synchronize()
+    outer = StageEvents(1, 1)
+    hip = outer.hip
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    hip.hipEventRecord(outer.row(0)[0], stream)
+    for i in range(args.steps):
+        B.layer_backward(cfg, wstructs[i % nsets], x, dout, grads=grads, ws=ws)
+    hip.hipEventRecord(outer.row(0)[1], stream)
+    torch.cuda.synchronize()
+    hip.hipEventSynchronize(outer.row(0)[1])
+    ms_per_step = outer.elapsed_ms(outer.row(0)[0], outer.row(0)[1]) / args.steps
+    outer.destroy()
+    log(f"[bench] backward: timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
+    ev = StageEvents(args.steps, B.MOE_NUM_BWD_STAGES)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        B.layer_backward(cfg, wstructs[i % nsets], x, dout, grads=grads, ws=ws,
+                         stage_events=ev.row(i))
+    torch.cuda.synchronize()
+    stage = np.array(ev.stage_ms())
+    traced_ms = ev.span_ms() / args.steps
+    ev.destroy()
+    mean_stage_us = {n: float(stage[:, i].mean() * 1e3) for i, n in enumerate(B.BWD_STAGE_NAMES)}
+    flops = R.backward_stage_flops(T, spec.d, spec.E, spec.h, spec.k, spec.shared_h,
+                                   spec.shared_gate)
+    dom = max(mean_stage_us, key=mean_stage_us.get)
+    achieved = flops[dom] / (mean_stage_us[dom] * 1e-6) / 1e12
+    roof = {"bound": "mfma", "achieved": achieved, "peak": R.PEAK_BF16_MFMA_FLOPS / 1e12,
+            "unit": "TFLOP/s", "frac": achieved / (R.PEAK_BF16_MFMA_FLOPS / 1e12),
+            "traffic": None, "alg_flops": flops[dom], "kernel": dom}
+    total = sum(flops.values())
+    sec = ms_per_step * 1e-3
+    result = {
+        "metric": "MoE layer bwd tokens/s on 1 GPU (gradients of sum(out*dout), route and "
+                  "pre-activations recomputed); % bf16 MFMA peak",
+        "value": T / sec, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.config} backward", "T": T, "d": spec.d, "E": spec.E,
+                   "h": spec.h, "top_k": spec.k, "shared_h": spec.shared_h,
+                   "weight_copies": nsets, "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": {"mfma_frac": total / sec / R.PEAK_BF16_MFMA_FLOPS, "alg_flops": total},
+        "stages_us": mean_stage_us,
+        "traced_us_per_step": traced_ms * 1e3,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle backward baseline")
+        result["cpu_baseline"] = cpu_baseline_backward(inp, dout_bits, args.cpu_budget_s)
     print(json.dumps(result), flush=True)
 
 

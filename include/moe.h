@@ -299,6 +299,21 @@ moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* w, const
                               const void* dout, const moe_grads* grads, void* ws,
                               size_t ws_bytes, void* stream);
 
+/* Stages of moe_layer_backward_traced: route and dispatch (recomputed), the
+ * gate/up pre-activations (recomputed), the down-projection gradient into
+ * the hidden units, the gate and logit gradients, dW_down, dW_gate|up, the
+ * routed and shared dx rows, and the router products with the final dx. */
+#define MOE_NUM_BWD_STAGES 8
+
+/* moe_layer_backward that also records stage_events[0] before the first
+ * launch and stage_events[i + 1] after stage i (MOE_NUM_BWD_STAGES stages).
+ * stage_events holds MOE_NUM_BWD_STAGES + 1 hipEvent_t created by the
+ * caller; NULL = untraced. With T == 0 no event is recorded. */
+moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w,
+                                     const void* x, const void* dout, const moe_grads* grads,
+                                     void* ws, size_t ws_bytes, void* const* stage_events,
+                                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

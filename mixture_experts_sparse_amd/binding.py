@@ -43,6 +43,9 @@ MOE_ENTRY_LAYER_BACKWARD = 7
 
 MOE_NUM_STAGES = 5
 STAGE_NAMES = ("route", "dispatch", "gate_up", "down", "combine")
+MOE_NUM_BWD_STAGES = 8
+BWD_STAGE_NAMES = ("route", "z", "d_hidden", "router_grad", "dw_down", "dw_gate_up", "dx_rows",
+                   "dx_router")
 
 
 class MoeConfig(ctypes.Structure):
@@ -95,6 +98,7 @@ _SIG = {
     "moe_layer_forward": ([_P] * 8 + [ctypes.c_size_t, _P], ctypes.c_int),
     "moe_layer_forward_traced": ([_P] * 8 + [ctypes.c_size_t, _P, _P], ctypes.c_int),
     "moe_layer_backward": ([_P] * 6 + [ctypes.c_size_t, _P], ctypes.c_int),
+    "moe_layer_backward_traced": ([_P] * 6 + [ctypes.c_size_t, _P, _P], ctypes.c_int),
 }
 
 
@@ -329,7 +333,7 @@ def layer_forward(cfg, weights, x, out=None, ids=None, gates=None, counts=None, 
 
 
 def layer_backward(cfg, weights, x, dout, grads=None, ws=None, want_intermediates=False,
-                   stream=None):
+                   stage_events=None, stream=None):
     """Gradients of sum(out * dout) for the layer (moe_layer_backward). Returns
     a dict of float32 device tensors keyed like moe_grads' fields (the shared
     expert's only when the layer has one; dgates / dlogits only when
@@ -355,7 +359,12 @@ def layer_backward(cfg, weights, x, dout, grads=None, ws=None, want_intermediate
         ws = alloc_workspace(cfg, MOE_ENTRY_LAYER_BACKWARD, dev)
     wst = weights if isinstance(weights, MoeWeights) else weights_struct(weights)
     gs = MoeGrads(*[_ptr(g.get(n)) for n, _ in MoeGrads._fields_])
-    _check(lib().moe_layer_backward(ctypes.byref(cfg), ctypes.byref(wst), _ptr(x), _ptr(dout),
-                                    ctypes.byref(gs), _ptr(ws), ws.numel(), _stream(stream)),
-           "moe_layer_backward")
+    args = (ctypes.byref(cfg), ctypes.byref(wst), _ptr(x), _ptr(dout), ctypes.byref(gs), _ptr(ws),
+            ws.numel())
+    if stage_events is None:
+        st = lib().moe_layer_backward(*args, _stream(stream))
+    else:
+        st = lib().moe_layer_backward_traced(*args, ctypes.cast(stage_events, ctypes.c_void_p),
+                                             _stream(stream))
+    _check(st, "moe_layer_backward")
     return g

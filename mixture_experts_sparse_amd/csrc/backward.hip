@@ -42,6 +42,10 @@ namespace {
 
 constexpr int NT_ = 256;  // threads per workgroup
 constexpr int TM = 128, TN = 128, TK = 32;
+constexpr int KS = TK / 32;                 // MFMA K steps per stage
+constexpr int CH = TM * TK / 8 / NT_;       // 16-byte chunks per thread per operand and stage
+static_assert(TM == TN && CH % 2 == 0, "square tiles, whole chunk pairs");
+constexpr int kRouterKChunk = kBwdRouterChunk;  // tokens per partial of dW_r
 
 enum : int {
   PROB_Z = 0,         // z = x W_{g|u}^T (gate/up pre-activations, interleaved 64-wide)
@@ -68,9 +72,11 @@ struct Tile {
   int k0, k1;      // K range (stored-row indices for K-as-row operands)
 };
 
-// LDS tile: TM rows of TK bf16 (4 chunks of 16 bytes, swizzled).
+// LDS tile: TM rows of TK bf16 (TK / 8 chunks of 16 bytes, swizzled so the
+// 8 rows LDS serves together read 8 distinct bank groups).
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * TK + ((chunk ^ ((row >> 1) & 3)) << 3);
+  if constexpr (TK == 64) return row * TK + ((chunk ^ (row & 7)) << 3);
+  else return row * TK + ((chunk ^ ((row >> 1) & 3)) << 3);
 }
 
 __device__ __forceinline__ u32x4_t ld16(const uint16_t* p, bool ok) {
@@ -128,18 +134,31 @@ __device__ bool decode(const BwdParams& p, Tile& t) {
       t.e = e; t.k0 = p.offsets[e]; t.k1 = p.offsets[e + 1];
     }
     return true;
-  } else {
-    // dense products over tokens
-    const int M = PROB == PROB_DXROUTER ? p.T : p.E;
-    const int N = p.d;
-    const int NT = (N + TN - 1) / TN;
+  } else if constexpr (PROB == PROB_DXROUTER) {
+    // dense product over tokens
+    const int NT = (p.d + TN - 1) / TN;
     const int mt = b / NT, nt = b - mt * NT;
     t.m0 = mt * TM; t.n0 = nt * TN;
-    if (t.m0 >= M) return false;
-    t.mlim = min(TM, M - t.m0); t.nlim = min(TN, N - t.n0);
+    if (t.m0 >= p.T) return false;
+    t.mlim = min(TM, p.T - t.m0); t.nlim = min(TN, p.d - t.n0);
     t.e = -1; t.row0 = t.m0;
     t.k0 = 0;
-    t.k1 = PROB == PROB_DXROUTER ? p.Epad : p.T;
+    t.k1 = p.Epad;
+    return true;
+  } else {
+    // dW_r: the token reduction split into chunks of kRouterKChunk, each
+    // chunk's tile written to its own partial slab (summed in chunk order)
+    const int MT = (p.E + TM - 1) / TM, NT = (p.d + TN - 1) / TN;
+    const int per = MT * NT;
+    const int ch = b / per;
+    const int r = b - ch * per;
+    const int mt = r / NT, nt = r - mt * NT;
+    t.m0 = mt * TM; t.n0 = nt * TN;
+    t.mlim = min(TM, p.E - t.m0); t.nlim = min(TN, p.d - t.n0);
+    t.e = ch; t.row0 = 0;
+    t.k0 = ch * kRouterKChunk;
+    if (t.k0 >= p.T) return false;
+    t.k1 = min(p.T, t.k0 + kRouterKChunk);
     return true;
   }
 }
@@ -224,32 +243,37 @@ __device__ __forceinline__ const uint16_t* b_chunk(const BwdParams& p, const Til
 }
 
 // Staging of one K step into registers and from there into LDS.
-// K-contiguous: thread q loads chunks q and q + 256 of the 128 x 4 chunk tile.
-// K-as-row: thread q loads K rows 2 (q % 16), 2 (q % 16) + 1 at tile columns
-// 8 (q / 16) .. + 7, and writes them as 8 (k, k + 1) pairs.
+// K-contiguous: thread q loads chunks q + 256 i (i < CH) of the TM x TK/8
+// chunk tile. K-as-row: thread q loads K rows 2 (q % 16 + 16 j) and the next
+// one (j < CH / 2) at tile columns 8 (q / 16) .. + 7, and writes them as 8
+// (k, k + 1) pairs each.
 struct Stage {
-  u32x4_t v0, v1;
+  u32x4_t v[CH];
 };
 
 template <int PROB, bool A>
 __device__ __forceinline__ void load_stage(const BwdParams& p, const Tile& t, int kbase, Stage& s) {
   const int tid = threadIdx.x;
   constexpr bool KC = A ? a_kcontig<PROB>() : b_kcontig<PROB>();
+  constexpr int CPR = TK / 8;
   if constexpr (KC) {
-    const int q0 = tid, q1 = tid + NT_;
-    const uint16_t* p0 = A ? a_chunk<PROB>(p, t, q0 >> 2, kbase + (q0 & 3) * 8)
-                           : b_chunk<PROB>(p, t, q0 >> 2, kbase + (q0 & 3) * 8);
-    const uint16_t* p1 = A ? a_chunk<PROB>(p, t, q1 >> 2, kbase + (q1 & 3) * 8)
-                           : b_chunk<PROB>(p, t, q1 >> 2, kbase + (q1 & 3) * 8);
-    s.v0 = ld16(p0, p0 != nullptr);
-    s.v1 = ld16(p1, p1 != nullptr);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int q = tid + i * NT_;
+      const uint16_t* ptr = A ? a_chunk<PROB>(p, t, q / CPR, kbase + (q % CPR) * 8)
+                              : b_chunk<PROB>(p, t, q / CPR, kbase + (q % CPR) * 8);
+      s.v[i] = ld16(ptr, ptr != nullptr);
+    }
   } else {
-    const int kp = tid & 15, c8 = (tid >> 4) * 8;
-    const int k = kbase + 2 * kp;
-    const uint16_t* p0 = A ? a_chunk<PROB>(p, t, c8, k) : b_chunk<PROB>(p, t, c8, k);
-    const uint16_t* p1 = A ? a_chunk<PROB>(p, t, c8, k + 1) : b_chunk<PROB>(p, t, c8, k + 1);
-    s.v0 = ld16(p0, p0 != nullptr);
-    s.v1 = ld16(p1, p1 != nullptr);
+    const int c8 = (tid >> 4) * 8;
+#pragma unroll
+    for (int j = 0; j < CH / 2; ++j) {
+      const int k = kbase + 2 * ((tid & 15) + 16 * j);
+      const uint16_t* p0 = A ? a_chunk<PROB>(p, t, c8, k) : b_chunk<PROB>(p, t, c8, k);
+      const uint16_t* p1 = A ? a_chunk<PROB>(p, t, c8, k + 1) : b_chunk<PROB>(p, t, c8, k + 1);
+      s.v[2 * j] = ld16(p0, p0 != nullptr);
+      s.v[2 * j + 1] = ld16(p1, p1 != nullptr);
+    }
   }
 }
 
@@ -257,20 +281,26 @@ template <int PROB, bool A>
 __device__ __forceinline__ void store_stage(uint16_t* lds, const Stage& s) {
   const int tid = threadIdx.x;
   constexpr bool KC = A ? a_kcontig<PROB>() : b_kcontig<PROB>();
+  constexpr int CPR = TK / 8;
   if constexpr (KC) {
-    const int q0 = tid, q1 = tid + NT_;
-    *reinterpret_cast<u32x4_t*>(lds + lds_off(q0 >> 2, q0 & 3)) = s.v0;
-    *reinterpret_cast<u32x4_t*>(lds + lds_off(q1 >> 2, q1 & 3)) = s.v1;
-  } else {
-    const int kp = tid & 15, c8 = (tid >> 4) * 8;
-    const int k = 2 * kp;  // even: the pair is one aligned 32-bit word
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // element i of each chunk: bf16 i of the 16 bytes
-      const uint32_t lo = (s.v0[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-      const uint32_t hi = (s.v1[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-      const int row = c8 + i;
-      *reinterpret_cast<uint32_t*>(lds + lds_off(row, k >> 3) + (k & 7)) = lo | (hi << 16);
+    for (int i = 0; i < CH; ++i) {
+      const int q = tid + i * NT_;
+      *reinterpret_cast<u32x4_t*>(lds + lds_off(q / CPR, q % CPR)) = s.v[i];
+    }
+  } else {
+    const int c8 = (tid >> 4) * 8;
+#pragma unroll
+    for (int j = 0; j < CH / 2; ++j) {
+      const int k = 2 * ((tid & 15) + 16 * j);  // even: the pair is one aligned 32-bit word
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // element i of each chunk: bf16 i of the 16 bytes
+        const uint32_t lo = (s.v[2 * j][i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+        const uint32_t hi = (s.v[2 * j + 1][i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+        const int row = c8 + i;
+        *reinterpret_cast<uint32_t*>(lds + lds_off(row, k >> 3) + (k & 7)) = lo | (hi << 16);
+      }
     }
   }
 }
@@ -304,6 +334,27 @@ __global__ __launch_bounds__(NT_) void bwd_gemm(BwdParams p) {
     for (int b = 0; b < 4; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = t.k1 > t.k0 ? (t.k1 - t.k0 + TK - 1) / TK : 0;
+  auto compute = [&](const uint16_t* as, const uint16_t* bs) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8_t af[4], bfr[4];
+#pragma unroll
+      for (int mf = 0; mf < 4; ++mf)
+        af[mf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                  as + lds_off(wm * 64 + mf * 16 + fr, ks * 4 + fq)));
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf)
+        bfr[nf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                   bs + lds_off(wn * 64 + nf * 16 + fr, ks * 4 + fq)));
+#pragma unroll
+      for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf)
+          acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mf], bfr[nf], acc[mf][nf], 0, 0, 0);
+    }
+  };
+  // One K step of loads in flight: step s + 1 loads into registers while
+  // step s is multiplied out of one LDS buffer, then goes to the other one.
   Stage sa, sb;
   if (nsteps > 0) {
     load_stage<PROB, true>(p, t, t.k0, sa);
@@ -319,20 +370,7 @@ __global__ __launch_bounds__(NT_) void bwd_gemm(BwdParams p) {
       load_stage<PROB, true>(p, t, t.k0 + (s + 1) * TK, sa);
       load_stage<PROB, false>(p, t, t.k0 + (s + 1) * TK, sb);
     }
-    bf16x8_t af[4], bfr[4];
-#pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
-      af[mf] = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const u32x4_t*>(As[cur] + lds_off(wm * 64 + mf * 16 + fr, fq)));
-#pragma unroll
-    for (int nf = 0; nf < 4; ++nf)
-      bfr[nf] = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const u32x4_t*>(Bs[cur] + lds_off(wn * 64 + nf * 16 + fr, fq)));
-#pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-      for (int nf = 0; nf < 4; ++nf)
-        acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mf], bfr[nf], acc[mf][nf], 0, 0, 0);
+    compute(As[cur], Bs[cur]);
     if (more) {
       store_stage<PROB, true>(As[cur ^ 1], sa);
       store_stage<PROB, false>(Bs[cur ^ 1], sb);
@@ -426,10 +464,13 @@ __global__ __launch_bounds__(NT_) void bwd_gemm(BwdParams p) {
             if (!sh) o += static_cast<size_t>(t.e) * H * p.d;
             o[static_cast<size_t>(up ? m - H : m) * p.d + n] = v;
           } else if constexpr (PROB == PROB_DXR) {
+            // routed rows go to their (token, slot) pair's row, so that a
+            // token's k rows are adjacent for the final sum
+            const int orow = sh ? t.row0 + ir : p.perm[t.row0 + ir];
             float* o = sh ? p.dx_s : p.dxr;
-            o[static_cast<size_t>(t.row0 + ir) * p.d + n] = v;
+            o[static_cast<size_t>(orow) * p.d + n] = v;
           } else {
-            p.dw_router[static_cast<size_t>(m) * p.d + n] = v;
+            p.rpart[(static_cast<size_t>(t.e) * p.E + m) * p.d + n] = v;
           }
         }
       }
@@ -448,8 +489,9 @@ __global__ __launch_bounds__(NT_) void bwd_gemm(BwdParams p) {
           if (j >= t.nlim) continue;
           const int c = t.n0 + j;
           float v = acc[mf][nf][i];
-          for (int s = 0; s < p.k; ++s)
-            v += p.dxr[static_cast<size_t>(p.inv[tok * p.k + s]) * p.d + c];
+          const float* rows = p.dxr + static_cast<size_t>(tok) * p.k * p.d + c;
+#pragma unroll 8
+          for (int s = 0; s < p.k; ++s) v += rows[static_cast<size_t>(s) * p.d];
           if (p.dx_s != nullptr) v += p.dx_s[static_cast<size_t>(tok) * p.d + c];
           if (p.dpre != nullptr) v += dpre * bf16_to_f32(p.w_shared_gate[c]);
           p.dx[static_cast<size_t>(tok) * p.d + c] = v;
@@ -531,6 +573,16 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(BwdParams p) {
   }
 }
 
+// dw_router = the dW_r partials summed in chunk order.
+__global__ __launch_bounds__(256) void router_grad_sum_kernel(BwdParams p, int nch) {
+  const size_t n = static_cast<size_t>(p.E) * p.d;
+  const size_t i = blockIdx.x * 256ull + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int c = 0; c < nch; ++c) s += p.rpart[static_cast<size_t>(c) * n + i];
+  p.dw_router[i] = s;
+}
+
 // dw_shared_gate[c] = sum_t dpre[t] x[t, c]: column partial sums over token
 // blocks of 256, then their sum in block order.
 __global__ __launch_bounds__(256) void sgate_grad_part_kernel(BwdParams p) {
@@ -562,9 +614,11 @@ hipError_t launch_prob(const BwdParams& p, hipStream_t s) {
     const int M = PROB == PROB_DWD ? p.d : 2 * H;
     const int N = PROB == PROB_DWD ? H : p.d;
     nblk = static_cast<long long>((M + TM - 1) / TM) * ((N + TN - 1) / TN) * (p.shared ? 1 : p.E);
+  } else if constexpr (PROB == PROB_DXROUTER) {
+    nblk = static_cast<long long>((p.T + TM - 1) / TM) * ((p.d + TN - 1) / TN);
   } else {
-    const int M = PROB == PROB_DXROUTER ? p.T : p.E;
-    nblk = static_cast<long long>((M + TM - 1) / TM) * ((p.d + TN - 1) / TN);
+    nblk = static_cast<long long>((p.E + TM - 1) / TM) * ((p.d + TN - 1) / TN) *
+           ((p.T + kRouterKChunk - 1) / kRouterKChunk);
   }
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -588,8 +642,9 @@ hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s) {
 
 // The backward after the route and the dispatch: see the sequence at the
 // top of this file. p.shared selects nothing here; the shared expert's
-// products are launched with a copy whose shared flag is set.
-hipError_t launch_backward(const BwdParams& p0, hipStream_t s) {
+// products are launched with a copy whose shared flag is set. ev: null, or
+// the caller's stage events (ev[1..7] are recorded here).
+hipError_t launch_backward(const BwdParams& p0, hipStream_t s, void* const* ev) {
   BwdParams p = p0;
   p.shared = 0;
   BwdParams q = p0;
@@ -597,22 +652,36 @@ hipError_t launch_backward(const BwdParams& p0, hipStream_t s) {
   const bool has_sh = p0.hs > 0;
   hipError_t err;
 #define BWD_TRY(x) do { if ((err = (x)) != hipSuccess) return err; } while (0)
+  // ev[i]: recorded after backward stage i (ev[0] closes the route stage)
+  auto mark = [&](int i) -> hipError_t {
+    return ev == nullptr ? hipSuccess : hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), s);
+  };
   BWD_TRY(launch_prob<PROB_Z>(p, s));
   if (has_sh) BWD_TRY(launch_prob<PROB_Z>(q, s));
+  BWD_TRY(mark(1));
   BWD_TRY(launch_prob<PROB_DA>(p, s));
   if (has_sh) BWD_TRY(launch_prob<PROB_DA>(q, s));
+  BWD_TRY(mark(2));
   router_bwd_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(p);
   BWD_TRY(hipGetLastError());
+  BWD_TRY(mark(3));
   BWD_TRY(launch_prob<PROB_DWD>(p, s));
+  if (has_sh) BWD_TRY(launch_prob<PROB_DWD>(q, s));
+  BWD_TRY(mark(4));
   BWD_TRY(launch_prob<PROB_DWGU>(p, s));
+  if (has_sh) BWD_TRY(launch_prob<PROB_DWGU>(q, s));
+  BWD_TRY(mark(5));
   BWD_TRY(launch_prob<PROB_DXR>(p, s));
-  if (has_sh) {
-    BWD_TRY(launch_prob<PROB_DWD>(q, s));
-    BWD_TRY(launch_prob<PROB_DWGU>(q, s));
-    BWD_TRY(launch_prob<PROB_DXR>(q, s));
-  }
+  if (has_sh) BWD_TRY(launch_prob<PROB_DXR>(q, s));
+  BWD_TRY(mark(6));
   BWD_TRY(launch_prob<PROB_DXROUTER>(p, s));
   BWD_TRY(launch_prob<PROB_DWROUTER>(p, s));
+  {
+    const int nch = (p.T + kRouterKChunk - 1) / kRouterKChunk;
+    const size_t n = static_cast<size_t>(p.E) * p.d;
+    router_grad_sum_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(p, nch);
+    BWD_TRY(hipGetLastError());
+  }
   if (p.dpre != nullptr) {
     const int nb = (p.T + 255) / 256;
     sgate_grad_part_kernel<<<dim3((p.d + 255) / 256, nb), 256, 0, s>>>(p);
@@ -620,6 +689,7 @@ hipError_t launch_backward(const BwdParams& p0, hipStream_t s) {
     sgate_grad_final_kernel<<<(p.d + 255) / 256, 256, 0, s>>>(p, nb);
     BWD_TRY(hipGetLastError());
   }
+  BWD_TRY(mark(7));
 #undef BWD_TRY
   return hipSuccess;
 }

@@ -132,7 +132,8 @@ WsLayout ws_layout(const moe_config& c) {
 // then the logits and the backward's own buffers.
 struct BwdLayout {
   WsLayout tables;
-  size_t logits, z, gact, dz, part, dxr, z_s, gact_s, dz_s, part_s, dx_s, dlb, dpre, sg_part, end;
+  size_t logits, z, gact, dz, part, dxr, z_s, gact_s, dz_s, part_s, dx_s, dlb, dpre, sg_part, rpart,
+      end;
 };
 
 BwdLayout bwd_layout(const moe_config& c) {
@@ -164,6 +165,7 @@ BwdLayout bwd_layout(const moe_config& c) {
   B.dlb = take(T * epad * 2);
   B.dpre = take(T * 4);
   B.sg_part = take(static_cast<size_t>(ceil_div(c.T, 256)) * d * 4);
+  B.rpart = take(static_cast<size_t>(ceil_div(c.T, kBwdRouterChunk)) * static_cast<size_t>(c.E) * d * 4);
   B.end = o;
   return B;
 }
@@ -577,6 +579,12 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const 
 moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* w, const void* x,
                               const void* dout, const moe_grads* gr, void* ws, size_t ws_bytes,
                               void* stream) {
+  return moe_layer_backward_traced(cfg, w, x, dout, gr, ws, ws_bytes, nullptr, stream);
+}
+
+moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w, const void* x,
+                                     const void* dout, const moe_grads* gr, void* ws,
+                                     size_t ws_bytes, void* const* stage_events, void* stream) {
   MOE_TRY(check_cfg(cfg));
   const moe_config& c = *cfg;
   if (c.dtype != MOE_BF16 || c.expert_quant != MOE_QUANT_NONE) return MOE_ERR_UNSUPPORTED;
@@ -598,6 +606,10 @@ moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* w, const
   MOE_TRY(check_ws(c, MOE_ENTRY_LAYER_BACKWARD, ws, ws_bytes));
 
   hipStream_t s = as_stream(stream);
+  auto mark = [&](int i) -> hipError_t {
+    if (stage_events == nullptr) return hipSuccess;
+    return hipEventRecord(reinterpret_cast<hipEvent_t>(stage_events[i]), s);
+  };
   const BwdLayout B = bwd_layout(c);
   const WsLayout& L = B.tables;
   if (c.T == 0) {
@@ -629,6 +641,7 @@ moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* w, const
   float* sg = gated ? at<float>(ws, L.sgate) : nullptr;
   float* logits = at<float>(ws, B.logits);
 
+  MOE_HIP(mark(0));
   RouteParams rp{};
   rp.x = x;
   rp.w_router = w->w_router;
@@ -694,9 +707,11 @@ moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* w, const
   bp.z = at<float>(ws, B.z); bp.gact = at<uint16_t>(ws, B.gact); bp.dz = at<uint16_t>(ws, B.dz);
   bp.part = at<float>(ws, B.part); bp.dxr = at<float>(ws, B.dxr);
   bp.dlb = at<uint16_t>(ws, B.dlb);
+  bp.rpart = at<float>(ws, B.rpart);
   bp.dx = gr->dx; bp.dw_router = gr->dw_router; bp.dw_gate = gr->dw_gate; bp.dw_up = gr->dw_up;
   bp.dw_down = gr->dw_down; bp.dgates = gr->dgates; bp.dlogits = gr->dlogits;
-  MOE_HIP(launch_backward(bp, s));
+  MOE_HIP(mark(1));
+  MOE_HIP(launch_backward(bp, s, stage_events != nullptr ? stage_events + 1 : nullptr));
   return MOE_OK;
 }
 

@@ -271,15 +271,19 @@ struct BwdParams {
   uint16_t *gact, *gact_s;    // [P, h], [T, hs] gate * silu(z_g) * z_u, bf16
   uint16_t *dz, *dz_s;        // [P, 2h], [T, 2hs] pre-activation gradients, bf16
   float *part, *part_s;       // [P, 2 ceil(h/128)], [T, 2 ceil(hs/128)] dG partial sums
-  float *dxr, *dx_s;          // [P, d] routed dx rows (sorted), [T, d] shared dx, or null
+  float *dxr, *dx_s;          // [P, d] routed dx rows (pair order t * k + slot), [T, d] shared dx, or null
   uint16_t* dlb;              // [T, Epad] dlogits, bf16, zero-padded
   float* dpre;                // [T] shared gate pre-activation gradient, or null
   float* sg_part;             // [ceil(T/256), d] partial sums of dw_shared_gate
+  float* rpart;               // [ceil(T/256), E, d] partial sums of dw_router
   float *dx, *dw_router, *dw_gate, *dw_up, *dw_down;
   float *dws_gate, *dws_up, *dws_down, *dw_shared_gate;
   float *dgates, *dlogits;    // optional copies
 };
-hipError_t launch_backward(const BwdParams& p, hipStream_t s);
+hipError_t launch_backward(const BwdParams& p, hipStream_t s, void* const* ev);
+// Tokens per partial sum of dW_r in the backward (the workspace holds
+// ceil(T / kBwdRouterChunk) partial [E, d] slabs).
+constexpr int kBwdRouterChunk = 256;
 // n float zeros at p (a fill kernel, not a memset: safe under graph capture).
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 

@@ -30,9 +30,9 @@ class StageEvents:
     """steps x (MOE_NUM_STAGES + 1) events; row i is passed to the traced
     layer call of step i."""
 
-    def __init__(self, steps: int):
+    def __init__(self, steps: int, stages: int = None):
         self.hip = _hip()
-        self.n = B.MOE_NUM_STAGES + 1
+        self.n = (B.MOE_NUM_STAGES if stages is None else stages) + 1
         self.rows = []
         for _ in range(steps):
             arr = (ctypes.c_void_p * self.n)()

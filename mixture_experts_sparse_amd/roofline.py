@@ -99,3 +99,18 @@ def batch1_decode_ceiling(total_params, active_params, bytes_per_param, mem_gb_s
 
 def ridge_flop_per_byte(peak_flops=PEAK_BF16_MFMA_FLOPS, peak_bytes=PEAK_HBM_BYTES):
     return peak_flops / peak_bytes
+
+
+def backward_stage_flops(T, d, E, h, k, hs=0, shared_gate=False):
+    """FLOPs of each stage of the layer backward (the products it runs,
+    the recomputed gate/up pre-activations included): z = 4 P d h, the
+    hidden-unit gradient 2 P d h, dW_down 2 P d h, dW_gate|up 4 P d h, the dx
+    rows 4 P d h (each + the shared expert's on T rows), the router's two
+    products 4 T d E."""
+    P = T * k
+    return {"route": 2.0 * T * d * E, "z": 4.0 * P * d * h + 4.0 * T * d * hs,
+            "d_hidden": 2.0 * P * d * h + 2.0 * T * d * hs, "router_grad": 0.0,
+            "dw_down": 2.0 * P * d * h + 2.0 * T * d * hs,
+            "dw_gate_up": 4.0 * P * d * h + 4.0 * T * d * hs,
+            "dx_rows": 4.0 * P * d * h + 4.0 * T * d * hs,
+            "dx_router": 4.0 * T * d * E + (4.0 * T * d if shared_gate else 0.0)}

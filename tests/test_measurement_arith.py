@@ -54,3 +54,18 @@ def test_workload_counts():
     # decode: 12,582,912 bytes per expert
     assert 3 * 2048 * 1024 * 2 == 12_582_912
     assert abs(R.ridge_flop_per_byte() - 312.5) < 1e-9
+
+
+def test_backward_stage_flops_add_up():
+    """The backward's products: the recomputed gate/up pre-activations (the
+    forward's gate/up FLOPs), then twice the forward's expert FLOPs (the
+    gradients into the inputs and into the weights), and the router's two
+    products; counted independently of the per-stage split."""
+    T, d, E, h, k, hs = 300, 200, 16, 136, 4, 96
+    P = T * k
+    st = R.backward_stage_flops(T, d, E, h, k, hs, True)
+    fwd_experts = 6.0 * P * d * h + 6.0 * T * d * hs
+    recompute = R.gate_up_flops(P, d, h, T, hs)
+    expect = 2.0 * T * d * E + recompute + 2.0 * fwd_experts + 2 * (2.0 * T * d * E) + 4.0 * T * d
+    assert abs(sum(st.values()) - expect) <= 1e-9 * expect
+    assert st["router_grad"] == 0.0
