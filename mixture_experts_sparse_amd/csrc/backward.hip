@@ -25,13 +25,14 @@
 //
 // Every product is one kernel, bwd_gemm<PROB>: 128 x 128 output tiles per
 // 256-thread workgroup (4 waves of 64 x 64 on v_mfma_f32_16x16x32_bf16), K in
-// steps of 32 staged through two LDS buffers by ordinary loads into registers
-// (issued before the current step's MFMAs, written to LDS after them). An
-// operand stored with K contiguous goes to LDS with 16-byte writes; one stored
-// with K as its row index (the weight gradients, and the weights read along
-// their output dimension) is loaded two K rows at a time and written as
-// 32-bit (k, k+1) pairs, which transposes it on the way into LDS. Everything
-// out of range loads as zero.
+// 32-deep stages streamed by direct global->LDS loads through a ring of S
+// stages. An operand stored with K contiguous is read out of LDS with 16-byte
+// reads; one stored with K as its row index (the weight gradients reduce
+// over rows; the weights are read along their output dimension for the
+// input gradients) lands as it is stored and is transposed by the fragment
+// reads themselves (ds_read_b64_tr_b16). The routed rows of x and dO are
+// gathered into sorted order once (gather_rows_kernel), so no product looks
+// up an index.
 
 #include "device_common.h"
 #include "moe_internal.h"
@@ -42,9 +43,11 @@ namespace {
 
 constexpr int NT_ = 256;  // threads per workgroup
 constexpr int TM = 128, TN = 128, TK = 32;
-constexpr int KS = TK / 32;                 // MFMA K steps per stage
 constexpr int CH = TM * TK / 8 / NT_;       // 16-byte chunks per thread per operand and stage
-static_assert(TM == TN && CH % 2 == 0, "square tiles, whole chunk pairs");
+constexpr int S = 3;                        // LDS stages
+constexpr int LPS = 2 * CH;                 // DMA loads per thread per stage
+static_assert(TM == TN && CH == 2, "the chunk mappings assume 128 x 32 stages");
+static_assert((S - 2) * LPS < 64, "vmcnt range");
 constexpr int kRouterKChunk = kBwdRouterChunk;  // tokens per partial of dW_r
 
 enum : int {
@@ -71,20 +74,6 @@ struct Tile {
   int row0;        // first sorted row (routed row tiles) or first token
   int k0, k1;      // K range (stored-row indices for K-as-row operands)
 };
-
-// LDS tile: TM rows of TK bf16 (TK / 8 chunks of 16 bytes, swizzled so the
-// 8 rows LDS serves together read 8 distinct bank groups).
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  if constexpr (TK == 64) return row * TK + ((chunk ^ (row & 7)) << 3);
-  else return row * TK + ((chunk ^ ((row >> 1) & 3)) << 3);
-}
-
-__device__ __forceinline__ u32x4_t ld16(const uint16_t* p, bool ok) {
-  return ok ? *reinterpret_cast<const u32x4_t*>(p) : u32x4_t{0u, 0u, 0u, 0u};
-}
-
-// Row of the shared or routed expert's token for sorted row r.
-__device__ __forceinline__ int tok_of(const BwdParams& p, int r) { return p.perm[r] / p.k; }
 
 template <int PROB>
 __device__ bool decode(const BwdParams& p, Tile& t) {
@@ -164,144 +153,167 @@ __device__ bool decode(const BwdParams& p, Tile& t) {
 }
 
 // ---- operand addressing --------------------------------------------------
-// K-contiguous operands: pointer to the 16-byte chunk (row i of the tile,
-// K index k) or null when out of range. K-as-row operands: pointer to the
-// chunk (K index k, tile column c .. c + 7) or null.
+// Every address is clamped in bounds (loads past a range reread valid data);
+// the A operand's K tail is zeroed in LDS after it lands, so the products
+// past K vanish, and rows or columns past M or N are never stored. Routed
+// token rows come pre-gathered in sorted order (xs, dos), so no operand
+// needs an index lookup.
+//
+// K-contiguous operands: the 16-byte chunk at tile row i, K index k.
+// K-as-row operands: the chunk at K index k, tile columns c .. c + 7.
 
 template <int PROB>
-__device__ __forceinline__ const uint16_t* a_chunk(const BwdParams& p, const Tile& t, int i, int k) {
+__device__ __forceinline__ const uint16_t* a_src(const BwdParams& p, const Tile& t, int i, int k) {
   const bool sh = p.shared;
   const int H = sh ? p.hs : p.h;
-  if constexpr (PROB == PROB_Z || PROB == PROB_DA) {
-    if (i >= t.mlim || k >= t.k1) return nullptr;
-    const int r = t.row0 + i;
-    const int tok = sh ? r : tok_of(p, r);
-    const uint16_t* base = PROB == PROB_Z ? p.x : p.dout;
-    return base + static_cast<size_t>(tok) * p.d + k;
-  } else if constexpr (PROB == PROB_DXR) {
-    if (i >= t.mlim || k >= t.k1) return nullptr;
-    const uint16_t* dz = sh ? p.dz_s : p.dz;
-    return dz + static_cast<size_t>(t.row0 + i) * (2 * H) + k;
-  } else if constexpr (PROB == PROB_DXROUTER) {
-    if (i >= t.mlim || k >= t.k1) return nullptr;
-    return p.dlb + static_cast<size_t>(t.row0 + i) * p.Epad + k;
-  } else if constexpr (PROB == PROB_DWD) {
-    // stored rows: sorted rows (routed) or tokens (shared); columns: d
-    if (k >= t.k1 || i >= t.mlim) return nullptr;
-    const int tok = sh ? k : tok_of(p, k);
-    return p.dout + static_cast<size_t>(tok) * p.d + t.m0 + i;
-  } else if constexpr (PROB == PROB_DWGU) {
-    if (k >= t.k1 || i >= t.mlim) return nullptr;
-    const uint16_t* dz = sh ? p.dz_s : p.dz;
-    return dz + static_cast<size_t>(k) * (2 * H) + t.m0 + i;
-  } else {  // PROB_DWROUTER: stored rows tokens, columns experts (padded)
-    if (k >= t.k1 || i >= t.mlim) return nullptr;
-    return p.dlb + static_cast<size_t>(k) * p.Epad + t.m0 + i;
+  if constexpr (a_kcontig<PROB>()) {
+    const int r = t.row0 + (i < t.mlim ? i : 0);
+    const int kk = min(k, t.k1 - 8);
+    if constexpr (PROB == PROB_Z || PROB == PROB_DA) {
+      const uint16_t* base = PROB == PROB_Z ? (sh ? p.x : p.xs) : (sh ? p.dout : p.dos);
+      return base + static_cast<size_t>(r) * p.d + kk;
+    } else if constexpr (PROB == PROB_DXR) {
+      return (sh ? p.dz_s : p.dz) + static_cast<size_t>(r) * (2 * H) + kk;
+    } else {  // PROB_DXROUTER
+      return p.dlb + static_cast<size_t>(r) * p.Epad + kk;
+    }
+  } else {
+    const int kk = min(k, t.k1 - 1);
+    const int c = t.m0 + (i < t.mlim ? i : 0);
+    if constexpr (PROB == PROB_DWD) {
+      return (sh ? p.dout : p.dos) + static_cast<size_t>(kk) * p.d + c;
+    } else if constexpr (PROB == PROB_DWGU) {
+      return (sh ? p.dz_s : p.dz) + static_cast<size_t>(kk) * (2 * H) + c;
+    } else {  // PROB_DWROUTER: stored rows tokens, columns experts (padded)
+      return p.dlb + static_cast<size_t>(kk) * p.Epad + c;
+    }
   }
 }
 
 template <int PROB>
-__device__ __forceinline__ const uint16_t* b_chunk(const BwdParams& p, const Tile& t, int j, int k) {
+__device__ __forceinline__ const uint16_t* b_src(const BwdParams& p, const Tile& t, int j, int k) {
   const bool sh = p.shared;
   const int H = sh ? p.hs : p.h;
   if constexpr (PROB == PROB_Z) {
     // tile column j -> hidden unit and projection: 64 hidden units per tile,
     // wave half w = j / 64 takes 32 of them, gate then up
-    if (k >= t.k1) return nullptr;
     const int w = j >> 6, c = j & 63;
-    const int hu = (t.n0 >> 1) + w * 32 + (c & 31);
-    if (hu >= H) return nullptr;
+    const int hu = min((t.n0 >> 1) + w * 32 + (c & 31), H - 1);
     const uint16_t* W = c < 32 ? (sh ? p.ws_gate : p.w_gate) : (sh ? p.ws_up : p.w_up);
     const size_t eoff = sh ? 0 : static_cast<size_t>(t.e) * H * p.d;
-    return W + eoff + static_cast<size_t>(hu) * p.d + k;
-  } else if constexpr (PROB == PROB_DA) {
-    // W_d [d, H]: stored rows k (model dim), columns hidden units
-    if (k >= t.k1 || j >= t.nlim) return nullptr;
-    const uint16_t* W = sh ? p.ws_down : p.w_down;
-    const size_t eoff = sh ? 0 : static_cast<size_t>(t.e) * p.d * H;
-    return W + eoff + static_cast<size_t>(k) * H + t.n0 + j;
-  } else if constexpr (PROB == PROB_DWD) {
-    // g a rows: stored rows sorted rows / tokens, columns hidden units
-    if (k >= t.k1 || j >= t.nlim) return nullptr;
-    const uint16_t* ga = sh ? p.gact_s : p.gact;
-    return ga + static_cast<size_t>(k) * H + t.n0 + j;
-  } else if constexpr (PROB == PROB_DWGU || PROB == PROB_DWROUTER) {
-    if (k >= t.k1 || j >= t.nlim) return nullptr;
-    const int tok = (PROB == PROB_DWROUTER || sh) ? k : tok_of(p, k);
-    return p.x + static_cast<size_t>(tok) * p.d + t.n0 + j;
-  } else if constexpr (PROB == PROB_DXR) {
-    // [W_g; W_u] rows k (2H of them), columns model dim
-    if (k >= t.k1 || j >= t.nlim) return nullptr;
-    const bool up = k >= H;
-    const uint16_t* W = up ? (sh ? p.ws_up : p.w_up) : (sh ? p.ws_gate : p.w_gate);
-    const size_t eoff = sh ? 0 : static_cast<size_t>(t.e) * H * p.d;
-    return W + eoff + static_cast<size_t>(up ? k - H : k) * p.d + t.n0 + j;
-  } else {  // PROB_DXROUTER: W_r rows (experts), columns model dim
-    if (k >= p.E || j >= t.nlim) return nullptr;
-    return p.w_router + static_cast<size_t>(k) * p.d + t.n0 + j;
-  }
-}
-
-// Staging of one K step into registers and from there into LDS.
-// K-contiguous: thread q loads chunks q + 256 i (i < CH) of the TM x TK/8
-// chunk tile. K-as-row: thread q loads K rows 2 (q % 16 + 16 j) and the next
-// one (j < CH / 2) at tile columns 8 (q / 16) .. + 7, and writes them as 8
-// (k, k + 1) pairs each.
-struct Stage {
-  u32x4_t v[CH];
-};
-
-template <int PROB, bool A>
-__device__ __forceinline__ void load_stage(const BwdParams& p, const Tile& t, int kbase, Stage& s) {
-  const int tid = threadIdx.x;
-  constexpr bool KC = A ? a_kcontig<PROB>() : b_kcontig<PROB>();
-  constexpr int CPR = TK / 8;
-  if constexpr (KC) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int q = tid + i * NT_;
-      const uint16_t* ptr = A ? a_chunk<PROB>(p, t, q / CPR, kbase + (q % CPR) * 8)
-                              : b_chunk<PROB>(p, t, q / CPR, kbase + (q % CPR) * 8);
-      s.v[i] = ld16(ptr, ptr != nullptr);
-    }
+    return W + eoff + static_cast<size_t>(hu) * p.d + min(k, t.k1 - 8);
   } else {
-    const int c8 = (tid >> 4) * 8;
-#pragma unroll
-    for (int j = 0; j < CH / 2; ++j) {
-      const int k = kbase + 2 * ((tid & 15) + 16 * j);
-      const uint16_t* p0 = A ? a_chunk<PROB>(p, t, c8, k) : b_chunk<PROB>(p, t, c8, k);
-      const uint16_t* p1 = A ? a_chunk<PROB>(p, t, c8, k + 1) : b_chunk<PROB>(p, t, c8, k + 1);
-      s.v[2 * j] = ld16(p0, p0 != nullptr);
-      s.v[2 * j + 1] = ld16(p1, p1 != nullptr);
+    const int n = t.n0 + (j < t.nlim ? j : 0);
+    if constexpr (PROB == PROB_DA) {
+      // W_d [d, H]: stored rows k (model dim), columns hidden units
+      const uint16_t* W = sh ? p.ws_down : p.w_down;
+      const size_t eoff = sh ? 0 : static_cast<size_t>(t.e) * p.d * H;
+      return W + eoff + static_cast<size_t>(min(k, t.k1 - 1)) * H + n;
+    } else if constexpr (PROB == PROB_DWD) {
+      // g a rows: stored rows sorted rows / tokens, columns hidden units
+      return (sh ? p.gact_s : p.gact) + static_cast<size_t>(min(k, t.k1 - 1)) * H + n;
+    } else if constexpr (PROB == PROB_DWGU) {
+      return (sh ? p.x : p.xs) + static_cast<size_t>(min(k, t.k1 - 1)) * p.d + n;
+    } else if constexpr (PROB == PROB_DWROUTER) {
+      return p.x + static_cast<size_t>(min(k, t.k1 - 1)) * p.d + n;
+    } else if constexpr (PROB == PROB_DXR) {
+      // [W_g; W_u] rows k (2H of them), columns model dim
+      const int kk = min(k, t.k1 - 1);
+      const bool up = kk >= H;
+      const uint16_t* W = up ? (sh ? p.ws_up : p.w_up) : (sh ? p.ws_gate : p.w_gate);
+      const size_t eoff = sh ? 0 : static_cast<size_t>(t.e) * H * p.d;
+      return W + eoff + static_cast<size_t>(up ? kk - H : kk) * p.d + n;
+    } else {  // PROB_DXROUTER: W_r rows (experts; the padded ones reread row E - 1)
+      return p.w_router + static_cast<size_t>(min(k, p.E - 1)) * p.d + n;
     }
   }
 }
 
+// LDS stage: A then B, TM x TK each. K-contiguous operand: row i (M or N
+// index) holds 4 chunks of 8 K values, chunk c at physical position
+// c ^ ((i >> 1) & 3). K-as-row operand: row k holds 16 chunks of 8 M (or N)
+// values, chunk c at physical position c ^ kr_swz(k); the fragment reads
+// then transpose it (ds_read_b64_tr_b16), two reads of four K values per lane.
+constexpr int SEL = (TM + TN) * TK;  // bf16 per stage
+__device__ __forceinline__ int kr_swz(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
+
+// LDS destination of a DMA, hidden from the compiler's load-counter
+// tracking: every wait on the ring is explicit and followed by a barrier.
+__device__ __forceinline__ lds_void_t* lds_untracked(uint16_t* q) {
+  lds_void_t* r = (lds_void_t*)q;
+  asm volatile("" : "+s"(r));
+  return r;
+}
+
+// Two 16-byte DMA loads per thread per operand and stage: slot q = tid and
+// tid + 256 of the stage's 512 chunks.
 template <int PROB, bool A>
-__device__ __forceinline__ void store_stage(uint16_t* lds, const Stage& s) {
+__device__ __forceinline__ void issue_op(const BwdParams& p, const Tile& t, int kbase, uint16_t* st) {
   const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr bool KC = A ? a_kcontig<PROB>() : b_kcontig<PROB>();
-  constexpr int CPR = TK / 8;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int q = i * NT_ + tid;
+    const uint16_t* src;
+    if constexpr (KC) {
+      const int row = q >> 2, c = (q & 3) ^ ((row >> 1) & 3);
+      src = A ? a_src<PROB>(p, t, row, kbase + 8 * c) : b_src<PROB>(p, t, row, kbase + 8 * c);
+    } else {
+      const int kr = q >> 4, c = (q & 15) ^ kr_swz(kr);
+      src = A ? a_src<PROB>(p, t, 8 * c, kbase + kr) : b_src<PROB>(p, t, 8 * c, kbase + kr);
+    }
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)src, lds_untracked(st + (i * NT_ + wave * 64) * 8),
+                                     16, 0, 0);
+  }
+}
+
+// The A operand's K positions at or past k1 in the stage of K base kbase:
+// zeroed (this thread's two chunks).
+template <int PROB>
+__device__ __forceinline__ void zero_a_tail(const Tile& t, int kbase, uint16_t* st) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int q = i * NT_ + tid;
+    bool past;
+    if constexpr (a_kcontig<PROB>()) {
+      const int row = q >> 2, c = (q & 3) ^ ((row >> 1) & 3);
+      past = kbase + 8 * c >= t.k1;
+    } else {
+      past = kbase + (q >> 4) >= t.k1;
+    }
+    if (past) *reinterpret_cast<u32x4_t*>(st + q * 8) = u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// MFMA operand (16 rows or columns x 32 K, lane l: row l % 16, K values
+// 8 (l / 16) .. + 7) of the 16 rows starting at r0.
+template <bool KC>
+__device__ __forceinline__ bf16x8_t frag(const uint16_t* op, int r0) {
+  const int lane = threadIdx.x & 63;
   if constexpr (KC) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int q = tid + i * NT_;
-      *reinterpret_cast<u32x4_t*>(lds + lds_off(q / CPR, q % CPR)) = s.v[i];
-    }
+    const int row = r0 + (lane & 15), c = lane >> 4;
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                            op + row * TK + ((c ^ ((row >> 1) & 3)) << 3)));
   } else {
-    const int c8 = (tid >> 4) * 8;
+    // transposing reads: in each group of 16 lanes, lane 4 q + r supplies
+    // K row 8 g + 4 h + q at columns r0 + 4 r .. + 3, and lane j receives
+    // column r0 + j of K rows 8 g + 4 h .. + 3
+    const int g = lane >> 4, q = (lane >> 2) & 3, r = lane & 3;
+    const int col = r0 + 4 * r;
+    v4i16_t v[2];
 #pragma unroll
-    for (int j = 0; j < CH / 2; ++j) {
-      const int k = 2 * ((tid & 15) + 16 * j);  // even: the pair is one aligned 32-bit word
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // element i of each chunk: bf16 i of the 16 bytes
-        const uint32_t lo = (s.v[2 * j][i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-        const uint32_t hi = (s.v[2 * j + 1][i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-        const int row = c8 + i;
-        *reinterpret_cast<uint32_t*>(lds + lds_off(row, k >> 3) + (k & 7)) = lo | (hi << 16);
-      }
+    for (int h = 0; h < 2; ++h) {
+      const int k = 8 * g + 4 * h + q;
+      const int e = k * TM + (((col >> 3) ^ kr_swz(k)) << 3) + (col & 7);
+      v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(op + e));
     }
+    struct { v4i16_t lo, hi; } pair = {v[0], v[1]};
+    return __builtin_bit_cast(bf16x8_t, pair);
   }
 }
 
@@ -318,18 +330,15 @@ __device__ __forceinline__ float silu_grad_f32(float z) {
   return s * (1.0f + z * (1.0f - s));
 }
 
-// Four workgroups per CU where the product fits 128 VGPRs without spilling
-// (measured: the z and dx-row products gain 10-15%); the hidden-unit
-// gradient and the final dx, whose epilogues need more, keep three.
+// Three workgroups per CU (the 48 KB stage ring of each).
 template <int PROB>
-constexpr int bwd_occupancy() { return PROB == PROB_DA || PROB == PROB_DXROUTER ? 3 : 4; }
+constexpr int bwd_occupancy() { return 3; }
 
 template <int PROB>
 __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams p) {
   Tile t;
   if (!decode<PROB>(p, t)) return;
-  __shared__ __align__(16) uint16_t As[2][TM * TK];
-  __shared__ __align__(16) uint16_t Bs[2][TN * TK];
+  __shared__ __align__(16) uint16_t Ring[S * SEL];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int fr = lane & 15, fq = lane >> 4;
@@ -340,49 +349,44 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
     for (int b = 0; b < 4; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = t.k1 > t.k0 ? (t.k1 - t.k0 + TK - 1) / TK : 0;
-  auto compute = [&](const uint16_t* as, const uint16_t* bs) {
+  const bool ktail = ((t.k1 - t.k0) % TK) != 0;
+  auto issue = [&](uint16_t* st, int kb) {
+    issue_op<PROB, true>(p, t, kb, st);
+    issue_op<PROB, false>(p, t, kb, st + TM * TK);
+  };
+  // S stages of DMA in flight ahead of the MFMAs; every thread issues LPS
+  // loads per stage (clamped past the end), so each wave's count of
+  // outstanding loads is uniform and one vmcnt wait covers a stage.
+  if (nsteps > 0) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8_t af[4], bfr[4];
+    for (int st = 0; st < S - 1; ++st) issue(Ring + st * SEL, t.k0 + st * TK);
+  }
+  int cur = 0, nxt = S - 1;
+  for (int s = 0; s < nsteps; ++s) {
+    wait_stage<(S - 2) * LPS>();
+    stage_barrier();
+    issue(Ring + nxt * SEL, t.k0 + (s + S - 1) * TK);
+    nxt = nxt + 1 == S ? 0 : nxt + 1;
+    uint16_t* st = Ring + cur * SEL;
+    cur = cur + 1 == S ? 0 : cur + 1;
+    if (ktail && s == nsteps - 1) {
+      zero_a_tail<PROB>(t, t.k0 + s * TK, st);
+      wait_stage<63>();
+      stage_barrier();
+    }
+    bf16x8_t af[4], bfr[4];
 #pragma unroll
-      for (int mf = 0; mf < 4; ++mf)
-        af[mf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
-                                                  as + lds_off(wm * 64 + mf * 16 + fr, ks * 4 + fq)));
+    for (int mf = 0; mf < 4; ++mf) af[mf] = frag<a_kcontig<PROB>()>(st, wm * 64 + mf * 16);
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) bfr[nf] = frag<b_kcontig<PROB>()>(st + TM * TK, wn * 64 + nf * 16);
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
       for (int nf = 0; nf < 4; ++nf)
-        bfr[nf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
-                                                   bs + lds_off(wn * 64 + nf * 16 + fr, ks * 4 + fq)));
-#pragma unroll
-      for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf)
-          acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mf], bfr[nf], acc[mf][nf], 0, 0, 0);
-    }
-  };
-  // One K step of loads in flight: step s + 1 loads into registers while
-  // step s is multiplied out of one LDS buffer, then goes to the other one.
-  Stage sa, sb;
-  if (nsteps > 0) {
-    load_stage<PROB, true>(p, t, t.k0, sa);
-    load_stage<PROB, false>(p, t, t.k0, sb);
-    store_stage<PROB, true>(As[0], sa);
-    store_stage<PROB, false>(Bs[0], sb);
+        acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mf], bfr[nf], acc[mf][nf], 0, 0, 0);
   }
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int cur = s & 1;
-    const bool more = s + 1 < nsteps;
-    if (more) {
-      load_stage<PROB, true>(p, t, t.k0 + (s + 1) * TK, sa);
-      load_stage<PROB, false>(p, t, t.k0 + (s + 1) * TK, sb);
-    }
-    compute(As[cur], Bs[cur]);
-    if (more) {
-      store_stage<PROB, true>(As[cur ^ 1], sa);
-      store_stage<PROB, false>(Bs[cur ^ 1], sb);
-    }
-    __syncthreads();
-  }
+  // the clamped loads past the last stage land before the workgroup's LDS goes
+  __builtin_amdgcn_s_waitcnt(0);
 
   // ---- epilogues: acc[mf][nf][i] is tile row wm*64 + mf*16 + fq*4 + i,
   // tile column wn*64 + nf*16 + fr ----
@@ -634,6 +638,20 @@ hipError_t launch_prob(const BwdParams& p, hipStream_t s) {
 
 }  // namespace
 
+// Sorted copies of the routed rows: xs[r] = x[t], dos[r] = dO[t] for sorted
+// row r of pair perm[r] = t k + slot (16 bytes per thread).
+__global__ __launch_bounds__(256) void gather_rows_kernel(BwdParams p) {
+  const int cpr = p.d / 8;
+  const size_t i = blockIdx.x * 256ull + threadIdx.x;
+  const size_t P = static_cast<size_t>(p.T) * p.k;
+  if (i >= P * cpr) return;
+  const size_t r = i / cpr;
+  const int c = static_cast<int>(i - r * cpr) * 8;
+  const size_t t = static_cast<size_t>(p.perm[r] / p.k);
+  *reinterpret_cast<u32x4_t*>(p.xs + r * p.d + c) = *reinterpret_cast<const u32x4_t*>(p.x + t * p.d + c);
+  *reinterpret_cast<u32x4_t*>(p.dos + r * p.d + c) = *reinterpret_cast<const u32x4_t*>(p.dout + t * p.d + c);
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, size_t n) {
   for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n; i += static_cast<size_t>(gridDim.x) * 256)
     p[i] = 0.f;
@@ -662,6 +680,11 @@ hipError_t launch_backward(const BwdParams& p0, hipStream_t s, void* const* ev) 
   auto mark = [&](int i) -> hipError_t {
     return ev == nullptr ? hipSuccess : hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), s);
   };
+  {
+    const size_t n = static_cast<size_t>(p.T) * p.k * (p.d / 8);
+    gather_rows_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(p);
+    BWD_TRY(hipGetLastError());
+  }
   BWD_TRY(launch_prob<PROB_Z>(p, s));
   if (has_sh) BWD_TRY(launch_prob<PROB_Z>(q, s));
   BWD_TRY(mark(1));
