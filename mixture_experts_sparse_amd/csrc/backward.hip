@@ -30,9 +30,10 @@
 // reads; one stored with K as its row index (the weight gradients reduce
 // over rows; the weights are read along their output dimension for the
 // input gradients) lands as it is stored and is transposed by the fragment
-// reads themselves (ds_read_b64_tr_b16). The routed rows of x and dO are
-// gathered into sorted order once (gather_rows_kernel), so no product looks
-// up an index.
+// reads themselves (ds_read_b64_tr_b16). Routed rows of x and dO are read
+// through their token (rtok[r] = perm[r] / k, one small kernel): once per
+// tile where the rows are the output rows, and by scalar loads one stage
+// ahead where they are the reduction (the weight gradients).
 
 #include "device_common.h"
 #include "moe_internal.h"
@@ -156,8 +157,8 @@ __device__ bool decode(const BwdParams& p, Tile& t) {
 // Every address is clamped in bounds (loads past a range reread valid data);
 // the A operand's K tail is zeroed in LDS after it lands, so the products
 // past K vanish, and rows or columns past M or N are never stored. Routed
-// token rows come pre-gathered in sorted order (xs, dos), so no operand
-// needs an index lookup.
+// token rows (x, dO) are addressed by issue_op from the tokens it is given;
+// a_src / b_src serve every other operand and the shared expert's.
 //
 // K-contiguous operands: the 16-byte chunk at tile row i, K index k.
 // K-as-row operands: the chunk at K index k, tile columns c .. c + 7.
@@ -169,10 +170,7 @@ __device__ __forceinline__ const uint16_t* a_src(const BwdParams& p, const Tile&
   if constexpr (a_kcontig<PROB>()) {
     const int r = t.row0 + (i < t.mlim ? i : 0);
     const int kk = min(k, t.k1 - 8);
-    if constexpr (PROB == PROB_Z || PROB == PROB_DA) {
-      const uint16_t* base = PROB == PROB_Z ? (sh ? p.x : p.xs) : (sh ? p.dout : p.dos);
-      return base + static_cast<size_t>(r) * p.d + kk;
-    } else if constexpr (PROB == PROB_DXR) {
+    if constexpr (PROB == PROB_DXR) {
       return (sh ? p.dz_s : p.dz) + static_cast<size_t>(r) * (2 * H) + kk;
     } else {  // PROB_DXROUTER
       return p.dlb + static_cast<size_t>(r) * p.Epad + kk;
@@ -181,7 +179,7 @@ __device__ __forceinline__ const uint16_t* a_src(const BwdParams& p, const Tile&
     const int kk = min(k, t.k1 - 1);
     const int c = t.m0 + (i < t.mlim ? i : 0);
     if constexpr (PROB == PROB_DWD) {
-      return (sh ? p.dout : p.dos) + static_cast<size_t>(kk) * p.d + c;
+      return p.dout + static_cast<size_t>(kk) * p.d + c;  // shared: rows are tokens
     } else if constexpr (PROB == PROB_DWGU) {
       return (sh ? p.dz_s : p.dz) + static_cast<size_t>(kk) * (2 * H) + c;
     } else {  // PROB_DWROUTER: stored rows tokens, columns experts (padded)
@@ -213,7 +211,7 @@ __device__ __forceinline__ const uint16_t* b_src(const BwdParams& p, const Tile&
       // g a rows: stored rows sorted rows / tokens, columns hidden units
       return (sh ? p.gact_s : p.gact) + static_cast<size_t>(min(k, t.k1 - 1)) * H + n;
     } else if constexpr (PROB == PROB_DWGU) {
-      return (sh ? p.x : p.xs) + static_cast<size_t>(min(k, t.k1 - 1)) * p.d + n;
+      return p.x + static_cast<size_t>(min(k, t.k1 - 1)) * p.d + n;  // shared: rows are tokens
     } else if constexpr (PROB == PROB_DWROUTER) {
       return p.x + static_cast<size_t>(min(k, t.k1 - 1)) * p.d + n;
     } else if constexpr (PROB == PROB_DXR) {
@@ -245,10 +243,43 @@ __device__ __forceinline__ lds_void_t* lds_untracked(uint16_t* q) {
   return r;
 }
 
+// Products whose operand rows are routed token rows of x or dO: z and the
+// hidden-unit gradient (A rows = output rows, fixed per tile), and dW_down
+// (A) and dW_gate|up (B), whose K index is the sorted row.
+template <int PROB> constexpr bool tok_out_rows() { return PROB == PROB_Z || PROB == PROB_DA; }
+template <int PROB> constexpr bool tok_k_rows() { return PROB == PROB_DWD || PROB == PROB_DWGU; }
+
+// Tokens of the 8 sorted rows this wave's lanes load in the stage at K base
+// kb (rows kb + 16 i + 4 wave + j), clamped into the expert's range. The
+// addresses are wave-uniform: scalar loads, waited by the next stage wait.
+typedef int int4v_t __attribute__((ext_vector_type(4)));
+struct StageToks {
+  int4v_t lo, hi;  // rows kb + 4 wave + j and kb + 16 + 4 wave + j, j = 0..3
+};
+
+template <int PROB>
+__device__ __forceinline__ void load_toks(const BwdParams& p, const Tile& t, int kb, StageToks& tk) {
+  if constexpr (tok_k_rows<PROB>()) {
+    if (!p.shared) {
+      const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      typedef __attribute__((address_space(4))) const int const_int_t;
+      const const_int_t* rt = (const const_int_t*)p.rtok;
+      const int r0 = kb + 4 * w, last = t.k1 - 1;
+      tk.lo = int4v_t{rt[min(r0, last)], rt[min(r0 + 1, last)], rt[min(r0 + 2, last)],
+                      rt[min(r0 + 3, last)]};
+      tk.hi = int4v_t{rt[min(r0 + 16, last)], rt[min(r0 + 17, last)], rt[min(r0 + 18, last)],
+                      rt[min(r0 + 19, last)]};
+    }
+  }
+}
+
 // Two 16-byte DMA loads per thread per operand and stage: slot q = tid and
-// tid + 256 of the stage's 512 chunks.
+// tid + 256 of the stage's 512 chunks. arow: this thread's two A rows (token
+// rows of x or dO) of z and the hidden-unit gradient; tk: the stage's tokens
+// of dW_down and dW_gate|up (routed experts).
 template <int PROB, bool A>
-__device__ __forceinline__ void issue_op(const BwdParams& p, const Tile& t, int kbase, uint16_t* st) {
+__device__ __forceinline__ void issue_op(const BwdParams& p, const Tile& t, int kbase, uint16_t* st,
+                                         const uint16_t* const (&arow)[CH], const StageToks& tk) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr bool KC = A ? a_kcontig<PROB>() : b_kcontig<PROB>();
@@ -258,10 +289,24 @@ __device__ __forceinline__ void issue_op(const BwdParams& p, const Tile& t, int 
     const uint16_t* src;
     if constexpr (KC) {
       const int row = q >> 2, c = (q & 3) ^ ((row >> 1) & 3);
-      src = A ? a_src<PROB>(p, t, row, kbase + 8 * c) : b_src<PROB>(p, t, row, kbase + 8 * c);
+      if constexpr (A && tok_out_rows<PROB>())
+        src = arow[i] + min(kbase + 8 * c, t.k1 - 8);
+      else
+        src = A ? a_src<PROB>(p, t, row, kbase + 8 * c) : b_src<PROB>(p, t, row, kbase + 8 * c);
     } else {
       const int kr = q >> 4, c = (q & 15) ^ kr_swz(kr);
-      src = A ? a_src<PROB>(p, t, 8 * c, kbase + kr) : b_src<PROB>(p, t, 8 * c, kbase + kr);
+      constexpr bool tok_op = tok_k_rows<PROB>() && (A == (PROB == PROB_DWD));
+      if (tok_op && !p.shared) {
+        // lane's row kr = 16 i + 4 wave + j
+        const int jj = (tid >> 4) & 3;
+        const int4v_t v = i == 0 ? tk.lo : tk.hi;
+        const int t01 = (jj & 1) ? v.y : v.x, t23 = (jj & 1) ? v.w : v.z;
+        const int tok = (jj & 2) ? t23 : t01;
+        const int col = A ? t.m0 + (8 * c < t.mlim ? 8 * c : 0) : t.n0 + (8 * c < t.nlim ? 8 * c : 0);
+        src = (PROB == PROB_DWD ? p.dout : p.x) + static_cast<size_t>(tok) * p.d + col;
+      } else {
+        src = A ? a_src<PROB>(p, t, 8 * c, kbase + kr) : b_src<PROB>(p, t, 8 * c, kbase + kr);
+      }
     }
     __builtin_amdgcn_global_load_lds((gbl_void_t*)src, lds_untracked(st + (i * NT_ + wave * 64) * 8),
                                      16, 0, 0);
@@ -350,22 +395,39 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
 
   const int nsteps = t.k1 > t.k0 ? (t.k1 - t.k0 + TK - 1) / TK : 0;
   const bool ktail = ((t.k1 - t.k0) % TK) != 0;
+  const uint16_t* arow[CH] = {};
+  if constexpr (tok_out_rows<PROB>()) {
+    const uint16_t* X = PROB == PROB_Z ? p.x : p.dout;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int row = (i * NT_ + tid) >> 2;
+      const int r = t.row0 + (row < t.mlim ? row : 0);
+      arow[i] = X + static_cast<size_t>(p.shared ? r : p.rtok[r]) * p.d;
+    }
+  }
+  StageToks tk{};
   auto issue = [&](uint16_t* st, int kb) {
-    issue_op<PROB, true>(p, t, kb, st);
-    issue_op<PROB, false>(p, t, kb, st + TM * TK);
+    issue_op<PROB, true>(p, t, kb, st, arow, tk);
+    issue_op<PROB, false>(p, t, kb, st + TM * TK, arow, tk);
   };
   // S stages of DMA in flight ahead of the MFMAs; every thread issues LPS
   // loads per stage (clamped past the end), so each wave's count of
-  // outstanding loads is uniform and one vmcnt wait covers a stage.
+  // outstanding loads is uniform and one vmcnt wait covers a stage. The
+  // tokens of a stage's sorted rows are loaded one stage before its issue.
   if (nsteps > 0) {
 #pragma unroll
-    for (int st = 0; st < S - 1; ++st) issue(Ring + st * SEL, t.k0 + st * TK);
+    for (int st = 0; st < S - 1; ++st) {
+      load_toks<PROB>(p, t, t.k0 + st * TK, tk);
+      issue(Ring + st * SEL, t.k0 + st * TK);
+    }
+    load_toks<PROB>(p, t, t.k0 + (S - 1) * TK, tk);
   }
   int cur = 0, nxt = S - 1;
   for (int s = 0; s < nsteps; ++s) {
     wait_stage<(S - 2) * LPS>();
     stage_barrier();
     issue(Ring + nxt * SEL, t.k0 + (s + S - 1) * TK);
+    load_toks<PROB>(p, t, t.k0 + (s + S) * TK, tk);
     nxt = nxt + 1 == S ? 0 : nxt + 1;
     uint16_t* st = Ring + cur * SEL;
     cur = cur + 1 == S ? 0 : cur + 1;
@@ -638,18 +700,10 @@ hipError_t launch_prob(const BwdParams& p, hipStream_t s) {
 
 }  // namespace
 
-// Sorted copies of the routed rows: xs[r] = x[t], dos[r] = dO[t] for sorted
-// row r of pair perm[r] = t k + slot (16 bytes per thread).
-__global__ __launch_bounds__(256) void gather_rows_kernel(BwdParams p) {
-  const int cpr = p.d / 8;
-  const size_t i = blockIdx.x * 256ull + threadIdx.x;
-  const size_t P = static_cast<size_t>(p.T) * p.k;
-  if (i >= P * cpr) return;
-  const size_t r = i / cpr;
-  const int c = static_cast<int>(i - r * cpr) * 8;
-  const size_t t = static_cast<size_t>(p.perm[r] / p.k);
-  *reinterpret_cast<u32x4_t*>(p.xs + r * p.d + c) = *reinterpret_cast<const u32x4_t*>(p.x + t * p.d + c);
-  *reinterpret_cast<u32x4_t*>(p.dos + r * p.d + c) = *reinterpret_cast<const u32x4_t*>(p.dout + t * p.d + c);
+// Token of each sorted row: rtok[r] = perm[r] / k.
+__global__ __launch_bounds__(256) void row_token_kernel(BwdParams p) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r < p.T * p.k) p.rtok[r] = p.perm[r] / p.k;
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, size_t n) {
@@ -680,11 +734,8 @@ hipError_t launch_backward(const BwdParams& p0, hipStream_t s, void* const* ev) 
   auto mark = [&](int i) -> hipError_t {
     return ev == nullptr ? hipSuccess : hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), s);
   };
-  {
-    const size_t n = static_cast<size_t>(p.T) * p.k * (p.d / 8);
-    gather_rows_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(p);
-    BWD_TRY(hipGetLastError());
-  }
+  row_token_kernel<<<(p.T * p.k + 255) / 256, 256, 0, s>>>(p);
+  BWD_TRY(hipGetLastError());
   BWD_TRY(launch_prob<PROB_Z>(p, s));
   if (has_sh) BWD_TRY(launch_prob<PROB_Z>(q, s));
   BWD_TRY(mark(1));

@@ -132,7 +132,7 @@ WsLayout ws_layout(const moe_config& c) {
 // then the logits and the backward's own buffers.
 struct BwdLayout {
   WsLayout tables;
-  size_t logits, xs, dos, z, gact, dz, part, dxr, z_s, gact_s, dz_s, part_s, dx_s, dlb, dpre, sg_part,
+  size_t logits, rtok, z, gact, dz, part, dxr, z_s, gact_s, dz_s, part_s, dx_s, dlb, dpre, sg_part,
       rpart, end;
 };
 
@@ -152,8 +152,7 @@ BwdLayout bwd_layout(const moe_config& c) {
   const size_t np = 2 * static_cast<size_t>(ceil_div(c.h, 128));
   const size_t nps = hs > 0 ? 2 * static_cast<size_t>(ceil_div(c.shared_h, 128)) : 0;
   B.logits = take(T * static_cast<size_t>(c.E) * 4);
-  B.xs = take(P * d * 2);
-  B.dos = take(P * d * 2);
+  B.rtok = take(P * 4);
   B.z = take(P * 2 * h * 4);
   B.gact = take(P * h * 2);
   B.dz = take(P * 2 * h * 2);
@@ -706,7 +705,7 @@ moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w
       bp.dw_shared_gate = gr->dw_shared_gate;
     }
   }
-  bp.xs = at<uint16_t>(ws, B.xs); bp.dos = at<uint16_t>(ws, B.dos);
+  bp.rtok = at<int>(ws, B.rtok);
   bp.z = at<float>(ws, B.z); bp.gact = at<uint16_t>(ws, B.gact); bp.dz = at<uint16_t>(ws, B.dz);
   bp.part = at<float>(ws, B.part); bp.dxr = at<float>(ws, B.dxr);
   bp.dlb = at<uint16_t>(ws, B.dlb);

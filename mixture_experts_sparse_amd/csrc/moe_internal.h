@@ -267,7 +267,7 @@ struct BwdParams {
   const float* sgate;         // [T] sigmoid(w_s . x), or null
   const uint16_t *x, *dout, *w_router, *w_gate, *w_up, *w_down;
   const uint16_t *ws_gate, *ws_up, *ws_down, *w_shared_gate;
-  uint16_t *xs, *dos;         // [P, d] x and dO rows in sorted order
+  int* rtok;                  // [P] token of each sorted row (perm[r] / k)
   float *z, *z_s;             // [P, 2h], [T, 2hs] gate | up pre-activations
   uint16_t *gact, *gact_s;    // [P, h], [T, hs] gate * silu(z_g) * z_u, bf16
   uint16_t *dz, *dz_s;        // [P, 2h], [T, 2hs] pre-activation gradients, bf16
