@@ -67,6 +67,12 @@ SMALL = {
     "sigmoid_one_block": small_spec("small_moe_sigmoid", T=16, d=256, E=64, h=64, k=8, shared_h=0),
     "sigmoid_k20": small_spec("small_moe_sigmoid", T=90, d=128, E=64, h=32, k=20, shared_h=0,
                               renormalize=False),
+    # gemma's d = 640 with at least 32 rows per expert (the persistent gate/up
+    # kernel): a column tail (h = 136), experts of two 128-row tiles, and the
+    # shared expert's tiles in the same persistent walk
+    "pers_d640": small_spec("gemma_upcycled", T=300, d=640, E=16, h=136, k=4),
+    "pers_d640_two_mtiles": small_spec("gemma_upcycled", T=700, d=640, E=8, h=64, k=2),
+    "pers_d640_shared": small_spec("shared_routed", T=260, d=640, E=8, h=96, k=2, shared_h=200),
 }
 
 
