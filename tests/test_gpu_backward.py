@@ -10,8 +10,8 @@ re-derived by the oracle with the GPU's own selection (taken from the forward
 on the same inputs), as in the forward parity protocol. Cases span several
 128-row tiles with ragged tails, one route block (the split router), 256
 experts, E not a multiple of 8, every gate mode, logit and balance biases,
-and gated and ungated shared experts; one full-size workload is checked
-whole.
+gated and ungated shared experts, and experts of 256 rows and more; one
+full-size workload is checked whole.
 """
 
 import numpy as np
@@ -52,6 +52,12 @@ CASES = {
     # E not a multiple of 8 (padded logit rows), k = 3, T just past one route block
     "e12_k3": small_spec("shared_routed", T=77, d=72, E=12, h=40, k=3, shared_h=0,
                          shared_gate=False),
+    # at least 256 rows per expert (several row tiles per expert), with K and N
+    # tails, the shared expert, and sigmoid gates
+    "big_tiles": small_spec("skewed_prefill", T=700, d=264, E=4, h=200, k=2),
+    "big_tiles_shared": small_spec("shared_routed", T=600, d=136, E=3, h=96, k=2, shared_h=200),
+    "big_tiles_sigmoid": small_spec("small_moe_sigmoid", T=520, d=128, E=4, h=64, k=2,
+                                    shared_h=128),
 }
 
 GRADS = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up", "dws_down",
