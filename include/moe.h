@@ -300,9 +300,10 @@ moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* w, const
                               size_t ws_bytes, void* stream);
 
 /* Stages of moe_layer_backward_traced: route and dispatch (recomputed), the
- * gate/up pre-activations (recomputed), the down-projection gradient into
- * the hidden units, the gate and logit gradients, dW_down, dW_gate|up, the
- * routed and shared dx rows, and the router products with the final dx. */
+ * down-projection gradient into the hidden units, the gate/up
+ * pre-activations (recomputed, with the pre-activation gradients formed from
+ * them), the gate and logit gradients, dW_down, dW_gate|up, the routed and
+ * shared dx rows, and the router products with the final dx. */
 #define MOE_NUM_BWD_STAGES 8
 
 /* moe_layer_backward that also records stage_events[0] before the first

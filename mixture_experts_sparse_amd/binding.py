@@ -44,7 +44,7 @@ MOE_ENTRY_LAYER_BACKWARD = 7
 MOE_NUM_STAGES = 5
 STAGE_NAMES = ("route", "dispatch", "gate_up", "down", "combine")
 MOE_NUM_BWD_STAGES = 8
-BWD_STAGE_NAMES = ("route", "z", "d_hidden", "router_grad", "dw_down", "dw_gate_up", "dx_rows",
+BWD_STAGE_NAMES = ("route", "d_hidden", "z", "router_grad", "dw_down", "dw_gate_up", "dx_rows",
                    "dx_router")
 
 

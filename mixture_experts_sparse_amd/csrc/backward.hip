@@ -10,8 +10,10 @@
 // With g the gate of a (token, slot) pair, rows r of expert e in sorted order,
 // t its token, z_g / z_u its pre-activations and a = silu(z_g) z_u:
 //
-//   da'[r]      = W_d[e]^T dO[t]                      (bwd_gemm, PROB_DA)
-//   dG[t, slot] = da'[r] . a[r]      (= dO[t] . y[r]; partial sums per tile)
+//   da'[r]      = W_d[e]^T dO[t]                      (bwd_gemm, PROB_DA; stored)
+//   z[r]        = x[t] W_g|u[e]^T                     (PROB_Z, never stored: its
+//                 epilogue forms g a, dz and the dG partial sums from z and da')
+//   dG[t, slot] = da'[r] . a[r]      (= dO[t] . y[r]; partial sums per 32 units)
 //   dz_g, dz_u  = g da' z_u silu'(z_g), g da' silu(z_g)
 //   dW_d[e]     = sum_r dO[t] (g a[r])^T              (PROB_DWD)
 //   dW_g|u[e]   = sum_r dz_g|u[r] x[t]^T              (PROB_DWGU)
@@ -370,6 +372,10 @@ __device__ __forceinline__ float row16_sum_x(float v) {
   return v;
 }
 
+// Partial sums of the gate gradient per row: one per 32 hidden units (a
+// wave's share of a z tile, 2 waves x 64 hidden units per 128-column tile).
+__device__ __forceinline__ int bwd_npart(int H) { return 2 * ((2 * H + TN - 1) / TN); }
+
 __device__ __forceinline__ float silu_grad_f32(float z) {
   const float s = sigmoid_f32(z);
   return s * (1.0f + z * (1.0f - s));
@@ -455,35 +461,17 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
   const bool sh = p.shared;
   const int H = sh ? p.hs : p.h;
   if constexpr (PROB == PROB_Z) {
-    // nf 0, 1: gate of hidden unit hu; nf 2, 3: up of the same unit
-    float* z = sh ? p.z_s : p.z;
+    // nf 0, 1: gate of hidden unit hu; nf 2, 3: up of the same unit. With
+    // da' of the row (stored by the hidden-unit product, which runs first)
+    // and the gate g: g a (bf16, for dW_down), the pre-activation gradients
+    // g da' z_u silu'(z_g) and g da' silu(z_g) (bf16), and this wave's
+    // partial sum of da' . a over its 32 hidden units (the gate gradient).
+    const float* dh = sh ? p.dh_s : p.dh;
     uint16_t* ga = sh ? p.gact_s : p.gact;
-#pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ir = wm * 64 + mf * 16 + fq * 4 + i;
-        if (ir >= t.mlim) continue;
-        const int r = t.row0 + ir;
-        float g;
-        if (sh) g = p.sgate != nullptr ? p.sgate[r] : 1.0f;
-        else g = p.gates[p.perm[r]];
-#pragma unroll
-        for (int nf = 0; nf < 2; ++nf) {
-          const int hu = (t.n0 >> 1) + wn * 32 + nf * 16 + fr;
-          if (hu >= H) continue;
-          const float zg = acc[mf][nf][i], zu = acc[mf][nf + 2][i];
-          z[static_cast<size_t>(r) * (2 * H) + hu] = zg;
-          z[static_cast<size_t>(r) * (2 * H) + H + hu] = zu;
-          ga[static_cast<size_t>(r) * H + hu] = f32_to_bf16(g * (silu_f32(zg) * zu));
-        }
-      }
-  } else if constexpr (PROB == PROB_DA) {
-    const float* z = sh ? p.z_s : p.z;
     uint16_t* dz = sh ? p.dz_s : p.dz;
     float* part = sh ? p.part_s : p.part;
-    const int npart = 2 * ((H + TN - 1) / TN);
-    const int pcol = 2 * (t.n0 / TN) + wn;
+    const int npart = bwd_npart(H);
+    const int pcol = (t.n0 >> 6) + wn;  // 32-unit group of the wave
 #pragma unroll
     for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
@@ -491,20 +479,20 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
         const int ir = wm * 64 + mf * 16 + fq * 4 + i;
         const bool rok = ir < t.mlim;
         const int r = t.row0 + (rok ? ir : 0);
-        float g = 1.0f;
+        float g;
         if (sh) g = p.sgate != nullptr ? p.sgate[r] : 1.0f;
         else g = p.gates[p.perm[r]];
         float dot = 0.f;
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf) {
-          const int j = wn * 64 + nf * 16 + fr;
-          if (rok && j < t.nlim) {
-            const int hu = t.n0 + j;
-            const float zg = z[static_cast<size_t>(r) * (2 * H) + hu];
-            const float zu = z[static_cast<size_t>(r) * (2 * H) + H + hu];
-            const float c = acc[mf][nf][i];
+        for (int nf = 0; nf < 2; ++nf) {
+          const int hu = (t.n0 >> 1) + wn * 32 + nf * 16 + fr;
+          if (rok && hu < H) {
+            const float zg = acc[mf][nf][i], zu = acc[mf][nf + 2][i];
+            const float c = dh[static_cast<size_t>(r) * H + hu];
             const float sg = silu_f32(zg);
-            dot += c * (sg * zu);
+            const float a = sg * zu;
+            dot += c * a;
+            ga[static_cast<size_t>(r) * H + hu] = f32_to_bf16(g * a);
             const float da = g * c;
             dz[static_cast<size_t>(r) * (2 * H) + hu] = f32_to_bf16(da * zu * silu_grad_f32(zg));
             dz[static_cast<size_t>(r) * (2 * H) + H + hu] = f32_to_bf16(da * sg);
@@ -512,6 +500,22 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
         }
         dot = row16_sum_x(dot);
         if (rok && fr == 0) part[static_cast<size_t>(r) * npart + pcol] = dot;
+      }
+  } else if constexpr (PROB == PROB_DA) {
+    // da' in float32, read back by the z product's epilogue
+    float* dh = sh ? p.dh_s : p.dh;
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ir = wm * 64 + mf * 16 + fq * 4 + i;
+        if (ir >= t.mlim) continue;
+        const int r = t.row0 + ir;
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) {
+          const int j = wn * 64 + nf * 16 + fr;
+          if (j < t.nlim) dh[static_cast<size_t>(r) * H + t.n0 + j] = acc[mf][nf][i];
+        }
       }
   } else if constexpr (PROB == PROB_DWD || PROB == PROB_DWGU || PROB == PROB_DXR ||
                        PROB == PROB_DWROUTER) {
@@ -577,20 +581,31 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
 // (zero-padded to Epad) for the two router products; and the shared gate's
 // pre-activation gradient.
 __global__ __launch_bounds__(256) void router_bwd_kernel(BwdParams p) {
-  const int lane = threadIdx.x & 63;
-  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // per wave (token): each slot's gate gradient, and the slot of each expert
+  __shared__ float sdg[4][MOE_MAX_EXPERTS];
+  __shared__ int slot_of[4][MOE_MAX_EXPERTS];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tok = blockIdx.x * 4 + w;
   if (tok >= p.T) return;
   const int k = p.k, E = p.E;
-  const int npart = 2 * ((p.h + TN - 1) / TN);
-  // slot s's gate gradient in lane s (k <= 64 is not required: loop)
+  const int npart = bwd_npart(p.h);
+  // slot s's gate gradient in lane s mod 64 (k <= E <= MOE_MAX_EXPERTS)
+  for (int e = lane; e < E; e += 64) slot_of[w][e] = -1;
+  __builtin_amdgcn_wave_barrier();
   float inner = 0.f;
-  for (int s = 0; s < k; ++s) {
+  for (int s = lane; s < k; s += 64) {
     const int r = p.inv[tok * k + s];
     float dg = 0.f;
     for (int q = 0; q < npart; ++q) dg += p.part[static_cast<size_t>(r) * npart + q];
     inner += dg * p.gates[tok * k + s];
-    if (p.dgates != nullptr && lane == 0) p.dgates[tok * k + s] = dg;
+    sdg[w][s] = dg;
+    slot_of[w][p.ids[tok * k + s]] = s;
+    if (p.dgates != nullptr) p.dgates[tok * k + s] = dg;
   }
+  inner = wave_sum(inner);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const float* L = p.logits + static_cast<size_t>(tok) * E;
   const bool soft_all = p.mode == MOE_SOFTMAX_ALL && !p.renorm;
   float m = -INFINITY, ssum = 0.f;
@@ -607,19 +622,11 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(BwdParams p) {
   for (int e = lane; e < p.Epad; e += 64) {
     float v = 0.f;
     if (e < E) {
-      // dG summed over the slots that chose e (at most one: experts are distinct)
-      float dge = 0.f, ge = 0.f;
-      bool chosen = false;
-      for (int s = 0; s < k; ++s) {
-        if (p.ids[tok * k + s] == e) {
-          const int r = p.inv[tok * k + s];
-          float dg = 0.f;
-          for (int q = 0; q < npart; ++q) dg += p.part[static_cast<size_t>(r) * npart + q];
-          dge = dg;
-          ge = p.gates[tok * k + s];
-          chosen = true;
-        }
-      }
+      // the slot that chose e, if any (experts of a token are distinct)
+      const int s = slot_of[w][e];
+      const bool chosen = s >= 0;
+      const float dge = chosen ? sdg[w][s] : 0.f;
+      const float ge = chosen ? p.gates[tok * k + s] : 0.f;
       if (soft_all) {
         const float pe = expf(L[e] - m) / ssum;
         v = pe * (dge - inner);
@@ -637,7 +644,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(BwdParams p) {
     p.dlb[static_cast<size_t>(tok) * p.Epad + e] = f32_to_bf16(v);
   }
   if (p.dpre != nullptr && lane == 0) {
-    const int nps = 2 * ((p.hs + TN - 1) / TN);
+    const int nps = bwd_npart(p.hs);
     float dc = 0.f;
     for (int q = 0; q < nps; ++q) dc += p.part_s[static_cast<size_t>(tok) * nps + q];
     const float c = p.sgate[tok];
@@ -736,11 +743,11 @@ hipError_t launch_backward(const BwdParams& p0, hipStream_t s, void* const* ev) 
   };
   row_token_kernel<<<(p.T * p.k + 255) / 256, 256, 0, s>>>(p);
   BWD_TRY(hipGetLastError());
-  BWD_TRY(launch_prob<PROB_Z>(p, s));
-  if (has_sh) BWD_TRY(launch_prob<PROB_Z>(q, s));
-  BWD_TRY(mark(1));
   BWD_TRY(launch_prob<PROB_DA>(p, s));
   if (has_sh) BWD_TRY(launch_prob<PROB_DA>(q, s));
+  BWD_TRY(mark(1));
+  BWD_TRY(launch_prob<PROB_Z>(p, s));
+  if (has_sh) BWD_TRY(launch_prob<PROB_Z>(q, s));
   BWD_TRY(mark(2));
   router_bwd_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(p);
   BWD_TRY(hipGetLastError());

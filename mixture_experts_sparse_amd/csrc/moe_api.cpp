@@ -132,7 +132,7 @@ WsLayout ws_layout(const moe_config& c) {
 // then the logits and the backward's own buffers.
 struct BwdLayout {
   WsLayout tables;
-  size_t logits, rtok, z, gact, dz, part, dxr, z_s, gact_s, dz_s, part_s, dx_s, dlb, dpre, sg_part,
+  size_t logits, rtok, dh, gact, dz, part, dxr, dh_s, gact_s, dz_s, part_s, dx_s, dlb, dpre, sg_part,
       rpart, end;
 };
 
@@ -149,16 +149,17 @@ BwdLayout bwd_layout(const moe_config& c) {
   const size_t d = static_cast<size_t>(c.d), h = static_cast<size_t>(c.h);
   const size_t hs = static_cast<size_t>(c.shared_h);
   const size_t epad = static_cast<size_t>(ceil_div(c.E, 8) * 8);
-  const size_t np = 2 * static_cast<size_t>(ceil_div(c.h, 128));
-  const size_t nps = hs > 0 ? 2 * static_cast<size_t>(ceil_div(c.shared_h, 128)) : 0;
+  // dG partial sums: one per 32 hidden units (a wave's share of a z tile)
+  const size_t np = 2 * static_cast<size_t>(ceil_div(c.h, 64));
+  const size_t nps = hs > 0 ? 2 * static_cast<size_t>(ceil_div(c.shared_h, 64)) : 0;
   B.logits = take(T * static_cast<size_t>(c.E) * 4);
   B.rtok = take(P * 4);
-  B.z = take(P * 2 * h * 4);
+  B.dh = take(P * h * 4);
   B.gact = take(P * h * 2);
   B.dz = take(P * 2 * h * 2);
   B.part = take(P * np * 4);
   B.dxr = take(P * d * 4);
-  B.z_s = take(T * 2 * hs * 4);
+  B.dh_s = take(T * hs * 4);
   B.gact_s = take(T * hs * 2);
   B.dz_s = take(T * 2 * hs * 2);
   B.part_s = take(T * nps * 4);
@@ -694,7 +695,7 @@ moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w
     bp.ws_gate = static_cast<const uint16_t*>(w->ws_gate);
     bp.ws_up = static_cast<const uint16_t*>(w->ws_up);
     bp.ws_down = static_cast<const uint16_t*>(w->ws_down);
-    bp.z_s = at<float>(ws, B.z_s); bp.gact_s = at<uint16_t>(ws, B.gact_s);
+    bp.dh_s = at<float>(ws, B.dh_s); bp.gact_s = at<uint16_t>(ws, B.gact_s);
     bp.dz_s = at<uint16_t>(ws, B.dz_s); bp.part_s = at<float>(ws, B.part_s);
     bp.dx_s = at<float>(ws, B.dx_s);
     bp.dws_gate = gr->dws_gate; bp.dws_up = gr->dws_up; bp.dws_down = gr->dws_down;
@@ -706,7 +707,7 @@ moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w
     }
   }
   bp.rtok = at<int>(ws, B.rtok);
-  bp.z = at<float>(ws, B.z); bp.gact = at<uint16_t>(ws, B.gact); bp.dz = at<uint16_t>(ws, B.dz);
+  bp.dh = at<float>(ws, B.dh); bp.gact = at<uint16_t>(ws, B.gact); bp.dz = at<uint16_t>(ws, B.dz);
   bp.part = at<float>(ws, B.part); bp.dxr = at<float>(ws, B.dxr);
   bp.dlb = at<uint16_t>(ws, B.dlb);
   bp.rpart = at<float>(ws, B.rpart);

@@ -268,10 +268,10 @@ struct BwdParams {
   const uint16_t *x, *dout, *w_router, *w_gate, *w_up, *w_down;
   const uint16_t *ws_gate, *ws_up, *ws_down, *w_shared_gate;
   int* rtok;                  // [P] token of each sorted row (perm[r] / k)
-  float *z, *z_s;             // [P, 2h], [T, 2hs] gate | up pre-activations
+  float *dh, *dh_s;           // [P, h], [T, hs] hidden-unit gradients da' (before the gate)
   uint16_t *gact, *gact_s;    // [P, h], [T, hs] gate * silu(z_g) * z_u, bf16
   uint16_t *dz, *dz_s;        // [P, 2h], [T, 2hs] pre-activation gradients, bf16
-  float *part, *part_s;       // [P, 2 ceil(h/128)], [T, 2 ceil(hs/128)] dG partial sums
+  float *part, *part_s;       // [P, 2 ceil(h/64)], [T, 2 ceil(hs/64)] dG partial sums (32 hidden units each)
   float *dxr, *dx_s;          // [P, d] routed dx rows (pair order t * k + slot), [T, d] shared dx, or null
   uint16_t* dlb;              // [T, Epad] dlogits, bf16, zero-padded
   float* dpre;                // [T] shared gate pre-activation gradient, or null
