@@ -19,7 +19,8 @@
 //   dW_g|u[e]   = sum_r dz_g|u[r] x[t]^T              (PROB_DWGU)
 //   dx rows     = dz_g W_g[e] + dz_u W_u[e]           (PROB_DXR)
 //   dL          = the gate-to-logit derivative of dG  (router_bwd_kernel)
-//   dX[t]       = sum_slots dx rows + dL[t] W_r (+ shared expert terms)  (PROB_DXROUTER)
+//   dX[t]       = dL[t] W_r (+ shared gate term)       (PROB_DXROUTER)
+//                 + sum_slots dx rows (+ shared dx row)  (dx_finish_kernel)
 //   dW_r        = dL^T X                              (PROB_DWROUTER)
 //
 // The shared expert is the same arithmetic on every token with the gate
@@ -550,7 +551,8 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
           }
         }
       }
-  } else {  // PROB_DXROUTER: the final dX rows
+  } else {  // PROB_DXROUTER: dL W_r (+ the shared gate's term); the dx rows
+            // are added by dx_finish_kernel
 #pragma unroll
     for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
@@ -565,15 +567,37 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
           if (j >= t.nlim) continue;
           const int c = t.n0 + j;
           float v = acc[mf][nf][i];
-          const float* rows = p.dxr + static_cast<size_t>(tok) * p.k * p.d + c;
-#pragma unroll 8
-          for (int s = 0; s < p.k; ++s) v += rows[static_cast<size_t>(s) * p.d];
-          if (p.dx_s != nullptr) v += p.dx_s[static_cast<size_t>(tok) * p.d + c];
           if (p.dpre != nullptr) v += dpre * bf16_to_f32(p.w_shared_gate[c]);
           p.dx[static_cast<size_t>(tok) * p.d + c] = v;
         }
       }
   }
+}
+
+// dx[t] += the token's k routed dx rows (adjacent, pair order) + its shared
+// dx row: four columns per thread, 16-byte loads, all issued before the sum.
+__global__ __launch_bounds__(256) void dx_finish_kernel(BwdParams p) {
+  const int cq = p.d / 4;
+  const size_t i = blockIdx.x * 256ull + threadIdx.x;
+  if (i >= static_cast<size_t>(p.T) * cq) return;
+  const size_t t = i / cq;
+  const int c = static_cast<int>(i - t * cq) * 4;
+  float4 v = *reinterpret_cast<const float4*>(p.dx + t * p.d + c);
+  const float* rows = p.dxr + t * p.k * p.d + c;
+  for (int s0 = 0; s0 < p.k; s0 += 8) {
+    float4 r[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s0 + s < p.k) r[s] = *reinterpret_cast<const float4*>(rows + static_cast<size_t>(s0 + s) * p.d);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      if (s0 + s < p.k) { v.x += r[s].x; v.y += r[s].y; v.z += r[s].z; v.w += r[s].w; }
+  }
+  if (p.dx_s != nullptr) {
+    const float4 u = *reinterpret_cast<const float4*>(p.dx_s + t * p.d + c);
+    v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+  }
+  *reinterpret_cast<float4*>(p.dx + t * p.d + c) = v;
 }
 
 // One wave per token: the gate gradients dG from the per-tile partial sums,
@@ -762,6 +786,11 @@ hipError_t launch_backward(const BwdParams& p0, hipStream_t s, void* const* ev) 
   if (has_sh) BWD_TRY(launch_prob<PROB_DXR>(q, s));
   BWD_TRY(mark(6));
   BWD_TRY(launch_prob<PROB_DXROUTER>(p, s));
+  {
+    const size_t n = static_cast<size_t>(p.T) * (p.d / 4);
+    dx_finish_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(p);
+    BWD_TRY(hipGetLastError());
+  }
   BWD_TRY(launch_prob<PROB_DWROUTER>(p, s));
   {
     const int nch = (p.T + kRouterKChunk - 1) / kRouterKChunk;
