@@ -48,10 +48,9 @@ namespace {
 constexpr int NT_ = 256;  // threads per workgroup
 constexpr int TM = 128, TN = 128, TK = 32;
 constexpr int CH = TM * TK / 8 / NT_;       // 16-byte chunks per thread per operand and stage
-constexpr int S = 3;                        // LDS stages
 constexpr int LPS = 2 * CH;                 // DMA loads per thread per stage
 static_assert(TM == TN && CH == 2, "the chunk mappings assume 128 x 32 stages");
-static_assert((S - 2) * LPS < 64, "vmcnt range");
+static_assert(LPS < 64, "vmcnt range");
 constexpr int kRouterKChunk = kBwdRouterChunk;  // tokens per partial of dW_r
 
 enum : int {
@@ -382,12 +381,20 @@ __device__ __forceinline__ float silu_grad_f32(float z) {
   return s * (1.0f + z * (1.0f - s));
 }
 
-// Three workgroups per CU (the 48 KB stage ring of each).
+// LDS stages and workgroups per CU by product: the weight gradients and the
+// dx rows run faster with more workgroups per CU than with deeper rings
+// (two 16 KB stages, four workgroups); the others keep three stages and
+// three workgroups (the final-dx router product's registers do not fit four).
 template <int PROB>
-constexpr int bwd_occupancy() { return 3; }
+constexpr bool bwd_wide() { return PROB == PROB_DWD || PROB == PROB_DWGU || PROB == PROB_DXR; }
+template <int PROB>
+constexpr int bwd_stages() { return bwd_wide<PROB>() ? 2 : 3; }
+template <int PROB>
+constexpr int bwd_occupancy() { return bwd_wide<PROB>() ? 4 : 3; }
 
 template <int PROB>
 __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams p) {
+  constexpr int S = bwd_stages<PROB>();
   Tile t;
   if (!decode<PROB>(p, t)) return;
   __shared__ __align__(16) uint16_t Ring[S * SEL];
