@@ -474,17 +474,36 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
     // and the gate g: g a (bf16, for dW_down), the pre-activation gradients
     // g da' z_u silu'(z_g) and g da' silu(z_g) (bf16), and this wave's
     // partial sum of da' . a over its 32 hidden units (the gate gradient).
+    // g a and dz are staged in this wave's 12 KB of the (now idle) stage ring
+    // ([64][32] and [64][64] bf16) and stored 16 bytes per lane.
     const float* dh = sh ? p.dh_s : p.dh;
     uint16_t* ga = sh ? p.gact_s : p.gact;
     uint16_t* dz = sh ? p.dz_s : p.dz;
     float* part = sh ? p.part_s : p.part;
     const int npart = bwd_npart(H);
-    const int pcol = (t.n0 >> 6) + wn;  // 32-unit group of the wave
+    const int hu0 = (t.n0 >> 1) + wn * 32;  // first hidden unit of the wave
+    const int pcol = (t.n0 >> 6) + wn;      // its 32-unit group
+    static_assert(S * SEL >= 4 * 6144, "staging fits the ring");
+    uint16_t* gaS = Ring + wave * 6144;  // [64][32]
+    uint16_t* dzS = gaS + 2048;          // [64][64]: gate units, then up units
+    __syncthreads();  // every wave is done with the ring
+    float c[4][4][2];
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int nf = 0; nf < 2; ++nf) {
+          const int ir = min(wm * 64 + mf * 16 + fq * 4 + i, t.mlim - 1);
+          const int hu = min(hu0 + nf * 16 + fr, H - 1);
+          c[mf][i][nf] = dh[static_cast<size_t>(t.row0 + ir) * H + hu];
+        }
 #pragma unroll
     for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int ir = wm * 64 + mf * 16 + fq * 4 + i;
+        const int lr = mf * 16 + fq * 4 + i;  // row within the wave
+        const int ir = wm * 64 + lr;
         const bool rok = ir < t.mlim;
         const int r = t.row0 + (rok ? ir : 0);
         float g;
@@ -493,22 +512,43 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
         float dot = 0.f;
 #pragma unroll
         for (int nf = 0; nf < 2; ++nf) {
-          const int hu = (t.n0 >> 1) + wn * 32 + nf * 16 + fr;
-          if (rok && hu < H) {
-            const float zg = acc[mf][nf][i], zu = acc[mf][nf + 2][i];
-            const float c = dh[static_cast<size_t>(r) * H + hu];
-            const float sg = silu_f32(zg);
-            const float a = sg * zu;
-            dot += c * a;
-            ga[static_cast<size_t>(r) * H + hu] = f32_to_bf16(g * a);
-            const float da = g * c;
-            dz[static_cast<size_t>(r) * (2 * H) + hu] = f32_to_bf16(da * zu * silu_grad_f32(zg));
-            dz[static_cast<size_t>(r) * (2 * H) + H + hu] = f32_to_bf16(da * sg);
-          }
+          const int hu = hu0 + nf * 16 + fr;
+          const float zg = acc[mf][nf][i], zu = acc[mf][nf + 2][i];
+          const float sgm = 1.0f / (1.0f + expf(-zg));  // sigmoid(z_g)
+          const float sg = zg * sgm;                     // silu(z_g)
+          const float a = sg * zu;
+          const float cv = (rok && hu < H) ? c[mf][i][nf] : 0.f;
+          dot += cv * a;
+          const float da = g * cv;
+          const int col = nf * 16 + fr;
+          gaS[lr * 32 + col] = f32_to_bf16(g * a);
+          dzS[lr * 64 + col] = f32_to_bf16(da * zu * (sgm * (1.0f + zg * (1.0f - sgm))));
+          dzS[lr * 64 + 32 + col] = f32_to_bf16(da * sg);
         }
         dot = row16_sum_x(dot);
         if (rok && fr == 0) part[static_cast<size_t>(r) * npart + pcol] = dot;
       }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // g a: 64 rows x 4 chunks; dz: 64 rows x 8 chunks (4 gate, 4 up)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = j * 64 + lane, lr = q >> 2, ch = q & 3;
+      const int ir = wm * 64 + lr;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(gaS + lr * 32 + ch * 8);
+      if (ir < t.mlim && hu0 + ch * 8 < H)
+        *reinterpret_cast<u32x4_t*>(ga + static_cast<size_t>(t.row0 + ir) * H + hu0 + ch * 8) = v;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = j * 64 + lane, lr = q >> 3, ch = q & 7;
+      const int ir = wm * 64 + lr;
+      const int u = hu0 + (ch & 3) * 8;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(dzS + lr * 64 + ch * 8);
+      if (ir < t.mlim && u < H)
+        *reinterpret_cast<u32x4_t*>(dz + static_cast<size_t>(t.row0 + ir) * (2 * H) + (ch < 4 ? 0 : H) + u) = v;
+    }
   } else if constexpr (PROB == PROB_DA) {
     // da' in float32, read back by the z product's epilogue
     float* dh = sh ? p.dh_s : p.dh;
