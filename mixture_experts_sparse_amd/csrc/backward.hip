@@ -549,75 +549,72 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
       if (ir < t.mlim && u < H)
         *reinterpret_cast<u32x4_t*>(dz + static_cast<size_t>(t.row0 + ir) * (2 * H) + (ch < 4 ? 0 : H) + u) = v;
     }
-  } else if constexpr (PROB == PROB_DA) {
-    // da' in float32, read back by the z product's epilogue
-    float* dh = sh ? p.dh_s : p.dh;
-#pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ir = wm * 64 + mf * 16 + fq * 4 + i;
-        if (ir >= t.mlim) continue;
-        const int r = t.row0 + ir;
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf) {
-          const int j = wn * 64 + nf * 16 + fr;
-          if (j < t.nlim) dh[static_cast<size_t>(r) * H + t.n0 + j] = acc[mf][nf][i];
-        }
+  } else {
+    // float32 outputs (da'; dW_down; dW_gate|up; the dx rows, in pair order so
+    // that a token's k rows are adjacent; dW_r partials; dL W_r plus the
+    // shared gate's term, to which dx_finish_kernel adds the dx rows). This
+    // wave's 64 x 64 block goes through its 8 KB of the (now idle) stage ring,
+    // 32 rows at a time, and out 16 bytes per lane. In the staging rows,
+    // 16-column blocks are XOR-swizzled by bits 2..3 of the row, so the four
+    // row groups of a fragment write to distinct banks.
+    static_assert(S * SEL * 2 >= 4 * 32 * 64 * 4, "staging fits the ring");
+    float* Sw = reinterpret_cast<float*>(Ring) + wave * (32 * 64);
+    auto dst_row = [&](int ir) -> float* {
+      const int m = t.m0 + ir;
+      if constexpr (PROB == PROB_DA) {
+        return (sh ? p.dh_s : p.dh) + static_cast<size_t>(t.row0 + ir) * H;
+      } else if constexpr (PROB == PROB_DWD) {
+        float* o = sh ? p.dws_down : p.dw_down + static_cast<size_t>(t.e) * p.d * H;
+        return o + static_cast<size_t>(m) * H;
+      } else if constexpr (PROB == PROB_DWGU) {
+        const bool up = m >= H;
+        float* o = up ? (sh ? p.dws_up : p.dw_up) : (sh ? p.dws_gate : p.dw_gate);
+        if (!sh) o += static_cast<size_t>(t.e) * H * p.d;
+        return o + static_cast<size_t>(up ? m - H : m) * p.d;
+      } else if constexpr (PROB == PROB_DXR) {
+        const int orow = sh ? t.row0 + ir : p.perm[t.row0 + ir];
+        return (sh ? p.dx_s : p.dxr) + static_cast<size_t>(orow) * p.d;
+      } else if constexpr (PROB == PROB_DWROUTER) {
+        return p.rpart + (static_cast<size_t>(t.e) * p.E + m) * p.d;
+      } else {  // PROB_DXROUTER
+        return p.dx + static_cast<size_t>(m) * p.d;
       }
-  } else if constexpr (PROB == PROB_DWD || PROB == PROB_DWGU || PROB == PROB_DXR ||
-                       PROB == PROB_DWROUTER) {
+    };
+    __syncthreads();  // every wave is done with the ring
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ir = wm * 64 + mf * 16 + fq * 4 + i;
-        if (ir >= t.mlim) continue;
+      for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf) {
-          const int j = wn * 64 + nf * 16 + fr;
-          if (j >= t.nlim) continue;
-          const float v = acc[mf][nf][i];
-          const int m = t.m0 + ir, n = t.n0 + j;
-          if constexpr (PROB == PROB_DWD) {
-            float* o = sh ? p.dws_down : p.dw_down + static_cast<size_t>(t.e) * p.d * H;
-            o[static_cast<size_t>(m) * H + n] = v;
-          } else if constexpr (PROB == PROB_DWGU) {
-            const bool up = m >= H;
-            float* o = up ? (sh ? p.dws_up : p.dw_up) : (sh ? p.dws_gate : p.dw_gate);
-            if (!sh) o += static_cast<size_t>(t.e) * H * p.d;
-            o[static_cast<size_t>(up ? m - H : m) * p.d + n] = v;
-          } else if constexpr (PROB == PROB_DXR) {
-            // routed rows go to their (token, slot) pair's row, so that a
-            // token's k rows are adjacent for the final sum
-            const int orow = sh ? t.row0 + ir : p.perm[t.row0 + ir];
-            float* o = sh ? p.dx_s : p.dxr;
-            o[static_cast<size_t>(orow) * p.d + n] = v;
-          } else {
-            p.rpart[(static_cast<size_t>(t.e) * p.E + m) * p.d + n] = v;
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int nf = 0; nf < 4; ++nf)
+            Sw[(mm * 16 + fq * 4 + i) * 64 + ((nf ^ fq) << 4) + fr] = acc[2 * pass + mm][nf][i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int q = j * 64 + lane, row = q >> 4, ch = q & 15;
+        float4 v = *reinterpret_cast<const float4*>(
+            Sw + row * 64 + ((((ch >> 2) ^ (row >> 2)) & 3) << 4) + (ch & 3) * 4);
+        const int ir = wm * 64 + pass * 32 + row, col = wn * 64 + ch * 4;
+        if (ir < t.mlim && col < t.nlim) {
+          if constexpr (PROB == PROB_DXROUTER) {
+            if (p.dpre != nullptr) {
+              const float dp = p.dpre[t.m0 + ir];
+              const uint16_t* w = p.w_shared_gate + t.n0 + col;
+              v.x += dp * bf16_to_f32(w[0]); v.y += dp * bf16_to_f32(w[1]);
+              v.z += dp * bf16_to_f32(w[2]); v.w += dp * bf16_to_f32(w[3]);
+            }
           }
+          *reinterpret_cast<float4*>(dst_row(ir) + t.n0 + col) = v;
         }
       }
-  } else {  // PROB_DXROUTER: dL W_r (+ the shared gate's term); the dx rows
-            // are added by dx_finish_kernel
-#pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ir = wm * 64 + mf * 16 + fq * 4 + i;
-        if (ir >= t.mlim) continue;
-        const int tok = t.m0 + ir;
-        const float dpre = p.dpre != nullptr ? p.dpre[tok] : 0.f;
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf) {
-          const int j = wn * 64 + nf * 16 + fr;
-          if (j >= t.nlim) continue;
-          const int c = t.n0 + j;
-          float v = acc[mf][nf][i];
-          if (p.dpre != nullptr) v += dpre * bf16_to_f32(p.w_shared_gate[c]);
-          p.dx[static_cast<size_t>(tok) * p.d + c] = v;
-        }
-      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
   }
 }
 
