@@ -28,15 +28,16 @@
 //
 // Every product is one kernel, bwd_gemm<PROB>: 128 x 128 output tiles per
 // 256-thread workgroup (4 waves of 64 x 64 on v_mfma_f32_16x16x32_bf16), K in
-// 32-deep stages streamed by direct global->LDS loads through a ring of S
-// stages. An operand stored with K contiguous is read out of LDS with 16-byte
+// 32-deep stages streamed by direct global->LDS loads through a ring of two or
+// three stages (by product). An operand stored with K contiguous is read out of LDS with 16-byte
 // reads; one stored with K as its row index (the weight gradients reduce
 // over rows; the weights are read along their output dimension for the
 // input gradients) lands as it is stored and is transposed by the fragment
 // reads themselves (ds_read_b64_tr_b16). Routed rows of x and dO are read
 // through their token (rtok[r] = perm[r] / k, one small kernel): once per
 // tile where the rows are the output rows, and by scalar loads one stage
-// ahead where they are the reduction (the weight gradients).
+// ahead where they are the reduction (the weight gradients). Every epilogue
+// stages its outputs through the then idle ring and stores 16 bytes per lane.
 
 #include "device_common.h"
 #include "moe_internal.h"
@@ -384,7 +385,8 @@ __device__ __forceinline__ float silu_grad_f32(float z) {
 // LDS stages and workgroups per CU by product: the weight gradients and the
 // dx rows run faster with more workgroups per CU than with deeper rings
 // (two 16 KB stages, four workgroups); the others keep three stages and
-// three workgroups (the final-dx router product's registers do not fit four).
+// three workgroups (z stages its bf16 outputs in the 48 KB ring; dW_r's
+// registers do not fit four workgroups).
 template <int PROB>
 constexpr bool bwd_wide() { return PROB == PROB_DWD || PROB == PROB_DWGU || PROB == PROB_DXR; }
 template <int PROB>
