@@ -101,6 +101,32 @@ def ridge_flop_per_byte(peak_flops=PEAK_BF16_MFMA_FLOPS, peak_bytes=PEAK_HBM_BYT
     return peak_flops / peak_bytes
 
 
+def backward_stage_bytes(T, d, E, h, k, hs=0, U=None):
+    """Bytes each stage of the layer backward must move through HBM at least
+    once (bf16 activations and weights, float32 gradients and float32 da'),
+    the shared expert's included; U: experts touched (all of E by default).
+    route: x and W_r in, logits out; d_hidden: dO and W_d in, da' out; z: x,
+    W_g|u and da' in, g a and dz out; router_grad: the gate-gradient partials
+    and logits in, dL out; dW_down: dO and g a in, dW_d out; dW_gate|up: dz
+    and x in, dW_g|u out; dx rows: dz and W_g|u in, the rows out; dx_router:
+    dL, W_r, x and the rows in, dx and dW_r out."""
+    P = T * k
+    U = min(E, P) if U is None else U
+    a, f = 2.0, 4.0  # bf16, float32
+    gp = -(-h // 32) + (-(-hs // 32) if hs else 0)
+    return {"route": (E * d + T * d) * a + T * E * f,
+            "d_hidden": T * d * a + (U * d * h + d * hs) * a + (P * h + T * hs) * f,
+            "z": T * d * a + 2.0 * (U * h * d + hs * d) * a + (P * h + T * hs) * f
+                 + 3.0 * (P * h + T * hs) * a,
+            "router_grad": P * gp * f + T * E * f + T * E * a,
+            "dw_down": T * d * a + (P * h + T * hs) * a + (E * d * h + d * hs) * f,
+            "dw_gate_up": 2.0 * (P * h + T * hs) * a + T * d * a + 2.0 * (E * h * d + hs * d) * f,
+            "dx_rows": 2.0 * (P * h + T * hs) * a + 2.0 * (U * h * d + hs * d) * a
+                       + (P * d + (T * d if hs else 0)) * f,
+            "dx_router": T * E * a + E * d * a + T * d * a + (P * d + (T * d if hs else 0)) * f
+                         + T * d * f + E * d * f}
+
+
 def backward_stage_flops(T, d, E, h, k, hs=0, shared_gate=False):
     """FLOPs of each stage of the layer backward (the products it runs,
     the recomputed gate/up pre-activations included): z = 4 P d h, the

@@ -69,3 +69,24 @@ def test_backward_stage_flops_add_up():
     expect = 2.0 * T * d * E + recompute + 2.0 * fwd_experts + 2 * (2.0 * T * d * E) + 4.0 * T * d
     assert abs(sum(st.values()) - expect) <= 1e-9 * expect
     assert st["router_grad"] == 0.0
+
+
+def test_backward_stage_bytes_terms():
+    """The backward's byte model, term by term for the weight gradients (the
+    float32 outputs dominate at the gemma shape: dW_gate|up is HBM-bound
+    there and MFMA-bound at the skewed-prefill shape)."""
+    T, d, E, h, k = 8192, 640, 256, 512, 4
+    P = T * k
+    b = R.backward_stage_bytes(T, d, E, h, k)
+    assert b["dw_gate_up"] == 2 * P * h * 2 + T * d * 2 + 2 * E * h * d * 4
+    assert b["dw_down"] == T * d * 2 + P * h * 2 + E * d * h * 4
+    f = R.backward_stage_flops(T, d, E, h, k)
+    assert f["dw_gate_up"] / R.PEAK_BF16_MFMA_FLOPS < b["dw_gate_up"] / R.PEAK_HBM_BYTES
+    T, d, E, h, k = 16384, 2048, 128, 768, 8
+    b = R.backward_stage_bytes(T, d, E, h, k)
+    f = R.backward_stage_flops(T, d, E, h, k)
+    assert f["dw_gate_up"] / R.PEAK_BF16_MFMA_FLOPS > b["dw_gate_up"] / R.PEAK_HBM_BYTES
+    # the shared expert adds its own rows and weights
+    bs = R.backward_stage_bytes(300, 64, 8, 32, 2, hs=96)
+    bn = R.backward_stage_bytes(300, 64, 8, 32, 2)
+    assert bs["dw_gate_up"] - bn["dw_gate_up"] == 2 * 300 * 96 * 2 + 2 * 96 * 64 * 4
