@@ -868,6 +868,12 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
       if (p.P >= 32 * p.E) return launch_pers<PersShape<0, 2, 4, 4, 3, 64>>(p, s);
       return launch_shape<GemmShape<0, 2, 2, 4, 4, 32>>(p, s);
     }
+    // down: output widths that are multiples of 160 (gemma's d = 640) in
+    // 160-column tiles of 5 fragments per wave and 64-deep slices: a fifth
+    // fewer re-reads of each row tile than 128-column tiles, and no column
+    // tail; other widths in 128-column tiles with 32-deep slices
+    if (p.N % 160 == 0 && (p.shared_T == 0 || p.sN % 160 == 0))
+      return launch_shape<GemmShape<1, 2, 2, 5, 2, 64>>(p, s);
     return launch_shape<GemmShape<1, 2, 2, 4, 4, 32>>(p, s);
   }
   const long long n = static_cast<long long>(p.P) * p.N + static_cast<long long>(p.shared_T) * p.sN;
