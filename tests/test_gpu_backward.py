@@ -58,6 +58,10 @@ CASES = {
     "big_tiles_shared": small_spec("shared_routed", T=600, d=136, E=3, h=96, k=2, shared_h=200),
     "big_tiles_sigmoid": small_spec("small_moe_sigmoid", T=520, d=128, E=4, h=64, k=2,
                                     shared_h=128),
+    # 20 slots per token without renormalisation (the dx rows summed in batches
+    # of 8 with a tail of 4; the slot gradients spread over lanes)
+    "sigmoid_k20": small_spec("small_moe_sigmoid", T=90, d=128, E=64, h=32, k=20, shared_h=0,
+                              renormalize=False),
 }
 
 GRADS = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up", "dws_down",
