@@ -144,9 +144,11 @@ def main():
                     help="minimum bytes of distinct weight copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
-    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
-                    help="forward (the headline) or the layer backward (gradients of "
-                         "sum(out * dout), recomputing route and pre-activations)")
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward", "stats"),
+                    default="forward",
+                    help="forward (the headline), the layer backward (gradients of "
+                         "sum(out * dout), recomputing route and pre-activations), or the "
+                         "routing statistics of the workload's router logits")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB "
                          "(a reference kernel for scaling profiler byte counters)")
@@ -195,6 +197,9 @@ def main():
     T = spec.T
     if args.which == "backward":
         run_backward(args, spec, inp, cfg, x, wstructs, nsets, B, R, StageEvents)
+        return
+    if args.which == "stats":
+        run_stats(args, spec, inp, cfg, x, w0, B, R, StageEvents)
         return
     out = torch.empty((T, spec.d), dtype=x.dtype, device="cuda")
     ids = torch.empty((T, spec.k), dtype=torch.int32, device="cuda")
@@ -423,6 +428,86 @@ def run_backward(args, spec, inp, cfg, x, wstructs, nsets, B, R, StageEvents):
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle backward baseline")
         result["cpu_baseline"] = cpu_baseline_backward(inp, dout_bits, args.cpu_budget_s)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_stats(inp, counts, budget_s=20.0):
+    """The oracle's routing statistics, as they stand, on a bounded sample of
+    tokens (router logits from the oracle's own router, not timed)."""
+    import oracle.moe_oracle as O
+    spec = inp["spec"]
+    bias = None if spec.mode == O.SIGMOID else inp.get("b_router")
+    L = O.router_logits(inp["x"], inp["w_router"], bias)
+
+    def run(Ts):
+        t0 = time.perf_counter()
+        O.routing_stats(L[:Ts], counts, spec.k, spec.mode, 0.01)
+        return time.perf_counter() - t0
+
+    Ts = min(spec.T, 256)
+    t = run(Ts)
+    while Ts < spec.T and t < budget_s / 6:
+        Ts = min(spec.T, Ts * 2)
+        t = run(Ts)
+    times = [t]
+    while len(times) < 3 and sum(times) + t < budget_s:
+        times.append(run(Ts))
+    med = statistics.median(times)
+    return {"value": Ts / med, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {Ts} of {spec.T} tokens' router logits, float64 NumPy oracle "
+                      f"routing_stats, median of {len(times)} run(s) of {med:.3f} s"}
+
+
+def run_stats(args, spec, inp, cfg, x, w0, B, R, StageEvents):
+    """Routing statistics over the workload's router logits (moe_route's
+    float32 output) and moe_dispatch's counts: K calls queued behind a long
+    matrix product, so the event span is device time, not launch rate."""
+    import torch
+    T, E = spec.T, spec.E
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ids, _ = B.route(cfg, x, w0["w_router"], w0["b_router"], logits=logits)
+    counts, _, _, _ = B.dispatch(cfg, ids)
+    ws = B.alloc_workspace(cfg, B.MOE_ENTRY_ROUTING_STATS)
+    outs = (torch.empty(E, dtype=torch.float32, device="cuda"),
+            torch.empty(E, dtype=torch.float32, device="cuda"),
+            torch.empty(4, dtype=torch.float32, device="cuda"))
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(args.warmup):
+        B.routing_stats(cfg, logits, counts, ws=ws, outs=outs)
+    a = torch.ones((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    ev = StageEvents(1, 1)
+    hip = ev.hip
+    for _ in range(8):  # keeps the device busy while the K calls are queued
+        a @ a
+    hip.hipEventRecord(ev.row(0)[0], stream)
+    for _ in range(args.steps):
+        B.routing_stats(cfg, logits, counts, ws=ws, outs=outs)
+    hip.hipEventRecord(ev.row(0)[1], stream)
+    torch.cuda.synchronize()
+    hip.hipEventSynchronize(ev.row(0)[1])
+    us = ev.elapsed_ms(ev.row(0)[0], ev.row(0)[1]) * 1e3 / args.steps
+    ev.destroy()
+    log(f"[bench] routing stats: {us:.2f} us/call over {args.steps} queued calls")
+    nbytes = R.routing_stats_bytes(T, E)
+    roof = {"bound": "hbm", "achieved": nbytes / (us * 1e-6) / 1e9,
+            "peak": R.PEAK_HBM_BYTES / 1e9, "unit": "GB/s"}
+    roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": None,
+                 "alg_bytes": nbytes, "kernel": "routing_stats (both kernels)"})
+    result = {
+        "metric": "MoE routing statistics tokens/s on 1 GPU (token share, mean router "
+                  "probability, router entropy, load-balance term)",
+        "value": T / (us * 1e-6), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": us * 1e-3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{args.config} routing statistics", "T": T, "E": E,
+                   "top_k": spec.k, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle routing statistics")
+        result["cpu_baseline"] = cpu_baseline_stats(inp, counts.cpu().numpy(), args.cpu_budget_s)
     print(json.dumps(result), flush=True)
 
 

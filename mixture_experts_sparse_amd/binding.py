@@ -289,14 +289,18 @@ def combine(cfg, y, inv, gates, shared=None, out=None, stream=None):
     return out
 
 
-def routing_stats(cfg, logits, counts, alpha=0.01, ws=None, stream=None):
+def routing_stats(cfg, logits, counts, alpha=0.01, ws=None, stream=None, outs=None):
     """(share [E], mean_prob [E], scalars [2] = (entropy, aux)) as device
-    tensors, from router logits [T, E] f32 and counts [E] int32."""
+    tensors, from router logits [T, E] f32 and counts [E] int32. ``outs``:
+    optional preallocated (share [E], mean_prob [E], scalars [>= 2]) f32."""
     import torch
     dev = logits.device
-    share = torch.empty(cfg.E, dtype=torch.float32, device=dev)
-    mean_prob = torch.empty(cfg.E, dtype=torch.float32, device=dev)
-    scalars = torch.empty(4, dtype=torch.float32, device=dev)
+    if outs is not None:
+        share, mean_prob, scalars = outs
+    else:
+        share = torch.empty(cfg.E, dtype=torch.float32, device=dev)
+        mean_prob = torch.empty(cfg.E, dtype=torch.float32, device=dev)
+        scalars = torch.empty(4, dtype=torch.float32, device=dev)
     if ws is None:
         ws = alloc_workspace(cfg, MOE_ENTRY_ROUTING_STATS, dev)
     _check(lib().moe_routing_stats(ctypes.byref(cfg), _ptr(logits), _ptr(counts),

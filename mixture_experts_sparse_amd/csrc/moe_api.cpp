@@ -427,7 +427,7 @@ moe_status moe_routing_stats(const moe_config* cfg, const float* logits, const i
   if (!(alpha >= 0.0f) || alpha == INFINITY) return MOE_ERR_INVALID_ARG;
   MOE_TRY(check_ws(c, MOE_ENTRY_ROUTING_STATS, ws, ws_bytes));
   StatsParams p{logits, counts, c.T, c.E, c.top_k, c.mode, alpha, static_cast<float*>(ws),
-                stats_blocks(c.T), share, mean_prob, scalars};
+                stats_blocks(c.T), stats_tokens_per_block(c.T), share, mean_prob, scalars};
   MOE_HIP(launch_stats(p, as_stream(stream)));
   return MOE_OK;
 }

@@ -233,12 +233,14 @@ struct StatsParams {
   int T, E, k, mode;
   float alpha;
   float* part;            // [nb][E + 1] partial sums (workspace)
-  int nb;                 // stats_blocks(T)
+  int nb;                 // stats_blocks(T), at most 256
+  int tpb;                // stats_tokens_per_block(T): tokens per block
   float* share;           // [E]
   float* mean_prob;       // [E]
   float* scalars;         // [2]: entropy, aux
 };
 int stats_blocks(int T);
+int stats_tokens_per_block(int T);
 hipError_t launch_stats(const StatsParams& p, hipStream_t s);
 
 hipError_t launch_route(const RouteParams& p, int dtype, hipStream_t s);

@@ -140,3 +140,10 @@ def backward_stage_flops(T, d, E, h, k, hs=0, shared_gate=False):
             "dw_gate_up": 4.0 * P * d * h + 4.0 * T * d * hs,
             "dx_rows": 4.0 * P * d * h + 4.0 * T * d * hs,
             "dx_router": 4.0 * T * d * E + (4.0 * T * d if shared_gate else 0.0)}
+
+
+def routing_stats_bytes(T, E):
+    """Algorithmic HBM bytes of one routing-statistics call: the float32
+    logits [T, E] and int32 counts [E] read once, share and mean probability
+    [E] and the two scalars written (the partial table stays in cache)."""
+    return 4.0 * T * E + 4.0 * E + 8.0 * E + 8.0

@@ -69,8 +69,13 @@ def test_workspace_sizes_are_bounded():
     assert ws < gathered / 10
     for e in range(7):
         assert B.workspace_size(c, e) <= ws
-    # routing statistics: one row of E + 1 floats per 256 tokens
-    assert 0 < B.workspace_size(c, B.MOE_ENTRY_ROUTING_STATS) <= (16384 // 256) * 129 * 4 + 256
+    # routing statistics: one row of E + 1 floats per block of at least 32
+    # tokens, at most 256 blocks
+    assert B.workspace_size(c, B.MOE_ENTRY_ROUTING_STATS) == 256 * 129 * 4
+    small = B.make_config(1000, 64, 64, 32, 8)
+    assert B.workspace_size(small, B.MOE_ENTRY_ROUTING_STATS) == (-(-1000 // 32) * 65 * 4 + 255) // 256 * 256
+    huge = B.make_config(1 << 20, 64, 256, 32, 8)
+    assert B.workspace_size(huge, B.MOE_ENTRY_ROUTING_STATS) == 256 * 257 * 4
     assert B.workspace_size(c, B.MOE_ENTRY_DISPATCH) < 8 * 2**20
     assert B.workspace_size(B.make_config(1, 64, 8, 32, 9)) == 0  # invalid cfg
 

@@ -333,6 +333,12 @@ STATS = {
     "stats_sigmoid": small_spec("small_moe_sigmoid", T=513, d=128, E=64, h=32, k=8, shared_h=0),
     "stats_fp32_tiny": SPECS["tiny_fp32"],
     "stats_T1": small_spec("decode", T=1, d=128, E=64, h=32, k=8),
+    # full token counts and expert counts of the layer workloads (the
+    # statistics read only the router): 256 blocks of 32 and of 64 tokens
+    "stats_gemma_full": small_spec("gemma_upcycled", h=16),
+    "stats_skewed_full": small_spec("skewed_prefill", d=256, h=16),
+    # 141 blocks of 64 tokens, the last one ragged inside a wave
+    "stats_ragged_9000": small_spec("skewed_prefill", T=9000, d=128, h=16),
 }
 
 

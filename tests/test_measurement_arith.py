@@ -90,3 +90,10 @@ def test_backward_stage_bytes_terms():
     bs = R.backward_stage_bytes(300, 64, 8, 32, 2, hs=96)
     bn = R.backward_stage_bytes(300, 64, 8, 32, 2)
     assert bs["dw_gate_up"] - bn["dw_gate_up"] == 2 * 300 * 96 * 2 + 2 * 96 * 64 * 4
+
+
+def test_routing_stats_bytes():
+    # the float32 logits dominate: T*E*4, plus counts in and share,
+    # mean probability and the two scalars out
+    assert R.routing_stats_bytes(8192, 256) == 8192 * 256 * 4 + 256 * 4 + 2 * 256 * 4 + 8
+    assert R.routing_stats_bytes(1, 8) == 32 + 32 + 64 + 8
