@@ -72,15 +72,23 @@ STAGE_KERNEL = {"route": ("route_kernel", "route_part_kernel"), "dispatch": ("sc
                 "combine": ("combine_",)}
 
 
-def kernel_sources_sha():
+FWD_SOURCES = ("expert_gemm.hip", "route_dispatch.hip", "combine.hip")
+BWD_SOURCES = ("backward.hip", "route_dispatch.hip")
+# kernel-name prefixes of each backward stage's product
+BWD_STAGE_KERNEL = {"d_hidden": ("bwd_gemm<1>",), "z": ("bwd_gemm<0>",),
+                    "dw_down": ("bwd_gemm<2>",), "dw_gate_up": ("bwd_gemm<3>",),
+                    "dx_rows": ("bwd_gemm<4>",), "dx_router": ("bwd_gemm<5>",),
+                    "router_grad": ("router_bwd_kernel",), "route": ("route_kernel",)}
+
+
+def kernel_sources_sha(files=FWD_SOURCES):
     import hashlib
     d = os.path.join(ROOT, "mixture_experts_sparse_amd", "csrc")
-    src = b"".join(open(os.path.join(d, f), "rb").read()
-                   for f in ("expert_gemm.hip", "route_dispatch.hip", "combine.hip"))
+    src = b"".join(open(os.path.join(d, f), "rb").read() for f in files)
     return hashlib.sha256(src).hexdigest()[:16]
 
 
-def recorded_traffic(workload, stage):
+def recorded_traffic(workload, stage, stage_kernel=STAGE_KERNEL, files=FWD_SOURCES):
     """HBM bytes per launch of a stage's kernel from the committed rocprofv3
     FETCH_SIZE/WRITE_SIZE record, or None when there is no record for this
     workload or the kernels have changed since it was taken."""
@@ -89,10 +97,10 @@ def recorded_traffic(workload, stage):
         rec = json.load(open(path)).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernels_sha256_16") != kernel_sources_sha():
+    if not rec or rec.get("kernels_sha256_16") != kernel_sources_sha(files):
         return None
     for name, t in rec["per_launch"].items():
-        if any(k in name for k in STAGE_KERNEL[stage]):
+        if any(k in name for k in stage_kernel.get(stage, ())):
             return t["fetch_bytes"] + t["write_bytes"]
     return None
 
@@ -392,6 +400,14 @@ def run_backward(args, spec, inp, cfg, x, wstructs, nsets, B, R, StageEvents):
     stage = np.array(ev.stage_ms())
     traced_ms = ev.span_ms() / args.steps
     ev.destroy()
+    if args.calibrate_copy_mib > 0:
+        src = torch.empty(args.calibrate_copy_mib * 2**20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] reference copy of {args.calibrate_copy_mib} MiB done")
+        del src, dst
     mean_stage_us = {n: float(stage[:, i].mean() * 1e3) for i, n in enumerate(B.BWD_STAGE_NAMES)}
     flops = R.backward_stage_flops(T, spec.d, spec.E, spec.h, spec.k, spec.shared_h,
                                    spec.shared_gate)
@@ -406,7 +422,9 @@ def run_backward(args, spec, inp, cfg, x, wstructs, nsets, B, R, StageEvents):
     else:
         roof = {"bound": "hbm", "achieved": nbytes[dom] / dsec / 1e9,
                 "peak": R.PEAK_HBM_BYTES / 1e9, "unit": "GB/s"}
-    roof.update({"frac": roof["achieved"] / roof["peak"], "traffic": None,
+    roof.update({"frac": roof["achieved"] / roof["peak"],
+                 "traffic": recorded_traffic(f"{args.config} backward", dom, BWD_STAGE_KERNEL,
+                                             BWD_SOURCES),
                  "alg_flops": flops[dom], "alg_bytes": nbytes[dom], "kernel": dom})
     total = sum(flops.values())
     sec = ms_per_step * 1e-3

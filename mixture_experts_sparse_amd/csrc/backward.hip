@@ -79,15 +79,37 @@ struct Tile {
   int k0, k1;      // K range (stored-row indices for K-as-row operands)
 };
 
+// Workgroup b runs on XCD b mod 8 (workgroups are dispatched round robin
+// over the 8 XCDs). For the row products (z, d_hidden, dx rows) whose
+// per-expert weight operand fits one XCD's 4 MB L2, each XCD gets one
+// contiguous range of the n real tiles, so the column tiles of a row tile
+// (which read the same rows) and the row tiles of an expert (which read the
+// same weights) share that L2; numbered straight through, column tile k of
+// a row tile fell to XCD k mod 8 and every XCD fetched the rows again.
+// With larger weights (or for the weight gradients, whose tile work grows
+// with the expert's rows) the straight order spreads each expert's weights
+// and work over all XCDs and is faster. Returns -1 for workgroups past the
+// real tiles of an upper-bound grid.
+__device__ __forceinline__ int xcd_tile(int b, int n) {
+  if (b >= n) return -1;
+  const int x = b & 7, j = b >> 3;
+  const int q = n >> 3, rem = n & 7;
+  return (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + j;
+}
+
 template <int PROB>
 __device__ bool decode(const BwdParams& p, Tile& t) {
-  const int b = blockIdx.x;
+  int b = blockIdx.x;
   const bool sh = p.shared;
   const int H = sh ? p.hs : p.h;
   if constexpr (PROB == PROB_Z || PROB == PROB_DA || PROB == PROB_DXR) {
     // rows of one expert (routed: through the tile table; shared: all tokens)
     const int ncols = PROB == PROB_Z ? 2 * H : (PROB == PROB_DA ? H : p.d);
     const int NT = (ncols + TN - 1) / TN;
+    if (p.xcd_rows) {
+      b = xcd_tile(b, NT * (sh ? (p.T + TM - 1) / TM : p.meta[0]));
+      if (b < 0) return false;
+    }
     const int q = b / NT, nt = b - q * NT;
     t.n0 = nt * TN;
     t.nlim = min(TN, ncols - t.n0);
@@ -771,7 +793,14 @@ hipError_t launch_prob(const BwdParams& p, hipStream_t s) {
   }
   if (nblk <= 0) return hipSuccess;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-  bwd_gemm<PROB><<<static_cast<unsigned>(nblk), NT_, 0, s>>>(p);
+  BwdParams q = p;
+  q.xcd_rows = 0;
+  if constexpr (PROB == PROB_Z || PROB == PROB_DA || PROB == PROB_DXR) {
+    // the expert's weight operand: [d, 2H] (z), [H, d] (d_hidden), [2H, d] (dx rows)
+    const long long wbytes = 2LL * p.d * (PROB == PROB_DA ? H : 2 * H);
+    q.xcd_rows = wbytes <= (4LL << 20) ? 1 : 0;
+  }
+  bwd_gemm<PROB><<<static_cast<unsigned>(nblk), NT_, 0, s>>>(q);
   return hipGetLastError();
 }
 

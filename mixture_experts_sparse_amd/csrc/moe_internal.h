@@ -282,6 +282,7 @@ struct BwdParams {
   float *dx, *dw_router, *dw_gate, *dw_up, *dw_down;
   float *dws_gate, *dws_up, *dws_down, *dw_shared_gate;
   float *dgates, *dlogits;    // optional copies
+  int xcd_rows;               // row products: one contiguous tile range per XCD (set per launch)
 };
 hipError_t launch_backward(const BwdParams& p, hipStream_t s, void* const* ev);
 // Tokens per partial sum of dW_r in the backward (the workspace holds
