@@ -745,13 +745,27 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(BwdParams p) {
 }
 
 // dw_router = the dW_r partials summed in chunk order.
+// Four adjacent elements per thread (E*d is a multiple of 8, the slabs and
+// dw_router 16-byte aligned), the slabs' 16-byte loads issued 8 at a time,
+// each element still summed in slab order.
 __global__ __launch_bounds__(256) void router_grad_sum_kernel(BwdParams p, int nch) {
   const size_t n = static_cast<size_t>(p.E) * p.d;
-  const size_t i = blockIdx.x * 256ull + threadIdx.x;
+  const size_t i = (blockIdx.x * 256ull + threadIdx.x) * 4;
   if (i >= n) return;
-  float s = 0.f;
-  for (int c = 0; c < nch; ++c) s += p.rpart[static_cast<size_t>(c) * n + i];
-  p.dw_router[i] = s;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < nch; c0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = *reinterpret_cast<const float4*>(p.rpart + static_cast<size_t>(min(c0 + u, nch - 1)) * n + i);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (c0 + u < nch) {
+        s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+      }
+    }
+  }
+  *reinterpret_cast<float4*>(p.dw_router + i) = s;
 }
 
 // dw_shared_gate[c] = sum_t dpre[t] x[t, c]: column partial sums over token
@@ -870,7 +884,8 @@ hipError_t launch_backward(const BwdParams& p0, hipStream_t s, void* const* ev) 
   {
     const int nch = (p.T + kRouterKChunk - 1) / kRouterKChunk;
     const size_t n = static_cast<size_t>(p.E) * p.d;
-    router_grad_sum_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(p, nch);
+    if (n % 4 != 0) return hipErrorInvalidValue;  // d is a multiple of 8
+    router_grad_sum_kernel<<<static_cast<unsigned>((n / 4 + 255) / 256), 256, 0, s>>>(p, nch);
     BWD_TRY(hipGetLastError());
   }
   if (p.dpre != nullptr) {
