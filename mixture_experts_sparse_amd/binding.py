@@ -106,8 +106,7 @@ def lib() -> ctypes.CDLL:
     """The loaded libmoe.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        # MOE_LIBRARY: an alternative build of the same library (tuning builds)
-        path = os.environ.get("MOE_LIBRARY") or LIB_PATH
+        path = LIB_PATH
         if not os.path.exists(path):
             raise RuntimeError(
                 f"{path} is missing: build it with "

@@ -18,7 +18,8 @@ Two formulas from the pages pin this module's arithmetic:
 * the gathered-weight tensor a naive dispatch builds, T*h*d*bytes
   ("Small models, sparse experts", section "Dispatch decides everything":
   one projection, one layer, 2,048 tokens, [2048, 512, 640] fp32 = 2.68 GB);
-* the batch-1 decode ceiling, bandwidth / bytes of active weights
+* the memory-bound decode limit: a step that must stream B bytes per
+  token from memory of bandwidth W runs at most W / B tokens per second
   ("Small MoE Architecture, in depth", section "Worked example: the batch-1
   budget on a device").
 """
@@ -89,12 +90,19 @@ def dense_to_sparse_flop_ratio(E, k):
     return E / k
 
 
-def batch1_decode_ceiling(total_params, active_params, bytes_per_param, mem_gb_s):
-    """(footprint GB, upper bound tokens/s) when every active weight is
-    streamed once per token."""
-    footprint_gb = total_params * bytes_per_param / 1e9
-    per_token_gb = active_params * bytes_per_param / 1e9
-    return footprint_gb, mem_gb_s / per_token_gb
+def stream_bound_tokens_per_s(bytes_per_token, bandwidth_bytes_per_s=PEAK_HBM_BYTES):
+    """Tokens per second a memory-bound step cannot exceed when each token
+    must stream ``bytes_per_token`` from memory at the given bandwidth."""
+    return bandwidth_bytes_per_s / bytes_per_token
+
+
+def decode_bound_tokens_per_s(T, d, E, h, U, elem_bytes, expert_bytes=None,
+                              bandwidth_bytes_per_s=PEAK_HBM_BYTES):
+    """The HBM bound of one decode-shaped layer call: the call's algorithmic
+    bytes (``layer_bytes``, U touched experts) streamed once at the given
+    bandwidth, for T tokens."""
+    per_call = layer_bytes(T, d, E, h, U, elem_bytes, expert_bytes=expert_bytes)
+    return T * stream_bound_tokens_per_s(per_call, bandwidth_bytes_per_s)
 
 
 def ridge_flop_per_byte(peak_flops=PEAK_BF16_MFMA_FLOPS, peak_bytes=PEAK_HBM_BYTES):

@@ -404,15 +404,6 @@ def route(inp, ids_override=None):
     return L, ids, g, p
 
 
-def route_scores(inp):
-    """The selection scores of ``route`` (logits, or sigmoid + balance bias)."""
-    spec = inp["spec"]
-    if spec.mode == SIGMOID:
-        return selection_scores(router_logits(inp["x"], inp["w_router"], None), SIGMOID,
-                                inp.get("b_router"))
-    return router_logits(inp["x"], inp["w_router"], inp.get("b_router"))
-
-
 def layer_forward(inp, ids_override=None):
     """Steps 1-7 on the whole batch. Returns a dict with out [T, d] (float64),
     logits, ids, gates, counts, offsets, perm, inv, y (sorted, un-gated),

@@ -31,10 +31,16 @@ The pins:
   4-bit experts   - the dequantisation against the error bound of an affine
                     4-bit code (at most half a step), exact recovery of
                     weights built from known codes (distinct per position, so
-                    a nibble-order or group-index slip shows), and the bytes
+                    a nibble-order or group-index slip shows), the bytes
                     per weight against the page's "about half a byte"
                     ("Small MoE Architecture, in depth", section "Worked
-                    example: the batch-1 budget on a device")
+                    example: the batch-1 budget on a device"), and the whole
+                    layer on quantised experts against the layer on the
+                    weights the codes stand for, decoded position by position
+  bf16 decode     - every finite bf16 bit pattern against the format's
+                    definition (sign, biased exponent, fraction, subnormals),
+                    and a whole layer on bf16 bits against the same layer on
+                    their float64 values
   routing stats   - the 12.5% ideal share of a balanced 8-expert top-2 layer
                     ("Mini-MoE", section "Results"; tests/golden), entropy ln E
                     for a flat router and 0 in the one-hot limit, the Switch
@@ -44,6 +50,7 @@ The pins:
 
 from __future__ import annotations
 
+import dataclasses
 import itertools
 import json
 import math
@@ -575,6 +582,124 @@ def check_q4_bytes_per_weight():
 
 
 # ---------------------------------------------------------------------------
+# exact bf16 input decode
+# ---------------------------------------------------------------------------
+
+def _bf16_value(bits):
+    """A bf16 bit pattern's value from the format's definition: sign bit 15,
+    8 exponent bits (bias 127), 7 fraction bits; exponent 0 holds zero and
+    the subnormals 2^-126 * m/128. Python integer and ldexp arithmetic,
+    exact."""
+    sign = -1.0 if (bits >> 15) & 1 else 1.0
+    e = (bits >> 7) & 0xFF
+    m = bits & 0x7F
+    if e == 0:
+        return sign * math.ldexp(m, -126 - 7)
+    return sign * math.ldexp(128 + m, e - 127 - 7)
+
+
+def check_bf16_decode():
+    """The oracle reads bf16 inputs exactly: every finite bit pattern (both
+    zeros, all subnormals and normals up to +-max) decodes to the value the
+    format defines, and a whole layer given bf16 bits equals the same layer
+    given those values as float64."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    finite = ((bits >> 7) & 0xFF) != 0xFF
+    bits = bits[finite].astype(np.uint16)
+    got = O.to_f64(bits)
+    assert got.dtype == np.float64
+    want = np.array([_bf16_value(int(b)) for b in bits], dtype=np.float64)
+    assert np.array_equal(got, want), np.nonzero(got != want)[0][:5]
+    # landmarks: +-0, the smallest subnormal, 1, -2, +-max
+    marks = {0x0000: 0.0, 0x8000: -0.0, 0x0001: 2.0 ** -133, 0x3F80: 1.0, 0xC000: -2.0,
+             0x7F7F: (2 - 2 ** -7) * 2.0 ** 127, 0xFF7F: -(2 - 2 ** -7) * 2.0 ** 127}
+    for b, v in marks.items():
+        assert O.to_f64(np.array([b], np.uint16))[0] == v, hex(b)
+    assert math.copysign(1.0, O.to_f64(np.array([0x8000], np.uint16))[0]) == -1.0
+
+    # a layer with every input in bf16 bits against the same layer on float64
+    from moe_inputs.spec import MoESpec, BF16
+    r = _rng(91)
+    T, d, E, h, k, hs = 9, 16, 6, 8, 2, 8
+    spec = MoESpec(name="pin_bf16", T=T, d=d, E=E, h=h, k=k, dtype=BF16, mode=O.SOFTMAX_ALL,
+                   renormalize=True, shared_h=hs, shared_gate=True)
+
+    def bits_of(shape, std):
+        f = (r.standard_normal(shape) * std).astype(np.float32)
+        return (f.view(np.uint32) >> 16).astype(np.uint16)  # truncation: any bf16 bits do
+
+    shapes = {"x": ((T, d), 1.0), "w_router": ((E, d), 0.5), "w_gate": ((E, h, d), 0.3),
+              "w_up": ((E, h, d), 0.3), "w_down": ((E, d, h), 0.3), "ws_gate": ((hs, d), 0.3),
+              "ws_up": ((hs, d), 0.3), "ws_down": ((d, hs), 0.3), "w_shared_gate": ((d,), 0.3)}
+    b_inp = {n: bits_of(*sv) for n, sv in shapes.items()}
+    f_inp = {n: np.vectorize(_bf16_value, otypes=[np.float64])(v.astype(np.int64))
+             for n, v in b_inp.items()}
+    for dct in (b_inp, f_inp):
+        dct.update(spec=spec, b_router=None, w_gate_sb=None, w_up_sb=None, w_down_sb=None)
+    rb, rf = O.layer_forward(b_inp), O.layer_forward(f_inp)
+    assert np.array_equal(rb["ids"], rf["ids"])
+    assert np.array_equal(rb["out"], rf["out"])
+    assert np.max(np.abs(rf["out"])) > 0
+
+
+# ---------------------------------------------------------------------------
+# the layer on 4-bit routed experts
+# ---------------------------------------------------------------------------
+
+def _q4_decode(packed, sb):
+    """The 4-bit format read back element by element: byte i of a row holds
+    position 2i in its low nibble and 2i+1 in its high nibble; word g holds
+    the bf16 scale of positions 64g..64g+63 in its low half and the bf16 bias
+    in its high half."""
+    packed = np.asarray(packed)
+    sb = np.asarray(sb)
+    rows = packed.reshape(-1, packed.shape[-1])
+    words = sb.reshape(-1, sb.shape[-1])
+    K = rows.shape[1] * 2
+    out = np.empty((rows.shape[0], K))
+    for r in range(rows.shape[0]):
+        for pos in range(K):
+            byte = int(rows[r, pos // 2])
+            q = (byte >> 4) if pos % 2 else (byte & 15)
+            w = int(words[r, pos // 64])
+            out[r, pos] = _bf16_value(w & 0xFFFF) * q + _bf16_value(w >> 16)
+    return out.reshape(packed.shape[:-1] + (K,))
+
+
+def check_q4_layer_forward():
+    """The layer on quantised routed experts equals the layer on the float64
+    weights those codes stand for (decoded here, position by position), with
+    a bf16 shared expert beside them. Each matrix has its own scale words, so
+    a pairing of one matrix's codes with another's scales shows."""
+    from moe_inputs.generate import quantize_q4_g64
+    from moe_inputs.spec import MoESpec, BF16
+    r = _rng(93)
+    T, d, E, h, k, hs = 10, 128, 4, 64, 2, 64
+    spec = MoESpec(name="pin_q4", T=T, d=d, E=E, h=h, k=k, dtype=BF16, mode=O.SOFTMAX_ALL,
+                   renormalize=False, shared_h=hs, expert_quant="q4_g64")
+
+    def bits(shape, std):
+        return ((r.standard_normal(shape) * std).astype(np.float32).view(np.uint32)
+                >> 16).astype(np.uint16)
+
+    q_inp = {"spec": spec, "x": bits((T, d), 1.0), "w_router": bits((E, d), 0.3),
+             "b_router": None, "ws_gate": bits((hs, d), 0.1), "ws_up": bits((hs, d), 0.1),
+             "ws_down": bits((d, hs), 0.1), "w_shared_gate": None}
+    f_inp = dict(q_inp, spec=dataclasses.replace(spec, expert_quant=None),
+                 w_gate_sb=None, w_up_sb=None, w_down_sb=None)
+    for name, shape, std in (("w_gate", (E, h, d), 0.1), ("w_up", (E, h, d), 0.05),
+                             ("w_down", (E, d, h), 0.2)):
+        w = (r.standard_normal(shape) * std).astype(np.float32)
+        q_inp[name], q_inp[name + "_sb"] = quantize_q4_g64(w)
+        f_inp[name] = _q4_decode(q_inp[name], q_inp[name + "_sb"])
+    rq, rf = O.layer_forward(q_inp), O.layer_forward(f_inp)
+    assert np.array_equal(rq["ids"], rf["ids"])
+    scale = float(np.max(np.abs(rf["out"])))
+    assert scale > 0
+    np.testing.assert_allclose(rq["out"], rf["out"], rtol=0, atol=1e-12 * scale)
+
+
+# ---------------------------------------------------------------------------
 # backward: pinned by automatic differentiation of the dense formulation and
 # by finite differences of the forward
 # ---------------------------------------------------------------------------
@@ -756,6 +881,8 @@ ALL_CHECKS = [
     check_q4_roundtrip_error_bound,
     check_q4_known_codes,
     check_q4_bytes_per_weight,
+    check_q4_layer_forward,
+    check_bf16_decode,
     check_backward_autograd_dense,
     check_backward_finite_differences,
     check_backward_softmax_logit_grads_sum_to_zero,

@@ -31,12 +31,30 @@ def test_dense_waste_ratio_matches_printed():
 
 
 def test_decode_ceilings_match_printed():
+    """The page's worked decode budget: a model's resident footprint is its
+    total parameter count times the bytes per parameter, and its batch-1 rate
+    is bounded by the memory bandwidth over the bytes of the parameters one
+    token activates. The bound is the product's own stream_bound_tokens_per_s."""
     g = _fig()["decode_ceilings"]
+    bw = g["mem_gb_s"] * 1e9
     for row in g["rows"]:
-        fp, tps = R.batch1_decode_ceiling(row["total"], row["active"], g["bytes_per_param"],
-                                          g["mem_gb_s"])
-        assert round(fp, 2) == row["footprint_gb"], row
-        assert round(tps) == row["ceiling_tok_s"], row
+        footprint_gb = row["total"] * g["bytes_per_param"] / 1e9
+        assert round(footprint_gb, 2) == row["footprint_gb"], row
+        per_token = row["active"] * g["bytes_per_param"]
+        assert round(R.stream_bound_tokens_per_s(per_token, bw)) == row["ceiling_tok_s"], row
+
+
+def test_decode_bound_uses_layer_bytes():
+    """The decode HBM bound the bench reports: the layer's algorithmic bytes
+    at T = 1 (8 touched experts of 12,582,912 bytes, router, x and out) at
+    8 TB/s, about 79.3 k tokens/s; 4-bit experts move 0.5625 / 2 of the
+    expert bytes."""
+    b = 8 * 12_582_912 + 64 * 2048 * 2 + 2 * 2048 * 2
+    assert R.layer_bytes(1, 2048, 64, 1024, 8, 2) == b
+    assert abs(R.decode_bound_tokens_per_s(1, 2048, 64, 1024, 8, 2) - 8e12 / b) < 1e-6
+    assert abs(R.decode_bound_tokens_per_s(1, 2048, 64, 1024, 8, 2) - 79.3e3) < 0.1e3
+    q = R.decode_bound_tokens_per_s(1, 2048, 64, 1024, 8, 2, R.Q4_BYTES_PER_WEIGHT)
+    assert q == 8e12 / (8 * 3 * 2048 * 1024 * 0.5625 + 64 * 2048 * 2 + 2 * 2048 * 2)
 
 
 def test_workload_counts():

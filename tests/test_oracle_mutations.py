@@ -161,7 +161,23 @@ def _swiglu_bwd_down_from_preactivation(X, Wg, Wu, Wd, dY):
     return dX, dWg, dWu, dY.T @ (X @ Wu.T)
 
 
-_ORIG = {n: getattr(O, n) for n in ("gate_weights", "dispatch", "combine", "gate_up",
+def _bf16_shift8(a):
+    # bf16 bits placed 8 bits too low in the float32 word
+    if a is not None and np.asarray(a).dtype == np.uint16:
+        return (np.asarray(a).astype(np.uint32) << np.uint32(8)).view(np.float32).astype(np.float64)
+    return _ORIG["to_f64"](a)
+
+
+def _q4_up_with_gate_scales(inp):
+    # the up projection's codes paired with the gate projection's scale words
+    if inp.get("w_gate_sb") is not None:
+        return (O.dequantize_q4(inp["w_gate"], inp["w_gate_sb"]),
+                O.dequantize_q4(inp["w_up"], inp["w_gate_sb"]),
+                O.dequantize_q4(inp["w_down"], inp["w_down_sb"]))
+    return _ORIG["expert_weights"](inp)
+
+
+_ORIG = {n: getattr(O, n) for n in ("to_f64", "expert_weights", "gate_weights", "dispatch", "combine", "gate_up",
                                     "down", "shared_expert", "router_logits", "topk_select",
                                     "silu", "selection_scores", "routing_stats",
                                     "dequantize_q4", "gate_logit_grad", "swiglu_backward")}
@@ -193,6 +209,8 @@ MUTATIONS = [
     ("gate_logit_grad", _logit_grad_renorm_ignored),
     ("swiglu_backward", _swiglu_bwd_up_uses_z),
     ("swiglu_backward", _swiglu_bwd_down_from_preactivation),
+    ("to_f64", _bf16_shift8),
+    ("expert_weights", _q4_up_with_gate_scales),
 ]
 
 
