@@ -4,17 +4,22 @@
 A step is one moe_layer_forward call (route, dispatch, gate/up, down,
 combine, and the shared expert where the workload has one) over one batch of
 seeded synthetic tokens, with the inputs already resident in HBM. Steps
-rotate over R distinct copies of the layer's weights (like a stack of
-layers), R chosen so that the copies span at least 2 GiB: the 256 MB
-Infinity Cache cannot serve repeats, so every step streams its weights from
-HBM.
+cycle over R slots, each with its own copy of the layer's weights (like a
+stack of layers) and its own x batch, R chosen from the weight bytes a first
+untimed call touches so that R of them span at least 2 GiB: the 256 MB
+Infinity Cache cannot serve a repeat, so every step streams its weights
+from HBM, and the routing changes from step to step.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
-Prints one JSON line. Stage durations come from HIP events the library
-records on its own stream inside the timed loop; ``roofline`` is the
-dominant stage's algorithmic bytes (HBM-bound workloads) or FLOPs
-(MFMA-bound workloads) per launch divided by its measured duration.
+With no --config it prints one JSON line for the largest single-GPU
+workload, the skewed prefill layer (T=16384, d=2048, E=128, h=768, top-8),
+carrying a sub-record for every other workload (tiny fp32, gemma-shaped,
+decode at T = 1/4/16/64, shared-plus-routed, the sigmoid-scored layer and
+4-bit decode) and measured achievable peaks. Stage durations come from HIP
+events the library records on its own stream; ``roofline`` is the dominant
+stage's algorithmic bytes (HBM-bound workloads) or FLOPs (MFMA-bound
+workloads) per launch divided by its measured duration.
 """
 
 from __future__ import annotations
@@ -105,16 +110,34 @@ def recorded_traffic(workload, stage, stage_kernel=STAGE_KERNEL, files=FWD_SOURC
     return None
 
 
-def cpu_baseline(inp, budget_s=20.0):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
-    import numpy as np
-    import oracle.moe_oracle as O
+def host_info():
+    """CPU model and the BLAS library NumPy calls, with its thread count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", os.cpu_count() or 1
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            i = infos[0]
+            blas = f"{i.get('internal_api', '?')} {i.get('version', '')}".strip()
+            threads = max(int(j.get("num_threads", 1)) for j in infos)
     except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = os.cpu_count() or 1
+        pass
+    return model, blas, int(threads)
+
+
+def cpu_baseline(inp, budget_s=20.0):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle.moe_oracle as O
+    model, blas, threads = host_info()
     spec = inp["spec"]
 
     def run(Ts):
@@ -135,9 +158,256 @@ def cpu_baseline(inp, budget_s=20.0):
     while len(times) < 3 and sum(times) + t < budget_s:
         times.append(run(Ts))
     med = statistics.median(times)
-    return {"value": Ts / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": Ts / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "blas": blas,
             "sample": f"first {Ts} of {spec.T} tokens of the same inputs, float64 NumPy oracle, "
                       f"median of {len(times)} run(s) of {med:.2f} s"}
+
+
+# What each workload is judged against: its binding roof and the fraction of
+# it the layer should reach (prefill-shaped: >= 50% of bf16 MFMA peak;
+# decode-shaped and the HBM-bound gemma shape: >= 60% of HBM peak).
+TARGET = {"gemma_upcycled": 0.60, "decode": 0.60, "decode_q4": 0.60,
+          "skewed_prefill": 0.50, "shared_routed": 0.50, "small_moe_sigmoid": 0.50}
+
+HEADLINE = "skewed_prefill"
+SUBRECORDS = ("tiny_fp32", "gemma_upcycled", "decode@T1", "decode@T4", "decode@T16",
+              "decode@T64", "shared_routed", "small_moe_sigmoid", "decode_q4@T1",
+              "decode_q4@T64")
+
+# at most this many weight copies (the tiny layer's 0.8 MB would need
+# thousands; its time is launch latency either way)
+MAX_SLOTS = 256
+
+WNAMES = ("w_router", "b_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down",
+          "w_shared_gate", "w_gate_sb", "w_up_sb", "w_down_sb")
+
+
+def to_device(a):
+    import numpy as np
+    import torch
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    if a.dtype == np.uint32:  # packed scale|bias words
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def touched_weight_bytes(spec, U):
+    """Bytes of weights one call must read: the U touched routed experts, the
+    router and the shared expert."""
+    from mixture_experts_sparse_amd import roofline as R
+    eb = R.Q4_BYTES_PER_WEIGHT if spec.expert_quant else spec.act_bytes
+    n = U * 3.0 * spec.d * spec.h * eb + spec.E * spec.d * spec.act_bytes
+    if spec.shared_h:
+        n += 3.0 * spec.d * spec.shared_h * spec.act_bytes
+    return n
+
+
+def measure_forward(name, steps, warmup, rotate_gib, inp=None, calibrate_copy_mib=0):
+    """Times moe_layer_forward on one workload. Steps cycle over R slots, each
+    with its own copy of the weights and its own x batch (copy 0: the
+    workload's x; others: moe_inputs.rotation_x), R chosen from the touched
+    weight bytes of a first untimed call so that R of them span at least
+    ``rotate_gib`` GiB: the 256 MB Infinity Cache cannot serve a repeat.
+    Returns (record, generated inputs)."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_sparse_amd.binding as B
+    from mixture_experts_sparse_amd import roofline as R
+    from mixture_experts_sparse_amd.hip_timing import StageEvents
+    from moe_inputs import generate, spec_by_name
+    from moe_inputs.generate import rotation_x
+
+    spec = spec_by_name(name)
+    base = name.split("@")[0]
+    T = spec.T
+    t0 = time.perf_counter()
+    if inp is None:
+        inp = generate(spec)
+    log(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f} s")
+    cfg = B.config_from_spec(spec)
+    w0 = {n: to_device(inp.get(n)) for n in WNAMES}
+    xs = [to_device(inp["x"][:T])]
+    out = torch.empty((T, spec.d), dtype=xs[0].dtype, device="cuda")
+    ids = torch.empty((T, spec.k), dtype=torch.int32, device="cuda")
+    counts = torch.empty(spec.E, dtype=torch.int32, device="cuda")
+    ws = B.alloc_workspace(cfg)
+    B.layer_forward(cfg, w0, xs[0], out=out, ids=ids, counts=counts, ws=ws)
+    torch.cuda.synchronize()
+    U0 = int((counts.cpu().numpy() > 0).sum())
+    nslots = max(2, math.ceil(rotate_gib * 2**30 / touched_weight_bytes(spec, U0)))
+    capped = nslots > MAX_SLOTS  # only the launch-bound tiny layer gets here
+    nslots = min(nslots, MAX_SLOTS)
+    wsets = [w0] + [{n: (t.clone() if t is not None else None) for n, t in w0.items()}
+                    for _ in range(nslots - 1)]
+    wstructs = [B.weights_struct(w) for w in wsets]
+    xs += [to_device(rotation_x(spec, i)) for i in range(1, nslots)]
+    # touched experts of every slot (the routing changes with x)
+    slot_U, slot_load = [], []
+    for i in range(nslots):
+        B.layer_forward(cfg, wstructs[i], xs[i], out=out, ids=ids, counts=counts, ws=ws)
+        torch.cuda.synchronize()
+        c = counts.cpu().numpy()
+        slot_U.append(int((c > 0).sum()))
+        slot_load.append(float(c.max() / max(c.mean(), 1e-9)))
+    set_bytes = sum(t.numel() * t.element_size() for t in w0.values() if t is not None)
+    log(f"[bench] {name}: {nslots} slots (weights {set_bytes / 2**20:.1f} MiB each, touched "
+        f"{touched_weight_bytes(spec, U0) / 2**20:.1f} MiB per call), workspace "
+        f"{ws.numel() / 2**20:.1f} MiB")
+
+    def call(i, ev=None):
+        j = i % nslots
+        B.layer_forward(cfg, wstructs[j], xs[j], out=out, ids=ids, counts=counts, ws=ws,
+                        stage_events=ev)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+
+    # timed region: K untraced steps between two events on the launch stream
+    outer = StageEvents(1, 1)
+    hip = outer.hip
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    w_start = time.perf_counter()
+    hip.hipEventRecord(outer.row(0)[0], stream)
+    for i in range(steps):
+        call(i)
+    hip.hipEventRecord(outer.row(0)[1], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w_start
+    hip.hipEventSynchronize(outer.row(0)[1])
+    span_ms = outer.elapsed_ms(outer.row(0)[0], outer.row(0)[1])
+    outer.destroy()
+    ms_per_step = span_ms / steps
+    log(f"[bench] {name}: {steps} steps, {ms_per_step * 1e3:.1f} us/step (events), "
+        f"{wall / steps * 1e6:.1f} us/step (wall)")
+
+    # stage durations: the same K steps again with an event at every stage
+    # boundary (each event pair adds a few microseconds of its own)
+    ev = StageEvents(steps)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        call(i, ev.row(i))
+    torch.cuda.synchronize()
+    stage = np.array(ev.stage_ms())  # [steps, stages]
+    traced_ms = ev.span_ms() / steps
+    ev.destroy()
+
+    if calibrate_copy_mib > 0:
+        n = calibrate_copy_mib * 2**20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] reference copy of {calibrate_copy_mib} MiB done")
+        del src, dst
+
+    step_U = [slot_U[i % nslots] for i in range(steps)]
+    Umean = float(np.mean(step_U))
+    mean_stage_us = {n: float(stage[:, i].mean() * 1e3) for i, n in enumerate(B.STAGE_NAMES)}
+    bound = BOUND[base]
+    dom = max(mean_stage_us, key=mean_stage_us.get)
+    dwork = [stage_work(spec, U, T)[dom] for U in step_U]
+    dbytes = float(np.mean([w[0] for w in dwork]))
+    dflops = float(np.mean([w[1] for w in dwork]))
+    dsec = mean_stage_us[dom] * 1e-6
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": dflops / dsec / 1e12,
+                "peak": R.PEAK_BF16_MFMA_FLOPS / 1e12, "unit": "TFLOP/s"}
+    elif bound == "alu":
+        roof = {"bound": "alu", "achieved": dflops / dsec / 1e12,
+                "peak": R.PEAK_FP32_VALU_FLOPS / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": dbytes / dsec / 1e9,
+                "peak": R.PEAK_HBM_BYTES / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = recorded_traffic(name, dom)
+    roof["alg_bytes"] = dbytes
+    roof["alg_flops"] = dflops
+    roof["kernel"] = dom
+
+    sec = ms_per_step * 1e-3
+    eb = R.Q4_BYTES_PER_WEIGHT if spec.expert_quant else None
+    lflops = R.layer_flops(T, spec.d, spec.E, spec.h, spec.k, spec.shared_h, spec.shared_gate)
+    lbytes = float(np.mean([R.layer_bytes(T, spec.d, spec.E, spec.h, U, spec.act_bytes,
+                                          spec.shared_h, spec.shared_gate,
+                                          spec.router_bias is not None, eb) for U in step_U]))
+    layer = {"mfma_frac": lflops / sec / R.PEAK_BF16_MFMA_FLOPS,
+             "hbm_frac": lbytes / sec / R.PEAK_HBM_BYTES,
+             "alg_flops": lflops, "alg_bytes": lbytes, "touched_experts_mean": Umean,
+             "touched_experts_first_call": U0,
+             "max_over_mean_load": float(np.mean(slot_load))}
+    rec = {
+        "workload": name, "tokens_per_s": T / sec, "ms_per_step": ms_per_step, "steps": steps,
+        "warmup": warmup, "dtype": "bf16" if spec.dtype == 1 else "f32",
+        "config": {"workload": name, "T": T, "d": spec.d, "E": spec.E, "h": spec.h,
+                   "top_k": spec.k, "shared_h": spec.shared_h,
+                   "gates": ["softmax over all", "softmax over the selected",
+                             "sigmoid affinities, selection-only balance bias"][spec.mode]
+                   + (" + renormalised" if spec.renormalize else ""),
+                   "routed_weights": spec.expert_quant or "activation dtype",
+                   "rotation_slots": nslots, "rotation_capped": capped, "x_rotates": True,
+                   "touched_weight_bytes_first_call": touched_weight_bytes(spec, U0),
+                   "parallelism": "single GPU"},
+        "roofline": roof, "layer": layer, "stages_us": mean_stage_us,
+        "traced_us_per_step": traced_ms * 1e3,
+    }
+    if base in TARGET:
+        frac = layer["mfma_frac"] if bound == "mfma" else layer["hbm_frac"]
+        rec["target"] = {"roof": bound, "layer_frac": frac, "needed": TARGET[base],
+                         "met": bool(frac >= TARGET[base])}
+    del wsets, wstructs, xs, w0, ws, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec, inp
+
+
+def achievable_peaks():
+    """Measured ceilings for context beside the published peaks: a 1 GiB
+    device-to-device copy (bytes read plus written over its time) and a
+    library bf16 matrix product of 8192^3 (torch's GEMM)."""
+    import torch
+    from mixture_experts_sparse_amd.hip_timing import StageEvents
+    ev = StageEvents(1, 1)
+    hip = ev.hip
+    stream = torch.cuda.current_stream().cuda_stream
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    hip.hipEventRecord(ev.row(0)[0], stream)
+    for _ in range(10):
+        dst.copy_(src)
+    hip.hipEventRecord(ev.row(0)[1], stream)
+    torch.cuda.synchronize()
+    copy_s = ev.elapsed_ms(ev.row(0)[0], ev.row(0)[1]) * 1e-3 / 10
+    del src, dst
+    a = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
+    b = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        a @ b
+    torch.cuda.synchronize()
+    hip.hipEventRecord(ev.row(0)[0], stream)
+    for _ in range(10):
+        a @ b
+    hip.hipEventRecord(ev.row(0)[1], stream)
+    torch.cuda.synchronize()
+    mm_s = ev.elapsed_ms(ev.row(0)[0], ev.row(0)[1]) * 1e-3 / 10
+    ev.destroy()
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBps": 2.0 * n / copy_s / 1e9,
+            "bf16_gemm_8192_TFLOPs": 2.0 * 8192 ** 3 / mm_s / 1e12,
+            "what": "1 GiB device copy (read + write bytes) and torch bf16 8192^3 matmul, "
+                    "10 calls each, HIP events"}
 
 
 def main():
@@ -145,12 +415,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="gemma_upcycled",
-                    help="workload name (gemma_upcycled, skewed_prefill, shared_routed, "
-                         "decode@T1/4/16/64, tiny_fp32)")
+    ap.add_argument("--config", default=None,
+                    help="one workload only (skewed_prefill, gemma_upcycled, shared_routed, "
+                         "decode@T1/4/16/64, decode_q4@T1/..., small_moe_sigmoid, tiny_fp32); "
+                         "default: the skewed_prefill headline plus a sub-record for every "
+                         "other workload")
     ap.add_argument("--rotate-gib", type=float, default=2.0,
-                    help="minimum bytes of distinct weight copies cycled through")
+                    help="minimum bytes of touched weights cycled through between repeats")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-subrecords", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--pass", dest="which", choices=("forward", "backward", "stats"),
                     default="forward",
@@ -168,6 +441,68 @@ def main():
               "and has no multi-GPU path (--gpus must be 1).", file=sys.stderr, flush=True)
         sys.exit(2)
 
+    import torch
+    torch.cuda.set_device(0)
+
+    if args.which != "forward":
+        run_other_pass(args)
+        return
+
+    name = args.config or HEADLINE
+    rec, inp = measure_forward(name, args.steps, args.warmup, args.rotate_gib,
+                               calibrate_copy_mib=args.calibrate_copy_mib)
+    result = {
+        "metric": METRIC,
+        "value": rec["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": rec["dtype"],
+        "data": "synthetic",
+        "config": rec["config"],
+        "roofline": rec["roofline"],
+        "layer": rec["layer"],
+        "target": rec.get("target"),
+        "stages_us": rec["stages_us"],
+        "traced_us_per_step": rec["traced_us_per_step"],
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)
+    del inp
+    if args.config is None and not args.no_subrecords:
+        subs = {}
+        cache = {}
+        for sub in SUBRECORDS:
+            base = sub.split("@")[0]
+            sub_inp = None
+            if "@T" in sub:
+                # the batch sizes of one decode workload share one draw
+                if base not in cache:
+                    cache.clear()
+                    from moe_inputs import generate, spec_by_name
+                    cache[base] = generate(spec_by_name(f"{base}@T64"))
+                from moe_inputs import spec_by_name
+                sp = spec_by_name(sub)
+                sub_inp = dict(cache[base], spec=sp, x=cache[base]["x"][:sp.T])
+            r, _ = measure_forward(sub, args.steps, args.warmup, args.rotate_gib, inp=sub_inp)
+            subs[sub] = {k: r[k] for k in ("tokens_per_s", "ms_per_step", "roofline", "layer",
+                                           "target", "stages_us") if k in r}
+            subs[sub]["rotation_slots"] = r["config"]["rotation_slots"]
+        result["subrecords"] = subs
+        result["achievable_peaks"] = achievable_peaks()
+    print(json.dumps(result), flush=True)
+
+
+def run_other_pass(args):
+    """The backward or routing-statistics line for one workload (gemma by
+    default): weight copies spanning --rotate-gib, one x."""
     import numpy as np
     import torch
 
@@ -176,165 +511,28 @@ def main():
     from mixture_experts_sparse_amd.hip_timing import StageEvents
     from moe_inputs import generate, spec_by_name
 
-    spec = spec_by_name(args.config)
-    base = args.config.split("@")[0]
-    t0 = time.perf_counter()
+    name = args.config or "gemma_upcycled"
+    args.config = name
+    spec = spec_by_name(name)
     inp = generate(spec)
-    log(f"[bench] generated {args.config} in {time.perf_counter() - t0:.1f} s")
-    torch.cuda.set_device(0)
-
-    def dev(a):
-        if a is None:
-            return None
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-        if a.dtype == np.uint32:  # packed scale|bias words
-            return torch.from_numpy(a.view(np.int32)).cuda()
-        return torch.from_numpy(a).cuda()
-
-    wnames = ("w_router", "b_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down",
-              "w_shared_gate", "w_gate_sb", "w_up_sb", "w_down_sb")
-    w0 = {n: dev(inp.get(n)) for n in wnames}
+    w0 = {n: to_device(inp.get(n)) for n in WNAMES}
     set_bytes = sum(t.numel() * t.element_size() for t in w0.values() if t is not None)
     nsets = max(1, math.ceil(args.rotate_gib * 2**30 / set_bytes))
     wsets = [w0] + [{n: (t.clone() if t is not None else None) for n, t in w0.items()}
                     for _ in range(nsets - 1)]
     wstructs = [B.weights_struct(w) for w in wsets]
-    x = dev(inp["x"])
+    x = to_device(inp["x"])
     cfg = B.config_from_spec(spec)
-    T = spec.T
     if args.which == "backward":
         run_backward(args, spec, inp, cfg, x, wstructs, nsets, B, R, StageEvents)
-        return
-    if args.which == "stats":
-        run_stats(args, spec, inp, cfg, x, w0, B, R, StageEvents)
-        return
-    out = torch.empty((T, spec.d), dtype=x.dtype, device="cuda")
-    ids = torch.empty((T, spec.k), dtype=torch.int32, device="cuda")
-    counts = torch.empty(spec.E, dtype=torch.int32, device="cuda")
-    ws = B.alloc_workspace(cfg)
-    log(f"[bench] {nsets} weight copies of {set_bytes / 2**20:.1f} MiB, workspace "
-        f"{ws.numel() / 2**20:.1f} MiB")
-
-    for i in range(args.warmup):
-        B.layer_forward(cfg, wstructs[i % nsets], x, out=out, ids=ids, counts=counts, ws=ws)
-    torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} done")
-
-    # Timed region: K untraced steps between two events on the launch stream.
-    outer = StageEvents(1)
-    hip = outer.hip
-    stream = torch.cuda.current_stream().cuda_stream
-    torch.cuda.synchronize()
-    w_start = time.perf_counter()
-    hip.hipEventRecord(outer.row(0)[0], stream)
-    for i in range(args.steps):
-        B.layer_forward(cfg, wstructs[i % nsets], x, out=out, ids=ids, counts=counts, ws=ws)
-    hip.hipEventRecord(outer.row(0)[1], stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w_start
-    hip.hipEventSynchronize(outer.row(0)[1])
-    span_ms = outer.elapsed_ms(outer.row(0)[0], outer.row(0)[1])
-    outer.destroy()
-    ms_per_step = span_ms / args.steps
-    log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (events), "
-        f"{wall / args.steps * 1e6:.1f} us/step (wall)")
-
-    # Stage durations: the same K steps again, with the library recording an
-    # event at every stage boundary on its stream (each event pair adds a
-    # few microseconds of its own, so these are upper bounds).
-    ev = StageEvents(args.steps)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        B.layer_forward(cfg, wstructs[i % nsets], x, out=out, ids=ids, counts=counts, ws=ws,
-                        stage_events=ev.row(i))
-    torch.cuda.synchronize()
-    stage = np.array(ev.stage_ms())  # [steps, stages]
-    traced_ms = ev.span_ms() / args.steps
-    ev.destroy()
-    log(f"[bench] traced steps: {traced_ms * 1e3:.1f} us/step")
-
-    if args.calibrate_copy_mib > 0:
-        n = args.calibrate_copy_mib * 2**20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] reference copy of {args.calibrate_copy_mib} MiB done")
-        del src, dst
-
-    cnt = counts.cpu().numpy()
-    U = int((cnt > 0).sum())
-    mean_stage_us = {n: float(stage[:, i].mean() * 1e3) for i, n in enumerate(B.STAGE_NAMES)}
-    work = stage_work(spec, U, T)
-    bound = BOUND[base]
-    dom = max(mean_stage_us, key=mean_stage_us.get)
-    dbytes, dflops = work[dom]
-    dsec = mean_stage_us[dom] * 1e-6
-    if bound == "mfma":
-        roof = {"bound": "mfma", "achieved": dflops / dsec / 1e12,
-                "peak": R.PEAK_BF16_MFMA_FLOPS / 1e12, "unit": "TFLOP/s"}
-    elif bound == "alu":
-        roof = {"bound": "alu", "achieved": dflops / dsec / 1e12,
-                "peak": R.PEAK_FP32_VALU_FLOPS / 1e12, "unit": "TFLOP/s"}
     else:
-        roof = {"bound": "hbm", "achieved": dbytes / dsec / 1e9,
-                "peak": R.PEAK_HBM_BYTES / 1e9, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = recorded_traffic(args.config, dom)
-    roof["alg_bytes"] = dbytes
-    roof["kernel"] = dom
-
-    sec = ms_per_step * 1e-3
-    lflops = R.layer_flops(T, spec.d, spec.E, spec.h, spec.k, spec.shared_h, spec.shared_gate)
-    lbytes = R.layer_bytes(T, spec.d, spec.E, spec.h, U, spec.act_bytes, spec.shared_h,
-                           spec.shared_gate, spec.router_bias is not None,
-                           R.Q4_BYTES_PER_WEIGHT if spec.expert_quant else None)
-    result = {
-        "metric": METRIC,
-        "value": T / sec,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if spec.dtype == 1 else "f32",
-        "data": "synthetic",
-        "config": {"workload": args.config, "T": T, "d": spec.d, "E": spec.E, "h": spec.h,
-                   "top_k": spec.k, "shared_h": spec.shared_h,
-                   "gates": ["softmax over all", "softmax over the selected",
-                             "sigmoid affinities, selection-only balance bias"][spec.mode]
-                   + (" + renormalised" if spec.renormalize else ""),
-                   "routed_weights": spec.expert_quant or "activation dtype",
-                   "weight_copies": nsets, "parallelism": "single GPU"},
-        "roofline": roof,
-        "layer": {"mfma_frac": lflops / sec / R.PEAK_BF16_MFMA_FLOPS,
-                  "hbm_frac": lbytes / sec / R.PEAK_HBM_BYTES,
-                  "alg_flops": lflops, "alg_bytes": lbytes, "touched_experts": U,
-                  "max_over_mean_load": float(cnt.max() / max(cnt.mean(), 1e-9))},
-        "stages_us": mean_stage_us,
-        "traced_us_per_step": traced_ms * 1e3,
-        "cpu_baseline": None,
-    }
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)
-    print(json.dumps(result), flush=True)
+        run_stats(args, spec, inp, cfg, x, w0, B, R, StageEvents)
 
 
 def cpu_baseline_backward(inp, dout, budget_s=20.0):
     """The oracle's backward, as it stands, on a bounded sample of tokens."""
     import oracle.moe_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    model, blas, threads = host_info()
     spec = inp["spec"]
 
     def run(Ts):
@@ -355,6 +553,7 @@ def cpu_baseline_backward(inp, dout, budget_s=20.0):
         times.append(run(Ts))
     med = statistics.median(times)
     return {"value": Ts / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": model, "blas": blas,
             "sample": f"first {Ts} of {spec.T} tokens of the same inputs, float64 NumPy oracle "
                       f"backward, median of {len(times)} run(s) of {med:.2f} s"}
 

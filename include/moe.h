@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 #define MOE_MAX_EXPERTS 256
 #define MOE_NUM_STAGES 5 /* route, dispatch, gate_up, down, combine */
 
@@ -173,6 +173,19 @@ size_t moe_workspace_size_entry(const moe_config* cfg, int32_t entry);
 
 /* Workspace bytes for moe_layer_forward (the largest of all entries). */
 size_t moe_workspace_size(const moe_config* cfg);
+
+/* Dispatch tables that moe_layer_forward leaves in its workspace. */
+typedef enum { MOE_TABLE_OFFSETS = 0, MOE_TABLE_PERM = 1, MOE_TABLE_INV = 2 } moe_table;
+
+/* Byte offset, inside a MOE_ENTRY_LAYER_FORWARD workspace sized for cfg, of
+ * one of the dispatch tables a moe_layer_forward call writes there: offsets
+ * (int32 [E+1]), perm and inv (int32 [T*top_k]), the stable counting sort of
+ * "Tutorial 11: Mixture of Experts (MoE)", section 3, step 1. Once the call
+ * has completed on its stream the tables hold its dispatch until the next
+ * call that uses the same workspace; this lets a caller inspect the fused
+ * call's routing. Host arithmetic only (no HIP call). Returns SIZE_MAX for an
+ * invalid cfg or table. */
+size_t moe_workspace_table_offset(const moe_config* cfg, int32_t table);
 
 /* Router: logits, top-k selection and gates ("Tutorial 11: Mixture of
  * Experts (MoE)", section 2 "The Router"; "Small models, sparse experts",

@@ -41,6 +41,10 @@ MOE_ENTRY_SHARED_EXPERT = 5
 MOE_ENTRY_ROUTING_STATS = 6
 MOE_ENTRY_LAYER_BACKWARD = 7
 
+MOE_TABLE_OFFSETS = 0
+MOE_TABLE_PERM = 1
+MOE_TABLE_INV = 2
+
 MOE_NUM_STAGES = 5
 STAGE_NAMES = ("route", "dispatch", "gate_up", "down", "combine")
 MOE_NUM_BWD_STAGES = 8
@@ -86,6 +90,7 @@ _SIG = {
     "moe_validate_config": ([_P], ctypes.c_int),
     "moe_workspace_size_entry": ([_P, ctypes.c_int32], ctypes.c_size_t),
     "moe_workspace_size": ([_P], ctypes.c_size_t),
+    "moe_workspace_table_offset": ([_P, ctypes.c_int32], ctypes.c_size_t),
     "moe_route": ([_P] * 8, ctypes.c_int),
     "moe_dispatch": ([_P] * 7 + [ctypes.c_size_t, _P], ctypes.c_int),
     "moe_gate_up": ([_P] * 8 + [ctypes.c_size_t, _P], ctypes.c_int),
@@ -169,6 +174,26 @@ def validate_config(cfg: MoeConfig) -> int:
 
 def workspace_size(cfg: MoeConfig, entry: int = MOE_ENTRY_LAYER_FORWARD) -> int:
     return int(lib().moe_workspace_size_entry(ctypes.byref(cfg), int(entry)))
+
+
+def workspace_table_offset(cfg: MoeConfig, table: int) -> int:
+    off = int(lib().moe_workspace_table_offset(ctypes.byref(cfg), int(table)))
+    if off == 2**64 - 1:
+        raise MoeError(MOE_ERR_INVALID_ARG, "moe_workspace_table_offset")
+    return off
+
+
+def workspace_tables(cfg: MoeConfig, ws):
+    """(offsets [E+1], perm [P], inv [P]) int32 views into a layer-forward
+    workspace ``ws`` (a uint8 tensor): the dispatch of the last
+    moe_layer_forward that used it, once that call has completed."""
+    import torch
+    P = cfg.T * cfg.top_k
+    out = []
+    for table, n in ((MOE_TABLE_OFFSETS, cfg.E + 1), (MOE_TABLE_PERM, P), (MOE_TABLE_INV, P)):
+        off = workspace_table_offset(cfg, table)
+        out.append(ws[off:off + 4 * n].view(torch.int32))
+    return tuple(out)
 
 
 # ----------------------------------------------------------------------------

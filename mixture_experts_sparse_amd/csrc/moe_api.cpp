@@ -214,6 +214,17 @@ size_t moe_workspace_size(const moe_config* cfg) {
   return moe_workspace_size_entry(cfg, MOE_ENTRY_LAYER_FORWARD);
 }
 
+size_t moe_workspace_table_offset(const moe_config* cfg, int32_t table) {
+  if (check_cfg(cfg) != MOE_OK) return SIZE_MAX;
+  const WsLayout L = ws_layout(*cfg);
+  switch (table) {
+    case MOE_TABLE_OFFSETS: return L.offsets;
+    case MOE_TABLE_PERM: return L.perm;
+    case MOE_TABLE_INV: return L.inv;
+    default: return SIZE_MAX;
+  }
+}
+
 moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
                      const float* b_router, int32_t* ids, float* gates, float* logits,
                      void* stream) {

@@ -184,6 +184,17 @@ def generate(spec: MoESpec) -> dict:
     return out
 
 
+def rotation_x(spec: MoESpec, i: int) -> np.ndarray:
+    """x for rotation copy i >= 1 of a timed loop (copy 0 is the workload's
+    own x): [T, d] N(0, x_std) float32 normals from
+    ``numpy.random.default_rng((seed, i))``, cast like x (bf16 RNE or
+    float32). Distinct draws so the routing changes from copy to copy."""
+    if i < 1:
+        raise ValueError("copy 0 is the workload's own x")
+    rng = np.random.default_rng((spec.seed, i))
+    return _cast(spec, _normal(rng, (spec.T, spec.d), spec.x_std))
+
+
 def lambda_upcycle(copies: int) -> float:
     """The drop-upcycling scale copies**(1/3) (64 copies -> 4.0)."""
     return round(math.pow(copies, 1.0 / 3.0), 12)

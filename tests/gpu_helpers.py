@@ -62,9 +62,9 @@ def device_inputs(inp: dict) -> dict:
     return {n: dev(inp.get(n)) for n in names}
 
 
-def run_layer(inp: dict, d_inp: dict = None, T: int = None):
+def run_layer(inp: dict, d_inp: dict = None, T: int = None, ws=None):
     """Fused moe_layer_forward through the C ABI. Returns numpy out (float64),
-    ids, gates, counts."""
+    ids, gates, counts. ``ws``: the workspace to use (None: a fresh one)."""
     spec = inp["spec"]
     cfg = B.config_from_spec(spec, T)
     d_inp = d_inp or device_inputs(inp)
@@ -78,7 +78,7 @@ def run_layer(inp: dict, d_inp: dict = None, T: int = None):
          "w_shared_gate": d_inp["w_shared_gate"], "w_gate_sb": d_inp.get("w_gate_sb"),
          "w_up_sb": d_inp.get("w_up_sb"), "w_down_sb": d_inp.get("w_down_sb")}
     x = d_inp["x"][:Tn]
-    out = B.layer_forward(cfg, w, x, ids=ids, gates=gates, counts=counts)
+    out = B.layer_forward(cfg, w, x, ids=ids, gates=gates, counts=counts, ws=ws)
     torch.cuda.synchronize()
     return {"out": host(out), "ids": ids.cpu().numpy().astype(np.int64),
             "gates": gates.cpu().numpy().astype(np.float64),
@@ -136,10 +136,11 @@ def oracle_logits_scores(inp: dict):
     return L, L
 
 
-def full_parity(inp: dict, d_inp: dict = None):
-    """Fused layer on the GPU against the whole-batch oracle."""
+def full_parity(inp: dict, d_inp: dict = None, ws=None):
+    """Fused layer on the GPU against the whole-batch oracle, every output
+    entry compared."""
     spec = inp["spec"]
-    g = run_layer(inp, d_inp)
+    g = run_layer(inp, d_inp, ws=ws)
     L, S = oracle_logits_scores(inp)
     near, mism = check_routing(S, g["ids"], spec.k)
     override = {int(t): g["ids"][t] for t in mism}
@@ -149,25 +150,3 @@ def full_parity(inp: dict, d_inp: dict = None):
     rel = check_out(g["out"], ref["out"], spec.dtype)
     say(f"    near-tie tokens {near}, rerouted {len(mism)}, gate err {gerr:.2e}")
     return g, ref, rel
-
-
-def sampled_parity(inp: dict, tokens, d_inp: dict = None):
-    """Fused layer at full size: routing and counts for every token, outputs
-    for a sample of tokens computed one by one by the oracle."""
-    spec = inp["spec"]
-    g = run_layer(inp, d_inp)
-    L, S = oracle_logits_scores(inp)
-    near, mism = check_routing(S, g["ids"], spec.k)
-    ids = O.topk_select(S, spec.k)
-    ids[mism] = g["ids"][mism]
-    gates, _ = O.gate_weights(L, ids, spec.mode, spec.renormalize)
-    counts, _, _, _ = O.dispatch(ids, spec.E)
-    assert np.array_equal(g["counts"], counts), "counts differ"
-    gerr = check_gates(g["gates"], gates)
-    tokens = np.asarray(sorted(set(int(t) for t in tokens)))
-    ref_rows = O.token_forward(inp, tokens, ids[tokens], gates[tokens])
-    rel = check_out(g["out"][tokens], ref_rows, spec.dtype, f"out[{len(tokens)} sampled rows]")
-    say(f"    near-tie tokens {near}, rerouted {len(mism)}, gate err {gerr:.2e}, "
-        f"touched experts {int((counts > 0).sum())}, max/mean load "
-        f"{counts.max() / max(counts.mean(), 1e-9):.2f}")
-    return g, rel

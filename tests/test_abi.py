@@ -17,7 +17,27 @@ def test_library_exports_every_header_function():
     assert len(names) >= 14
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
+
+
+def test_workspace_table_offsets():
+    """The dispatch tables a fused call leaves in its workspace lie inside the
+    layer-forward workspace, 256-byte aligned and disjoint; bad arguments
+    give SIZE_MAX (raised by the binding)."""
+    c = B.make_config(8192, 640, 256, 512, 4)
+    ws = B.workspace_size(c)
+    P = 8192 * 4
+    spans = []
+    for t, n in ((B.MOE_TABLE_OFFSETS, 257), (B.MOE_TABLE_PERM, P), (B.MOE_TABLE_INV, P)):
+        off = B.workspace_table_offset(c, t)
+        assert off % 256 == 0 and off + 4 * n <= ws
+        spans.append((off, off + 4 * n))
+    spans.sort()
+    assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+    with pytest.raises(B.MoeError):
+        B.workspace_table_offset(c, 3)
+    with pytest.raises(B.MoeError):
+        B.workspace_table_offset(B.make_config(1, 64, 8, 32, 9), B.MOE_TABLE_PERM)
 
 
 def test_status_strings():

@@ -10,8 +10,10 @@ re-derived by the oracle with the GPU's own selection (taken from the forward
 on the same inputs), as in the forward parity protocol. Cases span several
 128-row tiles with ragged tails, one route block (the split router), 256
 experts, E not a multiple of 8, every gate mode, logit and balance biases,
-gated and ungated shared experts, and experts of 256 rows and more; one
-full-size workload is checked whole.
+gated and ungated shared experts, experts of 256 rows and more, and
+per-expert weights larger than one XCD's L2 (the straight tile order of the
+row products); the gemma-shaped and skewed-prefill workloads are checked
+whole at full size.
 """
 
 import numpy as np
@@ -62,6 +64,12 @@ CASES = {
     # of 8 with a tail of 4; the slot gradients spread over lanes)
     "sigmoid_k20": small_spec("small_moe_sigmoid", T=90, d=128, E=64, h=32, k=20, shared_h=0,
                               renormalize=False),
+    # an expert's weight operand above one XCD's 4 MB L2 (2*d*2h and 2*d*h
+    # bytes > 4 MiB): the row products take the straight tile order, as at the
+    # prefill shapes; h = 2056 leaves an N tail
+    "wide_expert": small_spec("skewed_prefill", T=300, d=1024, E=2, h=2056, k=1),
+    # the same for the shared expert's row products (2*d*2*shared_h > 4 MiB)
+    "wide_shared": small_spec("shared_routed", T=260, d=1024, E=4, h=64, k=2, shared_h=2056),
 }
 
 GRADS = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up", "dws_down",
@@ -146,8 +154,10 @@ def test_backward_no_tokens_zero_weight_grads():
         assert torch.count_nonzero(got[n]).item() == 0, n
 
 
-def test_backward_gemma_full():
-    """The gemma-shaped workload at full size, every gradient entry checked."""
-    spec = spec_by_name("gemma_upcycled")
-    say(f"[backward] gemma_upcycled full: T={spec.T}")
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["gemma_upcycled", "skewed_prefill"])
+def test_backward_full(name):
+    """A workload at full size, every gradient entry checked."""
+    spec = spec_by_name(name)
+    say(f"[backward] {name} full: T={spec.T}")
     backward_parity(generate(spec), seed=11)

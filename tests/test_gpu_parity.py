@@ -3,8 +3,10 @@
 Small shapes run the whole-batch oracle and span several tiles with ragged
 tails (T not a multiple of the 64-token route block or the 128-row M tile,
 d not a multiple of the 64-deep K chunk, h not a multiple of the N tile).
-Full-size workloads check routing and counts for every token and outputs for
-a sample of rows. Every comparison follows the protocol in gpu_helpers.
+Full-size workloads run the whole-batch oracle too: routing and counts for
+every token, every output entry, and the fused call's dispatch tables (read
+back from its workspace) bit for bit against the oracle's stable sort of the
+GPU's ids. Every comparison follows the protocol in gpu_helpers.
 """
 
 import dataclasses
@@ -16,8 +18,7 @@ import torch
 import mixture_experts_sparse_amd.binding as B
 import oracle.moe_oracle as O
 from gpu_helpers import (EPS_TIE, check_gates, check_out, check_routing, dev, device_inputs,
-                         full_parity, host, oracle_logits_scores, run_layer, sampled_parity,
-                         say)
+                         full_parity, host, oracle_logits_scores, run_layer, say)
 from moe_inputs import generate, small_spec, spec_by_name
 from moe_inputs.spec import BF16, F32, SOFTMAX_ALL, SOFTMAX_SELECTED, SPECS, MoESpec
 
@@ -200,23 +201,43 @@ def _full_inputs(name):
     return inp
 
 
+def _check_tables(cfg, ws, gids, E, what):
+    """The dispatch tables in a workspace against the oracle's counting sort
+    of the GPU's ids, bit for bit."""
+    offs, perm, inv = (t.cpu().numpy().astype(np.int64) for t in B.workspace_tables(cfg, ws))
+    _, ro, rp, ri = O.dispatch(gids, E)
+    assert np.array_equal(offs, ro), f"{what}: offsets differ"
+    assert np.array_equal(perm, rp), f"{what}: perm differs"
+    assert np.array_equal(inv, ri), f"{what}: inv differs"
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", FULL)
 def test_layer_full_size(name):
+    """The whole batch against the whole-batch oracle: every one of the T*d
+    output entries within the bound, and the fused call's offsets, perm and
+    inv equal to the oracle's stable sort of the GPU's ids."""
     spec = spec_by_name(name)
     say(f"[gpu] full-size {name}: T={spec.T} d={spec.d} E={spec.E} h={spec.h} k={spec.k}")
     inp = _full_inputs(name)
-    if spec.T <= 64:
-        full_parity(inp)
-        return
-    rng = np.random.default_rng(1234)
-    sample = list(rng.choice(spec.T, size=48, replace=False)) + [0, spec.T - 1, spec.T // 2]
-    g, _ = sampled_parity(inp, sample)
-    # the hottest expert's rows: sample tokens routed to it
-    hot = int(np.argmax(g["counts"]))
-    rows = np.nonzero(np.any(g["ids"] == hot, axis=1))[0]
-    if rows.size:
-        pick = rows[np.linspace(0, rows.size - 1, 8).astype(int)]
-        sampled_parity(inp, pick)
+    cfg = B.config_from_spec(spec)
+    ws = B.alloc_workspace(cfg)
+    g, ref, _ = full_parity(inp, ws=ws)
+    _check_tables(cfg, ws, g["ids"], spec.E, "fused call")
+    counts = g["counts"]
+    say(f"    touched experts {int((counts > 0).sum())}, max/mean load "
+        f"{counts.max() / max(counts.mean(), 1e-9):.2f}, dispatch tables bit-exact")
+    if name in ("gemma_upcycled", "skewed_prefill"):
+        # the standalone dispatch entry point on the fused call's ids
+        d_ids = torch.from_numpy(g["ids"].astype(np.int32)).cuda()
+        c2, o2, p2, i2 = B.dispatch(cfg, d_ids)
+        torch.cuda.synchronize()
+        rc, ro, rp, ri = O.dispatch(g["ids"], spec.E)
+        assert np.array_equal(c2.cpu().numpy(), rc)
+        assert np.array_equal(o2.cpu().numpy(), ro)
+        assert np.array_equal(p2.cpu().numpy(), rp)
+        assert np.array_equal(i2.cpu().numpy(), ri)
+        say("    moe_dispatch on the same ids: bit-exact")
 
 
 def test_determinism():
