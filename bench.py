@@ -69,7 +69,8 @@ def stage_work(spec, U, T):
 
 
 # kernel-name prefixes of each stage's (first) kernel in a rocprofv3 record
-STAGE_KERNEL = {"route": ("route_kernel", "route_part_kernel"), "dispatch": ("scan_kernel",),
+STAGE_KERNEL = {"route": ("route_kernel", "route_part_kernel"),
+                "dispatch": ("scan_kernel", "route_finish_kernel"),
                 "gate_up": ("gemm_bf16_pers<0", "gemm_bf16_kernel<0", "gemm_small_kernel<0",
                             "gemm_small_q4_kernel<0"),
                 "down": ("gemm_bf16_pers<1", "gemm_bf16_kernel<1", "gemm_small_kernel<1",
@@ -77,7 +78,8 @@ STAGE_KERNEL = {"route": ("route_kernel", "route_part_kernel"), "dispatch": ("sc
                 "combine": ("combine_",)}
 
 
-FWD_SOURCES = ("expert_gemm.hip", "route_dispatch.hip", "combine.hip")
+FWD_SOURCES = ("expert_gemm.hip", "expert_gemm_small.hip", "route_dispatch.hip", "combine.hip",
+               "moe_api.cpp")
 BWD_SOURCES = ("backward.hip", "route_dispatch.hip")
 # kernel-name prefixes of each backward stage's product
 BWD_STAGE_KERNEL = {"d_hidden": ("bwd_gemm<1>",), "z": ("bwd_gemm<0>",),
