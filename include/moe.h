@@ -47,7 +47,8 @@
  *    E <= 0; top_k < 1 or top_k > E; bad enum), MOE_ERR_UNSUPPORTED (d, h or
  *    shared_h not a multiple of 8; E > MOE_MAX_EXPERTS; a pointer not 16-byte
  *    aligned; T*k*d, T*k*h, T*d or T*shared_h at least 2^30 elements), MOE_ERR_WORKSPACE (ws too small or not 256-byte aligned),
- *    MOE_ERR_HIP (a launch failed).
+ *    MOE_ERR_HIP (a launch failed), MOE_ERR_SCRATCH_LIMIT (the no-alloc
+ *    entry point's static workspace is too small for the call).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -68,7 +69,8 @@ typedef enum {
   MOE_ERR_INVALID_ARG = 1,
   MOE_ERR_UNSUPPORTED = 2,
   MOE_ERR_WORKSPACE = 3,
-  MOE_ERR_HIP = 4
+  MOE_ERR_HIP = 4,
+  MOE_ERR_SCRATCH_LIMIT = 5
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -289,6 +291,33 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
                                     const void* x, void* out, int32_t* ids, float* gates,
                                     int32_t* counts, void* ws, size_t ws_bytes,
                                     void* const* stage_events, void* stream);
+
+/* Bytes of the static device array moe_layer_forward_noalloc takes its
+ * workspace from (one array per GPU the library runs on, held until the
+ * process ends). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* moe_layer_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments as moe_layer_forward minus the workspace, same
+ * kernels and the same results; the workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU instead of the caller's ws. The call
+ * allocates nothing (no hipMalloc, no hipFree, no allocating library
+ * routine). A configuration whose workspace (moe_workspace_size(cfg))
+ * exceeds the array returns MOE_ERR_SCRATCH_LIMIT and enqueues nothing: the
+ * array serves decode- and serving-sized batches, for example up to T = 1024
+ * tokens at top_k = 8, d = 2048, h = 1024 (8192 routed rows, about 48 MiB),
+ * not the prefill shapes.
+ * The first call on each device (with that device current) looks up the
+ * device's address of the array (hipGetSymbolAddress; MOE_ERR_HIP if that
+ * fails). Every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents (every byte a call reads it has written first, so
+ * nothing needs clearing): calls that overlap on one GPU (two streams, or
+ * host threads without ordering) race and give wrong results; calls in order
+ * on one stream are safe. */
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, const moe_weights* w, const void* x,
+                                     void* out, int32_t* ids, float* gates, int32_t* counts,
+                                     void* stream);
 
 /* Backward of moe_layer_forward: the gradients of sum(out * dout) with the
  * selection held fixed (top-k is piecewise constant in the logits), for the

@@ -23,6 +23,8 @@ MOE_ERR_INVALID_ARG = 1
 MOE_ERR_UNSUPPORTED = 2
 MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
+MOE_ERR_SCRATCH_LIMIT = 5
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 MOE_F32 = 0
 MOE_BF16 = 1
@@ -102,6 +104,7 @@ _SIG = {
                           ctypes.c_int),
     "moe_layer_forward": ([_P] * 8 + [ctypes.c_size_t, _P], ctypes.c_int),
     "moe_layer_forward_traced": ([_P] * 8 + [ctypes.c_size_t, _P, _P], ctypes.c_int),
+    "moe_layer_forward_noalloc": ([_P] * 8, ctypes.c_int),
     "moe_layer_backward": ([_P] * 6 + [ctypes.c_size_t, _P], ctypes.c_int),
     "moe_layer_backward_traced": ([_P] * 6 + [ctypes.c_size_t, _P, _P], ctypes.c_int),
 }
@@ -357,6 +360,21 @@ def layer_forward(cfg, weights, x, out=None, ids=None, gates=None, counts=None, 
         st = lib().moe_layer_forward_traced(*args, ctypes.cast(stage_events, ctypes.c_void_p),
                                             _stream(stream))
     _check(st, "moe_layer_forward")
+    return out
+
+
+def layer_forward_noalloc(cfg, weights, x, out=None, ids=None, gates=None, counts=None,
+                          stream=None):
+    """The whole layer with the library's static device workspace
+    (moe_layer_forward_noalloc): no workspace argument, nothing allocated by
+    the library."""
+    import torch
+    if out is None:
+        out = torch.empty((cfg.T, cfg.d), dtype=_torch_dtype(cfg), device=x.device)
+    wst = weights if isinstance(weights, MoeWeights) else weights_struct(weights)
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(cfg), ctypes.byref(wst), _ptr(x),
+                                           _ptr(out), _ptr(ids), _ptr(gates), _ptr(counts),
+                                           _stream(stream)), "moe_layer_forward_noalloc")
     return out
 
 

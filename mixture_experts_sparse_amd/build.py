@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
 ARCH = "gfx950"
 
 SOURCES = ["moe_api.cpp", "route_dispatch.hip", "expert_gemm.hip", "expert_gemm_small.hip", "combine.hip",
-           "routing_stats.hip", "backward.hip"]
+           "routing_stats.hip", "backward.hip", "noalloc.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

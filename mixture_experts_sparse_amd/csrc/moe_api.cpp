@@ -187,6 +187,7 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape, alignment or expert count outside what the kernels support";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, too small or not 256-byte aligned";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+    case MOE_ERR_SCRATCH_LIMIT: return "MOE_ERR_SCRATCH_LIMIT: the call needs a larger workspace than the no-alloc entry point's static array (MOE_NOALLOC_SCRATCH_BYTES)";
   }
   return "MOE_ERR_UNKNOWN";
 }

@@ -20,6 +20,27 @@ def test_library_exports_every_header_function():
     assert L.moe_abi_version() == 4
 
 
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    """The no-alloc entry point refuses a configuration whose workspace is
+    larger than its static array, on the host, before any HIP call; T = 0
+    is a no-op and a bad configuration is an argument error."""
+    big = B.make_config(16384, 2048, 128, 768, 8)
+    assert B.workspace_size(big) > B.MOE_NOALLOC_SCRATCH_BYTES
+    w = B.MoeWeights()
+    st = B.lib().moe_layer_forward_noalloc(ctypes.byref(big), ctypes.byref(w), None, None,
+                                           None, None, None, None)
+    assert st == B.MOE_ERR_SCRATCH_LIMIT
+    assert "MOE_ERR_SCRATCH_LIMIT" in B.status_string(st)
+    zero = B.make_config(0, 2048, 64, 1024, 8)
+    assert B.lib().moe_layer_forward_noalloc(ctypes.byref(zero), ctypes.byref(w), None, None,
+                                             None, None, None, None) == B.MOE_OK
+    bad = B.make_config(10, 64, 8, 32, 9)
+    assert B.lib().moe_layer_forward_noalloc(ctypes.byref(bad), ctypes.byref(w), None, None,
+                                             None, None, None, None) == B.MOE_ERR_INVALID_ARG
+    # decode-shaped calls fit
+    assert B.workspace_size(B.make_config(64, 2048, 64, 1024, 8)) <= B.MOE_NOALLOC_SCRATCH_BYTES
+
+
 def test_workspace_table_offsets():
     """The dispatch tables a fused call leaves in its workspace lie inside the
     layer-forward workspace, 256-byte aligned and disjoint; bad arguments
@@ -41,7 +62,7 @@ def test_workspace_table_offsets():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert B.status_string(s).startswith("MOE_")
     assert "UNKNOWN" in B.status_string(99)
 
