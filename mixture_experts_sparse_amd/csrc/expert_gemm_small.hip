@@ -203,15 +203,35 @@ __device__ __forceinline__ u32x4_t codes_bf16(uint32_t D) {
   return r;
 }
 
+// A workgroup's codes and scale words are staged in LDS first. A column's
+// codes are K/2 contiguous bytes and the workgroup's columns are adjacent
+// rows of the expert's matrix, so direct global->LDS loads of 16 bytes per
+// lane read whole cache lines (1 KB per wave instruction); loading each
+// lane's 8 bytes of a group straight into registers instead touches 16 lines
+// per instruction for 32 bytes each, and the L2's request rate, not the
+// bytes, then sets the kernel's time (measured on MI355X: 4-bit decode at
+// T = 64 took 142 us per layer that way, 108 us staged).
+// Codes sit in LDS as rows of K/2 bytes with each row's 16-byte chunks
+// XOR-swizzled by the row (chunk c of row r at c ^ (r mod Z)), so the 16 rows
+// one MFMA fragment reads fall in different bank groups; scale words sit as
+// rows of (K/64 | 1) words (an odd stride: conflict-free word reads).
 template <int KIND, int NW, int KS, int NT>
-__global__ __launch_bounds__(NW * 64) void gemm_small_q4_kernel(GemmParams p) {
+__global__ __launch_bounds__(NW * 64) void gemm_small_q4_lds(GemmParams p) {
   constexpr int NB = KIND == 0 ? 2 : 1;
   constexpr int NCOL = 16 * NT;
-  constexpr int KG = KS / 2;  // scale groups per wave
+  constexpr int KG = KS / 2;
+  constexpr int NTHR = NW * 64;
+  constexpr int KMAX = NW * KS * 32;
   static_assert(KS % 2 == 0, "whole scale groups per wave");
+  constexpr int CODE_ROUND = (NB * NCOL * (KMAX / 2) + NTHR * 16 - 1) / (NTHR * 16) * (NTHR * 16);
+  constexpr int SW_MAX = (KMAX / 64) | 1;
+  constexpr int SC_ROUND = (NB * NCOL * SW_MAX + NTHR - 1) / NTHR * NTHR;
+  __shared__ __align__(16) uint8_t Lc[CODE_ROUND];
+  __shared__ __align__(16) uint32_t Ls[SC_ROUND];
   __shared__ float red[NW][NB][16][NCOL];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int N = p.N, K = p.K;
   const int ncs = (N + NCOL - 1) / NCOL;
   const int slot = blockIdx.x / ncs;
@@ -223,33 +243,47 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_q4_kernel(GemmParams p) {
   const int e = min(max(ti.x, 0), p.E - 1);
   const int r0 = min(max(ti.y, 0), p.P);
   const int cnt = min(max(ti.z, 0), p.P - r0);
-  const int kb = wave * KS * 32 + (lane >> 4) * 16;  // lane's first K index in group 0
   const uint16_t* A = static_cast<const uint16_t*>(p.a);
-
   int first_pair = 0;
   if constexpr (KIND == 0) first_pair = p.perm[min(max(r0 + min(lane & 15, cnt - 1), 0), p.P - 1)];
 
-  uint2 qc[NB][NT][KG];
-  uint32_t sb[NB][NT][KG];
-#pragma unroll
-  for (int m = 0; m < NB; ++m) {
-    const uint8_t* Q = static_cast<const uint8_t*>(m == 0 ? p.b0 : p.b1) +
-                       static_cast<size_t>(e) * N * (K / 2);
-    const uint32_t* S = (m == 0 ? p.b0_sb : p.b1_sb) + static_cast<size_t>(e) * N * (K / 64);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      // columns past N reread column N - 1; their sums are never stored
-      const int n = min(n0 + t * 16 + (lane & 15), N - 1);
-#pragma unroll
-      for (int G = 0; G < KG; ++G) {
-        // groups past K reread the last one: the x operand is zero there
-        const int kq = min(kb + 64 * G, K - 16);
-        qc[m][t][G] = *reinterpret_cast<const uint2*>(Q + (static_cast<size_t>(n) * K + kq) / 2);
-        sb[m][t][G] = S[static_cast<size_t>(n) * (K / 64) + kq / 64];
-      }
-    }
+  // codes: rows R = m * NCOL + r (matrix m, column n0 + r), RB bytes each
+  const int RB = K / 2;
+  const int CPR = RB / 16;  // 16-byte chunks per row (even: K is a multiple of 64)
+  const int Z = (CPR % 8 == 0) ? 8 : ((CPR % 4 == 0) ? 4 : 2);
+  const int nchunk = NB * NCOL * CPR;
+  const int crounds = (nchunk + NTHR - 1) / NTHR;
+  const uint8_t* Q0 = static_cast<const uint8_t*>(p.b0) + static_cast<size_t>(e) * N * RB;
+  const uint8_t* Q1 = static_cast<const uint8_t*>(KIND == 0 ? p.b1 : p.b0) + static_cast<size_t>(e) * N * RB;
+  for (int i = 0; i < crounds; ++i) {
+    const int pos = min(i * NTHR + tid, nchunk - 1);  // past the end: reload the last chunk (never read)
+    const int R = pos / CPR, pc = pos - R * CPR;
+    const int lc = pc ^ (R & (Z - 1));
+    const int m = R / NCOL, r = R - m * NCOL;
+    const int n = min(n0 + r, N - 1);
+    const uint8_t* src = (m == 0 ? Q0 : Q1) + static_cast<size_t>(n) * RB + lc * 16;
+    lds_void_t* dst = (lds_void_t*)(Lc + (i * NTHR + wave * 64) * 16);
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)src, dst, 16, 0, 0);
   }
-  asm volatile("" ::: "memory");
+  // scale words: rows of SW = (K / 64) | 1 words (the pad word reloads the last)
+  const int NG = K / 64;
+  const int SW = NG | 1;
+  const int nword = NB * NCOL * SW;
+  const int srounds = (nword + NTHR - 1) / NTHR;
+  const uint32_t* S0 = p.b0_sb + static_cast<size_t>(e) * N * NG;
+  const uint32_t* S1 = (KIND == 0 ? p.b1_sb : p.b0_sb) + static_cast<size_t>(e) * N * NG;
+  for (int i = 0; i < srounds; ++i) {
+    const int w = min(i * NTHR + tid, nword - 1);
+    const int R = w / SW, g = min(w - R * SW, NG - 1);
+    const int m = R / NCOL, r = R - m * NCOL;
+    const int n = min(n0 + r, N - 1);
+    const uint32_t* src = (m == 0 ? S0 : S1) + static_cast<size_t>(n) * NG + g;
+    lds_void_t* dst = (lds_void_t*)(Ls + i * NTHR + wave * 64);
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)src, dst, 4, 0, 0);
+  }
+  const int kb = wave * KS * 32 + (lane >> 4) * 16;  // lane's first K index in the wave's group 0
+  const int j = lane >> 4;
+  bool staged = false;
 
   for (int rb = 0; rb < cnt; rb += 16) {
     const int rr = min(rb + (lane & 15), cnt - 1);
@@ -266,6 +300,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_q4_kernel(GemmParams p) {
     for (int G = 0; G < KG; ++G)
 #pragma unroll
       for (int h = 0; h < 2; ++h) aq[2 * G + h] = load_k8(arow, kb + 64 * G + 8 * h, K);
+    if (!staged) {
+      // every wave's staging loads have landed (the x rows are behind them)
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      staged = true;
+    }
     floatx4_t acc[NB][NT];
 #pragma unroll
     for (int m = 0; m < NB; ++m)
@@ -275,44 +315,37 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_q4_kernel(GemmParams p) {
     const floatx4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int G = 0; G < KG; ++G) {
-      // one group at a time: its codes are taken (pinned) only after the
-      // previous group's accumulators are final, so the compiler forms each
-      // group's bf16 operands next to their MFMAs instead of all groups'
-      // at once (4x the registers of the packed codes, hoisted out of the
-      // row loop)
-#pragma unroll
-      for (int m = 0; m < NB; ++m)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) { pin(qc[m][t][G].x); pin(qc[m][t][G].y); }
+      // groups past K read the last group (the x operand is zero there)
+      const int Gw = min(wave * KG + G, NG - 1);
       const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, aq[2 * G]);
       const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, aq[2 * G + 1]);
-      // x row sums over the group (every column of the tile holds its row's)
       floatx4_t xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
           a0, __builtin_bit_cast(bf16x8_t, ones), zero, 0, 0, 0);
       xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8_t, ones), xs, 0,
                                                    0, 0);
+      const int lc = 2 * Gw + (j >> 1);
 #pragma unroll
       for (int m = 0; m < NB; ++m)
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
+          const int R = m * NCOL + t * 16 + (lane & 15);
+          const uint2 qc = *reinterpret_cast<const uint2*>(
+              Lc + R * RB + ((lc ^ (R & (Z - 1))) * 16) + (j & 1) * 8);
+          const uint32_t sb = Ls[R * SW + Gw];
           floatx4_t ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              a0, __builtin_bit_cast(bf16x8_t, codes_bf16(qc[m][t][G].x)), zero, 0, 0, 0);
+              a0, __builtin_bit_cast(bf16x8_t, codes_bf16(qc.x)), zero, 0, 0, 0);
           ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              a1, __builtin_bit_cast(bf16x8_t, codes_bf16(qc[m][t][G].y)), ag, 0, 0, 0);
-          // this lane's column: its own scale word
-          const float sc = bf16_to_f32(static_cast<uint16_t>(sb[m][t][G] & 0xFFFFu));
-          const float b2 =
-              fmaf(-128.0f, sc, bf16_to_f32(static_cast<uint16_t>(sb[m][t][G] >> 16)));
+              a1, __builtin_bit_cast(bf16x8_t, codes_bf16(qc.y)), ag, 0, 0, 0);
+          const float sc = bf16_to_f32(static_cast<uint16_t>(sb & 0xFFFFu));
+          const float b2 = fmaf(-128.0f, sc, bf16_to_f32(static_cast<uint16_t>(sb >> 16)));
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[m][t][i] = fmaf(sc, ag[i], fmaf(b2, xs[i], acc[m][t][i]));
         }
-#pragma unroll
-      for (int m = 0; m < NB; ++m)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) pin(acc[m][t]);
     }
     small_block_epilogue<KIND, NW, NB, NT>(p, red, acc, r0, rb, cnt, n0);
   }
+  // no staging load may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // ---------------------------------------------------------------------------
@@ -518,15 +551,20 @@ static hipError_t launch_small_kind(const GemmParams& p, int slots, hipStream_t 
 
 template <int KIND, int NT>
 static hipError_t launch_small_q4(const GemmParams& p, int slots, hipStream_t s) {
-  const SmallShape sh = small_shape(p.K);
+  // eight waves split reductions above 512 (half the registers per wave of
+  // four, so twice the workgroups per CU)
+  SmallShape sh;
+  if (p.K <= 4 * 4 * 32) sh = {4, 4};
+  else if (p.K <= 8 * 4 * 32) sh = {8, 4};
+  else if (p.K <= 8 * 8 * 32) sh = {8, 8};
+  else sh = {8, 16};
   const long long nblk = static_cast<long long>(slots) * ceil_div(p.N, 16 * NT);
   if (nblk <= 0) return hipSuccess;
   const unsigned g = static_cast<unsigned>(nblk);
-  if (sh.nw == 4 && sh.ks == 4) gemm_small_q4_kernel<KIND, 4, 4, NT><<<g, 256, 0, s>>>(p);
-  else if (sh.nw == 4 && sh.ks == 8) gemm_small_q4_kernel<KIND, 4, 8, NT><<<g, 256, 0, s>>>(p);
-  else if (sh.nw == 4 && sh.ks == 16) gemm_small_q4_kernel<KIND, 4, 16, NT><<<g, 256, 0, s>>>(p);
-  else if (sh.nw == 8 && sh.ks == 16) gemm_small_q4_kernel<KIND, 8, 16, NT><<<g, 512, 0, s>>>(p);
-  else return hipErrorInvalidValue;
+  if (sh.nw == 4) gemm_small_q4_lds<KIND, 4, 4, NT><<<g, 256, 0, s>>>(p);
+  else if (sh.ks == 4) gemm_small_q4_lds<KIND, 8, 4, NT><<<g, 512, 0, s>>>(p);
+  else if (sh.ks == 8) gemm_small_q4_lds<KIND, 8, 8, NT><<<g, 512, 0, s>>>(p);
+  else gemm_small_q4_lds<KIND, 8, 16, NT><<<g, 512, 0, s>>>(p);
   return hipGetLastError();
 }
 
