@@ -273,6 +273,50 @@ def test_edge_cases(name):
     full_parity(generate(spec))
 
 
+# At most 4 tokens and 64 experts: the split router's one-wave finish
+# (selection by rank, gates, dispatch tables) in every gating mode, with and
+# without the router bias and the shared-expert gate, k = 1 and k = E.
+TINY_ROUTE = {
+    "T1_softmax_all": small_spec("decode", T=1, d=264, E=64, h=64, k=8),
+    "T2_softmax_all_renorm_bias": small_spec("skewed_prefill", T=2, d=264, E=60, h=64, k=8),
+    "T3_softmax_selected": MoESpec(name="t3_sel", T=3, d=200, E=37, h=40, k=5,
+                                   mode=SOFTMAX_SELECTED),
+    "T4_shared_gate": small_spec("shared_routed", T=4, d=264, E=60, h=64, k=4, shared_h=96),
+    "T4_sigmoid_renorm": small_spec("small_moe_sigmoid", T=4, d=256, E=64, h=64, k=8,
+                                    shared_h=64),
+    "T3_sigmoid_raw_k20": small_spec("small_moe_sigmoid", T=3, d=128, E=64, h=32, k=20,
+                                     shared_h=0, renormalize=False),
+    "T4_k1": small_spec("skewed_prefill", T=4, d=128, E=16, h=64, k=1),
+    "T2_k_eq_E": small_spec("decode", T=2, d=64, E=8, h=32, k=8),
+    "T1_E1": small_spec("decode", T=1, d=64, E=1, h=32, k=1),
+    "T4_fp32": small_spec("tiny_fp32", T=4),
+}
+
+
+@pytest.mark.parametrize("name", list(TINY_ROUTE))
+def test_tiny_batch_routing(name):
+    spec = TINY_ROUTE[name]
+    say(f"[gpu] tiny route {name}: T={spec.T} d={spec.d} E={spec.E} k={spec.k} mode={spec.mode}")
+    inp = generate(spec)
+    cfg = B.config_from_spec(spec)
+    ws = B.alloc_workspace(cfg)
+    g, ref, _ = full_parity(inp, ws=ws)
+    _check_tables(cfg, ws, g["ids"], spec.E, name)
+    say("    dispatch tables bit-exact")
+
+
+def test_tiny_batch_ties():
+    """All-zero router on three tokens: every score ties, so the ids are
+    0..k-1 and the softmax-all gates 1/E."""
+    spec = small_spec("decode", T=3, d=64, E=12, h=32, k=3)
+    inp = generate(spec)
+    inp["w_router"] = np.zeros_like(inp["w_router"])
+    g = run_layer(inp)
+    assert np.all(g["ids"] == np.arange(3)[None, :])
+    assert np.allclose(g["gates"], 1.0 / 12, rtol=0, atol=1e-7)
+    assert np.array_equal(g["counts"], np.r_[np.full(3, 3), np.zeros(9)].astype(np.int64))
+
+
 def test_all_tokens_one_expert_and_empty_experts():
     """Router weights zero plus a bias that favours expert 5: every token
     picks 5 first (then the next-largest biases), most experts stay empty,
