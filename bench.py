@@ -70,7 +70,7 @@ def stage_work(spec, U, T):
 
 # kernel-name prefixes of each stage's (first) kernel in a rocprofv3 record
 STAGE_KERNEL = {"route": ("route_kernel", "route_part_kernel"),
-                "dispatch": ("scan_kernel", "route_finish_kernel"),
+                "dispatch": ("scan_kernel", "route_finish_kernel", "route_tiny_kernel"),
                 "gate_up": ("gemm_bf16_pers<0", "gemm_bf16_kernel<0", "gemm_small_kernel<0",
                             "gemm_small_q4_lds<0"),
                 "down": ("gemm_bf16_pers<1", "gemm_bf16_kernel<1", "gemm_small_kernel<1",
