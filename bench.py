@@ -180,6 +180,9 @@ SUBRECORDS = ("tiny_fp32", "gemma_upcycled", "decode@T1", "decode@T4", "decode@T
 # at most this many weight copies (the tiny layer's 0.8 MB would need
 # thousands; its time is launch latency either way)
 MAX_SLOTS = 256
+# spin-kernel cycles per traced step held ahead of the host's launches
+# (about 0.1 ms per step at the shader clock)
+HOLD_CYCLES_PER_STEP = 200_000
 
 WNAMES = ("w_router", "b_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down",
           "w_shared_gate", "w_gate_sb", "w_up_sb", "w_down_sb")
@@ -206,6 +209,39 @@ def touched_weight_bytes(spec, U):
     if spec.shared_h:
         n += 3.0 * spec.d * spec.shared_h * spec.act_bytes
     return n
+
+
+def isolated_stage_us(call, steps, nstages=None):
+    """Mean duration (us) of every stage of ``call(i, events)``, each timed in
+    a pass of ``steps`` calls of its own whose event rows hold only that
+    stage's two boundary events (the others NULL, which the library skips)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_sparse_amd.binding as B
+    from mixture_experts_sparse_amd.hip_timing import StageEvents
+
+    n = B.MOE_NUM_STAGES if nstages is None else nstages
+    out = []
+    for s in range(n):
+        ev = StageEvents(steps, n)
+        rows = []
+        for i in range(steps):
+            arr = (ctypes.c_void_p * (n + 1))()
+            arr[s], arr[s + 1] = ev.row(i)[s], ev.row(i)[s + 1]
+            rows.append(arr)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(HOLD_CYCLES_PER_STEP * steps)
+        for i in range(steps):
+            call(i, rows[i])
+        torch.cuda.synchronize()
+        ev.hip.hipEventSynchronize(ev.row(steps - 1)[s + 1])
+        out.append(float(np.mean([ev.elapsed_ms(ev.row(i)[s], ev.row(i)[s + 1])
+                                  for i in range(steps)])) * 1e3)
+        ev.destroy()
+    return out
 
 
 def measure_forward(name, steps, warmup, rotate_gib, inp=None, calibrate_copy_mib=0):
@@ -293,12 +329,18 @@ def measure_forward(name, steps, warmup, rotate_gib, inp=None, calibrate_copy_mi
     # boundary (each event pair adds a few microseconds of its own)
     ev = StageEvents(steps)
     torch.cuda.synchronize()
+    # a bounded spin kernel holds the stream while the host enqueues the
+    # traced steps, so that no stage interval absorbs a host launch gap
+    torch.cuda._sleep(HOLD_CYCLES_PER_STEP * steps)
     for i in range(steps):
         call(i, ev.row(i))
     torch.cuda.synchronize()
     stage = np.array(ev.stage_ms())  # [steps, stages]
     traced_ms = ev.span_ms() / steps
     ev.destroy()
+    # each stage alone: K more steps with events at that stage's two
+    # boundaries only, so no other event's overhead falls inside it
+    iso_us = isolated_stage_us(call, steps)
 
     if calibrate_copy_mib > 0:
         n = calibrate_copy_mib * 2**20
@@ -312,7 +354,7 @@ def measure_forward(name, steps, warmup, rotate_gib, inp=None, calibrate_copy_mi
 
     step_U = [slot_U[i % nslots] for i in range(steps)]
     Umean = float(np.mean(step_U))
-    mean_stage_us = {n: float(stage[:, i].mean() * 1e3) for i, n in enumerate(B.STAGE_NAMES)}
+    mean_stage_us = dict(zip(B.STAGE_NAMES, iso_us))
     bound = BOUND[base]
     dom = max(mean_stage_us, key=mean_stage_us.get)
     dwork = [stage_work(spec, U, T)[dom] for U in step_U]
@@ -594,13 +636,18 @@ def run_backward(args, spec, inp, cfg, x, wstructs, nsets, B, R, StageEvents):
     log(f"[bench] backward: timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
     ev = StageEvents(args.steps, B.MOE_NUM_BWD_STAGES)
     torch.cuda.synchronize()
+    torch.cuda._sleep(HOLD_CYCLES_PER_STEP * args.steps)  # as in the forward's traced loop
     for i in range(args.steps):
         B.layer_backward(cfg, wstructs[i % nsets], x, dout, grads=grads, ws=ws,
                          stage_events=ev.row(i))
     torch.cuda.synchronize()
-    stage = np.array(ev.stage_ms())
     traced_ms = ev.span_ms() / args.steps
     ev.destroy()
+
+    def bcall(i, row):
+        B.layer_backward(cfg, wstructs[i % nsets], x, dout, grads=grads, ws=ws, stage_events=row)
+
+    iso_us = isolated_stage_us(bcall, args.steps, B.MOE_NUM_BWD_STAGES)
     if args.calibrate_copy_mib > 0:
         src = torch.empty(args.calibrate_copy_mib * 2**20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -609,7 +656,7 @@ def run_backward(args, spec, inp, cfg, x, wstructs, nsets, B, R, StageEvents):
         torch.cuda.synchronize()
         log(f"[bench] reference copy of {args.calibrate_copy_mib} MiB done")
         del src, dst
-    mean_stage_us = {n: float(stage[:, i].mean() * 1e3) for i, n in enumerate(B.BWD_STAGE_NAMES)}
+    mean_stage_us = dict(zip(B.BWD_STAGE_NAMES, iso_us))
     flops = R.backward_stage_flops(T, spec.d, spec.E, spec.h, spec.k, spec.shared_h,
                                    spec.shared_gate)
     nbytes = R.backward_stage_bytes(T, spec.d, spec.E, spec.h, spec.k, spec.shared_h)

@@ -286,7 +286,8 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const 
 /* moe_layer_forward that also records stage_events[0] before the first
  * launch and stage_events[i + 1] after stage i (MOE_NUM_STAGES stages:
  * route, dispatch, gate_up, down, combine). stage_events holds
- * MOE_NUM_STAGES + 1 hipEvent_t created by the caller; NULL = untraced. */
+ * MOE_NUM_STAGES + 1 hipEvent_t created by the caller; NULL = untraced, and
+ * a NULL entry is not recorded (so one stage can be bracketed alone). */
 moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
                                     const void* x, void* out, int32_t* ids, float* gates,
                                     int32_t* counts, void* ws, size_t ws_bytes,
@@ -351,7 +352,8 @@ moe_status moe_layer_backward(const moe_config* cfg, const moe_weights* w, const
 /* moe_layer_backward that also records stage_events[0] before the first
  * launch and stage_events[i + 1] after stage i (MOE_NUM_BWD_STAGES stages).
  * stage_events holds MOE_NUM_BWD_STAGES + 1 hipEvent_t created by the
- * caller; NULL = untraced. With T == 0 no event is recorded. */
+ * caller; NULL = untraced, and a NULL entry is not recorded. With T == 0
+ * no event is recorded. */
 moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w,
                                      const void* x, const void* dout, const moe_grads* grads,
                                      void* ws, size_t ws_bytes, void* const* stage_events,

@@ -852,7 +852,8 @@ hipError_t launch_backward(const BwdParams& p0, hipStream_t s, void* const* ev) 
 #define BWD_TRY(x) do { if ((err = (x)) != hipSuccess) return err; } while (0)
   // ev[i]: recorded after backward stage i (ev[0] closes the route stage)
   auto mark = [&](int i) -> hipError_t {
-    return ev == nullptr ? hipSuccess : hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), s);
+    return (ev == nullptr || ev[i] == nullptr) ? hipSuccess
+                                             : hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), s);
   };
   row_token_kernel<<<(p.T * p.k + 255) / 256, 256, 0, s>>>(p);
   BWD_TRY(hipGetLastError());

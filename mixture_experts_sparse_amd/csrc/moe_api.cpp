@@ -472,7 +472,7 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
   const WsLayout L = ws_layout(c);
   hipStream_t s = as_stream(stream);
   auto mark = [&](int i) -> hipError_t {
-    if (stage_events == nullptr) return hipSuccess;
+    if (stage_events == nullptr || stage_events[i] == nullptr) return hipSuccess;
     return hipEventRecord(reinterpret_cast<hipEvent_t>(stage_events[i]), s);
   };
   const int rt = route_tokens(c.T);
@@ -621,7 +621,7 @@ moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w
 
   hipStream_t s = as_stream(stream);
   auto mark = [&](int i) -> hipError_t {
-    if (stage_events == nullptr) return hipSuccess;
+    if (stage_events == nullptr || stage_events[i] == nullptr) return hipSuccess;
     return hipEventRecord(reinterpret_cast<hipEvent_t>(stage_events[i]), s);
   };
   const BwdLayout B = bwd_layout(c);
