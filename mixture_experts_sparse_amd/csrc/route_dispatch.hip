@@ -175,8 +175,12 @@ struct RouteCfg {
   static constexpr int KS = RBK / 32;            // MFMA steps per slice
   static constexpr int SX = RT * RBK;            // x elements per slice
   static constexpr int SW = NC * RBK;            // router elements per slice
-  static constexpr int RR = RBK == 64 ? 3 : (NCH <= 4 ? 4 : 3);  // router ring slots
-  static constexpr int RX = RBK == 64 ? (RT == 64 ? 6 : 8) : 16;  // x ring slots
+  static constexpr int RX = RBK == 64 ? 6 : 16;  // x ring slots
+  // router ring slots: as many as the LDS left by the x ring holds, 3 to 8
+  // (deeper rings measured 1-3 us faster for 60 and 64 experts, no change
+  // for 128 and 256)
+  static constexpr int RRB = (163840 - 1024 - RX * RT * RBK * 2) / (NCH * 64 * RBK * 2);
+  static constexpr int RR = RRB > 8 ? 8 : (RRB < 3 ? 3 : RRB);
   static constexpr int XCH = RT * CPR;           // x chunks per slice
   static constexpr int LX = XCH <= 256 ? 1 : XCH / 256;  // x loads per x-wave lane per slice
   static constexpr int XW = XCH <= 256 ? XCH / 64 : 4;    // x-stream waves
