@@ -293,6 +293,38 @@ TINY_ROUTE = {
 }
 
 
+# One route block of up to 16 tokens at d from 128 to 2048: the split router
+# (every gating mode, bias, shared gate, k = 1, k = E, E = 1, T = 16), the
+# dispatch tables compared bit for bit.
+SHORT_ROUTE = {
+    "T1_d2048_softmax_all": small_spec("decode", T=1, d=2048, E=64, h=64, k=8),
+    "T16_d1024_renorm_bias": small_spec("skewed_prefill", T=16, d=1024, E=64, h=64, k=8),
+    "T9_d512_selected": MoESpec(name="t9_sel", T=9, d=512, E=40, h=40, k=5,
+                                mode=SOFTMAX_SELECTED),
+    "T7_d256_shared_gate": small_spec("shared_routed", T=7, d=256, E=60, h=64, k=4, shared_h=96),
+    "T16_d256_sigmoid_bias": small_spec("small_moe_sigmoid", T=16, d=256, E=64, h=64, k=8,
+                                        shared_h=64),
+    "T12_d128_sigmoid_raw_k20": small_spec("small_moe_sigmoid", T=12, d=128, E=64, h=32, k=20,
+                                           shared_h=0, renormalize=False),
+    "T5_d512_k1": small_spec("skewed_prefill", T=5, d=512, E=16, h=64, k=1),
+    "T3_d128_k_eq_E": small_spec("decode", T=3, d=128, E=8, h=32, k=8),
+    "T2_d256_E1": small_spec("decode", T=2, d=256, E=1, h=32, k=1),
+}
+
+
+@pytest.mark.parametrize("name", list(SHORT_ROUTE))
+def test_short_batch_router(name):
+    spec = SHORT_ROUTE[name]
+    say(f"[gpu] short-batch router {name}: T={spec.T} d={spec.d} E={spec.E} k={spec.k} "
+        f"mode={spec.mode}")
+    inp = generate(spec)
+    cfg = B.config_from_spec(spec)
+    ws = B.alloc_workspace(cfg)
+    g, ref, _ = full_parity(inp, ws=ws)
+    _check_tables(cfg, ws, g["ids"], spec.E, name)
+    say("    dispatch tables bit-exact")
+
+
 @pytest.mark.parametrize("name", list(TINY_ROUTE))
 def test_tiny_batch_routing(name):
     spec = TINY_ROUTE[name]
