@@ -41,6 +41,12 @@ SMALL = {
     # at least 256 rows per expert: the 256-row tiles; d and h leave K and N tails
     "big_tile_small": small_spec("skewed_prefill", T=600, d=200, E=4, h=136, k=2),
     "big_tile_shared_small": small_spec("shared_routed", T=700, d=264, E=3, h=96, k=2, shared_h=200),
+    # 256-row tiles: a column tail (d = 200); the shared group with a longer
+    # reduction than the routed one; more tiles than the GPU has CUs
+    "tile256_col_tail": small_spec("skewed_prefill", T=600, d=200, E=4, h=128, k=2),
+    "tile256_shared_longer_k": small_spec("shared_routed", T=700, d=264, E=3, h=128, k=2,
+                                          shared_h=256),
+    "tile256_many_tiles": small_spec("skewed_prefill", T=8192, d=2048, E=4, h=128, k=2),
     "shared_fp32_small": small_spec("shared_routed", T=130, d=48, E=6, h=24, k=2, shared_h=40,
                                     dtype=F32),
     "e256_small": MoESpec(name="e256", T=150, d=64, E=256, h=32, k=6, mode=SOFTMAX_SELECTED),
