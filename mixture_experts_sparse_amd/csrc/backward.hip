@@ -860,8 +860,12 @@ hipError_t launch_backward(const BwdParams& p0, hipStream_t s, void* const* ev) 
   BWD_TRY(launch_prob<PROB_DA>(p, s));
   if (has_sh) BWD_TRY(launch_prob<PROB_DA>(q, s));
   BWD_TRY(mark(1));
-  BWD_TRY(launch_prob<PROB_Z>(p, s));
-  if (has_sh) BWD_TRY(launch_prob<PROB_Z>(q, s));
+  if (p0.zg != nullptr) {
+    BWD_TRY(launch_gemm(*p0.zg, s));  // routed and shared rows in one launch
+  } else {
+    BWD_TRY(launch_prob<PROB_Z>(p, s));
+    if (has_sh) BWD_TRY(launch_prob<PROB_Z>(q, s));
+  }
   BWD_TRY(mark(2));
   router_bwd_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(p);
   BWD_TRY(hipGetLastError());

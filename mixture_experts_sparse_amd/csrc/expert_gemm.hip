@@ -110,6 +110,115 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, TileInfo& ti) {
   return ti.nrows > 0;
 }
 
+// KIND 2, the layer backward's gate/up product: z = x W_{g|u}^T recomputed
+// (never stored). With the hidden-unit gradient da' (float32, written by the
+// backward's earlier product) and the gate g of each row -- the routed
+// pair's gate, or the shared expert's sigmoid gate -- the epilogue forms,
+// per (row, hidden unit),
+//   g a = g silu(z_g) z_u                                 (bf16, for dW_down),
+//   dz_g = g da' z_u silu'(z_g),  dz_u = g da' silu(z_g)   (bf16),
+// and per 32 hidden units the partial sum of da' a (the gate gradient): the
+// arithmetic of the backward's own z product, on 256-row tiles. The bf16
+// outputs of each wave's 16-row blocks go through its 6 KB slice of the
+// idle first stage buffer and out 16 bytes per lane.
+__device__ __forceinline__ float zrow16_sum(float v) {
+  v += __shfl_xor(v, 1, kWave);
+  v += __shfl_xor(v, 2, kWave);
+  v += __shfl_xor(v, 4, kWave);
+  v += __shfl_xor(v, 8, kWave);
+  return v;
+}
+
+template <int NWM, int NWN, int NFW>
+__device__ __forceinline__ void z_epilogue(const GemmParams& p, const TileInfo& ti,
+                                           floatx4_t (&acc)[4][NFW], uint16_t* L0) {
+  static_assert(NFW == 8, "a wave holds 64 hidden units: 4 gate and 4 up fragments");
+  static_assert(NWM * NWN * 3072 * 2 <= (NWM * 64 + NWN * NFW * 16) * 64 * 2, "slices fit L0");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave % NWM, wn = wave / NWM;
+  const int fr = lane & 15, fq = lane >> 4;
+  const bool sh = ti.e < 0;
+  const int H = sh ? p.sN : p.N;
+  const float* dh = sh ? p.zdh_s : p.zdh;
+  uint16_t* ga = sh ? p.zga_s : p.zga;
+  uint16_t* dz = sh ? p.zdz_s : p.zdz;
+  float* part = sh ? p.zpart_s : p.zpart;
+  const int npart = sh ? p.znpart_s : p.znpart;
+  const int hu0 = ti.n0 + wn * 64;   // first hidden unit of the wave
+  uint16_t* gaS = L0 + wave * 3072;  // [16][64]
+  uint16_t* dzS = gaS + 1024;        // [16][128]: gate units, then up units
+  // the wave's da' values and gates, all loads issued together (rows past
+  // the group reread the last row, units past H the last unit: never used)
+  float c[4][4][4];
+  float g[4][4];
+#pragma unroll
+  for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rt = min(wm * 64 + mf * 16 + fq * 4 + i, ti.nrows - 1);
+      const int r = ti.row0 + rt;
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf)
+        c[mf][i][nf] = dh[static_cast<size_t>(r) * H + min(hu0 + nf * 16 + fr, H - 1)];
+      if (sh) g[mf][i] = p.zsgate != nullptr ? p.zsgate[r] : 1.0f;
+      else g[mf][i] = p.zgates[min(max(p.perm[r], 0), p.P - 1)];
+    }
+#pragma unroll
+  for (int mf = 0; mf < 4; ++mf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int lr = fq * 4 + i;  // row within the 16-row block
+      const int rt = wm * 64 + mf * 16 + lr;
+      const bool rok = rt < ti.nrows;
+      float dot0 = 0.f, dot1 = 0.f;
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) {
+        const int hu = hu0 + nf * 16 + fr;
+        const float zg = acc[mf][nf][i], zu = acc[mf][nf + 4][i];
+        const float sgm = 1.0f / (1.0f + expf(-zg));  // sigmoid(z_g)
+        const float sg = zg * sgm;                     // silu(z_g)
+        const float a = sg * zu;
+        const float cv = (rok && hu < H) ? c[mf][i][nf] : 0.f;
+        if (nf < 2) dot0 += cv * a;
+        else dot1 += cv * a;
+        const float da = g[mf][i] * cv;
+        const int col = nf * 16 + fr;
+        gaS[lr * 64 + col] = f32_to_bf16(g[mf][i] * a);
+        dzS[lr * 128 + col] = f32_to_bf16(da * zu * (sgm * (1.0f + zg * (1.0f - sgm))));
+        dzS[lr * 128 + 64 + col] = f32_to_bf16(da * sg);
+      }
+      dot0 = zrow16_sum(dot0);
+      dot1 = zrow16_sum(dot1);
+      const int grp = hu0 / 32;
+      if (rok && fr == 0) {
+        const size_t pr = static_cast<size_t>(ti.row0 + rt) * npart;
+        if (grp < npart) part[pr + grp] = dot0;
+        if (grp + 1 < npart) part[pr + grp + 1] = dot1;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+    // g a: 16 rows x 8 chunks; dz: 16 rows x 16 chunks (8 gate, 8 up)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int q = j * 64 + lane, lr = q >> 3, ch = q & 7;
+      const int rt = wm * 64 + mf * 16 + lr;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(gaS + lr * 64 + ch * 8);
+      if (rt < ti.nrows && hu0 + ch * 8 < H)
+        *reinterpret_cast<u32x4_t*>(ga + static_cast<size_t>(ti.row0 + rt) * H + hu0 + ch * 8) = v;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = j * 64 + lane, lr = q >> 4, c16 = q & 15;
+      const int rt = wm * 64 + mf * 16 + lr;
+      const int u = hu0 + (c16 & 7) * 8;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(dzS + lr * 128 + c16 * 8);
+      if (rt < ti.nrows && u < H)
+        *reinterpret_cast<u32x4_t*>(dz + static_cast<size_t>(ti.row0 + rt) * (2 * H) + (c16 < 8 ? 0 : H) + u) = v;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the slice is rewritten
+  }
+}
+
 // KIND 0: gate/up: B rows [0, GBR / 2) are gate rows n0.., [GBR / 2, GBR)
 //   the up rows of the same hidden units; N tile GBR / 2 hidden units.
 // KIND 1: down: B rows [0, GBR) are output columns n0..; N tile GBR.
@@ -138,14 +247,15 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
   constexpr int BM = NWM * 64;
   constexpr int GBR = NWN * NFW * 16;           // B rows per tile
   constexpr int HB = GBR / 2;                   // gate/up: hidden units per tile
-  constexpr int BN = KIND == 0 ? HB : GBR;      // output columns per tile
+  constexpr bool GU = KIND != 1;                // gate and up rows (gate/up, backward z)
+  constexpr int BN = GU ? HB : GBR;             // output columns per tile
   constexpr int SA = BM * BK;                   // A elements per stage
   constexpr int SEL = SA + GBR * BK;            // elements per stage
   constexpr int LA = SA / 8 / NTHR;             // 16-byte A loads per thread per stage
   constexpr int LB = GBR * BK / 8 / NTHR;       // B loads per thread per stage
   constexpr int LPS = LA + LB;
   static_assert(LA * NTHR * 8 == SA && LB * NTHR * 8 == GBR * BK, "whole loads per thread");
-  static_assert(KIND == 1 || NFW % 2 == 0, "gate/up pairs gate and up fragments");
+  static_assert(!GU || NFW % 2 == 0, "gate/up pairs gate and up fragments");
   static_assert(S >= 2 && S <= 8, "stages");
   static_assert((S - 2) * LPS < 64, "vmcnt range");
   __shared__ __align__(16) uint16_t L0[SEL];
@@ -182,7 +292,7 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
   if (!shared) {
     const size_t wstride = static_cast<size_t>(N) * K;
     B0 += static_cast<size_t>(ti.e) * wstride;
-    if (KIND == 0) B1 += static_cast<size_t>(ti.e) * wstride;
+    if (GU) B1 += static_cast<size_t>(ti.e) * wstride;
   }
 
   const int tid = threadIdx.x;
@@ -195,7 +305,7 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
   // are in flight, and only then are the A addresses formed.
   const uint16_t* asrc[LA];
   int achunk[LA], asrow[LA];
-  const bool gather = KIND == 0 && !shared;
+  const bool gather = GU && !shared;
   const int uwave = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
@@ -230,7 +340,7 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
     bchunk[i] = swz_phys_to_logical<BK>(r, tid % CPR) * 8;
     int n;
     const uint16_t* base;
-    if (KIND == 0) { n = ti.n0 + (r < HB ? r : r - HB); base = r < HB ? B0 : B1; }
+    if (GU) { n = ti.n0 + (r < HB ? r : r - HB); base = r < HB ? B0 : B1; }
     else { n = ti.n0 + r; base = B0; }
     n = n < N ? n : N - 1;  // columns past N reload a valid row (never stored)
     bsrc[i] = base + static_cast<size_t>(n) * K;
@@ -279,7 +389,7 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
 #pragma unroll
     for (int nf = 0; nf < NFW; ++nf) {
       int r;
-      if (KIND == 0) {
+      if (GU) {
         constexpr int H = NFW / 2;  // gate fragments per wave (the up ones follow)
         r = (nf < H ? 0 : HB) + wn * H * 16 + (nf % H) * 16 + fr;
       } else {
@@ -352,6 +462,10 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
   }(std::make_integer_sequence<int, S>{});
   // drain the clamped loads past the last stage before L0 is reused
   __syncthreads();
+  if constexpr (KIND == 2) {
+    z_epilogue<NWM, NWN, NFW>(p, ti, acc, L0);
+    return;
+  }
 
   // epilogue: each wave stages its own sub-tile through a private slice of
   // L0, 16 rows at a time, so every lane stores 16 contiguous bytes of an
@@ -794,7 +908,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 template <int KIND, int NWM, int NWN, int NFW, int S, int BK>
 struct GemmShape {
   static constexpr int BM = NWM * 64;
-  static constexpr int BN = KIND == 0 ? NWN * NFW * 8 : NWN * NFW * 16;
+  static constexpr int BN = KIND != 1 ? NWN * NFW * 8 : NWN * NFW * 16;
   static void launch(const GemmParams& p, unsigned nblk, hipStream_t s) {
     gemm_bf16_kernel<KIND, NWM, NWN, NFW, S, BK><<<nblk, NWM * NWN * 64, 0, s>>>(p);
   }
@@ -856,6 +970,7 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     // (128-byte row segments: twice the L2->LDS rate of 64-byte ones).
     if (p.tile_m == 256) {
       if (p.kind == 0) return launch_shape<GemmShape<0, 4, 2, 8, 2, 64>>(p, s);
+      if (p.kind == 2) return launch_shape<GemmShape<2, 4, 2, 8, 2, 64>>(p, s);
       return launch_shape<GemmShape<1, 4, 2, 8, 2, 64>>(p, s);
     }
     if (p.tile_m != 128) return hipErrorInvalidValue;

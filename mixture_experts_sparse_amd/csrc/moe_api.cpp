@@ -133,7 +133,9 @@ WsLayout ws_layout(const moe_config& c) {
 struct BwdLayout {
   WsLayout tables;
   size_t logits, rtok, dh, gact, dz, part, dxr, dh_s, gact_s, dz_s, part_s, dx_s, dlb, dpre, sg_part,
-      rpart, end;
+      rpart;
+  size_t tile_e256, exp_tile0_256, meta256;  // 256-row tile table (the z product's tiles)
+  size_t end;
 };
 
 BwdLayout bwd_layout(const moe_config& c) {
@@ -168,6 +170,9 @@ BwdLayout bwd_layout(const moe_config& c) {
   B.dpre = take(T * 4);
   B.sg_part = take(static_cast<size_t>(ceil_div(c.T, 256)) * d * 4);
   B.rpart = take(static_cast<size_t>(ceil_div(c.T, kBwdRouterChunk)) * static_cast<size_t>(c.E) * d * 4);
+  B.tile_e256 = take(static_cast<size_t>(max_m_tiles(c.T * c.top_k, c.E, kTileMLarge)) * 4);
+  B.exp_tile0_256 = take((static_cast<size_t>(c.E) + 1) * 4);
+  B.meta256 = take(16);
   B.end = o;
   return B;
 }
@@ -725,6 +730,33 @@ moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w
   bp.rpart = at<float>(ws, B.rpart);
   bp.dx = gr->dx; bp.dw_router = gr->dw_router; bp.dw_gate = gr->dw_gate; bp.dw_up = gr->dw_up;
   bp.dw_down = gr->dw_down; bp.dgates = gr->dgates; bp.dlogits = gr->dlogits;
+  // at least 256 rows per expert on average: the gate/up product (z) runs on
+  // the forward's 256-row tiles, from a 256-row tile table of the same
+  // dispatch, routed and shared rows in one launch
+  GemmParams zg{};
+  if (choose_tile_m(P, c.E) == kTileMLarge) {
+    TilesParams tp{offsets, c.E, P, max_m_tiles(P, c.E, kTileMLarge), kTileMLarge,
+                   at<int32_t>(ws, B.tile_e256), at<int32_t>(ws, B.exp_tile0_256),
+                   at<int32_t>(ws, B.meta256), nullptr};
+    MOE_HIP(launch_tiles(tp, s));
+    zg.kind = 2; zg.dtype = c.dtype;
+    zg.a = x; zg.perm = perm; zg.k = c.top_k; zg.K = c.d;
+    zg.b0 = w->w_gate; zg.b1 = w->w_up; zg.N = c.h;
+    zg.offsets = offsets; zg.tile_e = at<int32_t>(ws, B.tile_e256);
+    zg.exp_tile0 = at<int32_t>(ws, B.exp_tile0_256); zg.meta = at<int32_t>(ws, B.meta256);
+    zg.E = c.E; zg.P = P; zg.max_mtiles = max_m_tiles(P, c.E, kTileMLarge);
+    zg.tile_m = kTileMLarge; zg.a_rows = c.T;
+    if (has_sh) {
+      zg.shared_T = c.T; zg.sa = x; zg.sK = c.d; zg.sb0 = w->ws_gate; zg.sb1 = w->ws_up;
+      zg.sN = c.shared_h;
+    }
+    zg.zdh = bp.dh; zg.zdh_s = bp.dh_s; zg.zgates = gates; zg.zsgate = sg;
+    zg.zga = bp.gact; zg.zga_s = bp.gact_s; zg.zdz = bp.dz; zg.zdz_s = bp.dz_s;
+    zg.zpart = bp.part; zg.zpart_s = bp.part_s;
+    zg.znpart = 2 * ceil_div(c.h, 64);
+    zg.znpart_s = has_sh ? 2 * ceil_div(c.shared_h, 64) : 0;
+    bp.zg = &zg;
+  }
   MOE_HIP(mark(1));
   MOE_HIP(launch_backward(bp, s, stage_events != nullptr ? stage_events + 1 : nullptr));
   return MOE_OK;

@@ -199,6 +199,19 @@ struct GemmParams {
   const void* sb1;        // ws_up or unused
   int sN;                 // hs or d
   void* sout;             // act_s [T, hs] or ys [T, d]
+  // kind 2 (the backward's gate/up product): inputs and outputs of its
+  // epilogue, routed rows and the shared group
+  const float* zdh;       // da' [P, h]
+  const float* zdh_s;     // [T, hs]
+  const float* zgates;    // [T * k] by pair
+  const float* zsgate;    // [T] or null (ungated shared expert: 1)
+  uint16_t* zga;          // g a [P, h]
+  uint16_t* zga_s;        // [T, hs]
+  uint16_t* zdz;          // dz [P, 2h]: gate half, then up half
+  uint16_t* zdz_s;        // [T, 2 hs]
+  float* zpart;           // [P, znpart] partial sums of da' a, 32 hidden units each
+  float* zpart_s;         // [T, znpart_s]
+  int znpart, znpart_s;
 };
 
 struct CombineParams {
@@ -283,6 +296,7 @@ struct BwdParams {
   float *dws_gate, *dws_up, *dws_down, *dw_shared_gate;
   float *dgates, *dlogits;    // optional copies
   int xcd_rows;               // row products: one contiguous tile range per XCD (set per launch)
+  const GemmParams* zg;       // host: the z product on the forward's 256-row tiles, or null
 };
 hipError_t launch_backward(const BwdParams& p, hipStream_t s, void* const* ev);
 // Tokens per partial sum of dW_r in the backward (the workspace holds

@@ -70,6 +70,9 @@ CASES = {
     "wide_expert": small_spec("skewed_prefill", T=300, d=1024, E=2, h=2056, k=1),
     # the same for the shared expert's row products (2*d*2*shared_h > 4 MiB)
     "wide_shared": small_spec("shared_routed", T=260, d=1024, E=4, h=64, k=2, shared_h=2056),
+    # 256-row tiles with an N tail of 8 hidden units (2056 = 16 * 128 + 8) and
+    # a weight operand above 4 MiB
+    "wide_expert_tile256": small_spec("skewed_prefill", T=600, d=1024, E=2, h=2056, k=1),
 }
 
 GRADS = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dws_gate", "dws_up", "dws_down",
