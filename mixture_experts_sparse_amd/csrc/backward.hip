@@ -26,7 +26,11 @@
 // The shared expert is the same arithmetic on every token with the gate
 // sigmoid(w_s . x) (or 1), and its gate's gradient w_s gets dL_s = dG_s c (1 - c).
 //
-// Every product is one kernel, bwd_gemm<PROB>: 128 x 128 output tiles per
+// With at least 256 rows per expert on average, z instead runs on the
+// forward's 256 x 256 grouped GEMM as its third kind (the same epilogue,
+// expert_gemm.hip), from a 256-row tile table of the same dispatch.
+//
+// Every other product is one kernel, bwd_gemm<PROB>: 128 x 128 output tiles per
 // 256-thread workgroup (4 waves of 64 x 64 on v_mfma_f32_16x16x32_bf16), K in
 // 32-deep stages streamed by direct global->LDS loads through a ring of two or
 // three stages (by product). An operand stored with K contiguous is read out of LDS with 16-byte

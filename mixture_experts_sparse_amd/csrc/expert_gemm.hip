@@ -1,4 +1,5 @@
-// Grouped expert GEMMs for the sparse MoE layer forward (gfx950).
+// Grouped expert GEMMs for the sparse MoE layer forward (gfx950), and the
+// backward's recomputed gate/up product on the same 256-row tiles (kind 2).
 //
 // Each workgroup computes one (expert, M tile, N tile) block of
 //   gate/up: act[r, n] = silu(sum_i x[t_r, i] W_g[e, n, i]) * (sum_i x[t_r, i] W_u[e, n, i])
