@@ -974,7 +974,8 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
       if (p.kind == 2) return launch_shape<GemmShape<2, 4, 2, 8, 2, 64>>(p, s);
       return launch_shape<GemmShape<1, 4, 2, 8, 2, 64>>(p, s);
     }
-    if (p.tile_m != 128) return hipErrorInvalidValue;
+    // the backward's z product exists on the 256-row tiles only
+    if (p.tile_m != 128 || p.kind == 2) return hipErrorInvalidValue;
     // gate/up with at least 32 rows per expert on average: 2 x 4 waves over
     // 128 hidden units, 64-deep K slices, persistent (one workgroup per CU,
     // so tile changes are hidden by the pipeline running across them);
@@ -992,6 +993,7 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
       return launch_shape<GemmShape<1, 2, 2, 5, 2, 64>>(p, s);
     return launch_shape<GemmShape<1, 2, 2, 4, 4, 32>>(p, s);
   }
+  if (p.kind == 2) return hipErrorInvalidValue;
   const long long n = static_cast<long long>(p.P) * p.N + static_cast<long long>(p.shared_T) * p.sN;
   const long long nblk = (n + 255) / 256;
   if (nblk <= 0) return hipSuccess;
