@@ -341,6 +341,20 @@ def measure_forward(name, steps, warmup, rotate_gib, inp=None, calibrate_copy_mi
     # each stage alone: K more steps with events at that stage's two
     # boundaries only, so no other event's overhead falls inside it
     iso_us = isolated_stage_us(call, steps)
+    # every step on its own: an event pair around each of K more calls (the
+    # stream held while they are enqueued), for the spread of step times
+    pc = StageEvents(steps, 1)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(HOLD_CYCLES_PER_STEP * steps)
+    for i in range(steps):
+        r = pc.row(i)
+        hip.hipEventRecord(r[0], stream)
+        call(i)
+        hip.hipEventRecord(r[1], stream)
+    torch.cuda.synchronize()
+    step_us = np.array(pc.stage_ms())[:, 0] * 1e3
+    pc.destroy()
+    step_pct = {q: float(np.percentile(step_us, v)) for q, v in (("p10", 10), ("p50", 50), ("p90", 90))}
 
     if calibrate_copy_mib > 0:
         n = calibrate_copy_mib * 2**20
@@ -401,6 +415,7 @@ def measure_forward(name, steps, warmup, rotate_gib, inp=None, calibrate_copy_mi
                    "parallelism": "single GPU"},
         "roofline": roof, "layer": layer, "stages_us": mean_stage_us,
         "traced_us_per_step": traced_ms * 1e3,
+        "step_us_each": step_pct,
     }
     if base in TARGET:
         frac = layer["mfma_frac"] if bound == "mfma" else layer["hbm_frac"]
@@ -514,6 +529,7 @@ def main():
         "target": rec.get("target"),
         "stages_us": rec["stages_us"],
         "traced_us_per_step": rec["traced_us_per_step"],
+        "step_us_each": rec["step_us_each"],
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -537,7 +553,7 @@ def main():
                 sub_inp = dict(cache[base], spec=sp, x=cache[base]["x"][:sp.T])
             r, _ = measure_forward(sub, args.steps, args.warmup, args.rotate_gib, inp=sub_inp)
             subs[sub] = {k: r[k] for k in ("tokens_per_s", "ms_per_step", "roofline", "layer",
-                                           "target", "stages_us") if k in r}
+                                           "target", "stages_us", "step_us_each") if k in r}
             subs[sub]["rotation_slots"] = r["config"]["rotation_slots"]
         result["subrecords"] = subs
         result["achievable_peaks"] = achievable_peaks()
