@@ -226,9 +226,17 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_q4_lds(GemmParams p) {
   constexpr int CODE_ROUND = (NB * NCOL * (KMAX / 2) + NTHR * 16 - 1) / (NTHR * 16) * (NTHR * 16);
   constexpr int SW_MAX = (KMAX / 64) | 1;
   constexpr int SC_ROUND = (NB * NCOL * SW_MAX + NTHR - 1) / NTHR * NTHR;
-  __shared__ __align__(16) uint8_t Lc[CODE_ROUND];
+  // gate/up with 32 columns: the cross-wave partial sums reuse the code
+  // buffer once a row block's products are done (the codes are staged again
+  // for a further row block), so two such workgroups fit a CU; the other
+  // shapes, limited by registers rather than LDS, keep a buffer of their own
+  constexpr bool ALIAS = KIND == 0 && NT == 2;
+  constexpr int RED_BYTES = NW * NB * 16 * NCOL * 4;
+  constexpr int LC_BYTES = ALIAS && RED_BYTES > CODE_ROUND ? RED_BYTES : CODE_ROUND;
+  __shared__ __align__(16) uint8_t Lc[LC_BYTES];
   __shared__ __align__(16) uint32_t Ls[SC_ROUND];
-  __shared__ float red[NW][NB][16][NCOL];
+  __shared__ float red_own[ALIAS ? 1 : NW][NB][16][NCOL];
+  auto red = ALIAS ? reinterpret_cast<float (*)[NB][16][NCOL]>(Lc) : red_own;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -255,16 +263,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_q4_lds(GemmParams p) {
   const int crounds = (nchunk + NTHR - 1) / NTHR;
   const uint8_t* Q0 = static_cast<const uint8_t*>(p.b0) + static_cast<size_t>(e) * N * RB;
   const uint8_t* Q1 = static_cast<const uint8_t*>(KIND == 0 ? p.b1 : p.b0) + static_cast<size_t>(e) * N * RB;
-  for (int i = 0; i < crounds; ++i) {
-    const int pos = min(i * NTHR + tid, nchunk - 1);  // past the end: reload the last chunk (never read)
-    const int R = pos / CPR, pc = pos - R * CPR;
-    const int lc = pc ^ (R & (Z - 1));
-    const int m = R / NCOL, r = R - m * NCOL;
-    const int n = min(n0 + r, N - 1);
-    const uint8_t* src = (m == 0 ? Q0 : Q1) + static_cast<size_t>(n) * RB + lc * 16;
-    lds_void_t* dst = (lds_void_t*)(Lc + (i * NTHR + wave * 64) * 16);
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)src, dst, 16, 0, 0);
-  }
+  auto stage_codes = [&]() {
+    for (int i = 0; i < crounds; ++i) {
+      const int pos = min(i * NTHR + tid, nchunk - 1);  // past the end: reload the last chunk (never read)
+      const int R = pos / CPR, pc = pos - R * CPR;
+      const int lc = pc ^ (R & (Z - 1));
+      const int m = R / NCOL, r = R - m * NCOL;
+      const int n = min(n0 + r, N - 1);
+      const uint8_t* src = (m == 0 ? Q0 : Q1) + static_cast<size_t>(n) * RB + lc * 16;
+      lds_void_t* dst = (lds_void_t*)(Lc + (i * NTHR + wave * 64) * 16);
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)src, dst, 16, 0, 0);
+    }
+  };
+  stage_codes();
   // scale words: rows of SW = (K / 64) | 1 words (the pad word reloads the last)
   const int NG = K / 64;
   const int SW = NG | 1;
@@ -342,7 +353,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_q4_lds(GemmParams p) {
           for (int i = 0; i < 4; ++i) acc[m][t][i] = fmaf(sc, ag[i], fmaf(b2, xs[i], acc[m][t][i]));
         }
     }
+    if constexpr (ALIAS) __syncthreads();  // every wave is done with the codes: the sums overwrite them
     small_block_epilogue<KIND, NW, NB, NT>(p, red, acc, r0, rb, cnt, n0);
+    if (ALIAS && rb + 16 < cnt) {  // uniform: another row block needs the codes again
+      stage_codes();
+      staged = false;
+    }
   }
   // no staging load may still be writing this workgroup's LDS when it exits
   __builtin_amdgcn_s_waitcnt(0);
@@ -577,7 +593,13 @@ hipError_t launch_gemm_small(const GemmParams& p, hipStream_t s) {
   if (p.quant == MOE_QUANT_Q4_G64) {
     if (p.K % 64 != 0 || p.b0_sb == nullptr || (p.kind == 0 && p.b1_sb == nullptr))
       return hipErrorInvalidValue;
-    if (p.kind == 0) return launch_small_q4<0, 1>(p, slots, s);
+    // gate/up: 32 columns per workgroup once the grid has more than four
+    // workgroups of 16 columns per CU (two of them then fit a CU), else 16
+    if (p.kind == 0) {
+      if (static_cast<long long>(slots) * ceil_div(p.N, 16) > 4LL * device_cus())
+        return launch_small_q4<0, 2>(p, slots, s);
+      return launch_small_q4<0, 1>(p, slots, s);
+    }
     return launch_small_q4<1, 2>(p, slots, s);
   }
   if (p.kind == 0) return launch_small_kind<0, 1>(p, slots, s);

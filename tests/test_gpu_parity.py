@@ -175,6 +175,11 @@ SMALL_Q4 = {
     "q4_shared": small_spec("decode_q4", T=24, d=256, E=16, h=64, k=4, shared_h=128,
                             shared_gate=True),
     "q4_k4096": small_spec("decode_q4", T=8, d=4096, E=8, h=64, k=2),
+    # more than four 16-column workgroups per CU: the 32-column gate/up shape
+    # whose partial sums reuse the code buffer, with Zipf-skewed routing so
+    # that experts of several 16-row blocks stage their codes again
+    "q4_wide_rowblocks": small_spec("decode_q4", T=64, d=256, E=64, h=512, k=4,
+                                    router_bias="zipf", renormalize=True),
 }
 
 
