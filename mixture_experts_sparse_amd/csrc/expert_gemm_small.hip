@@ -226,11 +226,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_q4_lds(GemmParams p) {
   constexpr int CODE_ROUND = (NB * NCOL * (KMAX / 2) + NTHR * 16 - 1) / (NTHR * 16) * (NTHR * 16);
   constexpr int SW_MAX = (KMAX / 64) | 1;
   constexpr int SC_ROUND = (NB * NCOL * SW_MAX + NTHR - 1) / NTHR * NTHR;
-  // gate/up with 32 columns: the cross-wave partial sums reuse the code
-  // buffer once a row block's products are done (the codes are staged again
-  // for a further row block), so two such workgroups fit a CU; the other
-  // shapes, limited by registers rather than LDS, keep a buffer of their own
-  constexpr bool ALIAS = KIND == 0 && NT == 2;
+  // the wide shapes (gate/up with 32 columns, down with 128): the cross-wave
+  // partial sums reuse the code buffer once a row block's products are done
+  // (the codes are staged again for a further row block), so two such
+  // workgroups fit a CU; the narrow ones, limited by registers rather than
+  // LDS, keep a buffer of their own
+  constexpr bool ALIAS = KIND == 0 ? NT == 2 : NT == 8;
   constexpr int RED_BYTES = NW * NB * 16 * NCOL * 4;
   constexpr int LC_BYTES = ALIAS && RED_BYTES > CODE_ROUND ? RED_BYTES : CODE_ROUND;
   __shared__ __align__(16) uint8_t Lc[LC_BYTES];
@@ -579,8 +580,12 @@ static hipError_t launch_small_q4(const GemmParams& p, int slots, hipStream_t s)
   const unsigned g = static_cast<unsigned>(nblk);
   if (sh.nw == 4) gemm_small_q4_lds<KIND, 4, 4, NT><<<g, 256, 0, s>>>(p);
   else if (sh.ks == 4) gemm_small_q4_lds<KIND, 8, 4, NT><<<g, 512, 0, s>>>(p);
-  else if (sh.ks == 8) gemm_small_q4_lds<KIND, 8, 8, NT><<<g, 512, 0, s>>>(p);
-  else gemm_small_q4_lds<KIND, 8, 16, NT><<<g, 512, 0, s>>>(p);
+  else if constexpr (NT <= 2) {  // the widest shapes' codes do not fit LDS above K = 1024
+    if (sh.ks == 8) gemm_small_q4_lds<KIND, 8, 8, NT><<<g, 512, 0, s>>>(p);
+    else gemm_small_q4_lds<KIND, 8, 16, NT><<<g, 512, 0, s>>>(p);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -600,6 +605,10 @@ hipError_t launch_gemm_small(const GemmParams& p, hipStream_t s) {
         return launch_small_q4<0, 2>(p, slots, s);
       return launch_small_q4<0, 1>(p, slots, s);
     }
+    // down: 128 columns per workgroup on the same condition, for reductions
+    // up to 1024 (32 columns otherwise)
+    if (p.K <= 1024 && static_cast<long long>(slots) * ceil_div(p.N, 32) > 4LL * device_cus())
+      return launch_small_q4<1, 8>(p, slots, s);
     return launch_small_q4<1, 2>(p, slots, s);
   }
   if (p.kind == 0) return launch_small_kind<0, 1>(p, slots, s);

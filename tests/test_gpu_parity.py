@@ -180,6 +180,9 @@ SMALL_Q4 = {
     # that experts of several 16-row blocks stage their codes again
     "q4_wide_rowblocks": small_spec("decode_q4", T=64, d=256, E=64, h=512, k=4,
                                     router_bias="zipf", renormalize=True),
+    # the same for the 128-column down shape (reduction h = 256)
+    "q4_wide_down": small_spec("decode_q4", T=48, d=1024, E=64, h=256, k=4,
+                               router_bias="zipf", renormalize=True),
 }
 
 
