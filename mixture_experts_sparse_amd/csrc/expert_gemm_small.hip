@@ -176,30 +176,45 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmParams p) {
 // the low nibble of byte i) and scale|bias words [E, N, K/64], w = s q + b.
 // Every MFMA step must lie inside one 64-wide scale group, so the K layout
 // is: scale group G of a wave's range, half h in {0, 1}; lane group g holds
-// K values kb + 64 G + 16 g + 8 h .. + 7 (x and weights alike). A lane then
+// K values kb + 64 G + 16 g + 8 h .. + 7 (x and weights alike, each 8 in the
+// order codes_bf16 gives them). A lane then
 // reads its 16 codes of a group as one 8-byte load and the group's scale and
 // bias as one 4-byte word.
 //
 // The weights are never dequantised one by one. Within a group,
 //   sum_k x_k (s q_k + b) = s sum_k x_k (128 + q_k) + (b - 128 s) sum_k x_k,
 // and 128 + q (q < 16) is an exact bf16 whose bit pattern is 0x4300 | q, so
-// the codes become MFMA operands with two integer operations per pair; each
+// the codes become MFMA operands at under one integer operation each; each
 // group's two MFMA steps accumulate on their own, the x row sums of the group
 // come from two MFMAs against ones, and the scale and bias are applied to the
 // group's accumulator with two FMAs per output.
 // ---------------------------------------------------------------------------
 
-// bf16 pairs (128 + q_2j, 128 + q_2j+1), j = 0..3, of the 8 codes of D (code
-// i in nibble i), exact.
+// The 8 codes of D (code i in nibble i) as exact bf16 values 128 + q, in 7
+// integer operations: each 32-bit output takes one nibble from bytes 0 and 2
+// (or 1 and 3) of D, so a shift and one and-or make the pair. The K order is
+// then q0 q4 q2 q6 q1 q5 q3 q7, and the x operand is loaded in the same order
+// (x_perm8); an MFMA's sum over its K positions does not depend on their order.
 __device__ __forceinline__ u32x4_t codes_bf16(uint32_t D) {
-  const uint32_t lo = D & 0x0F0F0F0Fu;          // codes 0, 2, 4, 6 (one per byte)
-  const uint32_t hi = (D >> 4) & 0x0F0F0F0Fu;   // codes 1, 3, 5, 7
+  // the exponent bytes as a register operand, so that each pair is one
+  // and-or (a 3-operand instruction takes at most one constant)
+  uint32_t e = 0x43004300u;
+  asm("" : "+v"(e));
   u32x4_t r;
-  // byte j of lo -> bits 0..7, byte j of hi -> bits 16..23 (selector 0x0C: zero)
-  r[0] = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u;
-  r[1] = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u;
-  r[2] = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x43004300u;
-  r[3] = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u;
+  r[0] = (D & 0x000F000Fu) | e;          // q0, q4
+  r[1] = ((D >> 8) & 0x000F000Fu) | e;   // q2, q6
+  r[2] = ((D >> 4) & 0x000F000Fu) | e;   // q1, q5
+  r[3] = ((D >> 12) & 0x000F000Fu) | e;  // q3, q7
+  return r;
+}
+// 8 consecutive bf16 values x0..x7 (pairs in 32-bit words, low half first)
+// in the K order of codes_bf16: x0 x4 x2 x6 x1 x5 x3 x7.
+__device__ __forceinline__ u32x4_t x_perm8(u32x4_t w) {
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_perm(w[2], w[0], 0x05040100u);  // x0, x4
+  r[1] = __builtin_amdgcn_perm(w[3], w[1], 0x05040100u);  // x2, x6
+  r[2] = __builtin_amdgcn_perm(w[2], w[0], 0x07060302u);  // x1, x5
+  r[3] = __builtin_amdgcn_perm(w[3], w[1], 0x07060302u);  // x3, x7
   return r;
 }
 
@@ -311,7 +326,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_q4_lds(GemmParams p) {
 #pragma unroll
     for (int G = 0; G < KG; ++G)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) aq[2 * G + h] = load_k8(arow, kb + 64 * G + 8 * h, K);
+      for (int h = 0; h < 2; ++h) aq[2 * G + h] = x_perm8(load_k8(arow, kb + 64 * G + 8 * h, K));
     if (!staged) {
       // every wave's staging loads have landed (the x rows are behind them)
       __builtin_amdgcn_s_waitcnt(0);

@@ -183,6 +183,21 @@ SMALL_Q4 = {
     # the same for the 128-column down shape (reduction h = 256)
     "q4_wide_down": small_spec("decode_q4", T=48, d=1024, E=64, h=256, k=4,
                                router_bias="zipf", renormalize=True),
+    # the wide shapes at a gate/up reduction short of the 8-wave span
+    # (d = 1536: the last two waves' groups are past K) and a down reduction
+    # of 384 (the last of four waves partly past K)
+    "q4_wide_k1536": small_spec("decode_q4", T=32, d=1536, E=64, h=384, k=8),
+    # a column tail in the 128-column down slices (d = 576 = 4.5 slices)
+    "q4_wide_coltail": small_spec("decode_q4", T=24, d=576, E=64, h=320, k=4,
+                                  router_bias="zipf"),
+    # more than one route block (T > 64): the dispatch tables from the scan
+    # and scatter launches
+    "q4_multiblock": small_spec("decode_q4", T=128, d=576, E=64, h=320, k=8,
+                                router_bias="zipf", renormalize=True),
+    # every token on the same few experts (k = 1, strong skew): most
+    # workgroups of the wide grid find their slot empty
+    "q4_wide_few_experts": small_spec("decode_q4", T=64, d=576, E=64, h=320, k=1,
+                                      router_bias="zipf"),
 }
 
 
@@ -195,7 +210,7 @@ def test_layer_q4_small(name):
 
 FULL = ["tiny_fp32", "gemma_upcycled", "skewed_prefill", "shared_routed",
         "decode@T1", "decode@T4", "decode@T16", "decode@T64", "small_moe_sigmoid",
-        "decode_q4@T1", "decode_q4@T64"]
+        "decode_q4@T1", "decode_q4@T4", "decode_q4@T16", "decode_q4@T64"]
 
 _cache = {}
 
