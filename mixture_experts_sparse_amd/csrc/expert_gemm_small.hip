@@ -279,34 +279,52 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_q4_lds(GemmParams p) {
   const int crounds = (nchunk + NTHR - 1) / NTHR;
   const uint8_t* Q0 = static_cast<const uint8_t*>(p.b0) + static_cast<size_t>(e) * N * RB;
   const uint8_t* Q1 = static_cast<const uint8_t*>(KIND == 0 ? p.b1 : p.b0) + static_cast<size_t>(e) * N * RB;
+  // load i of this thread stages chunk i * NTHR + tid = row R, chunk pc of
+  // the row; (R, pc) advance by (NTHR / CPR, NTHR % CPR) per load, with no
+  // division in the loop. Past the last row: reload the last chunk (never read).
+  constexpr int NROWS = NB * NCOL;
+  const int qa = NTHR / CPR, ra = NTHR - qa * CPR;
+  const int R00 = tid / CPR, pc00 = tid - R00 * CPR;
   auto stage_codes = [&]() {
+    int R = R00, pc = pc00;
     for (int i = 0; i < crounds; ++i) {
-      const int pos = min(i * NTHR + tid, nchunk - 1);  // past the end: reload the last chunk (never read)
-      const int R = pos / CPR, pc = pos - R * CPR;
-      const int lc = pc ^ (R & (Z - 1));
-      const int m = R / NCOL, r = R - m * NCOL;
+      const bool past = R >= NROWS;
+      const int Rc = past ? NROWS - 1 : R, pcc = past ? CPR - 1 : pc;
+      const int lc = pcc ^ (Rc & (Z - 1));
+      const int m = Rc / NCOL, r = Rc - m * NCOL;
       const int n = min(n0 + r, N - 1);
       const uint8_t* src = (m == 0 ? Q0 : Q1) + static_cast<size_t>(n) * RB + lc * 16;
       lds_void_t* dst = (lds_void_t*)(Lc + (i * NTHR + wave * 64) * 16);
       __builtin_amdgcn_global_load_lds((gbl_void_t*)src, dst, 16, 0, 0);
+      pc += ra;
+      R += qa;
+      if (pc >= CPR) { pc -= CPR; ++R; }
     }
   };
   stage_codes();
-  // scale words: rows of SW = (K / 64) | 1 words (the pad word reloads the last)
+  // scale words: rows of SW = (K / 64) | 1 words (the pad word reloads the
+  // last), word i * NTHR + tid = (row R, word g) advanced the same way
   const int NG = K / 64;
   const int SW = NG | 1;
   const int nword = NB * NCOL * SW;
   const int srounds = (nword + NTHR - 1) / NTHR;
   const uint32_t* S0 = p.b0_sb + static_cast<size_t>(e) * N * NG;
   const uint32_t* S1 = (KIND == 0 ? p.b1_sb : p.b0_sb) + static_cast<size_t>(e) * N * NG;
-  for (int i = 0; i < srounds; ++i) {
-    const int w = min(i * NTHR + tid, nword - 1);
-    const int R = w / SW, g = min(w - R * SW, NG - 1);
-    const int m = R / NCOL, r = R - m * NCOL;
-    const int n = min(n0 + r, N - 1);
-    const uint32_t* src = (m == 0 ? S0 : S1) + static_cast<size_t>(n) * NG + g;
-    lds_void_t* dst = (lds_void_t*)(Ls + i * NTHR + wave * 64);
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)src, dst, 4, 0, 0);
+  {
+    const int qs = NTHR / SW, rs = NTHR - qs * SW;
+    int R = tid / SW, g = tid - (tid / SW) * SW;
+    for (int i = 0; i < srounds; ++i) {
+      const bool past = R >= NROWS;
+      const int Rc = past ? NROWS - 1 : R, gc = past ? NG - 1 : min(g, NG - 1);
+      const int m = Rc / NCOL, r = Rc - m * NCOL;
+      const int n = min(n0 + r, N - 1);
+      const uint32_t* src = (m == 0 ? S0 : S1) + static_cast<size_t>(n) * NG + gc;
+      lds_void_t* dst = (lds_void_t*)(Ls + i * NTHR + wave * 64);
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)src, dst, 4, 0, 0);
+      g += rs;
+      R += qs;
+      if (g >= SW) { g -= SW; ++R; }
+    }
   }
   const int kb = wave * KS * 32 + (lane >> 4) * 16;  // lane's first K index in the wave's group 0
   const int j = lane >> 4;
