@@ -26,9 +26,10 @@
 // The shared expert is the same arithmetic on every token with the gate
 // sigmoid(w_s . x) (or 1), and its gate's gradient w_s gets dL_s = dG_s c (1 - c).
 //
-// With at least 256 rows per expert on average, z instead runs on the
-// forward's 256 x 256 grouped GEMM as its third kind (the same epilogue,
-// expert_gemm.hip), from a 256-row tile table of the same dispatch.
+// With at least 256 rows per expert on average, z and the dx rows instead
+// run on the forward's 256 x 256 grouped GEMM as its third and fourth kinds
+// (the same epilogues, expert_gemm.hip), from a 256-row tile table of the
+// same dispatch.
 //
 // Every other product is one kernel, bwd_gemm<PROB>: 128 x 128 output tiles per
 // 256-thread workgroup (4 waves of 64 x 64 on v_mfma_f32_16x16x32_bf16), K in
@@ -880,8 +881,12 @@ hipError_t launch_backward(const BwdParams& p0, hipStream_t s, void* const* ev) 
   BWD_TRY(launch_prob<PROB_DWGU>(p, s));
   if (has_sh) BWD_TRY(launch_prob<PROB_DWGU>(q, s));
   BWD_TRY(mark(5));
-  BWD_TRY(launch_prob<PROB_DXR>(p, s));
-  if (has_sh) BWD_TRY(launch_prob<PROB_DXR>(q, s));
+  if (p0.xg != nullptr) {
+    BWD_TRY(launch_gemm(*p0.xg, s));  // routed and shared rows in one launch
+  } else {
+    BWD_TRY(launch_prob<PROB_DXR>(p, s));
+    if (has_sh) BWD_TRY(launch_prob<PROB_DXR>(q, s));
+  }
   BWD_TRY(mark(6));
   BWD_TRY(launch_prob<PROB_DXROUTER>(p, s));
   {

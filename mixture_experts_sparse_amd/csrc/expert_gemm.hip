@@ -1,5 +1,6 @@
-// Grouped expert GEMMs for the sparse MoE layer forward (gfx950), and the
-// backward's recomputed gate/up product on the same 256-row tiles (kind 2).
+// Grouped expert GEMMs for the sparse MoE layer forward (gfx950), and two
+// products of the layer backward on the same 256-row tiles: the recomputed
+// gate/up product (kind 2) and the dx rows (kind 3).
 //
 // Each workgroup computes one (expert, M tile, N tile) block of
 //   gate/up: act[r, n] = silu(sum_i x[t_r, i] W_g[e, n, i]) * (sum_i x[t_r, i] W_u[e, n, i])
@@ -220,6 +221,66 @@ __device__ __forceinline__ void z_epilogue(const GemmParams& p, const TileInfo& 
   }
 }
 
+// KIND 3, the layer backward's dx rows: dx_r = dz_g[r] W_g[e] + dz_u[r] W_u[e]
+// (K = 2H: the gate units, then the up units; N = d), float32, each row
+// written at its pair's row (routed) or its token's row (shared) so that a
+// token's rows sit together for the final sum. B is stored with K as its row
+// index (W_g and W_u rows are hidden units, contiguous along d): a stage
+// holds 64 K rows of the tile's 256 columns as stored, 16-byte chunk c of K
+// row k at position c ^ kar_swz(k), and the MFMA operand is built with two
+// transposing reads (ds_read_b64_tr_b16) per fragment. A fragment read takes
+// K rows 8 g + 4 h + q (lane group g, lane quad q) of 32 consecutive K; their
+// chunk positions differ in the low four bits, so the read meets each bank
+// twice (the minimum for 512 bytes).
+__device__ __forceinline__ int kar_swz(int k) { return (k & 3) | (((k >> 3) & 3) << 2); }
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// The dx rows' epilogue: each wave stages its 64 x 128 float32 block 16 rows
+// at a time through its 8 KB slice of the idle first stage buffer (16-byte
+// chunks XOR-swizzled by bits 2..3 of the row: conflict-free writes) and
+// stores 16 bytes per lane.
+template <int NWM, int NWN, int NFW>
+__device__ __forceinline__ void dxr_epilogue(const GemmParams& p, const TileInfo& ti,
+                                             floatx4_t (&acc)[4][NFW], uint16_t* L0) {
+  constexpr int WC = NFW * 16;  // output columns per wave
+  static_assert(NWM * NWN * 16 * WC * 4 <= (NWM * 64 + NWN * NFW * 16) * 64 * 2, "slices fit L0");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave % NWM, wn = wave / NWM;
+  const int fr = lane & 15, fq = lane >> 4;
+  const bool sh = ti.e < 0;
+  const int N = sh ? p.sN : p.N;
+  float* OUT = static_cast<float*>(sh ? p.sout : p.out);
+  float* Cw = reinterpret_cast<float*>(L0) + wave * 16 * WC;
+  const int c0 = ti.n0 + wn * WC;
+#pragma unroll
+  for (int mf = 0; mf < 4; ++mf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rc = fq * 4 + i;
+#pragma unroll
+      for (int nf = 0; nf < NFW; ++nf) {
+        const int ch = nf * 4 + (fr >> 2);
+        Cw[rc * WC + ((ch ^ (fq << 2)) << 2) + (fr & 3)] = acc[mf][nf][i];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+#pragma unroll
+    for (int pass = 0; pass < 16 * WC / 4 / 64; ++pass) {
+      const int idx = pass * 64 + lane;
+      const int rc = idx / (WC / 4), ch = idx % (WC / 4);
+      const int rt = wm * 64 + mf * 16 + rc;
+      const float4 v = *reinterpret_cast<const float4*>(Cw + rc * WC + ((ch ^ (((rc >> 2) & 3) << 2)) << 2));
+      if (rt < ti.nrows && c0 + ch * 4 < N) {
+        const int r = ti.row0 + rt;
+        const int orow = sh ? r : min(max(p.perm[r], 0), p.P - 1);
+        *reinterpret_cast<float4*>(OUT + static_cast<size_t>(orow) * N + c0 + ch * 4) = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the slice is rewritten
+  }
+}
+
 // KIND 0: gate/up: B rows [0, GBR / 2) are gate rows n0.., [GBR / 2, GBR)
 //   the up rows of the same hidden units; N tile GBR / 2 hidden units.
 // KIND 1: down: B rows [0, GBR) are output columns n0..; N tile GBR.
@@ -248,7 +309,9 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
   constexpr int BM = NWM * 64;
   constexpr int GBR = NWN * NFW * 16;           // B rows per tile
   constexpr int HB = GBR / 2;                   // gate/up: hidden units per tile
-  constexpr bool GU = KIND != 1;                // gate and up rows (gate/up, backward z)
+  constexpr bool GU = KIND == 0 || KIND == 2;   // gate and up rows (gate/up, backward z)
+  constexpr bool KAR = KIND == 3;               // B with K as its row index (backward dx rows)
+  static_assert(!KAR || (BK == 64 && NWN == 2 && NFW == 8), "K-as-row stages of 64 x 256");
   constexpr int BN = GU ? HB : GBR;             // output columns per tile
   constexpr int SA = BM * BK;                   // A elements per stage
   constexpr int SEL = SA + GBR * BK;            // elements per stage
@@ -291,9 +354,10 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
   const uint16_t* B1 = static_cast<const uint16_t*>(shared ? p.sb1 : p.b1);
   uint16_t* OUT = static_cast<uint16_t*>(shared ? p.sout : p.out);
   if (!shared) {
-    const size_t wstride = static_cast<size_t>(N) * K;
+    // dx rows: W_g and W_u are [H, N] each with K = 2H
+    const size_t wstride = static_cast<size_t>(N) * (KAR ? K / 2 : K);
     B0 += static_cast<size_t>(ti.e) * wstride;
-    if (GU) B1 += static_cast<size_t>(ti.e) * wstride;
+    if (GU || KAR) B1 += static_cast<size_t>(ti.e) * wstride;
   }
 
   const int tid = threadIdx.x;
@@ -333,23 +397,25 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
       asrc[i] = A + static_cast<size_t>(src) * K;
     }
   };
-  const uint16_t* bsrc[LB];
-  int bchunk[LB];
+  const uint16_t* bsrc[KAR ? 1 : LB];
+  int bchunk[KAR ? 1 : LB];
+  if constexpr (!KAR) {
 #pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    const int r = (i * NTHR + tid) / CPR;
-    bchunk[i] = swz_phys_to_logical<BK>(r, tid % CPR) * 8;
-    int n;
-    const uint16_t* base;
-    if (GU) { n = ti.n0 + (r < HB ? r : r - HB); base = r < HB ? B0 : B1; }
-    else { n = ti.n0 + r; base = B0; }
-    n = n < N ? n : N - 1;  // columns past N reload a valid row (never stored)
-    bsrc[i] = base + static_cast<size_t>(n) * K;
+    for (int i = 0; i < LB; ++i) {
+      const int r = (i * NTHR + tid) / CPR;
+      bchunk[i] = swz_phys_to_logical<BK>(r, tid % CPR) * 8;
+      int n;
+      const uint16_t* base;
+      if (GU) { n = ti.n0 + (r < HB ? r : r - HB); base = r < HB ? B0 : B1; }
+      else { n = ti.n0 + r; base = B0; }
+      n = n < N ? n : N - 1;  // columns past N reload a valid row (never stored)
+      bsrc[i] = base + static_cast<size_t>(n) * K;
+    }
   }
 
   const int nk = (K + BK - 1) / BK;
   const bool ktail = (K % BK) != 0;
-  auto issue_a = [&](uint16_t* st, int kc) {
+  auto issue_a = [&](uint16_t* st, int kc) __attribute__((always_inline)) {
     const int k0 = min(kc, nk - 1) * BK;
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
@@ -358,16 +424,29 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
                                        (lds_void_t*)(st + (i * NTHR + wbase) * 8), 16, 0, 0);
     }
   };
-  auto issue_b = [&](uint16_t* st, int kc) {
+  auto issue_b = [&](uint16_t* st, int kc) __attribute__((always_inline)) {
     const int k0 = min(kc, nk - 1) * BK;
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
-      const int kk = min(k0 + bchunk[i], K - 8);
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(bsrc[i] + kk),
+      const uint16_t* src;
+      if constexpr (KAR) {
+        // slot i * NTHR + tid: K row kr = its index / 32 (256 columns per K
+        // row), physical chunk tid % 32; K row k is gate unit k or up unit
+        // k - K / 2 (rows past K reread the last; columns past N a valid one)
+        const int kr = i * (NTHR / 32) + (tid >> 5);
+        const int col = min(ti.n0 + (((tid & 31) ^ kar_swz(kr)) << 3), N - 8);
+        const int k = min(k0 + kr, K - 1);
+        const int HK = K / 2;
+        const bool up = k >= HK;
+        src = (up ? B1 : B0) + static_cast<size_t>(up ? k - HK : k) * N + col;
+      } else {
+        src = bsrc[i] + min(k0 + bchunk[i], K - 8);
+      }
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)src,
                                        (lds_void_t*)(st + SA + (i * NTHR + wbase) * 8), 16, 0, 0);
     }
   };
-  auto issue = [&](uint16_t* st, int kc) {
+  auto issue = [&](uint16_t* st, int kc) __attribute__((always_inline)) {
     issue_a(st, kc);
     issue_b(st, kc);
   };
@@ -382,25 +461,38 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
     for (int b = 0; b < NFW; ++b) acc[a][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   // fragment offsets within a stage (the same for every stage), per MFMA K step
-  int aoff[KS][4], boff[KS][NFW];
+  int aoff[KS][4], boff[KAR ? 1 : KS][NFW];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
     for (int mf = 0; mf < 4; ++mf) aoff[ks][mf] = swz<BK>(wm * 64 + mf * 16 + fr, ks * 4 + fq);
+    if constexpr (!KAR) {
 #pragma unroll
-    for (int nf = 0; nf < NFW; ++nf) {
-      int r;
-      if (GU) {
-        constexpr int H = NFW / 2;  // gate fragments per wave (the up ones follow)
-        r = (nf < H ? 0 : HB) + wn * H * 16 + (nf % H) * 16 + fr;
-      } else {
-        r = wn * NFW * 16 + nf * 16 + fr;
+      for (int nf = 0; nf < NFW; ++nf) {
+        int r;
+        if (GU) {
+          constexpr int H = NFW / 2;  // gate fragments per wave (the up ones follow)
+          r = (nf < H ? 0 : HB) + wn * H * 16 + (nf % H) * 16 + fr;
+        } else {
+          r = wn * NFW * 16 + nf * 16 + fr;
+        }
+        boff[ks][nf] = SA + swz<BK>(r, ks * 4 + fq);
       }
-      boff[ks][nf] = SA + swz<BK>(r, ks * 4 + fq);
     }
   }
+  // K-as-row B: lane (group g, quad q, r) reads K row 32 ks + 8 g + 4 h + q
+  // at columns 16 nf + 4 r .. + 3 of the wave's 128; with s = kar_swz of
+  // that row (the same for every ks and h), the chunk position is
+  // (wn * 16 + 2 nf + r / 2) ^ s = wn * 16 + 2 (nf ^ (s >> 1)) + (r / 2 ^ (s & 1))
+  int kbase = 0, ksw = 0;  // K row 8 g + q, h = 0, ks = 0; the rest are constant offsets
+  if constexpr (KAR) {
+    const int g = lane >> 4, q = (lane >> 2) & 3, r = lane & 3;
+    const int sw = q | (g << 2);
+    ksw = sw >> 1;
+    kbase = SA + (8 * g + q) * GBR + wn * 128 + (((r >> 1) ^ (sw & 1)) << 3) + 4 * (r & 1);
+  }
 
-  auto compute = [&](const uint16_t* st) {
+  auto compute = [&](const uint16_t* st) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8_t af[4], bf[NFW];
@@ -408,8 +500,17 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
       for (int mf = 0; mf < 4; ++mf)
         af[mf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + aoff[ks][mf]));
 #pragma unroll
-      for (int nf = 0; nf < NFW; ++nf)
-        bf[nf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + boff[ks][nf]));
+      for (int nf = 0; nf < NFW; ++nf) {
+        if constexpr (KAR) {
+          const uint16_t* b = st + kbase + ((nf ^ ksw) << 4) + ks * 32 * GBR;
+          struct { v4i16_t lo, hi; } pr = {
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)b),
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(b + 4 * GBR))};
+          bf[nf] = __builtin_bit_cast(bf16x8_t, pr);
+        } else {
+          bf[nf] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(st + boff[ks][nf]));
+        }
+      }
 #pragma unroll
       for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
@@ -432,7 +533,7 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
     }(std::make_integer_sequence<int, S - 2>{});
   };
   // One pipeline step: stage kc lives in `cur`; `nxt` receives stage kc + S - 1.
-  auto step = [&](int kc, uint16_t* cur, uint16_t* nxt) {
+  auto step = [&](int kc, uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) {
     wait_for(kc);
     stage_barrier();
     issue(nxt, kc + S - 1);
@@ -465,6 +566,10 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
   __syncthreads();
   if constexpr (KIND == 2) {
     z_epilogue<NWM, NWN, NFW>(p, ti, acc, L0);
+    return;
+  }
+  if constexpr (KIND == 3) {
+    dxr_epilogue<NWM, NWN, NFW>(p, ti, acc, L0);
     return;
   }
 
@@ -909,7 +1014,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 template <int KIND, int NWM, int NWN, int NFW, int S, int BK>
 struct GemmShape {
   static constexpr int BM = NWM * 64;
-  static constexpr int BN = KIND != 1 ? NWN * NFW * 8 : NWN * NFW * 16;
+  static constexpr int BN = (KIND == 0 || KIND == 2) ? NWN * NFW * 8 : NWN * NFW * 16;
   static void launch(const GemmParams& p, unsigned nblk, hipStream_t s) {
     gemm_bf16_kernel<KIND, NWM, NWN, NFW, S, BK><<<nblk, NWM * NWN * 64, 0, s>>>(p);
   }
@@ -972,10 +1077,15 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     if (p.tile_m == 256) {
       if (p.kind == 0) return launch_shape<GemmShape<0, 4, 2, 8, 2, 64>>(p, s);
       if (p.kind == 2) return launch_shape<GemmShape<2, 4, 2, 8, 2, 64>>(p, s);
+      if (p.kind == 3) {
+        if (p.K % 2 != 0 || p.N % 8 != 0 || (p.shared_T > 0 && (p.sK % 2 != 0 || p.sN % 8 != 0)))
+          return hipErrorInvalidValue;
+        return launch_shape<GemmShape<3, 4, 2, 8, 2, 64>>(p, s);
+      }
       return launch_shape<GemmShape<1, 4, 2, 8, 2, 64>>(p, s);
     }
-    // the backward's z product exists on the 256-row tiles only
-    if (p.tile_m != 128 || p.kind == 2) return hipErrorInvalidValue;
+    // the backward's z and dx-row products exist on the 256-row tiles only
+    if (p.tile_m != 128 || p.kind >= 2) return hipErrorInvalidValue;
     // gate/up with at least 32 rows per expert on average: 2 x 4 waves over
     // 128 hidden units, 64-deep K slices, persistent (one workgroup per CU,
     // so tile changes are hidden by the pipeline running across them);
@@ -993,7 +1103,7 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
       return launch_shape<GemmShape<1, 2, 2, 5, 2, 64>>(p, s);
     return launch_shape<GemmShape<1, 2, 2, 4, 4, 32>>(p, s);
   }
-  if (p.kind == 2) return hipErrorInvalidValue;
+  if (p.kind >= 2) return hipErrorInvalidValue;
   const long long n = static_cast<long long>(p.P) * p.N + static_cast<long long>(p.shared_T) * p.sN;
   const long long nblk = (n + 255) / 256;
   if (nblk <= 0) return hipSuccess;

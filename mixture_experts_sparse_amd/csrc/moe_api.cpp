@@ -730,10 +730,10 @@ moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w
   bp.rpart = at<float>(ws, B.rpart);
   bp.dx = gr->dx; bp.dw_router = gr->dw_router; bp.dw_gate = gr->dw_gate; bp.dw_up = gr->dw_up;
   bp.dw_down = gr->dw_down; bp.dgates = gr->dgates; bp.dlogits = gr->dlogits;
-  // at least 256 rows per expert on average: the gate/up product (z) runs on
-  // the forward's 256-row tiles, from a 256-row tile table of the same
-  // dispatch, routed and shared rows in one launch
-  GemmParams zg{};
+  // at least 256 rows per expert on average: the gate/up product (z) and
+  // the dx rows run on the forward's 256-row tiles, from a 256-row tile
+  // table of the same dispatch, routed and shared rows in one launch each
+  GemmParams zg{}, xg{};
   if (choose_tile_m(P, c.E) == kTileMLarge) {
     TilesParams tp{offsets, c.E, P, max_m_tiles(P, c.E, kTileMLarge), kTileMLarge,
                    at<int32_t>(ws, B.tile_e256), at<int32_t>(ws, B.exp_tile0_256),
@@ -756,6 +756,18 @@ moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w
     zg.znpart = 2 * ceil_div(c.h, 64);
     zg.znpart_s = has_sh ? 2 * ceil_div(c.shared_h, 64) : 0;
     bp.zg = &zg;
+    // dx rows = dz [W_g; W_u] (K = 2h), float32 in pair order
+    xg.kind = 3; xg.dtype = c.dtype;
+    xg.a = bp.dz; xg.perm = perm; xg.k = c.top_k; xg.K = 2 * c.h;
+    xg.b0 = w->w_gate; xg.b1 = w->w_up; xg.N = c.d; xg.out = bp.dxr;
+    xg.offsets = offsets; xg.tile_e = zg.tile_e; xg.exp_tile0 = zg.exp_tile0; xg.meta = zg.meta;
+    xg.E = c.E; xg.P = P; xg.max_mtiles = zg.max_mtiles;
+    xg.tile_m = kTileMLarge; xg.a_rows = c.T;
+    if (has_sh) {
+      xg.shared_T = c.T; xg.sa = bp.dz_s; xg.sK = 2 * c.shared_h; xg.sb0 = w->ws_gate;
+      xg.sb1 = w->ws_up; xg.sN = c.d; xg.sout = bp.dx_s;
+    }
+    bp.xg = &xg;
   }
   MOE_HIP(mark(1));
   MOE_HIP(launch_backward(bp, s, stage_events != nullptr ? stage_events + 1 : nullptr));

@@ -297,6 +297,7 @@ struct BwdParams {
   float *dgates, *dlogits;    // optional copies
   int xcd_rows;               // row products: one contiguous tile range per XCD (set per launch)
   const GemmParams* zg;       // host: the z product on the forward's 256-row tiles, or null
+  const GemmParams* xg;       // host: the dx rows on the forward's 256-row tiles, or null
 };
 hipError_t launch_backward(const BwdParams& p, hipStream_t s, void* const* ev);
 // Tokens per partial sum of dW_r in the backward (the workspace holds
