@@ -580,10 +580,11 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
     }
   } else {
     // float32 outputs (da'; dW_down; dW_gate|up; the dx rows, in pair order so
-    // that a token's k rows are adjacent; dW_r partials; dL W_r plus the
-    // shared gate's term, to which dx_finish_kernel adds the dx rows). This
-    // wave's 64 x 64 block goes through its 8 KB of the (now idle) stage ring,
-    // 32 rows at a time, and out 16 bytes per lane. In the staging rows,
+    // that a token's k rows are adjacent, bf16 for the routed rows like the
+    // forward's y rows; dW_r partials; dL W_r plus the shared gate's term, to
+    // which dx_finish_kernel adds the dx rows). This wave's 64 x 64 block goes
+    // through its 8 KB of the (now idle) stage ring, 32 rows at a time, and
+    // out 16 bytes per lane (8 for bf16). In the staging rows,
     // 16-column blocks are XOR-swizzled by bits 2..3 of the row, so the four
     // row groups of a fragment write to distinct banks.
     static_assert(S * SEL * 2 >= 4 * 32 * 64 * 4, "staging fits the ring");
@@ -600,9 +601,8 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
         float* o = up ? (sh ? p.dws_up : p.dw_up) : (sh ? p.dws_gate : p.dw_gate);
         if (!sh) o += static_cast<size_t>(t.e) * H * p.d;
         return o + static_cast<size_t>(up ? m - H : m) * p.d;
-      } else if constexpr (PROB == PROB_DXR) {
-        const int orow = sh ? t.row0 + ir : p.perm[t.row0 + ir];
-        return (sh ? p.dx_s : p.dxr) + static_cast<size_t>(orow) * p.d;
+      } else if constexpr (PROB == PROB_DXR) {  // the shared expert's rows (routed: bf16, below)
+        return p.dx_s + static_cast<size_t>(t.row0 + ir) * p.d;
       } else if constexpr (PROB == PROB_DWROUTER) {
         return p.rpart + (static_cast<size_t>(t.e) * p.E + m) * p.d;
       } else {  // PROB_DXROUTER
@@ -637,6 +637,17 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
               v.z += dp * bf16_to_f32(w[2]); v.w += dp * bf16_to_f32(w[3]);
             }
           }
+          if constexpr (PROB == PROB_DXR) {
+            if (!sh) {  // routed dx rows in bf16 at the pair's row
+              const uint2 o = {static_cast<uint32_t>(f32_to_bf16(v.x)) |
+                                   (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16),
+                               static_cast<uint32_t>(f32_to_bf16(v.z)) |
+                                   (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16)};
+              *reinterpret_cast<uint2*>(p.dxr + static_cast<size_t>(p.perm[t.row0 + ir]) * p.d +
+                                        t.n0 + col) = o;
+              continue;
+            }
+          }
           *reinterpret_cast<float4*>(dst_row(ir) + t.n0 + col) = v;
         }
       }
@@ -647,8 +658,9 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
   }
 }
 
-// dx[t] += the token's k routed dx rows (adjacent, pair order) + its shared
-// dx row: four columns per thread, 16-byte loads, all issued before the sum.
+// dx[t] += the token's k routed dx rows (bf16, adjacent, pair order) + its
+// shared dx row, in float32: four columns per thread, all loads issued before
+// the sum.
 __global__ __launch_bounds__(256) void dx_finish_kernel(BwdParams p) {
   const int cq = p.d / 4;
   const size_t i = blockIdx.x * 256ull + threadIdx.x;
@@ -656,15 +668,18 @@ __global__ __launch_bounds__(256) void dx_finish_kernel(BwdParams p) {
   const size_t t = i / cq;
   const int c = static_cast<int>(i - t * cq) * 4;
   float4 v = *reinterpret_cast<const float4*>(p.dx + t * p.d + c);
-  const float* rows = p.dxr + t * p.k * p.d + c;
+  const uint16_t* rows = p.dxr + t * p.k * p.d + c;  // bf16, added in float32
   for (int s0 = 0; s0 < p.k; s0 += 8) {
-    float4 r[8];
+    uint2 r[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      if (s0 + s < p.k) r[s] = *reinterpret_cast<const float4*>(rows + static_cast<size_t>(s0 + s) * p.d);
+      if (s0 + s < p.k) r[s] = *reinterpret_cast<const uint2*>(rows + static_cast<size_t>(s0 + s) * p.d);
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      if (s0 + s < p.k) { v.x += r[s].x; v.y += r[s].y; v.z += r[s].z; v.w += r[s].w; }
+      if (s0 + s < p.k) {
+        v.x += __uint_as_float(r[s].x << 16); v.y += __uint_as_float(r[s].x & 0xFFFF0000u);
+        v.z += __uint_as_float(r[s].y << 16); v.w += __uint_as_float(r[s].y & 0xFFFF0000u);
+      }
   }
   if (p.dx_s != nullptr) {
     const float4 u = *reinterpret_cast<const float4*>(p.dx_s + t * p.d + c);

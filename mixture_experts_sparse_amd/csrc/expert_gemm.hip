@@ -222,9 +222,10 @@ __device__ __forceinline__ void z_epilogue(const GemmParams& p, const TileInfo& 
 }
 
 // KIND 3, the layer backward's dx rows: dx_r = dz_g[r] W_g[e] + dz_u[r] W_u[e]
-// (K = 2H: the gate units, then the up units; N = d), float32, each row
-// written at its pair's row (routed) or its token's row (shared) so that a
-// token's rows sit together for the final sum. B is stored with K as its row
+// (K = 2H: the gate units, then the up units; N = d), each row written at its
+// pair's row in bf16 (routed; like the forward's y rows, they are added in
+// float32 by the final sum) or at its token's row in float32 (shared), so
+// that a token's rows sit together for the final sum. B is stored with K as its row
 // index (W_g and W_u rows are hidden units, contiguous along d): a stage
 // holds 64 K rows of the tile's 256 columns as stored, 16-byte chunk c of K
 // row k at position c ^ kar_swz(k), and the MFMA operand is built with two
@@ -250,7 +251,6 @@ __device__ __forceinline__ void dxr_epilogue(const GemmParams& p, const TileInfo
   const int fr = lane & 15, fq = lane >> 4;
   const bool sh = ti.e < 0;
   const int N = sh ? p.sN : p.N;
-  float* OUT = static_cast<float*>(sh ? p.sout : p.out);
   float* Cw = reinterpret_cast<float*>(L0) + wave * 16 * WC;
   const int c0 = ti.n0 + wn * WC;
 #pragma unroll
@@ -273,8 +273,18 @@ __device__ __forceinline__ void dxr_epilogue(const GemmParams& p, const TileInfo
       const float4 v = *reinterpret_cast<const float4*>(Cw + rc * WC + ((ch ^ (((rc >> 2) & 3) << 2)) << 2));
       if (rt < ti.nrows && c0 + ch * 4 < N) {
         const int r = ti.row0 + rt;
-        const int orow = sh ? r : min(max(p.perm[r], 0), p.P - 1);
-        *reinterpret_cast<float4*>(OUT + static_cast<size_t>(orow) * N + c0 + ch * 4) = v;
+        if (sh) {
+          *reinterpret_cast<float4*>(static_cast<float*>(p.sout) + static_cast<size_t>(r) * N + c0 +
+                                     ch * 4) = v;
+        } else {
+          const int orow = min(max(p.perm[r], 0), p.P - 1);
+          const uint2 o = {static_cast<uint32_t>(f32_to_bf16(v.x)) |
+                               (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16),
+                           static_cast<uint32_t>(f32_to_bf16(v.z)) |
+                               (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16)};
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + static_cast<size_t>(orow) * N +
+                                    c0 + ch * 4) = o;
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the slice is rewritten

@@ -160,7 +160,7 @@ BwdLayout bwd_layout(const moe_config& c) {
   B.gact = take(P * h * 2);
   B.dz = take(P * 2 * h * 2);
   B.part = take(P * np * 4);
-  B.dxr = take(P * d * 4);
+  B.dxr = take(P * d * 2);
   B.dh_s = take(T * hs * 4);
   B.gact_s = take(T * hs * 2);
   B.dz_s = take(T * 2 * hs * 2);
@@ -725,7 +725,7 @@ moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w
   }
   bp.rtok = at<int>(ws, B.rtok);
   bp.dh = at<float>(ws, B.dh); bp.gact = at<uint16_t>(ws, B.gact); bp.dz = at<uint16_t>(ws, B.dz);
-  bp.part = at<float>(ws, B.part); bp.dxr = at<float>(ws, B.dxr);
+  bp.part = at<float>(ws, B.part); bp.dxr = at<uint16_t>(ws, B.dxr);
   bp.dlb = at<uint16_t>(ws, B.dlb);
   bp.rpart = at<float>(ws, B.rpart);
   bp.dx = gr->dx; bp.dw_router = gr->dw_router; bp.dw_gate = gr->dw_gate; bp.dw_up = gr->dw_up;

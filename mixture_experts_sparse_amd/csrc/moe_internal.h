@@ -287,7 +287,8 @@ struct BwdParams {
   uint16_t *gact, *gact_s;    // [P, h], [T, hs] gate * silu(z_g) * z_u, bf16
   uint16_t *dz, *dz_s;        // [P, 2h], [T, 2hs] pre-activation gradients, bf16
   float *part, *part_s;       // [P, 2 ceil(h/64)], [T, 2 ceil(hs/64)] dG partial sums (32 hidden units each)
-  float *dxr, *dx_s;          // [P, d] routed dx rows (pair order t * k + slot), [T, d] shared dx, or null
+  uint16_t* dxr;              // [P, d] routed dx rows, bf16 (pair order t * k + slot)
+  float* dx_s;                // [T, d] shared dx rows, or null
   uint16_t* dlb;              // [T, Epad] dlogits, bf16, zero-padded
   float* dpre;                // [T] shared gate pre-activation gradient, or null
   float* sg_part;             // [ceil(T/256), d] partial sums of dw_shared_gate

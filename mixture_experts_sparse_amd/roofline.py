@@ -111,7 +111,8 @@ def ridge_flop_per_byte(peak_flops=PEAK_BF16_MFMA_FLOPS, peak_bytes=PEAK_HBM_BYT
 
 def backward_stage_bytes(T, d, E, h, k, hs=0, U=None):
     """Bytes each stage of the layer backward must move through HBM at least
-    once (bf16 activations and weights, float32 gradients and float32 da'),
+    once (bf16 activations, weights and routed dx rows, float32 gradients,
+    da' and the shared expert's dx rows),
     the shared expert's included; U: experts touched (all of E by default).
     route: x and W_r in, logits out; d_hidden: dO and W_d in, da' out; z: x,
     W_g|u and da' in, g a and dz out; router_grad: the gate-gradient partials
@@ -130,8 +131,8 @@ def backward_stage_bytes(T, d, E, h, k, hs=0, U=None):
             "dw_down": T * d * a + (P * h + T * hs) * a + (E * d * h + d * hs) * f,
             "dw_gate_up": 2.0 * (P * h + T * hs) * a + T * d * a + 2.0 * (E * h * d + hs * d) * f,
             "dx_rows": 2.0 * (P * h + T * hs) * a + 2.0 * (U * h * d + hs * d) * a
-                       + (P * d + (T * d if hs else 0)) * f,
-            "dx_router": T * E * a + E * d * a + T * d * a + (P * d + (T * d if hs else 0)) * f
+                       + P * d * a + (T * d if hs else 0) * f,
+            "dx_router": T * E * a + E * d * a + T * d * a + P * d * a + (T * d if hs else 0) * f
                          + T * d * f + E * d * f}
 
 

@@ -98,6 +98,8 @@ def test_backward_stage_bytes_terms():
     b = R.backward_stage_bytes(T, d, E, h, k)
     assert b["dw_gate_up"] == 2 * P * h * 2 + T * d * 2 + 2 * E * h * d * 4
     assert b["dw_down"] == T * d * 2 + P * h * 2 + E * d * h * 4
+    # the routed dx rows are stored in bf16 (the shared expert's in float32)
+    assert b["dx_rows"] == 2 * P * h * 2 + 2 * E * h * d * 2 + P * d * 2
     f = R.backward_stage_flops(T, d, E, h, k)
     assert f["dw_gate_up"] / R.PEAK_BF16_MFMA_FLOPS < b["dw_gate_up"] / R.PEAK_HBM_BYTES
     T, d, E, h, k = 16384, 2048, 128, 768, 8
