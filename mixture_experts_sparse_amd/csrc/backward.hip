@@ -10,7 +10,7 @@
 // With g the gate of a (token, slot) pair, rows r of expert e in sorted order,
 // t its token, z_g / z_u its pre-activations and a = silu(z_g) z_u:
 //
-//   da'[r]      = W_d[e]^T dO[t]                      (bwd_gemm, PROB_DA; stored)
+//   da'[r]      = W_d[e]^T dO[t]                      (bwd_gemm, PROB_DA; stored, bf16)
 //   z[r]        = x[t] W_g|u[e]^T                     (PROB_Z, never stored: its
 //                 epilogue forms g a, dz and the dG partial sums from z and da')
 //   dG[t, slot] = da'[r] . a[r]      (= dO[t] . y[r]; partial sums per 32 units)
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
     // partial sum of da' . a over its 32 hidden units (the gate gradient).
     // g a and dz are staged in this wave's 12 KB of the (now idle) stage ring
     // ([64][32] and [64][64] bf16) and stored 16 bytes per lane.
-    const float* dh = sh ? p.dh_s : p.dh;
+    const uint16_t* dh = sh ? p.dh_s : p.dh;
     uint16_t* ga = sh ? p.gact_s : p.gact;
     uint16_t* dz = sh ? p.dz_s : p.dz;
     float* part = sh ? p.part_s : p.part;
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
         for (int nf = 0; nf < 2; ++nf) {
           const int ir = min(wm * 64 + mf * 16 + fq * 4 + i, t.mlim - 1);
           const int hu = min(hu0 + nf * 16 + fr, H - 1);
-          c[mf][i][nf] = dh[static_cast<size_t>(t.row0 + ir) * H + hu];
+          c[mf][i][nf] = bf16_to_f32(dh[static_cast<size_t>(t.row0 + ir) * H + hu]);
         }
 #pragma unroll
     for (int mf = 0; mf < 4; ++mf)
@@ -579,9 +579,9 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
         *reinterpret_cast<u32x4_t*>(dz + static_cast<size_t>(t.row0 + ir) * (2 * H) + (ch < 4 ? 0 : H) + u) = v;
     }
   } else {
-    // float32 outputs (da'; dW_down; dW_gate|up; the dx rows, in pair order so
-    // that a token's k rows are adjacent, bf16 for the routed rows like the
-    // forward's y rows; dW_r partials; dL W_r plus the shared gate's term, to
+    // float32 outputs (da', in bf16; dW_down; dW_gate|up; the dx rows, in pair
+    // order so that a token's k rows are adjacent, bf16 for the routed rows like
+    // the forward's y rows; dW_r partials; dL W_r plus the shared gate's term, to
     // which dx_finish_kernel adds the dx rows). This wave's 64 x 64 block goes
     // through its 8 KB of the (now idle) stage ring, 32 rows at a time, and
     // out 16 bytes per lane (8 for bf16). In the staging rows,
@@ -591,8 +591,8 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
     float* Sw = reinterpret_cast<float*>(Ring) + wave * (32 * 64);
     auto dst_row = [&](int ir) -> float* {
       const int m = t.m0 + ir;
-      if constexpr (PROB == PROB_DA) {
-        return (sh ? p.dh_s : p.dh) + static_cast<size_t>(t.row0 + ir) * H;
+      if constexpr (PROB == PROB_DA) {  // stored in bf16, below
+        return nullptr;
       } else if constexpr (PROB == PROB_DWD) {
         float* o = sh ? p.dws_down : p.dw_down + static_cast<size_t>(t.e) * p.d * H;
         return o + static_cast<size_t>(m) * H;
@@ -636,6 +636,15 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
               v.x += dp * bf16_to_f32(w[0]); v.y += dp * bf16_to_f32(w[1]);
               v.z += dp * bf16_to_f32(w[2]); v.w += dp * bf16_to_f32(w[3]);
             }
+          }
+          if constexpr (PROB == PROB_DA) {  // da' in bf16
+            const uint2 o = {static_cast<uint32_t>(f32_to_bf16(v.x)) |
+                                 (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16),
+                             static_cast<uint32_t>(f32_to_bf16(v.z)) |
+                                 (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16)};
+            *reinterpret_cast<uint2*>((sh ? p.dh_s : p.dh) + static_cast<size_t>(t.row0 + ir) * H +
+                                      t.n0 + col) = o;
+            continue;
           }
           if constexpr (PROB == PROB_DXR) {
             if (!sh) {  // routed dx rows in bf16 at the pair's row

@@ -113,7 +113,7 @@ __device__ __forceinline__ bool decode_tile(const GemmParams& p, TileInfo& ti) {
 }
 
 // KIND 2, the layer backward's gate/up product: z = x W_{g|u}^T recomputed
-// (never stored). With the hidden-unit gradient da' (float32, written by the
+// (never stored). With the hidden-unit gradient da' (bf16, written by the
 // backward's earlier product) and the gate g of each row -- the routed
 // pair's gate, or the shared expert's sigmoid gate -- the epilogue forms,
 // per (row, hidden unit),
@@ -141,7 +141,7 @@ __device__ __forceinline__ void z_epilogue(const GemmParams& p, const TileInfo& 
   const int fr = lane & 15, fq = lane >> 4;
   const bool sh = ti.e < 0;
   const int H = sh ? p.sN : p.N;
-  const float* dh = sh ? p.zdh_s : p.zdh;
+  const uint16_t* dh = sh ? p.zdh_s : p.zdh;
   uint16_t* ga = sh ? p.zga_s : p.zga;
   uint16_t* dz = sh ? p.zdz_s : p.zdz;
   float* part = sh ? p.zpart_s : p.zpart;
@@ -161,7 +161,7 @@ __device__ __forceinline__ void z_epilogue(const GemmParams& p, const TileInfo& 
       const int r = ti.row0 + rt;
 #pragma unroll
       for (int nf = 0; nf < 4; ++nf)
-        c[mf][i][nf] = dh[static_cast<size_t>(r) * H + min(hu0 + nf * 16 + fr, H - 1)];
+        c[mf][i][nf] = bf16_to_f32(dh[static_cast<size_t>(r) * H + min(hu0 + nf * 16 + fr, H - 1)]);
       if (sh) g[mf][i] = p.zsgate != nullptr ? p.zsgate[r] : 1.0f;
       else g[mf][i] = p.zgates[min(max(p.perm[r], 0), p.P - 1)];
     }

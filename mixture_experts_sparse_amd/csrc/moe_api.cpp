@@ -156,12 +156,12 @@ BwdLayout bwd_layout(const moe_config& c) {
   const size_t nps = hs > 0 ? 2 * static_cast<size_t>(ceil_div(c.shared_h, 64)) : 0;
   B.logits = take(T * static_cast<size_t>(c.E) * 4);
   B.rtok = take(P * 4);
-  B.dh = take(P * h * 4);
+  B.dh = take(P * h * 2);
   B.gact = take(P * h * 2);
   B.dz = take(P * 2 * h * 2);
   B.part = take(P * np * 4);
   B.dxr = take(P * d * 2);
-  B.dh_s = take(T * hs * 4);
+  B.dh_s = take(T * hs * 2);
   B.gact_s = take(T * hs * 2);
   B.dz_s = take(T * 2 * hs * 2);
   B.part_s = take(T * nps * 4);
@@ -712,7 +712,7 @@ moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w
     bp.ws_gate = static_cast<const uint16_t*>(w->ws_gate);
     bp.ws_up = static_cast<const uint16_t*>(w->ws_up);
     bp.ws_down = static_cast<const uint16_t*>(w->ws_down);
-    bp.dh_s = at<float>(ws, B.dh_s); bp.gact_s = at<uint16_t>(ws, B.gact_s);
+    bp.dh_s = at<uint16_t>(ws, B.dh_s); bp.gact_s = at<uint16_t>(ws, B.gact_s);
     bp.dz_s = at<uint16_t>(ws, B.dz_s); bp.part_s = at<float>(ws, B.part_s);
     bp.dx_s = at<float>(ws, B.dx_s);
     bp.dws_gate = gr->dws_gate; bp.dws_up = gr->dws_up; bp.dws_down = gr->dws_down;
@@ -724,7 +724,7 @@ moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w
     }
   }
   bp.rtok = at<int>(ws, B.rtok);
-  bp.dh = at<float>(ws, B.dh); bp.gact = at<uint16_t>(ws, B.gact); bp.dz = at<uint16_t>(ws, B.dz);
+  bp.dh = at<uint16_t>(ws, B.dh); bp.gact = at<uint16_t>(ws, B.gact); bp.dz = at<uint16_t>(ws, B.dz);
   bp.part = at<float>(ws, B.part); bp.dxr = at<uint16_t>(ws, B.dxr);
   bp.dlb = at<uint16_t>(ws, B.dlb);
   bp.rpart = at<float>(ws, B.rpart);

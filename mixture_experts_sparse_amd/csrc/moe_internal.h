@@ -201,8 +201,8 @@ struct GemmParams {
   void* sout;             // act_s [T, hs] or ys [T, d]
   // kind 2 (the backward's gate/up product): inputs and outputs of its
   // epilogue, routed rows and the shared group
-  const float* zdh;       // da' [P, h]
-  const float* zdh_s;     // [T, hs]
+  const uint16_t* zdh;    // da' [P, h], bf16
+  const uint16_t* zdh_s;  // [T, hs]
   const float* zgates;    // [T * k] by pair
   const float* zsgate;    // [T] or null (ungated shared expert: 1)
   uint16_t* zga;          // g a [P, h]
@@ -283,7 +283,7 @@ struct BwdParams {
   const uint16_t *x, *dout, *w_router, *w_gate, *w_up, *w_down;
   const uint16_t *ws_gate, *ws_up, *ws_down, *w_shared_gate;
   int* rtok;                  // [P] token of each sorted row (perm[r] / k)
-  float *dh, *dh_s;           // [P, h], [T, hs] hidden-unit gradients da' (before the gate)
+  uint16_t *dh, *dh_s;        // [P, h], [T, hs] hidden-unit gradients da' (before the gate), bf16
   uint16_t *gact, *gact_s;    // [P, h], [T, hs] gate * silu(z_g) * z_u, bf16
   uint16_t *dz, *dz_s;        // [P, 2h], [T, 2hs] pre-activation gradients, bf16
   float *part, *part_s;       // [P, 2 ceil(h/64)], [T, 2 ceil(hs/64)] dG partial sums (32 hidden units each)

@@ -111,8 +111,8 @@ def ridge_flop_per_byte(peak_flops=PEAK_BF16_MFMA_FLOPS, peak_bytes=PEAK_HBM_BYT
 
 def backward_stage_bytes(T, d, E, h, k, hs=0, U=None):
     """Bytes each stage of the layer backward must move through HBM at least
-    once (bf16 activations, weights and routed dx rows, float32 gradients,
-    da' and the shared expert's dx rows),
+    once (bf16 activations, weights, da' and routed dx rows, float32
+    gradients and the shared expert's dx rows),
     the shared expert's included; U: experts touched (all of E by default).
     route: x and W_r in, logits out; d_hidden: dO and W_d in, da' out; z: x,
     W_g|u and da' in, g a and dz out; router_grad: the gate-gradient partials
@@ -124,9 +124,8 @@ def backward_stage_bytes(T, d, E, h, k, hs=0, U=None):
     a, f = 2.0, 4.0  # bf16, float32
     gp = -(-h // 32) + (-(-hs // 32) if hs else 0)
     return {"route": (E * d + T * d) * a + T * E * f,
-            "d_hidden": T * d * a + (U * d * h + d * hs) * a + (P * h + T * hs) * f,
-            "z": T * d * a + 2.0 * (U * h * d + hs * d) * a + (P * h + T * hs) * f
-                 + 3.0 * (P * h + T * hs) * a,
+            "d_hidden": T * d * a + (U * d * h + d * hs) * a + (P * h + T * hs) * a,
+            "z": T * d * a + 2.0 * (U * h * d + hs * d) * a + 4.0 * (P * h + T * hs) * a,
             "router_grad": P * gp * f + T * E * f + T * E * a,
             "dw_down": T * d * a + (P * h + T * hs) * a + (E * d * h + d * hs) * f,
             "dw_gate_up": 2.0 * (P * h + T * hs) * a + T * d * a + 2.0 * (E * h * d + hs * d) * f,

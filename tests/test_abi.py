@@ -224,8 +224,9 @@ def test_backward_workspace_size():
     c = _cfg()
     n = B.workspace_size(c, B.MOE_ENTRY_LAYER_BACKWARD)
     P = 100 * 2
-    # at least the float32 pre-activations and the float32 dx rows
-    assert n >= P * 2 * 32 * 4 + P * 64 * 4
+    # at least the bf16 da' [P, h], the bf16 pre-activation gradients
+    # [P, 2h] and the bf16 dx rows [P, d] (h = 32, d = 64)
+    assert n >= P * 32 * 2 + P * 2 * 32 * 2 + P * 64 * 2
     assert n % 256 == 0
     assert B.workspace_size(_cfg(d=60), B.MOE_ENTRY_LAYER_BACKWARD) == 0
 
