@@ -899,11 +899,19 @@ hipError_t launch_backward(const BwdParams& p0, hipStream_t s, void* const* ev) 
   router_bwd_kernel<<<(p.T + 3) / 4, 256, 0, s>>>(p);
   BWD_TRY(hipGetLastError());
   BWD_TRY(mark(3));
-  BWD_TRY(launch_prob<PROB_DWD>(p, s));
-  if (has_sh) BWD_TRY(launch_prob<PROB_DWD>(q, s));
+  if (p0.wdn != nullptr) {
+    BWD_TRY(launch_gemm(*p0.wdn, s));  // routed and shared in one launch
+  } else {
+    BWD_TRY(launch_prob<PROB_DWD>(p, s));
+    if (has_sh) BWD_TRY(launch_prob<PROB_DWD>(q, s));
+  }
   BWD_TRY(mark(4));
-  BWD_TRY(launch_prob<PROB_DWGU>(p, s));
-  if (has_sh) BWD_TRY(launch_prob<PROB_DWGU>(q, s));
+  if (p0.wgu != nullptr) {
+    BWD_TRY(launch_gemm(*p0.wgu, s));
+  } else {
+    BWD_TRY(launch_prob<PROB_DWGU>(p, s));
+    if (has_sh) BWD_TRY(launch_prob<PROB_DWGU>(q, s));
+  }
   BWD_TRY(mark(5));
   if (p0.xg != nullptr) {
     BWD_TRY(launch_gemm(*p0.xg, s));  // routed and shared rows in one launch

@@ -236,6 +236,13 @@ __device__ __forceinline__ void z_epilogue(const GemmParams& p, const TileInfo& 
 __device__ __forceinline__ int kar_swz(int k) { return (k & 3) | (((k >> 3) & 3) << 2); }
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+// Workgroup barrier for LDS traffic alone (no fence: loads stay in flight).
+__device__ __forceinline__ void lds_barrier_g() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // The dx rows' epilogue: each wave stages its 64 x 128 float32 block 16 rows
 // at a time through its 8 KB slice of the idle first stage buffer (16-byte
@@ -619,6 +626,233 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
       if (idx < 16 * LPR && rt < ti.nrows && c0 + ch < N) {
         *reinterpret_cast<u32x4_t*>(OUT + static_cast<size_t>(ti.row0 + rt) * N + c0 + ch) =
             *reinterpret_cast<const u32x4_t*>(Cw + rc * WLD + ch);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the slice is rewritten
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Weight gradients of the layer backward on 256 x 256 tiles:
+//   KIND 4: dW_{g|u}[e][m][n] = sum_r dz[r][m] x[t_r][n]  (M = 2H: the gate
+//           rows, then the up rows; N = d),
+//   KIND 5: dW_d[e][i][j]    = sum_r dO[t_r][i] (g a)[r][j]  (M = d; N = H),
+// summed over the sorted rows r of expert e (t_r = perm[r] / k; the shared
+// expert: every token; the row tokens come from the rtok table). Both
+// operands are rows indexed by the reduction, so both land in LDS as stored,
+// BK rows of the tile's 256 columns per stage of an S-stage ring, in the
+// layout of the dx rows' B operand (chunk c of row k at c ^ kar_swz(k)), and
+// both MFMA operands are built by transposing reads. The gathered operand's
+// tokens (x for KIND 4, dO for KIND 5) are scalar loads made one stage
+// ahead. Rows past the expert's count reread its last row and are zeroed in
+// A after they land; experts without rows write zeros. Tiles run shared ones
+// first, then routed ones expert by expert (grouping an M tile's column tiles
+// on one XCD measured the same); the float32 outputs leave through the dx
+// rows' staging.
+// ---------------------------------------------------------------------------
+template <int KIND, int S, int BK>
+__global__ __launch_bounds__(512) void gemm_wgrad_kernel(GemmParams p) {
+  constexpr int NWM = 4, NWN = 2, NFW = 8, KS = BK / 32, NTHR = 512;
+  constexpr int BM = 256, BN = 256;
+  constexpr int SA = BK * BM, SEL = SA + BK * BN;  // bf16 per stage
+  constexpr int LA = SA / 8 / NTHR;                 // 16-byte loads per thread per operand and stage
+  constexpr int LPS = 2 * LA;
+  static_assert(BK == 32 || BK == 64, "K slices of 32 or 64 rows");
+  static_assert(S >= 2 && S <= 4 && (S - 2) * LPS < 64, "stages");
+  constexpr bool GATHER_A = KIND == 5, GATHER_B = KIND == 4;
+  // one LDS array per stage (static indices after unrolling), so the
+  // compiler can tell one stage's direct loads from another's reads
+  __shared__ __align__(16) uint16_t L0[SEL];
+  __shared__ __align__(16) uint16_t L1[SEL];
+  __shared__ __align__(16) uint16_t L2[S > 2 ? SEL : 8];
+  __shared__ __align__(16) uint16_t L3[S > 3 ? SEL : 8];
+  auto buf = [&]<int I>() -> uint16_t* {
+    if constexpr (I == 0) return L0;
+    else if constexpr (I == 1) return L1;
+    else if constexpr (I == 2) return L2;
+    else return L3;
+  };
+
+  // ---- tile: shared tiles first, then E x MT x NT routed ones
+  const bool has_sh = p.shared_T > 0;
+  const int MTs = has_sh ? (p.sM + BM - 1) / BM : 0, NTs = has_sh ? (p.sN + BN - 1) / BN : 0;
+  const int nsh = MTs * NTs;
+  const int MT = (p.M + BM - 1) / BM, NT = (p.N + BN - 1) / BN;
+  int b = blockIdx.x;
+  bool sh;
+  int e, mt, nt;
+  if (b < nsh) {
+    sh = true; e = -1; mt = b / NTs; nt = b - mt * NTs;
+  } else {
+    b -= nsh;
+    sh = false; e = b / (MT * NT);
+    if (e >= p.E) return;
+    const int r = b - e * (MT * NT);
+    mt = r / NT; nt = r - mt * NT;
+  }
+  const int M = sh ? p.sM : p.M, N = sh ? p.sN : p.N;
+  const int rows = sh ? p.shared_T : p.P;  // rows of the row-indexed operands
+  int row0 = 0, cnt = p.shared_T;
+  if (!sh) {
+    row0 = min(max(ldc(p.offsets, e), 0), p.P);
+    cnt = min(max(ldc(p.offsets, e + 1), 0), p.P) - row0;
+    cnt = max(cnt, 0);
+  }
+  const int m0 = mt * BM, n0 = nt * BN;
+  const uint16_t* A = static_cast<const uint16_t*>(sh ? p.sa : p.a);
+  const uint16_t* B = static_cast<const uint16_t*>(sh ? p.sb0 : p.b0);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wbase = wave * 64;
+  const int wm = wave % NWM, wn = wave / NWM;
+  const int fr = lane & 15, fq = lane >> 4;
+  // the reduction row of stage-local K row kr, clamped into the operand
+  auto row_of = [&](int k) __attribute__((always_inline)) {
+    return min(max(row0 + min(k, cnt - 1), 0), rows - 1);
+  };
+  // tokens of this wave's K rows of a stage (rows i * 16 + 2 wave + j):
+  // wave-uniform scalar loads, issued one stage before the loads that use them
+  int tk[LA][2];
+  auto load_toks = [&](int kbase) __attribute__((always_inline)) {
+    if constexpr (GATHER_A || GATHER_B) {
+#pragma unroll
+      for (int i = 0; i < LA; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int r = row_of(kbase + i * 16 + 2 * wave + j);
+          tk[i][j] = sh ? r : min(max(ldc(p.rtok, r), 0), p.a_rows - 1);
+        }
+    }
+  };
+  const int pc = tid & 31;  // physical chunk of every load of this thread
+  auto issue = [&](uint16_t* st, int kbase) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int kr = i * (NTHR / 32) + (tid >> 5);
+      const int c = pc ^ kar_swz(kr);
+      const int gk = lane < 32 ? tk[i][0] : tk[i][1];  // gathered row of this lane
+      const int dk = row_of(kbase + kr);               // direct row
+      const int ra = GATHER_A ? gk : dk, rb = GATHER_B ? gk : dk;
+      const uint16_t* sa_ = A + static_cast<size_t>(ra) * M + min(m0 + 8 * c, M - 8);
+      const uint16_t* sb_ = B + static_cast<size_t>(rb) * N + min(n0 + 8 * c, N - 8);
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)sa_, (lds_void_t*)(st + (i * NTHR + wbase) * 8),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)sb_,
+                                       (lds_void_t*)(st + SA + (i * NTHR + wbase) * 8), 16, 0, 0);
+    }
+  };
+
+  floatx4_t acc[4][NFW];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < NFW; ++c) acc[a][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  // transposing fragment reads: lane (group g, quad q, r) reads K row
+  // 32 ks + 8 g + 4 h + q at columns 4 r .. + 3 of a 16-column fragment; with
+  // s = kar_swz of the row, A's chunk (wm * 8 + 2 mf + r / 2) ^ s and B's
+  // (wn * 16 + 2 nf + r / 2) ^ s split into a base and a per-fragment XOR
+  const int g = lane >> 4, q = (lane >> 2) & 3, r4 = lane & 3;
+  const int sw = q | (g << 2);
+  const int sA = (sw >> 1) & 3, sB = sw >> 1;
+  const int klane = (8 * g + q) * BM + (((r4 >> 1) ^ (sw & 1)) << 3) + 4 * (r4 & 1);
+  const int abase = klane + (((wm * 8) ^ (sw & 8)) << 3);
+  const int bbase = SA + klane + wn * 128;
+  auto compute = [&](const uint16_t* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8_t af[4], bf[NFW];
+#pragma unroll
+      for (int mf = 0; mf < 4; ++mf) {
+        const uint16_t* a = st + abase + ((mf ^ sA) << 4) + ks * 32 * BM;
+        struct { v4i16_t lo, hi; } pr = {__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)a),
+                                         __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(a + 4 * BM))};
+        af[mf] = __builtin_bit_cast(bf16x8_t, pr);
+      }
+#pragma unroll
+      for (int nf = 0; nf < NFW; ++nf) {
+        const uint16_t* bb = st + bbase + ((nf ^ sB) << 4) + ks * 32 * BN;
+        struct { v4i16_t lo, hi; } pr = {__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)bb),
+                                         __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(bb + 4 * BN))};
+        bf[nf] = __builtin_bit_cast(bf16x8_t, pr);
+      }
+#pragma unroll
+      for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < NFW; ++nf)
+          acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mf], bf[nf], acc[mf][nf], 0, 0, 0);
+    }
+  };
+  const int nk = (cnt + BK - 1) / BK;
+  // one step: stage kc in cur (once at most S - 2 newer stages' loads are
+  // outstanding), kc + S - 1 issued into nxt
+  auto step = [&](int kc, uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) {
+    wait_stage<(S - 2) * LPS>();
+    stage_barrier();
+    issue(nxt, (kc + S - 1) * BK);  // past the last stage: clamped rereads, never used
+    load_toks((kc + S) * BK);
+    if (kc < nk) {
+      if ((kc + 1) * BK > cnt) {
+        // rows past the expert's count: zero them in A (B's rereads then multiply zeros)
+#pragma unroll
+        for (int i = 0; i < LA; ++i) {
+          const int kr = i * (NTHR / 32) + (tid >> 5);
+          if (kc * BK + kr >= cnt)
+            *reinterpret_cast<u32x4_t*>(cur + (i * NTHR + tid) * 8) = u32x4_t{0u, 0u, 0u, 0u};
+        }
+        lds_barrier_g();
+      }
+      compute(cur);
+    }
+  };
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    // prologue: stages 0 .. S - 2, each with the tokens loaded before it
+    ((I < S - 1 ? (load_toks(I * BK), issue(buf.template operator()<I>(), I * BK)) : void()), ...);
+    load_toks((S - 1) * BK);
+    for (int kc = 0; kc < nk; kc += S) {
+      (step(kc + I, buf.template operator()<I>(), buf.template operator()<(I + S - 1) % S>()), ...);
+    }
+  }(std::make_integer_sequence<int, S>{});
+  // the clamped loads past the last stage land before L0 is reused
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // ---- epilogue: float32 rows through each wave's 8 KB slice of L0
+  constexpr int WC = NFW * 16;
+  float* Cw = reinterpret_cast<float*>(L0) + wave * 16 * WC;
+  const int c0 = n0 + wn * WC;
+  const int H = M / 2;
+  float* O1 = static_cast<float*>(sh ? p.sout : p.out);
+  float* O2 = static_cast<float*>(sh ? p.sout2 : p.out2);
+#pragma unroll
+  for (int mf = 0; mf < 4; ++mf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rc = fq * 4 + i;
+#pragma unroll
+      for (int nf = 0; nf < NFW; ++nf) {
+        const int ch = nf * 4 + (fr >> 2);
+        Cw[rc * WC + ((ch ^ (fq << 2)) << 2) + (fr & 3)] = acc[mf][nf][i];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+#pragma unroll
+    for (int pass = 0; pass < 16 * WC / 4 / 64; ++pass) {
+      const int idx = pass * 64 + lane;
+      const int rc = idx / (WC / 4), ch = idx % (WC / 4);
+      const int m = m0 + wm * 64 + mf * 16 + rc;
+      const float4 v = *reinterpret_cast<const float4*>(Cw + rc * WC + ((ch ^ (((rc >> 2) & 3) << 2)) << 2));
+      if (m < M && c0 + ch * 4 < N) {
+        float* row;
+        if constexpr (KIND == 4) {
+          // gate rows [0, H), up rows [H, 2H) of expert e
+          const size_t eoff = sh ? 0 : static_cast<size_t>(e) * H * N;
+          row = (m < H ? O1 + eoff + static_cast<size_t>(m) * N
+                       : O2 + eoff + static_cast<size_t>(m - H) * N);
+        } else {
+          row = O1 + (sh ? 0 : static_cast<size_t>(e) * M * N) + static_cast<size_t>(m) * N;
+        }
+        *reinterpret_cast<float4*>(row + c0 + ch * 4) = v;
       }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the slice is rewritten
@@ -1087,6 +1321,18 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     if (p.tile_m == 256) {
       if (p.kind == 0) return launch_shape<GemmShape<0, 4, 2, 8, 2, 64>>(p, s);
       if (p.kind == 2) return launch_shape<GemmShape<2, 4, 2, 8, 2, 64>>(p, s);
+      if (p.kind == 4 || p.kind == 5) {
+        if (p.M % 8 != 0 || p.N % 8 != 0 || (p.shared_T > 0 && (p.sM % 8 != 0 || p.sN % 8 != 0)) ||
+            (p.kind == 4 && (p.M % 2 != 0 || (p.shared_T > 0 && p.sM % 2 != 0))))
+          return hipErrorInvalidValue;
+        long long nblk = static_cast<long long>(p.E) * ceil_div(p.M, 256) * ceil_div(p.N, 256);
+        if (p.shared_T > 0) nblk += static_cast<long long>(ceil_div(p.sM, 256)) * ceil_div(p.sN, 256);
+        if (nblk <= 0) return hipSuccess;
+        if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+        if (p.kind == 4) gemm_wgrad_kernel<4, 3, 32><<<static_cast<unsigned>(nblk), 512, 0, s>>>(p);
+        else gemm_wgrad_kernel<5, 3, 32><<<static_cast<unsigned>(nblk), 512, 0, s>>>(p);
+        return hipGetLastError();
+      }
       if (p.kind == 3) {
         if (p.K % 2 != 0 || p.N % 8 != 0 || (p.shared_T > 0 && (p.sK % 2 != 0 || p.sN % 8 != 0)))
           return hipErrorInvalidValue;

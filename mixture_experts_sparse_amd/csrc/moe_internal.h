@@ -212,6 +212,13 @@ struct GemmParams {
   float* zpart;           // [P, znpart] partial sums of da' a, 32 hidden units each
   float* zpart_s;         // [T, znpart_s]
   int znpart, znpart_s;
+  // kinds 4 and 5 (the backward's weight gradients): output rows M (sM for
+  // the shared group); kind 4 writes rows [0, M / 2) to out and the rest to
+  // out2 (sout, sout2)
+  int M, sM;
+  void* out2;
+  void* sout2;
+  const int32_t* rtok;    // token of each sorted row (perm / k)
 };
 
 struct CombineParams {
@@ -299,6 +306,8 @@ struct BwdParams {
   int xcd_rows;               // row products: one contiguous tile range per XCD (set per launch)
   const GemmParams* zg;       // host: the z product on the forward's 256-row tiles, or null
   const GemmParams* xg;       // host: the dx rows on the forward's 256-row tiles, or null
+  const GemmParams* wgu;      // host: dW_gate|up on 256 x 256 tiles, or null
+  const GemmParams* wdn;      // host: dW_down on 256 x 256 tiles, or null
 };
 hipError_t launch_backward(const BwdParams& p, hipStream_t s, void* const* ev);
 // Tokens per partial sum of dW_r in the backward (the workspace holds
