@@ -798,21 +798,48 @@ __global__ __launch_bounds__(256) void router_grad_sum_kernel(BwdParams p, int n
 }
 
 // dw_shared_gate[c] = sum_t dpre[t] x[t, c]: column partial sums over token
-// blocks of 256, then their sum in block order.
+// blocks of kSgateTokens (8 columns per thread, 16-byte loads, a block's 8
+// rows of loads issued before their products), then their sum in block order.
 __global__ __launch_bounds__(256) void sgate_grad_part_kernel(BwdParams p) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= p.d) return;
-  const int t0 = blockIdx.y * 256, t1 = min(p.T, t0 + 256);
-  float s = 0.f;
-  for (int t = t0; t < t1; ++t) s += p.dpre[t] * bf16_to_f32(p.x[static_cast<size_t>(t) * p.d + c]);
-  p.sg_part[static_cast<size_t>(blockIdx.y) * p.d + c] = s;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (c >= p.d) return;  // d is a multiple of 8
+  const int t0 = blockIdx.y * kSgateTokens, t1 = min(p.T, t0 + kSgateTokens);
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int tb = t0; tb < t1; tb += 8) {
+    u32x4_t v[8];
+    float w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = min(tb + u, t1 - 1);  // past the block: reread its last row (weight 0)
+      v[u] = *reinterpret_cast<const u32x4_t*>(p.x + static_cast<size_t>(t) * p.d + c);
+      w[u] = tb + u < t1 ? p.dpre[t] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[2 * j] += w[u] * __uint_as_float(v[u][j] << 16);
+        s[2 * j + 1] += w[u] * __uint_as_float(v[u][j] & 0xFFFF0000u);
+      }
+  }
+  float* o = p.sg_part + static_cast<size_t>(blockIdx.y) * p.d + c;
+  *reinterpret_cast<float4*>(o) = float4{s[0], s[1], s[2], s[3]};
+  *reinterpret_cast<float4*>(o + 4) = float4{s[4], s[5], s[6], s[7]};
 }
 __global__ __launch_bounds__(256) void sgate_grad_final_kernel(BwdParams p, int nb) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (c >= p.d) return;
-  float s = 0.f;
-  for (int b = 0; b < nb; ++b) s += p.sg_part[static_cast<size_t>(b) * p.d + c];
-  p.dw_shared_gate[c] = s;
+  float4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int b0 = 0; b0 < nb; b0 += 8) {
+    float4 v[8];  // eight partials in flight, then added in block order
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = *reinterpret_cast<const float4*>(p.sg_part + static_cast<size_t>(min(b0 + u, nb - 1)) * p.d + c);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (b0 + u < nb) { s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w; }
+  }
+  *reinterpret_cast<float4*>(p.dw_shared_gate + c) = s;
 }
 
 template <int PROB>
@@ -935,10 +962,10 @@ hipError_t launch_backward(const BwdParams& p0, hipStream_t s, void* const* ev) 
     BWD_TRY(hipGetLastError());
   }
   if (p.dpre != nullptr) {
-    const int nb = (p.T + 255) / 256;
-    sgate_grad_part_kernel<<<dim3((p.d + 255) / 256, nb), 256, 0, s>>>(p);
+    const int nb = (p.T + kSgateTokens - 1) / kSgateTokens;
+    sgate_grad_part_kernel<<<dim3((p.d / 8 + 255) / 256, nb), 256, 0, s>>>(p);
     BWD_TRY(hipGetLastError());
-    sgate_grad_final_kernel<<<(p.d + 255) / 256, 256, 0, s>>>(p, nb);
+    sgate_grad_final_kernel<<<(p.d / 4 + 255) / 256, 256, 0, s>>>(p, nb);
     BWD_TRY(hipGetLastError());
   }
   BWD_TRY(mark(7));

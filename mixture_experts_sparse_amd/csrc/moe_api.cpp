@@ -168,7 +168,7 @@ BwdLayout bwd_layout(const moe_config& c) {
   B.dx_s = take(hs > 0 ? T * d * 4 : 0);
   B.dlb = take(T * epad * 2);
   B.dpre = take(T * 4);
-  B.sg_part = take(static_cast<size_t>(ceil_div(c.T, 256)) * d * 4);
+  B.sg_part = take(static_cast<size_t>(ceil_div(c.T, kSgateTokens)) * d * 4);
   B.rpart = take(static_cast<size_t>(ceil_div(c.T, kBwdRouterChunk)) * static_cast<size_t>(c.E) * d * 4);
   B.tile_e256 = take(static_cast<size_t>(max_m_tiles(c.T * c.top_k, c.E, kTileMLarge)) * 4);
   B.exp_tile0_256 = take((static_cast<size_t>(c.E) + 1) * 4);

@@ -32,6 +32,9 @@ constexpr int kTileNDown = 128;
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Tokens per partial sum of the shared gate's weight gradient.
+constexpr int kSgateTokens = 32;
+
 // Upper bound on the number of M tiles over all experts:
 // sum_e ceil(c_e / BM) <= floor(P / BM) + min(E, P).
 inline int max_m_tiles(int P, int E, int bm = kTileM) { return P / bm + (E < P ? E : P) + 1; }
@@ -298,7 +301,7 @@ struct BwdParams {
   float* dx_s;                // [T, d] shared dx rows, or null
   uint16_t* dlb;              // [T, Epad] dlogits, bf16, zero-padded
   float* dpre;                // [T] shared gate pre-activation gradient, or null
-  float* sg_part;             // [ceil(T/256), d] partial sums of dw_shared_gate
+  float* sg_part;             // [ceil(T/kSgateTokens), d] partial sums of dw_shared_gate
   float* rpart;               // [ceil(T/256), E, d] partial sums of dw_router
   float *dx, *dw_router, *dw_gate, *dw_up, *dw_down;
   float *dws_gate, *dws_up, *dws_down, *dw_shared_gate;
