@@ -21,6 +21,9 @@
 
 #include "device_common.h"
 #include "moe_internal.h"
+#include "tiny_route.h"
+
+#include <type_traits>
 
 namespace moe {
 
@@ -89,22 +92,56 @@ __device__ __forceinline__ void small_block_epilogue(const GemmParams& p,
   __syncthreads();
 }
 
-template <int KIND, int NW, int KS, int NT>
-__global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmParams p) {
+// The slot's expert, first row and rows, from the touched table, or with FR
+// (route in gate/up) from the split router's logits through tiny_route.
+template <bool FR>
+__device__ __forceinline__ void small_slot(const GemmParams& p, const RouteParams& rp,
+                                           std::conditional_t<FR, TinyRouteLds, int>& S,
+                                           int slot, int& ntouched, int4& ti) {
+  if constexpr (FR) {
+    tiny_route(rp, S, blockIdx.x == 0, true);
+    ntouched = S.ntouched;
+    ti = S.touched[min(slot, kWave - 1)];
+  } else {
+    // one load gives the slot's expert and rows (slot < E: always in the table)
+    ntouched = p.meta[1];
+    ti = *reinterpret_cast<const int4*>(p.touched + 4 * slot);
+    // both loads in flight together, ahead of the exit test
+    pin_s(ntouched); pin_s(ti.x); pin_s(ti.y); pin_s(ti.z);
+  }
+}
+
+// The word that names sorted row r's token (r in [0, P)): its perm entry
+// (the pair), or with FR the token tiny_route left in LDS; and the token it
+// names. The division waits for the load, so it stays apart from it.
+template <bool FR>
+__device__ __forceinline__ int small_row_word(const GemmParams& p,
+                                              const std::conditional_t<FR, TinyRouteLds, int>& S,
+                                              int r) {
+  if constexpr (FR) return S.row_token[min(r, kTinyT * kWave - 1)];
+  else return p.perm[r];
+}
+template <bool FR>
+__device__ __forceinline__ int small_word_token(const GemmParams& p, int w) {
+  return min(max(FR ? w : w / p.k, 0), p.a_rows - 1);
+}
+
+template <int KIND, int NW, int KS, int NT, bool FR>
+__global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmParams p, RouteParams rp) {
+  static_assert(!FR || (KIND == 0 && NW >= kTinyT), "the route runs in gate/up workgroups");
   constexpr int NB = KIND == 0 ? 2 : 1;  // weight matrices: gate and up, or down
   constexpr int NCOL = 16 * NT;          // output columns per workgroup
   __shared__ float red[NW][NB][16][NCOL];
+  __shared__ std::conditional_t<FR, TinyRouteLds, int> S;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int N = p.N, K = p.K;
   const int ncs = (N + NCOL - 1) / NCOL;
   const int slot = blockIdx.x / ncs;
   const int n0 = (blockIdx.x - slot * ncs) * NCOL;
-  // one load gives the slot's expert and rows (slot < E: always in the table)
-  int ntouched = p.meta[1];
-  int4 ti = *reinterpret_cast<const int4*>(p.touched + 4 * slot);
-  // both loads in flight together, ahead of the exit test
-  pin_s(ntouched); pin_s(ti.x); pin_s(ti.y); pin_s(ti.z);
+  int ntouched;
+  int4 ti;
+  small_slot<FR>(p, rp, S, slot, ntouched, ti);
   if (slot >= ntouched) return;
   const int e = min(max(ti.x, 0), p.E - 1);
   // rows are clamped so every row index stays in [0, P)
@@ -115,8 +152,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmParams p) {
 
   // the first row block's perm words go out before the weights, so the
   // x rows' addresses are known while the weights are still in flight
-  int first_pair = 0;
-  if constexpr (KIND == 0) first_pair = p.perm[min(max(r0 + min(lane & 15, cnt - 1), 0), p.P - 1)];
+  int first_word = 0;
+  if constexpr (KIND == 0)
+    first_word = small_row_word<FR>(p, S, min(max(r0 + min(lane & 15, cnt - 1), 0), p.P - 1));
 
   u32x4_t bq[NB][NT][KS];
 #pragma unroll
@@ -141,8 +179,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmParams p) {
     const int rr = min(rb + (lane & 15), cnt - 1);
     const uint16_t* arow;
     if constexpr (KIND == 0) {
-      const int pair = rb == 0 ? first_pair : p.perm[r0 + rr];
-      const int tok = min(max(pair / p.k, 0), p.a_rows - 1);
+      const int tok = small_word_token<FR>(p, rb == 0 ? first_word : small_row_word<FR>(p, S, r0 + rr));
       arow = A + static_cast<size_t>(tok) * K;
     } else {
       arow = A + static_cast<size_t>(r0 + rr) * K;
@@ -230,8 +267,9 @@ __device__ __forceinline__ u32x4_t x_perm8(u32x4_t w) {
 // XOR-swizzled by the row (chunk c of row r at c ^ (r mod Z)), so the 16 rows
 // one MFMA fragment reads fall in different bank groups; scale words sit as
 // rows of (K/64 | 1) words (an odd stride: conflict-free word reads).
-template <int KIND, int NW, int KS, int NT>
-__global__ __launch_bounds__(NW * 64) void gemm_small_q4_lds(GemmParams p) {
+template <int KIND, int NW, int KS, int NT, bool FR>
+__global__ __launch_bounds__(NW * 64) void gemm_small_q4_lds(GemmParams p, RouteParams rp) {
+  static_assert(!FR || (KIND == 0 && NW >= kTinyT), "the route runs in gate/up workgroups");
   constexpr int NB = KIND == 0 ? 2 : 1;
   constexpr int NCOL = 16 * NT;
   constexpr int KG = KS / 2;
@@ -251,8 +289,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_q4_lds(GemmParams p) {
   constexpr int LC_BYTES = ALIAS && RED_BYTES > CODE_ROUND ? RED_BYTES : CODE_ROUND;
   __shared__ __align__(16) uint8_t Lc[LC_BYTES];
   __shared__ __align__(16) uint32_t Ls[SC_ROUND];
-  __shared__ float red_own[ALIAS ? 1 : NW][NB][16][NCOL];
+  __shared__ __align__(16) float red_own[ALIAS ? 1 : NW][NB][16][NCOL];
   auto red = ALIAS ? reinterpret_cast<float (*)[NB][16][NCOL]>(Lc) : red_own;
+  // the route's LDS lies over red_own: its last read (the slot's first row
+  // tokens) comes before the staging barrier, the first write to red_own
+  // after it, and no other buffer has room to spare when two wide
+  // workgroups share a CU
+  using RouteLds = std::conditional_t<FR, TinyRouteLds, int>;
+  static_assert(sizeof(RouteLds) <= sizeof(red_own), "route LDS fits the partial-sum buffer");
+  RouteLds& S = *reinterpret_cast<RouteLds*>(&red_own[0][0][0][0]);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -260,16 +305,17 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_q4_lds(GemmParams p) {
   const int ncs = (N + NCOL - 1) / NCOL;
   const int slot = blockIdx.x / ncs;
   const int n0 = (blockIdx.x - slot * ncs) * NCOL;
-  int ntouched = p.meta[1];
-  int4 ti = *reinterpret_cast<const int4*>(p.touched + 4 * slot);
-  pin_s(ntouched); pin_s(ti.x); pin_s(ti.y); pin_s(ti.z);
+  int ntouched;
+  int4 ti;
+  small_slot<FR>(p, rp, S, slot, ntouched, ti);
   if (slot >= ntouched) return;
   const int e = min(max(ti.x, 0), p.E - 1);
   const int r0 = min(max(ti.y, 0), p.P);
   const int cnt = min(max(ti.z, 0), p.P - r0);
   const uint16_t* A = static_cast<const uint16_t*>(p.a);
-  int first_pair = 0;
-  if constexpr (KIND == 0) first_pair = p.perm[min(max(r0 + min(lane & 15, cnt - 1), 0), p.P - 1)];
+  int first_word = 0;
+  if constexpr (KIND == 0)
+    first_word = small_row_word<FR>(p, S, min(max(r0 + min(lane & 15, cnt - 1), 0), p.P - 1));
 
   // codes: rows R = m * NCOL + r (matrix m, column n0 + r), RB bytes each
   const int RB = K / 2;
@@ -334,8 +380,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_q4_lds(GemmParams p) {
     const int rr = min(rb + (lane & 15), cnt - 1);
     const uint16_t* arow;
     if constexpr (KIND == 0) {
-      const int pair = rb == 0 ? first_pair : p.perm[r0 + rr];
-      const int tok = min(max(pair / p.k, 0), p.a_rows - 1);
+      const int tok = small_word_token<FR>(p, rb == 0 ? first_word : small_row_word<FR>(p, S, r0 + rr));
       arow = A + static_cast<size_t>(tok) * K;
     } else {
       arow = A + static_cast<size_t>(r0 + rr) * K;
@@ -573,8 +618,9 @@ __global__ __launch_bounds__(512) void gemm_small_pers(GemmParams p) {
 // measured on MI355X it helps the down projection (one weight matrix, 32
 // columns per item) and not gate/up, whose one-shot workgroups already
 // stream its two matrices at about 5.8 TB/s.
-template <int KIND, int NT>
-static hipError_t launch_small_kind(const GemmParams& p, int slots, hipStream_t s) {
+template <int KIND, int NT, bool FR>
+static hipError_t launch_small_kind(const GemmParams& p, const RouteParams& rp, int slots,
+                                    hipStream_t s) {
   const SmallShape sh = small_shape(p.K);
   const int ncs = ceil_div(p.N, 16 * NT);
   const long long nblk = static_cast<long long>(slots) * ncs;
@@ -591,16 +637,17 @@ static hipError_t launch_small_kind(const GemmParams& p, int slots, hipStream_t 
       return hipGetLastError();
     }
   }
-  if (sh.nw == 4 && sh.ks == 4) gemm_small_kernel<KIND, 4, 4, NT><<<g, 256, 0, s>>>(p);
-  else if (sh.nw == 4 && sh.ks == 8) gemm_small_kernel<KIND, 4, 8, NT><<<g, 256, 0, s>>>(p);
-  else if (sh.nw == 4 && sh.ks == 16) gemm_small_kernel<KIND, 4, 16, NT><<<g, 256, 0, s>>>(p);
-  else if (sh.nw == 8 && sh.ks == 16) gemm_small_kernel<KIND, 8, 16, NT><<<g, 512, 0, s>>>(p);
+  if (sh.nw == 4 && sh.ks == 4) gemm_small_kernel<KIND, 4, 4, NT, FR><<<g, 256, 0, s>>>(p, rp);
+  else if (sh.nw == 4 && sh.ks == 8) gemm_small_kernel<KIND, 4, 8, NT, FR><<<g, 256, 0, s>>>(p, rp);
+  else if (sh.nw == 4 && sh.ks == 16) gemm_small_kernel<KIND, 4, 16, NT, FR><<<g, 256, 0, s>>>(p, rp);
+  else if (sh.nw == 8 && sh.ks == 16) gemm_small_kernel<KIND, 8, 16, NT, FR><<<g, 512, 0, s>>>(p, rp);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-template <int KIND, int NT>
-static hipError_t launch_small_q4(const GemmParams& p, int slots, hipStream_t s) {
+template <int KIND, int NT, bool FR>
+static hipError_t launch_small_q4(const GemmParams& p, const RouteParams& rp, int slots,
+                                  hipStream_t s) {
   // eight waves split reductions above 512 (half the registers per wave of
   // four, so twice the workgroups per CU)
   SmallShape sh;
@@ -611,20 +658,34 @@ static hipError_t launch_small_q4(const GemmParams& p, int slots, hipStream_t s)
   const long long nblk = static_cast<long long>(slots) * ceil_div(p.N, 16 * NT);
   if (nblk <= 0) return hipSuccess;
   const unsigned g = static_cast<unsigned>(nblk);
-  if (sh.nw == 4) gemm_small_q4_lds<KIND, 4, 4, NT><<<g, 256, 0, s>>>(p);
-  else if (sh.ks == 4) gemm_small_q4_lds<KIND, 8, 4, NT><<<g, 512, 0, s>>>(p);
+  if (sh.nw == 4) gemm_small_q4_lds<KIND, 4, 4, NT, FR><<<g, 256, 0, s>>>(p, rp);
+  else if (sh.ks == 4) gemm_small_q4_lds<KIND, 8, 4, NT, FR><<<g, 512, 0, s>>>(p, rp);
   else if constexpr (NT <= 2) {  // the widest shapes' codes do not fit LDS above K = 1024
-    if (sh.ks == 8) gemm_small_q4_lds<KIND, 8, 8, NT><<<g, 512, 0, s>>>(p);
-    else gemm_small_q4_lds<KIND, 8, 16, NT><<<g, 512, 0, s>>>(p);
+    if (sh.ks == 8) gemm_small_q4_lds<KIND, 8, 8, NT, FR><<<g, 512, 0, s>>>(p, rp);
+    else gemm_small_q4_lds<KIND, 8, 16, NT, FR><<<g, 512, 0, s>>>(p, rp);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_small(const GemmParams& p, hipStream_t s) {
+template <int NT>
+static hipError_t launch_q4_gate_up(const GemmParams& p, const RouteParams* route, int slots,
+                                    hipStream_t s) {
+  if (route != nullptr) return launch_small_q4<0, NT, true>(p, *route, slots, s);
+  return launch_small_q4<0, NT, false>(p, RouteParams{}, slots, s);
+}
+
+hipError_t launch_gemm_small(const GemmParams& p, hipStream_t s, const RouteParams* route) {
   if (p.dtype != MOE_BF16 || p.touched == nullptr || p.shared_T != 0 || p.N % 8 != 0 ||
       p.K % 8 != 0 || small_shape(p.K).nw == 0)
+    return hipErrorInvalidValue;
+  // the route inside gate/up: at most kTinyT tokens and kWave experts, from
+  // the split router's logits, with the dispatch tables to store
+  if (route != nullptr &&
+      (p.kind != 0 || route->T < 1 || route->T > kTinyT || route->E > kWave ||
+       route->T != p.a_rows || route->E != p.E || route->T * route->k != p.P ||
+       route->part == nullptr || route->counts == nullptr || route->touched == nullptr))
     return hipErrorInvalidValue;
   // at most min(P, E) experts hold rows
   const int slots = p.P < p.E ? p.P : p.E;
@@ -635,17 +696,20 @@ hipError_t launch_gemm_small(const GemmParams& p, hipStream_t s) {
     // workgroups of 16 columns per CU (two of them then fit a CU), else 16
     if (p.kind == 0) {
       if (static_cast<long long>(slots) * ceil_div(p.N, 16) > 4LL * device_cus())
-        return launch_small_q4<0, 2>(p, slots, s);
-      return launch_small_q4<0, 1>(p, slots, s);
+        return launch_q4_gate_up<2>(p, route, slots, s);
+      return launch_q4_gate_up<1>(p, route, slots, s);
     }
     // down: 128 columns per workgroup on the same condition, for reductions
     // up to 1024 (32 columns otherwise)
     if (p.K <= 1024 && static_cast<long long>(slots) * ceil_div(p.N, 32) > 4LL * device_cus())
-      return launch_small_q4<1, 8>(p, slots, s);
-    return launch_small_q4<1, 2>(p, slots, s);
+      return launch_small_q4<1, 8, false>(p, RouteParams{}, slots, s);
+    return launch_small_q4<1, 2, false>(p, RouteParams{}, slots, s);
   }
-  if (p.kind == 0) return launch_small_kind<0, 1>(p, slots, s);
-  return launch_small_kind<1, 2>(p, slots, s);
+  if (p.kind == 0) {
+    if (route != nullptr) return launch_small_kind<0, 1, true>(p, *route, slots, s);
+    return launch_small_kind<0, 1, false>(p, RouteParams{}, slots, s);
+  }
+  return launch_small_kind<1, 2, false>(p, RouteParams{}, slots, s);
 }
 
 }  // namespace moe

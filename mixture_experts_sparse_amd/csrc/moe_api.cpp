@@ -492,6 +492,7 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
   const bool gated = c.shared_h > 0 && c.shared_gate;
   float* sg = gated ? at<float>(ws, L.sgate) : nullptr;
 
+  const bool fused_route = NB == 1 && route_in_gate_up(c);
   MOE_HIP(mark(0));
   RouteParams rp{};
   rp.x = x;
@@ -517,7 +518,10 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
     if (use_small_gemm(c)) rp.tile_e = nullptr;
     rp.part = at<float>(ws, L.part);
     rp.ncp = route_part_cols(c.E, gated);
-    MOE_HIP(launch_route_split(rp, c.dtype, s));
+    // at most four tokens: the selection and the dispatch tables are made
+    // inside the gate/up launch from the logits of this one
+    if (fused_route) MOE_HIP(launch_route_part(rp, c.dtype, s));
+    else MOE_HIP(launch_route_split(rp, c.dtype, s));
   } else {
     MOE_HIP(launch_route(rp, c.dtype, s));
   }
@@ -557,7 +561,7 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
   g.a = x; g.perm = perm; g.K = c.d; g.b0 = w->w_gate; g.b1 = w->w_up; g.N = c.h; g.out = act;
   if (q4) { g.quant = MOE_QUANT_Q4_G64; g.b0_sb = w->w_gate_sb; g.b1_sb = w->w_up_sb; }
   if (small) {
-    MOE_HIP(launch_gemm_small(g, s));
+    MOE_HIP(launch_gemm_small(g, s, fused_route ? &rp : nullptr));
     if (c.shared_h > 0) MOE_HIP(launch_gemm(shared_only(0), s));
   } else {
     if (c.shared_h > 0) {
@@ -660,6 +664,7 @@ moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w
   float* sg = gated ? at<float>(ws, L.sgate) : nullptr;
   float* logits = at<float>(ws, B.logits);
 
+  const bool fused_route = NB == 1 && route_in_gate_up(c);
   MOE_HIP(mark(0));
   RouteParams rp{};
   rp.x = x;

@@ -275,8 +275,27 @@ hipError_t launch_tiles(const TilesParams& p, hipStream_t s);
 int device_cus();
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
-hipError_t launch_gemm_small(const GemmParams& p, hipStream_t s);
+// route != null (gate/up only, T <= 4 tokens, E <= 64): every workgroup
+// derives its expert and rows from route->part (the split router's logits)
+// instead of the touched table, and workgroup 0 stores the selection and the
+// dispatch tables through *route, as the split router's finish would.
+hipError_t launch_gemm_small(const GemmParams& p, hipStream_t s,
+                             const RouteParams* route = nullptr);
+// The split router's logits kernel alone, then with its finish.
+hipError_t launch_route_part(const RouteParams& p, int dtype, hipStream_t s);
 hipError_t launch_route_split(const RouteParams& p, int dtype, hipStream_t s);
+// The split router's finish runs inside the small-batch gate/up GEMM for
+// batches of at most MOE_FUSE_ROUTE_MAX_T tokens. Every gate/up workgroup
+// then runs the selection before its weight loads can go out, which pays
+// only while the grid is one round of resident workgroups (measured on
+// MI355X at d = 2048, h = 1024, 64 experts, top-8: 0.9 us per layer gained
+// at one token, 1.5 lost at two, 8 at four; the 4-bit layer likewise).
+#ifndef MOE_FUSE_ROUTE_MAX_T
+#define MOE_FUSE_ROUTE_MAX_T 1
+#endif
+inline bool route_in_gate_up(const moe_config& c) {
+  return use_small_gemm(c) && c.T <= MOE_FUSE_ROUTE_MAX_T && c.E <= 64;
+}
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 hipError_t launch_scale_rows(const ScaleRowsParams& p, hipStream_t s);
 hipError_t launch_rowdot_sigmoid(const RowDotSigmoidParams& p, hipStream_t s);

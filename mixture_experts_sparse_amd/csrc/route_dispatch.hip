@@ -16,6 +16,7 @@
 
 #include "device_common.h"
 #include "moe_internal.h"
+#include "tiny_route.h"
 
 namespace moe {
 
@@ -895,138 +896,15 @@ __global__ __launch_bounds__(RTHR) void route_finish_kernel(RouteParams p) {
 
 // ---------------------------------------------------------------------------
 // Finish of the split router for the smallest batches (T <= 4 tokens, at most
-// 64 experts): wave t takes token t, lane e expert e. The lane's selection
-// score becomes an order-preserving 32-bit key in LDS, and its rank is the
-// number of keys that beat it (a larger score, or an equal one at a lower
-// index: the order of the top-k), counted over broadcast LDS reads; the
-// gates follow from wave reductions. After one barrier wave 0 builds the
-// dispatch tables with lane e owning expert e: its pairs are the tokens that
-// chose it, in token order (which is pair order), and counts, offsets, the
-// tile prefix and the touched table come from wave prefix sums. The outputs
+// 64 experts), one workgroup: wave t takes token t, lane e expert e. A lane's
+// rank is the number of selection keys that beat its own, counted over
+// broadcast LDS reads; the gates follow from wave reductions, and wave 0
+// builds the dispatch tables with wave prefix sums (tiny_route). The outputs
 // are those of route_finish_kernel.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int wave_excl_scan(int v, int& total) {
-  const int lane = threadIdx.x & 63;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int y = __shfl_up(x, off, kWave);
-    if (lane >= off) x += y;
-  }
-  total = __shfl(x, kWave - 1, kWave);
-  return x - v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
-}
-
-constexpr int kTinyT = 4;  // most tokens of the one-launch finish (one wave each)
-
 __global__ __launch_bounds__(kTinyT * kWave) void route_tiny_kernel(RouteParams p) {
-  __shared__ __align__(16) uint32_t keys[kTinyT][kWave];
-  __shared__ int8_t slot_of[kTinyT][kWave];  // slot of (token, expert), -1: not chosen
-  const int e = threadIdx.x & 63;  // expert of this lane
-  const int t = threadIdx.x >> 6;  // token of this wave
-  const int E = p.E, k = p.k, T = p.T;
-  const bool valid = e < E;
-  const bool live = t < T;  // uniform across the wave
-  const bool sig = p.mode == MOE_SIGMOID;
-  // every load before the first use, clamped: the bias, this (token,
-  // expert) logit and, on lane 0, the token's shared-gate logit
-  float b = 0.f;
-  if (p.bias != nullptr) b = p.bias[min(e, E - 1)];
-  const size_t row = static_cast<size_t>(min(t, T - 1)) * p.ncp;
-  float raw = p.part[row + min(e, E - 1)];
-  float sgl = 0.f;
-  if (p.sgate != nullptr) sgl = p.part[row + E];
-  pin(b);
-  pin(raw);
-  pin(sgl);
-  if (!valid) b = 0.f;
-  // logits (in the softmax modes with the bias) and the selection score
-  const float v = sig ? raw : raw + b;
-  const float score = sig ? sigmoid_f32(raw) + b : v;
-  const uint32_t key = valid ? order_key32(score + 0.0f) : 0u;  // -0 -> +0
-  keys[t][e] = key;
-  __syncthreads();
-  int rank = 0;
-  {
-    int n4[4] = {0, 0, 0, 0};
-    int q = 0;
-    for (; q + 4 <= E; q += 4) {
-      const u32x4_t kq = *reinterpret_cast<const u32x4_t*>(&keys[t][q]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) n4[u] += (kq[u] > key || (kq[u] == key && q + u < e)) ? 1 : 0;
-    }
-    for (; q < E; ++q) n4[0] += (keys[t][q] > key || (keys[t][q] == key && q < e)) ? 1 : 0;
-    rank = (n4[0] + n4[1]) + (n4[2] + n4[3]);
-  }
-  const bool sel = live && valid && rank < k;
-  // gate numerators: exp(L - max) in the softmax modes (the largest logit
-  // is always chosen), the raw affinity in the sigmoid mode
-  float ej;
-  if (sig) {
-    ej = valid ? sigmoid_f32(raw) : 0.f;
-  } else {
-    const float m = wave_max(valid ? v : -INFINITY);
-    ej = valid ? expf(v - m) : 0.f;
-  }
-  float denom = wave_sum(sel ? ej : 0.f);
-  if (p.mode == MOE_SOFTMAX_ALL && !p.renorm) denom = wave_sum(ej);
-  if (sig && !p.renorm) denom = 1.0f;
-  if (live) {
-    if (p.logits != nullptr && valid) p.logits[static_cast<size_t>(t) * E + e] = v;
-    if (p.sgate != nullptr && e == 0) p.sgate[t] = sigmoid_f32(sgl);
-    if (sel) {
-      p.ids[static_cast<size_t>(t) * k + rank] = e;
-      p.gates[static_cast<size_t>(t) * k + rank] = ej * (1.0f / denom);
-    }
-  }
-  if (p.counts == nullptr) return;  // uniform: route only
-  slot_of[t][e] = static_cast<int8_t>(sel ? rank : -1);
-  __syncthreads();
-  if (t != 0) return;
-  // dispatch on wave 0: this lane's pairs, in token order
-  int cnt = 0;
-#pragma unroll
-  for (int u = 0; u < kTinyT; ++u) cnt += slot_of[u][e] >= 0 ? 1 : 0;
-  int total = 0;
-  const int off = wave_excl_scan(cnt, total);
-  int ntl = 0;
-  const int tl = (cnt + p.tile_m - 1) / p.tile_m;
-  const int toff = wave_excl_scan(tl, ntl);
-  int ntouched = 0;
-  const int tidx = wave_excl_scan(cnt > 0 ? 1 : 0, ntouched);
-  if (valid) {
-    p.counts[e] = cnt;
-    p.offsets[e] = off;
-    p.exp_tile0[e] = toff;
-    if (cnt > 0 && p.touched != nullptr)
-      *reinterpret_cast<int4*>(p.touched + 4 * tidx) = make_int4(e, off, cnt, 0);
-    if (p.tile_e != nullptr)
-      for (int j = 0; j < tl; ++j)
-        if (toff + j < p.max_tiles) p.tile_e[toff + j] = e;
-    int r = off;
-#pragma unroll
-    for (int u = 0; u < kTinyT; ++u) {
-      const int j = slot_of[u][e];
-      if (j >= 0) {
-        const int pair = u * k + j;
-        p.perm[r] = pair;
-        p.inv[pair] = r;
-        ++r;
-      }
-    }
-  }
-  if (e == 0) {
-    p.offsets[E] = total;
-    p.exp_tile0[E] = ntl;
-    p.meta[0] = min(ntl, p.max_tiles);
-    p.meta[1] = ntouched;
-  }
+  __shared__ TinyRouteLds S;
+  tiny_route(p, S, true, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -1216,13 +1094,20 @@ static void launch_finish_nch(const RouteParams& p, hipStream_t s) {
   route_finish_kernel<NCH><<<1, RTHR, 0, s>>>(p);
 }
 
-hipError_t launch_route_split(const RouteParams& p, int dtype, hipStream_t s) {
+hipError_t launch_route_part(const RouteParams& p, int dtype, hipStream_t s) {
   const int cols = p.E + (p.w_sgate != nullptr ? 1 : 0);
   if (p.T < 1 || p.T > RTM || p.part == nullptr || p.ncp != ceil_div(cols, 16) * 16)
     return hipErrorInvalidValue;
   const dim3 grid(p.ncp / 16, ceil_div(p.T, 16));
   if (dtype == MOE_BF16) route_part_kernel<true><<<grid, RTHR, 0, s>>>(p);
   else route_part_kernel<false><<<grid, RTHR, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_split(const RouteParams& p, int dtype, hipStream_t s) {
+  const hipError_t err = launch_route_part(p, dtype, s);
+  if (err != hipSuccess) return err;
+  const int cols = p.E + (p.w_sgate != nullptr ? 1 : 0);
   if (p.T <= kTinyT && p.E <= kWave) {
     route_tiny_kernel<<<1, kTinyT * kWave, 0, s>>>(p);
     return hipGetLastError();

@@ -198,6 +198,17 @@ SMALL_Q4 = {
     # workgroups of the wide grid find their slot empty
     "q4_wide_few_experts": small_spec("decode_q4", T=64, d=576, E=64, h=320, k=1,
                                       router_bias="zipf"),
+    # at most four tokens: the gate/up launch makes the selection and the
+    # dispatch tables itself (16- and 32-column shapes, a gated shared
+    # expert beside it, one expert)
+    "q4_tiny_T1": small_spec("decode_q4", T=1, d=256, E=32, h=128, k=4),
+    "q4_tiny_T3_sel": small_spec("decode_q4", T=3, d=512, E=64, h=192, k=8,
+                                 mode=SOFTMAX_SELECTED),
+    "q4_tiny_T4_wide": small_spec("decode_q4", T=4, d=512, E=64, h=640, k=8,
+                                  router_bias="zipf", renormalize=True),
+    "q4_tiny_T2_shared": small_spec("decode_q4", T=2, d=256, E=16, h=64, k=2, shared_h=128,
+                                    shared_gate=True),
+    "q4_tiny_T1_E1": small_spec("decode_q4", T=1, d=128, E=1, h=64, k=1),
 }
 
 
@@ -205,7 +216,14 @@ SMALL_Q4 = {
 def test_layer_q4_small(name):
     spec = SMALL_Q4[name]
     say(f"[gpu] layer_forward q4 {name}: T={spec.T} d={spec.d} E={spec.E} h={spec.h} k={spec.k}")
-    full_parity(generate(spec))
+    if spec.T <= 4:
+        cfg = B.config_from_spec(spec)
+        ws = B.alloc_workspace(cfg)
+        g, _, _ = full_parity(generate(spec), ws=ws)
+        _check_tables(cfg, ws, g["ids"], spec.E, name)
+        say("    dispatch tables bit-exact")
+    else:
+        full_parity(generate(spec))
 
 
 FULL = ["tiny_fp32", "gemma_upcycled", "skewed_prefill", "shared_routed",
@@ -319,6 +337,17 @@ TINY_ROUTE = {
     "T2_k_eq_E": small_spec("decode", T=2, d=64, E=8, h=32, k=8),
     "T1_E1": small_spec("decode", T=1, d=64, E=1, h=32, k=1),
     "T4_fp32": small_spec("tiny_fp32", T=4),
+    # one token: the selection and the tables come from the gate/up launch,
+    # in every gate mode, with a logit bias and a gated shared expert
+    "T1_softmax_all_renorm_bias": small_spec("skewed_prefill", T=1, d=264, E=60, h=64, k=8),
+    "T1_softmax_selected": MoESpec(name="t1_sel", T=1, d=200, E=37, h=40, k=5,
+                                   mode=SOFTMAX_SELECTED),
+    "T1_shared_gate": small_spec("shared_routed", T=1, d=264, E=60, h=64, k=4, shared_h=96),
+    "T1_sigmoid_renorm": small_spec("small_moe_sigmoid", T=1, d=256, E=64, h=64, k=8,
+                                    shared_h=64),
+    "T1_sigmoid_raw_k20": small_spec("small_moe_sigmoid", T=1, d=128, E=64, h=32, k=20,
+                                     shared_h=0, renormalize=False),
+    "T1_d4096_eight_waves": small_spec("decode", T=1, d=4096, E=16, h=128, k=4),
 }
 
 
