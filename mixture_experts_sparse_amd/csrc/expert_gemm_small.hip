@@ -613,6 +613,100 @@ __global__ __launch_bounds__(512) void gemm_small_pers(GemmParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// One token (T = 1): the down projection and the combine in one launch.
+// With one token each chosen expert holds one row, sorted row w being the
+// w-th touched expert. A workgroup owns kDcCols output columns of every
+// row: wave w takes row w, lane l column n0 + l / 8, and load i of a lane
+// reads K values 64 i + 8 (l % 8) .. + 7 of its column's weight row and of
+// the act row -- one whole 128-byte line of each of the 8 columns per load
+// instruction. The lane's dot product is summed over the 8 lanes of its
+// column by DPP moves and rounded to bf16, the value the down kernel would
+// store as y; after a barrier 8 threads add the rows in slot order with
+// their gates, then the gated shared row, and round once, as the combine
+// kernel does ("Tutorial 11: Mixture of Experts (MoE)", section 3, steps
+// 2 and 3).
+// ---------------------------------------------------------------------------
+constexpr int kDcCols = 8;  // output columns per workgroup (8 lanes each)
+__global__ __launch_bounds__(kDownCombineRows * 64) void down_combine_t1_kernel(GemmParams p,
+                                                                              CombineParams c) {
+  constexpr int NL = kDownCombineMaxK / 64;  // loads per lane at the longest reduction
+  __shared__ float yv[kDownCombineRows][kDcCols];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int n0 = blockIdx.x * kDcCols;
+  const int K = p.K, N = p.N, P = p.P;
+  const int nk = K / 64;  // K is a multiple of 64, at most kDownCombineMaxK
+  // the combine's inputs do not depend on the products: they go out first
+  int rj[kDownCombineRows];
+  float gj[kDownCombineRows];
+  float sh = 0.f, sc = 0.f;
+  if (tid < kDcCols) {
+#pragma unroll
+    for (int j = 0; j < kDownCombineRows; ++j) {
+      rj[j] = c.inv[min(j, c.k - 1)];
+      gj[j] = c.gates[min(j, c.k - 1)];
+    }
+    if (c.shared != nullptr) {
+      sh = bf16_to_f32(static_cast<const uint16_t*>(c.shared)[n0 + tid]);
+      sc = c.shared_scale != nullptr ? c.shared_scale[0] : 1.0f;
+    }
+  }
+  // this wave's row: its expert from the touched table
+  const int r = min(__builtin_amdgcn_readfirstlane(wave), P - 1);  // wave-uniform
+  int4 ti = *reinterpret_cast<const int4*>(p.touched + 4 * r);
+  pin_s(ti.x); pin_s(ti.y);
+  const int e = min(max(ti.x, 0), p.E - 1);
+  const int row = min(max(ti.y, 0), P - 1);
+  const int sub = (lane & 7) * 8;
+  const uint16_t* wrow = static_cast<const uint16_t*>(p.b0) +
+                         (static_cast<size_t>(e) * N + min(n0 + (lane >> 3), N - 1)) * K + sub;
+  const uint16_t* arow = static_cast<const uint16_t*>(p.a) + static_cast<size_t>(row) * K + sub;
+  u32x4_t wq[NL], aq[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    // loads past K reread the last line (their products are skipped)
+    const int ki = min(i, nk - 1) * 64;
+    wq[i] = *reinterpret_cast<const u32x4_t*>(wrow + ki);
+    aq[i] = *reinterpret_cast<const u32x4_t*>(arow + ki);
+  }
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    if (i < nk) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s0 = fmaf(__uint_as_float(aq[i][q] << 16), __uint_as_float(wq[i][q] << 16), s0);
+        s1 = fmaf(__uint_as_float(aq[i][q] & 0xFFFF0000u), __uint_as_float(wq[i][q] & 0xFFFF0000u), s1);
+      }
+    }
+  }
+  float v = s0 + s1;
+  // the 8 lanes of a column: pairs, quads, then the two quads of the 8
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  if ((lane & 7) == 0) yv[wave][lane >> 3] = wave < P ? bf16_to_f32(f32_to_bf16(v)) : 0.f;
+  __syncthreads();
+  if (tid < kDcCols) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < kDownCombineRows; ++j)
+      if (j < c.k) acc = fmaf(gj[j], yv[min(max(rj[j], 0), P - 1)][tid], acc);
+    if (c.shared != nullptr) acc = fmaf(sc, sh, acc);
+    static_cast<uint16_t*>(c.out)[n0 + tid] = f32_to_bf16(acc);
+  }
+}
+
+hipError_t launch_down_combine_t1(const GemmParams& p, const CombineParams& c, hipStream_t s) {
+  if (p.dtype != MOE_BF16 || p.quant != MOE_QUANT_NONE || p.kind != 1 || c.T != 1 ||
+      c.k != p.P || p.P < 1 || p.P > kDownCombineRows || p.K % 64 != 0 ||
+      p.K > kDownCombineMaxK || p.N != c.d || p.N % kDcCols != 0 || p.touched == nullptr)
+    return hipErrorInvalidValue;
+  down_combine_t1_kernel<<<p.N / kDcCols, kDownCombineRows * 64, 0, s>>>(p, c);
+  return hipGetLastError();
+}
+
 // One launch of the small-batch GEMM. The persistent form keeps the weight
 // stream running across items, which pays when every CU has several items;
 // measured on MI355X it helps the down projection (one weight matrix, 32

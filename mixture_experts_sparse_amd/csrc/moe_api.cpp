@@ -574,7 +574,14 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
   GemmParams g2 = gemm_base(c, ws, offsets, 1);
   g2.a = act; g2.K = c.h; g2.b0 = w->w_down; g2.N = c.d; g2.out = y;
   if (q4) { g2.quant = MOE_QUANT_Q4_G64; g2.b0_sb = w->w_down_sb; }
-  if (small) {
+  CombineParams cp{y, inv, gates_p, c.shared_h > 0 ? ys : nullptr, sg, out, c.T, c.d, c.top_k,
+                    c.dtype, c.T * c.top_k};
+  const bool fused_combine = down_combine_one_token(c);
+  if (fused_combine) {
+    // the shared row first: the one-token down launch adds it
+    if (c.shared_h > 0) MOE_HIP(launch_gemm(shared_only(1), s));
+    MOE_HIP(launch_down_combine_t1(g2, cp, s));
+  } else if (small) {
     MOE_HIP(launch_gemm_small(g2, s));
     if (c.shared_h > 0) MOE_HIP(launch_gemm(shared_only(1), s));
   } else {
@@ -585,9 +592,7 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
     MOE_HIP(launch_gemm(g2, s));
   }
   MOE_HIP(mark(4));
-  CombineParams cp{y, inv, gates_p, c.shared_h > 0 ? ys : nullptr, sg, out, c.T, c.d, c.top_k,
-                    c.dtype, c.T * c.top_k};
-  MOE_HIP(launch_combine(cp, s));
+  if (!fused_combine) MOE_HIP(launch_combine(cp, s));
   MOE_HIP(mark(5));
   return MOE_OK;
 }

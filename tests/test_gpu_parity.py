@@ -348,6 +348,9 @@ TINY_ROUTE = {
     "T1_sigmoid_raw_k20": small_spec("small_moe_sigmoid", T=1, d=128, E=64, h=32, k=20,
                                      shared_h=0, renormalize=False),
     "T1_d4096_eight_waves": small_spec("decode", T=1, d=4096, E=16, h=128, k=4),
+    # one token, down and combine in one launch: three rows, a reduction of
+    # three 64-wide loads, a width of 40 eight-column slices
+    "T1_k3_h192": small_spec("decode", T=1, d=320, E=16, h=192, k=3),
 }
 
 
