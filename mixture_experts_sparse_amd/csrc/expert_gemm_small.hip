@@ -628,15 +628,94 @@ __global__ __launch_bounds__(512) void gemm_small_pers(GemmParams p) {
 // 2 and 3).
 // ---------------------------------------------------------------------------
 constexpr int kDcCols = 8;  // output columns per workgroup (8 lanes each)
+
+// A lane's share of one column's product, bf16 weights: load i holds K
+// values 64 i + sub .. + 7 of the weight row and of the act row.
+template <int NL>
+__device__ __forceinline__ float dc_dot_bf16(const GemmParams& p, int e, int col, int row, int sub) {
+  const int K = p.K, nk = K / 64;
+  const uint16_t* wrow = static_cast<const uint16_t*>(p.b0) +
+                         (static_cast<size_t>(e) * p.N + col) * K + sub;
+  const uint16_t* arow = static_cast<const uint16_t*>(p.a) + static_cast<size_t>(row) * K + sub;
+  u32x4_t wq[NL], aq[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    // loads past K reread the last line (their products are skipped)
+    const int ki = min(i, nk - 1) * 64;
+    wq[i] = *reinterpret_cast<const u32x4_t*>(wrow + ki);
+    aq[i] = *reinterpret_cast<const u32x4_t*>(arow + ki);
+  }
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    if (i < nk) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s0 = fmaf(__uint_as_float(aq[i][q] << 16), __uint_as_float(wq[i][q] << 16), s0);
+        s1 = fmaf(__uint_as_float(aq[i][q] & 0xFFFF0000u), __uint_as_float(wq[i][q] & 0xFFFF0000u), s1);
+      }
+    }
+  }
+  return s0 + s1;
+}
+
+// The same for 4-bit weights (codes [E, N, K/2], scale|bias words
+// [E, N, K/64], w = s q + b): load i holds the 16 code bytes of chunk
+// ch = sub8 + 8 i (K values 32 ch .. + 31, one scale group), the group's
+// word and the 32 act values; per chunk s * sum(a q) + b * sum(a).
+template <int NQ>
+__device__ __forceinline__ float dc_dot_q4(const GemmParams& p, int e, int col, int row, int sub8) {
+  const int K = p.K, nch = K / 32, NG = K / 64;
+  const uint8_t* crow = static_cast<const uint8_t*>(p.b0) +
+                        (static_cast<size_t>(e) * p.N + col) * (K / 2);
+  const uint32_t* srow = p.b0_sb + (static_cast<size_t>(e) * p.N + col) * NG;
+  const uint16_t* arow = static_cast<const uint16_t*>(p.a) + static_cast<size_t>(row) * K;
+  u32x4_t cq[NQ], aq[NQ][4];
+  uint32_t sb[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    // chunks past K reread the last (their products are skipped)
+    const int ch = min(sub8 + 8 * i, nch - 1);
+    cq[i] = *reinterpret_cast<const u32x4_t*>(crow + ch * 16);
+    sb[i] = srow[ch >> 1];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) aq[i][w] = *reinterpret_cast<const u32x4_t*>(arow + ch * 32 + w * 8);
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    if (sub8 + 8 * i < nch) {
+      float saq = 0.f, sa = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // code word w: byte m holds K values 8 w + 2 m (low nibble) and + 1
+        // (high nibble), act dword m the same two values (low, high half)
+        const uint32_t lo = cq[i][w] & 0x0F0F0F0Fu, hi = (cq[i][w] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float a0 = __uint_as_float(aq[i][w][m] << 16);
+          const float a1 = __uint_as_float(aq[i][w][m] & 0xFFFF0000u);
+          saq = fmaf(a0, static_cast<float>((lo >> (8 * m)) & 0xFFu), saq);
+          saq = fmaf(a1, static_cast<float>((hi >> (8 * m)) & 0xFFu), saq);
+          sa += a0 + a1;
+        }
+      }
+      const float sc = bf16_to_f32(static_cast<uint16_t>(sb[i] & 0xFFFFu));
+      const float bi = bf16_to_f32(static_cast<uint16_t>(sb[i] >> 16));
+      acc = fmaf(sc, saq, fmaf(bi, sa, acc));
+    }
+  }
+  return acc;
+}
+
+template <bool Q4>
 __global__ __launch_bounds__(kDownCombineRows * 64) void down_combine_t1_kernel(GemmParams p,
                                                                               CombineParams c) {
-  constexpr int NL = kDownCombineMaxK / 64;  // loads per lane at the longest reduction
   __shared__ float yv[kDownCombineRows][kDcCols];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tid = threadIdx.x;
   const int n0 = blockIdx.x * kDcCols;
-  const int K = p.K, N = p.N, P = p.P;
-  const int nk = K / 64;  // K is a multiple of 64, at most kDownCombineMaxK
+  const int P = p.P;
   // the combine's inputs do not depend on the products: they go out first
   int rj[kDownCombineRows];
   float gj[kDownCombineRows];
@@ -658,30 +737,10 @@ __global__ __launch_bounds__(kDownCombineRows * 64) void down_combine_t1_kernel(
   pin_s(ti.x); pin_s(ti.y);
   const int e = min(max(ti.x, 0), p.E - 1);
   const int row = min(max(ti.y, 0), P - 1);
-  const int sub = (lane & 7) * 8;
-  const uint16_t* wrow = static_cast<const uint16_t*>(p.b0) +
-                         (static_cast<size_t>(e) * N + min(n0 + (lane >> 3), N - 1)) * K + sub;
-  const uint16_t* arow = static_cast<const uint16_t*>(p.a) + static_cast<size_t>(row) * K + sub;
-  u32x4_t wq[NL], aq[NL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    // loads past K reread the last line (their products are skipped)
-    const int ki = min(i, nk - 1) * 64;
-    wq[i] = *reinterpret_cast<const u32x4_t*>(wrow + ki);
-    aq[i] = *reinterpret_cast<const u32x4_t*>(arow + ki);
-  }
-  float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    if (i < nk) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        s0 = fmaf(__uint_as_float(aq[i][q] << 16), __uint_as_float(wq[i][q] << 16), s0);
-        s1 = fmaf(__uint_as_float(aq[i][q] & 0xFFFF0000u), __uint_as_float(wq[i][q] & 0xFFFF0000u), s1);
-      }
-    }
-  }
-  float v = s0 + s1;
+  const int col = min(n0 + (lane >> 3), p.N - 1);
+  float v;
+  if constexpr (Q4) v = dc_dot_q4<kDownCombineMaxK / 256>(p, e, col, row, lane & 7);
+  else v = dc_dot_bf16<kDownCombineMaxK / 64>(p, e, col, row, (lane & 7) * 8);
   // the 8 lanes of a column: pairs, quads, then the two quads of the 8
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
@@ -699,11 +758,15 @@ __global__ __launch_bounds__(kDownCombineRows * 64) void down_combine_t1_kernel(
 }
 
 hipError_t launch_down_combine_t1(const GemmParams& p, const CombineParams& c, hipStream_t s) {
-  if (p.dtype != MOE_BF16 || p.quant != MOE_QUANT_NONE || p.kind != 1 || c.T != 1 ||
-      c.k != p.P || p.P < 1 || p.P > kDownCombineRows || p.K % 64 != 0 ||
-      p.K > kDownCombineMaxK || p.N != c.d || p.N % kDcCols != 0 || p.touched == nullptr)
+  const bool q4 = p.quant == MOE_QUANT_Q4_G64;
+  if (p.dtype != MOE_BF16 || (!q4 && p.quant != MOE_QUANT_NONE) || (q4 && p.b0_sb == nullptr) ||
+      p.kind != 1 || c.T != 1 || c.k != p.P || p.P < 1 || p.P > kDownCombineRows ||
+      p.K % 64 != 0 || p.K > kDownCombineMaxK || p.N != c.d || p.N % kDcCols != 0 ||
+      p.touched == nullptr)
     return hipErrorInvalidValue;
-  down_combine_t1_kernel<<<p.N / kDcCols, kDownCombineRows * 64, 0, s>>>(p, c);
+  const unsigned g = static_cast<unsigned>(p.N / kDcCols);
+  if (q4) down_combine_t1_kernel<true><<<g, kDownCombineRows * 64, 0, s>>>(p, c);
+  else down_combine_t1_kernel<false><<<g, kDownCombineRows * 64, 0, s>>>(p, c);
   return hipGetLastError();
 }
 

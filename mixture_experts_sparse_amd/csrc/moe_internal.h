@@ -283,13 +283,13 @@ hipError_t launch_gemm_small(const GemmParams& p, hipStream_t s,
                              const RouteParams* route = nullptr);
 // One token: the routed down projection and the combine in one launch
 // (y is never stored). k <= kDownCombineRows rows, h a multiple of 64 up to
-// kDownCombineMaxK, bf16 activation-dtype experts; the shared expert's row,
-// if any, must already be in c.shared.
+// kDownCombineMaxK, bf16 layers with activation-dtype or 4-bit experts; the
+// shared expert's row, if any, must already be in c.shared.
 constexpr int kDownCombineRows = 8;
 constexpr int kDownCombineMaxK = 1024;
 inline bool down_combine_one_token(const moe_config& c) {
-  return c.T == 1 && use_small_gemm(c) && c.expert_quant == MOE_QUANT_NONE &&
-         c.top_k <= kDownCombineRows && c.h % 64 == 0 && c.h <= kDownCombineMaxK;
+  return c.T == 1 && use_small_gemm(c) && c.top_k <= kDownCombineRows && c.h % 64 == 0 &&
+         c.h <= kDownCombineMaxK;
 }
 hipError_t launch_down_combine_t1(const GemmParams& p, const CombineParams& c, hipStream_t s);
 // The split router's logits kernel alone, then with its finish.

@@ -209,6 +209,9 @@ SMALL_Q4 = {
     "q4_tiny_T2_shared": small_spec("decode_q4", T=2, d=256, E=16, h=64, k=2, shared_h=128,
                                     shared_gate=True),
     "q4_tiny_T1_E1": small_spec("decode_q4", T=1, d=128, E=1, h=64, k=1),
+    # one token, down and combine in one launch: six 32-code chunks per
+    # column (lanes 6 and 7 of each column idle), three rows
+    "q4_tiny_T1_h192": small_spec("decode_q4", T=1, d=320, E=16, h=192, k=3),
 }
 
 
