@@ -74,13 +74,13 @@ STAGE_KERNEL = {"route": ("route_kernel", "route_part_kernel"),
                 "gate_up": ("gemm_bf16_pers<0", "gemm_bf16_kernel<0", "gemm_small_kernel<0",
                             "gemm_small_q4_lds<0"),
                 "down": ("gemm_bf16_pers<1", "gemm_bf16_kernel<1", "gemm_small_kernel<1",
-                         "gemm_small_pers<1", "gemm_small_q4_lds<1"),
+                         "gemm_small_pers<1", "gemm_small_q4_lds<1", "down_combine_t1"),
                 "combine": ("combine_",)}
 
 
 FWD_SOURCES = ("expert_gemm.hip", "expert_gemm_small.hip", "route_dispatch.hip", "combine.hip",
-               "moe_api.cpp")
-BWD_SOURCES = ("backward.hip", "route_dispatch.hip")
+               "moe_api.cpp", "tiny_route.h")
+BWD_SOURCES = ("backward.hip", "route_dispatch.hip", "tiny_route.h")
 # kernel-name prefixes of each backward stage's product
 BWD_STAGE_KERNEL = {"d_hidden": ("bwd_gemm<1>",), "z": ("bwd_gemm<0>",),
                     "dw_down": ("bwd_gemm<2>",), "dw_gate_up": ("bwd_gemm<3>",),
