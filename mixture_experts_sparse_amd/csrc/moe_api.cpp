@@ -275,12 +275,16 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* ids, int32_t* coun
   MOE_HIP(launch_rank(rp, s));
   const int tm = choose_tile_m(c.T * c.top_k, c.E);
   ScanParams sp{at<int32_t>(ws, L.blk_hist), ceil_div(c.T, rt), c.E, counts};
-  MOE_HIP(launch_scan(sp, s));
   ScatterParams xp{ids, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank), c.T, c.E,
                    c.top_k, rt, perm, inv, counts, offsets, max_m_tiles(c.T * c.top_k, c.E, tm), tm,
                    at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0), at<int32_t>(ws, L.meta),
                    at<int32_t>(ws, L.touched)};
-  MOE_HIP(launch_scatter(xp, s));
+  if (dispatch_fused(sp.NB, c.E)) {
+    MOE_HIP(launch_dispatch(sp, xp, s));
+  } else {
+    MOE_HIP(launch_scan(sp, s));
+    MOE_HIP(launch_scatter(xp, s));
+  }
   return MOE_OK;
 }
 
@@ -528,12 +532,16 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
   MOE_HIP(mark(1));
   if (NB > 1) {
     ScanParams sp{at<int32_t>(ws, L.blk_hist), NB, c.E, counts_p};
-    MOE_HIP(launch_scan(sp, s));
     ScatterParams xp{ids_p, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank), c.T, c.E,
                      c.top_k, rt, perm, inv, counts_p, offsets, max_m_tiles(c.T * c.top_k, c.E, tm), tm,
                      at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0), at<int32_t>(ws, L.meta),
                      at<int32_t>(ws, L.touched)};
-    MOE_HIP(launch_scatter(xp, s));
+    if (dispatch_fused(sp.NB, c.E)) {
+      MOE_HIP(launch_dispatch(sp, xp, s));
+    } else {
+      MOE_HIP(launch_scan(sp, s));
+      MOE_HIP(launch_scatter(xp, s));
+    }
   }
   MOE_HIP(mark(2));
 
@@ -697,12 +705,16 @@ moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w
   } else {
     MOE_HIP(launch_route(rp, c.dtype, s));
     ScanParams sp{at<int32_t>(ws, L.blk_hist), NB, c.E, counts};
-    MOE_HIP(launch_scan(sp, s));
     ScatterParams xp{ids, at<int32_t>(ws, L.blk_hist), at<int32_t>(ws, L.lrank), c.T, c.E,
                      c.top_k, rt, perm, inv, counts, offsets, max_m_tiles(P, c.E, tm), tm,
                      at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.exp_tile0), at<int32_t>(ws, L.meta),
                      at<int32_t>(ws, L.touched)};
-    MOE_HIP(launch_scatter(xp, s));
+    if (dispatch_fused(sp.NB, c.E)) {
+      MOE_HIP(launch_dispatch(sp, xp, s));
+    } else {
+      MOE_HIP(launch_scan(sp, s));
+      MOE_HIP(launch_scatter(xp, s));
+    }
   }
 
   BwdParams bp{};

@@ -270,6 +270,14 @@ hipError_t launch_route(const RouteParams& p, int dtype, hipStream_t s);
 hipError_t launch_rank(const RankParams& p, hipStream_t s);
 hipError_t launch_scan(const ScanParams& p, hipStream_t s);
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
+// The scan and the scatter in one launch (sp.blk_hist is read, not rewritten;
+// sp.counts receives the counts), for at most kDispMaxOwn * 64 route blocks
+// and kDispHist histogram entries (every workgroup reads the whole
+// histogram); larger dispatches take launch_scan then launch_scatter.
+constexpr int kDispMaxOwn = 8;
+constexpr long long kDispHist = 65536;
+bool dispatch_fused(int NB, int E);
+hipError_t launch_dispatch(const ScanParams& sp, const ScatterParams& p, hipStream_t s);
 hipError_t launch_tiles(const TilesParams& p, hipStream_t s);
 // Compute units of the current device (cached per device; 256 if unknown).
 int device_cus();

@@ -1011,6 +1011,143 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// dispatch kernel: the scan and the scatter in one launch, for histograms of
+// at most kDispHist entries. Each 1024-thread workgroup owns route blocks
+// [bs, bs + bpw) and reads the whole [NB, E] block histogram once itself
+// (thread (slice, e) sums blocks slice, slice + nsl, ... of expert e, all
+// loads of a batch of 32 in flight): the sum over all blocks is the expert's
+// count, the sum over blocks before bs the base of its first block (four
+// experts per thread with 16-byte loads when E is a multiple of 4). Offsets
+// are the exclusive scan of the counts; each owned block's base follows in
+// block order; every owned pair gets perm[offs[e] + base + rank] = pair and
+// inv[pair] = that row, as the scan and scatter kernels give. Workgroup 0
+// also writes counts, offsets, the tile table and the touched table.
+// ---------------------------------------------------------------------------
+constexpr int DTHR = 1024;
+__global__ __launch_bounds__(DTHR) void dispatch_kernel(ScanParams sp, ScatterParams p, int bpw) {
+  // per (slice, expert) partial sums: nsl slices of W entries
+  __shared__ int pre_s[4 * DTHR];
+  __shared__ int tot_s[4 * DTHR];
+  __shared__ int tot[kMaxE + 1];
+  __shared__ int offs[kMaxE + 1];
+  __shared__ int tp[kMaxE + 1];
+  __shared__ int flag[kMaxE + 1];
+  __shared__ int tpos[kMaxE + 1];
+  __shared__ int base[kDispMaxOwn][kMaxE];
+  const int tid = threadIdx.x, E = p.E, NB = sp.NB;
+  const int bs = blockIdx.x * bpw, be = min(bs + bpw, NB);
+  const int32_t* hist = sp.blk_hist;
+  constexpr int BB = 32;  // loads of a batch, all in flight
+  int nsl, W;
+  if (E % 4 == 0) {
+    // four experts per thread, 16-byte loads (rows of E ints stay aligned);
+    // 16 in flight (1024 threads leave 128 registers a lane)
+    constexpr int BV = 16;
+    const int Eq = E / 4;
+    const int Eqp = Eq <= 16 ? 16 : (Eq <= 32 ? 32 : 64);  // a power of two >= Eq
+    nsl = DTHR / Eqp;
+    W = 4 * Eqp;
+    const int eq = tid & (Eqp - 1), sl = tid / Eqp;
+    i32x4_t sum_pre = {0, 0, 0, 0}, sum_tot = {0, 0, 0, 0};
+    if (eq < Eq) {
+      for (int b0 = sl; b0 < NB; b0 += BV * nsl) {
+        i32x4_t v[BV];
+#pragma unroll
+        for (int u = 0; u < BV; ++u) {
+          const int b = min(b0 + u * nsl, NB - 1);
+          v[u] = *reinterpret_cast<const i32x4_t*>(hist + static_cast<size_t>(b) * E + 4 * eq);
+        }
+#pragma unroll
+        for (int u = 0; u < BV; ++u) pin(v[u]);
+#pragma unroll
+        for (int u = 0; u < BV; ++u) {
+          const int b = b0 + u * nsl;
+          if (b < NB) {
+            sum_tot += v[u];
+            if (b < bs) sum_pre += v[u];
+          }
+        }
+      }
+    }
+    *reinterpret_cast<i32x4_t*>(&pre_s[sl * W + 4 * eq]) = sum_pre;
+    *reinterpret_cast<i32x4_t*>(&tot_s[sl * W + 4 * eq]) = sum_tot;
+  } else {
+    const int Ep = E <= 64 ? 64 : (E <= 128 ? 128 : 256);  // a power of two >= E
+    nsl = DTHR / Ep;
+    W = Ep;
+    const int e = tid & (Ep - 1), sl = tid / Ep;
+    int sum_pre = 0, sum_tot = 0;
+    if (e < E) {
+      for (int b0 = sl; b0 < NB; b0 += BB * nsl) {
+        int v[BB];
+#pragma unroll
+        for (int u = 0; u < BB; ++u) {
+          const int b = min(b0 + u * nsl, NB - 1);
+          v[u] = hist[static_cast<size_t>(b) * E + e];
+        }
+#pragma unroll
+        for (int u = 0; u < BB; ++u) pin(v[u]);
+#pragma unroll
+        for (int u = 0; u < BB; ++u) {
+          const int b = b0 + u * nsl;
+          if (b < NB) {
+            sum_tot += v[u];
+            if (b < bs) sum_pre += v[u];
+          }
+        }
+      }
+    }
+    pre_s[sl * W + e] = sum_pre;
+    tot_s[sl * W + e] = sum_tot;
+  }
+  // the owned blocks' own counts
+  for (int i = tid; i < (be - bs) * E; i += DTHR) {
+    const int j = i / E, ee = i - j * E;
+    base[j][ee] = hist[static_cast<size_t>(bs + j) * E + ee];
+  }
+  __syncthreads();
+  if (tid < E) {
+    int a = 0, t = 0;
+    for (int q = 0; q < nsl; ++q) {
+      a += pre_s[q * W + tid];
+      t += tot_s[q * W + tid];
+    }
+    tot[tid] = t;
+    for (int j = 0; j < be - bs; ++j) {
+      const int v = base[j][tid];
+      base[j][tid] = a;
+      a += v;
+    }
+  }
+  __syncthreads();
+  if (tid < kWave) wave_exclusive_scan256(tot, offs, E);
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int ee = tid; ee < E; ee += DTHR) {
+      sp.counts[ee] = tot[ee];
+      tp[ee] = (tot[ee] + p.tile_m - 1) / p.tile_m;
+    }
+    __syncthreads();
+    if (tid < kWave) wave_exclusive_scan256(tp, tp, E);
+    __syncthreads();
+    for (int ee = tid; ee <= E; ee += DTHR) p.offsets[ee] = offs[ee];
+    write_tile_table(tp, E, p.max_tiles, p.tile_e, p.exp_tile0, p.meta);
+    if (p.touched != nullptr)
+      write_touched([&](int x) { return tot[x]; }, [&](int x) { return offs[x]; }, E, flag, tpos,
+                    p.touched, p.meta);
+  }
+  const int q0 = bs * p.rt * p.k, q1 = min(be * p.rt, p.T) * p.k;
+  for (int q = q0 + tid; q < q1; q += DTHR) {
+    const int t = q / p.k;
+    const int j = min(max(t / p.rt - bs, 0), bpw - 1);
+    const int ex = min(max(p.ids[q], 0), E - 1);
+    const int pos = offs[ex] + base[j][ex] + p.lrank[q];
+    p.perm[pos] = q;
+    p.inv[q] = pos;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // tile table from offsets (one workgroup)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void tiles_kernel(TilesParams p) {
@@ -1131,6 +1268,20 @@ hipError_t launch_rank(const RankParams& p, hipStream_t s) {
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t s) {
   scan_kernel<<<ceil_div(p.E, 16), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+int dispatch_blocks_per_wg(int NB) { return min(kDispMaxOwn, max(1, ceil_div(NB, 64))); }
+
+bool dispatch_fused(int NB, int E) {
+  return NB <= 64 * kDispMaxOwn && static_cast<long long>(NB) * E <= kDispHist;
+}
+
+hipError_t launch_dispatch(const ScanParams& sp, const ScatterParams& p, hipStream_t s) {
+  if (!dispatch_fused(sp.NB, p.E) || sp.NB != ceil_div(p.T, p.rt) || sp.E != p.E)
+    return hipErrorInvalidValue;
+  const int bpw = dispatch_blocks_per_wg(sp.NB);
+  dispatch_kernel<<<ceil_div(sp.NB, bpw), DTHR, 0, s>>>(sp, p, bpw);
   return hipGetLastError();
 }
 

@@ -80,6 +80,12 @@ SMALL = {
     "pers_d640": small_spec("gemma_upcycled", T=300, d=640, E=16, h=136, k=4),
     "pers_d640_two_mtiles": small_spec("gemma_upcycled", T=700, d=640, E=8, h=64, k=2),
     "pers_d640_shared": small_spec("shared_routed", T=260, d=640, E=8, h=96, k=2, shared_h=200),
+    # dispatch: the one-launch scan and scatter at eight route blocks per
+    # workgroup (500 blocks of 32 tokens, 128 experts), and the two-launch
+    # path once the block histogram passes 65536 entries (282 blocks x 256)
+    "dispatch_fused_8_blocks": small_spec("skewed_prefill", T=16000, d=64, E=128, h=32, k=2),
+    "dispatch_split_e256": MoESpec(name="e256_t9000", T=9000, d=64, E=256, h=32, k=2,
+                                   mode=SOFTMAX_SELECTED),
 }
 
 
