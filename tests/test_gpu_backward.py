@@ -158,7 +158,8 @@ def test_backward_no_tokens_zero_weight_grads():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["gemma_upcycled", "skewed_prefill", "shared_routed"])
+@pytest.mark.parametrize("name", ["gemma_upcycled", "skewed_prefill", "shared_routed",
+                                  "small_moe_sigmoid"])
 def test_backward_full(name):
     """A workload at full size, every gradient entry checked."""
     spec = spec_by_name(name)
