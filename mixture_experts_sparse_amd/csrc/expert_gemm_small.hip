@@ -757,16 +757,79 @@ __global__ __launch_bounds__(kDownCombineRows * 64) void down_combine_t1_kernel(
   }
 }
 
-hipError_t launch_down_combine_t1(const GemmParams& p, const CombineParams& c, hipStream_t s) {
+// A few tokens (2 <= T <= MOE_DOWN_COMBINE_MAX_T, at most kDownCombineMaxRows
+// rows, k <= kDownCombineRows; bf16 experts): the same launch with each wave
+// taking rows wave, wave + 8, ..., a row's expert read from a row -> expert
+// table the workgroup first builds in LDS from the touched table (an expert
+// may hold several rows now), and thread (t, column) combining token t.
+__global__ __launch_bounds__(kDownCombineRows * 64) void down_combine_few_kernel(GemmParams p,
+                                                                               CombineParams c) {
+  __shared__ float yv[kDownCombineMaxRows][kDcCols];
+  __shared__ int rowexp[kDownCombineMaxRows];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int n0 = blockIdx.x * kDcCols;
+  const int P = p.P, T = c.T, k = c.k;
+  // the combine's inputs first: thread (ct, cc) combines token ct, column n0 + cc
+  const int ct = tid / kDcCols, cc = tid - (tid / kDcCols) * kDcCols;
+  int rj[kDownCombineRows];
+  float gj[kDownCombineRows];
+  float sh = 0.f, sc = 0.f;
+  if (ct < T) {
+#pragma unroll
+    for (int j = 0; j < kDownCombineRows; ++j) {
+      const int q = ct * k + min(j, k - 1);
+      rj[j] = c.inv[q];
+      gj[j] = c.gates[q];
+    }
+    if (c.shared != nullptr) {
+      sh = bf16_to_f32(static_cast<const uint16_t*>(c.shared)[static_cast<size_t>(ct) * c.d + n0 + cc]);
+      sc = c.shared_scale != nullptr ? c.shared_scale[ct] : 1.0f;
+    }
+  }
+  // row -> expert: touched entry i covers rows [first, first + rows)
+  if (tid < min(P, p.E) && tid < p.meta[1]) {
+    const int4 ti = *reinterpret_cast<const int4*>(p.touched + 4 * tid);
+    const int r0 = min(max(ti.y, 0), P), r1 = min(r0 + max(ti.z, 0), P);
+    for (int r = r0; r < r1; ++r) rowexp[r] = ti.x;
+  }
+  __syncthreads();
+  const int col = min(n0 + (lane >> 3), p.N - 1);
+#pragma unroll 1
+  for (int r = wave; r < P; r += kDownCombineRows) {
+    const int e = min(max(__builtin_amdgcn_readfirstlane(rowexp[r]), 0), p.E - 1);
+    float v = dc_dot_bf16<kDownCombineMaxK / 64>(p, e, col, r, (lane & 7) * 8);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    if ((lane & 7) == 0) yv[r][lane >> 3] = bf16_to_f32(f32_to_bf16(v));
+  }
+  __syncthreads();
+  if (ct < T) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < kDownCombineRows; ++j)
+      if (j < k) acc = fmaf(gj[j], yv[min(max(rj[j], 0), P - 1)][cc], acc);
+    if (c.shared != nullptr) acc = fmaf(sc, sh, acc);
+    static_cast<uint16_t*>(c.out)[static_cast<size_t>(ct) * c.d + n0 + cc] = f32_to_bf16(acc);
+  }
+}
+
+hipError_t launch_down_combine(const GemmParams& p, const CombineParams& c, hipStream_t s) {
   const bool q4 = p.quant == MOE_QUANT_Q4_G64;
   if (p.dtype != MOE_BF16 || (!q4 && p.quant != MOE_QUANT_NONE) || (q4 && p.b0_sb == nullptr) ||
-      p.kind != 1 || c.T != 1 || c.k != p.P || p.P < 1 || p.P > kDownCombineRows ||
+      p.kind != 1 || c.T < 1 || c.T > MOE_DOWN_COMBINE_MAX_T || (q4 && c.T != 1) || c.k < 1 ||
+      c.k > kDownCombineRows || c.T * c.k != p.P || p.P > kDownCombineMaxRows ||
       p.K % 64 != 0 || p.K > kDownCombineMaxK || p.N != c.d || p.N % kDcCols != 0 ||
-      p.touched == nullptr)
+      p.touched == nullptr || p.meta == nullptr)
     return hipErrorInvalidValue;
   const unsigned g = static_cast<unsigned>(p.N / kDcCols);
-  if (q4) down_combine_t1_kernel<true><<<g, kDownCombineRows * 64, 0, s>>>(p, c);
-  else down_combine_t1_kernel<false><<<g, kDownCombineRows * 64, 0, s>>>(p, c);
+  if (c.T == 1) {
+    if (q4) down_combine_t1_kernel<true><<<g, kDownCombineRows * 64, 0, s>>>(p, c);
+    else down_combine_t1_kernel<false><<<g, kDownCombineRows * 64, 0, s>>>(p, c);
+  } else {
+    down_combine_few_kernel<<<g, kDownCombineRows * 64, 0, s>>>(p, c);
+  }
   return hipGetLastError();
 }
 

@@ -584,11 +584,11 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
   if (q4) { g2.quant = MOE_QUANT_Q4_G64; g2.b0_sb = w->w_down_sb; }
   CombineParams cp{y, inv, gates_p, c.shared_h > 0 ? ys : nullptr, sg, out, c.T, c.d, c.top_k,
                     c.dtype, c.T * c.top_k};
-  const bool fused_combine = down_combine_one_token(c);
+  const bool fused_combine = down_combine_fused(c);
   if (fused_combine) {
-    // the shared row first: the one-token down launch adds it
+    // the shared rows first: the down launch adds them
     if (c.shared_h > 0) MOE_HIP(launch_gemm(shared_only(1), s));
-    MOE_HIP(launch_down_combine_t1(g2, cp, s));
+    MOE_HIP(launch_down_combine(g2, cp, s));
   } else if (small) {
     MOE_HIP(launch_gemm_small(g2, s));
     if (c.shared_h > 0) MOE_HIP(launch_gemm(shared_only(1), s));

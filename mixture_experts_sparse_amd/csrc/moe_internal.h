@@ -289,17 +289,28 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 // dispatch tables through *route, as the split router's finish would.
 hipError_t launch_gemm_small(const GemmParams& p, hipStream_t s,
                              const RouteParams* route = nullptr);
-// One token: the routed down projection and the combine in one launch
-// (y is never stored). k <= kDownCombineRows rows, h a multiple of 64 up to
-// kDownCombineMaxK, bf16 layers with activation-dtype or 4-bit experts; the
-// shared expert's row, if any, must already be in c.shared.
+// A few tokens: the routed down projection and the combine in one launch
+// (y is never stored). T <= MOE_DOWN_COMBINE_MAX_T, k <= kDownCombineRows,
+// T * k <= kDownCombineMaxRows rows, h a multiple of 64 up to
+// kDownCombineMaxK, bf16 layers with activation-dtype experts, or 4-bit
+// experts at one token; the shared expert's rows, if any, must already be in
+// c.shared. Measured on MI355X at d = 2048, h = 1024, 64 experts, top-8:
+// bf16 layers gain 4 / 4 / 1.3 us per layer at 1 / 2 / 4 tokens; 4-bit ones
+// gain 1.2 us at one token, none at two and lose 4 at four (their
+// vector-ALU code expansion then runs row after row in each wave, where the
+// separate 4-bit down kernel puts it on MFMA operands).
+#ifndef MOE_DOWN_COMBINE_MAX_T
+#define MOE_DOWN_COMBINE_MAX_T 4
+#endif
 constexpr int kDownCombineRows = 8;
+constexpr int kDownCombineMaxRows = 32;
 constexpr int kDownCombineMaxK = 1024;
-inline bool down_combine_one_token(const moe_config& c) {
-  return c.T == 1 && use_small_gemm(c) && c.top_k <= kDownCombineRows && c.h % 64 == 0 &&
-         c.h <= kDownCombineMaxK;
+inline bool down_combine_fused(const moe_config& c) {
+  return c.T <= MOE_DOWN_COMBINE_MAX_T && (c.T == 1 || c.expert_quant == MOE_QUANT_NONE) &&
+         use_small_gemm(c) && c.top_k <= kDownCombineRows &&
+         c.T * c.top_k <= kDownCombineMaxRows && c.h % 64 == 0 && c.h <= kDownCombineMaxK;
 }
-hipError_t launch_down_combine_t1(const GemmParams& p, const CombineParams& c, hipStream_t s);
+hipError_t launch_down_combine(const GemmParams& p, const CombineParams& c, hipStream_t s);
 // The split router's logits kernel alone, then with its finish.
 hipError_t launch_route_part(const RouteParams& p, int dtype, hipStream_t s);
 hipError_t launch_route_split(const RouteParams& p, int dtype, hipStream_t s);

@@ -362,6 +362,10 @@ TINY_ROUTE = {
     # one token, down and combine in one launch: three rows, a reduction of
     # three 64-wide loads, a width of 40 eight-column slices
     "T1_k3_h192": small_spec("decode", T=1, d=320, E=16, h=192, k=3),
+    # a few tokens, down and combine in one launch: experts holding several
+    # rows (4 tokens, 4 experts, top-2), and 15 rows over a 9-slice width
+    "T4_E4_multirow": small_spec("decode", T=4, d=256, E=4, h=128, k=2),
+    "T3_k5_h128": small_spec("decode", T=3, d=72, E=16, h=128, k=5),
 }
 
 
