@@ -74,7 +74,7 @@ STAGE_KERNEL = {"route": ("route_kernel", "route_part_kernel"),
                 "gate_up": ("gemm_bf16_pers<0", "gemm_bf16_kernel<0", "gemm_small_kernel<0",
                             "gemm_small_q4_lds<0"),
                 "down": ("gemm_bf16_pers<1", "gemm_bf16_kernel<1", "gemm_small_kernel<1",
-                         "gemm_small_pers<1", "gemm_small_q4_lds<1", "down_combine_t1"),
+                         "gemm_small_pers<1", "gemm_small_q4_lds<1", "down_combine_"),
                 "combine": ("combine_",)}
 
 
