@@ -57,6 +57,7 @@ def _both(inp, d, T):
 
 @pytest.mark.parametrize("name,T1,T2", [
     ("decode", 64, 16),          # full decode shape, then a smaller batch
+    ("decode", 4, 1),            # the few-token and one-token launch sequences
     ("shared_small", 700, 300),  # several route blocks and tiled GEMMs, shared expert
 ])
 def test_noalloc_matches_workspace_entry(name, T1, T2):
