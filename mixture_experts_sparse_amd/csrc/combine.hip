@@ -50,7 +50,10 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineParams p) {
 #pragma unroll
     for (int u = 0; u < CKB; ++u) {
       const int rr = min(max(r[u], 0), p.y_rows - 1);
-      v[u] = *reinterpret_cast<const u32x4_t*>(y + static_cast<size_t>(rr) * p.d + c);
+      // y is read once: streamed past the caches (measured on MI355X at the
+      // skewed prefill shape, 537 MB of y: 118 -> 100 us)
+      v[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(y + static_cast<size_t>(rr) * p.d + c));
     }
 #pragma unroll
     for (int u = 0; u < CKB; ++u) pin(v[u]);
@@ -78,7 +81,8 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(CombineParams p) {
     o[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i])) |
            (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
   }
-  *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.out) + static_cast<size_t>(t) * p.d + c) = o;
+  __builtin_nontemporal_store(
+      o, reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.out) + static_cast<size_t>(t) * p.d + c));
 }
 
 template <int CKB>
