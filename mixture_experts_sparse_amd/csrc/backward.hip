@@ -657,7 +657,13 @@ __global__ __launch_bounds__(NT_, bwd_occupancy<PROB>()) void bwd_gemm(BwdParams
               continue;
             }
           }
-          *reinterpret_cast<float4*>(dst_row(ir) + t.n0 + col) = v;
+          if constexpr (PROB == PROB_DWD || PROB == PROB_DWGU) {
+            // weight gradients are written once and not read here: past the caches
+            __builtin_nontemporal_store(floatx4_t{v.x, v.y, v.z, v.w},
+                                        reinterpret_cast<floatx4_t*>(dst_row(ir) + t.n0 + col));
+          } else {
+            *reinterpret_cast<float4*>(dst_row(ir) + t.n0 + col) = v;
+          }
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -852,7 +852,9 @@ __global__ __launch_bounds__(512) void gemm_wgrad_kernel(GemmParams p) {
         } else {
           row = O1 + (sh ? 0 : static_cast<size_t>(e) * M * N) + static_cast<size_t>(m) * N;
         }
-        *reinterpret_cast<float4*>(row + c0 + ch * 4) = v;
+        // written once and not read here: past the caches
+        __builtin_nontemporal_store(floatx4_t{v.x, v.y, v.z, v.w},
+                                    reinterpret_cast<floatx4_t*>(row + c0 + ch * 4));
       }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the slice is rewritten
