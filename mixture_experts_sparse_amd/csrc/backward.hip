@@ -688,7 +688,12 @@ __global__ __launch_bounds__(256) void dx_finish_kernel(BwdParams p) {
     uint2 r[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      if (s0 + s < p.k) r[s] = *reinterpret_cast<const uint2*>(rows + static_cast<size_t>(s0 + s) * p.d);
+      if (s0 + s < p.k) {  // each dx row is read once: past the caches
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t q = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x2_t*>(rows + static_cast<size_t>(s0 + s) * p.d));
+        r[s] = uint2{q.x, q.y};
+      }
 #pragma unroll
     for (int s = 0; s < 8; ++s)
       if (s0 + s < p.k) {
@@ -700,7 +705,8 @@ __global__ __launch_bounds__(256) void dx_finish_kernel(BwdParams p) {
     const float4 u = *reinterpret_cast<const float4*>(p.dx_s + t * p.d + c);
     v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
   }
-  *reinterpret_cast<float4*>(p.dx + t * p.d + c) = v;
+  __builtin_nontemporal_store(floatx4_t{v.x, v.y, v.z, v.w},
+                              reinterpret_cast<floatx4_t*>(p.dx + t * p.d + c));
 }
 
 // One wave per token: the gate gradients dG from the per-tile partial sums,
