@@ -652,7 +652,7 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bf16_kernel(GemmParams p)
 // ---------------------------------------------------------------------------
 template <int KIND, int S, int BK>
 __global__ __launch_bounds__(512) void gemm_wgrad_kernel(GemmParams p) {
-  constexpr int NWM = 4, NWN = 2, NFW = 8, KS = BK / 32, NTHR = 512;
+  constexpr int NWM = 4, NFW = 8, KS = BK / 32, NTHR = 512;  // 4 x 2 waves of 64 x 128
   constexpr int BM = 256, BN = 256;
   constexpr int SA = BK * BM, SEL = SA + BK * BN;  // bf16 per stage
   constexpr int LA = SA / 8 / NTHR;                 // 16-byte loads per thread per operand and stage

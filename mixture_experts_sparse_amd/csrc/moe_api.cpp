@@ -522,8 +522,8 @@ moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
     if (use_small_gemm(c)) rp.tile_e = nullptr;
     rp.part = at<float>(ws, L.part);
     rp.ncp = route_part_cols(c.E, gated);
-    // at most four tokens: the selection and the dispatch tables are made
-    // inside the gate/up launch from the logits of this one
+    // the smallest batches (route_in_gate_up): the selection and the
+    // dispatch tables are made inside the gate/up launch from these logits
     if (fused_route) MOE_HIP(launch_route_part(rp, c.dtype, s));
     else MOE_HIP(launch_route_split(rp, c.dtype, s));
   } else {
@@ -677,7 +677,6 @@ moe_status moe_layer_backward_traced(const moe_config* cfg, const moe_weights* w
   float* sg = gated ? at<float>(ws, L.sgate) : nullptr;
   float* logits = at<float>(ws, B.logits);
 
-  const bool fused_route = NB == 1 && route_in_gate_up(c);
   MOE_HIP(mark(0));
   RouteParams rp{};
   rp.x = x;

@@ -21,8 +21,6 @@
 namespace moe {
 
 constexpr int RTM = kRouteTokensMax;  // most tokens per route block
-constexpr int RK = 64;            // K chunk of the router GEMM
-constexpr int RLD = RK + 8;       // padded LDS row (bf16 elements)
 constexpr int kMaxE = MOE_MAX_EXPERTS;
 
 // ---------------------------------------------------------------------------
