@@ -86,6 +86,9 @@ SMALL = {
     "dispatch_fused_8_blocks": small_spec("skewed_prefill", T=16000, d=64, E=128, h=32, k=2),
     "dispatch_split_e256": MoESpec(name="e256_t9000", T=9000, d=64, E=256, h=32, k=2,
                                    mode=SOFTMAX_SELECTED),
+    # exactly at the one-launch limits: 512 route blocks of 32 tokens x 128
+    # experts = 65536 histogram entries, eight blocks per workgroup
+    "dispatch_fused_at_limit": small_spec("skewed_prefill", T=16383, d=64, E=128, h=32, k=2),
     # the two-launch path past 512 route blocks (625 blocks of 64 tokens, 8 experts)
     "dispatch_split_625_blocks": small_spec("decode", T=40000, d=64, E=8, h=32, k=2),
 }
