@@ -278,7 +278,9 @@ moe_status moe_routing_stats(const moe_config* cfg, const float* logits, const i
  *   on average (T * top_k <= 16 * E) with d and h multiples of 64 and at most
  *   4096, in bf16; other quantised shapes return MOE_ERR_UNSUPPORTED. Per
  *   scale group the kernels form s * sum x (128 + q) + (b - 128 s) * sum x
- *   with bf16 products and float32 accumulation (128 + q is exact in bf16). */
+ *   with bf16 products and float32 accumulation (128 + q is exact in bf16);
+ *   at one token the down projection forms s * sum a q + b * sum a in
+ *   float32 instead. */
 moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const void* x,
                              void* out, int32_t* ids, float* gates, int32_t* counts,
                              void* ws, size_t ws_bytes, void* stream);
@@ -287,7 +289,10 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const 
  * launch and stage_events[i + 1] after stage i (MOE_NUM_STAGES stages:
  * route, dispatch, gate_up, down, combine). stage_events holds
  * MOE_NUM_STAGES + 1 hipEvent_t created by the caller; NULL = untraced, and
- * a NULL entry is not recorded (so one stage can be bracketed alone). */
+ * a NULL entry is not recorded (so one stage can be bracketed alone). A
+ * stage whose work a neighbouring launch does brackets no launch: the
+ * dispatch at one token (made inside gate/up) and the combine at up to four
+ * tokens on the small-batch kernels (made inside down). */
 moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
                                     const void* x, void* out, int32_t* ids, float* gates,
                                     int32_t* counts, void* ws, size_t ws_bytes,
