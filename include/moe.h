@@ -291,8 +291,9 @@ moe_status moe_layer_forward(const moe_config* cfg, const moe_weights* w, const 
  * MOE_NUM_STAGES + 1 hipEvent_t created by the caller; NULL = untraced, and
  * a NULL entry is not recorded (so one stage can be bracketed alone). A
  * stage whose work a neighbouring launch does brackets no launch: the
- * dispatch at one token (made inside gate/up) and the combine at up to four
- * tokens on the small-batch kernels (made inside down). */
+ * dispatch at one token (made inside gate/up) and, on the small-batch
+ * kernels, the combine at one token and, with activation-dtype experts, at
+ * up to four (made inside down). */
 moe_status moe_layer_forward_traced(const moe_config* cfg, const moe_weights* w,
                                     const void* x, void* out, int32_t* ids, float* gates,
                                     int32_t* counts, void* ws, size_t ws_bytes,
